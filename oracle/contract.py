@@ -1,0 +1,104 @@
+"""Decomposed pairwise tropical einsum, the oracle's version.
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+Follows the pipeline of omeinsum-rs issue #52 ("GPU tropical path: keep
+tensors device-resident + device-side permute"), section "Resolved design
+for step 3" and its "Structural lessons from OMEinsum": repeated labels are
+removed by a separate unary pre-pass (diagonal, or a (+)-reduction for a
+label that appears in one operand only), the operands are permuted into
+canonical order, one batched tropical GEMM runs, and its value and argmax
+are permuted into the output order with one and the same index mapping.
+
+Canonical orders (row-major):
+    A'' = (batch..., left..., contracted...)
+    B'' = (batch..., contracted..., right...)
+    C'' = (batch..., left..., right...)
+batch / left / right labels are taken in output order, contracted labels in
+the order they first appear in A's subscript.  The argmax is therefore the
+row-major linear index over the contracted labels in A-subscript order.
+"""
+import numpy as np
+
+from . import OracleError
+
+
+def parse(spec):
+    spec = spec.replace(" ", "")
+    if spec.count("->") != 1:
+        raise OracleError("spec needs exactly one '->'")
+    lhs, out = spec.split("->")
+    if lhs.count(",") != 1:
+        raise OracleError("spec needs exactly two operands")
+    la, lb = lhs.split(",")
+    for c in la + lb + out:
+        if not c.isalpha() or not c.isascii():
+            raise OracleError(f"bad label {c!r}")
+    if len(set(out)) != len(out):
+        raise OracleError("repeated output label")
+    for c in out:
+        if c not in la and c not in lb:
+            raise OracleError(f"output label {c!r} appears in no operand")
+    return la, lb, out
+
+
+def _unique(s):
+    seen = []
+    for c in s:
+        if c not in seen:
+            seen.append(c)
+    return seen
+
+
+def roles(la, lb, out):
+    batch = [c for c in out if c in la and c in lb]
+    left = [c for c in out if c in la and c not in lb]
+    right = [c for c in out if c in lb and c not in la]
+    contracted = [c for c in _unique(la) if c in lb and c not in out]
+    a_reduce = [c for c in _unique(la) if c not in lb and c not in out]
+    b_reduce = [c for c in _unique(lb) if c not in la and c not in out]
+    return batch, left, right, contracted, a_reduce, b_reduce
+
+
+def _prepare(orc, sr, x, sub, reduce_labels, canonical):
+    """Unary pre-pass (diagonal / trace), then permute to `canonical`."""
+    kept = [c for c in _unique(sub) if c not in reduce_labels]
+    y = orc.diag_gather(sr, x, sub, "".join(kept))
+    perm = [kept.index(c) for c in canonical]
+    return orc.permute(y, perm)
+
+
+def contract_pair(orc, spec, sr, A, B, argmax=True):
+    A = np.asarray(A)
+    B = np.asarray(B)
+    la, lb, out = parse(spec)
+    if len(la) != A.ndim or len(lb) != B.ndim:
+        raise OracleError("subscript rank mismatch")
+    ext = {}
+    for sub, arr in ((la, A), (lb, B)):
+        for c, e in zip(sub, arr.shape):
+            if c in ext and ext[c] != e:
+                raise OracleError(f"extent mismatch for label {c!r}")
+            ext[c] = e
+    batch, left, right, contracted, a_red, b_red = roles(la, lb, out)
+    if argmax and (a_red or b_red):
+        raise OracleError("argmax through a pre-pass reduction is unsupported")
+
+    A2 = _prepare(orc, sr, A, la, a_red, batch + left + contracted)
+    B2 = _prepare(orc, sr, B, lb, b_red, batch + contracted + right)
+
+    def prod(labels):
+        p = 1
+        for c in labels:
+            p *= ext[c]
+        return p
+
+    nb, m, n, k = prod(batch), prod(left), prod(right), prod(contracted)
+    C2, I2 = orc.gemm(sr, A2.reshape(nb, m, k), B2.reshape(nb, k, n), argmax=argmax)
+
+    canon = batch + left + right
+    shape = [ext[c] for c in canon]
+    perm = [canon.index(c) for c in out]
+    C = orc.permute(C2.reshape(shape), perm)
+    I = orc.permute(I2.reshape(shape), perm) if argmax else None
+    return C, I

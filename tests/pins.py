@@ -1,0 +1,449 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle.
+
+Each pin takes an ``oracle.Oracle`` handle and raises AssertionError when
+the oracle disagrees with:
+  * hand-worked examples (tests/golden/, each with its citation),
+  * library routines (torch CPU broadcast + amax/argmax, whose argmax is
+    documented to return the first maximal index; torch.permute;
+    torch.diagonal),
+  * algebraic identities of the semirings (unit, absorbing zero,
+    associativity on exactly representable data, transpose symmetry),
+  * a textbook algorithm (Floyd-Warshall shortest paths vs min-plus
+    repeated squaring),
+  * brute-force enumeration (the einsum path vs the decomposed path).
+
+They are deliberately small so that tests/test_oracle_mutants.py can run
+them all against many planted-mistake builds of the oracle in seconds.
+"""
+import itertools
+
+import numpy as np
+import torch
+
+import golden_io as gio
+
+I32_INF = 1 << 30
+SR = ("max_plus", "min_plus", "max_mul")
+
+
+def _bits_equal(a, b, what):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    ok = np.array_equal(a.view(np.int32), b.view(np.int32))
+    if not ok:
+        bad = np.argwhere(a.view(np.int32) != b.view(np.int32))
+        pos = tuple(bad[0])
+        raise AssertionError(f"{what}: first mismatch at {pos}: {a[pos]!r} vs {b[pos]!r} "
+                             f"({len(bad)} mismatches)")
+
+
+def _eq(a, b, what):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    if not np.array_equal(a, b):
+        bad = np.argwhere(a != b)
+        pos = tuple(bad[0])
+        raise AssertionError(f"{what}: first mismatch at {pos}: {a[pos]!r} vs {b[pos]!r}")
+
+
+# ----------------------------------------------------------------------
+# hand-worked examples
+# ----------------------------------------------------------------------
+
+def pin_golden_gemm(orc):
+    for case in gio.load("gemm_3x3.json")["cases"]:
+        A = gio.array(case["A"], case["dtype"])
+        B = gio.array(case["B"], case["dtype"])
+        C, I = orc.gemm(case["semiring"], A, B)
+        _bits_equal(C[0], gio.array(case["C"], case["dtype"]), case["name"])
+        _eq(I[0], np.array(case["argmax"]), case["name"] + " argmax")
+
+
+def pin_golden_special_values(orc):
+    for case in gio.load("special_values.json")["cases"]:
+        A = gio.array(case["A"], case["dtype"])
+        B = gio.array(case["B"], case["dtype"])
+        C, I = orc.gemm(case["semiring"], A, B)
+        _bits_equal(C[0], gio.array(case["C"], case["dtype"]), case["name"])
+        _eq(I[0], np.array(case["argmax"]), case["name"] + " argmax")
+
+
+def pin_golden_einsum(orc):
+    g = gio.load("einsum_iijb_kjb_bki.json")
+    A = np.zeros(g["A_shape"], dtype=np.float32)
+    for e in g["A_entries"]:
+        A[tuple(e["index"])] = gio.f32(e["value"])
+    B = gio.nested(g["B"], "f32")
+    want = gio.nested(g["out"], "f32")
+    wanti = np.array(g["argmax"], dtype=np.int32)
+    for fn in (orc.contract_pair, None):
+        if fn is None:
+            C, I = orc.einsum_brute(g["semiring"], g["spec"], A, B)
+        else:
+            C, I = fn(g["spec"], g["semiring"], A, B)
+        _bits_equal(C, want, "einsum golden")
+        _eq(I, wanti, "einsum golden argmax")
+
+
+# ----------------------------------------------------------------------
+# library routine: torch CPU broadcast + amax / argmax
+# ----------------------------------------------------------------------
+
+def torch_tropical(sr, A, B):
+    """Reference through torch: materialise every term, reduce with
+    torch's amax/argmax (first index on ties), then apply the zero-side
+    rule (a result that is not strictly better than the zero element is
+    the zero element, with argmax 0)."""
+    At = torch.from_numpy(np.ascontiguousarray(A))
+    Bt = torch.from_numpy(np.ascontiguousarray(B))
+    if At.dtype == torch.int32:
+        T = At.to(torch.int64)[:, :, :, None] + Bt.to(torch.int64)[:, None, :, :]
+        T = T.clamp(-(2 ** 31), 2 ** 31 - 1)
+        zero = I32_INF if sr == "min_plus" else -I32_INF
+    else:
+        if sr == "max_mul":
+            T = At[:, :, :, None] * Bt[:, None, :, :]
+            zero = 0.0
+        else:
+            T = At[:, :, :, None] + Bt[:, None, :, :]
+            zero = float("inf") if sr == "min_plus" else float("-inf")
+    if sr == "min_plus":
+        val, arg = T.min(dim=2)
+        none = val >= zero
+    else:
+        val, arg = T.max(dim=2)
+        none = val <= zero
+    val = torch.where(none, torch.full_like(val, zero), val)
+    arg = torch.where(none, torch.zeros_like(arg), arg)
+    return val.to(At.dtype).numpy(), arg.to(torch.int32).numpy()
+
+
+def _rand_case(sr, dtype, shape_b_m_k_n, seed):
+    b, m, k, n = shape_b_m_k_n
+    g = torch.Generator().manual_seed(seed)
+    if dtype == "i32":
+        A = torch.randint(-6, 7, (b, m, k), generator=g, dtype=torch.int32)
+        B = torch.randint(-6, 7, (b, k, n), generator=g, dtype=torch.int32)
+        A[torch.rand((b, m, k), generator=g) < 0.2] = I32_INF if sr == "min_plus" else -I32_INF
+        B[torch.rand((b, k, n), generator=g) < 0.2] = I32_INF if sr == "min_plus" else -I32_INF
+    elif sr == "max_mul":
+        A = torch.randint(1, 5, (b, m, k), generator=g).to(torch.float32) * 0.25
+        B = torch.randint(1, 5, (b, k, n), generator=g).to(torch.float32) * 0.5
+    else:
+        A = torch.randint(-4, 5, (b, m, k), generator=g).to(torch.float32)
+        B = torch.randint(-4, 5, (b, k, n), generator=g).to(torch.float32)
+        inf = float("inf") if sr == "min_plus" else float("-inf")
+        A[torch.rand((b, m, k), generator=g) < 0.1] = inf
+    return A.numpy(), B.numpy()
+
+
+def pin_torch_crosscheck(orc):
+    shapes = [(2, 5, 7, 3), (1, 1, 1, 1), (3, 4, 9, 6)]
+    for sr in SR:
+        for dtype in ("f32", "i32"):
+            if sr == "max_mul" and dtype == "i32":
+                continue
+            for s, shp in enumerate(shapes):
+                A, B = _rand_case(sr, dtype, shp, 100 + s)
+                C, I = orc.gemm(sr, A, B)
+                Cr, Ir = torch_tropical(sr, A, B)
+                _bits_equal(C, Cr, f"torch {sr} {dtype} {shp}")
+                _eq(I, Ir, f"torch {sr} {dtype} {shp} argmax")
+
+
+def pin_torch_random_normal(orc):
+    """Continuous data: no ties, so value and index are fixed by torch."""
+    g = torch.Generator().manual_seed(7)
+    A = torch.randn(3, 6, 11, generator=g).numpy()
+    B = torch.randn(3, 11, 5, generator=g).numpy()
+    for sr in ("max_plus", "min_plus"):
+        C, I = orc.gemm(sr, A, B)
+        Cr, Ir = torch_tropical(sr, A, B)
+        _bits_equal(C, Cr, f"normal {sr}")
+        _eq(I, Ir, f"normal {sr} argmax")
+    Ap, Bp = np.abs(A) + 0.5, np.abs(B) + 0.5
+    C, I = orc.gemm("max_mul", Ap, Bp)
+    Cr, Ir = torch_tropical("max_mul", Ap, Bp)
+    _bits_equal(C, Cr, "normal max_mul")
+    _eq(I, Ir, "normal max_mul argmax")
+
+
+# ----------------------------------------------------------------------
+# semiring identities
+# ----------------------------------------------------------------------
+
+def _unit(sr, n, dtype):
+    if dtype == "i32":
+        z = I32_INF if sr == "min_plus" else -I32_INF
+        M = np.full((n, n), z, dtype=np.int32)
+        np.fill_diagonal(M, 0)
+    else:
+        z = {"max_plus": -np.inf, "min_plus": np.inf, "max_mul": 0.0}[sr]
+        M = np.full((n, n), z, dtype=np.float32)
+        np.fill_diagonal(M, 1.0 if sr == "max_mul" else 0.0)
+    return M
+
+
+def pin_unit_and_zero(orc):
+    rng = np.random.default_rng(3)
+    for sr in SR:
+        for dtype in ("f32", "i32"):
+            if sr == "max_mul" and dtype == "i32":
+                continue
+            if dtype == "i32":
+                # the int32 sentinel is absorbing only on its own side of 0:
+                # entries <= 0 for max-plus, >= 0 for min-plus
+                A = rng.integers(1, 51, size=(5, 7)).astype(np.int32)
+                if sr == "max_plus":
+                    A = -A
+            elif sr == "max_mul":
+                A = (rng.integers(1, 9, size=(5, 7)) * 0.125).astype(np.float32)
+            else:
+                A = rng.standard_normal((5, 7)).astype(np.float32)
+            C, I = orc.gemm(sr, A, _unit(sr, 7, dtype))
+            _bits_equal(C[0], A, f"A (x) I {sr} {dtype}")
+            _eq(I[0], np.tile(np.arange(7), (5, 1)), f"A (x) I argmax {sr} {dtype}")
+            C, I = orc.gemm(sr, _unit(sr, 5, dtype), A)
+            _bits_equal(C[0], A, f"I (x) A {sr} {dtype}")
+            _eq(I[0], np.tile(np.arange(5)[:, None], (1, 7)), f"I (x) A argmax {sr} {dtype}")
+            Z = _unit(sr, 7, dtype)
+            np.fill_diagonal(Z, Z[0, 1])
+            C, I = orc.gemm(sr, A, Z)
+            _bits_equal(C[0], np.full((5, 7), Z[0, 1], dtype=Z.dtype), f"A (x) 0 {sr} {dtype}")
+            _eq(I[0], np.zeros((5, 7), dtype=np.int32), f"A (x) 0 argmax {sr} {dtype}")
+
+
+def pin_empty_and_k0(orc):
+    for sr in SR:
+        A = np.zeros((2, 3, 0), dtype=np.float32)
+        B = np.zeros((2, 0, 4), dtype=np.float32)
+        C, I = orc.gemm(sr, A, B)
+        z = {"max_plus": -np.inf, "min_plus": np.inf, "max_mul": 0.0}[sr]
+        _bits_equal(C, np.full((2, 3, 4), z, dtype=np.float32), f"K=0 {sr}")
+        _eq(I, np.zeros((2, 3, 4), dtype=np.int32), f"K=0 argmax {sr}")
+    C, I = orc.gemm("max_plus", np.zeros((1, 0, 3), np.float32), np.zeros((1, 3, 2), np.float32))
+    assert C.shape == (1, 0, 2) and I.shape == (1, 0, 2)
+
+
+def pin_associativity(orc):
+    rng = np.random.default_rng(11)
+    cases = [
+        ("max_plus", rng.integers(-20, 21, size=(3, 4, 5)).astype(np.float32),
+         rng.integers(-20, 21, size=(3, 5, 6)).astype(np.float32),
+         rng.integers(-20, 21, size=(3, 6, 2)).astype(np.float32)),
+        ("min_plus", rng.integers(0, 30, size=(2, 5, 4)).astype(np.float32),
+         rng.integers(0, 30, size=(2, 4, 7)).astype(np.float32),
+         rng.integers(0, 30, size=(2, 7, 3)).astype(np.float32)),
+        ("max_mul", np.exp2(rng.integers(-6, 7, size=(2, 4, 6))).astype(np.float32),
+         np.exp2(rng.integers(-6, 7, size=(2, 6, 5))).astype(np.float32),
+         np.exp2(rng.integers(-6, 7, size=(2, 5, 3))).astype(np.float32)),
+    ]
+    Ai = rng.integers(0, 1000, size=(2, 5, 6)).astype(np.int32)
+    Bi = rng.integers(0, 1000, size=(2, 6, 4)).astype(np.int32)
+    Ci = rng.integers(0, 1000, size=(2, 4, 3)).astype(np.int32)
+    for M in (Ai, Bi, Ci):
+        M[rng.random(M.shape) < 0.3] = I32_INF
+    cases.append(("min_plus", Ai, Bi, Ci))
+    for sr, A, B, Cm in cases:
+        AB, _ = orc.gemm(sr, A, B)
+        left, _ = orc.gemm(sr, AB, Cm)
+        BC, _ = orc.gemm(sr, B, Cm)
+        right, _ = orc.gemm(sr, A, BC)
+        _bits_equal(left, right, f"associativity {sr} {A.dtype}")
+
+
+def pin_transpose_symmetry(orc):
+    """(A (x) B)^T = B^T (x) A^T with the same argmax, using transposed
+    (column-major) views so that both stride paths are exercised."""
+    rng = np.random.default_rng(5)
+    A = rng.integers(-3, 4, size=(2, 6, 9)).astype(np.float32)
+    B = rng.integers(-3, 4, size=(2, 9, 4)).astype(np.float32)
+    for sr in ("max_plus", "min_plus"):
+        C, I = orc.gemm(sr, A, B)
+        Ct, It = orc.gemm(sr, B.transpose(0, 2, 1), A.transpose(0, 2, 1))
+        _bits_equal(Ct, C.transpose(0, 2, 1), f"transpose {sr}")
+        _eq(It, I.transpose(0, 2, 1), f"transpose argmax {sr}")
+        Cc, Ic = orc.gemm(sr, np.ascontiguousarray(A.transpose(0, 2, 1)).transpose(0, 2, 1),
+                          np.ascontiguousarray(B.transpose(0, 2, 1)).transpose(0, 2, 1))
+        _bits_equal(Cc, C, f"column-major operands {sr}")
+        _eq(Ic, I, f"column-major operands argmax {sr}")
+
+
+def _floyd_warshall(W, inf):
+    n = len(W)
+    d = [[int(W[i][j]) for j in range(n)] for i in range(n)]
+    for k in range(n):
+        for i in range(n):
+            for j in range(n):
+                if d[i][k] + d[k][j] < d[i][j]:
+                    d[i][j] = d[i][k] + d[k][j]
+    return [[min(x, inf) for x in row] for row in d]
+
+
+def pin_floyd_warshall(orc):
+    rng = np.random.default_rng(17)
+    n = 13
+    Wi = rng.integers(1, 60, size=(n, n)).astype(np.int64)
+    Wi[rng.random((n, n)) < 0.6] = I32_INF
+    np.fill_diagonal(Wi, 0)
+    ref = np.array(_floyd_warshall(Wi, I32_INF))
+    for dtype in ("i32", "f32"):
+        if dtype == "i32":
+            D = Wi.astype(np.int32)
+        else:
+            D = np.where(Wi >= I32_INF, np.inf, Wi).astype(np.float32)
+        for _ in range(4):  # 2^4 >= n - 1 hops
+            Dn, I = orc.gemm("min_plus", D, D)
+            # the argmin is a valid intermediate vertex wherever the path exists
+            for i, j in itertools.product(range(n), range(n)):
+                k = I[0, i, j]
+                fin = Dn[0, i, j] < (I32_INF if dtype == "i32" else np.inf)
+                if fin:
+                    via = (int(D[i, k]) + int(D[k, j])) if dtype == "i32" else D[i, k] + D[k, j]
+                    assert via == Dn[0, i, j], "witness"
+            D = Dn[0]
+        got = np.where(np.isinf(D), I32_INF, D).astype(np.int64) if dtype == "f32" else D
+        _eq(got, ref, f"Floyd-Warshall {dtype}")
+
+
+def pin_semirings_distinct(orc):
+    rng = np.random.default_rng(23)
+    A = (rng.random((4, 6)) + 0.5).astype(np.float32)
+    B = (rng.random((6, 5)) + 0.5).astype(np.float32)
+    outs = [orc.gemm(sr, A, B)[0] for sr in SR]
+    std = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)[None]
+    for a, b in itertools.combinations(outs + [std], 2):
+        assert not np.array_equal(a, b), "two semirings gave the same product"
+
+
+def pin_points(orc):
+    rng = np.random.default_rng(29)
+    A = rng.standard_normal((3, 8, 10)).astype(np.float32)
+    B = rng.standard_normal((3, 10, 7)).astype(np.float32)
+    pts = np.array([[b, i, j] for b in range(3) for i in range(8) for j in range(7)])
+    pts = pts[rng.permutation(len(pts))[:60]]
+    for sr in ("max_plus", "min_plus"):
+        C, I = orc.gemm(sr, A, B)
+        v, a = orc.gemm_points(sr, A, B, pts)
+        _bits_equal(v, C[pts[:, 0], pts[:, 1], pts[:, 2]], f"points {sr}")
+        _eq(a, I[pts[:, 0], pts[:, 1], pts[:, 2]], f"points argmax {sr}")
+    Bc = np.ascontiguousarray(B.transpose(0, 2, 1)).transpose(0, 2, 1)
+    v, a = orc.gemm_points("max_plus", A, Bc, pts)
+    C, I = orc.gemm("max_plus", A, B)
+    _bits_equal(v, C[pts[:, 0], pts[:, 1], pts[:, 2]], "points column-major B")
+
+
+# ----------------------------------------------------------------------
+# permute and diagonal / trace against torch
+# ----------------------------------------------------------------------
+
+def pin_permute(orc):
+    g = torch.Generator().manual_seed(31)
+    for shape in [(3,), (4, 5), (2, 3, 4), (3, 1, 4, 2), (2, 3, 2, 2, 3)]:
+        x = torch.randn(shape, generator=g)
+        for p in itertools.permutations(range(len(shape))):
+            out = orc.permute(x.numpy(), p)
+            _bits_equal(out, x.permute(*p).contiguous().numpy(), f"permute {shape} {p}")
+            inv = [p.index(d) for d in range(len(p))]
+            _bits_equal(orc.permute(out, inv), x.numpy(), f"inverse {shape} {p}")
+    xi = torch.randint(-9, 9, (3, 4, 5), generator=g, dtype=torch.int32)
+    _eq(orc.permute(xi.numpy(), (2, 0, 1)), xi.permute(2, 0, 1).contiguous().numpy(), "permute i32")
+    # strided input view
+    base = torch.randn(6, 8, generator=g)
+    view = base.numpy()[::2, 1::3]
+    _bits_equal(orc.permute(view, (1, 0)), np.ascontiguousarray(view.T), "strided view")
+
+
+def pin_diag(orc):
+    g = torch.Generator().manual_seed(37)
+    A = torch.randn(4, 4, 3, 2, generator=g)
+    _bits_equal(orc.diag_gather("max_plus", A.numpy(), "iijb", "bij"),
+                torch.einsum("iijb->bij", A).contiguous().numpy(), "iijb->bij")
+    _bits_equal(orc.diag_gather("max_plus", A.numpy(), "iijb", "ijb"),
+                torch.diagonal(A, dim1=0, dim2=1).permute(2, 0, 1).contiguous().numpy(),
+                "iijb->ijb")
+    T = torch.randn(3, 5, 3, 3, generator=g)
+    _bits_equal(orc.diag_gather("max_plus", T.numpy(), "iaii", "ai"),
+                torch.stack([T[i, :, i, i] for i in range(3)], dim=1).numpy(), "iaii->ai")
+    # trace: the repeated label is reduced with the semiring's (+)
+    M = torch.randn(5, 5, 4, generator=g)
+    d = torch.diagonal(M, dim1=0, dim2=1)  # (4, 5)
+    _bits_equal(orc.diag_gather("max_plus", M.numpy(), "iij", "j"), d.amax(dim=1).numpy(),
+                "trace max")
+    _bits_equal(orc.diag_gather("min_plus", M.numpy(), "iij", "j"), d.amin(dim=1).numpy(),
+                "trace min")
+    # reduce of a plain (non-repeated) label
+    _bits_equal(orc.diag_gather("max_plus", M.numpy(), "abj", "ja"),
+                M.amax(dim=1).t().contiguous().numpy(), "reduce b")
+    Mi = torch.randint(-100, 100, (4, 4, 6), generator=g, dtype=torch.int32)
+    _eq(orc.diag_gather("min_plus", Mi.numpy(), "iij", "j"),
+        torch.diagonal(Mi, dim1=0, dim2=1).amin(dim=1).numpy(), "trace i32")
+    _eq(orc.diag_gather("max_plus", Mi.numpy(), "iij", "ji"),
+        torch.diagonal(Mi, dim1=0, dim2=1).numpy(), "diag i32")
+
+
+# ----------------------------------------------------------------------
+# contraction: decomposed path vs brute force, brute force vs torch
+# ----------------------------------------------------------------------
+
+def pin_brute_vs_torch(orc):
+    rng = np.random.default_rng(41)
+    A = rng.integers(-4, 5, size=(3, 6, 5)).astype(np.float32)
+    B = rng.integers(-4, 5, size=(3, 5, 4)).astype(np.float32)
+    for sr in ("max_plus", "min_plus"):
+        C, I = orc.einsum_brute(sr, "bik,bkj->bij", A, B)
+        Cr, Ir = torch_tropical(sr, A, B)
+        _bits_equal(C, Cr, f"brute vs torch {sr}")
+        _eq(I, Ir, f"brute vs torch argmax {sr}")
+
+
+CONTRACT_SPECS = [
+    ("iijb,kjb->bki", [(3, 3, 4, 2), (5, 4, 2)]),
+    ("ij,jk->ik", [(4, 6), (6, 3)]),
+    ("ij,jk->ki", [(4, 6), (6, 3)]),
+    ("bij,bjk->bki", [(2, 3, 5), (2, 5, 4)]),
+    ("abcd,cdbe->ea", [(2, 3, 4, 2), (4, 2, 3, 3)]),
+    ("ijk,jl->lik", [(3, 4, 2), (4, 5)]),
+    ("ij,jj->ij", [(3, 4), (4, 4)]),
+    ("ab,ab->ab", [(3, 4), (3, 4)]),
+    ("ab,cd->abcd", [(2, 3), (2, 2)]),
+    ("kjb,iijb->bik", [(5, 4, 2), (3, 3, 4, 2)]),
+]
+
+
+def pin_contract_vs_brute(orc):
+    rng = np.random.default_rng(43)
+    for spec, (sa, sb) in CONTRACT_SPECS:
+        A = rng.integers(-3, 4, size=sa).astype(np.float32)
+        B = rng.integers(-3, 4, size=sb).astype(np.float32)
+        for sr in SR:
+            if sr == "max_mul":
+                A2, B2 = np.abs(A) * 0.5 + 0.25, np.abs(B) * 0.5 + 0.25
+            else:
+                A2, B2 = A, B
+            lhs = spec.split("->")[0].split(",")
+            out = spec.split("->")[1]
+            contracted = [c for c in dict.fromkeys(lhs[0]) if c in lhs[1] and c not in out]
+            C, I = orc.contract_pair(spec, sr, A2, B2)
+            Cb, Ib = orc.einsum_brute(sr, spec, A2, B2, sum_order=contracted)
+            _bits_equal(C, Cb, f"contract {spec} {sr}")
+            _eq(I, Ib, f"contract {spec} {sr} argmax")
+    # a label in one operand only is reduced in the pre-pass (values only)
+    A = rng.integers(-3, 4, size=(3, 3, 4)).astype(np.float32)
+    B = rng.integers(-3, 4, size=(4, 2, 5)).astype(np.float32)
+    for spec in ("iij,jkl->k", "aij,jkl->ik"):
+        for sr in ("max_plus", "min_plus"):
+            C, _ = orc.contract_pair(spec, sr, A, B, argmax=False)
+            Cb, _ = orc.einsum_brute(sr, spec, A, B, argmax=False)
+            _bits_equal(C, Cb, f"contract-with-reduce {spec} {sr}")
+
+
+ALL_PINS = [
+    pin_golden_gemm, pin_golden_special_values, pin_golden_einsum,
+    pin_torch_crosscheck, pin_torch_random_normal, pin_unit_and_zero,
+    pin_empty_and_k0, pin_associativity, pin_transpose_symmetry,
+    pin_floyd_warshall, pin_semirings_distinct, pin_points, pin_permute,
+    pin_diag, pin_brute_vs_torch, pin_contract_vs_brute,
+]

@@ -1,0 +1,88 @@
+"""The oracle's pins have teeth: each planted mistake must fail at least one.
+
+Every mutant is a copy of oracle/tropical_oracle.c with one textual edit
+(a dropped term, a wrong comparison, sign, stride, index or element),
+compiled into a temporary library and run through tests/pins.py.  Nothing
+here touches a GPU.  If an edit's source text is no longer found, the test
+fails so that the list is kept in step with the oracle.
+"""
+import os
+
+import pytest
+
+import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "tropical_oracle.c")
+
+MUTANTS = [
+    ("drop_last_k_f32",
+     "float best = zero_f32(sr);\n        for (int64_t kk = 0; kk < k; ++kk)",
+     "float best = zero_f32(sr);\n        for (int64_t kk = 0; kk < k - 1; ++kk)"),
+    ("drop_last_k_i32",
+     "int32_t best = zero_i32(sr);\n        for (int64_t kk = 0; kk < k; ++kk)",
+     "int32_t best = zero_i32(sr);\n        for (int64_t kk = 0; kk < k - 1; ++kk)"),
+    ("ties_to_last_max_f32",
+     "static int better_f32(int sr, float t, float best)\n{\n    if (sr == ORC_MIN_PLUS) return t < best;\n    return t > best;",
+     "static int better_f32(int sr, float t, float best)\n{\n    if (sr == ORC_MIN_PLUS) return t < best;\n    return t >= best;"),
+    ("ties_to_last_min_i32",
+     "static int better_i32(int sr, int32_t t, int32_t best)\n{\n    if (sr == ORC_MIN_PLUS) return t < best;",
+     "static int better_i32(int sr, int32_t t, int32_t best)\n{\n    if (sr == ORC_MIN_PLUS) return t <= best;"),
+    ("min_plus_uses_max",
+     "static int better_f32(int sr, float t, float best)\n{\n    if (sr == ORC_MIN_PLUS) return t < best;",
+     "static int better_f32(int sr, float t, float best)\n{\n    if (sr == ORC_MIN_PLUS) return t > best;"),
+    ("transposed_A_f32",
+     "float x = a[b * sA[2] + i * sA[0] + kk * sA[1]];",
+     "float x = a[b * sA[2] + i * sA[1] + kk * sA[0]];"),
+    ("transposed_B_i32",
+     "int32_t y = bm[b * sB[2] + kk * sB[0] + j * sB[1]];",
+     "int32_t y = bm[b * sB[2] + kk * sB[1] + j * sB[0]];"),
+    ("batch_stride_ignored",
+     "float y = bm[b * sB[2] + kk * sB[0] + j * sB[1]];",
+     "float y = bm[kk * sB[0] + j * sB[1]];"),
+    ("plus_is_minus", "    return a + b;\n}", "    return a - b;\n}"),
+    ("max_mul_adds", "if (sr == ORC_MAX_MUL) return a * b;", "if (sr == ORC_MAX_MUL) return a + b;"),
+    ("wrapping_i32", "    if (s > INT32_MAX) return INT32_MAX;\n", ""),
+    ("max_plus_zero_finite", "if (sr == ORC_MAX_PLUS) return -INFINITY;",
+     "if (sr == ORC_MAX_PLUS) return -1e30f;"),
+    ("min_plus_zero_i32_off", "return sr == ORC_MIN_PLUS ? ORC_I32_INF : -ORC_I32_INF;",
+     "return sr == ORC_MIN_PLUS ? ORC_I32_INF - 1 : -ORC_I32_INF;"),
+    ("argmax_off_by_one",
+     "best = t;\n                arg = (int32_t)kk;\n            }\n        }\n        *(float*)cval = best;",
+     "best = t;\n                arg = (int32_t)kk + 1;\n            }\n        }\n        *(float*)cval = best;"),
+    ("permute_unpermuted_strides", "off += digit * in_strides[perm[d]];", "off += digit * in_strides[d];"),
+    ("permute_column_major_decode",
+     "        for (int d = ndim - 1; d >= 0; --d) {\n            int64_t digit = rem % out_shape[d];",
+     "        for (int d = 0; d < ndim; ++d) {\n            int64_t digit = rem % out_shape[d];"),
+    ("diag_stride_not_summed", "str[found] += in_strides[a];", "str[found] = in_strides[a];"),
+    ("trace_last_wins", "if (better_f32(sr, t, best)) best = t;", "best = t;"),
+    ("brute_argmax_shifted", "bestf = t;\n                    arg = (int32_t)p;",
+     "bestf = t;\n                    arg = (int32_t)(p > 0 ? p - 1 : 0);"),
+    ("points_swap_ij",
+     "pts[3 * p], pts[3 * p + 1], pts[3 * p + 2]", "pts[3 * p], pts[3 * p + 2], pts[3 * p + 1]"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, find, repl):
+    import oracle
+    from oracle import build as obuild
+    assert source.count(find) >= 1, f"mutation {name}: source text not found"
+    mutated = source.replace(find, repl, 1)
+    src = tmp_path / f"{name}.c"
+    src.write_text(mutated)
+    lib = obuild.build(str(src), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, oracle.OracleError, ValueError, IndexError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"mutant {name} passed every pin"
