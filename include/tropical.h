@@ -1,0 +1,244 @@
+/*
+ * tropical.h -- C ABI of libtropical.so, the MI355X (gfx950) tropical
+ * contraction hot path.
+ *
+ * Four operations, all device-resident and enqueued on a caller stream:
+ *   tropical_gemm_strided_batched  batched tropical matrix product + argmax
+ *   tropical_permute               N-d permute of one or two 4-byte tensors
+ *   tropical_diag_gather           repeated-label diagonal / trace pre-pass
+ *   tropical_contract_pair         one pairwise einsum built from the three
+ *
+ * Sources (web pages the method is taken from):
+ *   [PR35]  tropical-gemm PR #35 "feat: batched GPU ops with DLPack zero-copy
+ *           output" -- Summary / Key changes (batched max-plus, min-plus,
+ *           max-mul f32 kernels with argmax, batch on the third grid axis,
+ *           per-device context cache; reject host memory, guard zero-sized
+ *           dims, validate same-device tensors).
+ *   [I52]   omeinsum-rs issue #52 "GPU tropical path: keep tensors
+ *           device-resident + device-side permute" -- "Resolved design for
+ *           step 3" kernels (a) permute and (b) diagonal/trace gather;
+ *           "Structural lessons from OMEinsum" (unary pre-pass, then permute,
+ *           batched GEMM, output permute); "Acceptance criteria"
+ *           (intermediates stay in device memory, context and module created
+ *           once, value and argmax permuted with one identical mapping).
+ *
+ * Conventions for every entry point
+ *   - Element strides and sizes are counted in ELEMENTS, not bytes.
+ *   - Every data pointer must be device memory of the current HIP device
+ *     (hipMalloc / PyTorch's allocator).  Host or pinned-host pointers are
+ *     rejected with TROP_ERR_NOT_DEVICE_MEMORY, pointers of another device
+ *     with TROP_ERR_INVALID_ARGUMENT.
+ *   - Ownership: the caller owns every buffer, including the workspace.
+ *     The library allocates no device memory, keeps no pointer after the
+ *     call returns and copies shape / stride arrays into kernel arguments.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream) and the call returns without synchronising
+ *     the host.  Argument errors are returned synchronously and then
+ *     nothing is enqueued.  A fault inside a kernel surfaces at the
+ *     caller's next synchronisation, as for any HIP launch.
+ *   - Errors: a trop_status code; tropical_last_error() returns a
+ *     thread-local text for the last failing call of the calling thread.
+ *   - Thread safety: per-device module loading is guarded; calls are
+ *     otherwise stateless and may be issued from several threads.
+ *   - An output with zero elements makes any call a no-op returning
+ *     TROP_OK before any pointer is inspected.
+ */
+#ifndef TROPICAL_H
+#define TROPICAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define TROP_API __attribute__((visibility("default")))
+#else
+#define TROP_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TROP_OK = 0,
+    TROP_ERR_INVALID_ARGUMENT = 1,
+    TROP_ERR_UNSUPPORTED = 2,
+    TROP_ERR_NOT_DEVICE_MEMORY = 3,
+    TROP_ERR_WORKSPACE_TOO_SMALL = 4,
+    TROP_ERR_HIP = 5
+} trop_status;
+
+/*
+ * The three semirings of [PR35].  The pages name them without writing the
+ * operations out; the standard tropical algebra is used:
+ *   TROP_MAX_PLUS  (+) = max, (x) = +, zero = -inf (int32: -2^30)
+ *   TROP_MIN_PLUS  (+) = min, (x) = +, zero = +inf (int32: +2^30)
+ *   TROP_MAX_MUL   (+) = max, (x) = *, zero = +0   (float32 only)
+ * float32 (x) is one IEEE-754 add / multiply, round to nearest even,
+ * denormals kept.  int32 (x) is a saturating 32-bit add.
+ */
+typedef enum { TROP_MAX_PLUS = 0, TROP_MIN_PLUS = 1, TROP_MAX_MUL = 2 } trop_semiring;
+typedef enum { TROP_F32 = 0, TROP_I32 = 1 } trop_dtype;
+
+/* Strides of a batched matrix X[b][r][c] = base[b*batch + r*row + c*col]. */
+typedef struct {
+    int64_t row, col, batch;
+} trop_strides;
+
+/* Kernel families counted by trop_stats.launches[]. */
+typedef enum {
+    TROP_K_GEMM_TILED = 0,   /* LDS-tiled GEMM with chunked argmax      */
+    TROP_K_GEMM_SIMPLE = 1,  /* one-thread-per-output exact GEMM         */
+    TROP_K_FILL = 2,         /* K = 0: C = zero, argmax = 0              */
+    TROP_K_GATHER_COPY = 3,  /* permute/gather keeping the inner axis    */
+    TROP_K_GATHER_TILED = 4, /* permute/gather through an LDS tile       */
+    TROP_K_GATHER_NAIVE = 5, /* permute/gather, one thread per element   */
+    TROP_K_GATHER_REDUCE = 6,/* gather with a (+)-reduction (trace)      */
+    TROP_K_FAMILIES = 8
+} trop_kernel_family;
+
+typedef struct {
+    uint64_t module_loads;             /* hipModuleLoadData calls, all devices  */
+    uint64_t launches_total;           /* kernels enqueued                      */
+    uint64_t launches[TROP_K_FAMILIES];/* per trop_kernel_family                */
+    uint64_t host_syncs;               /* host-blocking syncs issued: always 0  */
+    uint64_t memcpy_calls;             /* host<->device copies issued: always 0 */
+} trop_stats;
+
+/*
+ * Load the kernel code object on `device` (once per process and device,
+ * [I52] "Compilation & caching"; [PR35] per-device context cache).  Optional:
+ * every other call loads lazily on the current device.  Idempotent.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (no such device), TROP_ERR_HIP (load
+ * failed; nothing is cached, a later call retries).
+ */
+TROP_API trop_status tropical_init(int device);
+
+/*
+ * Strided-batched tropical GEMM with argmax ([PR35] batched kernels; [I52]
+ * "Proposed plan" step 2):
+ *   C[b][i][j] = (+)_{k<K} A[b][i][k] (x) B[b][k][j]
+ *   argmax[b][i][j] = the smallest k whose term is the result
+ * for b < batch, i < m, j < n.  The scan starts from the zero element and
+ * only a strictly better term replaces the running best, so ties go to the
+ * smaller k, a NaN term never wins, and a result that nothing beat is the
+ * zero element with argmax 0 (C then holds the zero element's bits;
+ * otherwise C holds the bits of the winning term, so signed zeros are kept).
+ *
+ * A, B, C: device pointers of `dtype` elements (float32 or int32).
+ * sA, sB, sC: element strides; any non-negative values (A[b][i][k] at
+ *   b*sA.batch + i*sA.row + k*sA.col, B[b][k][j] likewise with row = k,
+ *   col = j).  Row-major and column-major A and B take the fast path.
+ * argmax: device int32 pointer with the strides sC, or NULL (not written).
+ * m, n, k, batch >= 0; k < 2^31.  k == 0 writes C = zero, argmax = 0.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, negative size or stride),
+ *   TROP_ERR_UNSUPPORTED (int32 max-mul), TROP_ERR_NOT_DEVICE_MEMORY,
+ *   TROP_ERR_HIP (launch failure).
+ */
+TROP_API trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_dtype dtype,
+                                          const void* A, trop_strides sA,
+                                          const void* B, trop_strides sB,
+                                          void* C, trop_strides sC, int32_t* argmax,
+                                          int64_t m, int64_t n, int64_t k, int64_t batch,
+                                          void* stream);
+
+/*
+ * N-d permute ([I52] "Resolved design for step 3", kernel (a)):
+ *   out[o_0..o_{d-1}] = in[sum_d o_d * in_strides[perm[d]]]
+ * with out contiguous row-major of shape shape[perm[0]], ..., shape[perm[d-1]].
+ * ntensors = 1 or 2: with 2, in[1] -> out[1] is moved with the identical
+ * mapping in the same launch (value and argmax, [I52] "Acceptance criteria").
+ * elem_bytes must be 4 (float32 / int32); ndim <= 8; perm a permutation of
+ * 0..ndim-1; shape >= 0; in_strides >= 0.  in and out must not overlap.
+ * Errors: TROP_ERR_INVALID_ARGUMENT, TROP_ERR_UNSUPPORTED (elem_bytes != 4),
+ *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ */
+TROP_API trop_status tropical_permute(size_t elem_bytes, int ndim, const int64_t* shape,
+                             const int64_t* in_strides, const int32_t* perm,
+                             int ntensors, const void* const* in, void* const* out,
+                             void* stream);
+
+/*
+ * Repeated-label diagonal / trace gather ([I52] "Resolved design for step
+ * 3", kernel (b): the unary pre-pass with the tropical max / min fused in).
+ * Input axis a carries label in_labels[a] (any int32 ids).  Axes that share
+ * a label are walked with one index (their extents must agree; their strides
+ * add).  out is contiguous row-major over out_labels (distinct, each present
+ * in the input).  Input labels absent from out_labels are reduced with the
+ * semiring's (+), from its zero element with the strict "better" test, in
+ * row-major order over those labels; without such labels the semiring is
+ * ignored and the call is a pure 4-byte gather.
+ * in_ndim, out_ndim <= 8.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (extent mismatch, unknown or repeated
+ *   output label), TROP_ERR_UNSUPPORTED (int32 max-mul with a reduction),
+ *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ */
+TROP_API trop_status tropical_diag_gather(trop_semiring semiring, trop_dtype dtype,
+                                 int in_ndim, const int64_t* in_shape,
+                                 const int64_t* in_strides, const int32_t* in_labels,
+                                 int out_ndim, const int32_t* out_labels,
+                                 const void* in, void* out, void* stream);
+
+/*
+ * Workspace (bytes) that tropical_contract_pair needs for `spec` with these
+ * operand shapes.  Host-only, touches no device.  Errors as for
+ * tropical_contract_pair's argument checks.
+ */
+TROP_API trop_status tropical_contract_pair_workspace_size(const char* spec, const int64_t* shapeA,
+                                                  const int64_t* shapeB, size_t* bytes);
+
+/*
+ * One pairwise tropical einsum, all on `stream` with no host round trip
+ * ([I52] "Structural lessons from OMEinsum" and "Acceptance criteria"):
+ *   1. diagonal / trace pre-pass and permute of A into (batch, left,
+ *      contracted) and of B into (batch, contracted, right);
+ *   2. one strided-batched tropical GEMM with argmax;
+ *   3. one paired permute of value and argmax into the output order.
+ * An operand already in canonical contiguous order is used in place.
+ * spec: "lhs,rhs->out" with single-letter labels a-z A-Z, explicit output,
+ *   no ellipsis; every output label appears in an operand, output labels
+ *   are distinct.  batch labels are in A, B and out; left in A and out;
+ *   right in B and out; contracted in A and B only.  A label found in one
+ *   operand only and absent from the output is (+)-reduced in the pre-pass.
+ * A, B: device pointers, shapes and element strides (rank = subscript
+ *   length, <= 8).  C: contiguous row-major over the output labels.
+ * argmax: NULL or a contiguous int32 tensor shaped like C; it holds the
+ *   row-major linear index over the contracted labels taken in A-subscript
+ *   order.  Requesting it when a pre-pass reduction exists is
+ *   TROP_ERR_UNSUPPORTED.
+ * workspace: device memory of at least tropical_contract_pair_workspace_size
+ *   bytes (may be NULL when that size is 0), used only by work on `stream`.
+ * Errors: TROP_ERR_INVALID_ARGUMENT, TROP_ERR_UNSUPPORTED,
+ *   TROP_ERR_WORKSPACE_TOO_SMALL, TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ */
+TROP_API trop_status tropical_contract_pair(const char* spec, trop_semiring semiring, trop_dtype dtype,
+                                   const void* A, const int64_t* shapeA, const int64_t* stridesA,
+                                   const void* B, const int64_t* shapeB, const int64_t* stridesB,
+                                   void* C, int32_t* argmax,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-only: write a one-line text description of the plan that
+ * tropical_contract_pair would enqueue (label roles, GEMM sizes, which
+ * pre-passes and which kernel paths) into buf (NUL-terminated, truncated to
+ * buflen).  Touches no device.
+ */
+TROP_API trop_status tropical_contract_pair_describe(const char* spec,
+                                            const int64_t* shapeA, const int64_t* stridesA,
+                                            const int64_t* shapeB, const int64_t* stridesB,
+                                            char* buf, size_t buflen);
+
+/* Text of the calling thread's last error ("" if none). */
+TROP_API const char* tropical_last_error(void);
+
+/* Copy the process-wide counters. */
+TROP_API trop_status tropical_get_stats(trop_stats* out);
+
+/* Zero the launch counters (module_loads is kept). */
+TROP_API void tropical_reset_stats(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TROPICAL_H */

@@ -1,0 +1,162 @@
+"""The C-ABI library on the CPU: it loads, exports what include/tropical.h
+declares, and its host-only logic (argument checks, spec parsing, planning,
+workspace sizing) behaves as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tropical.h")
+
+
+@pytest.fixture(scope="module")
+def tb():
+    from tropical_semiring_tensor_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from tropical_semiring_tensor_amd.csrc import build
+        build.build()
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"TROP_API\s+[\w\s\*]+?\b(tropical_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    fns = declared_functions()
+    for f in ("tropical_gemm_strided_batched", "tropical_permute", "tropical_diag_gather",
+              "tropical_contract_pair"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(tb):
+    fns = declared_functions()
+    assert len(fns) >= 10
+    for f in fns:
+        assert hasattr(tb.lib(), f), f
+    out = subprocess.run(["nm", "-D", "--defined-only", tb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(fns) == exported, f"exported {sorted(exported)} vs declared {fns}"
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "tropical.h"\nint main(void){trop_strides s={1,2,3};'
+                   'return (int)sizeof(s) + (int)TROP_OK;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c",
+                    str(src), "-o", str(tmp_path / "use.o")], check=True)
+
+
+def test_code_object_is_gfx950_only():
+    from tropical_semiring_tensor_amd.csrc import build
+    co = os.path.join(build.BUILD, "tropical_kernels.co")
+    if not os.path.exists(co):
+        build.build()
+    data = open(co, "rb").read()
+    assert data[:4] == b"\x7fELF"
+    assert b"gfx950" in data
+    for other in (b"gfx90a", b"gfx942", b"gfx1100"):
+        assert other not in data
+
+
+def _status(tb, fn, *args):
+    return getattr(tb.lib(), fn)(*args)
+
+
+def test_gemm_argument_errors_before_any_device_call(tb):
+    L = tb.lib()
+    s = tb.trop_strides(1, 1, 1)
+    nul = ctypes.c_void_p(0)
+    # unknown semiring / dtype, int32 max-mul, negative sizes and strides
+    assert L.tropical_gemm_strided_batched(7, 0, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
+    assert "semiring" in tb.tropical_last_error()
+    assert L.tropical_gemm_strided_batched(0, 9, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
+    assert L.tropical_gemm_strided_batched(2, 1, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.UNSUPPORTED
+    assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, -1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
+    neg = tb.trop_strides(-1, 1, 1)
+    assert L.tropical_gemm_strided_batched(0, 0, nul, neg, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
+    assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, 1, 1, 2 ** 31, 1, nul) == tb.INVALID_ARGUMENT
+    # an empty output is a no-op before any pointer is looked at
+    assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, 0, 5, 5, 3, nul) == tb.OK
+    assert L.tropical_gemm_strided_batched(1, 1, nul, s, nul, s, nul, s, nul, 4, 4, 4, 0, nul) == tb.OK
+    assert tb.tropical_last_error() == ""
+
+
+def test_permute_argument_errors(tb):
+    L = tb.lib()
+    shape = tb._i64([2, 3])
+    strides = tb._i64([3, 1])
+    arr = (ctypes.c_void_p * 2)(0, 0)
+    assert L.tropical_permute(4, 2, shape, strides, tb._i32([0, 0]), 1, arr, arr, None) == tb.INVALID_ARGUMENT
+    assert "permutation" in tb.tropical_last_error()
+    assert L.tropical_permute(4, 2, shape, strides, tb._i32([1, 2]), 1, arr, arr, None) == tb.INVALID_ARGUMENT
+    assert L.tropical_permute(4, 2, shape, strides, tb._i32([1, 0]), 3, arr, arr, None) == tb.INVALID_ARGUMENT
+    assert L.tropical_permute(8, 2, shape, strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.UNSUPPORTED
+    assert L.tropical_permute(4, 9, shape, strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.INVALID_ARGUMENT
+    # zero-size output: no-op
+    assert L.tropical_permute(4, 2, tb._i64([0, 3]), strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.OK
+
+
+def test_diag_argument_errors(tb):
+    L = tb.lib()
+    nul = ctypes.c_void_p(0)
+    # repeated label with mismatched extents
+    st = L.tropical_diag_gather(0, 0, 2, tb._i64([3, 4]), tb._i64([4, 1]), tb._i32([1, 1]), 1,
+                                tb._i32([1]), nul, nul, None)
+    assert st == tb.INVALID_ARGUMENT and "extent" in tb.tropical_last_error()
+    # output label missing from the input, or repeated in the output
+    assert L.tropical_diag_gather(0, 0, 2, tb._i64([3, 3]), tb._i64([3, 1]), tb._i32([1, 1]), 1,
+                                  tb._i32([2]), nul, nul, None) == tb.INVALID_ARGUMENT
+    assert L.tropical_diag_gather(0, 0, 2, tb._i64([3, 4]), tb._i64([4, 1]), tb._i32([1, 2]), 2,
+                                  tb._i32([1, 1]), nul, nul, None) == tb.INVALID_ARGUMENT
+    # int32 max-mul with a reduction
+    assert L.tropical_diag_gather(2, 1, 2, tb._i64([3, 3]), tb._i64([3, 1]), tb._i32([1, 1]), 0,
+                                  tb._i32([]), nul, nul, None) == tb.UNSUPPORTED
+
+
+def test_contract_plan_config5(tb):
+    d = tb.tropical_contract_pair_describe("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
+    assert "batch=b left=i right=k contracted=j" in d
+    assert "gemm batch=32 m=128 n=256 k=256" in d
+    assert "A=gather:tiled" in d and "B=gather:tiled" in d and "out=permute:tiled" in d
+    ws = tb.tropical_contract_pair_workspace_size("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
+    assert ws == 4 * (32 * 128 * 256 + 32 * 256 * 256 + 2 * 32 * 128 * 256)
+
+
+def test_contract_plan_folds_canonical_operands(tb):
+    d = tb.tropical_contract_pair_describe("bij,bjk->bik", (4, 5, 6), (4, 6, 7))
+    assert "A=fold" in d and "B=fold" in d and "out=direct" in d and "workspace=0" in d
+    # a column-major B (k unit-stride) is read in place too
+    d = tb.tropical_contract_pair_describe("bij,bjk->bik", (4, 5, 6), (4, 6, 7), (30, 6, 1), (42, 1, 6))
+    assert "B=fold" in d
+    # a label reduced in the pre-pass forces the gather
+    d = tb.tropical_contract_pair_describe("aij,jk->ik", (3, 4, 5), (5, 6))
+    assert "reduceA=a" in d and "A=gather:reduce" in d
+
+
+@pytest.mark.parametrize("spec,err", [
+    ("ij,jk", tb_err := "INVALID"), ("ij->i", "INVALID"), ("ij,jk->iq", "INVALID"),
+    ("i1,jk->ik", "INVALID"), ("ij,jk->ii", "INVALID"), ("ij,j,k->ik", "INVALID"),
+])
+def test_contract_spec_errors(tb, spec, err):
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_contract_pair_describe(spec, (2, 3), (3, 4))
+    assert e.value.status == tb.INVALID_ARGUMENT
+
+
+def test_contract_extent_mismatch(tb):
+    with pytest.raises(tb.TropicalError):
+        tb.tropical_contract_pair_describe("ij,jk->ik", (2, 3), (4, 5))
+
+
+def test_stats_start_clean(tb):
+    s = tb.tropical_get_stats()
+    assert s["host_syncs"] == 0 and s["memcpy_calls"] == 0
+    assert set(s["launches"]) == set(tb.KERNEL_FAMILIES)

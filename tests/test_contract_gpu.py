@@ -1,0 +1,130 @@
+"""Parity of tropical_contract_pair with the oracle's decomposed pipeline
+(bit-exact values and argmax), the full workload-5 einsum, and the
+device-residency counters (no host syncs, no copies, one module load)."""
+import numpy as np
+import pytest
+import torch
+
+import golden_io as gio
+from gpu_util import DEV, assert_bits_equal, assert_equal, device_copy
+from tropical_semiring_tensor_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SPECS = [
+    ("iijb,kjb->bki", [(9, 9, 40, 3), (70, 40, 3)]),
+    ("ij,jk->ik", [(70, 130), (130, 66)]),
+    ("ij,jk->ki", [(70, 130), (130, 66)]),
+    ("bij,bjk->bki", [(3, 65, 90), (3, 90, 70)]),
+    ("abcd,cdbe->ea", [(5, 3, 20, 4), (20, 4, 3, 33)]),
+    ("ijk,jl->lik", [(13, 40, 6), (40, 70)]),
+    ("ij,jj->ij", [(30, 44), (44, 44)]),
+    ("ab,ab->ab", [(30, 40), (30, 40)]),
+    ("ab,cd->abcd", [(7, 9), (6, 5)]),
+    ("kjb,iijb->bik", [(70, 40, 3), (9, 9, 40, 3)]),
+    ("bij,bjk->bik", [(4, 70, 300), (4, 300, 66)]),
+]
+
+
+@pytest.fixture(scope="module")
+def tb():
+    from tropical_semiring_tensor_amd import binding
+    binding.tropical_init(0)
+    return binding
+
+
+def operands(sr, sa, sb, seed):
+    g = torch.Generator().manual_seed(seed)
+    if sr == "max_mul":
+        return (torch.randint(1, 9, sa, generator=g).float() * 0.125,
+                torch.randint(1, 9, sb, generator=g).float() * 0.25)
+    return (torch.randint(-6, 7, sa, generator=g).float(), torch.randint(-6, 7, sb, generator=g).float())
+
+
+@pytest.mark.parametrize("sr", ["max_plus", "min_plus", "max_mul"])
+@pytest.mark.parametrize("spec,shapes", SPECS, ids=[s for s, _ in SPECS])
+def test_specs(tb, orc, sr, spec, shapes):
+    A, B = operands(sr, shapes[0], shapes[1], seed=len(spec))
+    C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr}")
+    assert_equal(I.cpu().numpy(), Ir, f"{spec} {sr} argmax")
+
+
+def test_int32_and_strided_operands(tb, orc):
+    g = torch.Generator().manual_seed(8)
+    A = torch.randint(0, 100, (9, 9, 40, 3), generator=g, dtype=torch.int32)
+    Bbig = torch.randint(0, 100, (70, 50, 3), generator=g, dtype=torch.int32)
+    B = Bbig[:, 5:45, :]  # non-contiguous operand
+    for sr in ("min_plus", "max_plus"):
+        C, I = tb.tropical_contract_pair("iijb,kjb->bki", sr, A.to(DEV), device_copy(B))
+        torch.cuda.synchronize()
+        Cr, Ir = orc.contract_pair("iijb,kjb->bki", sr, A.numpy(), B.numpy())
+        assert_equal(C.cpu().numpy(), Cr, f"i32 {sr}")
+        assert_equal(I.cpu().numpy(), Ir, f"i32 {sr} argmax")
+    # a column-major operand that is read in place
+    Ac = torch.randint(0, 100, (4, 60, 50), generator=g, dtype=torch.int32)
+    Bc = torch.randint(0, 100, (4, 70, 50), generator=g, dtype=torch.int32).transpose(1, 2)
+    d = tb.tropical_contract_pair_describe("bij,bjk->bik", Ac.shape, Bc.shape, Ac.stride(), Bc.stride())
+    assert "B=fold" in d
+    C, I = tb.tropical_contract_pair("bij,bjk->bik", "min_plus", Ac.to(DEV), device_copy(Bc))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair("bij,bjk->bik", "min_plus", Ac.numpy(), Bc.numpy())
+    assert_equal(C.cpu().numpy(), Cr, "folded column-major B")
+    assert_equal(I.cpu().numpy(), Ir, "folded column-major B argmax")
+
+
+def test_pre_pass_reduction_values(tb, orc):
+    g = torch.Generator().manual_seed(9)
+    A = torch.randint(-5, 6, (6, 6, 40), generator=g).float()
+    B = torch.randint(-5, 6, (40, 7, 9), generator=g).float()
+    for spec in ("iij,jkl->k", "aij,jkl->ik"):
+        for sr in ("max_plus", "min_plus"):
+            Ad = A.to(DEV) if spec.startswith("iij") else A[:, :, :].to(DEV)
+            C, I = tb.tropical_contract_pair(spec, sr, Ad, B.to(DEV), argmax=None)
+            torch.cuda.synchronize()
+            assert I is None
+            Cr, _ = orc.contract_pair(spec, sr, A.numpy(), B.numpy(), argmax=False)
+            assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr}")
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_contract_pair("iij,jkl->k", "max_plus", A.to(DEV), B.to(DEV), argmax=True)
+    assert e.value.status == tb.UNSUPPORTED
+
+
+def test_golden_einsum(tb):
+    gdata = gio.load("einsum_iijb_kjb_bki.json")
+    A = np.zeros(gdata["A_shape"], dtype=np.float32)
+    for e in gdata["A_entries"]:
+        A[tuple(e["index"])] = gio.f32(e["value"])
+    B = gio.nested(gdata["B"], "f32")
+    C, I = tb.tropical_contract_pair(gdata["spec"], gdata["semiring"], torch.from_numpy(A).to(DEV),
+                                     torch.from_numpy(B).to(DEV))
+    torch.cuda.synchronize()
+    assert_bits_equal(C.cpu().numpy(), gio.nested(gdata["out"], "f32"), "golden einsum")
+    assert_equal(I.cpu().numpy(), np.array(gdata["argmax"]), "golden einsum argmax")
+
+
+def test_workspace_too_small(tb):
+    A = torch.zeros(4, 4, 5, 2, device=DEV)
+    B = torch.zeros(6, 5, 2, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_contract_pair("iijb,kjb->bki", "max_plus", A, B, workspace=ws)
+    assert e.value.status == tb.WORKSPACE_TOO_SMALL
+
+
+def test_workload5_full(tb, orc):
+    A, B = inputs.einsum_operands()
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    tb.tropical_reset_stats()
+    C, I = tb.tropical_contract_pair("iijb,kjb->bki", "max_plus", Ad, Bd)
+    torch.cuda.synchronize()
+    st = tb.tropical_get_stats()
+    # diag gather, B permute, GEMM, paired output permute: four launches
+    assert st["launches_total"] == 4, st
+    assert st["launches"]["gather_tiled"] == 3 and st["launches"]["gemm_tiled"] == 1, st
+    assert st["host_syncs"] == 0 and st["memcpy_calls"] == 0
+    Cr, Ir = orc.contract_pair("iijb,kjb->bki", "max_plus", A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, "workload 5")
+    assert_equal(I.cpu().numpy(), Ir, "workload 5 argmax")

@@ -1,0 +1,159 @@
+"""Parity of the HIP permute and diagonal / trace gather with the CPU oracle
+(bit-exact), through every kernel path (copy, tiled, naive, reduce)."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, assert_bits_equal, assert_equal, device_copy
+from tropical_semiring_tensor_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tb():
+    from tropical_semiring_tensor_amd import binding
+    binding.tropical_init(0)
+    return binding
+
+
+def launches(tb):
+    return dict(tb.tropical_get_stats()["launches"])
+
+
+def delta(before, after):
+    return {k: after[k] - before[k] for k in after if after[k] != before[k]}
+
+
+SHAPES = [(7,), (5, 9), (64, 64), (65, 130), (3, 1, 70, 2), (2, 3, 4, 5, 6), (33, 2, 65),
+          (4, 1, 1, 9, 2, 3)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_permute_all_perms(tb, orc, shape):
+    g = torch.Generator().manual_seed(len(shape) * 100 + shape[0])
+    x = torch.randn(shape, generator=g)
+    xd = x.to(DEV)
+    perms = list(itertools.permutations(range(len(shape))))
+    if len(perms) > 40:
+        perms = perms[:: len(perms) // 40]
+    for p in perms:
+        out = tb.tropical_permute(xd, p)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), p), f"permute {shape} {p}")
+
+
+def test_permute_paths_and_pairs(tb, orc):
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(6, 70, 130, generator=g)
+    idx = torch.randint(0, 1000, (6, 70, 130), generator=g, dtype=torch.int32)
+    xd, idd = x.to(DEV), idx.to(DEV)
+    cases = {(0, 1, 2): "gather_copy", (1, 0, 2): "gather_copy", (0, 2, 1): "gather_tiled",
+             (2, 1, 0): "gather_tiled"}
+    for p, path in cases.items():
+        before = launches(tb)
+        out, out2 = tb.tropical_permute(xd, p, x2=idd)
+        torch.cuda.synchronize()
+        assert delta(before, launches(tb)) == {path: 1}, (p, delta(before, launches(tb)))
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), p), f"pair value {p}")
+        assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), p), f"pair index {p}")
+
+
+def test_permute_strided_input_and_naive(tb, orc, monkeypatch):
+    g = torch.Generator().manual_seed(4)
+    base = torch.randn(10, 90, 80, generator=g)
+    view = base[1:9:2, 3:80:3, ::2]     # no unit stride: naive path
+    vd = device_copy(view)
+    before = launches(tb)
+    out = tb.tropical_permute(vd, (2, 0, 1))
+    torch.cuda.synchronize()
+    assert delta(before, launches(tb)) == {"gather_naive": 1}
+    assert_bits_equal(out.cpu().numpy(), orc.permute(view.numpy(), (2, 0, 1)), "strided naive")
+    # unaligned copy path
+    v2 = base[:, 1:, 1:]
+    out = tb.tropical_permute(device_copy(v2), (1, 0, 2))
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(v2.numpy(), (1, 0, 2)), "unaligned copy")
+    # the forced naive path gives the same bits
+    x = torch.randn(5, 66, 70, generator=g)
+    monkeypatch.setenv("TROPICAL_FORCE_NAIVE_PERMUTE", "1")
+    before = launches(tb)
+    out = tb.tropical_permute(x.to(DEV), (2, 1, 0))
+    torch.cuda.synchronize()
+    assert delta(before, launches(tb)) == {"gather_naive": 1}
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), (2, 1, 0)), "forced naive")
+
+
+def test_permute_int32_and_scalar(tb, orc):
+    x = torch.arange(2 * 3 * 4, dtype=torch.int32).reshape(2, 3, 4)
+    out = tb.tropical_permute(x.to(DEV), (2, 0, 1))
+    torch.cuda.synchronize()
+    assert_equal(out.cpu().numpy(), orc.permute(x.numpy(), (2, 0, 1)), "int32")
+    s = torch.tensor(3.5)
+    out = tb.tropical_permute(s.to(DEV), ())
+    torch.cuda.synchronize()
+    assert out.item() == 3.5
+
+
+DIAG_CASES = [
+    ("iijb", "bij", (9, 9, 70, 5)),
+    ("iijb", "ijb", (9, 9, 70, 5)),
+    ("iaii", "ai", (6, 70, 6, 6)),
+    ("ijij", "ij", (5, 7, 5, 7)),
+    ("abc", "cab", (20, 30, 70)),
+]
+
+
+@pytest.mark.parametrize("inl,outl,shape", DIAG_CASES)
+def test_diag(tb, orc, inl, outl, shape):
+    g = torch.Generator().manual_seed(sum(shape))
+    x = torch.randn(shape, generator=g)
+    out = tb.tropical_diag_gather("max_plus", x.to(DEV), inl, outl)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.diag_gather("max_plus", x.numpy(), inl, outl),
+                      f"{inl}->{outl}")
+
+
+TRACE_CASES = [("iij", "j", (7, 7, 70)), ("iij", "ji", (7, 7, 9)), ("abj", "ja", (5, 6, 7)),
+               ("iaib", "b", (4, 3, 4, 9)), ("ii", "", (6, 6))]
+
+
+@pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
+                                   ("max_plus", "i32"), ("min_plus", "i32")])
+@pytest.mark.parametrize("inl,outl,shape", TRACE_CASES)
+def test_trace_reduce(tb, orc, sr, dt, inl, outl, shape):
+    g = torch.Generator().manual_seed(len(inl) * 7 + shape[0])
+    if dt == "i32":
+        x = torch.randint(-100, 100, shape, generator=g, dtype=torch.int32)
+    else:
+        x = torch.randint(-4, 5, shape, generator=g).float()
+        x[torch.rand(shape, generator=g) < 0.1] = float("nan")
+        x[torch.rand(shape, generator=g) < 0.1] = -0.0
+    out = tb.tropical_diag_gather(sr, x.to(DEV), inl, outl)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.diag_gather(sr, x.numpy(), inl, outl),
+                      f"{sr} {dt} {inl}->{outl}")
+
+
+def test_workload5_diag_full(tb, orc):
+    A, _ = inputs.einsum_operands()
+    out = tb.tropical_diag_gather("max_plus", A.to(DEV), "iijb", "bij")
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.diag_gather("max_plus", A.numpy(), "iijb", "bij"),
+                      "workload 5 diagonal")
+
+
+def test_workload5_permutes_full(tb, orc):
+    _, B = inputs.einsum_operands(shape_a=(1, 1, 256, 32))
+    out = tb.tropical_permute(B.to(DEV), (2, 1, 0))
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(B.numpy(), (2, 1, 0)), "workload 5 B permute")
+    g = torch.Generator().manual_seed(55)
+    C = torch.randn(32, 128, 256, generator=g)
+    I = torch.randint(0, 256, (32, 128, 256), generator=g, dtype=torch.int32)
+    oc, oi = tb.tropical_permute(C.to(DEV), (0, 2, 1), x2=I.to(DEV))
+    torch.cuda.synchronize()
+    assert_bits_equal(oc.cpu().numpy(), orc.permute(C.numpy(), (0, 2, 1)), "workload 5 C permute")
+    assert_equal(oi.cpu().numpy(), orc.permute(I.numpy(), (0, 2, 1)), "workload 5 argmax permute")

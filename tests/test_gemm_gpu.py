@@ -1,0 +1,255 @@
+"""Parity of the HIP tropical GEMM with the CPU oracle: bit-exact values and
+exact argmax indices (tolerance 0), over semirings, dtypes, layouts, ragged
+sizes, K around the 16-term chunk and 256-term LDS block, special values,
+and the four GEMM workloads at full size."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import golden_io as gio
+from gpu_util import DEV, assert_bits_equal, assert_equal, gpu_gemm
+from tropical_semiring_tensor_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+I32_INF = 1 << 30
+PAIRS = [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
+         ("max_plus", "i32"), ("min_plus", "i32")]
+
+
+@pytest.fixture(scope="module")
+def tb():
+    from tropical_semiring_tensor_amd import binding
+    binding.tropical_init(0)
+    return binding
+
+
+def make(sr, dt, b, m, k, n, seed, ties=True, a_col=False, b_col=False):
+    g = torch.Generator().manual_seed(seed)
+    if dt == "i32":
+        A = torch.randint(-50, 51, (b, m, k), generator=g, dtype=torch.int32)
+        B = torch.randint(-50, 51, (b, k, n), generator=g, dtype=torch.int32)
+        z = I32_INF if sr == "min_plus" else -I32_INF
+        A[torch.rand(A.shape, generator=g) < 0.15] = z
+        B[torch.rand(B.shape, generator=g) < 0.15] = z
+    elif sr == "max_mul":
+        if ties:
+            A = torch.randint(0, 9, (b, m, k), generator=g).float() * 0.125
+            B = torch.randint(0, 9, (b, k, n), generator=g).float() * 0.25
+        else:
+            A = torch.rand(b, m, k, generator=g)
+            B = torch.rand(b, k, n, generator=g)
+    else:
+        if ties:
+            A = torch.randint(-8, 9, (b, m, k), generator=g).float()
+            B = torch.randint(-8, 9, (b, k, n), generator=g).float()
+        else:
+            A = torch.randn(b, m, k, generator=g)
+            B = torch.randn(b, k, n, generator=g)
+    if a_col:
+        A = A.transpose(1, 2).contiguous().transpose(1, 2)
+    if b_col:
+        B = B.transpose(1, 2).contiguous().transpose(1, 2)
+    return A, B
+
+
+def check(tb, orc, sr, A, B, what, c_layout="row", argmax=True):
+    C, I = gpu_gemm(tb, sr, A, B, argmax=argmax, c_layout=c_layout)
+    Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy(), argmax=argmax)
+    assert_bits_equal(C, Cr, what + " C")
+    if argmax:
+        assert_equal(I, Ir, what + " argmax")
+
+
+SHAPES = [(1, 1, 1, 1), (2, 3, 7, 5), (1, 64, 64, 64), (3, 65, 17, 63), (1, 130, 33, 70),
+          (2, 127, 255, 129), (1, 70, 300, 90), (1, 33, 600, 40), (1, 17, 513, 200)]
+
+
+@pytest.mark.parametrize("sr,dt", PAIRS)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_row_major(tb, orc, sr, dt, shape):
+    b, m, k, n = shape
+    A, B = make(sr, dt, b, m, k, n, seed=zlib.crc32(repr((sr, dt, shape)).encode()) % 10000)
+    check(tb, orc, sr, A, B, f"{sr} {dt} {shape}")
+
+
+@pytest.mark.parametrize("sr,dt", PAIRS)
+@pytest.mark.parametrize("a_col,b_col", [(False, True), (True, False), (True, True)])
+def test_layouts(tb, orc, sr, dt, a_col, b_col):
+    A, B = make(sr, dt, 2, 97, 300, 75, seed=11, a_col=a_col, b_col=b_col)
+    check(tb, orc, sr, A, B, f"{sr} {dt} a_col={a_col} b_col={b_col}")
+
+
+@pytest.mark.parametrize("k", [1, 2, 15, 16, 17, 31, 32, 255, 256, 257, 511, 512, 513, 1000])
+def test_k_around_chunk_and_block(tb, orc, k):
+    for sr in ("max_plus", "min_plus"):
+        A, B = make(sr, "f32", 1, 40, k, 72, seed=k, ties=True)
+        check(tb, orc, sr, A, B, f"{sr} k={k} ties")
+        A, B = make(sr, "f32", 1, 40, k, 72, seed=k + 1, ties=False)
+        check(tb, orc, sr, A, B, f"{sr} k={k} normal")
+
+
+def test_increasing_terms_resolve_every_block(tb, orc):
+    # every later term is larger: the best improves in every chunk of every block
+    k = 800
+    A = torch.arange(k, dtype=torch.float32).repeat(1, 70, 1) * 0.5
+    B = torch.arange(k, dtype=torch.float32)[:, None].repeat(1, 1, 66) * 0.25
+    A = A + torch.arange(70, dtype=torch.float32)[None, :, None]
+    check(tb, orc, "max_plus", A, B, "increasing max-plus")
+    check(tb, orc, "min_plus", -A, -B, "decreasing min-plus")
+
+
+def test_all_ties(tb, orc):
+    A = torch.zeros(2, 66, 300)
+    B = torch.zeros(2, 300, 67)
+    check(tb, orc, "max_plus", A, B, "all zero ties")
+    check(tb, orc, "max_mul", A + 1, B + 1, "all one ties")
+
+
+def special_matrix(shape, g, kinds):
+    base = torch.randint(-4, 5, shape, generator=g).float()
+    r = torch.rand(shape, generator=g)
+    vals = {"inf": float("inf"), "-inf": float("-inf"), "nan": float("nan"), "-0": -0.0, "0": 0.0,
+            "den": 1e-45, "-den": -3e-45}
+    edges = np.linspace(0, 0.5, len(kinds) + 1)
+    for i, kind in enumerate(kinds):
+        base[(r >= edges[i]) & (r < edges[i + 1])] = vals[kind]
+    return base
+
+
+@pytest.mark.parametrize("sr", ["max_plus", "min_plus", "max_mul"])
+def test_special_values(tb, orc, sr):
+    g = torch.Generator().manual_seed(5)
+    kinds = ["inf", "-inf", "nan", "-0", "0", "den", "-den"]
+    A = special_matrix((2, 70, 290), g, kinds)
+    B = special_matrix((2, 290, 68), g, kinds)
+    check(tb, orc, sr, A, B, f"special {sr}")
+
+
+def test_signed_zero_first_winner(tb, orc):
+    # every term is -0 or +0; the first one decides the sign of C
+    g = torch.Generator().manual_seed(9)
+    A = torch.where(torch.rand(1, 64, 64, generator=g) < 0.5, -0.0, 0.0)
+    B = torch.full((1, 64, 64), -0.0)
+    check(tb, orc, "max_plus", A, B, "signed zeros")
+    check(tb, orc, "min_plus", A, B, "signed zeros min")
+
+
+def test_int32_saturation(tb, orc):
+    g = torch.Generator().manual_seed(13)
+    big = torch.tensor([2 ** 31 - 1, -(2 ** 31), I32_INF, -I32_INF, 0, 1, -1], dtype=torch.int32)
+    A = big[torch.randint(0, 7, (1, 65, 100), generator=g)]
+    B = big[torch.randint(0, 7, (1, 100, 66), generator=g)]
+    for sr in ("max_plus", "min_plus"):
+        check(tb, orc, sr, A, B, f"saturation {sr}")
+
+
+def test_golden_fixtures(tb):
+    for case in gio.load("gemm_3x3.json")["cases"] + gio.load("special_values.json")["cases"]:
+        A = torch.from_numpy(gio.array(case["A"], case["dtype"]))
+        B = torch.from_numpy(gio.array(case["B"], case["dtype"]))
+        C, I = gpu_gemm(tb, case["semiring"], A, B)
+        assert_bits_equal(C[0], gio.array(case["C"], case["dtype"]), case["name"])
+        assert_equal(I[0], np.array(case["argmax"]), case["name"])
+
+
+def test_k_zero_and_empty(tb, orc):
+    for sr, dt in PAIRS:
+        dtype = torch.float32 if dt == "f32" else torch.int32
+        A = torch.zeros(2, 5, 0, dtype=dtype)
+        B = torch.zeros(2, 0, 7, dtype=dtype)
+        C, I = gpu_gemm(tb, sr, A, B)
+        Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy())
+        assert_bits_equal(C, Cr, f"k=0 {sr} {dt}")
+        assert_equal(I, Ir, f"k=0 {sr} {dt}")
+    # zero-sized outputs enqueue nothing
+    Cd = torch.empty(3, 0, 4, device=DEV)
+    tb.tropical_gemm_strided_batched("max_plus", torch.empty(3, 0, 5, device=DEV),
+                                     torch.empty(3, 5, 4, device=DEV), Cd)
+
+
+def test_no_argmax_and_column_major_c(tb, orc):
+    A, B = make("max_plus", "f32", 2, 70, 100, 90, seed=21, ties=False)
+    check(tb, orc, "max_plus", A, B, "no argmax", argmax=False)
+    check(tb, orc, "max_plus", A, B, "column-major C", c_layout="col")
+
+
+def test_strided_views_and_unaligned(tb, orc):
+    g = torch.Generator().manual_seed(17)
+    big = torch.randint(-5, 6, (3, 90, 160), generator=g).float()
+    A = big[:, 1:80:1, 3:150:1]          # unaligned base, row stride 160
+    A2 = big[:, ::2, ::2]                # no unit stride at all
+    Bbig = torch.randint(-5, 6, (3, 200, 100), generator=g).float()
+    B = Bbig[:, 5:152, 1:70]             # k = 147 rows to match A
+    check(tb, orc, "max_plus", A, B, "unaligned views")
+    B2 = Bbig[:, ::2, ::3][:, :80, :]    # k = 80 to match A2's 80 columns
+    check(tb, orc, "min_plus", A2, B2, "non-unit strides")
+    # batch stride larger than m * k (padding between batch entries)
+    P = torch.randint(-5, 6, (3, 40, 50), generator=g).float()
+    check(tb, orc, "max_plus", P[:, :30, :20], P[:, :20, :33], "padded batches")
+    # broadcast batch: stride 0 on B
+    Bb = torch.randint(-5, 6, (1, 20, 33), generator=g).float().expand(3, 20, 33)
+    check(tb, orc, "max_plus", P[:, :30, :20], Bb, "batch stride 0")
+
+
+def test_simple_kernel_and_no_swizzle(tb, orc, monkeypatch):
+    A, B = make("max_plus", "f32", 3, 70, 130, 66, seed=31)
+    monkeypatch.setenv("TROPICAL_FORCE_SIMPLE_GEMM", "1")
+    check(tb, orc, "max_plus", A, B, "simple kernel")
+    Ai, Bi = make("min_plus", "i32", 2, 33, 70, 40, seed=32)
+    check(tb, orc, "min_plus", Ai, Bi, "simple kernel i32")
+    monkeypatch.delenv("TROPICAL_FORCE_SIMPLE_GEMM")
+    monkeypatch.setenv("TROPICAL_NO_XCD_SWIZZLE", "1")
+    check(tb, orc, "max_plus", A, B, "no swizzle")
+
+
+# ---------------------------------------------------------------------------
+# the four GEMM workloads at full size, in the launch configuration that the
+# benchmark times
+
+def test_workload1_full(tb, orc):
+    A, B = inputs.gemm_operands(1)
+    check(tb, orc, "max_plus", A, B, "workload 1")
+
+
+def test_workload2_full(tb, orc):
+    A, B = inputs.gemm_operands(2)
+    check(tb, orc, "max_plus", A, B, "workload 2")
+
+
+def _sampled(tb, orc, w, npts):
+    spec = inputs.WORKLOADS[w]
+    A, B = inputs.gemm_operands(w)
+    C, I = gpu_gemm(tb, spec["semiring"], A, B)
+    pts = inputs.random_points(spec["batch"], spec["m"], spec["n"], npts, salt=w).numpy()
+    v, a = orc.gemm_points(spec["semiring"], A.numpy(), B.numpy(), pts)
+    assert_bits_equal(C[pts[:, 0], pts[:, 1], pts[:, 2]], v, f"workload {w} sampled C")
+    assert_equal(I[pts[:, 0], pts[:, 1], pts[:, 2]], a, f"workload {w} sampled argmax")
+    return C, I
+
+
+def test_workload3_full_sampled(tb, orc):
+    C, I = _sampled(tb, orc, 3, 3000)
+    # properties at every output: values are 2^30 (no path) or a sum of two
+    # weights in [1, 1000]; argmax in range
+    assert ((C == I32_INF) | ((C >= 2) & (C <= 2000))).all()
+    assert ((I >= 0) & (I < 4096)).all()
+    assert (I[C == I32_INF] == 0).all()
+
+
+def test_workload4_full_sampled(tb, orc):
+    C, I = _sampled(tb, orc, 4, 3000)
+    assert ((C > 0) & (C <= 1)).all()
+    assert ((I >= 0) & (I < 2048)).all()
+
+
+def test_workload3_reduced_full_check(tb, orc):
+    A, B = inputs.gemm_operands(3, m=300, n=260, k=1100)
+    check(tb, orc, "min_plus", A, B, "workload 3 recipe, 300x260x1100")
+
+
+def test_workload4_reduced_full_check(tb, orc):
+    A, B = inputs.gemm_operands(4, batch=3, m=200, n=150, k=700)
+    check(tb, orc, "max_mul", A, B, "workload 4 recipe, 3x200x150x700")

@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libtropical.so (see include/tropical.h).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch tensors become data pointers, element strides and sizes,
+the stream defaults to torch's current stream.  All computation happens in
+the library's gfx950 kernels.  There is no fallback: if the library was not
+built, the first call raises ``TropicalLibraryMissing``.
+
+Output tensors are allocated with torch when the caller passes none; torch
+is used only for device memory and streams.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libtropical.so")
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, NOT_DEVICE_MEMORY, WORKSPACE_TOO_SMALL, HIP_ERROR = range(6)
+STATUS_NAMES = {0: "TROP_OK", 1: "TROP_ERR_INVALID_ARGUMENT", 2: "TROP_ERR_UNSUPPORTED",
+                3: "TROP_ERR_NOT_DEVICE_MEMORY", 4: "TROP_ERR_WORKSPACE_TOO_SMALL",
+                5: "TROP_ERR_HIP"}
+SEMIRINGS = {"max_plus": 0, "min_plus": 1, "max_mul": 2}
+F32, I32 = 0, 1
+KERNEL_FAMILIES = ["gemm_tiled", "gemm_simple", "fill", "gather_copy", "gather_tiled",
+                   "gather_naive", "gather_reduce"]
+MAX_DIMS = 8
+
+
+class TropicalLibraryMissing(RuntimeError):
+    pass
+
+
+class TropicalError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+class trop_strides(ctypes.Structure):
+    _fields_ = [("row", ctypes.c_int64), ("col", ctypes.c_int64), ("batch", ctypes.c_int64)]
+
+
+class trop_stats(ctypes.Structure):
+    _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
+                ("launches", ctypes.c_uint64 * 8), ("host_syncs", ctypes.c_uint64),
+                ("memcpy_calls", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise TropicalLibraryMissing(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() "
+            "(python tropical_semiring_tensor_amd/csrc/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    L.tropical_init.argtypes = [i32]
+    L.tropical_gemm_strided_batched.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp,
+                                                trop_strides, vp, i64, i64, i64, i64, vp]
+    L.tropical_permute.argtypes = [sz, i32, I64P, I64P, I32P, i32, ctypes.POINTER(vp),
+                                   ctypes.POINTER(vp), vp]
+    L.tropical_diag_gather.argtypes = [i32, i32, i32, I64P, I64P, I32P, i32, I32P, vp, vp, vp]
+    L.tropical_contract_pair_workspace_size.argtypes = [ctypes.c_char_p, I64P, I64P,
+                                                        ctypes.POINTER(sz)]
+    L.tropical_contract_pair.argtypes = [ctypes.c_char_p, i32, i32, vp, I64P, I64P, vp, I64P, I64P,
+                                         vp, vp, vp, sz, vp]
+    L.tropical_contract_pair_describe.argtypes = [ctypes.c_char_p, I64P, I64P, I64P, I64P,
+                                                  ctypes.c_char_p, sz]
+    L.tropical_last_error.restype = ctypes.c_char_p
+    L.tropical_get_stats.argtypes = [ctypes.POINTER(trop_stats)]
+    L.tropical_reset_stats.restype = None
+    for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_permute",
+               "tropical_diag_gather", "tropical_contract_pair_workspace_size",
+               "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats"):
+        getattr(L, fn).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != OK:
+        msg = lib().tropical_last_error().decode(errors="replace")
+        raise TropicalError(status, f"{what}: {msg}")
+
+
+def _sr(semiring):
+    return SEMIRINGS[semiring] if isinstance(semiring, str) else int(semiring)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.int32:
+        return I32
+    raise TypeError(f"float32 or int32 tensors only, got {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * max(1, len(vals)))(*[int(v) for v in vals])
+
+
+def _i32(vals):
+    return (ctypes.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _as3(t):
+    return t.unsqueeze(0) if t.dim() == 2 else t
+
+
+# ---------------------------------------------------------------------------
+
+def tropical_init(device=0):
+    _check(lib().tropical_init(int(device)), "tropical_init")
+
+
+def tropical_gemm_strided_batched(semiring, A, B, C, argmax=None, stream=None):
+    """C[b,i,j] = (+)_k A[b,i,k] (x) B[b,k,j] and argmax[b,i,j] = first winning k.
+
+    A: (batch, m, k), B: (batch, k, n), C and argmax: (batch, m, n) views
+    (2-d tensors are batch 1).  Any non-negative strides; argmax must share
+    C's strides.  Enqueued on `stream` (default: torch's current stream).
+    """
+    A3, B3, C3 = _as3(A), _as3(B), _as3(C)
+    batch, m, k = A3.shape
+    n = B3.shape[2]
+    if argmax is not None and _as3(argmax).stride() != C3.stride():
+        raise ValueError("argmax must have the strides of C")
+    sA = trop_strides(A3.stride(1), A3.stride(2), A3.stride(0))
+    sB = trop_strides(B3.stride(1), B3.stride(2), B3.stride(0))
+    sC = trop_strides(C3.stride(1), C3.stride(2), C3.stride(0))
+    st = lib().tropical_gemm_strided_batched(_sr(semiring), _dt(A3), _ptr(A3), sA, _ptr(B3), sB,
+                                             _ptr(C3), sC, _ptr(argmax), m, n, k, batch,
+                                             _stream(stream))
+    _check(st, "tropical_gemm_strided_batched")
+    return C, argmax
+
+
+def tropical_permute(x, perm, out=None, x2=None, out2=None, stream=None):
+    """out = x.permute(perm) made contiguous; x2 -> out2 with the same mapping."""
+    perm = [int(p) for p in perm]
+    shape = [x.shape[p] for p in perm]
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    n = 1
+    ins = [x.data_ptr()]
+    outs = [out.data_ptr()]
+    if x2 is not None:
+        if x2.shape != x.shape or x2.stride() != x.stride():
+            raise ValueError("x2 must have the shape and strides of x")
+        if out2 is None:
+            out2 = torch.empty(shape, dtype=x2.dtype, device=x2.device)
+        ins.append(x2.data_ptr())
+        outs.append(out2.data_ptr())
+        n = 2
+    in_arr = (ctypes.c_void_p * 2)(*ins, *([0] * (2 - n)))
+    out_arr = (ctypes.c_void_p * 2)(*outs, *([0] * (2 - n)))
+    st = lib().tropical_permute(x.element_size(), x.dim(), _i64(x.shape), _i64(x.stride()),
+                                _i32(perm), n, in_arr, out_arr, _stream(stream))
+    _check(st, "tropical_permute")
+    return (out, out2) if x2 is not None else out
+
+
+def _label_ids(labels):
+    return [ord(c) if isinstance(c, str) else int(c) for c in labels]
+
+
+def tropical_diag_gather(semiring, x, in_labels, out_labels, out=None, stream=None):
+    """Repeated-label diagonal (and (+)-reduction of labels absent from out)."""
+    il, ol = _label_ids(in_labels), _label_ids(out_labels)
+    if len(il) != x.dim():
+        raise ValueError("one label per input axis")
+    ext = {}
+    for lab, e in zip(il, x.shape):
+        ext.setdefault(lab, e)
+    if out is None:
+        out = torch.empty([ext.get(lab, 0) for lab in ol], dtype=x.dtype, device=x.device)
+    st = lib().tropical_diag_gather(_sr(semiring), _dt(x), x.dim(), _i64(x.shape), _i64(x.stride()),
+                                    _i32(il), len(ol), _i32(ol), _ptr(x), _ptr(out),
+                                    _stream(stream))
+    _check(st, "tropical_diag_gather")
+    return out
+
+
+def tropical_contract_pair_workspace_size(spec, shapeA, shapeB):
+    n = ctypes.c_size_t(0)
+    st = lib().tropical_contract_pair_workspace_size(spec.encode(), _i64(shapeA), _i64(shapeB),
+                                                     ctypes.byref(n))
+    _check(st, "tropical_contract_pair_workspace_size")
+    return n.value
+
+
+def tropical_contract_pair_describe(spec, shapeA, shapeB, stridesA=None, stridesB=None):
+    buf = ctypes.create_string_buffer(1024)
+    st = lib().tropical_contract_pair_describe(
+        spec.encode(), _i64(shapeA), _i64(stridesA) if stridesA is not None else None,
+        _i64(shapeB), _i64(stridesB) if stridesB is not None else None, buf, len(buf))
+    _check(st, "tropical_contract_pair_describe")
+    return buf.value.decode()
+
+
+def _out_shape(spec, A, B):
+    lhs, out = spec.replace(" ", "").split("->")
+    la, lb = lhs.split(",")
+    ext = {}
+    for sub, t in ((la, A), (lb, B)):
+        for c, e in zip(sub, t.shape):
+            ext.setdefault(c, e)
+    return [ext.get(c, 0) for c in out]
+
+
+def tropical_contract_pair(spec, semiring, A, B, C=None, argmax=True, workspace=None, stream=None):
+    """Pairwise tropical einsum; returns (C, argmax) (argmax None if not asked).
+
+    argmax=True allocates the int32 argmax; pass a tensor to reuse one, or
+    None / False to skip it.  The workspace is allocated with torch when
+    not given.
+    """
+    shape = _out_shape(spec, A, B)
+    if C is None:
+        C = torch.empty(shape, dtype=A.dtype, device=A.device)
+    if argmax is True:
+        argmax = torch.empty(shape, dtype=torch.int32, device=A.device)
+    elif argmax is False:
+        argmax = None
+    if workspace is None:
+        nbytes = tropical_contract_pair_workspace_size(spec, A.shape, B.shape)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+    st = lib().tropical_contract_pair(spec.encode(), _sr(semiring), _dt(A), _ptr(A), _i64(A.shape),
+                                      _i64(A.stride()), _ptr(B), _i64(B.shape), _i64(B.stride()),
+                                      _ptr(C), _ptr(argmax), _ptr(workspace), workspace.numel(),
+                                      _stream(stream))
+    _check(st, "tropical_contract_pair")
+    return C, argmax
+
+
+def tropical_get_stats():
+    s = trop_stats()
+    _check(lib().tropical_get_stats(ctypes.byref(s)), "tropical_get_stats")
+    return {"module_loads": s.module_loads, "launches_total": s.launches_total,
+            "launches": {name: s.launches[i] for i, name in enumerate(KERNEL_FAMILIES)},
+            "host_syncs": s.host_syncs, "memcpy_calls": s.memcpy_calls}
+
+
+def tropical_reset_stats():
+    lib().tropical_reset_stats()
+
+
+def tropical_last_error():
+    return lib().tropical_last_error().decode(errors="replace")

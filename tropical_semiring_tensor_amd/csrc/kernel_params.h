@@ -1,0 +1,65 @@
+// Kernel argument blocks, passed by value to every launch.  Plain structs
+// shared by the host runtime and the device code so that both agree on the
+// layout; no pointer in them is kept after a call returns.
+#pragma once
+#include <stdint.h>
+
+#define TROP_MAX_DIMS 8
+
+// Semiring ids (match trop_semiring in include/tropical.h).
+#define TROP_SR_MAX_PLUS 0
+#define TROP_SR_MIN_PLUS 1
+#define TROP_SR_MAX_MUL 2
+
+// How a GEMM operand tile is read from global memory.
+#define TROP_LOAD_K_CONTIG 0   // k is the unit-stride axis (or neither is)
+#define TROP_LOAD_MN_CONTIG 1  // the row (A) / column (B) axis is unit-stride
+
+struct TropGemmParams {
+    const void* A;
+    const void* B;
+    void* C;
+    int32_t* argmax;  // may be null
+    int64_t sa_row, sa_col, sa_batch;
+    int64_t sb_row, sb_col, sb_batch;
+    int64_t sc_row, sc_col, sc_batch;
+    int64_t m, n, k, batch;
+    int32_t tiles_m, tiles_n;  // tiled kernel: tile counts along m and n
+    int32_t a_mode, b_mode;    // TROP_LOAD_*
+    int32_t a_vec, b_vec;      // 16-byte vector loads are aligned and legal
+    int32_t swizzle;           // remap workgroups so each XCD owns a tile range
+    int32_t pad_;
+};
+
+struct TropFillParams {
+    void* C;
+    int32_t* argmax;  // may be null
+    int64_t sc_row, sc_col, sc_batch;
+    int64_t m, n, batch;
+    uint32_t zero_bits;  // bit pattern of the semiring's zero element
+    int32_t pad_;
+};
+
+// Gather: out (contiguous, row-major over `shape`) from an input walked with
+// one stride per output axis; optional (+)-reduction over extra axes.
+struct TropGatherParams {
+    const void* in[2];
+    void* out[2];
+    int32_t ntensors;  // 1 or 2 (same mapping for both)
+    int32_t ndim;      // output rank, 1..TROP_MAX_DIMS
+    int64_t shape[TROP_MAX_DIMS];
+    int64_t istride[TROP_MAX_DIMS];
+    int64_t total;     // number of output elements
+    // tiled transpose: the output axis `ax_in` has input stride 1 and the
+    // last output axis has output stride 1
+    int32_t ax_in;
+    int32_t vec;       // copy path: 16-byte vectors along the last axis
+    int64_t tiles_p, tiles_q;  // tiles along ax_in (p) and the last axis (q)
+    int64_t nbatch;            // product of the remaining axes
+    // reduction (trace)
+    int32_t nred;
+    int32_t pad_;
+    int64_t rshape[TROP_MAX_DIMS];
+    int64_t rstride[TROP_MAX_DIMS];
+    int64_t rtotal;
+};

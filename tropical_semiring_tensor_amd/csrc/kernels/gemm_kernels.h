@@ -1,0 +1,334 @@
+// Strided-batched tropical GEMM with argmax for gfx950.
+//
+// Computes C[b][i][j] = (+)_k A[b][i][k] (x) B[b][k][j] and the smallest k
+// whose term is the result -- the batched "with argmax" kernels of
+// tropical-gemm PR #35 ("feat: batched GPU ops with DLPack zero-copy
+// output", Key changes), re-designed for CDNA4:
+//
+//  * A max-plus product is not a multiply-accumulate, so it runs on the
+//    VALU, not on MFMA.  The value path costs 1.5 VALU instructions per
+//    (output, k): one add / multiply per term and one v_max3 / v_min3 per
+//    two terms.
+//  * An exact per-term argmax would add a compare and two selects per term.
+//    Instead the running value is compared once per chunk of BK = 16 terms
+//    (one compare + one select: which chunk last improved strictly), and the
+//    exact index inside that chunk is resolved afterwards by re-scanning the
+//    chunk for the first term equal to the final value.  That re-scan reads
+//    the operands from LDS: the kernel keeps a whole K-block of KBLK terms
+//    of both operand tiles resident, and resolves at the end of each block
+//    every output whose best improved inside it.  The result is the exact
+//    first winner: a strictly better chunk is recorded only when it holds a
+//    term above everything before it, and inside it the first term equal
+//    to the final value is that first winner.
+//  * C is written with the bits of the winning term (recomputed at the
+//    resolved index), so signed zeros come out as the sequential
+//    strict-compare scan produces them; an output that nothing beat keeps
+//    the zero element and argmax 0.
+//
+// Tiling: 256 threads (4 waves), a 64x64 output tile per workgroup, a 4x4
+// register tile per thread, K staged in BK = 16 slices through LDS.  LDS
+// holds A as [k][i] and B as [k][j] (row length 64 + 4 words of padding),
+// whatever the global layout: k-contiguous operands are transposed on the
+// way in.  Global loads of the next slice are issued into registers while
+// the current slice computes.
+#pragma once
+#include "ring.h"
+
+namespace trop {
+
+constexpr int GEMM_BM = 64;
+constexpr int GEMM_BN = 64;
+constexpr int GEMM_BK = 16;
+constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_TM = 4;
+constexpr int GEMM_TN = 4;
+constexpr int GEMM_LDP = 64 + 4;  // LDS row length (words)
+constexpr int GEMM_KBLK = 256;    // K terms resident in LDS per block
+
+// Bijective remap of the linear workgroup id so that each of the 8 XCDs
+// (which receive workgroups round-robin) owns one contiguous range of
+// logical tiles; neighbouring tiles then share operand panels in one L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t L, int64_t total) {
+    constexpr int64_t NX = 8;
+    const int64_t per = (total + NX - 1) / NX;
+    int64_t tall = total % NX;
+    if (tall == 0) tall = NX;
+    const int64_t x = L % NX;
+    const int64_t local = L / NX;
+    if (x < tall) return x * per + local;
+    return tall * per + (x - tall) * (per - 1) + local;
+}
+
+template <int SR, typename T>
+struct GemmTile {
+    using R = Ring<SR, T>;
+    using V = vec4<T>;
+
+    // Per-thread view of one operand tile: this thread loads 4 elements of
+    // every K-slice.  `mn_contig`: the 4 elements run along the row (A) /
+    // column (B) axis at one k; otherwise they run along k at one row /
+    // column.  `base` points at the thread's first element of slice 0 and
+    // `step` advances one slice.
+    struct Loader {
+        const T* base;
+        int64_t step;     // elements per K-slice
+        int64_t inner;    // stride between the 4 elements
+        int64_t kfirst;   // k of element 0 in slice 0
+        int64_t mn0;      // row (A) / column (B) of element 0
+        int64_t mn_lim;   // m (A) or n (B)
+        int64_t k_lim;    // K
+        int64_t mn_str;   // stride of the row / column axis
+        int64_t k_str;    // stride of the k axis
+        bool mn_contig;
+        bool fast_mn;     // all 4 (or this thread's 1) row / column in range
+        bool vec;         // 16-byte loads allowed
+
+        __device__ __forceinline__ void load(int g, T pad, T (&r)[4]) const {
+            const int64_t k = kfirst + (int64_t)g * GEMM_BK;
+            const bool full = fast_mn && (mn_contig ? (k < k_lim) : (k + 3 < k_lim));
+            if (full && vec) {
+                const V v = *reinterpret_cast<const V*>(base + g * step);
+                r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+            } else if (full) {
+                const T* q = base + g * step;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = q[e * inner];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t kk = mn_contig ? k : k + e;
+                    const int64_t mm = mn_contig ? mn0 + e : mn0;
+                    r[e] = (kk < k_lim && mm < mn_lim) ? base[g * step + e * inner] : pad;
+                }
+            }
+        }
+    };
+
+    // mode: TROP_LOAD_*; for A (mn = rows i, str_mn = sa_row, str_k = sa_col),
+    // for B (mn = columns j, str_mn = sb_col, str_k = sb_row).
+    static __device__ __forceinline__ Loader make(const T* X, int mode, int vec, int64_t mn_start,
+                                                  int64_t mn_lim, int64_t k_lim, int64_t str_mn,
+                                                  int64_t str_k, int tid) {
+        Loader L;
+        L.mn_contig = (mode == TROP_LOAD_MN_CONTIG);
+        L.mn_lim = mn_lim;
+        L.k_lim = k_lim;
+        L.mn_str = str_mn;
+        L.k_str = str_k;
+        L.vec = vec != 0;
+        L.step = GEMM_BK * str_k;
+        if (L.mn_contig) {
+            L.kfirst = tid >> 4;
+            L.mn0 = mn_start + (tid & 15) * 4;
+            L.inner = str_mn;
+            L.fast_mn = L.mn0 + 3 < mn_lim;
+        } else {
+            L.kfirst = (tid & 3) * 4;
+            L.mn0 = mn_start + (tid >> 2);
+            L.inner = str_k;
+            L.fast_mn = L.mn0 < mn_lim;
+        }
+        L.base = X + L.mn0 * str_mn + L.kfirst * str_k;
+        return L;
+    }
+
+    // Write a slice held in registers into LDS slot `s`: A as [k][i], B as
+    // [k][j]; k-contiguous operands are transposed here.
+    static __device__ __forceinline__ void store(const Loader& L, T* S, int s, int tid,
+                                                 const T (&r)[4]) {
+        T* dst = S + s * GEMM_BK * GEMM_LDP;
+        if (L.mn_contig) {
+            const V v = {r[0], r[1], r[2], r[3]};
+            *reinterpret_cast<V*>(dst + (tid >> 4) * GEMM_LDP + (tid & 15) * 4) = v;
+        } else {
+            const int mn = tid >> 2, kq = (tid & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(kq + e) * GEMM_LDP + mn] = r[e];
+        }
+    }
+};
+
+template <int SR, typename T>
+__device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
+    using R = Ring<SR, T>;
+    using V = vec4<T>;
+    using G = GemmTile<SR, T>;
+    constexpr int NST = GEMM_KBLK / GEMM_BK;  // slices per resident K-block
+    __shared__ __attribute__((aligned(16))) T As[GEMM_KBLK * GEMM_LDP];
+    __shared__ __attribute__((aligned(16))) T Bs[GEMM_KBLK * GEMM_LDP];
+
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t total = tiles * p.batch;
+    const int nslices = (int)((p.k + GEMM_BK - 1) / GEMM_BK);
+
+    for (int64_t L = blockIdx.x; L < total; L += gridDim.x) {
+        const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
+        const int64_t b = lg / tiles;
+        const int64_t t = lg % tiles;
+        const int64_t row0 = (t / p.tiles_n) * GEMM_BM;
+        const int64_t col0 = (t % p.tiles_n) * GEMM_BN;
+        const T* __restrict__ A = static_cast<const T*>(p.A) + b * p.sa_batch;
+        const T* __restrict__ B = static_cast<const T*>(p.B) + b * p.sb_batch;
+
+        T best[GEMM_TM][GEMM_TN];
+        T cv[GEMM_TM][GEMM_TN];
+        int win[GEMM_TM][GEMM_TN];
+        int idx[GEMM_TM][GEMM_TN];
+#pragma unroll
+        for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+            for (int c = 0; c < GEMM_TN; ++c) {
+                best[r][c] = R::zero();
+                cv[r][c] = R::zero();
+                win[r][c] = -1;
+                idx[r][c] = 0;
+            }
+
+        const typename G::Loader la =
+            G::make(A, p.a_mode, p.a_vec, row0, p.m, p.k, p.sa_row, p.sa_col, tid);
+        const typename G::Loader lb =
+            G::make(B, p.b_mode, p.b_vec, col0, p.n, p.k, p.sb_col, p.sb_row, tid);
+        T ra[4], rb[4];
+        la.load(0, R::zero(), ra);
+        lb.load(0, R::one(), rb);
+        G::store(la, As, 0, tid, ra);
+        G::store(lb, Bs, 0, tid, rb);
+        __syncthreads();
+        if (nslices > 1) {
+            la.load(1, R::zero(), ra);
+            lb.load(1, R::one(), rb);
+        }
+
+        int64_t block_k0 = 0;  // first k of the resident block
+        for (int g = 0; g < nslices; ++g) {
+            const int s = g % NST;
+            const T* as = As + s * GEMM_BK * GEMM_LDP + ty * 4;
+            const T* bs = Bs + s * GEMM_BK * GEMM_LDP + tx * 4;
+            T run[GEMM_TM][GEMM_TN];
+#pragma unroll
+            for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+                for (int c = 0; c < GEMM_TN; ++c) run[r][c] = best[r][c];
+#pragma unroll
+            for (int kk = 0; kk < GEMM_BK; kk += 2) {
+                const V a0 = *reinterpret_cast<const V*>(as + kk * GEMM_LDP);
+                const V b0 = *reinterpret_cast<const V*>(bs + kk * GEMM_LDP);
+                const V a1 = *reinterpret_cast<const V*>(as + (kk + 1) * GEMM_LDP);
+                const V b1 = *reinterpret_cast<const V*>(bs + (kk + 1) * GEMM_LDP);
+#pragma unroll
+                for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; ++c)
+                        run[r][c] = R::add3(run[r][c], R::mul(a0[r], b0[c]), R::mul(a1[r], b1[c]));
+            }
+#pragma unroll
+            for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+                for (int c = 0; c < GEMM_TN; ++c) {
+                    if (R::better(run[r][c], best[r][c])) win[r][c] = s;
+                    best[r][c] = run[r][c];
+                }
+
+            const bool last = (g + 1 == nslices);
+            const bool boundary = last || ((g + 1) % NST == 0);
+            if (boundary) {
+                // Resolve the outputs whose best improved inside this block:
+                // the first term of the winning slice equal to the best.
+#pragma unroll
+                for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; ++c) {
+                        if (win[r][c] >= 0) {
+                            const int kb = win[r][c] * GEMM_BK;
+                            const T* ac = As + kb * GEMM_LDP + ty * 4 + r;
+                            const T* bc = Bs + kb * GEMM_LDP + tx * 4 + c;
+                            int found = GEMM_BK - 1;
+#pragma unroll
+                            for (int kk = GEMM_BK - 1; kk >= 0; --kk) {
+                                const T term = R::mul(ac[kk * GEMM_LDP], bc[kk * GEMM_LDP]);
+                                found = (term == best[r][c]) ? kk : found;
+                            }
+                            idx[r][c] = (int)(block_k0 + kb + found);
+                            cv[r][c] = R::mul(ac[found * GEMM_LDP], bc[found * GEMM_LDP]);
+                            win[r][c] = -1;
+                        }
+                    }
+                block_k0 += GEMM_KBLK;
+            }
+            if (!last) {
+                if (boundary) __syncthreads();  // the block's LDS is free again
+                G::store(la, As, (g + 1) % NST, tid, ra);
+                G::store(lb, Bs, (g + 1) % NST, tid, rb);
+                if (g + 2 < nslices) {
+                    la.load(g + 2, R::zero(), ra);
+                    lb.load(g + 2, R::one(), rb);
+                }
+                __syncthreads();
+            }
+        }
+
+        T* __restrict__ C = static_cast<T*>(p.C) + b * p.sc_batch;
+        int32_t* __restrict__ I = p.argmax ? p.argmax + b * p.sc_batch : nullptr;
+#pragma unroll
+        for (int r = 0; r < GEMM_TM; ++r) {
+            const int64_t i = row0 + ty * 4 + r;
+            if (i >= p.m) continue;
+#pragma unroll
+            for (int c = 0; c < GEMM_TN; ++c) {
+                const int64_t j = col0 + tx * 4 + c;
+                if (j >= p.n) continue;
+                const int64_t off = i * p.sc_row + j * p.sc_col;
+                C[off] = cv[r][c];
+                if (I) I[off] = idx[r][c];
+            }
+        }
+        __syncthreads();  // LDS is reused by the next tile of this workgroup
+    }
+}
+
+// One thread per output, k ascending, strict compare: the sequential scan
+// itself.  Used for small or oddly strided problems and as a check.
+template <int SR, typename T>
+__device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
+    using R = Ring<SR, T>;
+    const int64_t mn = p.m * p.n;
+    const int64_t total = mn * p.batch;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = o / mn;
+        const int64_t ij = o % mn;
+        const int64_t i = ij / p.n;
+        const int64_t j = ij % p.n;
+        const T* A = static_cast<const T*>(p.A) + b * p.sa_batch + i * p.sa_row;
+        const T* B = static_cast<const T*>(p.B) + b * p.sb_batch + j * p.sb_col;
+        T best = R::zero();
+        int arg = 0;
+        for (int64_t k = 0; k < p.k; ++k) {
+            const T term = R::mul(A[k * p.sa_col], B[k * p.sb_row]);
+            if (R::better(term, best)) {
+                best = term;
+                arg = (int)k;
+            }
+        }
+        const int64_t off = b * p.sc_batch + i * p.sc_row + j * p.sc_col;
+        static_cast<T*>(p.C)[off] = best;
+        if (p.argmax) p.argmax[off] = arg;
+    }
+}
+
+__device__ __forceinline__ void fill_body(const TropFillParams& p) {
+    const int64_t mn = p.m * p.n;
+    const int64_t total = mn * p.batch;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = o / mn;
+        const int64_t ij = o % mn;
+        const int64_t off = b * p.sc_batch + (ij / p.n) * p.sc_row + (ij % p.n) * p.sc_col;
+        static_cast<uint32_t*>(p.C)[off] = p.zero_bits;
+        if (p.argmax) p.argmax[off] = 0;
+    }
+}
+
+}  // namespace trop

@@ -1,0 +1,40 @@
+// The one gfx950 code object of libtropical.so: every kernel entry point.
+// Built with hipcc --genco and embedded in the library, which loads it once
+// per device with hipModuleLoadData and looks the entry points up by name.
+#include "gather_kernels.h"
+#include "gemm_kernels.h"
+
+using namespace trop;
+
+#define TROP_GEMM_ENTRIES(NAME, SR, T)                                                        \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_##NAME(         \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T>(p);                                                              \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gemm_simple_##NAME(TropGemmParams p) { \
+        gemm_simple_body<SR, T>(p);                                                             \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gather_reduce_##NAME(                \
+        TropGatherParams p) {                                                                   \
+        gather_reduce_body<SR, T>(p);                                                           \
+    }
+
+TROP_GEMM_ENTRIES(maxplus_f32, TROP_SR_MAX_PLUS, float)
+TROP_GEMM_ENTRIES(minplus_f32, TROP_SR_MIN_PLUS, float)
+TROP_GEMM_ENTRIES(maxmul_f32, TROP_SR_MAX_MUL, float)
+TROP_GEMM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS, int32_t)
+TROP_GEMM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS, int32_t)
+
+extern "C" __global__ __launch_bounds__(256) void trop_fill(TropFillParams p) { fill_body(p); }
+
+extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_copy(TropGatherParams p) {
+    gather_copy_body(p);
+}
+
+extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled(TropGatherParams p) {
+    gather_tiled_body(p);
+}
+
+extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
+    gather_naive_body(p);
+}

@@ -1,0 +1,413 @@
+// tropical_contract_pair: one pairwise tropical einsum, device-resident.
+//
+// omeinsum-rs issue #52 ("GPU tropical path: keep tensors device-resident +
+// device-side permute") describes the data flow this reproduces on one
+// stream: repeated labels are handled by a unary pre-pass so that the GEMM
+// core only sees clean operands ("Structural lessons from OMEinsum"), the
+// operands are permuted into canonical order, one strided-batched tropical
+// GEMM runs, and its value and argmax are permuted into the output order
+// with one shared mapping ("Acceptance criteria").  Nothing leaves the
+// device and the host never waits: all intermediates live in the caller's
+// workspace and every step is enqueued on the caller's stream.  The same
+// section's advice to let GEMM strides absorb a permute "where the layout
+// allows" is followed for operands: an operand whose batch, row and column
+// label groups each collapse to one stride, with a unit row or column
+// stride, is read in place instead of being gathered.
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace trop {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Operand {
+    std::string sub;             // subscript
+    int64_t shape[TROP_MAX_DIMS];
+    int64_t stride[TROP_MAX_DIMS];
+    bool has_strides = false;
+};
+
+struct Plan {
+    std::string la, lb, lo;
+    std::string batch, left, right, contracted, a_red, b_red;
+    int64_t ext[128];
+    int64_t nb = 1, M = 1, N = 1, K = 1;
+    int64_t out_total = 1;
+    bool a_fold = false, b_fold = false, c_direct = false;
+    trop_strides sA{}, sB{};
+    GatherPlan ga{}, gb{}, gc{};
+    size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, ws = 0;
+};
+
+bool is_label(char c) { return (c >= 'a' && c <= 'z') || (c >= 'A' && c <= 'Z'); }
+
+bool has(const std::string& s, char c) { return s.find(c) != std::string::npos; }
+
+std::string unique(const std::string& s) {
+    std::string u;
+    for (char c : s)
+        if (!has(u, c)) u.push_back(c);
+    return u;
+}
+
+trop_status parse(const char* spec, Plan& P) {
+    if (!spec) return fail(TROP_ERR_INVALID_ARGUMENT, "spec is NULL");
+    std::string s;
+    for (const char* q = spec; *q; ++q)
+        if (*q != ' ') s.push_back(*q);
+    const size_t arrow = s.find("->");
+    if (arrow == std::string::npos || s.find("->", arrow + 2) != std::string::npos)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly one '->' (explicit output)");
+    const std::string lhs = s.substr(0, arrow);
+    P.lo = s.substr(arrow + 2);
+    const size_t comma = lhs.find(',');
+    if (comma == std::string::npos || lhs.find(',', comma + 1) != std::string::npos)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly two operands");
+    P.la = lhs.substr(0, comma);
+    P.lb = lhs.substr(comma + 1);
+    for (const std::string* part : {&P.la, &P.lb, &P.lo}) {
+        if (part->size() > TROP_MAX_DIMS) return fail(TROP_ERR_INVALID_ARGUMENT, "subscript longer than 8");
+        for (char c : *part)
+            if (!is_label(c)) return fail(TROP_ERR_INVALID_ARGUMENT, std::string("bad label '") + c + "'");
+    }
+    if (unique(P.lo).size() != P.lo.size()) return fail(TROP_ERR_INVALID_ARGUMENT, "repeated output label");
+    for (char c : P.lo)
+        if (!has(P.la, c) && !has(P.lb, c))
+            return fail(TROP_ERR_INVALID_ARGUMENT, std::string("output label '") + c + "' is in no operand");
+    // label roles, in output order for batch / left / right and in
+    // A-subscript order for contracted labels
+    for (char c : P.lo) {
+        const bool a = has(P.la, c), b = has(P.lb, c);
+        if (a && b) P.batch.push_back(c);
+        else if (a) P.left.push_back(c);
+        else P.right.push_back(c);
+    }
+    for (char c : unique(P.la)) {
+        if (has(P.lo, c)) continue;
+        if (has(P.lb, c)) P.contracted.push_back(c);
+        else P.a_red.push_back(c);
+    }
+    for (char c : unique(P.lb))
+        if (!has(P.lo, c) && !has(P.la, c)) P.b_red.push_back(c);
+    return TROP_OK;
+}
+
+trop_status bind_shapes(Plan& P, const int64_t* shapeA, const int64_t* shapeB) {
+    for (int i = 0; i < 128; ++i) P.ext[i] = -1;
+    const std::string* subs[2] = {&P.la, &P.lb};
+    const int64_t* shapes[2] = {shapeA, shapeB};
+    for (int o = 0; o < 2; ++o) {
+        if (!subs[o]->empty() && !shapes[o]) return fail(TROP_ERR_INVALID_ARGUMENT, "NULL shape");
+        for (size_t d = 0; d < subs[o]->size(); ++d) {
+            const char c = (*subs[o])[d];
+            const int64_t e = shapes[o][d];
+            if (e < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent");
+            if (P.ext[(int)c] >= 0 && P.ext[(int)c] != e)
+                return fail(TROP_ERR_INVALID_ARGUMENT, std::string("extent mismatch for label '") + c + "'");
+            P.ext[(int)c] = e;
+        }
+    }
+    auto prod = [&](const std::string& labels, int64_t* out) {
+        int64_t p = 1;
+        for (char c : labels)
+            if (__builtin_mul_overflow(p, P.ext[(int)c], &p)) return false;
+        *out = p;
+        return true;
+    };
+    if (!prod(P.batch, &P.nb) || !prod(P.left, &P.M) || !prod(P.right, &P.N) || !prod(P.contracted, &P.K) ||
+        !prod(P.lo, &P.out_total))
+        return fail(TROP_ERR_INVALID_ARGUMENT, "sizes overflow");
+    if (P.K > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "contracted size must be < 2^31 (int32 argmax)");
+    int64_t t;
+    if (__builtin_mul_overflow(P.nb, P.M, &t) || __builtin_mul_overflow(t, P.K, &t) ||
+        __builtin_mul_overflow(P.nb, P.K, &t) || __builtin_mul_overflow(t, P.N, &t) ||
+        __builtin_mul_overflow(P.nb * P.M, P.N, &t))
+        return fail(TROP_ERR_INVALID_ARGUMENT, "sizes overflow");
+    return TROP_OK;
+}
+
+// Stride of a label group when it collapses to one axis of `op` (labels in
+// group order, outermost first).  Returns false if the group is not
+// collapsible or a label of it is repeated in the operand.
+bool group_stride(const Plan& P, const Operand& op, const std::string& group, int64_t* out) {
+    int64_t want = -1;  // stride the next (outer) label must have
+    int64_t s_inner = 0;
+    bool any = false;
+    for (int g = (int)group.size() - 1; g >= 0; --g) {
+        const char c = group[g];
+        int pos = -1, count = 0;
+        for (size_t d = 0; d < op.sub.size(); ++d)
+            if (op.sub[d] == c) {
+                pos = (int)d;
+                ++count;
+            }
+        if (count != 1) return false;
+        const int64_t e = P.ext[(int)c];
+        if (e == 1) continue;
+        const int64_t s = op.stride[pos];
+        if (!any) {
+            s_inner = s;
+            any = true;
+        } else if (s != want) {
+            return false;
+        }
+        want = s * e;
+    }
+    *out = any ? s_inner : 0;
+    return true;
+}
+
+// Can `op` be read in place as a batched matrix (batch, rows, cols)?
+bool try_fold(const Plan& P, const Operand& op, const std::string& reduce, const std::string& gb,
+              const std::string& gr, const std::string& gc, trop_strides* s) {
+    if (!reduce.empty()) return false;
+    if (unique(op.sub).size() != op.sub.size()) return false;  // repeated label: needs the diagonal pass
+    int64_t sb, sr, sc;
+    if (!group_stride(P, op, gb, &sb) || !group_stride(P, op, gr, &sr) || !group_stride(P, op, gc, &sc))
+        return false;
+    const int64_t rows = [&] { int64_t p = 1; for (char c : gr) p *= P.ext[(int)c]; return p; }();
+    const int64_t cols = [&] { int64_t p = 1; for (char c : gc) p *= P.ext[(int)c]; return p; }();
+    // a unit stride on the row or column axis keeps the GEMM loads coalesced
+    const bool unit = (sc == 1 || cols == 1) || (sr == 1 || rows == 1);
+    if (!unit) return false;
+    s->batch = sb;
+    s->row = sr;
+    s->col = sc;
+    return true;
+}
+
+trop_status plan_operand(const Plan& P, const Operand& op, const std::string& canonical, GatherPlan* g) {
+    int32_t in_lab[TROP_MAX_DIMS], out_lab[TROP_MAX_DIMS];
+    for (size_t d = 0; d < op.sub.size(); ++d) in_lab[d] = op.sub[d];
+    for (size_t d = 0; d < canonical.size(); ++d) out_lab[d] = canonical[d];
+    return plan_diag((int)op.sub.size(), op.shape, op.stride, in_lab, (int)canonical.size(), out_lab, g);
+}
+
+void default_strides(Operand& op) {
+    int64_t s = 1;
+    for (int d = (int)op.sub.size() - 1; d >= 0; --d) {
+        op.stride[d] = s;
+        s *= op.shape[d] > 0 ? op.shape[d] : 1;
+    }
+}
+
+trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
+                       const int64_t* stridesB, Plan& P, Operand& A, Operand& B) {
+    trop_status st = parse(spec, P);
+    if (st != TROP_OK) return st;
+    st = bind_shapes(P, shapeA, shapeB);
+    if (st != TROP_OK) return st;
+    A.sub = P.la;
+    B.sub = P.lb;
+    for (size_t d = 0; d < A.sub.size(); ++d) A.shape[d] = shapeA[d];
+    for (size_t d = 0; d < B.sub.size(); ++d) B.shape[d] = shapeB[d];
+    if (stridesA) {
+        for (size_t d = 0; d < A.sub.size(); ++d) A.stride[d] = stridesA[d];
+        A.has_strides = true;
+    } else {
+        default_strides(A);
+    }
+    if (stridesB) {
+        for (size_t d = 0; d < B.sub.size(); ++d) B.stride[d] = stridesB[d];
+        B.has_strides = true;
+    } else {
+        default_strides(B);
+    }
+    for (size_t d = 0; d < A.sub.size(); ++d)
+        if (A.stride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride in A");
+    for (size_t d = 0; d < B.sub.size(); ++d)
+        if (B.stride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride in B");
+
+    const std::string canA = P.batch + P.left + P.contracted;
+    const std::string canB = P.batch + P.contracted + P.right;
+    const std::string canC = P.batch + P.left + P.right;
+
+    P.a_fold = try_fold(P, A, P.a_red, P.batch, P.left, P.contracted, &P.sA);
+    if (!P.a_fold) {
+        st = plan_operand(P, A, canA, &P.ga);
+        if (st != TROP_OK) return st;
+        P.sA = {P.K, 1, P.M * P.K};
+    }
+    P.b_fold = try_fold(P, B, P.b_red, P.batch, P.contracted, P.right, &P.sB);
+    if (!P.b_fold) {
+        st = plan_operand(P, B, canB, &P.gb);
+        if (st != TROP_OK) return st;
+        P.sB = {P.N, 1, P.K * P.N};
+    }
+    P.c_direct = (canC == P.lo);
+    if (!P.c_direct) {
+        // C'' is contiguous over canC; the output walks it in P.lo order
+        int64_t cstr[TROP_MAX_DIMS];
+        int64_t s = 1;
+        for (int d = (int)canC.size() - 1; d >= 0; --d) {
+            cstr[d] = s;
+            s *= P.ext[(int)canC[d]];
+        }
+        int64_t oshape[TROP_MAX_DIMS], ostride[TROP_MAX_DIMS];
+        for (size_t d = 0; d < P.lo.size(); ++d) {
+            const size_t pos = canC.find(P.lo[d]);
+            oshape[d] = P.ext[(int)P.lo[d]];
+            ostride[d] = cstr[pos];
+        }
+        st = plan_gather((int)P.lo.size(), oshape, ostride, 0, nullptr, nullptr, &P.gc);
+        if (st != TROP_OK) return st;
+    }
+    // workspace layout
+    size_t off = 0;
+    if (!P.a_fold) {
+        P.off_a = off;
+        off += align_up((size_t)(P.nb * P.M * P.K) * 4);
+    }
+    if (!P.b_fold) {
+        P.off_b = off;
+        off += align_up((size_t)(P.nb * P.K * P.N) * 4);
+    }
+    if (!P.c_direct) {
+        P.off_c = off;
+        off += align_up((size_t)(P.nb * P.M * P.N) * 4);
+        P.off_i = off;
+        off += align_up((size_t)(P.nb * P.M * P.N) * 4);
+    }
+    P.ws = off;
+    return TROP_OK;
+}
+
+std::string describe(const Plan& P) {
+    char buf[512];
+    std::snprintf(buf, sizeof(buf),
+                  "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm batch=%lld m=%lld "
+                  "n=%lld k=%lld; A=%s%s B=%s%s out=%s%s; workspace=%zu",
+                  P.batch.c_str(), P.left.c_str(), P.right.c_str(), P.contracted.c_str(), P.a_red.c_str(),
+                  P.b_red.c_str(), (long long)P.nb, (long long)P.M, (long long)P.N, (long long)P.K,
+                  P.a_fold ? "fold" : "gather:", P.a_fold ? "" : gather_path_name(P.ga.path),
+                  P.b_fold ? "fold" : "gather:", P.b_fold ? "" : gather_path_name(P.gb.path),
+                  P.c_direct ? "direct" : "permute:", P.c_direct ? "" : gather_path_name(P.gc.path), P.ws);
+    return buf;
+}
+
+}  // namespace
+
+}  // namespace trop
+
+using namespace trop;
+
+extern "C" trop_status tropical_contract_pair_workspace_size(const char* spec, const int64_t* shapeA,
+                                                             const int64_t* shapeB, size_t* bytes) {
+    if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    Plan P;
+    Operand A, B;
+    // default (contiguous) strides: the bound below does not depend on them
+    trop_status st = build_plan(spec, shapeA, nullptr, shapeB, nullptr, P, A, B);
+    if (st != TROP_OK) return st;
+    // upper bound: room for both operand pre-passes and the output permute
+    size_t ws = align_up((size_t)(P.nb * P.M * P.K) * 4) + align_up((size_t)(P.nb * P.K * P.N) * 4);
+    if (!P.c_direct) ws += 2 * align_up((size_t)(P.nb * P.M * P.N) * 4);
+    *bytes = ws;
+    return ok();
+}
+
+extern "C" trop_status tropical_contract_pair_describe(const char* spec, const int64_t* shapeA,
+                                                       const int64_t* stridesA, const int64_t* shapeB,
+                                                       const int64_t* stridesB, char* buf, size_t buflen) {
+    Plan P;
+    Operand A, B;
+    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P, A, B);
+    if (st != TROP_OK) return st;
+    const std::string d = describe(P);
+    if (buf && buflen > 0) {
+        std::strncpy(buf, d.c_str(), buflen - 1);
+        buf[buflen - 1] = '\0';
+    }
+    return ok();
+}
+
+extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring semiring, trop_dtype dtype,
+                                              const void* Aptr, const int64_t* shapeA, const int64_t* stridesA,
+                                              const void* Bptr, const int64_t* shapeB, const int64_t* stridesB,
+                                              void* C, int32_t* argmax, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    if (semiring < TROP_MAX_PLUS || semiring > TROP_MAX_MUL) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring");
+    if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    Plan P;
+    Operand A, B;
+    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P, A, B);
+    if (st != TROP_OK) return st;
+    if (argmax && (!P.a_red.empty() || !P.b_red.empty()))
+        return fail(TROP_ERR_UNSUPPORTED, "argmax through a pre-pass reduction is not defined");
+    if (P.out_total == 0) return ok();
+    if (P.ws > 0 && workspace_bytes < P.ws)
+        return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(P.ws) + " bytes, got " + std::to_string(workspace_bytes));
+
+    int dev = -1;
+    st = current_device(&dev);
+    if (st != TROP_OK) return st;
+    // operand spans over their own axes
+    for (int o = 0; o < 2; ++o) {
+        const Operand& op = o ? B : A;
+        const void* ptr = o ? Bptr : Aptr;
+        bool empty = false;
+        for (size_t d = 0; d < op.sub.size(); ++d) empty = empty || op.shape[d] == 0;
+        if (empty) continue;
+        int64_t span = 0;
+        if (!max_offset((int)op.sub.size(), op.shape, op.stride, &span))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "operand extent overflows");
+        st = check_device_span(ptr, dev, span + 1, 4, o ? "B" : "A");
+        if (st != TROP_OK) return st;
+    }
+    st = check_device_span(C, dev, P.out_total, 4, "C");
+    if (st != TROP_OK) return st;
+    if (argmax) {
+        st = check_device_span(argmax, dev, P.out_total, 4, "argmax");
+        if (st != TROP_OK) return st;
+    }
+    if (P.ws > 0) {
+        st = check_device_span(workspace, dev, (int64_t)(P.ws / 4), 4, "workspace");
+        if (st != TROP_OK) return st;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+
+    // 1. unary pre-pass + permute into canonical operand order
+    const void* a_use = Aptr;
+    const void* b_use = Bptr;
+    if (!P.a_fold) {
+        void* dst = ws + P.off_a;
+        const void* in[1] = {Aptr};
+        void* out[1] = {dst};
+        st = run_gather(dev, P.ga, 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+        a_use = dst;
+    }
+    if (!P.b_fold) {
+        void* dst = ws + P.off_b;
+        const void* in[1] = {Bptr};
+        void* out[1] = {dst};
+        st = run_gather(dev, P.gb, 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+        b_use = dst;
+    }
+    // 2. batched GEMM into the canonical (batch, left, right) result
+    void* c_gemm = P.c_direct ? C : static_cast<void*>(ws + P.off_c);
+    int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
+    const trop_strides sC = {P.N, 1, P.M * P.N};
+    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.M, P.N, P.K, P.nb, s);
+    if (st != TROP_OK) return st;
+    // 3. one paired permute of value and argmax into the output order
+    if (!P.c_direct) {
+        const void* in[2] = {c_gemm, i_gemm};
+        void* out[2] = {C, argmax};
+        st = run_gather(dev, P.gc, argmax ? 2 : 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+    }
+    return ok();
+}

@@ -1,0 +1,295 @@
+// tropical_permute and tropical_diag_gather: planning and launch.
+//
+// Kernels (a) and (b) of omeinsum-rs issue #52 ("GPU tropical path: keep
+// tensors device-resident + device-side permute", "Resolved design for
+// step 3") share one description here: the output is contiguous row-major,
+// each output axis walks the input with one stride (the sum of strides for
+// a repeated label), and optional extra axes are (+)-reduced.  Planning
+// drops size-1 axes and merges output neighbours that are also contiguous
+// in the input, then picks the copy / tiled / naive / reduce kernel.
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace trop {
+
+namespace {
+
+constexpr uint32_t kMaxGrid = 1u << 30;
+
+uint32_t grid_for(int64_t work, int64_t per_block) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return (uint32_t)g;
+}
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+const char* gather_path_name(GatherPath p) {
+    switch (p) {
+        case GP_NONE: return "none";
+        case GP_COPY: return "copy";
+        case GP_TILED: return "tiled";
+        case GP_NAIVE: return "naive";
+        case GP_REDUCE: return "reduce";
+    }
+    return "?";
+}
+
+trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride, int nred,
+                        const int64_t* rshape, const int64_t* rstride, GatherPlan* plan) {
+    std::memset(plan, 0, sizeof(*plan));
+    TropGatherParams& p = plan->params;
+    if (ndim < 0 || ndim > TROP_MAX_DIMS || nred < 0 || nred > TROP_MAX_DIMS)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "rank above 8");
+    int64_t total = 1;
+    for (int d = 0; d < ndim; ++d) {
+        if (oshape[d] < 0 || ostride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent or stride");
+        if (__builtin_mul_overflow(total, oshape[d], &total))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "output too large");
+    }
+    int64_t rtotal = 1;
+    for (int d = 0; d < nred; ++d) {
+        if (rshape[d] < 0 || rstride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent or stride");
+        if (__builtin_mul_overflow(rtotal, rshape[d], &rtotal))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "reduction too large");
+    }
+    if (total == 0) {
+        plan->path = GP_NONE;
+        return TROP_OK;
+    }
+    // An empty reduction yields the zero element everywhere: keep it on the
+    // reduce path, whose loop then runs zero times.
+
+    // input span (for the allocation check)
+    int64_t span = 0;
+    if (!max_offset(ndim, oshape, ostride, &span)) return fail(TROP_ERR_INVALID_ARGUMENT, "input extent overflows");
+    if (rtotal > 0) {
+        int64_t rs = 0;
+        if (!max_offset(nred, rshape, rstride, &rs) || __builtin_add_overflow(span, rs, &span))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "input extent overflows");
+        plan->in_span = span + 1;
+    } else {
+        plan->in_span = 0;
+    }
+
+    // normalise output axes: drop extent 1, merge contiguous neighbours
+    int nd = 0;
+    for (int d = 0; d < ndim; ++d) {
+        if (oshape[d] == 1) continue;
+        if (nd > 0 && p.istride[nd - 1] == ostride[d] * oshape[d]) {
+            p.shape[nd - 1] *= oshape[d];
+            p.istride[nd - 1] = ostride[d];
+        } else {
+            p.shape[nd] = oshape[d];
+            p.istride[nd] = ostride[d];
+            ++nd;
+        }
+    }
+    if (nd == 0) {  // a single element
+        p.shape[0] = 1;
+        p.istride[0] = 0;
+        nd = 1;
+    }
+    p.ndim = nd;
+    p.total = total;
+
+    int nr = 0;
+    for (int d = 0; d < nred; ++d) {
+        if (rshape[d] == 1) continue;
+        p.rshape[nr] = rshape[d];
+        p.rstride[nr] = rstride[d];
+        ++nr;
+    }
+    p.nred = nr;
+    p.rtotal = rtotal;
+    if (nr > 0 || rtotal == 0) {
+        plan->path = GP_REDUCE;
+        return TROP_OK;
+    }
+    if (env_flag("TROPICAL_FORCE_NAIVE_PERMUTE")) {
+        plan->path = GP_NAIVE;
+        return TROP_OK;
+    }
+    if (p.istride[nd - 1] == 1) {
+        plan->path = GP_COPY;
+        return TROP_OK;
+    }
+    for (int d = nd - 2; d >= 0; --d) {
+        if (p.istride[d] == 1) {
+            plan->path = GP_TILED;
+            p.ax_in = d;
+            p.tiles_p = (p.shape[d] + 63) / 64;
+            p.tiles_q = (p.shape[nd - 1] + 63) / 64;
+            p.nbatch = total / (p.shape[d] * p.shape[nd - 1]);
+            return TROP_OK;
+        }
+    }
+    plan->path = GP_NAIVE;
+    return TROP_OK;
+}
+
+trop_status plan_diag(int in_ndim, const int64_t* in_shape, const int64_t* in_strides,
+                      const int32_t* in_labels, int out_ndim, const int32_t* out_labels,
+                      GatherPlan* plan) {
+    if (in_ndim < 0 || in_ndim > TROP_MAX_DIMS || out_ndim < 0 || out_ndim > TROP_MAX_DIMS)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "rank above 8");
+    if ((in_ndim > 0 && (!in_shape || !in_strides || !in_labels)) || (out_ndim > 0 && !out_labels))
+        return fail(TROP_ERR_INVALID_ARGUMENT, "NULL shape / stride / label array");
+    int32_t lab[TROP_MAX_DIMS];
+    int64_t ext[TROP_MAX_DIMS], str[TROP_MAX_DIMS];
+    int nlab = 0;
+    for (int a = 0; a < in_ndim; ++a) {
+        if (in_shape[a] < 0 || in_strides[a] < 0)
+            return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent or stride");
+        int f = -1;
+        for (int l = 0; l < nlab; ++l)
+            if (lab[l] == in_labels[a]) f = l;
+        if (f < 0) {
+            lab[nlab] = in_labels[a];
+            ext[nlab] = in_shape[a];
+            str[nlab] = in_strides[a];
+            ++nlab;
+        } else {
+            if (ext[f] != in_shape[a])
+                return fail(TROP_ERR_INVALID_ARGUMENT, "axes with the same label differ in extent");
+            str[f] += in_strides[a];
+        }
+    }
+    bool used[TROP_MAX_DIMS] = {false};
+    int64_t oshape[TROP_MAX_DIMS], ostride[TROP_MAX_DIMS];
+    for (int d = 0; d < out_ndim; ++d) {
+        int f = -1;
+        for (int l = 0; l < nlab; ++l)
+            if (lab[l] == out_labels[d]) f = l;
+        if (f < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "output label not present in the input");
+        if (used[f]) return fail(TROP_ERR_INVALID_ARGUMENT, "output label repeated");
+        used[f] = true;
+        oshape[d] = ext[f];
+        ostride[d] = str[f];
+    }
+    int64_t rshape[TROP_MAX_DIMS], rstride[TROP_MAX_DIMS];
+    int nred = 0;
+    for (int l = 0; l < nlab; ++l) {
+        if (used[l]) continue;
+        rshape[nred] = ext[l];
+        rstride[nred] = str[l];
+        ++nred;
+    }
+    return plan_gather(out_ndim, oshape, ostride, nred, rshape, rstride, plan);
+}
+
+trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* const* in, void* const* out,
+                       trop_semiring sr, trop_dtype dt, hipStream_t stream) {
+    TropGatherParams& p = plan.params;
+    p.ntensors = ntensors;
+    for (int t = 0; t < 2; ++t) {
+        p.in[t] = t < ntensors ? in[t] : nullptr;
+        p.out[t] = t < ntensors ? out[t] : nullptr;
+    }
+    switch (plan.path) {
+        case GP_NONE:
+            return TROP_OK;
+        case GP_COPY: {
+            const int64_t inner = p.shape[p.ndim - 1];
+            bool vec = inner % 4 == 0;
+            for (int d = 0; d < p.ndim - 1 && vec; ++d) vec = p.istride[d] % 4 == 0;
+            for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
+            p.vec = vec ? 1 : 0;
+            const int64_t work = vec ? p.total / 4 : p.total;
+            return launch(dev, K_GATHER_COPY, TROP_K_GATHER_COPY, grid_for(work, 256), 256, &p, stream);
+        }
+        case GP_TILED: {
+            int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
+            uint32_t grid = nblk > kMaxGrid ? kMaxGrid : (uint32_t)nblk;
+            return launch(dev, K_GATHER_TILED, TROP_K_GATHER_TILED, grid, 256, &p, stream);
+        }
+        case GP_NAIVE:
+            return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);
+        case GP_REDUCE: {
+            const int ri = ring_index(sr, dt);
+            if (ri < 0) return fail(TROP_ERR_UNSUPPORTED, "reduction needs a float32 semiring or int32 max/min-plus");
+            return launch(dev, (KernelId)(K_GATHER_REDUCE_MAXPLUS_F32 + ri), TROP_K_GATHER_REDUCE,
+                          grid_for(p.total, 256), 256, &p, stream);
+        }
+    }
+    return fail(TROP_ERR_INVALID_ARGUMENT, "bad gather plan");
+}
+
+}  // namespace trop
+
+using namespace trop;
+
+extern "C" trop_status tropical_permute(size_t elem_bytes, int ndim, const int64_t* shape,
+                                        const int64_t* in_strides, const int32_t* perm, int ntensors,
+                                        const void* const* in, void* const* out, void* stream) {
+    if (ndim < 0 || ndim > TROP_MAX_DIMS) return fail(TROP_ERR_INVALID_ARGUMENT, "ndim must be 0..8");
+    if (ntensors != 1 && ntensors != 2) return fail(TROP_ERR_INVALID_ARGUMENT, "ntensors must be 1 or 2");
+    if (ndim > 0 && (!shape || !in_strides || !perm))
+        return fail(TROP_ERR_INVALID_ARGUMENT, "NULL shape / stride / perm array");
+    if (!in || !out) return fail(TROP_ERR_INVALID_ARGUMENT, "NULL tensor array");
+    bool seen[TROP_MAX_DIMS] = {false};
+    int64_t oshape[TROP_MAX_DIMS], ostride[TROP_MAX_DIMS];
+    for (int d = 0; d < ndim; ++d) {
+        const int q = perm[d];
+        if (q < 0 || q >= ndim || seen[q]) return fail(TROP_ERR_INVALID_ARGUMENT, "perm is not a permutation");
+        seen[q] = true;
+        if (shape[q] < 0 || in_strides[q] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent or stride");
+        oshape[d] = shape[q];
+        ostride[d] = in_strides[q];
+    }
+    if (elem_bytes != 4) return fail(TROP_ERR_UNSUPPORTED, "only 4-byte elements (float32, int32)");
+    GatherPlan plan;
+    trop_status st = plan_gather(ndim, oshape, ostride, 0, nullptr, nullptr, &plan);
+    if (st != TROP_OK) return st;
+    if (plan.path == GP_NONE) return ok();
+    int dev = -1;
+    st = current_device(&dev);
+    if (st != TROP_OK) return st;
+    for (int t = 0; t < ntensors; ++t) {
+        st = check_device_span(in[t], dev, plan.in_span, 4, t ? "in[1]" : "in[0]");
+        if (st != TROP_OK) return st;
+        st = check_device_span(out[t], dev, plan.params.total, 4, t ? "out[1]" : "out[0]");
+        if (st != TROP_OK) return st;
+    }
+    st = run_gather(dev, plan, ntensors, in, out, TROP_MAX_PLUS, TROP_F32, static_cast<hipStream_t>(stream));
+    return st == TROP_OK ? ok() : st;
+}
+
+extern "C" trop_status tropical_diag_gather(trop_semiring semiring, trop_dtype dtype, int in_ndim,
+                                            const int64_t* in_shape, const int64_t* in_strides,
+                                            const int32_t* in_labels, int out_ndim,
+                                            const int32_t* out_labels, const void* in, void* out,
+                                            void* stream) {
+    if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (semiring < TROP_MAX_PLUS || semiring > TROP_MAX_MUL)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring");
+    GatherPlan plan;
+    trop_status st = plan_diag(in_ndim, in_shape, in_strides, in_labels, out_ndim, out_labels, &plan);
+    if (st != TROP_OK) return st;
+    if (plan.path == GP_REDUCE && ring_index(semiring, dtype) < 0)
+        return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    if (plan.path == GP_NONE) return ok();
+    int dev = -1;
+    st = current_device(&dev);
+    if (st != TROP_OK) return st;
+    if (plan.in_span > 0) {
+        st = check_device_span(in, dev, plan.in_span, 4, "in");
+        if (st != TROP_OK) return st;
+    }
+    st = check_device_span(out, dev, plan.params.total, 4, "out");
+    if (st != TROP_OK) return st;
+    const void* ins[1] = {in};
+    void* outs[1] = {out};
+    st = run_gather(dev, plan, 1, ins, outs, semiring, dtype, static_cast<hipStream_t>(stream));
+    return st == TROP_OK ? ok() : st;
+}

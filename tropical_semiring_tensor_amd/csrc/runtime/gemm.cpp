@@ -1,0 +1,183 @@
+// tropical_gemm_strided_batched: argument checks, kernel choice, launch.
+//
+// The batched tropical product with argmax of tropical-gemm PR #35
+// ("feat: batched GPU ops with DLPack zero-copy output", Key changes).  That
+// PR puts the batch on the third grid axis; here the batch and the output
+// tiles share one flat grid so that the workgroup -> XCD remap in the kernel
+// can keep neighbouring tiles of one batch entry on one XCD.  Which of
+// A / B is row- or column-major is read from the strides (one kernel serves
+// every layout; a column-major operand is transposed into LDS on load).
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace trop {
+
+namespace {
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+constexpr uint32_t kMaxGrid = 1u << 30;
+
+uint32_t grid_for(int64_t work, int64_t per_block) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return (uint32_t)g;
+}
+
+uint32_t zero_bits(trop_semiring sr, trop_dtype dt) {
+    if (dt == TROP_I32) {
+        const int32_t z = (sr == TROP_MIN_PLUS) ? (1 << 30) : -(1 << 30);
+        uint32_t b;
+        std::memcpy(&b, &z, 4);
+        return b;
+    }
+    if (sr == TROP_MAX_PLUS) return 0xff800000u;  // -inf
+    if (sr == TROP_MIN_PLUS) return 0x7f800000u;  // +inf
+    return 0u;                                    // +0
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, trop_strides sB,
+                            trop_strides sC, int64_t m, int64_t n, int64_t k, int64_t batch) {
+    if (sr < TROP_MAX_PLUS || sr > TROP_MAX_MUL)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring " + std::to_string((int)sr));
+    if (dt != TROP_F32 && dt != TROP_I32)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype " + std::to_string((int)dt));
+    if (ring_index(sr, dt) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    if (m < 0 || n < 0 || k < 0 || batch < 0)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
+    if (k > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "k must be < 2^31 (int32 argmax)");
+    const trop_strides* all[3] = {&sA, &sB, &sC};
+    for (const trop_strides* s : all)
+        if (s->row < 0 || s->col < 0 || s->batch < 0)
+            return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride");
+    return TROP_OK;
+}
+
+trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
+                     const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
+                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream) {
+    if (m == 0 || n == 0 || batch == 0) return TROP_OK;
+    const int ri = ring_index(sr, dt);
+    if (k == 0) {
+        TropFillParams f{};
+        f.C = C;
+        f.argmax = argmax;
+        f.sc_row = sC.row;
+        f.sc_col = sC.col;
+        f.sc_batch = sC.batch;
+        f.m = m;
+        f.n = n;
+        f.batch = batch;
+        f.zero_bits = zero_bits(sr, dt);
+        return launch(dev, K_FILL, TROP_K_FILL, grid_for(m * n * batch, 256), 256, &f, stream);
+    }
+
+    TropGemmParams p{};
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.argmax = argmax;
+    p.sa_row = sA.row;
+    p.sa_col = sA.col;
+    p.sa_batch = sA.batch;
+    p.sb_row = sB.row;
+    p.sb_col = sB.col;
+    p.sb_batch = sB.batch;
+    p.sc_row = sC.row;
+    p.sc_col = sC.col;
+    p.sc_batch = sC.batch;
+    p.m = m;
+    p.n = n;
+    p.k = k;
+    p.batch = batch;
+
+    if (env_flag("TROPICAL_FORCE_SIMPLE_GEMM")) {
+        return launch(dev, (KernelId)(K_GEMM_SIMPLE_MAXPLUS_F32 + ri), TROP_K_GEMM_SIMPLE,
+                      grid_for(m * n * batch, 256), 256, &p, stream);
+    }
+
+    // A: row-major (k unit-stride), column-major (i unit-stride), or
+    // neither (element-wise loads along k).
+    if (sA.col == 1) {
+        p.a_mode = TROP_LOAD_K_CONTIG;
+        p.a_vec = aligned16(A) && sA.row % 4 == 0 && sA.batch % 4 == 0;
+    } else if (sA.row == 1) {
+        p.a_mode = TROP_LOAD_MN_CONTIG;
+        p.a_vec = aligned16(A) && sA.col % 4 == 0 && sA.batch % 4 == 0;
+    } else {
+        p.a_mode = TROP_LOAD_K_CONTIG;
+        p.a_vec = 0;
+    }
+    // B: row-major (j unit-stride), column-major (k unit-stride), or neither.
+    if (sB.col == 1) {
+        p.b_mode = TROP_LOAD_MN_CONTIG;
+        p.b_vec = aligned16(B) && sB.row % 4 == 0 && sB.batch % 4 == 0;
+    } else if (sB.row == 1) {
+        p.b_mode = TROP_LOAD_K_CONTIG;
+        p.b_vec = aligned16(B) && sB.col % 4 == 0 && sB.batch % 4 == 0;
+    } else {
+        p.b_mode = TROP_LOAD_K_CONTIG;
+        p.b_vec = 0;
+    }
+    const int64_t tm = (m + 63) / 64, tn = (n + 63) / 64;
+    if (tm > INT32_MAX || tn > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "matrix too large");
+    p.tiles_m = (int32_t)tm;
+    p.tiles_n = (int32_t)tn;
+    p.swizzle = env_flag("TROPICAL_NO_XCD_SWIZZLE") ? 0 : 1;
+    int64_t total = tm * tn * batch;
+    uint32_t grid = total > kMaxGrid ? kMaxGrid : (uint32_t)total;
+    return launch(dev, (KernelId)(K_GEMM_TILED_MAXPLUS_F32 + ri), TROP_K_GEMM_TILED, grid, 256, &p,
+                  stream);
+}
+
+}  // namespace trop
+
+extern "C" trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_dtype dtype,
+                                                     const void* A, trop_strides sA, const void* B,
+                                                     trop_strides sB, void* C, trop_strides sC,
+                                                     int32_t* argmax, int64_t m, int64_t n, int64_t k,
+                                                     int64_t batch, void* stream) {
+    using namespace trop;
+    trop_status st = check_gemm_args(semiring, dtype, sA, sB, sC, m, n, k, batch);
+    if (st != TROP_OK) return st;
+    if (m == 0 || n == 0 || batch == 0) return ok();
+    int dev = -1;
+    st = current_device(&dev);
+    if (st != TROP_OK) return st;
+
+    int64_t spanA = 0, spanB = 0, spanC = 0;
+    if (k > 0) {
+        const int64_t eA[3] = {batch, m, k}, sa[3] = {sA.batch, sA.row, sA.col};
+        const int64_t eB[3] = {batch, k, n}, sb[3] = {sB.batch, sB.row, sB.col};
+        if (!max_offset(3, eA, sa, &spanA) || !max_offset(3, eB, sb, &spanB))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "operand extent overflows");
+        ++spanA;
+        ++spanB;
+        st = check_device_span(A, dev, spanA, 4, "A");
+        if (st != TROP_OK) return st;
+        st = check_device_span(B, dev, spanB, 4, "B");
+        if (st != TROP_OK) return st;
+    }
+    const int64_t eC[3] = {batch, m, n}, sc[3] = {sC.batch, sC.row, sC.col};
+    if (!max_offset(3, eC, sc, &spanC)) return fail(TROP_ERR_INVALID_ARGUMENT, "C extent overflows");
+    ++spanC;
+    st = check_device_span(C, dev, spanC, 4, "C");
+    if (st != TROP_OK) return st;
+    if (argmax) {
+        st = check_device_span(argmax, dev, spanC, 4, "argmax");
+        if (st != TROP_OK) return st;
+    }
+    st = run_gemm(dev, semiring, dtype, A, sA, B, sB, C, sC, argmax, m, n, k, batch,
+                  static_cast<hipStream_t>(stream));
+    return st == TROP_OK ? ok() : st;
+}

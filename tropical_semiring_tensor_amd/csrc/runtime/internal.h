@@ -1,0 +1,97 @@
+// Internal interfaces of the host runtime of libtropical.so.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../../include/tropical.h"
+#include "../kernel_params.h"
+
+namespace trop {
+
+// ---- errors and counters (status.cpp) ------------------------------------
+trop_status fail(trop_status st, const std::string& msg);  // records the text
+trop_status ok();                                         // clears the text
+trop_status hip_fail(hipError_t e, const char* what);
+void count_launch(trop_kernel_family fam);
+
+// ---- kernels and the per-device module cache (module.cpp) ----------------
+enum KernelId : int {
+    K_GEMM_TILED_MAXPLUS_F32 = 0,
+    K_GEMM_TILED_MINPLUS_F32,
+    K_GEMM_TILED_MAXMUL_F32,
+    K_GEMM_TILED_MAXPLUS_I32,
+    K_GEMM_TILED_MINPLUS_I32,
+    K_GEMM_SIMPLE_MAXPLUS_F32,
+    K_GEMM_SIMPLE_MINPLUS_F32,
+    K_GEMM_SIMPLE_MAXMUL_F32,
+    K_GEMM_SIMPLE_MAXPLUS_I32,
+    K_GEMM_SIMPLE_MINPLUS_I32,
+    K_GATHER_REDUCE_MAXPLUS_F32,
+    K_GATHER_REDUCE_MINPLUS_F32,
+    K_GATHER_REDUCE_MAXMUL_F32,
+    K_GATHER_REDUCE_MAXPLUS_I32,
+    K_GATHER_REDUCE_MINPLUS_I32,
+    K_FILL,
+    K_GATHER_COPY,
+    K_GATHER_TILED,
+    K_GATHER_NAIVE,
+    K_COUNT
+};
+const char* kernel_name(KernelId id);
+
+// Index of (semiring, dtype) among the five supported pairs, or -1.
+int ring_index(trop_semiring sr, trop_dtype dt);
+
+// Current device, with the module loaded on it.  On failure returns an
+// error status (message recorded) and caches nothing.
+trop_status current_device(int* dev);
+trop_status ensure_module(int dev);
+
+// Enqueue kernel `id` (one by-value argument block) on `stream`.
+trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,
+                   void* params, hipStream_t stream);
+
+// ---- argument checks (validate.cpp) --------------------------------------
+// `p` must be device memory of `dev` holding at least `span_elems` elements
+// of `elem_bytes` from p on (span_elems == 0: only the pointer is checked).
+trop_status check_device_span(const void* p, int dev, int64_t span_elems, size_t elem_bytes,
+                              const char* what);
+// Largest element offset reached by sum_d (extent_d - 1) * stride_d, with
+// overflow detection; extents must be >= 1.
+bool max_offset(int n, const int64_t* extent, const int64_t* stride, int64_t* out);
+
+// ---- gather planning (gather.cpp) ----------------------------------------
+enum GatherPath { GP_NONE = 0, GP_COPY, GP_TILED, GP_NAIVE, GP_REDUCE };
+struct GatherPlan {
+    TropGatherParams params;
+    GatherPath path;
+    int64_t in_span;  // elements of input reached (max offset + 1), 0 if empty
+};
+// Output axes with extents `oshape` and input strides `ostride`; reduce axes
+// likewise.  Builds the normalised plan (size-1 axes dropped, contiguous
+// neighbours merged) and picks the kernel path.
+trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride, int nred,
+                        const int64_t* rshape, const int64_t* rstride, GatherPlan* plan);
+const char* gather_path_name(GatherPath p);
+// Enqueue a planned gather (pointers are set here; checks done by caller).
+trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* const* in,
+                       void* const* out, trop_semiring sr, trop_dtype dt, hipStream_t stream);
+
+// Label-based diagonal / trace gather into a plan (used by the public call
+// and by the contraction driver).
+trop_status plan_diag(int in_ndim, const int64_t* in_shape, const int64_t* in_strides,
+                      const int32_t* in_labels, int out_ndim, const int32_t* out_labels,
+                      GatherPlan* plan);
+
+// ---- GEMM (gemm.cpp) -------------------------------------------------------
+// Enqueue without re-validating pointers (used by the contraction driver).
+trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
+                     const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
+                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream);
+trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, trop_strides sB,
+                            trop_strides sC, int64_t m, int64_t n, int64_t k, int64_t batch);
+
+}  // namespace trop

@@ -1,0 +1,165 @@
+// Per-device cache of the kernel module.
+//
+// omeinsum-rs issue #52 ("GPU tropical path: keep tensors device-resident +
+// device-side permute") traces part of the GPU slowdown to the driver
+// context and kernel module being rebuilt for every contraction node
+// ("Current state in the code", "Proposed plan" step 1) and asks for them to
+// be created once ("Compilation & caching", "Acceptance criteria");
+// tropical-gemm PR #35 keeps one context per device (Key changes).  Here the
+// gfx950 code object is compiled ahead of time, embedded in this library,
+// loaded with hipModuleLoadData at most once per process and device, and
+// every entry point is looked up once.  A failed load caches nothing, so a
+// later call tries again.
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+// Embedded code object (co_blob.S).
+extern "C" const unsigned char trop_code_object[];
+extern "C" const unsigned char trop_code_object_end[];
+
+namespace trop {
+
+extern std::atomic<uint64_t> g_module_loads;
+
+static const char* const kNames[K_COUNT] = {
+    "trop_gemm_tiled_maxplus_f32",   "trop_gemm_tiled_minplus_f32",
+    "trop_gemm_tiled_maxmul_f32",    "trop_gemm_tiled_maxplus_i32",
+    "trop_gemm_tiled_minplus_i32",   "trop_gemm_simple_maxplus_f32",
+    "trop_gemm_simple_minplus_f32",  "trop_gemm_simple_maxmul_f32",
+    "trop_gemm_simple_maxplus_i32",  "trop_gemm_simple_minplus_i32",
+    "trop_gather_reduce_maxplus_f32", "trop_gather_reduce_minplus_f32",
+    "trop_gather_reduce_maxmul_f32", "trop_gather_reduce_maxplus_i32",
+    "trop_gather_reduce_minplus_i32", "trop_fill",
+    "trop_gather_copy",              "trop_gather_tiled",
+    "trop_gather_naive",
+};
+
+const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
+
+int ring_index(trop_semiring sr, trop_dtype dt) {
+    if (dt == TROP_F32) {
+        if (sr == TROP_MAX_PLUS) return 0;
+        if (sr == TROP_MIN_PLUS) return 1;
+        if (sr == TROP_MAX_MUL) return 2;
+    } else if (dt == TROP_I32) {
+        if (sr == TROP_MAX_PLUS) return 3;
+        if (sr == TROP_MIN_PLUS) return 4;
+    }
+    return -1;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceModule {
+    hipModule_t module = nullptr;
+    hipFunction_t fn[K_COUNT] = {};
+};
+
+std::mutex g_mu;
+std::atomic<DeviceModule*> g_dev[kMaxDevices];
+
+// The code object to load: the embedded one, or (for testing the failure
+// path) the file named by TROPICAL_CODE_OBJECT.
+bool code_object_image(std::vector<unsigned char>& storage, const void** image, std::string* err) {
+    const char* path = std::getenv("TROPICAL_CODE_OBJECT");
+    if (!path || !*path) {
+        *image = trop_code_object;
+        return true;
+    }
+    FILE* f = std::fopen(path, "rb");
+    if (!f) {
+        *err = std::string("cannot open TROPICAL_CODE_OBJECT=") + path;
+        return false;
+    }
+    unsigned char buf[65536];
+    size_t got;
+    while ((got = std::fread(buf, 1, sizeof(buf), f)) > 0) storage.insert(storage.end(), buf, buf + got);
+    std::fclose(f);
+    storage.push_back(0);
+    *image = storage.data();
+    return true;
+}
+
+}  // namespace
+
+trop_status current_device(int* dev) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (*dev < 0 || *dev >= kMaxDevices) return fail(TROP_ERR_INVALID_ARGUMENT, "device index out of range");
+    return ensure_module(*dev);
+}
+
+trop_status ensure_module(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(TROP_ERR_INVALID_ARGUMENT, "device index out of range");
+    if (g_dev[dev].load(std::memory_order_acquire)) return TROP_OK;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_dev[dev].load(std::memory_order_acquire)) return TROP_OK;
+
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev) {
+        e = hipSetDevice(dev);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    }
+    std::vector<unsigned char> storage;
+    const void* image = nullptr;
+    std::string err;
+    trop_status st = TROP_OK;
+    DeviceModule* dm = nullptr;
+    if (!code_object_image(storage, &image, &err)) {
+        st = fail(TROP_ERR_HIP, err);
+    } else {
+        dm = new DeviceModule;
+        e = hipModuleLoadData(&dm->module, image);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "hipModuleLoadData (gfx950 code object)");
+        } else {
+            g_module_loads.fetch_add(1);
+            for (int i = 0; i < K_COUNT && st == TROP_OK; ++i) {
+                e = hipModuleGetFunction(&dm->fn[i], dm->module, kNames[i]);
+                if (e != hipSuccess) st = hip_fail(e, kNames[i]);
+            }
+            if (st != TROP_OK) (void)hipModuleUnload(dm->module);
+        }
+    }
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (st != TROP_OK) {
+        delete dm;
+        return st;
+    }
+    g_dev[dev].store(dm, std::memory_order_release);
+    return TROP_OK;
+}
+
+trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,
+                   void* params, hipStream_t stream) {
+    DeviceModule* dm = g_dev[dev].load(std::memory_order_acquire);
+    if (!dm) return fail(TROP_ERR_HIP, "kernel module not loaded on this device");
+    if (grid == 0) return TROP_OK;
+    void* args[] = {params};
+    hipError_t e = hipModuleLaunchKernel(dm->fn[id], grid, 1, 1, block, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return hip_fail(e, kNames[id]);
+    count_launch(fam);
+    return TROP_OK;
+}
+
+}  // namespace trop
+
+extern "C" trop_status tropical_init(int device) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return trop::hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= n)
+        return trop::fail(TROP_ERR_INVALID_ARGUMENT, "tropical_init: no device " + std::to_string(device));
+    trop_status st = trop::ensure_module(device);
+    return st == TROP_OK ? trop::ok() : st;
+}
