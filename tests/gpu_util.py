@@ -35,6 +35,10 @@ def assert_equal(got, want, what=""):
 def gpu_gemm(tb, sr, A, B, argmax=True, c_layout="row"):
     """Run the HIP GEMM on CPU tensors A (b,m,k), B (b,k,n) (any strides:
     the device copies keep the same strides).  Returns numpy (C, I)."""
+    if A.dim() == 2:
+        A = A.unsqueeze(0)
+    if B.dim() == 2:
+        B = B.unsqueeze(0)
     Ad = device_copy(A)
     Bd = device_copy(B)
     batch, m, _ = Ad.shape

@@ -25,12 +25,13 @@
 //    strict-compare scan produces them; an output that nothing beat keeps
 //    the zero element and argmax 0.
 //
-// Tiling: 256 threads (4 waves), a 64x64 output tile per workgroup, a 4x4
-// register tile per thread, K staged in BK = 16 slices through LDS.  LDS
-// holds A as [k][i] and B as [k][j] (row length 64 + 4 words of padding),
-// whatever the global layout: k-contiguous operands are transposed on the
-// way in.  Global loads of the next slice are issued into registers while
-// the current slice computes.
+// Tiling: 256 threads (4 waves), a 64x64 output tile per workgroup, 16
+// outputs per thread (rows 2ty, 2ty+1, 2ty+32, 2ty+33 and the same pattern
+// of columns, see own()), K staged in BK = 16 slices through LDS.  LDS holds A as [k][i] and B as [k][j] (row
+// length 64 + 4 words of padding), whatever the global layout:
+// k-contiguous operands are transposed on the way in.  Global loads of the next slice are issued into registers while
+// the current slice computes; the next slice is written to LDS at the start
+// of the current one, so one barrier per slice suffices.
 #pragma once
 #include "ring.h"
 
@@ -43,7 +44,22 @@ constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_TM = 4;
 constexpr int GEMM_TN = 4;
 constexpr int GEMM_LDP = 64 + 4;  // LDS row length (words)
-constexpr int GEMM_KBLK = 256;    // K terms resident in LDS per block
+#ifndef TROP_GEMM_KBLK
+#define TROP_GEMM_KBLK 128
+#endif
+// K terms resident in LDS per block.  Larger blocks resolve less often but
+// use more LDS (2 x KBLK x 68 words): 128 leaves room for two workgroups
+// (eight waves) per CU.
+constexpr int GEMM_KBLK = TROP_GEMM_KBLK;
+// Words per LDS slice slot.  Slots are skewed by 4 words so that the same
+// (k, row) of different slices falls in different LDS banks: the resolve
+// reads one slice per lane, chosen by that lane's own data.
+constexpr int GEMM_SLOT = GEMM_BK * GEMM_LDP + 4;
+
+// Offset of a thread's r-th row (or column) from 2*ty (2*tx): the thread owns
+// the pairs {2t, 2t+1} and {2t+32, 2t+33}, so one ds_read2_b64 fetches its 4
+// values at one k, and lanes that read different slices hit different banks.
+__device__ __forceinline__ constexpr int own(int r) { return (r & 1) + 32 * (r >> 1); }
 
 // Bijective remap of the linear workgroup id so that each of the 8 XCDs
 // (which receive workgroups round-robin) owns one contiguous range of
@@ -136,7 +152,7 @@ struct GemmTile {
     // [k][j]; k-contiguous operands are transposed here.
     static __device__ __forceinline__ void store(const Loader& L, T* S, int s, int tid,
                                                  const T (&r)[4]) {
-        T* dst = S + s * GEMM_BK * GEMM_LDP;
+        T* dst = S + s * GEMM_SLOT;
         if (L.mn_contig) {
             const V v = {r[0], r[1], r[2], r[3]};
             *reinterpret_cast<V*>(dst + (tid >> 4) * GEMM_LDP + (tid & 15) * 4) = v;
@@ -154,8 +170,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using V = vec4<T>;
     using G = GemmTile<SR, T>;
     constexpr int NST = GEMM_KBLK / GEMM_BK;  // slices per resident K-block
-    __shared__ __attribute__((aligned(16))) T As[GEMM_KBLK * GEMM_LDP];
-    __shared__ __attribute__((aligned(16))) T Bs[GEMM_KBLK * GEMM_LDP];
+    __shared__ __attribute__((aligned(16))) T As[NST * GEMM_SLOT];
+    __shared__ __attribute__((aligned(16))) T Bs[NST * GEMM_SLOT];
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
@@ -204,24 +220,56 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
         int64_t block_k0 = 0;  // first k of the resident block
         for (int g = 0; g < nslices; ++g) {
             const int s = g % NST;
-            const T* as = As + s * GEMM_BK * GEMM_LDP + ty * 4;
-            const T* bs = Bs + s * GEMM_BK * GEMM_LDP + tx * 4;
+            const bool last = (g + 1 == nslices);
+            const bool boundary = last || ((g + 1) % NST == 0);
+            // Slice g+1 arrived in registers during slice g-1: park it in
+            // its LDS slot now (inside a block the slot is free) and start
+            // fetching slice g+2, so both overlap this slice's compute.
+            if (!boundary) {
+                G::store(la, As, s + 1, tid, ra);
+                G::store(lb, Bs, s + 1, tid, rb);
+                if (g + 2 < nslices) {
+                    la.load(g + 2, R::zero(), ra);
+                    lb.load(g + 2, R::one(), rb);
+                }
+            }
+
+            const T* as = As + s * GEMM_SLOT + 2 * ty;
+            const T* bs = Bs + s * GEMM_SLOT + 2 * tx;
             T run[GEMM_TM][GEMM_TN];
 #pragma unroll
             for (int r = 0; r < GEMM_TM; ++r)
 #pragma unroll
                 for (int c = 0; c < GEMM_TN; ++c) run[r][c] = best[r][c];
+            // fragments of term pairs, double-buffered: pair p+1 is read
+            // from LDS while pair p computes
+            T fa[2][2][GEMM_TM], fb[2][2][GEMM_TN];
 #pragma unroll
-            for (int kk = 0; kk < GEMM_BK; kk += 2) {
-                const V a0 = *reinterpret_cast<const V*>(as + kk * GEMM_LDP);
-                const V b0 = *reinterpret_cast<const V*>(bs + kk * GEMM_LDP);
-                const V a1 = *reinterpret_cast<const V*>(as + (kk + 1) * GEMM_LDP);
-                const V b1 = *reinterpret_cast<const V*>(bs + (kk + 1) * GEMM_LDP);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int r = 0; r < GEMM_TM; ++r) fa[0][h][r] = as[h * GEMM_LDP + own(r)];
+#pragma unroll
+                for (int c = 0; c < GEMM_TN; ++c) fb[0][h][c] = bs[h * GEMM_LDP + own(c)];
+            }
+#pragma unroll
+            for (int pr = 0; pr < GEMM_BK / 2; ++pr) {
+                const int cur = pr & 1, nxt = cur ^ 1;
+                if (pr + 1 < GEMM_BK / 2) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int kk = 2 * pr + 2 + h;
+#pragma unroll
+                        for (int r = 0; r < GEMM_TM; ++r) fa[nxt][h][r] = as[kk * GEMM_LDP + own(r)];
+#pragma unroll
+                        for (int c = 0; c < GEMM_TN; ++c) fb[nxt][h][c] = bs[kk * GEMM_LDP + own(c)];
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < GEMM_TM; ++r)
 #pragma unroll
                     for (int c = 0; c < GEMM_TN; ++c)
-                        run[r][c] = R::add3(run[r][c], R::mul(a0[r], b0[c]), R::mul(a1[r], b1[c]));
+                        run[r][c] = R::add3(run[r][c], R::mul(fa[cur][0][r], fb[cur][0][c]),
+                                            R::mul(fa[cur][1][r], fb[cur][1][c]));
             }
 #pragma unroll
             for (int r = 0; r < GEMM_TM; ++r)
@@ -231,53 +279,63 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                     best[r][c] = run[r][c];
                 }
 
-            const bool last = (g + 1 == nslices);
-            const bool boundary = last || ((g + 1) % NST == 0);
             if (boundary) {
                 // Resolve the outputs whose best improved inside this block:
-                // the first term of the winning slice equal to the best.
+                // the first term of the winning slice equal to the best.  The
+                // four outputs of a row are scanned together (independent
+                // chains, no branch); an output that did not improve scans
+                // slot 0 and keeps its earlier result.
 #pragma unroll
-                for (int r = 0; r < GEMM_TM; ++r)
+                for (int r = 0; r < GEMM_TM; ++r) {
+                    const T* ac[GEMM_TN];
+                    const T* bc[GEMM_TN];
+                    int found[GEMM_TN];
 #pragma unroll
                     for (int c = 0; c < GEMM_TN; ++c) {
-                        if (win[r][c] >= 0) {
-                            const int kb = win[r][c] * GEMM_BK;
-                            const T* ac = As + kb * GEMM_LDP + ty * 4 + r;
-                            const T* bc = Bs + kb * GEMM_LDP + tx * 4 + c;
-                            int found = GEMM_BK - 1;
-#pragma unroll
-                            for (int kk = GEMM_BK - 1; kk >= 0; --kk) {
-                                const T term = R::mul(ac[kk * GEMM_LDP], bc[kk * GEMM_LDP]);
-                                found = (term == best[r][c]) ? kk : found;
-                            }
-                            idx[r][c] = (int)(block_k0 + kb + found);
-                            cv[r][c] = R::mul(ac[found * GEMM_LDP], bc[found * GEMM_LDP]);
-                            win[r][c] = -1;
-                        }
+                        const int w = win[r][c] < 0 ? 0 : win[r][c];
+                        ac[c] = As + w * GEMM_SLOT + 2 * ty + own(r);
+                        bc[c] = Bs + w * GEMM_SLOT + 2 * tx + own(c);
+                        found[c] = GEMM_BK - 1;
                     }
-                block_k0 += GEMM_KBLK;
-            }
-            if (!last) {
-                if (boundary) __syncthreads();  // the block's LDS is free again
-                G::store(la, As, (g + 1) % NST, tid, ra);
-                G::store(lb, Bs, (g + 1) % NST, tid, rb);
-                if (g + 2 < nslices) {
-                    la.load(g + 2, R::zero(), ra);
-                    lb.load(g + 2, R::one(), rb);
+#pragma unroll
+                    for (int kk = GEMM_BK - 1; kk >= 0; --kk)
+#pragma unroll
+                        for (int c = 0; c < GEMM_TN; ++c) {
+                            const T term = R::mul(ac[c][kk * GEMM_LDP], bc[c][kk * GEMM_LDP]);
+                            found[c] = (term == best[r][c]) ? kk : found[c];
+                        }
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; ++c) {
+                        const T term = R::mul(ac[c][found[c] * GEMM_LDP], bc[c][found[c] * GEMM_LDP]);
+                        const bool hit = win[r][c] >= 0;
+                        idx[r][c] = hit ? (int)(block_k0 + win[r][c] * GEMM_BK + found[c]) : idx[r][c];
+                        cv[r][c] = hit ? term : cv[r][c];
+                        win[r][c] = -1;
+                    }
                 }
-                __syncthreads();
+                block_k0 += GEMM_KBLK;
+                if (!last) {
+                    __syncthreads();  // every wave is done with this block's LDS
+                    G::store(la, As, 0, tid, ra);
+                    G::store(lb, Bs, 0, tid, rb);
+                    if (g + 2 < nslices) {
+                        la.load(g + 2, R::zero(), ra);
+                        lb.load(g + 2, R::one(), rb);
+                    }
+                }
             }
+            if (!last) __syncthreads();  // slice g+1 is visible in LDS
         }
 
         T* __restrict__ C = static_cast<T*>(p.C) + b * p.sc_batch;
         int32_t* __restrict__ I = p.argmax ? p.argmax + b * p.sc_batch : nullptr;
 #pragma unroll
         for (int r = 0; r < GEMM_TM; ++r) {
-            const int64_t i = row0 + ty * 4 + r;
+            const int64_t i = row0 + 2 * ty + own(r);
             if (i >= p.m) continue;
 #pragma unroll
             for (int c = 0; c < GEMM_TN; ++c) {
-                const int64_t j = col0 + tx * 4 + c;
+                const int64_t j = col0 + 2 * tx + own(c);
                 if (j >= p.n) continue;
                 const int64_t off = i * p.sc_row + j * p.sc_col;
                 C[off] = cv[r][c];
