@@ -96,25 +96,27 @@ struct GemmTile {
         int64_t mn_str;   // stride of the row / column axis
         int64_t k_str;    // stride of the k axis
         bool mn_contig;
-        bool fast_mn;     // all 4 (or this thread's 1) row / column in range
         bool vec;         // 16-byte loads allowed
 
-        __device__ __forceinline__ void load(int g, T pad, T (&r)[4]) const {
-            const int64_t k = kfirst + (int64_t)g * GEMM_BK;
-            const bool full = fast_mn && (mn_contig ? (k < k_lim) : (k + 3 < k_lim));
-            if (full && vec) {
-                const V v = *reinterpret_cast<const V*>(base + g * step);
-                r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
-            } else if (full) {
-                const T* q = base + g * step;
+        // `full`: the whole slice of the whole tile is in range (a uniform
+        // condition, so the common case is unguarded and branch-free).
+        __device__ __forceinline__ void load(int g, bool full, T pad, T (&r)[4]) const {
+            const T* q = base + (int64_t)g * step;
+            if (full) {
+                if (vec) {
+                    const V v = *reinterpret_cast<const V*>(q);
+                    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = q[e * inner];
+                    for (int e = 0; e < 4; ++e) r[e] = q[e * inner];
+                }
             } else {
+                const int64_t k = kfirst + (int64_t)g * GEMM_BK;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t kk = mn_contig ? k : k + e;
                     const int64_t mm = mn_contig ? mn0 + e : mn0;
-                    r[e] = (kk < k_lim && mm < mn_lim) ? base[g * step + e * inner] : pad;
+                    r[e] = (kk < k_lim && mm < mn_lim) ? q[e * inner] : pad;
                 }
             }
         }
@@ -137,12 +139,10 @@ struct GemmTile {
             L.kfirst = tid >> 4;
             L.mn0 = mn_start + (tid & 15) * 4;
             L.inner = str_mn;
-            L.fast_mn = L.mn0 + 3 < mn_lim;
         } else {
             L.kfirst = (tid & 3) * 4;
             L.mn0 = mn_start + (tid >> 2);
             L.inner = str_k;
-            L.fast_mn = L.mn0 < mn_lim;
         }
         L.base = X + L.mn0 * str_mn + L.kfirst * str_k;
         return L;
@@ -150,10 +150,10 @@ struct GemmTile {
 
     // Write a slice held in registers into LDS slot `s`: A as [k][i], B as
     // [k][j]; k-contiguous operands are transposed here.
-    static __device__ __forceinline__ void store(const Loader& L, T* S, int s, int tid,
+    static __device__ __forceinline__ void store(bool mn_contig, T* S, int s, int tid,
                                                  const T (&r)[4]) {
         T* dst = S + s * GEMM_SLOT;
-        if (L.mn_contig) {
+        if (mn_contig) {
             const V v = {r[0], r[1], r[2], r[3]};
             *reinterpret_cast<V*>(dst + (tid >> 4) * GEMM_LDP + (tid & 15) * 4) = v;
         } else {
@@ -164,11 +164,28 @@ struct GemmTile {
     }
 };
 
+// Batch entry and output-tile origin of logical tile L.
+struct TileCoord {
+    int64_t b, row0, col0;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
+                                                int64_t total) {
+    const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
+    const int64_t t = lg % tiles;
+    return {lg / tiles, (t / p.tiles_n) * GEMM_BM, (t % p.tiles_n) * GEMM_BN};
+}
+
+// The tiled kernel.  A workgroup walks the tiles L = blockIdx.x,
+// blockIdx.x + gridDim.x, ... as one stream of (tile, K-slice) steps, so the
+// fetch of a tile's first slice overlaps the previous tile's last slice,
+// argmax resolve and stores: only the first tile of a workgroup pays the
+// latency of starting up.
 template <int SR, typename T>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
-    using V = vec4<T>;
     using G = GemmTile<SR, T>;
+    using Loader = typename G::Loader;
     constexpr int NST = GEMM_KBLK / GEMM_BK;  // slices per resident K-block
     __shared__ __attribute__((aligned(16))) T As[NST * GEMM_SLOT];
     __shared__ __attribute__((aligned(16))) T Bs[NST * GEMM_SLOT];
@@ -178,20 +195,66 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     const int64_t total = tiles * p.batch;
     const int nslices = (int)((p.k + GEMM_BK - 1) / GEMM_BK);
+    const int full_slices = (int)(p.k / GEMM_BK);
+    const int64_t stride = gridDim.x;
 
-    for (int64_t L = blockIdx.x; L < total; L += gridDim.x) {
-        const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
-        const int64_t b = lg / tiles;
-        const int64_t t = lg % tiles;
-        const int64_t row0 = (t / p.tiles_n) * GEMM_BM;
-        const int64_t col0 = (t % p.tiles_n) * GEMM_BN;
-        const T* __restrict__ A = static_cast<const T*>(p.A) + b * p.sa_batch;
-        const T* __restrict__ B = static_cast<const T*>(p.B) + b * p.sb_batch;
+    int64_t cL = blockIdx.x;  // tile being computed
+    if (cL >= total || nslices == 0) return;  // K = 0 is handled by the fill kernel
 
-        T best[GEMM_TM][GEMM_TN];
-        T cv[GEMM_TM][GEMM_TN];
-        int win[GEMM_TM][GEMM_TN];
-        int idx[GEMM_TM][GEMM_TN];
+    // Fetch cursor: the (tile, slice) whose data was last requested into
+    // registers, and the loaders of that tile.
+    int64_t fL = cL;
+    int fg = 0;
+    TileCoord ft = tile_coord(p, fL, tiles, total);
+    auto make_loaders = [&](const TileCoord& tc, Loader& la, Loader& lb, bool& fa, bool& fb) {
+        la = G::make(static_cast<const T*>(p.A) + tc.b * p.sa_batch, p.a_mode, p.a_vec, tc.row0, p.m,
+                     p.k, p.sa_row, p.sa_col, tid);
+        lb = G::make(static_cast<const T*>(p.B) + tc.b * p.sb_batch, p.b_mode, p.b_vec, tc.col0, p.n,
+                     p.k, p.sb_col, p.sb_row, tid);
+        fa = tc.row0 + GEMM_BM <= p.m;
+        fb = tc.col0 + GEMM_BN <= p.n;
+    };
+    Loader la, lb;
+    bool fa_full, fb_full;
+    make_loaders(ft, la, lb, fa_full, fb_full);
+    bool fetch_valid = true;
+    // advance the fetch cursor by one step and request that slice
+    T ra[4], rb[4];
+    auto fetch_next = [&]() {
+        ++fg;
+        if (fg == nslices) {
+            fg = 0;
+            fL += stride;
+            fetch_valid = fL < total;
+            if (fetch_valid) {
+                ft = tile_coord(p, fL, tiles, total);
+                make_loaders(ft, la, lb, fa_full, fb_full);
+            }
+        }
+        if (fetch_valid) {
+            la.load(fg, fa_full && fg < full_slices, R::zero(), ra);
+            lb.load(fg, fb_full && fg < full_slices, R::one(), rb);
+        }
+    };
+
+    // prologue: the first slice goes to LDS slot 0, the step after it to
+    // registers (both requests in flight together)
+    {
+        T r0a[4], r0b[4];
+        la.load(0, fa_full && 0 < full_slices, R::zero(), r0a);
+        lb.load(0, fb_full && 0 < full_slices, R::one(), r0b);
+        fetch_next();
+        G::store(la.mn_contig, As, 0, tid, r0a);
+        G::store(lb.mn_contig, Bs, 0, tid, r0b);
+    }
+    __syncthreads();
+
+    TileCoord ct = tile_coord(p, cL, tiles, total);
+    T best[GEMM_TM][GEMM_TN];
+    T cv[GEMM_TM][GEMM_TN];
+    int win[GEMM_TM][GEMM_TN];
+    int idx[GEMM_TM][GEMM_TN];
+    auto reset_outputs = [&]() {
 #pragma unroll
         for (int r = 0; r < GEMM_TM; ++r)
 #pragma unroll
@@ -201,148 +264,151 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 win[r][c] = -1;
                 idx[r][c] = 0;
             }
+    };
+    reset_outputs();
 
-        const typename G::Loader la =
-            G::make(A, p.a_mode, p.a_vec, row0, p.m, p.k, p.sa_row, p.sa_col, tid);
-        const typename G::Loader lb =
-            G::make(B, p.b_mode, p.b_vec, col0, p.n, p.k, p.sb_col, p.sb_row, tid);
-        T ra[4], rb[4];
-        la.load(0, R::zero(), ra);
-        lb.load(0, R::one(), rb);
-        G::store(la, As, 0, tid, ra);
-        G::store(lb, Bs, 0, tid, rb);
-        __syncthreads();
-        if (nslices > 1) {
-            la.load(1, R::zero(), ra);
-            lb.load(1, R::one(), rb);
+    int g = 0;           // slice of the current tile
+    int block_k0 = 0;    // first k of the resident block
+    for (;;) {
+        const int s = g % NST;
+        const bool last = (g + 1 == nslices);
+        const bool boundary = last || ((g + 1) % NST == 0);
+        // The registers hold slice g+1 of this tile: inside a block its LDS
+        // slot is free, so park it now and fetch the step after it; both
+        // overlap this slice's compute.
+        if (!boundary) {
+            G::store(la.mn_contig, As, s + 1, tid, ra);
+            G::store(lb.mn_contig, Bs, s + 1, tid, rb);
+            fetch_next();
         }
 
-        int64_t block_k0 = 0;  // first k of the resident block
-        for (int g = 0; g < nslices; ++g) {
-            const int s = g % NST;
-            const bool last = (g + 1 == nslices);
-            const bool boundary = last || ((g + 1) % NST == 0);
-            // Slice g+1 arrived in registers during slice g-1: park it in
-            // its LDS slot now (inside a block the slot is free) and start
-            // fetching slice g+2, so both overlap this slice's compute.
-            if (!boundary) {
-                G::store(la, As, s + 1, tid, ra);
-                G::store(lb, Bs, s + 1, tid, rb);
-                if (g + 2 < nslices) {
-                    la.load(g + 2, R::zero(), ra);
-                    lb.load(g + 2, R::one(), rb);
+        const T* as = As + s * GEMM_SLOT + 2 * ty;
+        const T* bs = Bs + s * GEMM_SLOT + 2 * tx;
+        T run[GEMM_TM][GEMM_TN];
+#pragma unroll
+        for (int r = 0; r < GEMM_TM; ++r)
+#pragma unroll
+            for (int c = 0; c < GEMM_TN; ++c) run[r][c] = best[r][c];
+        // fragments of term pairs, double-buffered: pair p+1 is read from
+        // LDS while pair p computes
+        T fa[2][2][GEMM_TM], fb[2][2][GEMM_TN];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int r = 0; r < GEMM_TM; ++r) fa[0][h][r] = as[h * GEMM_LDP + own(r)];
+#pragma unroll
+            for (int c = 0; c < GEMM_TN; ++c) fb[0][h][c] = bs[h * GEMM_LDP + own(c)];
+        }
+#pragma unroll
+        for (int pr = 0; pr < GEMM_BK / 2; ++pr) {
+            const int cur = pr & 1, nxt = cur ^ 1;
+            if (pr + 1 < GEMM_BK / 2) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kk = 2 * pr + 2 + h;
+#pragma unroll
+                    for (int r = 0; r < GEMM_TM; ++r) fa[nxt][h][r] = as[kk * GEMM_LDP + own(r)];
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; ++c) fb[nxt][h][c] = bs[kk * GEMM_LDP + own(c)];
                 }
-            }
-
-            const T* as = As + s * GEMM_SLOT + 2 * ty;
-            const T* bs = Bs + s * GEMM_SLOT + 2 * tx;
-            T run[GEMM_TM][GEMM_TN];
-#pragma unroll
-            for (int r = 0; r < GEMM_TM; ++r)
-#pragma unroll
-                for (int c = 0; c < GEMM_TN; ++c) run[r][c] = best[r][c];
-            // fragments of term pairs, double-buffered: pair p+1 is read
-            // from LDS while pair p computes
-            T fa[2][2][GEMM_TM], fb[2][2][GEMM_TN];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int r = 0; r < GEMM_TM; ++r) fa[0][h][r] = as[h * GEMM_LDP + own(r)];
-#pragma unroll
-                for (int c = 0; c < GEMM_TN; ++c) fb[0][h][c] = bs[h * GEMM_LDP + own(c)];
-            }
-#pragma unroll
-            for (int pr = 0; pr < GEMM_BK / 2; ++pr) {
-                const int cur = pr & 1, nxt = cur ^ 1;
-                if (pr + 1 < GEMM_BK / 2) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int kk = 2 * pr + 2 + h;
-#pragma unroll
-                        for (int r = 0; r < GEMM_TM; ++r) fa[nxt][h][r] = as[kk * GEMM_LDP + own(r)];
-#pragma unroll
-                        for (int c = 0; c < GEMM_TN; ++c) fb[nxt][h][c] = bs[kk * GEMM_LDP + own(c)];
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < GEMM_TM; ++r)
-#pragma unroll
-                    for (int c = 0; c < GEMM_TN; ++c)
-                        run[r][c] = R::add3(run[r][c], R::mul(fa[cur][0][r], fb[cur][0][c]),
-                                            R::mul(fa[cur][1][r], fb[cur][1][c]));
             }
 #pragma unroll
             for (int r = 0; r < GEMM_TM; ++r)
 #pragma unroll
-                for (int c = 0; c < GEMM_TN; ++c) {
-                    if (R::better(run[r][c], best[r][c])) win[r][c] = s;
-                    best[r][c] = run[r][c];
-                }
-
-            if (boundary) {
-                // Resolve the outputs whose best improved inside this block:
-                // the first term of the winning slice equal to the best.  The
-                // four outputs of a row are scanned together (independent
-                // chains, no branch); an output that did not improve scans
-                // slot 0 and keeps its earlier result.
-#pragma unroll
-                for (int r = 0; r < GEMM_TM; ++r) {
-                    const T* ac[GEMM_TN];
-                    const T* bc[GEMM_TN];
-                    int found[GEMM_TN];
-#pragma unroll
-                    for (int c = 0; c < GEMM_TN; ++c) {
-                        const int w = win[r][c] < 0 ? 0 : win[r][c];
-                        ac[c] = As + w * GEMM_SLOT + 2 * ty + own(r);
-                        bc[c] = Bs + w * GEMM_SLOT + 2 * tx + own(c);
-                        found[c] = GEMM_BK - 1;
-                    }
-#pragma unroll
-                    for (int kk = GEMM_BK - 1; kk >= 0; --kk)
-#pragma unroll
-                        for (int c = 0; c < GEMM_TN; ++c) {
-                            const T term = R::mul(ac[c][kk * GEMM_LDP], bc[c][kk * GEMM_LDP]);
-                            found[c] = (term == best[r][c]) ? kk : found[c];
-                        }
-#pragma unroll
-                    for (int c = 0; c < GEMM_TN; ++c) {
-                        const T term = R::mul(ac[c][found[c] * GEMM_LDP], bc[c][found[c] * GEMM_LDP]);
-                        const bool hit = win[r][c] >= 0;
-                        idx[r][c] = hit ? (int)(block_k0 + win[r][c] * GEMM_BK + found[c]) : idx[r][c];
-                        cv[r][c] = hit ? term : cv[r][c];
-                        win[r][c] = -1;
-                    }
-                }
-                block_k0 += GEMM_KBLK;
-                if (!last) {
-                    __syncthreads();  // every wave is done with this block's LDS
-                    G::store(la, As, 0, tid, ra);
-                    G::store(lb, Bs, 0, tid, rb);
-                    if (g + 2 < nslices) {
-                        la.load(g + 2, R::zero(), ra);
-                        lb.load(g + 2, R::one(), rb);
-                    }
-                }
-            }
-            if (!last) __syncthreads();  // slice g+1 is visible in LDS
+                for (int c = 0; c < GEMM_TN; ++c)
+                    run[r][c] = R::add3(run[r][c], R::mul(fa[cur][0][r], fb[cur][0][c]),
+                                        R::mul(fa[cur][1][r], fb[cur][1][c]));
         }
-
-        T* __restrict__ C = static_cast<T*>(p.C) + b * p.sc_batch;
-        int32_t* __restrict__ I = p.argmax ? p.argmax + b * p.sc_batch : nullptr;
 #pragma unroll
-        for (int r = 0; r < GEMM_TM; ++r) {
-            const int64_t i = row0 + 2 * ty + own(r);
-            if (i >= p.m) continue;
+        for (int r = 0; r < GEMM_TM; ++r)
 #pragma unroll
             for (int c = 0; c < GEMM_TN; ++c) {
-                const int64_t j = col0 + 2 * tx + own(c);
-                if (j >= p.n) continue;
-                const int64_t off = i * p.sc_row + j * p.sc_col;
-                C[off] = cv[r][c];
-                if (I) I[off] = idx[r][c];
+                if (R::better(run[r][c], best[r][c])) win[r][c] = s;
+                best[r][c] = run[r][c];
+            }
+
+        if (boundary) {
+            // Resolve the outputs whose best improved inside this block: the
+            // first term of the winning slice equal to the best.  The four
+            // outputs of a row are scanned together (independent chains, no
+            // branch); an output that did not improve scans slot 0 and keeps
+            // its earlier result.
+#pragma unroll
+            for (int r = 0; r < GEMM_TM; ++r) {
+                const T* ac[GEMM_TN];
+                const T* bc[GEMM_TN];
+                int found[GEMM_TN];
+#pragma unroll
+                for (int c = 0; c < GEMM_TN; ++c) {
+                    const int w = win[r][c] < 0 ? 0 : win[r][c];
+                    ac[c] = As + w * GEMM_SLOT + 2 * ty + own(r);
+                    bc[c] = Bs + w * GEMM_SLOT + 2 * tx + own(c);
+                    found[c] = GEMM_BK - 1;
+                }
+#pragma unroll
+                for (int kk = GEMM_BK - 1; kk >= 0; --kk)
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; ++c) {
+                        const T term = R::mul(ac[c][kk * GEMM_LDP], bc[c][kk * GEMM_LDP]);
+                        found[c] = (term == best[r][c]) ? kk : found[c];
+                    }
+#pragma unroll
+                for (int c = 0; c < GEMM_TN; ++c) {
+                    const T term = R::mul(ac[c][found[c] * GEMM_LDP], bc[c][found[c] * GEMM_LDP]);
+                    const bool hit = win[r][c] >= 0;
+                    idx[r][c] = hit ? block_k0 + win[r][c] * GEMM_BK + found[c] : idx[r][c];
+                    cv[r][c] = hit ? term : cv[r][c];
+                    win[r][c] = -1;
+                }
+            }
+            block_k0 += GEMM_KBLK;
+
+            if (last) {
+                // the tile is complete: store C and argmax
+                T* __restrict__ C = static_cast<T*>(p.C) + ct.b * p.sc_batch;
+                int32_t* __restrict__ I = p.argmax ? p.argmax + ct.b * p.sc_batch : nullptr;
+                const bool pairs = p.c_vec2 && ct.col0 + GEMM_BN <= p.n;
+#pragma unroll
+                for (int r = 0; r < GEMM_TM; ++r) {
+                    const int64_t i = ct.row0 + 2 * ty + own(r);
+                    if (i >= p.m) continue;
+#pragma unroll
+                    for (int c = 0; c < GEMM_TN; c += 2) {
+                        const int64_t j = ct.col0 + 2 * tx + own(c);
+                        const int64_t off = i * p.sc_row + j;
+                        if (pairs) {
+                            using V2 = T __attribute__((ext_vector_type(2)));
+                            using I2 = int32_t __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<V2*>(C + off) = V2{cv[r][c], cv[r][c + 1]};
+                            if (I) *reinterpret_cast<I2*>(I + off) = I2{idx[r][c], idx[r][c + 1]};
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const int64_t jj = j + e;
+                                if (jj >= p.n) continue;
+                                const int64_t o = i * p.sc_row + jj * p.sc_col;
+                                C[o] = cv[r][c + e];
+                                if (I) I[o] = idx[r][c + e];
+                            }
+                        }
+                    }
+                }
+            }
+            if (!fetch_valid) break;  // no further step for this workgroup
+            __syncthreads();          // every wave is done with this block's LDS
+            G::store(la.mn_contig, As, 0, tid, ra);
+            G::store(lb.mn_contig, Bs, 0, tid, rb);
+            fetch_next();
+            if (last) {
+                cL += stride;
+                ct = tile_coord(p, cL, tiles, total);
+                reset_outputs();
+                g = -1;
+                block_k0 = 0;
             }
         }
-        __syncthreads();  // LDS is reused by the next tile of this workgroup
+        __syncthreads();  // the next slice is visible in LDS
+        ++g;
     }
 }
 

@@ -134,8 +134,21 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.tiles_m = (int32_t)tm;
     p.tiles_n = (int32_t)tn;
     p.swizzle = env_flag("TROPICAL_NO_XCD_SWIZZLE") ? 0 : 1;
+    // C and argmax rows take 8-byte pair stores when contiguous and aligned
+    p.c_vec2 = sC.col == 1 && sC.row % 2 == 0 && sC.batch % 2 == 0 &&
+               (reinterpret_cast<uintptr_t>(C) & 7u) == 0 &&
+               (argmax == nullptr || (reinterpret_cast<uintptr_t>(argmax) & 7u) == 0);
     int64_t total = tm * tn * batch;
-    uint32_t grid = total > kMaxGrid ? kMaxGrid : (uint32_t)total;
+    // Persistent grid: two workgroups per CU (the LDS budget of one
+    // workgroup is 70 KB), each walking a stream of tiles.  A multiple of 8
+    // keeps every workgroup's tiles on one XCD.
+    int64_t slots = (int64_t)device_cu_count(dev) * 2 / 8 * 8;
+    if (slots < 8) slots = 8;
+    if (const char* cap = std::getenv("TROPICAL_GEMM_MAX_WORKGROUPS")) {  // tuning knob
+        long v = std::strtol(cap, nullptr, 10);
+        if (v >= 8) slots = v / 8 * 8;
+    }
+    uint32_t grid = (uint32_t)(total < slots ? total : slots);
     return launch(dev, (KernelId)(K_GEMM_TILED_MAXPLUS_F32 + ri), TROP_K_GEMM_TILED, grid, 256, &p,
                   stream);
 }

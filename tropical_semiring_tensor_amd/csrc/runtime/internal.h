@@ -49,6 +49,8 @@ int ring_index(trop_semiring sr, trop_dtype dt);
 // error status (message recorded) and caches nothing.
 trop_status current_device(int* dev);
 trop_status ensure_module(int dev);
+// Compute units of a device whose module is loaded.
+int device_cu_count(int dev);
 
 // Enqueue kernel `id` (one by-value argument block) on `stream`.
 trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,

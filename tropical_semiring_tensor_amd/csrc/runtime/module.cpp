@@ -61,6 +61,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceModule {
     hipModule_t module = nullptr;
     hipFunction_t fn[K_COUNT] = {};
+    int cu_count = 0;
 };
 
 std::mutex g_mu;
@@ -128,6 +129,10 @@ trop_status ensure_module(int dev) {
                 e = hipModuleGetFunction(&dm->fn[i], dm->module, kNames[i]);
                 if (e != hipSuccess) st = hip_fail(e, kNames[i]);
             }
+            if (st == TROP_OK) {
+                e = hipDeviceGetAttribute(&dm->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+                if (e != hipSuccess) st = hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+            }
             if (st != TROP_OK) (void)hipModuleUnload(dm->module);
         }
     }
@@ -138,6 +143,11 @@ trop_status ensure_module(int dev) {
     }
     g_dev[dev].store(dm, std::memory_order_release);
     return TROP_OK;
+}
+
+int device_cu_count(int dev) {
+    DeviceModule* dm = g_dev[dev].load(std::memory_order_acquire);
+    return dm ? dm->cu_count : 0;
 }
 
 trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,
