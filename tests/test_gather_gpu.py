@@ -157,3 +157,39 @@ def test_workload5_permutes_full(tb, orc):
     torch.cuda.synchronize()
     assert_bits_equal(oc.cpu().numpy(), orc.permute(C.numpy(), (0, 2, 1)), "workload 5 C permute")
     assert_equal(oi.cpu().numpy(), orc.permute(I.numpy(), (0, 2, 1)), "workload 5 argmax permute")
+
+
+VEC_TILED = [
+    ((5, 36, 44), (0, 2, 1)),    # P = 36 -> 32-wide tiles, partial along P
+    ((3, 20, 48), (0, 2, 1)),    # P = 20 -> 16-wide tiles
+    ((2, 100, 72), (0, 2, 1)),   # P = 100 -> 64-wide tiles, partial along P and Q
+    ((128, 12, 8), (2, 1, 0)),   # batch axis between P and Q
+    ((4, 8, 260, 16), (3, 1, 0, 2)),
+    ((33, 64, 64), (0, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("shape,perm", VEC_TILED, ids=[str(s) for s, _ in VEC_TILED])
+def test_permute_vectorised_tiles(tb, orc, shape, perm):
+    g = torch.Generator().manual_seed(sum(shape))
+    x = torch.randn(shape, generator=g)
+    i = torch.randint(-1000, 1000, shape, generator=g, dtype=torch.int32)
+    before = launches(tb)
+    out, out2 = tb.tropical_permute(x.to(DEV), perm, x2=i.to(DEV))
+    torch.cuda.synchronize()
+    assert delta(before, launches(tb)) == {"gather_tiled": 1}
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"vec tiled {shape} {perm}")
+    assert_equal(out2.cpu().numpy(), orc.permute(i.numpy(), perm), f"vec tiled pair {shape} {perm}")
+
+
+VEC_COPY = [((7, 12, 3, 8), (1, 2, 0, 3)), ((9, 5, 4), (1, 0, 2)), ((3, 1000, 12), (1, 0, 2)),
+            ((2, 3, 4, 5, 8), (4, 3, 2, 1, 0)[::-1]), ((6, 7, 16), (1, 0, 2))]
+
+
+@pytest.mark.parametrize("shape,perm", VEC_COPY, ids=[str(s) for s, _ in VEC_COPY])
+def test_permute_vectorised_copy(tb, orc, shape, perm):
+    g = torch.Generator().manual_seed(len(shape) + shape[0])
+    x = torch.randn(shape, generator=g)
+    out = tb.tropical_permute(x.to(DEV), perm)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"vec copy {shape} {perm}")

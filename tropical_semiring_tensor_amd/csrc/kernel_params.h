@@ -56,9 +56,15 @@ struct TropGatherParams {
     int32_t vec;       // copy path: 16-byte vectors along the last axis
     int64_t tiles_p, tiles_q;  // tiles along ax_in (p) and the last axis (q)
     int64_t nbatch;            // product of the remaining axes
+    // 32-bit index math: every output linear index is below 2^31, and
+    // floor(n / shape[d]) = umulhi(n, mag_m[d]) >> mag_s[d] (shape[d] >= 2)
+    int32_t idx32;
+    uint32_t mag_m[TROP_MAX_DIMS];
+    uint32_t mag_s[TROP_MAX_DIMS];
+    uint32_t vpr, vpr_m, vpr_s;  // copy path: 16-byte vectors per output row
+    int32_t tile_p;              // vectorised tiled path: tile extent along ax_in
     // reduction (trace)
     int32_t nred;
-    int32_t pad_;
     int64_t rshape[TROP_MAX_DIMS];
     int64_t rstride[TROP_MAX_DIMS];
     int64_t rtotal;

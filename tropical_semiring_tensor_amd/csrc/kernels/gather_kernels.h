@@ -20,6 +20,10 @@
 //  * naive: one thread per output element, digits decoded from the
 //           linear index (the fallback).
 //
+// The copy path uses 32-bit indices with magic-number division when the
+// output has fewer than 2^31 elements; the tiled path has a vectorised form
+// (16-byte loads along ax_in, 16-byte stores along the last axis).
+//
 // With ntensors = 2 the second tensor is moved with the identical mapping
 // in the same launch (the value and its argmax, issue #52 "Acceptance
 // criteria").  All elements are 4 bytes and are moved as raw bits.
@@ -36,6 +40,11 @@ namespace trop {
 constexpr int GATHER_THREADS = 256;
 constexpr int TILE = 64;
 
+// floor(n / d) for n < 2^31 with the host-computed magic pair of d >= 2.
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t m, uint32_t sh) {
+    return __umulhi(n, m) >> sh;
+}
+
 // Input offset of output row `row` (all axes but the last), by digits.
 __device__ __forceinline__ int64_t gather_row_offset(const TropGatherParams& p, int64_t row) {
     int64_t off = 0;
@@ -49,6 +58,47 @@ __device__ __forceinline__ int64_t gather_row_offset(const TropGatherParams& p, 
 
 __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
     const int64_t inner = p.shape[p.ndim - 1];
+    if (p.vec && p.idx32) {
+        // 16-byte vectors, 32-bit indices, magic-number division; each thread
+        // keeps four independent vectors in flight per iteration
+        const uint32_t nv = (uint32_t)(p.total / 4);
+        const uint32_t vpr = p.vpr;
+        const uint32_t step = gridDim.x * blockDim.x;
+        auto offsets = [&](uint32_t v, int64_t& src, int64_t& dst) {
+            const uint32_t row = vpr == 1 ? v : fdiv(v, p.vpr_m, p.vpr_s);
+            const uint32_t col = (v - row * vpr) * 4;
+            src = col;
+            uint32_t r = row;
+            for (int d = p.ndim - 2; d >= 0; --d) {
+                const uint32_t q = fdiv(r, p.mag_m[d], p.mag_s[d]);
+                src += (int64_t)(r - q * (uint32_t)p.shape[d]) * p.istride[d];
+                r = q;
+            }
+            dst = (int64_t)row * inner + col;
+        };
+        for (uint32_t v0 = blockIdx.x * blockDim.x + threadIdx.x; v0 < nv; v0 += 4 * step) {
+            int64_t src[4], dst[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t v = v0 + u * step;
+                ok[u] = v < nv && v >= v0;  // (v >= v0 guards wrap-around)
+                if (ok[u]) offsets(v, src[u], dst[u]);
+            }
+            for (int t = 0; t < p.ntensors; ++t) {
+                const uint32_t* in = static_cast<const uint32_t*>(p.in[t]);
+                uint32_t* out = static_cast<uint32_t*>(p.out[t]);
+                uint4 x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (ok[u]) x[u] = *reinterpret_cast<const uint4*>(in + src[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (ok[u]) *reinterpret_cast<uint4*>(out + dst[u]) = x[u];
+            }
+        }
+        return;
+    }
     const int64_t rows = p.total / inner;
     if (p.vec) {
         // inner % 4 == 0 and every row start is 16-byte aligned on both sides
@@ -73,6 +123,85 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
             for (int t = 0; t < p.ntensors; ++t)
                 static_cast<uint32_t*>(p.out[t])[o] = static_cast<const uint32_t*>(p.in[t])[src];
         }
+    }
+}
+
+// Transpose through LDS with 16-byte global accesses on both sides.  A tile
+// covers TP elements along ax_in (P, input stride 1) and TQ = 4096 / TP
+// along the last output axis (Q, output stride 1).  Each thread loads four
+// 16-byte vectors along P and stores four along Q.  Needs EP, EQ, the input
+// stride of Q and of every other axis to be multiples of 4 and both pointers
+// 16-byte aligned (checked on the host).
+template <int TP, int NT>
+__device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p) {
+    constexpr int TQ = 4096 / TP;
+    constexpr int LDT = TP + 1;          // LDS row (fixed q) length in words
+    constexpr int LPR = TP / 4;          // read phase: lanes per q-row
+    constexpr int RPP = GATHER_THREADS / LPR;   // q-rows per pass
+    constexpr int LPQ = TQ / 4;          // write phase: lanes per p-row
+    constexpr int PPP = GATHER_THREADS / LPQ;   // p-rows per pass
+    static_assert(RPP * 4 == TQ && PPP * 4 == TP, "four passes per phase");
+    __shared__ uint32_t tile[NT][TQ * LDT];
+    const int nd = p.ndim;
+    const int P = p.ax_in, Q = nd - 1;
+    const int64_t EP = p.shape[P], EQ = p.shape[Q];
+    const int64_t sQ = p.istride[Q];
+    int64_t oP = 1;
+    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    const int tid = threadIdx.x;
+    const int64_t per_batch = p.tiles_p * p.tiles_q;
+    const int64_t nblk = per_batch * p.nbatch;
+    const int rp = (tid % LPR) * 4, rq = tid / LPR;   // read-phase lane position
+    const int wq = (tid % LPQ) * 4, wp = tid / LPQ;   // write-phase lane position
+
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t tq = blk % p.tiles_q;
+        const int64_t tp = (blk / p.tiles_q) % p.tiles_p;
+        int64_t bi = blk / per_batch;
+        int64_t ibase = 0, obase = 0, ostride = 1;
+        for (int d = nd - 1; d >= 0; --d) {
+            const int64_t e = p.shape[d];
+            if (d != P && d != Q) {
+                const int64_t digit = bi % e;
+                bi /= e;
+                ibase += digit * p.istride[d];
+                obase += digit * ostride;
+            }
+            ostride *= e;
+        }
+        const int64_t p0 = tp * TP, q0 = tq * TQ;
+        const int64_t pp = p0 + rp;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int ql = pass * RPP + rq;
+            const int64_t q = q0 + ql;
+            if (pp < EP && q < EQ) {
+                const int64_t src = ibase + pp + q * sQ;
+                #pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(p.in[t]) + src);
+                    uint32_t* row = &tile[t][ql * LDT + rp];
+                    row[0] = x.x; row[1] = x.y; row[2] = x.z; row[3] = x.w;
+                }
+            }
+        }
+        __syncthreads();
+        const int64_t q = q0 + wq;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int pl = pass * PPP + wp;
+            const int64_t pv = p0 + pl;
+            if (pv < EP && q < EQ) {
+                const int64_t dst = obase + pv * oP + q;
+                #pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint32_t* col = &tile[t][wq * LDT + pl];
+                    const uint4 x = {col[0], col[LDT], col[2 * LDT], col[3 * LDT]};
+                    *reinterpret_cast<uint4*>(static_cast<uint32_t*>(p.out[t]) + dst) = x;
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 

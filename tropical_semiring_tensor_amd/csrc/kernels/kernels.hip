@@ -35,6 +35,18 @@ extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled(T
     gather_tiled_body(p);
 }
 
+#define TROP_TILED_VEC(TPV, NTV)                                                                \
+    extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled_v##TPV##_n##NTV( \
+        TropGatherParams p) {                                                                   \
+        gather_tiled_vec_body<TPV, NTV>(p);                                                     \
+    }
+TROP_TILED_VEC(16, 1)
+TROP_TILED_VEC(32, 1)
+TROP_TILED_VEC(64, 1)
+TROP_TILED_VEC(16, 2)
+TROP_TILED_VEC(32, 2)
+TROP_TILED_VEC(64, 2)
+
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
     gather_naive_body(p);
 }

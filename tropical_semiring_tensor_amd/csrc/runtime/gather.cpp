@@ -32,6 +32,17 @@ bool env_flag(const char* name) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Magic pair for floor(n / d), n < 2^31, d >= 2: m = floor(2^(31+s) / d) + 1
+// with s = ceil(log2 d); then floor(n / d) = umulhi(n, m) >> (s - 1).  The
+// error term n * (m * d - 2^(31+s)) / (d * 2^(31+s)) stays below 1/d, so
+// the floor is exact.
+void magic(uint64_t d, uint32_t* m, uint32_t* sh) {
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    *m = (uint32_t)(((uint64_t(1) << (31 + s)) / d) + 1);
+    *sh = s - 1;
+}
+
 }  // namespace
 
 const char* gather_path_name(GatherPath p) {
@@ -102,6 +113,9 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
     }
     p.ndim = nd;
     p.total = total;
+    p.idx32 = total < (int64_t(1) << 31) ? 1 : 0;
+    for (int d = 0; d < nd && p.idx32; ++d)
+        if (p.shape[d] >= 2) magic((uint64_t)p.shape[d], &p.mag_m[d], &p.mag_s[d]);
 
     int nr = 0;
     for (int d = 0; d < nred; ++d) {
@@ -205,13 +219,34 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             for (int d = 0; d < p.ndim - 1 && vec; ++d) vec = p.istride[d] % 4 == 0;
             for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
             p.vec = vec ? 1 : 0;
-            const int64_t work = vec ? p.total / 4 : p.total;
+            if (vec) {
+                p.vpr = (uint32_t)(inner / 4);
+                if (p.vpr >= 2 && p.idx32) magic(p.vpr, &p.vpr_m, &p.vpr_s);
+            }
+            // the 32-bit vector path moves four vectors per thread and pass
+            const int64_t work = vec ? (p.idx32 ? (p.total / 4 + 3) / 4 : p.total / 4) : p.total;
             return launch(dev, K_GATHER_COPY, TROP_K_GATHER_COPY, grid_for(work, 256), 256, &p, stream);
         }
         case GP_TILED: {
+            const int nd = p.ndim, P = p.ax_in, Q = nd - 1;
+            const int64_t EP = p.shape[P], EQ = p.shape[Q];
+            // 16-byte accesses on both sides when every stride and extent allows
+            bool vec = EP % 4 == 0 && EQ % 4 == 0 && EP >= 4;
+            for (int d = 0; d < nd && vec; ++d)
+                if (d != P) vec = p.istride[d] % 4 == 0;
+            for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
+            KernelId kid = K_GATHER_TILED;
+            if (vec) {
+                const int tp = EP >= 64 ? 64 : (EP >= 32 ? 32 : 16);
+                p.tile_p = tp;
+                p.tiles_p = (EP + tp - 1) / tp;
+                p.tiles_q = (EQ + 4096 / tp - 1) / (4096 / tp);
+                const int base = ntensors == 2 ? K_GATHER_TILED_V16_N2 : K_GATHER_TILED_V16_N1;
+                kid = (KernelId)(base + (tp == 64 ? 2 : (tp == 32 ? 1 : 0)));
+            }
             int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
             uint32_t grid = nblk > kMaxGrid ? kMaxGrid : (uint32_t)nblk;
-            return launch(dev, K_GATHER_TILED, TROP_K_GATHER_TILED, grid, 256, &p, stream);
+            return launch(dev, kid, TROP_K_GATHER_TILED, grid, 256, &p, stream);
         }
         case GP_NAIVE:
             return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);

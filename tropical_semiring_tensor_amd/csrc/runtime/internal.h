@@ -38,6 +38,12 @@ enum KernelId : int {
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,
+    K_GATHER_TILED_V16_N1,
+    K_GATHER_TILED_V32_N1,
+    K_GATHER_TILED_V64_N1,
+    K_GATHER_TILED_V16_N2,
+    K_GATHER_TILED_V32_N2,
+    K_GATHER_TILED_V64_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);

@@ -37,7 +37,10 @@ static const char* const kNames[K_COUNT] = {
     "trop_gather_reduce_maxmul_f32", "trop_gather_reduce_maxplus_i32",
     "trop_gather_reduce_minplus_i32", "trop_fill",
     "trop_gather_copy",              "trop_gather_tiled",
-    "trop_gather_naive",
+    "trop_gather_naive",             "trop_gather_tiled_v16_n1",
+    "trop_gather_tiled_v32_n1",      "trop_gather_tiled_v64_n1",
+    "trop_gather_tiled_v16_n2",      "trop_gather_tiled_v32_n2",
+    "trop_gather_tiled_v64_n2",
 };
 
 const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
