@@ -31,6 +31,7 @@ FP32_DATASHEET_T = 157.3                     # packed-FMA FP32 vector peak
 ISA_CEILING_T = VALU_PEAK_T * 2 / 3          # 1.5 VALU instructions per term
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["tropical_semiring_tensor_amd/csrc/kernels/gemm_kernels.h",
+                  "tropical_semiring_tensor_amd/csrc/kernels/gemm_tiled.h",
                   "tropical_semiring_tensor_amd/csrc/kernels/ring.h",
                   "tropical_semiring_tensor_amd/csrc/kernels/gather_kernels.h",
                   "tropical_semiring_tensor_amd/csrc/kernels/kernels.hip"]

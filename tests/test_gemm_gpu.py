@@ -253,3 +253,42 @@ def test_workload3_reduced_full_check(tb, orc):
 def test_workload4_reduced_full_check(tb, orc):
     A, B = inputs.gemm_operands(4, batch=3, m=200, n=150, k=700)
     check(tb, orc, "max_mul", A, B, "workload 4 recipe, 3x200x150x700")
+
+
+# ---------------------------------------------------------------------------
+# value-only launches (no argmax output) run their own kernel: same parity bar
+
+VO_SHAPES = [(1, 1, 1, 1), (2, 3, 7, 5), (3, 65, 17, 63), (2, 127, 255, 129), (1, 33, 600, 40)]
+
+
+@pytest.mark.parametrize("sr,dt", PAIRS)
+@pytest.mark.parametrize("shape", VO_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_value_only_ragged(tb, orc, sr, dt, shape):
+    b, m, k, n = shape
+    A, B = make(sr, dt, b, m, k, n, seed=zlib.crc32(repr(("vo", sr, dt, shape)).encode()) % 10000)
+    check(tb, orc, sr, A, B, f"value only {sr} {dt} {shape}", argmax=False)
+
+
+@pytest.mark.parametrize("a_col,b_col", [(False, True), (True, False)])
+def test_value_only_layouts(tb, orc, a_col, b_col):
+    for sr, dt in PAIRS:
+        A, B = make(sr, dt, 2, 97, 300, 75, seed=12, a_col=a_col, b_col=b_col)
+        check(tb, orc, sr, A, B, f"value only {sr} {dt} a_col={a_col} b_col={b_col}", argmax=False)
+
+
+def test_value_only_special_values_and_signed_zeros(tb, orc):
+    g = torch.Generator().manual_seed(6)
+    kinds = ["inf", "-inf", "nan", "-0", "0", "den", "-den"]
+    A = special_matrix((2, 70, 290), g, kinds)
+    B = special_matrix((2, 290, 68), g, kinds)
+    for sr in ("max_plus", "min_plus", "max_mul"):
+        check(tb, orc, sr, A, B, f"value only special {sr}", argmax=False)
+    Z = torch.where(torch.rand(1, 64, 64, generator=g) < 0.5, -0.0, 0.0)
+    Bz = torch.full((1, 64, 64), -0.0)
+    for sr in ("max_plus", "min_plus"):
+        check(tb, orc, sr, Z, Bz, f"value only signed zeros {sr}", argmax=False)
+
+
+def test_value_only_workload2_full(tb, orc):
+    A, B = inputs.gemm_operands(2)
+    check(tb, orc, "max_plus", A, B, "workload 2 value only", argmax=False)

@@ -28,7 +28,7 @@ struct TropGemmParams {
     int32_t a_mode, b_mode;    // TROP_LOAD_*
     int32_t a_vec, b_vec;      // 16-byte vector loads are aligned and legal
     int32_t swizzle;           // remap workgroups so each XCD owns a tile range
-    int32_t c_vec2;            // C / argmax rows take aligned 8-byte pair stores
+    int32_t pad_;
 };
 
 struct TropFillParams {

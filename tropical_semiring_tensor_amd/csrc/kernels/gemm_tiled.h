@@ -1,0 +1,509 @@
+// Strided-batched tropical GEMM with argmax: the tiled kernel for gfx950.
+//
+// Computes C[b][i][j] = (+)_k A[b][i][k] (x) B[b][k][j] and the smallest k
+// whose term is the result -- the batched "with argmax" kernels of
+// tropical-gemm PR #35 ("feat: batched GPU ops with DLPack zero-copy
+// output", Key changes), re-designed for CDNA4:
+//
+//  * A max-plus product is not a multiply-accumulate, so it runs on the
+//    VALU, not on MFMA.  The value path costs 1.5 VALU instructions per
+//    (output, k): one add / multiply per term and one v_max3 / v_min3 per
+//    two terms.
+//  * An exact per-term argmax would add a compare and two selects per term.
+//    Instead the running value is compared once per chunk of CH = 16 terms
+//    (one compare + one select: which chunk last improved strictly).  The
+//    kernel keeps a whole K-block of KBLK terms of both operand tiles
+//    resident in LDS; at the end of each block every output whose best
+//    improved inside it re-scans its winning chunk for the first term equal
+//    to the block's best.  That is the exact first winner: a chunk is
+//    recorded only when it holds a term above everything before it, and
+//    inside it the first term equal to the final value is that first winner.
+//    A wave skips the re-scan of an output slot that none of its lanes needs.
+//  * LDS holds both operands k-contiguous ([row][k] for A, [column][k] for
+//    B, rows padded by 4 words), so the main loop reads four k at a time
+//    per row or column with one 16-byte LDS read, and the re-scan reads its
+//    16 terms with four.  k-contiguous global operands are copied in as
+//    16-byte vectors; row- or column-contiguous ones are transposed on the
+//    way in.
+//  * C takes the bits of the first winning term.  Those differ from the
+//    running maximum's bits only for a zero result (+0 against -0), so only
+//    outputs whose value is zero are recomputed from global memory at the
+//    resolved index; an output that nothing beat holds the zero element.
+//
+// Tiling: 256 threads (4 waves) or 512 (8 waves), a 64x64 output tile per
+// workgroup, 16 or 8 outputs per thread at rows ty + RS r and columns
+// tx + 16 c (tx = tid % 16, ty = tid / 16, RS = threads / 16).  K is staged through LDS in slices of SL terms;
+// the slice after next is fetched into registers while the current one
+// computes and the next one is written to LDS at its start, so one barrier
+// per slice suffices (one more at the end of each resident block).
+//
+// Without an argmax output the same loop runs with no record and no
+// re-scan, and LDS holds a ring of two slices instead of a block.
+#pragma once
+#include <type_traits>
+
+#include "ring.h"
+
+namespace trop {
+
+#ifndef TROP_GEMM_THREADS
+#define TROP_GEMM_THREADS 512
+#endif
+constexpr int GEMM_THREADS = TROP_GEMM_THREADS;  // 256 or 512
+static_assert(GEMM_THREADS == 256 || GEMM_THREADS == 512, "4 or 8 waves");
+// Thread tx = tid % 16, ty = tid / 16 owns rows ty + GEMM_RS r (r < GEMM_TR)
+// and columns tx + 16 c (c < 4) of the 64x64 tile.
+constexpr int GEMM_RS = GEMM_THREADS / 16;
+constexpr int GEMM_TR = 64 / GEMM_RS;
+constexpr int GEMM_BM = 64;
+constexpr int GEMM_BN = 64;
+#ifndef TROP_GEMM_CH
+#define TROP_GEMM_CH 16
+#endif
+#ifndef TROP_GEMM_RESOLVE_SKIP
+#define TROP_GEMM_RESOLVE_SKIP 1
+#endif
+constexpr int GEMM_CH = TROP_GEMM_CH;  // argmax chunk (terms): 8 or 16
+static_assert(GEMM_CH == 8 || GEMM_CH == 16, "chunks of 8 or 16 terms");
+#ifndef TROP_GEMM_SLICE
+#define TROP_GEMM_SLICE 32
+#endif
+#ifndef TROP_GEMM_KBLK
+#define TROP_GEMM_KBLK 256
+#endif
+constexpr int GEMM_SL = TROP_GEMM_SLICE;  // LDS staging slice (terms)
+static_assert(GEMM_SL % GEMM_CH == 0, "a slice holds whole chunks");
+static_assert(TROP_GEMM_KBLK % GEMM_SL == 0, "a block holds whole slices");
+
+template <bool ARG>
+struct GemmCfg {
+    // K terms resident in LDS: a block (argmax) or a ring of two slices
+    static constexpr int KB = ARG ? TROP_GEMM_KBLK : 2 * GEMM_SL;
+    static constexpr int NSL = KB / GEMM_SL;  // slices per block
+    // LDS row length in words: 4 words of padding put rows r and r + 1 in
+    // different 16-byte bank groups, so 16 lanes reading 16 consecutive rows
+    // at one k take distinct banks
+    static constexpr int LDR = KB + 4;
+};
+
+// Bijective remap of the linear workgroup id so that each of the 8 XCDs
+// (which receive workgroups round-robin) owns one contiguous range of
+// logical tiles; neighbouring tiles then share operand panels in one L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t L, int64_t total) {
+    constexpr int64_t NX = 8;
+    const int64_t per = (total + NX - 1) / NX;
+    int64_t tall = total % NX;
+    if (tall == 0) tall = NX;
+    const int64_t x = L % NX;
+    const int64_t local = L / NX;
+    if (x < tall) return x * per + local;
+    return tall * per + (x - tall) * (per - 1) + local;
+}
+
+// Batch entry and output-tile origin of logical tile L.
+struct TileCoord {
+    int64_t b, row0, col0;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
+                                                int64_t total) {
+    const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
+    const int64_t t = lg % tiles;
+    return {lg / tiles, (t / p.tiles_n) * GEMM_BM, (t % p.tiles_n) * GEMM_BN};
+}
+
+// One thread's share of one operand tile per slice: NV vectors of 4
+// elements.  K_CONTIG: a vector runs along k at one row (A) / column (B);
+// MN_CONTIG: along the rows / columns at one k.  Vector v sits 16 k after
+// vector v - 1.
+// Vector vi = tid + GEMM_THREADS v of a slice; K_CONTIG: 8 consecutive
+// vectors take 8 rows at one k, so their 16-byte LDS writes fall in distinct
+// bank groups; MN_CONTIG: 16 consecutive vectors cover 64 rows at one k.
+__device__ __forceinline__ int kc_row(int vi) { return (vi & 7) + 8 * ((vi >> 5) & 7); }
+__device__ __forceinline__ int kc_k(int vi) { return ((vi >> 3) & 3) * 4 + 16 * (vi >> 8); }
+__device__ __forceinline__ int mc_row(int vi) { return (vi & 15) * 4; }
+__device__ __forceinline__ int mc_k(int vi) { return vi >> 4; }
+
+template <typename T, int NV, int LDR>
+struct OpLoad {
+    using V = vec4<T>;
+    const T* q0;       // element 0 of vector 0 of slice 0
+    int64_t k_step;    // elements per slice along k
+    int64_t v_step;    // elements between vectors v and v + 1
+    int64_t e_str;     // elements between the 4 elements of a vector
+    int64_t mn;        // row / column of element 0
+    int64_t k0;        // k of element 0 in slice 0
+    int64_t mn_lim, k_lim;
+    int lds0;          // LDS word offset of element 0 (slot 0)
+    int lds_v;         // LDS words between vectors v and v + 1
+    int kv;            // k between vectors v and v + 1
+    bool mn_c, vec, mn_full;
+
+    // Position of this thread's elements (independent of the tile).
+    __device__ __forceinline__ void init(int mode, int v16, int64_t str_mn, int64_t str_k,
+                                         int64_t mnl, int64_t kl, int tid) {
+        mn_c = (mode == TROP_LOAD_MN_CONTIG);
+        vec = v16 != 0;
+        mn_lim = mnl;
+        k_lim = kl;
+        k_step = (int64_t)GEMM_SL * str_k;
+        // vector v + 1 = vector index + GEMM_THREADS: the same row, k further
+        // on by GEMM_THREADS / 16 (MN_CONTIG) or 16 GEMM_THREADS / 256
+        // (K_CONTIG)
+        kv = mn_c ? mc_k(GEMM_THREADS) : kc_k(GEMM_THREADS);
+        v_step = kv * str_k;
+        lds_v = kv;
+        if (mn_c) {
+            e_str = str_mn;
+            k0 = mc_k(tid);
+            mn = mc_row(tid);
+            lds0 = mc_row(tid) * LDR + mc_k(tid);
+        } else {
+            e_str = str_k;
+            k0 = kc_k(tid);
+            mn = kc_row(tid);
+            lds0 = kc_row(tid) * LDR + kc_k(tid);
+        }
+    }
+
+    // Point at a tile: X is the operand of the batch entry, mn_start the
+    // tile's first row / column, str_mn the stride along it.
+    __device__ __forceinline__ void at(const T* X, int64_t mn_start, int64_t str_mn, int64_t str_k,
+                                       int tid) {
+        const int64_t m_rel = mn_c ? mc_row(tid) : kc_row(tid);
+        mn = mn_start + m_rel;
+        q0 = X + mn * str_mn + k0 * str_k;
+        mn_full = mn_start + 64 <= mn_lim;
+    }
+
+    __device__ __forceinline__ void load(int g, T pad, T (&r)[NV][4]) const {
+        const T* q = q0 + (int64_t)g * k_step;
+        const int64_t kb = k0 + (int64_t)g * GEMM_SL;
+        const bool full = mn_full && (int64_t)(g + 1) * GEMM_SL <= k_lim;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const T* qv = q + v * v_step;
+            if (full) {
+                if (vec) {
+                    const V x = *reinterpret_cast<const V*>(qv);
+                    r[v][0] = x.x;
+                    r[v][1] = x.y;
+                    r[v][2] = x.z;
+                    r[v][3] = x.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[v][e] = qv[e * e_str];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t kk = kb + kv * v + (mn_c ? 0 : e);
+                    const int64_t mm = mn + (mn_c ? e : 0);
+                    r[v][e] = (kk < k_lim && mm < mn_lim) ? qv[e * e_str] : pad;
+                }
+            }
+        }
+    }
+
+    // Write a slice held in registers to LDS at k offset `sk` of the block.
+    __device__ __forceinline__ void store(T* S, int sk, const T (&r)[NV][4]) const {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            T* d = S + lds0 + sk + lds_v * v;
+            if (mn_c) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e * LDR] = r[v][e];
+            } else {
+                *reinterpret_cast<V*>(d) = V{r[v][0], r[v][1], r[v][2], r[v][3]};
+            }
+        }
+    }
+};
+
+// C bits of the outputs whose value is zero (max-plus / min-plus float32):
+// the bits of the first winning term, recomputed from global memory at the
+// resolved index (with argmax) or found by a scan along k (value only).
+// Rare and only taken by a wave that holds such an output.
+template <int SR, typename T, bool ARG>
+__device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoord ct, int tx,
+                                                          int ty, T (&best)[GEMM_TR][4],
+                                                          const int (&idx)[GEMM_TR][4]) {
+    using R = Ring<SR, T>;
+    const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch;
+    const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch;
+    for (int r = 0; r < GEMM_TR; ++r)
+        for (int c = 0; c < 4; ++c) {
+            const int64_t i = ct.row0 + ty + GEMM_RS * r, j = ct.col0 + tx + 16 * c;
+            if (i >= p.m || j >= p.n || !(best[r][c] == (T)0)) continue;
+            const T* a = A + i * p.sa_row;
+            const T* b = B + j * p.sb_col;
+            if constexpr (ARG) {
+                const int64_t k = idx[r][c];
+                best[r][c] = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
+            } else {
+                for (int64_t k = 0; k < p.k; ++k) {
+                    const T t = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
+                    if (t == best[r][c]) {
+                        best[r][c] = t;
+                        break;
+                    }
+                }
+            }
+        }
+}
+
+// The tiled kernel.  A workgroup walks the tiles L = blockIdx.x,
+// blockIdx.x + gridDim.x, ... as one stream of (tile, slice) steps, so the
+// fetch of a tile's first slice overlaps the previous tile's last slice,
+// re-scan and stores.
+template <int SR, typename T, bool ARG>
+__device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
+    using R = Ring<SR, T>;
+    using V = vec4<T>;
+    using Cfg = GemmCfg<ARG>;
+    constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR;
+    constexpr int NV = 16 * GEMM_SL / GEMM_THREADS;  // vectors per thread, operand and slice
+    static_assert(NV >= 1 && NV * GEMM_THREADS == 16 * GEMM_SL, "whole vectors per thread");
+    constexpr int NQ = GEMM_SL / 4;         // k-quads per slice
+    constexpr int QPC = GEMM_CH / 4;        // k-quads per chunk
+    constexpr int CPS = GEMM_SL / GEMM_CH;  // chunks per slice
+    using L = OpLoad<T, NV, LDR>;
+    __shared__ __attribute__((aligned(16))) T As[GEMM_BM * LDR];
+    __shared__ __attribute__((aligned(16))) T Bs[GEMM_BN * LDR];
+
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t total = tiles * p.batch;
+    const int nslices = (int)((p.k + GEMM_SL - 1) / GEMM_SL);
+    const int64_t gstride = gridDim.x;
+
+    int64_t cL = blockIdx.x;  // tile being computed
+    if (cL >= total || nslices == 0) return;  // K = 0 is handled by the fill kernel
+    if (blockDim.x != GEMM_THREADS) return;   // launched with a block it was not built for
+
+    L la, lb;
+    la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid);
+    lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid);
+    const T* const Ag = static_cast<const T*>(p.A);
+    const T* const Bg = static_cast<const T*>(p.B);
+    auto point = [&](const TileCoord& tc) {
+        la.at(Ag + tc.b * p.sa_batch, tc.row0, p.sa_row, p.sa_col, tid);
+        lb.at(Bg + tc.b * p.sb_batch, tc.col0, p.sb_col, p.sb_row, tid);
+    };
+
+    // Fetch cursor: the (tile, slice) whose data was last requested.
+    int64_t fL = cL;
+    int fg = 0;
+    point(tile_coord(p, fL, tiles, total));
+    bool fetch_valid = true;
+    T ra[NV][4], rb[NV][4];
+    auto fetch_next = [&]() {
+        ++fg;
+        if (fg == nslices) {
+            fg = 0;
+            fL += gstride;
+            fetch_valid = fL < total;
+            if (fetch_valid) point(tile_coord(p, fL, tiles, total));
+        }
+        if (fetch_valid) {
+            la.load(fg, R::zero(), ra);
+            lb.load(fg, R::one(), rb);
+        }
+    };
+
+    // prologue: slice 0 goes to LDS slot 0, slice 1 to registers
+    {
+        T r0a[NV][4], r0b[NV][4];
+        la.load(0, R::zero(), r0a);
+        lb.load(0, R::one(), r0b);
+        fetch_next();
+        la.store(As, 0, r0a);
+        lb.store(Bs, 0, r0b);
+    }
+    __syncthreads();
+
+    TileCoord ct = tile_coord(p, cL, tiles, total);
+    T best[GEMM_TR][4];
+    int win[GEMM_TR][4];
+    int idx[GEMM_TR][4];
+    auto reset_outputs = [&]() {
+#pragma unroll
+        for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                best[r][c] = R::zero();
+                win[r][c] = -1;
+                idx[r][c] = 0;
+            }
+    };
+    reset_outputs();
+
+    const T* const a_row = As + ty * LDR;  // row ty + GEMM_RS r at + GEMM_RS r LDR
+    const T* const b_col = Bs + tx * LDR;
+
+    int g = 0;           // slice of the current tile
+    int64_t blk_k0 = 0;  // first k of the resident block
+    int ring = 0;        // value only: ring slot of the current slice
+    for (;;) {
+        const int s = ARG ? g % NSL : ring;
+        const bool last = (g + 1 == nslices);
+        const bool bend = ARG ? (last || s == NSL - 1) : last;
+        // The registers hold slice g + 1 of this tile: its LDS slot is free
+        // (argmax: inside the block; value only: the ring slot read two
+        // slices ago), so park it now and fetch the step after it.
+        if (!bend) {
+            const int sn = (ARG ? s + 1 : s ^ 1) * GEMM_SL;
+            la.store(As, sn, ra);
+            lb.store(Bs, sn, rb);
+            fetch_next();
+        }
+
+        // ---- compute the slice: 4 k per 16-byte fragment ----
+        {
+            const int sk = s * GEMM_SL;
+            V fa[2][GEMM_TR], fb[2][4];
+#pragma unroll
+            for (int r = 0; r < GEMM_TR; ++r) fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk);
+            T cm[GEMM_TR][4];  // argmax: (+) of the current chunk's terms
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int cur = q & 1, nxt = cur ^ 1;
+                if (q + 1 < NQ) {
+#pragma unroll
+                    for (int r = 0; r < GEMM_TR; ++r)
+                        fa[nxt][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * (q + 1));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * (q + 1));
+                }
+#pragma unroll
+                for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const V a = fa[cur][r], b = fb[cur][c];
+                        if constexpr (ARG) {
+                            T v = (q % QPC == 0) ? R::add2(R::mul(a.x, b.x), R::mul(a.y, b.y))
+                                                 : R::add3(cm[r][c], R::mul(a.x, b.x), R::mul(a.y, b.y));
+                            cm[r][c] = R::add3(v, R::mul(a.z, b.z), R::mul(a.w, b.w));
+                        } else {
+                            T v = R::add3(best[r][c], R::mul(a.x, b.x), R::mul(a.y, b.y));
+                            best[r][c] = R::add3(v, R::mul(a.z, b.z), R::mul(a.w, b.w));
+                        }
+                    }
+                if constexpr (ARG) {
+                    if (q % QPC == QPC - 1) {
+                        // record the chunk if it beats everything before it
+                        const int cid = s * CPS + q / QPC;  // chunk within the block
+#pragma unroll
+                        for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                // one compare feeds both selects (a select,
+                                // unlike max, needs no NaN canonicalisation)
+                                const bool up = R::better(cm[r][c], best[r][c]);
+                                win[r][c] = up ? cid : win[r][c];
+                                best[r][c] = up ? cm[r][c] : best[r][c];
+                            }
+                    }
+                }
+            }
+        }
+
+        if (bend) {
+            if constexpr (ARG) {
+                // Re-scan the winning chunk of every output that improved in
+                // this block: the first term equal to the best.
+#pragma unroll
+                for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const bool need = win[r][c] >= 0;
+                        if (!TROP_GEMM_RESOLVE_SKIP || __any(need)) {
+                            constexpr int NU = GEMM_CH / 4;
+                            const int w = need ? win[r][c] : 0;
+                            const V* ap = reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + w * GEMM_CH);
+                            const V* bp = reinterpret_cast<const V*>(b_col + c * 16 * LDR + w * GEMM_CH);
+                            V av[NU], bv[NU];
+#pragma unroll
+                            for (int u = 0; u < NU; ++u) {
+                                av[u] = ap[u];
+                                bv[u] = bp[u];
+                            }
+                            int f = GEMM_CH - 1;
+#pragma unroll
+                            for (int u = NU - 1; u >= 0; --u) {
+                                f = (R::mul(av[u].w, bv[u].w) == best[r][c]) ? 4 * u + 3 : f;
+                                f = (R::mul(av[u].z, bv[u].z) == best[r][c]) ? 4 * u + 2 : f;
+                                f = (R::mul(av[u].y, bv[u].y) == best[r][c]) ? 4 * u + 1 : f;
+                                f = (R::mul(av[u].x, bv[u].x) == best[r][c]) ? 4 * u : f;
+                            }
+                            idx[r][c] = need ? (int)blk_k0 + w * GEMM_CH + f : idx[r][c];
+                        }
+                        win[r][c] = -1;
+                    }
+                blk_k0 += Cfg::KB;
+            }
+
+            if (last) {
+                // The tile is complete.  C takes the bits of the first
+                // winning term; they can differ from the running maximum's
+                // only for a zero value (+0 against -0).
+                if constexpr (std::is_same<T, float>::value) {
+                    if constexpr (SR == TROP_SR_MAX_MUL) {
+                        // the zero element is +0 and a term must exceed it to
+                        // win: a zero value means nothing won
+#pragma unroll
+                        for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                best[r][c] = best[r][c] == (T)0 ? R::zero() : best[r][c];
+                    } else {
+                        bool any0 = false;
+#pragma unroll
+                        for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) any0 |= best[r][c] == (T)0;
+                        if (__any(any0))
+                            zero_bits_fixup<SR, T, ARG>(p, ct, tx, ty, best, idx);
+                    }
+                }
+                T* __restrict__ C = static_cast<T*>(p.C) + ct.b * p.sc_batch;
+                int32_t* __restrict__ I = ARG ? p.argmax + ct.b * p.sc_batch : nullptr;
+#pragma unroll
+                for (int r = 0; r < GEMM_TR; ++r) {
+                    const int64_t i = ct.row0 + ty + GEMM_RS * r;
+                    if (i >= p.m) continue;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int64_t j = ct.col0 + tx + 16 * c;
+                        if (j >= p.n) continue;
+                        const int64_t o = i * p.sc_row + j * p.sc_col;
+                        C[o] = best[r][c];
+                        if constexpr (ARG) I[o] = idx[r][c];
+                    }
+                }
+            }
+            if (!fetch_valid) break;  // no further step for this workgroup
+            if constexpr (ARG) __syncthreads();  // every wave is done with this block
+            const int sn = ARG ? 0 : (s ^ 1) * GEMM_SL;
+            la.store(As, sn, ra);
+            lb.store(Bs, sn, rb);
+            fetch_next();
+            if (last) {
+                cL += gstride;
+                ct = tile_coord(p, cL, tiles, total);
+                reset_outputs();
+                g = -1;
+                blk_k0 = 0;
+            }
+        }
+        __syncthreads();  // the next slice is visible in LDS
+        ++g;
+        ring ^= 1;
+    }
+}
+
+}  // namespace trop

@@ -9,7 +9,11 @@ using namespace trop;
 #define TROP_GEMM_ENTRIES(NAME, SR, T)                                                        \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_##NAME(         \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, T>(p);                                                              \
+        gemm_tiled_body<SR, T, true>(p);                                                        \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo_##NAME(      \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, false>(p);                                                       \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_simple_##NAME(TropGemmParams p) { \
         gemm_simple_body<SR, T>(p);                                                             \

@@ -11,7 +11,8 @@
 // math, FTZ or FMA contraction); int32 (x) is a saturating add, which gfx950
 // does in one instruction (v_add_i32 with the clamp bit).
 //
-// add3() folds two terms into a running value with one v_max3 / v_min3; it
+// add2() is the two-input (+).  add3() folds two terms into a running value
+// with one v_max3 / v_min3; it
 // is written as op(op(r, x), y) so that a chain of add3() calls maps onto
 // one 3-input instruction per call rather than a re-balanced tree.
 // IEEE mode is on, so a NaN term is ignored by max / min: it can never
@@ -33,6 +34,7 @@ struct Ring<TROP_SR_MAX_PLUS, float> {
     static __device__ __forceinline__ float one() { return 0.0f; }
     static __device__ __forceinline__ float mul(float a, float b) { return a + b; }
     static __device__ __forceinline__ bool better(float t, float b) { return t > b; }
+    static __device__ __forceinline__ float add2(float x, float y) { return __builtin_fmaxf(x, y); }
     static __device__ __forceinline__ float add3(float r, float x, float y) {
         return __builtin_fmaxf(__builtin_fmaxf(r, x), y);
     }
@@ -44,6 +46,7 @@ struct Ring<TROP_SR_MIN_PLUS, float> {
     static __device__ __forceinline__ float one() { return 0.0f; }
     static __device__ __forceinline__ float mul(float a, float b) { return a + b; }
     static __device__ __forceinline__ bool better(float t, float b) { return t < b; }
+    static __device__ __forceinline__ float add2(float x, float y) { return __builtin_fminf(x, y); }
     static __device__ __forceinline__ float add3(float r, float x, float y) {
         return __builtin_fminf(__builtin_fminf(r, x), y);
     }
@@ -55,6 +58,7 @@ struct Ring<TROP_SR_MAX_MUL, float> {
     static __device__ __forceinline__ float one() { return 1.0f; }
     static __device__ __forceinline__ float mul(float a, float b) { return a * b; }
     static __device__ __forceinline__ bool better(float t, float b) { return t > b; }
+    static __device__ __forceinline__ float add2(float x, float y) { return __builtin_fmaxf(x, y); }
     static __device__ __forceinline__ float add3(float r, float x, float y) {
         return __builtin_fmaxf(__builtin_fmaxf(r, x), y);
     }
@@ -68,6 +72,7 @@ struct Ring<TROP_SR_MAX_PLUS, int32_t> {
         return __builtin_elementwise_add_sat(a, b);
     }
     static __device__ __forceinline__ bool better(int32_t t, int32_t b) { return t > b; }
+    static __device__ __forceinline__ int32_t add2(int32_t x, int32_t y) { return max(x, y); }
     static __device__ __forceinline__ int32_t add3(int32_t r, int32_t x, int32_t y) {
         return max(max(r, x), y);
     }
@@ -81,6 +86,7 @@ struct Ring<TROP_SR_MIN_PLUS, int32_t> {
         return __builtin_elementwise_add_sat(a, b);
     }
     static __device__ __forceinline__ bool better(int32_t t, int32_t b) { return t < b; }
+    static __device__ __forceinline__ int32_t add2(int32_t x, int32_t y) { return min(x, y); }
     static __device__ __forceinline__ int32_t add3(int32_t r, int32_t x, int32_t y) {
         return min(min(r, x), y);
     }

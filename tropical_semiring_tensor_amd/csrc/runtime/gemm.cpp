@@ -134,23 +134,27 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.tiles_m = (int32_t)tm;
     p.tiles_n = (int32_t)tn;
     p.swizzle = env_flag("TROPICAL_NO_XCD_SWIZZLE") ? 0 : 1;
-    // C and argmax rows take 8-byte pair stores when contiguous and aligned
-    p.c_vec2 = sC.col == 1 && sC.row % 2 == 0 && sC.batch % 2 == 0 &&
-               (reinterpret_cast<uintptr_t>(C) & 7u) == 0 &&
-               (argmax == nullptr || (reinterpret_cast<uintptr_t>(argmax) & 7u) == 0);
     int64_t total = tm * tn * batch;
-    // Persistent grid: two workgroups per CU (the LDS budget of one
-    // workgroup is 70 KB), each walking a stream of tiles.  A multiple of 8
+    // without an argmax output the value-only kernel skips the chunk record
+    // and the re-scan
+    const KernelId kid = (KernelId)((argmax ? K_GEMM_TILED_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
+    // Persistent grid: as many workgroups as the CUs hold at once (LDS and
+    // registers decide), each walking a stream of tiles.  A multiple of 8
     // keeps every workgroup's tiles on one XCD.
-    int64_t slots = (int64_t)device_cu_count(dev) * 2 / 8 * 8;
+    int per_cu = kernel_occupancy(dev, kid);
+    if (per_cu < 1) per_cu = 1;
+    int64_t slots = (int64_t)device_cu_count(dev) * per_cu / 8 * 8;
     if (slots < 8) slots = 8;
     if (const char* cap = std::getenv("TROPICAL_GEMM_MAX_WORKGROUPS")) {  // tuning knob
         long v = std::strtol(cap, nullptr, 10);
         if (v >= 8) slots = v / 8 * 8;
     }
     uint32_t grid = (uint32_t)(total < slots ? total : slots);
-    return launch(dev, (KernelId)(K_GEMM_TILED_MAXPLUS_F32 + ri), TROP_K_GEMM_TILED, grid, 256, &p,
-                  stream);
+    const int block = kernel_block(dev, kid);  // the launch bound the kernel was built with
+    if (block != 256 && block != 512)
+        return fail(TROP_ERR_HIP, std::string(kernel_name(kid)) + ": unexpected launch bound " +
+                                      std::to_string(block));
+    return launch(dev, kid, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
 }
 
 }  // namespace trop

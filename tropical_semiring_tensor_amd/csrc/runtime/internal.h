@@ -44,6 +44,11 @@ enum KernelId : int {
     K_GATHER_TILED_V16_N2,
     K_GATHER_TILED_V32_N2,
     K_GATHER_TILED_V64_N2,
+    K_GEMM_TILED_VO_MAXPLUS_F32,  // value only (no argmax output)
+    K_GEMM_TILED_VO_MINPLUS_F32,
+    K_GEMM_TILED_VO_MAXMUL_F32,
+    K_GEMM_TILED_VO_MAXPLUS_I32,
+    K_GEMM_TILED_VO_MINPLUS_I32,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
@@ -57,6 +62,10 @@ trop_status current_device(int* dev);
 trop_status ensure_module(int dev);
 // Compute units of a device whose module is loaded.
 int device_cu_count(int dev);
+// Workgroups of kernel `id` (at its launch bound) that one CU holds at once.
+int kernel_occupancy(int dev, KernelId id);
+// Threads per workgroup kernel `id` is built for (its launch bound).
+int kernel_block(int dev, KernelId id);
 
 // Enqueue kernel `id` (one by-value argument block) on `stream`.
 trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,

@@ -40,7 +40,9 @@ static const char* const kNames[K_COUNT] = {
     "trop_gather_naive",             "trop_gather_tiled_v16_n1",
     "trop_gather_tiled_v32_n1",      "trop_gather_tiled_v64_n1",
     "trop_gather_tiled_v16_n2",      "trop_gather_tiled_v32_n2",
-    "trop_gather_tiled_v64_n2",
+    "trop_gather_tiled_v64_n2",      "trop_gemm_tiled_vo_maxplus_f32",
+    "trop_gemm_tiled_vo_minplus_f32", "trop_gemm_tiled_vo_maxmul_f32",
+    "trop_gemm_tiled_vo_maxplus_i32", "trop_gemm_tiled_vo_minplus_i32",
 };
 
 const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
@@ -64,6 +66,8 @@ constexpr int kMaxDevices = 64;
 struct DeviceModule {
     hipModule_t module = nullptr;
     hipFunction_t fn[K_COUNT] = {};
+    int occupancy[K_COUNT] = {};  // resident workgroups per CU
+    int block[K_COUNT] = {};      // threads per workgroup (the kernel's launch bound)
     int cu_count = 0;
 };
 
@@ -130,7 +134,18 @@ trop_status ensure_module(int dev) {
             g_module_loads.fetch_add(1);
             for (int i = 0; i < K_COUNT && st == TROP_OK; ++i) {
                 e = hipModuleGetFunction(&dm->fn[i], dm->module, kNames[i]);
-                if (e != hipSuccess) st = hip_fail(e, kNames[i]);
+                if (e != hipSuccess) {
+                    st = hip_fail(e, kNames[i]);
+                    break;
+                }
+                e = hipFuncGetAttribute(&dm->block[i], HIP_FUNC_ATTRIBUTE_MAX_THREADS_PER_BLOCK, dm->fn[i]);
+                if (e != hipSuccess) {
+                    st = hip_fail(e, "hipFuncGetAttribute(max threads per block)");
+                    break;
+                }
+                e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&dm->occupancy[i], dm->fn[i],
+                                                                       dm->block[i], 0);
+                if (e != hipSuccess) st = hip_fail(e, "hipModuleOccupancyMaxActiveBlocksPerMultiprocessor");
             }
             if (st == TROP_OK) {
                 e = hipDeviceGetAttribute(&dm->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
@@ -151,6 +166,16 @@ trop_status ensure_module(int dev) {
 int device_cu_count(int dev) {
     DeviceModule* dm = g_dev[dev].load(std::memory_order_acquire);
     return dm ? dm->cu_count : 0;
+}
+
+int kernel_occupancy(int dev, KernelId id) {
+    DeviceModule* dm = g_dev[dev].load(std::memory_order_acquire);
+    return (dm && id >= 0 && id < K_COUNT) ? dm->occupancy[id] : 0;
+}
+
+int kernel_block(int dev, KernelId id) {
+    DeviceModule* dm = g_dev[dev].load(std::memory_order_acquire);
+    return (dm && id >= 0 && id < K_COUNT) ? dm->block[id] : 0;
 }
 
 trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,
