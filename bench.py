@@ -138,6 +138,13 @@ def main():
         log("[bench] traffic probe done")
         return
 
+    # Settle: about 0.3 s of untimed launches first, so the timed steps see
+    # the clocks the GPU holds under this load rather than its idle ramp.
+    settle_t0 = time.perf_counter()
+    while time.perf_counter() - settle_t0 < 0.3:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     log(f"[bench] workload 2 headline: warmup {args.warmup}, steps {args.steps}")
     for _ in range(args.warmup):
         step()
@@ -153,12 +160,14 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
     value_gops = ops / (ms_per_step * 1e-3) / 1e9
-    # per-launch kernel duration (events bracketing each launch)
-    per = timer.time(step, reps=max(10, args.steps), warmup=0)
-    kern_ms = per["median_ms"]
+    # One step is one launch of the GEMM kernel, back to back on one stream:
+    # the timed region's per-step time is the kernel's average duration.
+    kern_ms = ms_per_step
     achieved_t = ops / (kern_ms * 1e-3) / 1e12
+    # for reference, events bracketing single launches (adds launch overhead)
+    per = timer.time(step, reps=max(10, args.steps), warmup=0)
     log(f"[bench] workload 2: {ms_per_step * 1e3:.1f} us/step, {value_gops:.0f} GOPS, "
-        f"kernel {kern_ms * 1e3:.1f} us, wall {wall:.3f} s")
+        f"single-launch events {per['median_ms'] * 1e3:.1f} us, wall {wall:.3f} s")
 
     result = {
         "metric": "tropical GOPS (batched GEMM+argmax) % VALU peak; permute/gather GB/s % HBM",
@@ -184,6 +193,7 @@ def main():
             "traffic": traffic_from_profile(w["name"]),
             "kernel": "trop_gemm_tiled_maxplus_f32",
             "kernel_us": round(kern_ms * 1e3, 2),
+            "single_launch_event_us": round(per["median_ms"] * 1e3, 2),
             "frac_of_fp32_datasheet": round(achieved_t / FP32_DATASHEET_T, 4),
             "frac_of_isa_ceiling": round(achieved_t / ISA_CEILING_T, 4),
         },

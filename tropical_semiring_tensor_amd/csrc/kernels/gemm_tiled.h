@@ -18,7 +18,6 @@
 //    to the block's best.  That is the exact first winner: a chunk is
 //    recorded only when it holds a term above everything before it, and
 //    inside it the first term equal to the final value is that first winner.
-//    A wave skips the re-scan of an output slot that none of its lanes needs.
 //  * LDS holds both operands k-contiguous ([row][k] for A, [column][k] for
 //    B, rows padded by 4 words), so the main loop reads four k at a time
 //    per row or column with one 16-byte LDS read, and the re-scan reads its
@@ -57,29 +56,34 @@ constexpr int GEMM_RS = GEMM_THREADS / 16;
 constexpr int GEMM_TR = 64 / GEMM_RS;
 constexpr int GEMM_BM = 64;
 constexpr int GEMM_BN = 64;
-#ifndef TROP_GEMM_CH
-#define TROP_GEMM_CH 16
+constexpr int GEMM_CH = 16;  // argmax chunk (terms)
+// Chunk record: 1 = the running best flows through the chunk's max3 chain
+// and is compared with its value before the chunk (one compare, one
+// select; with an even number of chunks per slice the two values trade
+// registers with no copies); 0 = a separate per-chunk (+) is compared with
+// the running best (one compare, two selects).
+#ifndef TROP_GEMM_CHAIN_RECORD
+#define TROP_GEMM_CHAIN_RECORD 1
 #endif
-#ifndef TROP_GEMM_RESOLVE_SKIP
-#define TROP_GEMM_RESOLVE_SKIP 1
+constexpr bool GEMM_CHAIN_RECORD = TROP_GEMM_CHAIN_RECORD != 0;
+// LDS staging slice (terms) of the argmax and the value-only kernels
+#ifndef TROP_GEMM_SLICE_ARG
+#define TROP_GEMM_SLICE_ARG 64
 #endif
-constexpr int GEMM_CH = TROP_GEMM_CH;  // argmax chunk (terms): 8 or 16
-static_assert(GEMM_CH == 8 || GEMM_CH == 16, "chunks of 8 or 16 terms");
-#ifndef TROP_GEMM_SLICE
-#define TROP_GEMM_SLICE 32
+#ifndef TROP_GEMM_SLICE_VO
+#define TROP_GEMM_SLICE_VO 32
 #endif
 #ifndef TROP_GEMM_KBLK
 #define TROP_GEMM_KBLK 256
 #endif
-constexpr int GEMM_SL = TROP_GEMM_SLICE;  // LDS staging slice (terms)
-static_assert(GEMM_SL % GEMM_CH == 0, "a slice holds whole chunks");
-static_assert(TROP_GEMM_KBLK % GEMM_SL == 0, "a block holds whole slices");
 
 template <bool ARG>
 struct GemmCfg {
     // K terms resident in LDS: a block (argmax) or a ring of two slices
-    static constexpr int KB = ARG ? TROP_GEMM_KBLK : 2 * GEMM_SL;
-    static constexpr int NSL = KB / GEMM_SL;  // slices per block
+    static constexpr int SL = ARG ? TROP_GEMM_SLICE_ARG : TROP_GEMM_SLICE_VO;  // slice (terms)
+    static constexpr int KB = ARG ? TROP_GEMM_KBLK : 2 * SL;
+    static constexpr int NSL = KB / SL;  // slices per block
+    static_assert(SL % GEMM_CH == 0 && KB % SL == 0, "whole chunks per slice, whole slices per block");
     // LDS row length in words: 4 words of padding put rows r and r + 1 in
     // different 16-byte bank groups, so 16 lanes reading 16 consecutive rows
     // at one k take distinct banks
@@ -124,7 +128,15 @@ __device__ __forceinline__ int kc_k(int vi) { return ((vi >> 3) & 3) * 4 + 16 * 
 __device__ __forceinline__ int mc_row(int vi) { return (vi & 15) * 4; }
 __device__ __forceinline__ int mc_k(int vi) { return vi >> 4; }
 
-template <typename T, int NV, int LDR>
+// B's LDS rows are swizzled: logical column k of row j sits at k ^ bsw(j),
+// bsw(j) = 4 ((j / 16) mod 4).  That only permutes the 16-byte quads inside
+// each aligned group of four, so 16-byte reads stay whole, and it makes the
+// transposed stores of a row-contiguous B (16 rows 4 apart at 4 k per
+// instruction) hit distinct banks.  A thread's columns tx + 16 c all share
+// bsw = 4 c, a compile-time constant in the compute loop.
+__device__ __forceinline__ int bsw(int row) { return ((row >> 4) & 3) << 2; }
+
+template <typename T, int NV, int LDR, bool SWZ, int SL>
 struct OpLoad {
     using V = vec4<T>;
     const T* q0;       // element 0 of vector 0 of slice 0
@@ -146,23 +158,25 @@ struct OpLoad {
         vec = v16 != 0;
         mn_lim = mnl;
         k_lim = kl;
-        k_step = (int64_t)GEMM_SL * str_k;
+        k_step = (int64_t)SL * str_k;
         // vector v + 1 = vector index + GEMM_THREADS: the same row, k further
         // on by GEMM_THREADS / 16 (MN_CONTIG) or 16 GEMM_THREADS / 256
         // (K_CONTIG)
         kv = mn_c ? mc_k(GEMM_THREADS) : kc_k(GEMM_THREADS);
         v_step = kv * str_k;
         lds_v = kv;
+        // (the swizzle only touches bits 2-3 of k, and the slot offset and
+        // vector steps added later are multiples of 16)
         if (mn_c) {
             e_str = str_mn;
             k0 = mc_k(tid);
             mn = mc_row(tid);
-            lds0 = mc_row(tid) * LDR + mc_k(tid);
+            lds0 = mc_row(tid) * LDR + (mc_k(tid) ^ (SWZ ? bsw(mc_row(tid)) : 0));
         } else {
             e_str = str_k;
             k0 = kc_k(tid);
             mn = kc_row(tid);
-            lds0 = kc_row(tid) * LDR + kc_k(tid);
+            lds0 = kc_row(tid) * LDR + (kc_k(tid) ^ (SWZ ? bsw(kc_row(tid)) : 0));
         }
     }
 
@@ -178,8 +192,8 @@ struct OpLoad {
 
     __device__ __forceinline__ void load(int g, T pad, T (&r)[NV][4]) const {
         const T* q = q0 + (int64_t)g * k_step;
-        const int64_t kb = k0 + (int64_t)g * GEMM_SL;
-        const bool full = mn_full && (int64_t)(g + 1) * GEMM_SL <= k_lim;
+        const int64_t kb = k0 + (int64_t)g * SL;
+        const bool full = mn_full && (int64_t)(g + 1) * SL <= k_lim;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const T* qv = q + v * v_step;
@@ -261,13 +275,15 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
     using Cfg = GemmCfg<ARG>;
-    constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR;
+    constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR, GEMM_SL = Cfg::SL;
     constexpr int NV = 16 * GEMM_SL / GEMM_THREADS;  // vectors per thread, operand and slice
     static_assert(NV >= 1 && NV * GEMM_THREADS == 16 * GEMM_SL, "whole vectors per thread");
     constexpr int NQ = GEMM_SL / 4;         // k-quads per slice
     constexpr int QPC = GEMM_CH / 4;        // k-quads per chunk
     constexpr int CPS = GEMM_SL / GEMM_CH;  // chunks per slice
-    using L = OpLoad<T, NV, LDR>;
+    using LA = OpLoad<T, NV, LDR, false, GEMM_SL>;
+    using LB = OpLoad<T, NV, LDR, true, GEMM_SL>;
+    static_assert(GEMM_SL % 16 == 0 && LDR % 4 == 0, "slots and rows keep the swizzle inside 16-word groups");
     __shared__ __attribute__((aligned(16))) T As[GEMM_BM * LDR];
     __shared__ __attribute__((aligned(16))) T Bs[GEMM_BN * LDR];
 
@@ -282,7 +298,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     if (cL >= total || nslices == 0) return;  // K = 0 is handled by the fill kernel
     if (blockDim.x != GEMM_THREADS) return;   // launched with a block it was not built for
 
-    L la, lb;
+    LA la;
+    LB lb;
     la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid);
     lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid);
     const T* const Ag = static_cast<const T*>(p.A);
@@ -366,8 +383,9 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
             for (int r = 0; r < GEMM_TR; ++r) fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk);
-            T cm[GEMM_TR][4];  // argmax: (+) of the current chunk's terms
+            for (int c = 0; c < 4; ++c) fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * c);
+            T cm[GEMM_TR][4];    // argmax: (+) of the current chunk's terms
+            T prev[GEMM_TR][4];  // argmax: the best before the current chunk
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const int cur = q & 1, nxt = cur ^ 1;
@@ -377,18 +395,20 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         fa[nxt][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * (q + 1));
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * (q + 1));
+                        fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk +
+                                                                 4 * (((q + 1) & ~3) | (((q + 1) & 3) ^ c)));
                 }
 #pragma unroll
                 for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const V a = fa[cur][r], b = fb[cur][c];
-                        if constexpr (ARG) {
+                        if constexpr (ARG && !GEMM_CHAIN_RECORD) {
                             T v = (q % QPC == 0) ? R::add2(R::mul(a.x, b.x), R::mul(a.y, b.y))
                                                  : R::add3(cm[r][c], R::mul(a.x, b.x), R::mul(a.y, b.y));
                             cm[r][c] = R::add3(v, R::mul(a.z, b.z), R::mul(a.w, b.w));
                         } else {
+                            if (ARG && q % QPC == 0) prev[r][c] = best[r][c];
                             T v = R::add3(best[r][c], R::mul(a.x, b.x), R::mul(a.y, b.y));
                             best[r][c] = R::add3(v, R::mul(a.z, b.z), R::mul(a.w, b.w));
                         }
@@ -403,9 +423,13 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                             for (int c = 0; c < 4; ++c) {
                                 // one compare feeds both selects (a select,
                                 // unlike max, needs no NaN canonicalisation)
-                                const bool up = R::better(cm[r][c], best[r][c]);
-                                win[r][c] = up ? cid : win[r][c];
-                                best[r][c] = up ? cm[r][c] : best[r][c];
+                                if constexpr (GEMM_CHAIN_RECORD) {
+                                    win[r][c] = R::better(best[r][c], prev[r][c]) ? cid : win[r][c];
+                                } else {
+                                    const bool up = R::better(cm[r][c], best[r][c]);
+                                    win[r][c] = up ? cid : win[r][c];
+                                    best[r][c] = up ? cm[r][c] : best[r][c];
+                                }
                             }
                     }
                 }
@@ -415,35 +439,41 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
         if (bend) {
             if constexpr (ARG) {
                 // Re-scan the winning chunk of every output that improved in
-                // this block: the first term equal to the best.
+                // this block: the first term equal to the best.  Slots run in
+                // sequence with the 16-byte reads of the next slot issued
+                // before the current slot's scan.  A slot that did not improve
+                // scans chunk 0 and keeps its index.
+                constexpr int NS = GEMM_TR * 4;
+                V av[2][4], bv[2][4];
+                auto rs_load = [&](int n, int buf) {
+                    const int r = n / 4, c = n % 4;
+                    const int w = win[r][c] < 0 ? 0 : win[r][c];
+                    const T* ap = a_row + r * GEMM_RS * LDR + w * GEMM_CH;
+                    const T* bp = b_col + c * 16 * LDR + w * GEMM_CH;
 #pragma unroll
-                for (int r = 0; r < GEMM_TR; ++r)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const bool need = win[r][c] >= 0;
-                        if (!TROP_GEMM_RESOLVE_SKIP || __any(need)) {
-                            constexpr int NU = GEMM_CH / 4;
-                            const int w = need ? win[r][c] : 0;
-                            const V* ap = reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + w * GEMM_CH);
-                            const V* bp = reinterpret_cast<const V*>(b_col + c * 16 * LDR + w * GEMM_CH);
-                            V av[NU], bv[NU];
-#pragma unroll
-                            for (int u = 0; u < NU; ++u) {
-                                av[u] = ap[u];
-                                bv[u] = bp[u];
-                            }
-                            int f = GEMM_CH - 1;
-#pragma unroll
-                            for (int u = NU - 1; u >= 0; --u) {
-                                f = (R::mul(av[u].w, bv[u].w) == best[r][c]) ? 4 * u + 3 : f;
-                                f = (R::mul(av[u].z, bv[u].z) == best[r][c]) ? 4 * u + 2 : f;
-                                f = (R::mul(av[u].y, bv[u].y) == best[r][c]) ? 4 * u + 1 : f;
-                                f = (R::mul(av[u].x, bv[u].x) == best[r][c]) ? 4 * u : f;
-                            }
-                            idx[r][c] = need ? (int)blk_k0 + w * GEMM_CH + f : idx[r][c];
-                        }
-                        win[r][c] = -1;
+                    for (int u = 0; u < 4; ++u) {
+                        av[buf][u] = *reinterpret_cast<const V*>(ap + 4 * u);
+                        bv[buf][u] = *reinterpret_cast<const V*>(bp + 4 * (u ^ c));
                     }
+                };
+                rs_load(0, 0);
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const int r = n / 4, c = n % 4, cur = n & 1;
+                    if (n + 1 < NS) rs_load(n + 1, cur ^ 1);
+                    const T bst = best[r][c];
+                    int f = GEMM_CH - 1;
+#pragma unroll
+                    for (int u = 3; u >= 0; --u) {
+                        const V a = av[cur][u], b = bv[cur][u];
+                        f = (R::mul(a.w, b.w) == bst) ? 4 * u + 3 : f;
+                        f = (R::mul(a.z, b.z) == bst) ? 4 * u + 2 : f;
+                        f = (R::mul(a.y, b.y) == bst) ? 4 * u + 1 : f;
+                        f = (R::mul(a.x, b.x) == bst) ? 4 * u : f;
+                    }
+                    idx[r][c] = win[r][c] >= 0 ? (int)blk_k0 + win[r][c] * GEMM_CH + f : idx[r][c];
+                    win[r][c] = -1;
+                }
                 blk_k0 += Cfg::KB;
             }
 
