@@ -124,10 +124,15 @@ def test_diag_argument_errors(tb):
 def test_contract_plan_config5(tb):
     d = tb.tropical_contract_pair_describe("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
     assert "batch=b left=i right=k contracted=j" in d
-    assert "gemm batch=32 m=128 n=256 k=256" in d
-    assert "A=gather:tiled" in d and "B=gather:tiled" in d and "out=permute:tiled" in d
+    # the output order is (batch, B-side, A-side): the product is taken as
+    # B (x) A and lands in (b, k, i) with no output permute
+    assert "gemm B(x)A batch=32 m=256 n=128 k=256" in d
+    assert "A=gather:tiled" in d and "B=gather:tiled" in d and "out=direct" in d
     ws = tb.tropical_contract_pair_workspace_size("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
-    assert ws == 4 * (32 * 128 * 256 + 32 * 256 * 256 + 2 * 32 * 128 * 256)
+    assert ws == 4 * (32 * 128 * 256 + 32 * 256 * 256)
+    # the canonical order keeps A (x) B and permutes the output
+    d = tb.tropical_contract_pair_describe("iijb,kjb->kbi", (128, 128, 256, 32), (256, 256, 32))
+    assert "gemm A(x)B batch=32 m=128 n=256 k=256" in d and "out=permute:" in d
 
 
 def test_contract_plan_folds_canonical_operands(tb):

@@ -6,7 +6,9 @@
 // core only sees clean operands ("Structural lessons from OMEinsum"), the
 // operands are permuted into canonical order, one strided-batched tropical
 // GEMM runs, and its value and argmax are permuted into the output order
-// with one shared mapping ("Acceptance criteria").  Nothing leaves the
+// with one shared mapping ("Acceptance criteria") -- or, when the output
+// order is (batch, B-side labels, A-side labels), the product is taken as
+// B (x) A and lands in the output order with no permute.  Nothing leaves the
 // device and the host never waits: all intermediates live in the caller's
 // workspace and every step is enqueued on the caller's stream.  The same
 // section's advice to let GEMM strides absorb a permute "where the layout
@@ -42,6 +44,10 @@ struct Plan {
     int64_t nb = 1, M = 1, N = 1, K = 1;
     int64_t out_total = 1;
     bool a_fold = false, b_fold = false, c_direct = false;
+    // swap: the GEMM's left operand is B and its right operand is A, so that
+    // the product comes out as (batch, right, left), the output order
+    bool swap = false;
+    int64_t gm = 1, gn = 1;  // GEMM rows and columns
     trop_strides sA{}, sB{};
     GatherPlan ga{}, gb{}, gc{};
     size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, ws = 0;
@@ -226,21 +232,37 @@ trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* s
     for (size_t d = 0; d < B.sub.size(); ++d)
         if (B.stride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride in B");
 
-    const std::string canA = P.batch + P.left + P.contracted;
-    const std::string canB = P.batch + P.contracted + P.right;
-    const std::string canC = P.batch + P.left + P.right;
+    // Every (x) here is commutative bit for bit (IEEE add and multiply,
+    // saturating int32 add), so the product may be taken as B (x) A when
+    // that writes the output order directly: C[b][r][l] = (+)_k B[b][r][k]
+    // (x) A[b][k][l].  The contracted labels keep A-subscript order on both
+    // sides, so the argmax index means the same either way.
+    P.swap = (P.batch + P.left + P.right != P.lo) && (P.batch + P.right + P.left == P.lo);
+    const std::string rows = P.swap ? P.right : P.left;   // GEMM row labels
+    const std::string cols = P.swap ? P.left : P.right;   // GEMM column labels
+    P.gm = P.swap ? P.N : P.M;
+    P.gn = P.swap ? P.M : P.N;
+    const std::string canL = P.batch + rows + P.contracted;  // GEMM left operand
+    const std::string canR = P.batch + P.contracted + cols;  // GEMM right operand
+    const std::string canC = P.batch + rows + cols;
+    // ga / sA / a_fold describe the GEMM's left operand (A, or B when
+    // swapped), gb / sB / b_fold its right operand
+    const Operand& L = P.swap ? B : A;
+    const Operand& Rt = P.swap ? A : B;
+    const std::string& l_red = P.swap ? P.b_red : P.a_red;
+    const std::string& r_red = P.swap ? P.a_red : P.b_red;
 
-    P.a_fold = try_fold(P, A, P.a_red, P.batch, P.left, P.contracted, &P.sA);
+    P.a_fold = try_fold(P, L, l_red, P.batch, rows, P.contracted, &P.sA);
     if (!P.a_fold) {
-        st = plan_operand(P, A, canA, &P.ga);
+        st = plan_operand(P, L, canL, &P.ga);
         if (st != TROP_OK) return st;
-        P.sA = {P.K, 1, P.M * P.K};
+        P.sA = {P.K, 1, P.gm * P.K};
     }
-    P.b_fold = try_fold(P, B, P.b_red, P.batch, P.contracted, P.right, &P.sB);
+    P.b_fold = try_fold(P, Rt, r_red, P.batch, P.contracted, cols, &P.sB);
     if (!P.b_fold) {
-        st = plan_operand(P, B, canB, &P.gb);
+        st = plan_operand(P, Rt, canR, &P.gb);
         if (st != TROP_OK) return st;
-        P.sB = {P.N, 1, P.K * P.N};
+        P.sB = {P.gn, 1, P.K * P.gn};
     }
     P.c_direct = (canC == P.lo);
     if (!P.c_direct) {
@@ -264,11 +286,11 @@ trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* s
     size_t off = 0;
     if (!P.a_fold) {
         P.off_a = off;
-        off += align_up((size_t)(P.nb * P.M * P.K) * 4);
+        off += align_up((size_t)(P.nb * P.gm * P.K) * 4);
     }
     if (!P.b_fold) {
         P.off_b = off;
-        off += align_up((size_t)(P.nb * P.K * P.N) * 4);
+        off += align_up((size_t)(P.nb * P.K * P.gn) * 4);
     }
     if (!P.c_direct) {
         P.off_c = off;
@@ -283,12 +305,15 @@ trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* s
 std::string describe(const Plan& P) {
     char buf[512];
     std::snprintf(buf, sizeof(buf),
-                  "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm batch=%lld m=%lld "
+                  "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm %s batch=%lld m=%lld "
                   "n=%lld k=%lld; A=%s%s B=%s%s out=%s%s; workspace=%zu",
                   P.batch.c_str(), P.left.c_str(), P.right.c_str(), P.contracted.c_str(), P.a_red.c_str(),
-                  P.b_red.c_str(), (long long)P.nb, (long long)P.M, (long long)P.N, (long long)P.K,
-                  P.a_fold ? "fold" : "gather:", P.a_fold ? "" : gather_path_name(P.ga.path),
-                  P.b_fold ? "fold" : "gather:", P.b_fold ? "" : gather_path_name(P.gb.path),
+                  P.b_red.c_str(), P.swap ? "B(x)A" : "A(x)B", (long long)P.nb, (long long)P.gm,
+                  (long long)P.gn, (long long)P.K,
+                  (P.swap ? P.b_fold : P.a_fold) ? "fold" : "gather:",
+                  (P.swap ? P.b_fold : P.a_fold) ? "" : gather_path_name((P.swap ? P.gb : P.ga).path),
+                  (P.swap ? P.a_fold : P.b_fold) ? "fold" : "gather:",
+                  (P.swap ? P.a_fold : P.b_fold) ? "" : gather_path_name((P.swap ? P.ga : P.gb).path),
                   P.c_direct ? "direct" : "permute:", P.c_direct ? "" : gather_path_name(P.gc.path), P.ws);
     return buf;
 }
@@ -377,12 +402,15 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
 
-    // 1. unary pre-pass + permute into canonical operand order
-    const void* a_use = Aptr;
-    const void* b_use = Bptr;
+    // 1. unary pre-pass + permute into canonical operand order (a_* is the
+    // GEMM's left operand: A, or B when the product is taken as B (x) A)
+    const void* l_ptr = P.swap ? Bptr : Aptr;
+    const void* r_ptr = P.swap ? Aptr : Bptr;
+    const void* a_use = l_ptr;
+    const void* b_use = r_ptr;
     if (!P.a_fold) {
         void* dst = ws + P.off_a;
-        const void* in[1] = {Aptr};
+        const void* in[1] = {l_ptr};
         void* out[1] = {dst};
         st = run_gather(dev, P.ga, 1, in, out, semiring, dtype, s);
         if (st != TROP_OK) return st;
@@ -390,7 +418,7 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     }
     if (!P.b_fold) {
         void* dst = ws + P.off_b;
-        const void* in[1] = {Bptr};
+        const void* in[1] = {r_ptr};
         void* out[1] = {dst};
         st = run_gather(dev, P.gb, 1, in, out, semiring, dtype, s);
         if (st != TROP_OK) return st;
@@ -399,8 +427,8 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     // 2. batched GEMM into the canonical (batch, left, right) result
     void* c_gemm = P.c_direct ? C : static_cast<void*>(ws + P.off_c);
     int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
-    const trop_strides sC = {P.N, 1, P.M * P.N};
-    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.M, P.N, P.K, P.nb, s);
+    const trop_strides sC = {P.gn, 1, P.gm * P.gn};
+    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s);
     if (st != TROP_OK) return st;
     // 3. one paired permute of value and argmax into the output order
     if (!P.c_direct) {

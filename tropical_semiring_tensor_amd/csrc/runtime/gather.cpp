@@ -32,6 +32,31 @@ bool env_flag(const char* name) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+long env_long(const char* name, long dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    const long x = std::strtol(v, nullptr, 10);
+    return x > 0 ? x : dflt;
+}
+
+// Grid of a grid-stride streaming kernel with `work` thread-items: a few
+// workgroups per CU, each looping, keeps enough 16-byte requests in flight
+// without paying for hundreds of thousands of workgroup launches.
+uint32_t stream_grid(int dev, int64_t work) {
+    const int64_t per_cu = env_long("TROPICAL_GATHER_BLOCKS_PER_CU", 2);  // tuning knob
+    const int64_t cap = (int64_t)device_cu_count(dev) * per_cu;
+    const int64_t g = (work + 255) / 256;
+    return (uint32_t)(g < cap ? (g < 1 ? 1 : g) : cap);
+}
+
+// Grid of the tiled transpose: one workgroup per tile up to a cap of
+// resident workgroups, each looping over tiles.
+uint32_t tile_grid(int dev, int64_t tiles) {
+    const int64_t per_cu = env_long("TROPICAL_TILED_BLOCKS_PER_CU", 4);  // tuning knob
+    const int64_t cap = (int64_t)device_cu_count(dev) * per_cu;
+    return (uint32_t)(tiles < cap ? tiles : cap);
+}
+
 // Magic pair for floor(n / d), n < 2^31, d >= 2: m = floor(2^(31+s) / d) + 1
 // with s = ceil(log2 d); then floor(n / d) = umulhi(n, m) >> (s - 1).  The
 // error term n * (m * d - 2^(31+s)) / (d * 2^(31+s)) stays below 1/d, so
@@ -225,7 +250,7 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             }
             // the 32-bit vector path moves four vectors per thread and pass
             const int64_t work = vec ? (p.idx32 ? (p.total / 4 + 3) / 4 : p.total / 4) : p.total;
-            return launch(dev, K_GATHER_COPY, TROP_K_GATHER_COPY, grid_for(work, 256), 256, &p, stream);
+            return launch(dev, K_GATHER_COPY, TROP_K_GATHER_COPY, stream_grid(dev, work), 256, &p, stream);
         }
         case GP_TILED: {
             const int nd = p.ndim, P = p.ax_in, Q = nd - 1;
@@ -244,9 +269,8 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
                 const int base = ntensors == 2 ? K_GATHER_TILED_V16_N2 : K_GATHER_TILED_V16_N1;
                 kid = (KernelId)(base + (tp == 64 ? 2 : (tp == 32 ? 1 : 0)));
             }
-            int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
-            uint32_t grid = nblk > kMaxGrid ? kMaxGrid : (uint32_t)nblk;
-            return launch(dev, kid, TROP_K_GATHER_TILED, grid, 256, &p, stream);
+            const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
+            return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
         }
         case GP_NAIVE:
             return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);
