@@ -96,10 +96,12 @@ class Oracle:
                                        i32, _I32P, _I64P, vp,
                                        i32, _I32P, vp, _I32P,
                                        i32, _I32P]
+        L.orc_gemm_backward.argtypes = [i32, vp, _I64P, vp, _I64P, _I32P, vp, _I64P,
+                                        vp, _I64P, vp, _I64P, i64, i64, i64, i64]
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         for fn in ("orc_gemm", "orc_gemm_points", "orc_permute", "orc_diag_gather",
-                   "orc_einsum_brute"):
+                   "orc_einsum_brute", "orc_gemm_backward"):
             getattr(L, fn).restype = ctypes.c_int
 
     @staticmethod
@@ -167,6 +169,50 @@ class Oracle:
                                       _ptr(vals), args.ctypes.data_as(_I32P))
         self._check(st, "orc_gemm_points")
         return vals, args
+
+    def gemm_backward(self, sr, argmax, G, A=None, B=None, k=None, grad_a=True, grad_b=True):
+        """Gradients routed along the argmax (winner routing).
+
+        argmax and G are (batch, m, n) (int32 / float32, same strides); A
+        (batch, m, k) and B (batch, k, n) are float32 and needed for max-mul
+        only.  k is the contracted size (taken from A or B when omitted).
+        Returns (dA (batch, m, k), dB (batch, k, n)) as float32, each None
+        if not requested.
+        """
+        argmax = np.asarray(argmax)
+        G = np.asarray(G)
+        if argmax.ndim == 2:
+            argmax, G = argmax[None], G[None]
+        if argmax.dtype != np.int32 or G.dtype != np.float32 or argmax.shape != G.shape:
+            raise TypeError("argmax must be int32 and G float32 of one shape")
+        if _elem_strides(argmax) != _elem_strides(G):
+            G = np.ascontiguousarray(G)
+            argmax = np.ascontiguousarray(argmax)
+        batch, m, n = argmax.shape
+        A = None if A is None else np.asarray(A, dtype=np.float32)
+        B = None if B is None else np.asarray(B, dtype=np.float32)
+        if A is not None and A.ndim == 2:
+            A = A[None]
+        if B is not None and B.ndim == 2:
+            B = B[None]
+        if k is None:
+            k = A.shape[2] if A is not None else B.shape[1]
+        sc = _elem_strides(argmax)
+        sa = _elem_strides(A) if A is not None else [0, 0, 0]
+        sb = _elem_strides(B) if B is not None else [0, 0, 0]
+        dA = np.empty((batch, m, k), dtype=np.float32) if grad_a else None
+        dB = np.empty((batch, k, n), dtype=np.float32) if grad_b else None
+        sda = _elem_strides(dA) if grad_a else [0, 0, 0]
+        sdb = _elem_strides(dB) if grad_b else [0, 0, 0]
+        nul = ctypes.c_void_p(0)
+        st = self.lib.orc_gemm_backward(
+            _sr_code(sr), _ptr(A) if A is not None else nul, _i64([sa[1], sa[2], sa[0]]),
+            _ptr(B) if B is not None else nul, _i64([sb[1], sb[2], sb[0]]),
+            argmax.ctypes.data_as(_I32P), _ptr(G), _i64([sc[1], sc[2], sc[0]]),
+            _ptr(dA) if grad_a else nul, _i64([sda[1], sda[2], sda[0]]),
+            _ptr(dB) if grad_b else nul, _i64([sdb[1], sdb[2], sdb[0]]), m, n, k, batch)
+        self._check(st, "orc_gemm_backward")
+        return dA, dB
 
     # -- permute ----------------------------------------------------------
     def permute(self, x, perm):

@@ -27,6 +27,9 @@
  *    that never beats the zero element (a NaN, or a term equal to zero)
  *    leaves the argmax at 0.
  *
+ *  - orc_gemm_backward: gradients of the product routed along its argmax
+ *    (winner routing), see the function's comment.
+ *
  *  - orc_permute: the generic N-d permute of omeinsum-rs issue #52 "GPU
  *    tropical path: keep tensors device-resident + device-side permute",
  *    section "Resolved design for step 3", kernel (a): for each output
@@ -217,6 +220,79 @@ int orc_gemm_points(int sr, int dt,
         void* dst = (char*)cvals + 4 * p;
         gemm_one(sr, dt, A, sA, B, sB, k, pts[3 * p], pts[3 * p + 1], pts[3 * p + 2],
                  dst, &args[p]);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* backward: winner routing                                             */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Gradients of L = sum_{b,i,j} G[b][i][j] * C[b][i][j] through the tropical
+ * product, routed along its argmax.  The pages ask for the backward to stay
+ * consistent with the CPU path and to use the argmax the forward produces:
+ * omeinsum-rs issue #52 ("Acceptance criteria": forward, backward and argmax
+ * bit-for-bit; the u32 argmax buffer is the "tropical winner-routing"),
+ * tropical-gemm PR #35 (the batched autograd functions route the gradient
+ * through the argmax with scatter_add_ / gather, review comments), and the
+ * rustytorch commit "rtx-backend-cuda: native index_select / index_add"
+ * (scatter-add as a deterministic walk of the adjoint of the selection).
+ *
+ * With k* = argmax[b][i][j], C[b][i][j] = A[b][i][k*] (x) B[b][k*][j], so
+ *     dA[b][i][k] = sum over j with k* = k of G[b][i][j] * dC/dA
+ *     dB[b][k][j] = sum over i with k* = k of G[b][i][j] * dC/dB
+ * where dC/dA = dC/dB = 1 for max-plus and min-plus (x = +), and
+ * dC/dA = B[b][k*][j], dC/dB = A[b][i][k*] for max-mul (x = *).  Every
+ * output that has an argmax routes its gradient, also one that nothing beat
+ * (its argmax is 0).  Each sum starts at +0.0 and adds its terms in
+ * ascending j (dA) or ascending i (dB), one IEEE multiply (max-mul) and one
+ * IEEE add per term.  Argmax entries outside [0, k) route nothing.  The
+ * float operands A and B are read for max-mul only and may be NULL
+ * otherwise; either gradient may be NULL (not computed).  Strides: s[0] row,
+ * s[1] column, s[2] batch; G shares the argmax's strides sC.
+ */
+int orc_gemm_backward(int sr, const float* A, const int64_t* sA,
+                      const float* B, const int64_t* sB,
+                      const int32_t* argmax, const float* G, const int64_t* sC,
+                      float* dA, const int64_t* sdA, float* dB, const int64_t* sdB,
+                      int64_t m, int64_t n, int64_t k, int64_t batch)
+{
+    if (sr < ORC_MAX_PLUS || sr > ORC_MAX_MUL) return ORC_BAD_ARG;
+    if (m < 0 || n < 0 || k < 0 || batch < 0) return ORC_BAD_ARG;
+    if (sr == ORC_MAX_MUL && ((dA && !B) || (dB && !A))) return ORC_BAD_ARG;
+    const int mul = sr == ORC_MAX_MUL;
+    if (dA) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < batch * m; ++r) {
+            int64_t b = r / m, i = r % m;
+            for (int64_t kk = 0; kk < k; ++kk) dA[b * sdA[2] + i * sdA[0] + kk * sdA[1]] = 0.0f;
+            for (int64_t j = 0; j < n; ++j) {
+                int64_t c = b * sC[2] + i * sC[0] + j * sC[1];
+                int32_t ks = argmax[c];
+                if (ks < 0 || ks >= k) continue;
+                float v = G[c];
+                if (mul) v = v * B[b * sB[2] + ks * sB[0] + j * sB[1]];
+                float* d = &dA[b * sdA[2] + i * sdA[0] + ks * sdA[1]];
+                *d = *d + v;
+            }
+        }
+    }
+    if (dB) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < batch * n; ++r) {
+            int64_t b = r / n, j = r % n;
+            for (int64_t kk = 0; kk < k; ++kk) dB[b * sdB[2] + kk * sdB[0] + j * sdB[1]] = 0.0f;
+            for (int64_t i = 0; i < m; ++i) {
+                int64_t c = b * sC[2] + i * sC[0] + j * sC[1];
+                int32_t ks = argmax[c];
+                if (ks < 0 || ks >= k) continue;
+                float v = G[c];
+                if (mul) v = v * A[b * sA[2] + i * sA[0] + ks * sA[1]];
+                float* d = &dB[b * sdB[2] + ks * sdB[0] + j * sdB[1]];
+                *d = *d + v;
+            }
+        }
     }
     return ORC_OK;
 }

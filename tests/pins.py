@@ -10,7 +10,9 @@ the oracle disagrees with:
     associativity on exactly representable data, transpose symmetry),
   * a textbook algorithm (Floyd-Warshall shortest paths vs min-plus
     repeated squaring),
-  * brute-force enumeration (the einsum path vs the decomposed path).
+  * brute-force enumeration (the einsum path vs the decomposed path),
+  * for the backward: torch autograd, the adjoint identity, and finite
+    differences of the oracle's own forward.
 
 They are deliberately small so that tests/test_oracle_mutants.py can run
 them all against many planted-mistake builds of the oracle in seconds.
@@ -440,10 +442,108 @@ def pin_contract_vs_brute(orc):
             _bits_equal(C, Cb, f"contract-with-reduce {spec} {sr}")
 
 
+# ----------------------------------------------------------------------
+# backward (winner routing)
+# ----------------------------------------------------------------------
+
+def pin_golden_backward(orc):
+    for case in gio.load("backward_3x3.json")["cases"]:
+        A = gio.array(case["A"], "f32")[None]
+        B = gio.array(case["B"], "f32")[None]
+        C, I = orc.gemm(case["semiring"], A, B)
+        _eq(I[0], np.array(case["argmax"]), case["name"] + " forward argmax")
+        G = gio.array(case["G"], "f32")[None]
+        dA, dB = orc.gemm_backward(case["semiring"], I, G, A, B)
+        _bits_equal(dA[0], gio.array(case["dA"], "f32"), case["name"] + " dA")
+        _bits_equal(dB[0], gio.array(case["dB"], "f32"), case["name"] + " dB")
+
+
+def pin_backward_torch_autograd(orc):
+    """torch autograd through the materialised terms and max/min over k:
+    torch.max(dim) / torch.min(dim) return the first extreme index and their
+    backward routes the gradient to it.  Integer-valued (or dyadic) data
+    keeps every sum exact, so the summation order cannot matter."""
+    g = torch.Generator().manual_seed(41)
+    for sr in SR:
+        for shape in ((2, 5, 7, 6), (1, 9, 3, 11), (3, 4, 16, 4)):
+            b, m, k, n = shape
+            if sr == "max_mul":
+                A = torch.randint(1, 5, (b, m, k), generator=g).float() * 0.5
+                B = torch.randint(1, 5, (b, k, n), generator=g).float() * 0.25
+            else:
+                A = torch.randint(-4, 5, (b, m, k), generator=g).float()
+                B = torch.randint(-4, 5, (b, k, n), generator=g).float()
+            G = torch.randint(-3, 4, (b, m, n), generator=g).float()
+            At = A.clone().requires_grad_(True)
+            Bt = B.clone().requires_grad_(True)
+            T = At[:, :, :, None] * Bt[:, None, :, :] if sr == "max_mul" else At[:, :, :, None] + Bt[:, None, :, :]
+            val, arg = (T.min(dim=2) if sr == "min_plus" else T.max(dim=2))
+            (val * G).sum().backward()
+            C, I = orc.gemm(sr, A.numpy(), B.numpy())
+            _eq(I, arg.to(torch.int32).numpy(), f"{sr} {shape} argmax vs torch")
+            dA, dB = orc.gemm_backward(sr, I, G.numpy(), A.numpy(), B.numpy())
+            _bits_equal(dA, At.grad.numpy(), f"{sr} {shape} dA vs torch autograd")
+            _bits_equal(dB, Bt.grad.numpy(), f"{sr} {shape} dB vs torch autograd")
+
+
+def pin_backward_adjoint_identity(orc):
+    """<G, dC> = <dA, delta_A> + <dB, delta_B>, where dC is the first-order
+    change of C along (delta_A, delta_B) with the argmax held fixed: the
+    adjoint identity that autograd relies on.  Integer data: exact."""
+    g = np.random.default_rng(5)
+    for sr in SR:
+        b, m, k, n = 2, 6, 9, 7
+        if sr == "max_mul":
+            A = g.integers(1, 5, (b, m, k)).astype(np.float32)
+            B = g.integers(1, 5, (b, k, n)).astype(np.float32)
+        else:
+            A = g.integers(-5, 6, (b, m, k)).astype(np.float32)
+            B = g.integers(-5, 6, (b, k, n)).astype(np.float32)
+        G = g.integers(-4, 5, (b, m, n)).astype(np.float32)
+        dltA = g.integers(-3, 4, (b, m, k)).astype(np.float64)
+        dltB = g.integers(-3, 4, (b, k, n)).astype(np.float64)
+        _, I = orc.gemm(sr, A, B)
+        bb, ii, jj = np.meshgrid(np.arange(b), np.arange(m), np.arange(n), indexing="ij")
+        if sr == "max_mul":
+            dC = dltA[bb, ii, I] * B[bb, I, jj] + A[bb, ii, I] * dltB[bb, I, jj]
+        else:
+            dC = dltA[bb, ii, I] + dltB[bb, I, jj]
+        dA, dB = orc.gemm_backward(sr, I, G, A, B)
+        lhs = float((G.astype(np.float64) * dC).sum())
+        rhs = float((dA.astype(np.float64) * dltA).sum() + (dB.astype(np.float64) * dltB).sum())
+        assert lhs == rhs, f"{sr}: adjoint identity {lhs} != {rhs}"
+
+
+def pin_backward_finite_difference(orc):
+    """Against the forward itself: A's entries are distinct multiples of
+    100 and B's distinct even numbers below 98, so the terms of any output
+    are distinct and at least 2 apart; raising one entry of A or B by 1/2
+    then changes no winner, and L = sum G * C moves by exactly 1/2 * dL/dx
+    (max-plus, min-plus)."""
+    g = np.random.default_rng(8)
+    for sr in ("max_plus", "min_plus"):
+        b, m, k, n = 1, 5, 6, 4
+        A = (g.permutation(m * k) * 100).astype(np.float32).reshape(b, m, k)
+        B = (g.permutation(49)[: k * n] * 2).astype(np.float32).reshape(b, k, n)
+        G = g.integers(-3, 4, (b, m, n)).astype(np.float32)
+        C, I = orc.gemm(sr, A, B)
+        dA, dB = orc.gemm_backward(sr, I, G, A, B)
+        L0 = float((G.astype(np.float64) * C).sum())
+        for which, X, D in (("A", A, dA), ("B", B, dB)):
+            for idx in np.ndindex(X.shape):
+                Xp = X.copy()
+                Xp[idx] += 0.5
+                Cp, _ = orc.gemm(sr, Xp, B) if which == "A" else orc.gemm(sr, A, Xp)
+                L1 = float((G.astype(np.float64) * Cp).sum())
+                assert L1 - L0 == 0.5 * float(D[idx]), f"{sr} d{which}{idx}: {L1 - L0} vs {0.5 * D[idx]}"
+
+
 ALL_PINS = [
     pin_golden_gemm, pin_golden_special_values, pin_golden_einsum,
     pin_torch_crosscheck, pin_torch_random_normal, pin_unit_and_zero,
     pin_empty_and_k0, pin_associativity, pin_transpose_symmetry,
     pin_floyd_warshall, pin_semirings_distinct, pin_points, pin_permute,
     pin_diag, pin_brute_vs_torch, pin_contract_vs_brute,
+    pin_golden_backward, pin_backward_torch_autograd, pin_backward_adjoint_identity,
+    pin_backward_finite_difference,
 ]

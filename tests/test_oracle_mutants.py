@@ -60,6 +60,17 @@ MUTANTS = [
      "bestf = t;\n                    arg = (int32_t)(p > 0 ? p - 1 : 0);"),
     ("points_swap_ij",
      "pts[3 * p], pts[3 * p + 1], pts[3 * p + 2]", "pts[3 * p], pts[3 * p + 2], pts[3 * p + 1]"),
+    # backward (winner routing)
+    ("bwd_maxmul_no_factor_dA", "if (mul) v = v * B[b * sB[2] + ks * sB[0] + j * sB[1]];", ""),
+    ("bwd_maxmul_factor_wrong_k_dB", "if (mul) v = v * A[b * sA[2] + i * sA[0] + ks * sA[1]];",
+     "if (mul) v = v * A[b * sA[2] + i * sA[0] + 0 * sA[1]];"),
+    ("bwd_dB_routed_to_next_k", "float* d = &dB[b * sdB[2] + ks * sdB[0] + j * sdB[1]];",
+     "float* d = &dB[b * sdB[2] + ((ks + 1) % k) * sdB[0] + j * sdB[1]];"),
+    ("bwd_dA_drops_last_j", "for (int64_t j = 0; j < n; ++j) {\n                int64_t c",
+     "for (int64_t j = 0; j < n - 1; ++j) {\n                int64_t c"),
+    ("bwd_dA_starts_at_one", "dA[b * sdA[2] + i * sdA[0] + kk * sdA[1]] = 0.0f;",
+     "dA[b * sdA[2] + i * sdA[0] + kk * sdA[1]] = 1.0f;"),
+    ("bwd_gradient_ignored", "float v = G[c];", "float v = 1.0f;"),
 ]
 
 
