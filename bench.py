@@ -263,6 +263,30 @@ def other_workloads(torch, tb, inputs, timer, dev):
         del Ad, Bd, C, I
         torch.cuda.empty_cache()
 
+    # backward (winner routing) of the headline product: grad_a and grad_b
+    # from its argmax and an N(0, 1) upstream gradient
+    w = inputs.WORKLOADS[2]
+    A, B = inputs.gemm_operands(2)
+    Ad, Bd = A.to(dev), B.to(dev)
+    C = torch.empty(w["batch"], w["m"], w["n"], device=dev)
+    I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
+    tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, I)
+    G = torch.randn(w["batch"], w["m"], w["n"], generator=torch.Generator().manual_seed(22)).to(dev)
+    gA = torch.empty(w["batch"], w["m"], w["k"], device=dev)
+    gB = torch.empty(w["batch"], w["k"], w["n"], device=dev)
+    fwd_bwd = lambda: tb.tropical_gemm_backward("max_plus", I, G, k=w["k"], grad_a=gA, grad_b=gB)
+    b2b = back_to_back(torch, fwd_bwd)
+    cold = timer.time(fwd_bwd, reps=reps, warmup=1, flush=flush)
+    # algorithmic bytes: argmax and gradient read, grad_a and grad_b written
+    nbytes = 4 * (2 * C.numel() + gA.numel() + gB.numel())
+    out["backward_maxplus_f32_b64_256"] = {
+        "back_to_back_us": round(b2b * 1e3, 2), "cold_us": round(cold["median_ms"] * 1e3, 2),
+        "bytes": nbytes, "back_to_back_GBs": round(nbytes / (b2b * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "launches": 2}
+    log(f"[bench] backward (workload 2): {out['backward_maxplus_f32_b64_256']}")
+    del Ad, Bd, C, I, G, gA, gB
+    torch.cuda.empty_cache()
+
     # workload 5: the einsum path, whole and per kernel
     A, B = inputs.einsum_operands()
     Ad, Bd = A.to(dev), B.to(dev)

@@ -2,8 +2,9 @@
  * tropical.h -- C ABI of libtropical.so, the MI355X (gfx950) tropical
  * contraction hot path.
  *
- * Four operations, all device-resident and enqueued on a caller stream:
+ * Five operations, all device-resident and enqueued on a caller stream:
  *   tropical_gemm_strided_batched  batched tropical matrix product + argmax
+ *   tropical_gemm_backward         gradients routed along that argmax
  *   tropical_permute               N-d permute of one or two 4-byte tensors
  *   tropical_diag_gather           repeated-label diagonal / trace pre-pass
  *   tropical_contract_pair         one pairwise einsum built from the three
@@ -20,7 +21,12 @@
  *           "Structural lessons from OMEinsum" (unary pre-pass, then permute,
  *           batched GEMM, output permute); "Acceptance criteria"
  *           (intermediates stay in device memory, context and module created
- *           once, value and argmax permuted with one identical mapping).
+ *           once, value and argmax permuted with one identical mapping;
+ *           forward, backward and argmax consistent with the CPU path, the
+ *           argmax buffer being the "tropical winner-routing").
+ *   [RT]    rustytorch commit "rtx-backend-cuda: native index_select /
+ *           index_add" -- scatter-add as a deterministic walk of the
+ *           adjoint of the selection, no atomics, bit-identical to the host.
  *
  * Conventions for every entry point
  *   - Element strides and sizes are counted in ELEMENTS, not bytes.
@@ -94,6 +100,7 @@ typedef enum {
     TROP_K_GATHER_TILED = 4, /* permute/gather through an LDS tile       */
     TROP_K_GATHER_NAIVE = 5, /* permute/gather, one thread per element   */
     TROP_K_GATHER_REDUCE = 6,/* gather with a (+)-reduction (trace)      */
+    TROP_K_GEMM_BACKWARD = 7,/* gradient routed along the argmax         */
     TROP_K_FAMILIES = 8
 } trop_kernel_family;
 
@@ -141,6 +148,44 @@ TROP_API trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_
                                           void* C, trop_strides sC, int32_t* argmax,
                                           int64_t m, int64_t n, int64_t k, int64_t batch,
                                           void* stream);
+
+/*
+ * Backward of tropical_gemm_strided_batched: the gradients of
+ * L = sum_{b,i,j} grad_c[b][i][j] * C[b][i][j] routed along the argmax the
+ * forward produced (winner routing, [I52] "Acceptance criteria"; the
+ * scatter-add of [PR35]'s batched autograd functions, done as in [RT]):
+ *   grad_a[b][i][k] = sum over j with argmax[b][i][j] = k of
+ *                     grad_c[b][i][j] * w,  w = 1 (max-plus, min-plus)
+ *                                           or B[b][k][j] (max-mul)
+ *   grad_b[b][k][j] = sum over i with argmax[b][i][j] = k of
+ *                     grad_c[b][i][j] * w,  w = 1 or A[b][i][k]
+ * Each sum starts at +0.0 and adds its terms in ascending j (grad_a) or
+ * ascending i (grad_b), one IEEE multiply and one IEEE add per term, with no
+ * atomics: results are deterministic and bit-identical to that sequential
+ * loop.  Every output routes its gradient, also one that nothing beat
+ * (argmax 0); argmax entries outside [0, k) route nothing.  Every element of
+ * the requested gradients is written (zeros where nothing routes).
+ *
+ * dtype: of A and B.  A and B are read for max-mul only (float32, required
+ *   there, may be NULL otherwise); max-plus and min-plus work for float32
+ *   and int32 products alike since only the argmax is read.
+ * argmax (int32) and grad_c (float32) share the strides sC.
+ * grad_a (batch, m, k) with strides sGA, grad_b (batch, k, n) with strides
+ *   sGB: float32 device pointers, either may be NULL (not computed); they
+ *   must not overlap each other or the inputs.
+ * m, n, k, batch >= 0.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, negative size or stride,
+ *   max-mul without A / B), TROP_ERR_UNSUPPORTED (int32 max-mul),
+ *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ */
+TROP_API trop_status tropical_gemm_backward(trop_semiring semiring, trop_dtype dtype,
+                                   const void* A, trop_strides sA,
+                                   const void* B, trop_strides sB,
+                                   const int32_t* argmax, const float* grad_c, trop_strides sC,
+                                   float* grad_a, trop_strides sGA,
+                                   float* grad_b, trop_strides sGB,
+                                   int64_t m, int64_t n, int64_t k, int64_t batch,
+                                   void* stream);
 
 /*
  * N-d permute ([I52] "Resolved design for step 3", kernel (a)):
@@ -194,7 +239,12 @@ TROP_API trop_status tropical_contract_pair_workspace_size(const char* spec, con
  *      contracted) and of B into (batch, contracted, right);
  *   2. one strided-batched tropical GEMM with argmax;
  *   3. one paired permute of value and argmax into the output order.
- * An operand already in canonical contiguous order is used in place.
+ * When the output order is (batch, right, left) the product is taken as
+ * B (x) A instead -- B into (batch, right, contracted), A into (batch,
+ * contracted, left) -- and lands in the output order with no step 3 (every
+ * (x) here is commutative bit for bit, so values and argmax are the same).
+ * An operand already collapsible to a batched matrix with a unit row or
+ * column stride is used in place.
  * spec: "lhs,rhs->out" with single-letter labels a-z A-Z, explicit output,
  *   no ellipsis; every output label appears in an operand, output labels
  *   are distinct.  batch labels are in A, B and out; left in A and out;

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "TROP_OK", 1: "TROP_ERR_INVALID_ARGUMENT", 2: "TROP_ERR_UNSUP
 SEMIRINGS = {"max_plus": 0, "min_plus": 1, "max_mul": 2}
 F32, I32 = 0, 1
 KERNEL_FAMILIES = ["gemm_tiled", "gemm_simple", "fill", "gather_copy", "gather_tiled",
-                   "gather_naive", "gather_reduce"]
+                   "gather_naive", "gather_reduce", "gemm_backward"]
 MAX_DIMS = 8
 
 
@@ -67,6 +67,9 @@ def lib():
     L.tropical_init.argtypes = [i32]
     L.tropical_gemm_strided_batched.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp,
                                                 trop_strides, vp, i64, i64, i64, i64, vp]
+    L.tropical_gemm_backward.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp, vp,
+                                         trop_strides, vp, trop_strides, vp, trop_strides,
+                                         i64, i64, i64, i64, vp]
     L.tropical_permute.argtypes = [sz, i32, I64P, I64P, I32P, i32, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), vp]
     L.tropical_diag_gather.argtypes = [i32, i32, i32, I64P, I64P, I32P, i32, I32P, vp, vp, vp]
@@ -79,7 +82,7 @@ def lib():
     L.tropical_last_error.restype = ctypes.c_char_p
     L.tropical_get_stats.argtypes = [ctypes.POINTER(trop_stats)]
     L.tropical_reset_stats.restype = None
-    for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_permute",
+    for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_gemm_backward", "tropical_permute",
                "tropical_diag_gather", "tropical_contract_pair_workspace_size",
                "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
@@ -155,6 +158,43 @@ def tropical_gemm_strided_batched(semiring, A, B, C, argmax=None, stream=None):
                                              _stream(stream))
     _check(st, "tropical_gemm_strided_batched")
     return C, argmax
+
+
+def tropical_gemm_backward(semiring, argmax, grad_c, A=None, B=None, k=None, grad_a=True,
+                           grad_b=True, stream=None):
+    """Gradients of sum(grad_c * C) routed along the forward's argmax.
+
+    argmax (int32) and grad_c (float32): (batch, m, n) with equal strides.
+    A (batch, m, k) and B (batch, k, n) are read for max-mul only.  k is the
+    contracted size (from A or B when omitted).  grad_a / grad_b: True to
+    allocate (float32, contiguous), a tensor to fill, or None to skip.
+    Returns (grad_a, grad_b).
+    """
+    I3, G3 = _as3(argmax), _as3(grad_c)
+    if I3.stride() != G3.stride() or I3.shape != G3.shape:
+        raise ValueError("argmax and grad_c must share shape and strides")
+    batch, m, n = I3.shape
+    A3 = _as3(A) if A is not None else None
+    B3 = _as3(B) if B is not None else None
+    if k is None:
+        k = A3.shape[2] if A3 is not None else B3.shape[1]
+    dev = I3.device
+    if grad_a is True:
+        grad_a = torch.empty(batch, m, k, dtype=torch.float32, device=dev)
+    if grad_b is True:
+        grad_b = torch.empty(batch, k, n, dtype=torch.float32, device=dev)
+    ga3 = _as3(grad_a) if grad_a is not None else None
+    gb3 = _as3(grad_b) if grad_b is not None else None
+
+    def strides(t):
+        return trop_strides(t.stride(1), t.stride(2), t.stride(0)) if t is not None else trop_strides(0, 0, 0)
+
+    dt = _dt(A3) if A3 is not None else (_dt(B3) if B3 is not None else F32)
+    st = lib().tropical_gemm_backward(_sr(semiring), dt, _ptr(A3), strides(A3), _ptr(B3), strides(B3),
+                                      _ptr(I3), _ptr(G3), strides(I3), _ptr(ga3), strides(ga3),
+                                      _ptr(gb3), strides(gb3), m, n, int(k), batch, _stream(stream))
+    _check(st, "tropical_gemm_backward")
+    return grad_a, grad_b
 
 
 def tropical_permute(x, perm, out=None, x2=None, out2=None, stream=None):

@@ -69,3 +69,20 @@ struct TropGatherParams {
     int64_t rstride[TROP_MAX_DIMS];
     int64_t rtotal;
 };
+
+// Backward (winner routing): one segmented histogram, either the rows of
+// grad_a (segments i, items j, bins k) or the columns of grad_b (segments
+// j, items i, bins k).  The max-mul weight of item t with key k sits at
+// w + b * w_batch + k * w_key + t * w_item.
+struct TropBackwardParams {
+    const int32_t* idx;  // argmax
+    const float* grad;   // upstream gradient, strides of argmax
+    const float* w;      // max-mul weight operand (B for grad_a, A for grad_b)
+    float* out;          // grad_a or grad_b
+    int64_t c_batch, c_seg, c_item;  // argmax / gradient strides
+    int64_t w_batch, w_key, w_item;  // weight operand strides
+    int64_t o_batch, o_seg, o_bin;   // output strides
+    int64_t segs, batch, items, bins;
+    int32_t mul;  // max-mul: multiply by the weight
+    int32_t pad_;
+};

@@ -1,6 +1,7 @@
 // The one gfx950 code object of libtropical.so: every kernel entry point.
 // Built with hipcc --genco and embedded in the library, which loads it once
 // per device with hipModuleLoadData and looks the entry points up by name.
+#include "backward_kernels.h"
 #include "gather_kernels.h"
 #include "gemm_kernels.h"
 
@@ -54,3 +55,22 @@ TROP_TILED_VEC(64, 2)
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
     gather_naive_body(p);
 }
+
+#define TROP_BACKWARD(NB)                                                                        \
+    extern "C" __global__ __launch_bounds__(GBW_THREADS) void trop_gemm_backward_b##NB(          \
+        TropBackwardParams p) {                                                                  \
+        gemm_backward_body<NB>(p);                                                               \
+    }
+TROP_BACKWARD(256)
+TROP_BACKWARD(1024)
+TROP_BACKWARD(4096)
+
+#define TROP_BACKWARD_LANE(NAME, MUL, VEC)                                                       \
+    extern "C" __global__ __launch_bounds__(64) void trop_gemm_backward_lane_##NAME(             \
+        TropBackwardParams p) {                                                                  \
+        gemm_backward_lane_body<MUL, VEC>(p);                                                    \
+    }
+TROP_BACKWARD_LANE(plus, false, false)
+TROP_BACKWARD_LANE(plus_vec, false, true)
+TROP_BACKWARD_LANE(mul, true, false)
+TROP_BACKWARD_LANE(mul_vec, true, true)

@@ -49,6 +49,13 @@ enum KernelId : int {
     K_GEMM_TILED_VO_MAXMUL_F32,
     K_GEMM_TILED_VO_MAXPLUS_I32,
     K_GEMM_TILED_VO_MINPLUS_I32,
+    K_GEMM_BACKWARD_B256,  // backward, 256 / 1024 / 4096 bins per LDS chunk
+    K_GEMM_BACKWARD_B1024,
+    K_GEMM_BACKWARD_B4096,
+    K_GEMM_BACKWARD_LANE_PLUS,  // backward, one lane per segment (bins <= 256)
+    K_GEMM_BACKWARD_LANE_PLUS_VEC,
+    K_GEMM_BACKWARD_LANE_MUL,
+    K_GEMM_BACKWARD_LANE_MUL_VEC,
     K_COUNT
 };
 const char* kernel_name(KernelId id);

@@ -43,6 +43,10 @@ static const char* const kNames[K_COUNT] = {
     "trop_gather_tiled_v64_n2",      "trop_gemm_tiled_vo_maxplus_f32",
     "trop_gemm_tiled_vo_minplus_f32", "trop_gemm_tiled_vo_maxmul_f32",
     "trop_gemm_tiled_vo_maxplus_i32", "trop_gemm_tiled_vo_minplus_i32",
+    "trop_gemm_backward_b256",       "trop_gemm_backward_b1024",
+    "trop_gemm_backward_b4096",      "trop_gemm_backward_lane_plus",
+    "trop_gemm_backward_lane_plus_vec", "trop_gemm_backward_lane_mul",
+    "trop_gemm_backward_lane_mul_vec",
 };
 
 const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
