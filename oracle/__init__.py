@@ -12,11 +12,14 @@ plans a pairwise einsum the way omeinsum-rs issue #52 ("GPU tropical path:
 keep tensors device-resident + device-side permute", section "Resolved
 design for step 3") describes it: a diagonal/trace unary pre-pass, a
 permute into canonical operand order, one batched tropical GEMM, and a
-permute of the value and the argmax into the output order.
+permute of the value and the argmax into the output order; a contraction
+tree is a sequence of such pairwise steps whose results feed later steps.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (hand-worked examples, library routines, algebraic identities, a textbook
-shortest-path algorithm and brute force); none is "parity unpinned".
+shortest-path algorithm, brute force over every label assignment of small
+networks, and the routing of each tree's argmax back to its inputs); none
+is "parity unpinned".
 """
 import ctypes
 import os
@@ -301,6 +304,10 @@ class Oracle:
     def contract_pair(self, spec, sr, A, B, argmax=True):
         from .contract import contract_pair
         return contract_pair(self, spec, sr, A, B, argmax=argmax)
+
+    def contract_tree(self, sr, inputs, subs, steps, argmax=True):
+        from .contract import contract_tree
+        return contract_tree(self, sr, inputs, subs, steps, argmax=argmax)
 
 
 _default = None

@@ -102,3 +102,37 @@ def contract_pair(orc, spec, sr, A, B, argmax=True):
     C = orc.permute(C2.reshape(shape), perm)
     I = orc.permute(I2.reshape(shape), perm) if argmax else None
     return C, I
+
+
+def contract_tree(orc, sr, inputs, subs, steps, argmax=True):
+    """A contraction tree evaluated one pairwise step at a time.
+
+    omeinsum-rs issue #52 asks for the pairwise path to run "across the
+    contraction tree" with every intermediate kept where it was made
+    ("Acceptance criteria"); this is that tree, on the CPU.  Tensor slots
+    are numbered inputs first (0 .. n-1), then the result of step s as slot
+    n + s.  Step s is ``(lhs, rhs, out)``: the pairwise contraction
+    ``subs[lhs],subs[rhs]->out`` of two earlier slots, done by
+    ``contract_pair`` above.  The last step's result is the tree's result.
+
+    ``argmax``: True / False for every step, or one flag per step.
+    Returns (result, [argmax of each step or None]).
+    """
+    if len(inputs) != len(subs):
+        raise OracleError("one subscript per input")
+    if not steps:
+        raise OracleError("a tree needs at least one step")
+    flags = [bool(argmax)] * len(steps) if isinstance(argmax, bool) else [bool(f) for f in argmax]
+    if len(flags) != len(steps):
+        raise OracleError("one argmax flag per step")
+    slots = [(sub, np.asarray(x)) for sub, x in zip(subs, inputs)]
+    winners = []
+    for s, (lhs, rhs, out) in enumerate(steps):
+        if not (0 <= lhs < len(slots) and 0 <= rhs < len(slots)):
+            raise OracleError(f"step {s} names a slot that does not exist yet")
+        la, A = slots[lhs]
+        lb, B = slots[rhs]
+        C, I = contract_pair(orc, f"{la},{lb}->{out}", sr, A, B, argmax=flags[s])
+        slots.append((out, C))
+        winners.append(I)
+    return slots[-1][1], winners

@@ -538,6 +538,165 @@ def pin_backward_finite_difference(orc):
                 assert L1 - L0 == 0.5 * float(D[idx]), f"{sr} d{which}{idx}: {L1 - L0} vs {0.5 * D[idx]}"
 
 
+# ----------------------------------------------------------------------
+# contraction trees
+# ----------------------------------------------------------------------
+
+def _network_brute(sr, subs, arrays, out):
+    """Every assignment of every label, enumerated: the value at each output
+    position is the (+) over the assignments that agree with it of the (x)
+    of one entry per tensor.  Exact only on data whose sums and products
+    are exact (small integers, dyadic fractions), which is what the pins
+    below use.  Also returns, per output position, the first assignment (in
+    row-major order over all labels) that reaches the value, and whether
+    a different assignment reaches it too."""
+    labels = []
+    for c in "".join(subs) + out:
+        if c not in labels:
+            labels.append(c)
+    ext = {}
+    for sub, X in zip(subs, arrays):
+        for c, e in zip(sub, X.shape):
+            assert ext.setdefault(c, e) == e
+    is_int = arrays[0].dtype == np.int32
+    if sr == "max_plus":
+        zero, mul, better = (-I32_INF if is_int else -np.inf), (lambda a, b: a + b), (lambda t, b: t > b)
+    elif sr == "min_plus":
+        zero, mul, better = (I32_INF if is_int else np.inf), (lambda a, b: a + b), (lambda t, b: t < b)
+    else:
+        zero, mul, better = 0.0, (lambda a, b: a * b), (lambda t, b: t > b)
+    shape = tuple(ext[c] for c in out)
+    best = {}
+    for vals in itertools.product(*[range(ext[c]) for c in labels]):
+        a = dict(zip(labels, vals))
+        t = None
+        for sub, X in zip(subs, arrays):
+            e = X[tuple(a[c] for c in sub)].item()
+            t = e if t is None else mul(t, e)
+        pos = tuple(a[c] for c in out)
+        cur = best.get(pos)
+        if cur is None or better(t, cur[0]):
+            best[pos] = [t, a, False]
+        elif t == cur[0]:
+            cur[2] = True
+    C = np.full(shape, zero, dtype=arrays[0].dtype)
+    for pos, (t, _, _) in best.items():
+        if better(t, zero):
+            C[pos] = t
+    return C, best
+
+
+def _tree_inputs(sr, subs, shapes, rng, dtype=np.float32):
+    arrays = []
+    for sh in shapes:
+        if sr == "max_mul":
+            arrays.append((rng.integers(1, 5, size=sh) * 0.5).astype(np.float32))
+        else:
+            arrays.append(rng.integers(-4, 5, size=sh).astype(dtype))
+    return arrays
+
+
+def _grid(rows, cols):
+    from tropical_semiring_tensor_amd import inputs
+    return inputs.grid_network(rows, cols, 2, integer=1)
+
+
+# a hand-built tree with a repeated label (diagonal), a batch label kept to
+# the output and a non-scalar result
+TREE_BATCH = dict(subs=["aab", "bcz", "cdz", "dez"], shapes=[(2, 2, 3), (3, 2, 2), (2, 3, 2), (3, 2, 2)],
+                  steps=[(0, 1, "acz"), (4, 2, "zad"), (5, 3, "aez")])
+
+
+def pin_tree_vs_brute(orc):
+    rng = np.random.default_rng(47)
+    nets = [("grid 2x3", _grid(2, 3)), ("grid 3x3", _grid(3, 3)), ("batch tree", TREE_BATCH)]
+    for name, net in nets:
+        for sr in SR:
+            for dt in ((np.float32, np.int32) if sr != "max_mul" else (np.float32,)):
+                arrays = _tree_inputs(sr, net["subs"], net["shapes"], rng, dt)
+                out = net["steps"][-1][2]
+                C, _ = orc.contract_tree(sr, arrays, net["subs"], net["steps"])
+                Cb, _ = _network_brute(sr, net["subs"], arrays, out)
+                _bits_equal(C, Cb, f"tree {name} {sr} {dt.__name__}")
+    # a label found in one tensor only and absent from the output is
+    # (+)-reduced in its step's pre-pass (values only)
+    subs = ["ab", "bcf", "cd"]
+    shapes = [(2, 3), (3, 2, 3), (2, 2)]
+    steps = [(0, 1, "ac"), (3, 2, "ad")]
+    for sr in ("max_plus", "min_plus"):
+        arrays = _tree_inputs(sr, subs, shapes, rng)
+        C, I = orc.contract_tree(sr, arrays, subs, steps, argmax=[False, True])
+        assert I[0] is None and I[1] is not None
+        Cb, _ = _network_brute(sr, subs, arrays, "ad")
+        _bits_equal(C, Cb, f"tree with a reduced label {sr}")
+
+
+def _contracted(la, lb, out):
+    seen = []
+    for c in la:
+        if c not in seen and c in lb and c not in out:
+            seen.append(c)
+    return seen
+
+
+def _backtrack(net, winners, arrays, pos, ext):
+    """Follow the per-step argmax from one output position down to the
+    inputs: the argmax of a step is the row-major index over its contracted
+    labels taken in left-operand order.  Returns the assignment of every
+    label and the list of input entries it selects."""
+    subs = list(net["subs"])
+    n = len(subs)
+    for lhs, rhs, out in net["steps"]:
+        subs.append(out)
+    assign = dict(zip(net["steps"][-1][2], pos))
+
+    def walk(slot):
+        if slot < n:
+            return [arrays[slot][tuple(assign[c] for c in subs[slot])].item()]
+        s = slot - n
+        lhs, rhs, out = net["steps"][s]
+        con = _contracted(subs[lhs], subs[rhs], out)
+        code = int(winners[s][tuple(assign[c] for c in out)])
+        for c in reversed(con):
+            assign[c] = code % ext[c]
+            code //= ext[c]
+        return walk(lhs) + walk(rhs)
+
+    entries = walk(n + len(net["steps"]) - 1)
+    return assign, entries
+
+
+def pin_tree_winner_backtrack(orc):
+    """The per-step argmax is the tree's winner routing: following it from
+    the result down to the inputs must select one entry per input whose (x)
+    is the result, and -- where the optimum is unique -- the same labels the
+    brute-force search finds."""
+    rng = np.random.default_rng(53)
+    for name, net in (("grid 3x3", _grid(3, 3)), ("batch tree", TREE_BATCH)):
+        ext = {}
+        for sub, sh in zip(net["subs"], net["shapes"]):
+            ext.update(zip(sub, sh))
+        for sr in SR:
+            if sr == "max_mul":
+                # (1 or 3) * 2^e: products of up to nine entries stay exact
+                arrays = [(rng.choice([1.0, 3.0], size=sh) * 2.0 ** rng.integers(-20, 21, size=sh))
+                          .astype(np.float32) for sh in net["shapes"]]
+            else:
+                arrays = [rng.integers(-1000, 1001, size=sh).astype(np.float32) for sh in net["shapes"]]
+            out = net["steps"][-1][2]
+            C, W = orc.contract_tree(sr, arrays, net["subs"], net["steps"])
+            _, best = _network_brute(sr, net["subs"], arrays, out)
+            for pos in np.ndindex(C.shape):
+                assign, entries = _backtrack(net, W, arrays, pos, ext)
+                t = entries[0]
+                for e in entries[1:]:
+                    t = t * e if sr == "max_mul" else t + e
+                assert np.float32(t) == C[pos], f"{name} {sr} {pos}: routed {t} vs {C[pos]}"
+                bt, ba, tie = best[pos]
+                if not tie:
+                    assert assign == ba, f"{name} {sr} {pos}: routed labels {assign} vs {ba}"
+
+
 ALL_PINS = [
     pin_golden_gemm, pin_golden_special_values, pin_golden_einsum,
     pin_torch_crosscheck, pin_torch_random_normal, pin_unit_and_zero,
@@ -545,5 +704,5 @@ ALL_PINS = [
     pin_floyd_warshall, pin_semirings_distinct, pin_points, pin_permute,
     pin_diag, pin_brute_vs_torch, pin_contract_vs_brute,
     pin_golden_backward, pin_backward_torch_autograd, pin_backward_adjoint_identity,
-    pin_backward_finite_difference,
+    pin_backward_finite_difference, pin_tree_vs_brute, pin_tree_winner_backtrack,
 ]

@@ -2,11 +2,15 @@
 
 Every mutant is a copy of oracle/tropical_oracle.c with one textual edit
 (a dropped term, a wrong comparison, sign, stride, index or element),
-compiled into a temporary library and run through tests/pins.py.  Nothing
-here touches a GPU.  If an edit's source text is no longer found, the test
-fails so that the list is kept in step with the oracle.
+compiled into a temporary library and run through tests/pins.py; the
+Python planner of pairwise steps and trees (oracle/contract.py) gets the
+same treatment, its mutated copy standing in for the module while the pins
+run.  Nothing here touches a GPU.  If an edit's source text is no longer
+found, the test fails so that the list is kept in step with the oracle.
 """
 import os
+import sys
+import types
 
 import pytest
 
@@ -14,6 +18,7 @@ import pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "tropical_oracle.c")
+PY_SRC = os.path.join(ROOT, "oracle", "contract.py")
 
 MUTANTS = [
     ("drop_last_k_f32",
@@ -95,5 +100,44 @@ def test_mutant_is_caught(tmp_path, source, name, find, repl):
         try:
             pin(orc)
         except (AssertionError, oracle.OracleError, ValueError, IndexError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"mutant {name} passed every pin"
+
+
+PY_MUTANTS = [
+    ("pair_contracted_in_b_order",
+     "contracted = [c for c in _unique(la) if c in lb and c not in out]",
+     "contracted = [c for c in _unique(lb) if c in la and c not in out]"),
+    ("pair_output_not_permuted", "C = orc.permute(C2.reshape(shape), perm)", "C = C2.reshape(shape)"),
+    ("pair_argmax_permuted_differently", "I = orc.permute(I2.reshape(shape), perm) if argmax else None",
+     "I = orc.permute(I2.reshape(shape), perm[::-1]) if argmax else None"),
+    ("tree_rhs_is_lhs", "lb, B = slots[rhs]", "lb, B = slots[lhs]"),
+    ("tree_returns_first_step", "return slots[-1][1], winners", "return slots[len(subs)][1], winners"),
+    ("tree_result_keeps_lhs_subscript", "slots.append((out, C))", "slots.append((la, C))"),
+    ("tree_argmax_flags_shifted", "argmax=flags[s])", "argmax=flags[s - 1])"),
+]
+
+
+@pytest.fixture(scope="module")
+def py_source():
+    with open(PY_SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,find,repl", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(monkeypatch, py_source, name, find, repl):
+    import oracle
+    assert py_source.count(find) >= 1, f"mutation {name}: source text not found"
+    mod = types.ModuleType("oracle.contract")
+    mod.__package__ = "oracle"
+    mod.__file__ = PY_SRC
+    exec(compile(py_source.replace(find, repl, 1), f"<{name}>", "exec"), mod.__dict__)
+    monkeypatch.setitem(sys.modules, "oracle.contract", mod)
+    orc = oracle.default()
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, oracle.OracleError, ValueError, IndexError, KeyError, TypeError) as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, f"mutant {name} passed every pin"

@@ -12,7 +12,11 @@ Workloads (sizes as used by the benchmark and the parity tests):
   4  max-mul f32, batch 16, 2048^3, U(0, 1], B column-major
   5  max-plus f32 einsum 'iijb,kjb->bki', A (128,128,256,32) N(0,1),
      B (256,256,32) U[-1, 1]
+  6  a square-lattice tropical network (one tensor per site, one label per
+     bond) contracted site by site down to a scalar; see grid_network
 """
+import string
+
 import torch
 
 SEED_BASE = 20261202
@@ -122,3 +126,66 @@ def random_points(batch, m, n, count, salt=0, edges=True):
                     extra.append((bb, ii, jj))
         pts = torch.cat([pts, torch.tensor(extra, dtype=torch.int64)], dim=0)
     return pts.to(torch.int64)
+
+
+LABELS = string.ascii_lowercase + string.ascii_uppercase
+
+
+def grid_network(rows, cols, bond, salt=0, integer=None):
+    """A rows x cols square-lattice tensor network: the tensor of site (r, c)
+    has one axis per bond at that site, in the order up, left, down, right
+    (those that exist), every bond has extent `bond` and its own label, and
+    entries are N(0, 1) float32 (or integers uniform on [-integer, integer]
+    stored as float32 when `integer` is given).
+
+    The contraction order sweeps the sites row by row: step t joins the
+    running result with site t + 1.  A step keeps the labels that are still
+    shared with later sites (every bond belongs to exactly two sites, so
+    these are the labels found in one of the two operands only), the running
+    result's first, in its order, then the new site's.  The last step leaves
+    no label: a scalar.
+
+    Returns dict(subs, shapes, tensors, steps) with steps as
+    (lhs_slot, rhs_slot, out_subscript); slots 0..n-1 are the sites in
+    row-major order and slot n + s is the result of step s.
+    """
+    nh, nv = rows * (cols - 1), (rows - 1) * cols
+    if rows * cols < 2:
+        raise ValueError("a network needs at least two sites")
+    if nh + nv > len(LABELS):
+        raise ValueError("more bonds than single-letter labels")
+
+    def hb(r, c):  # bond between (r, c) and (r, c + 1)
+        return LABELS[r * (cols - 1) + c]
+
+    def vb(r, c):  # bond between (r, c) and (r + 1, c)
+        return LABELS[nh + r * cols + c]
+
+    subs = []
+    for r in range(rows):
+        for c in range(cols):
+            s = ""
+            if r > 0:
+                s += vb(r - 1, c)
+            if c > 0:
+                s += hb(r, c - 1)
+            if r < rows - 1:
+                s += vb(r, c)
+            if c < cols - 1:
+                s += hb(r, c)
+            subs.append(s)
+    g = generator(6, salt)
+    shapes = [tuple([bond] * len(s)) for s in subs]
+    if integer is None:
+        tensors = [normal_f32(sh, g) for sh in shapes]
+    else:
+        tensors = [int_uniform_f32(sh, -integer, integer, g) for sh in shapes]
+    n = len(subs)
+    steps = []
+    cur, cur_sub = 0, subs[0]
+    for t in range(1, n):
+        new = subs[t]
+        out = "".join([c for c in cur_sub if c not in new] + [c for c in new if c not in cur_sub])
+        steps.append((cur, t, out))
+        cur, cur_sub = n + len(steps) - 1, out
+    return dict(subs=subs, shapes=shapes, tensors=tensors, steps=steps)
