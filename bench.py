@@ -341,6 +341,8 @@ def other_workloads(torch, tb, inputs, timer, dev):
     del Ad, Bd, Bkj, Aji, C2, I2, Cbik, Ibik, C, I, ws
     torch.cuda.empty_cache()
 
+    out["network_tree"] = tree_workloads(torch, tb, inputs, timer, dev)
+
     # supplementary sweep: the workload-5 permute patterns at >= 256 MiB
     sweep = {}
     g = torch.Generator(device="cpu").manual_seed(7)
@@ -361,6 +363,66 @@ def other_workloads(torch, tb, inputs, timer, dev):
     if clk:
         out["sclk_mhz_reported"] = clk
     return out
+
+
+def tree_workloads(torch, tb, inputs, timer, dev):
+    """Square-lattice tropical networks contracted site by site to a scalar
+    by the tree executor (one plan, one workspace, one stream), against the
+    same steps issued as separate pairwise calls with freshly allocated
+    intermediates, and (small network) against a captured graph replay."""
+    import re
+    res = {}
+    for rows, cols, bond, reps in ((5, 5, 16, 10), (4, 4, 4, 50)):
+        net = inputs.grid_network(rows, cols, bond)
+        plan = tb.tropical_tree_plan_create("max_plus", torch.float32, net["subs"], net["shapes"], net["steps"])
+        desc = tb.tropical_tree_describe(plan)
+        gemms = [tuple(int(v) for v in m) for m in
+                 re.findall(r"batch=(\d+) m=(\d+) n=(\d+) k=(\d+)", desc)]
+        ops = sum(2 * b * m * n * k for b, m, n, k in gemms)
+        launches = len(gemms) + desc.count("gather:") + desc.count("permute:")
+        xs = [x.to(dev) for x in net["tensors"]]
+        ws = torch.empty(max(1, tb.tropical_tree_workspace_size(plan)), dtype=torch.uint8, device=dev)
+        outT = torch.empty((), device=dev)
+        ams = [torch.empty(tb.tropical_tree_step_info(plan, s)[1], dtype=torch.int32, device=dev)
+               for s in range(len(net["steps"]))]
+        run_arg = lambda: tb.tropical_tree_run(plan, xs, out=outT, argmax=ams, workspace=ws)
+        run_val = lambda: tb.tropical_tree_run(plan, xs, out=outT, argmax=False, workspace=ws)
+        subs = list(net["subs"]) + [o for _, _, o in net["steps"]]
+
+        def pairwise():
+            slots = list(xs)
+            for l, r, o in net["steps"]:
+                C, _ = tb.tropical_contract_pair(f"{subs[l]},{subs[r]}->{o}", "max_plus", slots[l], slots[r])
+                slots.append(C)
+            return slots[-1]
+
+        t_arg = timer.time(run_arg, reps=reps, warmup=2)
+        t_val = timer.time(run_val, reps=reps, warmup=2)
+        t_pair = timer.time(pairwise, reps=reps, warmup=2)
+        rec = {"steps": len(net["steps"]), "launches": launches, "gemm_GOP": round(ops / 1e9, 3),
+               "workspace_MiB": round(ws.numel() / 2 ** 20, 2),
+               "results_MiB": round(int(re.search(r"results=(\d+)", desc).group(1)) / 2 ** 20, 2),
+               "tree_argmax_ms": round(t_arg["median_ms"], 4), "tree_value_only_ms": round(t_val["median_ms"], 4),
+               "pairwise_calls_argmax_ms": round(t_pair["median_ms"], 4),
+               "tree_argmax_GOPS": round(ops / (t_arg["median_ms"] * 1e-3) / 1e9, 1),
+               "tree_value_only_GOPS": round(ops / (t_val["median_ms"] * 1e-3) / 1e9, 1)}
+        if bond <= 4:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                tb.tropical_tree_run(plan, xs, out=outT, argmax=ams, workspace=ws, stream=s)
+            t_graph = timer.time(graph.replay, reps=reps, warmup=2)
+            rec["graph_replay_argmax_ms"] = round(t_graph["median_ms"], 4)
+            rec["tree_back_to_back_ms"] = round(back_to_back(torch, run_arg), 4)
+            rec["graph_back_to_back_ms"] = round(back_to_back(torch, graph.replay), 4)
+            del graph
+        res[f"grid_{rows}x{cols}_bond{bond}"] = rec
+        log(f"[bench] network {rows}x{cols} bond {bond}: {rec}")
+        del xs, ws, ams, plan
+        torch.cuda.empty_cache()
+    return res
 
 
 def back_to_back(torch, fn, n=50):

@@ -2,12 +2,14 @@
  * tropical.h -- C ABI of libtropical.so, the MI355X (gfx950) tropical
  * contraction hot path.
  *
- * Five operations, all device-resident and enqueued on a caller stream:
+ * Six operations, all device-resident and enqueued on a caller stream:
  *   tropical_gemm_strided_batched  batched tropical matrix product + argmax
  *   tropical_gemm_backward         gradients routed along that argmax
  *   tropical_permute               N-d permute of one or two 4-byte tensors
  *   tropical_diag_gather           repeated-label diagonal / trace pre-pass
  *   tropical_contract_pair         one pairwise einsum built from the three
+ *   tropical_tree_run              a contraction tree of pairwise einsums
+ *                                  with every intermediate kept on device
  *
  * Sources (web pages the method is taken from):
  *   [PR35]  tropical-gemm PR #35 "feat: batched GPU ops with DLPack zero-copy
@@ -27,6 +29,11 @@
  *   [RT]    rustytorch commit "rtx-backend-cuda: native index_select /
  *           index_add" -- scatter-add as a deterministic walk of the
  *           adjoint of the selection, no atomics, bit-identical to the host.
+ *   [WR]    tenferro-rs design note "cuTENSOR workspace retirement without a
+ *           stream barrier" -- "Problem" (a per-node plan cache smaller than
+ *           the number of distinct contractions evicts continuously, and each
+ *           eviction releases a workspace behind a stream barrier) and
+ *           "Proposal" (stream order as the completion witness for reuse).
  *
  * Conventions for every entry point
  *   - Element strides and sizes are counted in ELEMENTS, not bytes.
@@ -277,6 +284,96 @@ TROP_API trop_status tropical_contract_pair_describe(const char* spec,
                                             const int64_t* shapeA, const int64_t* stridesA,
                                             const int64_t* shapeB, const int64_t* stridesB,
                                             char* buf, size_t buflen);
+
+/*
+ * ---- Contraction trees ([I52] "Acceptance criteria": intermediates stay in
+ * device memory across the contraction tree; the module is loaded once) ----
+ *
+ * A tree is planned once and run any number of times.  Tensor slots are
+ * numbered inputs first (0 .. n_inputs-1), then the result of step s as
+ * slot n_inputs + s.  Step s contracts two earlier slots with
+ * tropical_contract_pair's rules ("lhs_sub,rhs_sub->out"); the last step's
+ * result is the tree's output.  Every step result except the last must be
+ * read by a later step; inputs and results may be read by several steps.
+ *
+ * The plan holds one pairwise plan per step (so nothing is re-planned, and
+ * no plan is ever evicted, whatever the number of distinct contractions --
+ * [WR] "Problem") and a fixed layout of ONE workspace: each step's result
+ * lives from its step to its last reader, each step's scratch during its
+ * step only, and buffers whose lifetimes do not meet share memory.  All
+ * steps are enqueued in order on the caller's stream, which is what makes
+ * the sharing safe ([WR] "Proposal": stream order is the completion
+ * witness); a run allocates, frees and waits for nothing.
+ */
+typedef struct trop_tree_plan_s* trop_tree_plan;
+
+typedef struct {
+    int32_t lhs, rhs;  /* operand slots (earlier inputs or step results)   */
+    const char* out;   /* output subscript of the step (copied at planning) */
+} trop_tree_step;
+
+/*
+ * Plan a tree.  input_subs[i]: subscript of input i (single letters a-z A-Z,
+ * rank <= 8, repeated labels allowed); input_shapes[i]: its extents (may be
+ * NULL for rank 0); input_strides: NULL (all contiguous row-major) or one
+ * entry per input, NULL for a contiguous input, else its element strides.
+ * Every step's subscripts follow tropical_contract_pair's rules, with the
+ * operands' subscripts taken from their slots.  Host-only: touches no
+ * device.  On success *plan owns host memory until
+ * tropical_tree_plan_destroy.  A plan is immutable: several threads may run
+ * it at once, each with its own workspace.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, slot, subscript or extent;
+ *   a step result that no later step reads), TROP_ERR_UNSUPPORTED (int32
+ *   max-mul).  The message names the failing step.
+ */
+TROP_API trop_status tropical_tree_plan_create(trop_semiring semiring, trop_dtype dtype, int n_inputs,
+                                      const char* const* input_subs,
+                                      const int64_t* const* input_shapes,
+                                      const int64_t* const* input_strides,
+                                      int n_steps, const trop_tree_step* steps,
+                                      trop_tree_plan* plan);
+
+/* Free a plan (NULL is ignored).  Runs already enqueued are unaffected. */
+TROP_API void tropical_tree_plan_destroy(trop_tree_plan plan);
+
+/* Device workspace (bytes) a run of this plan needs. */
+TROP_API trop_status tropical_tree_workspace_size(trop_tree_plan plan, size_t* bytes);
+
+/*
+ * Output of step `step`: its subscript (NUL-terminated, buffer of at least
+ * 9 bytes, or NULL), extents (at least rank entries, or NULL) and element
+ * count (or NULL).  The argmax of a step, when requested, is a contiguous
+ * int32 tensor of that shape.
+ */
+TROP_API trop_status tropical_tree_step_info(trop_tree_plan plan, int step, char* subscript,
+                                    int64_t* shape, int64_t* elements);
+
+/*
+ * Run the tree on `stream`:
+ *   inputs[i]: device pointer of input i (strides as planned);
+ *   out: contiguous device tensor over the last step's subscript;
+ *   step_argmax: NULL, or n_steps entries each NULL or a contiguous device
+ *     int32 tensor shaped like that step's output, filled with the step's
+ *     argmax exactly as tropical_contract_pair defines it (the winner
+ *     routing of the tree: following it from the output down selects one
+ *     entry of every input);
+ *   workspace: at least tropical_tree_workspace_size bytes of device
+ *     memory, not touched by other work until this run has finished on
+ *     `stream` (a later run of any plan on the same stream may reuse it).
+ * All argument checks precede the first launch; on error nothing is
+ * enqueued.  Errors: as tropical_contract_pair (UNSUPPORTED for an argmax
+ *   requested on a step with a pre-pass reduction).
+ */
+TROP_API trop_status tropical_tree_run(trop_tree_plan plan, const void* const* inputs, void* out,
+                              int32_t* const* step_argmax, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Host-only: one line per step (slots, subscripts, workspace offsets and
+ * tropical_contract_pair_describe's text), then the workspace size and
+ * the sum of the intermediate results' sizes, into buf (truncated).
+ */
+TROP_API trop_status tropical_tree_describe(trop_tree_plan plan, char* buf, size_t buflen);
 
 /* Text of the calling thread's last error ("" if none). */
 TROP_API const char* tropical_last_error(void);

@@ -165,3 +165,99 @@ def test_stats_start_clean(tb):
     s = tb.tropical_get_stats()
     assert s["host_syncs"] == 0 and s["memcpy_calls"] == 0
     assert set(s["launches"]) == set(tb.KERNEL_FAMILIES)
+
+
+# ---------------------------------------------------------------------------
+# contraction trees (host-side planning only)
+# ---------------------------------------------------------------------------
+
+def _grid_plan(tb, rows=5, cols=5, bond=16, sr="max_plus"):
+    import torch
+    from tropical_semiring_tensor_amd import inputs
+    net = inputs.grid_network(rows, cols, bond)
+    return net, tb.tropical_tree_plan_create(sr, torch.float32, net["subs"], net["shapes"], net["steps"])
+
+
+def _parse_tree_description(text):
+    """(step, result offset or None, result bytes, scratch offset or None,
+    scratch bytes) per step line of tropical_tree_describe."""
+    rows = []
+    for line in text.splitlines():
+        m = re.match(r"step (\d+): \S+->(\w*) result=(ws@(\d+)|out)( scratch=ws@(\d+))?;.*workspace=(\d+)$", line)
+        if m:
+            rows.append((int(m.group(1)), m.group(2), int(m.group(4)) if m.group(4) else None,
+                         int(m.group(6)) if m.group(6) else None, int(m.group(7))))
+    return rows
+
+
+def test_tree_plan_workspace_is_liveness_packed(tb):
+    net, plan = _grid_plan(tb)
+    text = tb.tropical_tree_describe(plan)
+    rows = _parse_tree_description(text)
+    assert len(rows) == len(net["steps"]) == 24
+    n = len(net["subs"])
+    last_use = {}
+    for s, (lhs, rhs, _) in enumerate(net["steps"]):
+        for slot in (lhs, rhs):
+            if slot >= n:
+                last_use[slot - n] = s
+    bufs = []  # (first, last, begin, end)
+    for s, out, r_off, x_off, x_bytes in rows:
+        elems = 16 ** len(out)
+        if r_off is not None:
+            bufs.append((s, last_use[s], r_off, r_off + elems * 4))
+        if x_off is not None:
+            bufs.append((s, s, x_off, x_off + x_bytes))
+    ws = tb.tropical_tree_workspace_size(plan)
+    for i, a in enumerate(bufs):
+        assert a[3] <= ws
+        for b in bufs[i + 1:]:
+            if a[0] <= b[1] and b[0] <= a[1]:  # lifetimes meet
+                assert a[3] <= b[2] or b[3] <= a[2], f"live buffers overlap: {a} {b}"
+    results = int(re.search(r"results=(\d+)", text).group(1))
+    # 19 of the 23 intermediates are 64 MiB or 4 MiB; liveness keeps two
+    # results and one scratch buffer resident at a time
+    assert results > 700 << 20 and ws < 256 << 20
+
+
+def test_tree_step_info_and_plan_reuse(tb):
+    net, plan = _grid_plan(tb, 3, 4, 5)
+    for s, (_, _, out) in enumerate(net["steps"]):
+        sub, shape = tb.tropical_tree_step_info(plan, s)
+        assert sub == out and shape == [5] * len(out)
+    with pytest.raises(tb.TropicalError):
+        tb.tropical_tree_step_info(plan, len(net["steps"]))
+    tb.tropical_tree_plan_destroy(plan)
+    tb.tropical_tree_plan_destroy(plan)  # second destroy is a no-op
+
+
+@pytest.mark.parametrize("case", [
+    "bad_slot", "future_slot", "unused_result", "extent_mismatch", "bad_label", "maxmul_i32", "long_sub",
+    "no_steps"])
+def test_tree_plan_errors(tb, case):
+    import torch
+    subs, shapes = ["ab", "bc", "cd"], [(2, 3), (3, 4), (4, 5)]
+    steps = [(0, 1, "ac"), (3, 2, "ad")]
+    sr, dt = "max_plus", torch.float32
+    if case == "bad_slot":
+        steps = [(0, -1, "ac"), (3, 2, "ad")]
+    elif case == "future_slot":
+        steps = [(0, 4, "ac"), (3, 2, "ad")]
+    elif case == "unused_result":
+        steps = [(0, 1, "ac"), (1, 2, "bd")]
+    elif case == "extent_mismatch":
+        shapes = [(2, 3), (3, 4), (5, 5)]
+    elif case == "bad_label":
+        steps = [(0, 1, "a1"), (3, 2, "ad")]
+    elif case == "maxmul_i32":
+        sr, dt = "max_mul", torch.int32
+    elif case == "long_sub":
+        subs, shapes = ["abcdefghi", "bc", "cd"], [(1,) * 9, (1, 4), (4, 5)]
+    elif case == "no_steps":
+        steps = []
+    want = tb.UNSUPPORTED if case == "maxmul_i32" else tb.INVALID_ARGUMENT
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_tree_plan_create(sr, dt, subs, shapes, steps)
+    assert e.value.status == want
+    if case in ("extent_mismatch", "future_slot", "unused_result"):
+        assert "step" in str(e.value)

@@ -42,6 +42,10 @@ class trop_strides(ctypes.Structure):
     _fields_ = [("row", ctypes.c_int64), ("col", ctypes.c_int64), ("batch", ctypes.c_int64)]
 
 
+class trop_tree_step(ctypes.Structure):
+    _fields_ = [("lhs", ctypes.c_int32), ("rhs", ctypes.c_int32), ("out", ctypes.c_char_p)]
+
+
 class trop_stats(ctypes.Structure):
     _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
                 ("launches", ctypes.c_uint64 * 8), ("host_syncs", ctypes.c_uint64),
@@ -79,12 +83,23 @@ def lib():
                                          vp, vp, vp, sz, vp]
     L.tropical_contract_pair_describe.argtypes = [ctypes.c_char_p, I64P, I64P, I64P, I64P,
                                                   ctypes.c_char_p, sz]
+    PP = ctypes.POINTER
+    L.tropical_tree_plan_create.argtypes = [i32, i32, i32, PP(ctypes.c_char_p), PP(I64P), PP(I64P), i32,
+                                            PP(trop_tree_step), PP(vp)]
+    L.tropical_tree_plan_destroy.argtypes = [vp]
+    L.tropical_tree_plan_destroy.restype = None
+    L.tropical_tree_workspace_size.argtypes = [vp, PP(sz)]
+    L.tropical_tree_step_info.argtypes = [vp, i32, ctypes.c_char_p, I64P, I64P]
+    L.tropical_tree_run.argtypes = [vp, PP(vp), vp, PP(vp), vp, sz, vp]
+    L.tropical_tree_describe.argtypes = [vp, ctypes.c_char_p, sz]
     L.tropical_last_error.restype = ctypes.c_char_p
     L.tropical_get_stats.argtypes = [ctypes.POINTER(trop_stats)]
     L.tropical_reset_stats.restype = None
     for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_gemm_backward", "tropical_permute",
                "tropical_diag_gather", "tropical_contract_pair_workspace_size",
-               "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats"):
+               "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats",
+               "tropical_tree_plan_create", "tropical_tree_workspace_size", "tropical_tree_step_info",
+               "tropical_tree_run", "tropical_tree_describe"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -293,6 +308,108 @@ def tropical_contract_pair(spec, semiring, A, B, C=None, argmax=True, workspace=
                                       _stream(stream))
     _check(st, "tropical_contract_pair")
     return C, argmax
+
+
+class TreePlan:
+    """Handle of a planned contraction tree (owns the library's plan)."""
+
+    def __init__(self, handle, n_inputs, n_steps, dtype):
+        self.handle = handle
+        self.n_inputs = n_inputs
+        self.n_steps = n_steps
+        self.dtype = dtype
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tropical_tree_plan_destroy(self.handle)
+            self.handle = None
+
+
+def tropical_tree_plan_create(semiring, dtype, subs, shapes, steps, strides=None):
+    """Plan a tree.  subs / shapes: per input; strides: None, or per input
+    None (contiguous) or its element strides; steps: (lhs_slot, rhs_slot,
+    out_subscript) with slots 0..n-1 the inputs and n + s step s's result.
+    dtype: torch.float32 or torch.int32."""
+    n, m = len(subs), len(steps)
+    dt = F32 if dtype == torch.float32 else (I32 if dtype == torch.int32 else None)
+    if dt is None:
+        raise TypeError(f"float32 or int32 only, got {dtype}")
+    sub_arr = (ctypes.c_char_p * n)(*[x.encode() for x in subs])
+    shape_keep = [_i64(sh) for sh in shapes]
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    shape_arr = (I64P * n)(*[ctypes.cast(a, I64P) for a in shape_keep])
+    stride_arr = None
+    if strides is not None:
+        stride_keep = [_i64(st) if st is not None else None for st in strides]
+        stride_arr = (I64P * n)(*[ctypes.cast(a, I64P) if a is not None else I64P() for a in stride_keep])
+    out_keep = [o.encode() for _, _, o in steps]
+    step_arr = (trop_tree_step * m)(*[trop_tree_step(int(a), int(b), o) for (a, b, _), o in zip(steps, out_keep)])
+    h = ctypes.c_void_p(0)
+    st = lib().tropical_tree_plan_create(_sr(semiring), dt, n, sub_arr, shape_arr, stride_arr, m, step_arr,
+                                         ctypes.byref(h))
+    _check(st, "tropical_tree_plan_create")
+    return TreePlan(h.value, n, m, dtype)
+
+
+def tropical_tree_plan_destroy(plan):
+    if plan.handle:
+        lib().tropical_tree_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def tropical_tree_workspace_size(plan):
+    n = ctypes.c_size_t(0)
+    _check(lib().tropical_tree_workspace_size(plan.handle, ctypes.byref(n)), "tropical_tree_workspace_size")
+    return n.value
+
+
+def tropical_tree_step_info(plan, step):
+    """(subscript, shape) of step `step`'s output."""
+    sub = ctypes.create_string_buffer(16)
+    shape = (ctypes.c_int64 * 8)()
+    _check(lib().tropical_tree_step_info(plan.handle, int(step), sub, shape, None), "tropical_tree_step_info")
+    s = sub.value.decode()
+    return s, [shape[d] for d in range(len(s))]
+
+
+def tropical_tree_describe(plan):
+    buf = ctypes.create_string_buffer(64 * 1024)
+    _check(lib().tropical_tree_describe(plan.handle, buf, len(buf)), "tropical_tree_describe")
+    return buf.value.decode()
+
+
+def tropical_tree_run(plan, inputs, out=None, argmax=False, workspace=None, stream=None):
+    """Run a planned tree; returns (out, [argmax of each step or None]).
+
+    argmax: False (none), True (every step) or one flag / tensor / None per
+    step; requested ones are allocated as contiguous int32 tensors.  The
+    workspace is allocated with torch when not given.
+    """
+    if len(inputs) != plan.n_inputs:
+        raise ValueError(f"the plan has {plan.n_inputs} inputs")
+    dev = inputs[0].device
+    if out is None:
+        _, shape = tropical_tree_step_info(plan, plan.n_steps - 1)
+        out = torch.empty(shape, dtype=plan.dtype, device=dev)
+    flags = [argmax] * plan.n_steps if isinstance(argmax, bool) else list(argmax)
+    if len(flags) != plan.n_steps:
+        raise ValueError("one argmax entry per step")
+    ams = []
+    for s, f in enumerate(flags):
+        if f is True:
+            ams.append(torch.empty(tropical_tree_step_info(plan, s)[1], dtype=torch.int32, device=dev))
+        elif f is False or f is None:
+            ams.append(None)
+        else:
+            ams.append(f)
+    if workspace is None:
+        workspace = torch.empty(max(tropical_tree_workspace_size(plan), 1), dtype=torch.uint8, device=dev)
+    in_arr = (ctypes.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
+    am_arr = (ctypes.c_void_p * plan.n_steps)(*[a.data_ptr() if a is not None else 0 for a in ams])
+    st = lib().tropical_tree_run(plan.handle, in_arr, _ptr(out), am_arr, _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check(st, "tropical_tree_run")
+    return out, ams
 
 
 def tropical_get_stats():

@@ -30,7 +30,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
 RUNTIME_SRCS = ["status.cpp", "module.cpp", "validate.cpp", "gemm.cpp", "gather.cpp", "contract.cpp",
-                "backward.cpp"]
+                "backward.cpp", "tree.cpp"]
 
 
 def _run(cmd):

@@ -20,38 +20,15 @@
 #include <string>
 #include <vector>
 
-#include "internal.h"
+#include "contract_plan.h"
 
 namespace trop {
 
 namespace {
 
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-struct Operand {
-    std::string sub;             // subscript
-    int64_t shape[TROP_MAX_DIMS];
-    int64_t stride[TROP_MAX_DIMS];
-    bool has_strides = false;
-};
-
-struct Plan {
-    std::string la, lb, lo;
-    std::string batch, left, right, contracted, a_red, b_red;
-    int64_t ext[128];
-    int64_t nb = 1, M = 1, N = 1, K = 1;
-    int64_t out_total = 1;
-    bool a_fold = false, b_fold = false, c_direct = false;
-    // swap: the GEMM's left operand is B and its right operand is A, so that
-    // the product comes out as (batch, right, left), the output order
-    bool swap = false;
-    int64_t gm = 1, gn = 1;  // GEMM rows and columns
-    trop_strides sA{}, sB{};
-    GatherPlan ga{}, gb{}, gc{};
-    size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, ws = 0;
-};
+using Plan = PairPlan;
+using Operand = PairOperand;
+size_t align_up(size_t x) { return ws_align(x); }
 
 bool is_label(char c) { return (c >= 'a' && c <= 'z') || (c >= 'A' && c <= 'Z'); }
 
@@ -64,21 +41,7 @@ std::string unique(const std::string& s) {
     return u;
 }
 
-trop_status parse(const char* spec, Plan& P) {
-    if (!spec) return fail(TROP_ERR_INVALID_ARGUMENT, "spec is NULL");
-    std::string s;
-    for (const char* q = spec; *q; ++q)
-        if (*q != ' ') s.push_back(*q);
-    const size_t arrow = s.find("->");
-    if (arrow == std::string::npos || s.find("->", arrow + 2) != std::string::npos)
-        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly one '->' (explicit output)");
-    const std::string lhs = s.substr(0, arrow);
-    P.lo = s.substr(arrow + 2);
-    const size_t comma = lhs.find(',');
-    if (comma == std::string::npos || lhs.find(',', comma + 1) != std::string::npos)
-        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly two operands");
-    P.la = lhs.substr(0, comma);
-    P.lb = lhs.substr(comma + 1);
+trop_status assign_roles(Plan& P) {
     for (const std::string* part : {&P.la, &P.lb, &P.lo}) {
         if (part->size() > TROP_MAX_DIMS) return fail(TROP_ERR_INVALID_ARGUMENT, "subscript longer than 8");
         for (char c : *part)
@@ -143,6 +106,28 @@ trop_status bind_shapes(Plan& P, const int64_t* shapeA, const int64_t* shapeB) {
 // Stride of a label group when it collapses to one axis of `op` (labels in
 // group order, outermost first).  Returns false if the group is not
 // collapsible or a label of it is repeated in the operand.
+}  // namespace
+
+trop_status pair_parse(const char* spec, std::string* la, std::string* lb, std::string* lo) {
+    if (!spec) return fail(TROP_ERR_INVALID_ARGUMENT, "spec is NULL");
+    std::string s;
+    for (const char* q = spec; *q; ++q)
+        if (*q != ' ') s.push_back(*q);
+    const size_t arrow = s.find("->");
+    if (arrow == std::string::npos || s.find("->", arrow + 2) != std::string::npos)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly one '->' (explicit output)");
+    const std::string lhs = s.substr(0, arrow);
+    *lo = s.substr(arrow + 2);
+    const size_t comma = lhs.find(',');
+    if (comma == std::string::npos || lhs.find(',', comma + 1) != std::string::npos)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "spec needs exactly two operands");
+    *la = lhs.substr(0, comma);
+    *lb = lhs.substr(comma + 1);
+    return TROP_OK;
+}
+
+namespace {
+
 bool group_stride(const Plan& P, const Operand& op, const std::string& group, int64_t* out) {
     int64_t want = -1;  // stride the next (outer) label must have
     int64_t s_inner = 0;
@@ -205,25 +190,42 @@ void default_strides(Operand& op) {
     }
 }
 
-trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
-                       const int64_t* stridesB, Plan& P, Operand& A, Operand& B) {
-    trop_status st = parse(spec, P);
+// Elements of `op` reached from its base (0 when it has no element).
+bool operand_span(const Operand& op, int64_t* span) {
+    *span = 0;
+    for (size_t d = 0; d < op.sub.size(); ++d)
+        if (op.shape[d] == 0) return true;
+    int64_t off = 0;
+    if (!max_offset((int)op.sub.size(), op.shape, op.stride, &off)) return false;
+    *span = off + 1;
+    return true;
+}
+
+}  // namespace
+
+trop_status pair_plan(const std::string& la, const std::string& lb, const std::string& lo,
+                      const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
+                      const int64_t* stridesB, Plan& P) {
+    P = Plan();
+    P.la = la;
+    P.lb = lb;
+    P.lo = lo;
+    trop_status st = assign_roles(P);
     if (st != TROP_OK) return st;
     st = bind_shapes(P, shapeA, shapeB);
     if (st != TROP_OK) return st;
+    Operand A, B;
     A.sub = P.la;
     B.sub = P.lb;
     for (size_t d = 0; d < A.sub.size(); ++d) A.shape[d] = shapeA[d];
     for (size_t d = 0; d < B.sub.size(); ++d) B.shape[d] = shapeB[d];
     if (stridesA) {
         for (size_t d = 0; d < A.sub.size(); ++d) A.stride[d] = stridesA[d];
-        A.has_strides = true;
     } else {
         default_strides(A);
     }
     if (stridesB) {
         for (size_t d = 0; d < B.sub.size(); ++d) B.stride[d] = stridesB[d];
-        B.has_strides = true;
     } else {
         default_strides(B);
     }
@@ -231,6 +233,8 @@ trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* s
         if (A.stride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride in A");
     for (size_t d = 0; d < B.sub.size(); ++d)
         if (B.stride[d] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride in B");
+    if (!operand_span(A, &P.span_a) || !operand_span(B, &P.span_b))
+        return fail(TROP_ERR_INVALID_ARGUMENT, "operand extent overflows");
 
     // Every (x) here is commutative bit for bit (IEEE add and multiply,
     // saturating int32 add), so the product may be taken as B (x) A when
@@ -302,7 +306,7 @@ trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* s
     return TROP_OK;
 }
 
-std::string describe(const Plan& P) {
+std::string pair_describe(const Plan& P) {
     char buf[512];
     std::snprintf(buf, sizeof(buf),
                   "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm %s batch=%lld m=%lld "
@@ -318,6 +322,64 @@ std::string describe(const Plan& P) {
     return buf;
 }
 
+trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype dtype, const void* Aptr,
+                     const void* Bptr, void* C, int32_t* argmax, void* scratch, hipStream_t s) {
+    if (P.out_total == 0) return TROP_OK;
+    char* ws = static_cast<char*>(scratch);
+    trop_status st;
+    // 1. unary pre-pass + permute into canonical operand order (a_* is the
+    // GEMM's left operand: A, or B when the product is taken as B (x) A).
+    // The gather plans are copied: running sets their pointers, and a plan
+    // may be run from several threads at once.
+    const void* l_ptr = P.swap ? Bptr : Aptr;
+    const void* r_ptr = P.swap ? Aptr : Bptr;
+    const void* a_use = l_ptr;
+    const void* b_use = r_ptr;
+    if (!P.a_fold) {
+        GatherPlan g = P.ga;
+        void* dst = ws + P.off_a;
+        const void* in[1] = {l_ptr};
+        void* out[1] = {dst};
+        st = run_gather(dev, g, 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+        a_use = dst;
+    }
+    if (!P.b_fold) {
+        GatherPlan g = P.gb;
+        void* dst = ws + P.off_b;
+        const void* in[1] = {r_ptr};
+        void* out[1] = {dst};
+        st = run_gather(dev, g, 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+        b_use = dst;
+    }
+    // 2. batched GEMM into the canonical (batch, rows, cols) result
+    void* c_gemm = P.c_direct ? C : static_cast<void*>(ws + P.off_c);
+    int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
+    const trop_strides sC = {P.gn, 1, P.gm * P.gn};
+    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s);
+    if (st != TROP_OK) return st;
+    // 3. one paired permute of value and argmax into the output order
+    if (!P.c_direct) {
+        GatherPlan g = P.gc;
+        const void* in[2] = {c_gemm, i_gemm};
+        void* out[2] = {C, argmax};
+        st = run_gather(dev, g, argmax ? 2 : 1, in, out, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+    }
+    return TROP_OK;
+}
+
+namespace {
+
+trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
+                       const int64_t* stridesB, Plan& P) {
+    std::string la, lb, lo;
+    trop_status st = pair_parse(spec, &la, &lb, &lo);
+    if (st != TROP_OK) return st;
+    return pair_plan(la, lb, lo, shapeA, stridesA, shapeB, stridesB, P);
+}
+
 }  // namespace
 
 }  // namespace trop
@@ -328,9 +390,8 @@ extern "C" trop_status tropical_contract_pair_workspace_size(const char* spec, c
                                                              const int64_t* shapeB, size_t* bytes) {
     if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
     Plan P;
-    Operand A, B;
     // default (contiguous) strides: the bound below does not depend on them
-    trop_status st = build_plan(spec, shapeA, nullptr, shapeB, nullptr, P, A, B);
+    trop_status st = build_plan(spec, shapeA, nullptr, shapeB, nullptr, P);
     if (st != TROP_OK) return st;
     // upper bound: room for both operand pre-passes and the output permute
     size_t ws = align_up((size_t)(P.nb * P.M * P.K) * 4) + align_up((size_t)(P.nb * P.K * P.N) * 4);
@@ -343,10 +404,9 @@ extern "C" trop_status tropical_contract_pair_describe(const char* spec, const i
                                                        const int64_t* stridesA, const int64_t* shapeB,
                                                        const int64_t* stridesB, char* buf, size_t buflen) {
     Plan P;
-    Operand A, B;
-    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P, A, B);
+    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P);
     if (st != TROP_OK) return st;
-    const std::string d = describe(P);
+    const std::string d = pair_describe(P);
     if (buf && buflen > 0) {
         std::strncpy(buf, d.c_str(), buflen - 1);
         buf[buflen - 1] = '\0';
@@ -363,8 +423,7 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
     Plan P;
-    Operand A, B;
-    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P, A, B);
+    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P);
     if (st != TROP_OK) return st;
     if (argmax && (!P.a_red.empty() || !P.b_red.empty()))
         return fail(TROP_ERR_UNSUPPORTED, "argmax through a pre-pass reduction is not defined");
@@ -376,17 +435,12 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     int dev = -1;
     st = current_device(&dev);
     if (st != TROP_OK) return st;
-    // operand spans over their own axes
-    for (int o = 0; o < 2; ++o) {
-        const Operand& op = o ? B : A;
-        const void* ptr = o ? Bptr : Aptr;
-        bool empty = false;
-        for (size_t d = 0; d < op.sub.size(); ++d) empty = empty || op.shape[d] == 0;
-        if (empty) continue;
-        int64_t span = 0;
-        if (!max_offset((int)op.sub.size(), op.shape, op.stride, &span))
-            return fail(TROP_ERR_INVALID_ARGUMENT, "operand extent overflows");
-        st = check_device_span(ptr, dev, span + 1, 4, o ? "B" : "A");
+    if (P.span_a > 0) {
+        st = check_device_span(Aptr, dev, P.span_a, 4, "A");
+        if (st != TROP_OK) return st;
+    }
+    if (P.span_b > 0) {
+        st = check_device_span(Bptr, dev, P.span_b, 4, "B");
         if (st != TROP_OK) return st;
     }
     st = check_device_span(C, dev, P.out_total, 4, "C");
@@ -399,43 +453,7 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
         st = check_device_span(workspace, dev, (int64_t)(P.ws / 4), 4, "workspace");
         if (st != TROP_OK) return st;
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-
-    // 1. unary pre-pass + permute into canonical operand order (a_* is the
-    // GEMM's left operand: A, or B when the product is taken as B (x) A)
-    const void* l_ptr = P.swap ? Bptr : Aptr;
-    const void* r_ptr = P.swap ? Aptr : Bptr;
-    const void* a_use = l_ptr;
-    const void* b_use = r_ptr;
-    if (!P.a_fold) {
-        void* dst = ws + P.off_a;
-        const void* in[1] = {l_ptr};
-        void* out[1] = {dst};
-        st = run_gather(dev, P.ga, 1, in, out, semiring, dtype, s);
-        if (st != TROP_OK) return st;
-        a_use = dst;
-    }
-    if (!P.b_fold) {
-        void* dst = ws + P.off_b;
-        const void* in[1] = {r_ptr};
-        void* out[1] = {dst};
-        st = run_gather(dev, P.gb, 1, in, out, semiring, dtype, s);
-        if (st != TROP_OK) return st;
-        b_use = dst;
-    }
-    // 2. batched GEMM into the canonical (batch, left, right) result
-    void* c_gemm = P.c_direct ? C : static_cast<void*>(ws + P.off_c);
-    int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
-    const trop_strides sC = {P.gn, 1, P.gm * P.gn};
-    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s);
+    st = pair_run(dev, P, semiring, dtype, Aptr, Bptr, C, argmax, workspace, static_cast<hipStream_t>(stream));
     if (st != TROP_OK) return st;
-    // 3. one paired permute of value and argmax into the output order
-    if (!P.c_direct) {
-        const void* in[2] = {c_gemm, i_gemm};
-        void* out[2] = {C, argmax};
-        st = run_gather(dev, P.gc, argmax ? 2 : 1, in, out, semiring, dtype, s);
-        if (st != TROP_OK) return st;
-    }
     return ok();
 }

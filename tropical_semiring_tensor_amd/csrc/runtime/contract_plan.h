@@ -1,0 +1,58 @@
+// The plan of one pairwise tropical contraction, shared by
+// tropical_contract_pair (contract.cpp) and the contraction-tree executor
+// (tree.cpp).  A plan is built once on the host from subscripts, shapes and
+// strides; running it only sets pointers and enqueues kernels.
+#pragma once
+#include <string>
+
+#include "internal.h"
+
+namespace trop {
+
+constexpr size_t kWsAlign = 256;
+inline size_t ws_align(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct PairOperand {
+    std::string sub;  // subscript
+    int64_t shape[TROP_MAX_DIMS];
+    int64_t stride[TROP_MAX_DIMS];
+};
+
+struct PairPlan {
+    std::string la, lb, lo;
+    // label roles: batch / left / right in output order, contracted and the
+    // pre-pass reductions in operand-subscript order
+    std::string batch, left, right, contracted, a_red, b_red;
+    int64_t ext[128];
+    int64_t nb = 1, M = 1, N = 1, K = 1;
+    int64_t out_total = 1;
+    int64_t span_a = 0, span_b = 0;  // elements of A / B reached (0: empty operand)
+    bool a_fold = false, b_fold = false, c_direct = false;
+    // swap: the GEMM's left operand is B and its right operand is A, so that
+    // the product comes out as (batch, right, left), the output order
+    bool swap = false;
+    int64_t gm = 1, gn = 1;  // GEMM rows and columns
+    trop_strides sA{}, sB{};
+    GatherPlan ga{}, gb{}, gc{};
+    // workspace layout of the step (bytes, relative to its scratch base)
+    size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, ws = 0;
+};
+
+// "lhs,rhs->out" into its three subscripts (spaces ignored).
+trop_status pair_parse(const char* spec, std::string* la, std::string* lb, std::string* lo);
+
+// Plan `la,lb->lo` for operands of these shapes and element strides
+// (strides NULL: contiguous row-major).
+trop_status pair_plan(const std::string& la, const std::string& lb, const std::string& lo,
+                      const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
+                      const int64_t* stridesB, PairPlan& P);
+
+std::string pair_describe(const PairPlan& P);
+
+// Enqueue a planned contraction on `stream`: no pointer checks here (the
+// callers check spans).  `scratch` holds P.ws bytes.  Requesting `argmax`
+// with a pre-pass reduction is the caller's error to reject.
+trop_status pair_run(int dev, const PairPlan& P, trop_semiring sr, trop_dtype dt, const void* A,
+                     const void* B, void* C, int32_t* argmax, void* scratch, hipStream_t stream);
+
+}  // namespace trop
