@@ -30,11 +30,11 @@ VALU_PEAK_T = 256 * 64 * 2.4e9 * 2 / 1e12   # 78.6 T tropical ops/s
 FP32_DATASHEET_T = 157.3                     # packed-FMA FP32 vector peak
 ISA_CEILING_T = VALU_PEAK_T * 2 / 3          # 1.5 VALU instructions per term
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["tropical_semiring_tensor_amd/csrc/kernels/gemm_kernels.h",
-                  "tropical_semiring_tensor_amd/csrc/kernels/gemm_tiled.h",
+# the sources of the headline kernel (trop_gemm_tiled_maxplus_f32): its
+# body, its semiring operations and its argument block
+KERNEL_SOURCES = ["tropical_semiring_tensor_amd/csrc/kernels/gemm_tiled.h",
                   "tropical_semiring_tensor_amd/csrc/kernels/ring.h",
-                  "tropical_semiring_tensor_amd/csrc/kernels/gather_kernels.h",
-                  "tropical_semiring_tensor_amd/csrc/kernels/kernels.hip"]
+                  "tropical_semiring_tensor_amd/csrc/kernel_params.h"]
 
 
 def log(*a):
@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="run a 256 MiB copy and 3 headline GEMMs, print nothing else")
+    ap.add_argument("--network-only", action="store_true",
+                    help="run only the lattice-network (contraction tree) legs and print their JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -111,6 +113,9 @@ def main():
     torch.cuda.set_device(dev)
     tb.tropical_init(0)
     timer = Timer(torch)
+    if args.network_only:
+        print(json.dumps(tree_workloads(torch, tb, inputs, timer, dev)), flush=True)
+        return
 
     # ---------------- headline: workload 2 ----------------
     w = inputs.WORKLOADS[2]

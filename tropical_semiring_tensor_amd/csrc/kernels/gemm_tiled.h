@@ -379,6 +379,11 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
         // ---- compute the slice: 4 k per 16-byte fragment ----
         {
             const int sk = s * GEMM_SL;
+            // Chunks of the last slice that lie wholly past K hold only
+            // padding (terms that cannot win): they are skipped, which makes
+            // a small K cost its own chunks and not a whole slice.
+            const int64_t k_left = p.k - (int64_t)g * GEMM_SL;
+            const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + GEMM_CH - 1) / GEMM_CH) * QPC;
             V fa[2][GEMM_TR], fb[2][4];
 #pragma unroll
             for (int r = 0; r < GEMM_TR; ++r) fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk);
@@ -388,6 +393,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             T prev[GEMM_TR][4];  // argmax: the best before the current chunk
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
+                if (q % QPC == 0 && q > 0 && q >= q_end) break;  // uniform over the workgroup
                 const int cur = q & 1, nxt = cur ^ 1;
                 if (q + 1 < NQ) {
 #pragma unroll
