@@ -363,6 +363,15 @@ def other_workloads(torch, tb, inputs, timer, dev):
                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"[bench] sweep {name}: {gbs:.0f} GB/s")
         del Y
+    # the same bytes as 8-byte elements (float64): moved as word pairs
+    X64 = X.view(torch.float64)
+    Y = torch.empty(256, 64, 2048, dtype=torch.float64, device=dev)
+    t = timer.time(lambda: tb.tropical_permute(X64, (0, 2, 1), out=Y), reps=reps, warmup=2, flush=flush)
+    gbs = 2 * 8 * X64.numel() / (t["median_ms"] * 1e-3) / 1e9
+    sweep["batched_transpose_f64_(b,i,k)->(b,k,i)"] = {"MiB_moved": 2 * 8 * X64.numel() // 2 ** 20,
+                                                        "cold_GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] sweep f64 batched transpose: {gbs:.0f} GB/s")
+    del Y, X64
     out["permute_sweep_256MiB"] = sweep
     clk = clock_mhz()
     if clk:

@@ -200,10 +200,17 @@ TROP_API trop_status tropical_gemm_backward(trop_semiring semiring, trop_dtype d
  * with out contiguous row-major of shape shape[perm[0]], ..., shape[perm[d-1]].
  * ntensors = 1 or 2: with 2, in[1] -> out[1] is moved with the identical
  * mapping in the same launch (value and argmax, [I52] "Acceptance criteria").
- * elem_bytes must be 4 (float32 / int32); ndim <= 8; perm a permutation of
- * 0..ndim-1; shape >= 0; in_strides >= 0.  in and out must not overlap.
- * Errors: TROP_ERR_INVALID_ARGUMENT, TROP_ERR_UNSUPPORTED (elem_bytes != 4),
- *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ * elem_bytes: 4 (float32, int32, uint32), 8 (float64, int64, complex64) or
+ * 16 (complex128) -- [I52] (a) serves f32 / f64 / c32 / c64 tensors and the
+ * u32 argmax; elements are moved as opaque bytes (their 4-byte words in
+ * order), so any type of that size works.  Pointers need 4-byte alignment
+ * (wider alignment enables wider accesses).  ndim <= 8; perm a permutation
+ * of 0..ndim-1; shape >= 0; in_strides >= 0, in elements.  in and out must
+ * not overlap.
+ * Errors: TROP_ERR_INVALID_ARGUMENT, TROP_ERR_UNSUPPORTED (another
+ *   elem_bytes; 8- or 16-byte elements with 8 output axes of which no two
+ *   neighbours, nor the last axis and the element's own words, are
+ *   contiguous in the input), TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
  */
 TROP_API trop_status tropical_permute(size_t elem_bytes, int ndim, const int64_t* shape,
                              const int64_t* in_strides, const int32_t* perm,

@@ -81,7 +81,8 @@ class Oracle:
     def __init__(self, lib_path=None):
         if lib_path is None:
             lib_path = _build.LIB
-            if not os.path.exists(lib_path):
+            # (re)build when missing or older than its source
+            if not os.path.exists(lib_path) or os.path.getmtime(_build.SRC) > os.path.getmtime(lib_path):
                 _build.build()
         self.path = lib_path
         self.lib = ctypes.CDLL(lib_path)

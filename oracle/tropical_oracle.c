@@ -310,7 +310,7 @@ int orc_permute(int elem_bytes, int ndim, const int64_t* shape,
                 const void* in, void* out)
 {
     if (ndim < 0 || ndim > ORC_MAX_RANK) return ORC_BAD_ARG;
-    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8 && elem_bytes != 16)
         return ORC_BAD_ARG;
     int seen[ORC_MAX_RANK] = {0};
     int64_t out_shape[ORC_MAX_RANK];

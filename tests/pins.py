@@ -356,6 +356,17 @@ def pin_permute(orc):
     base = torch.randn(6, 8, generator=g)
     view = base.numpy()[::2, 1::3]
     _bits_equal(orc.permute(view, (1, 0)), np.ascontiguousarray(view.T), "strided view")
+    # 8- and 16-byte elements (the permute serves f64 / c32 / c64 tensors
+    # too), against torch.permute, including a strided view
+    for dt in (torch.float64, torch.complex64, torch.complex128, torch.int64):
+        x = (torch.randn(2, 3, 4, 5, generator=g, dtype=torch.float64) * 1000).to(dt)
+        if dt.is_complex:
+            x = x + 1j * torch.randn(2, 3, 4, 5, generator=g, dtype=torch.float64).to(dt)
+        for p in ((3, 1, 0, 2), (0, 2, 1, 3), (1, 0, 3, 2)):
+            _bits_equal(orc.permute(x.numpy(), p), x.permute(*p).contiguous().numpy(), f"permute {dt} {p}")
+        v = x[:, ::2, 1:, ::3]
+        _bits_equal(orc.permute(v.numpy(), (2, 0, 3, 1)), v.permute(2, 0, 3, 1).contiguous().numpy(),
+                    f"strided permute {dt}")
 
 
 def pin_diag(orc):

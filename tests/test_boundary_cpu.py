@@ -98,7 +98,15 @@ def test_permute_argument_errors(tb):
     assert "permutation" in tb.tropical_last_error()
     assert L.tropical_permute(4, 2, shape, strides, tb._i32([1, 2]), 1, arr, arr, None) == tb.INVALID_ARGUMENT
     assert L.tropical_permute(4, 2, shape, strides, tb._i32([1, 0]), 3, arr, arr, None) == tb.INVALID_ARGUMENT
-    assert L.tropical_permute(8, 2, shape, strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.UNSUPPORTED
+    for eb in (1, 2, 12, 32):
+        assert L.tropical_permute(eb, 2, shape, strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.UNSUPPORTED
+    # 8- and 16-byte elements are moved as 4-byte words; eight output axes
+    # that stay apart, plus the element's words, exceed the 8 kernel axes
+    s8, t8 = tb._i64([2, 3] * 4), tb._i64([648, 216, 108, 36, 18, 6, 3, 1])
+    rev = tb._i32(list(range(7, -1, -1)))
+    for eb in (8, 16):
+        assert L.tropical_permute(eb, 8, s8, t8, rev, 1, arr, arr, None) == tb.UNSUPPORTED
+        assert L.tropical_permute(eb, 2, tb._i64([0, 3]), strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.OK
     assert L.tropical_permute(4, 9, shape, strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.INVALID_ARGUMENT
     # zero-size output: no-op
     assert L.tropical_permute(4, 2, tb._i64([0, 3]), strides, tb._i32([1, 0]), 1, arr, arr, None) == tb.OK

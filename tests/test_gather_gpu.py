@@ -193,3 +193,75 @@ def test_permute_vectorised_copy(tb, orc, shape, perm):
     out = tb.tropical_permute(x.to(DEV), perm)
     torch.cuda.synchronize()
     assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"vec copy {shape} {perm}")
+
+
+WIDE = [torch.float64, torch.complex64, torch.complex128, torch.int64]
+
+
+def wide_tensor(shape, dt, g):
+    x = torch.randn(shape, generator=g, dtype=torch.float64) * 1000
+    if dt.is_complex:
+        x = x + 1j * torch.randn(shape, generator=g, dtype=torch.float64)
+    return x.to(dt)
+
+
+@pytest.mark.parametrize("dt", WIDE, ids=lambda d: str(d).replace("torch.", ""))
+@pytest.mark.parametrize("shape", [(5, 9), (65, 130), (3, 1, 70, 2), (2, 3, 4, 5, 6), (33, 2, 65)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_permute_wide_elements(tb, orc, dt, shape):
+    """8- and 16-byte elements (f64, c32, c64, i64) through the same kernels."""
+    g = torch.Generator().manual_seed(sum(shape))
+    x = wide_tensor(shape, dt, g)
+    xd = x.to(DEV)
+    perms = list(itertools.permutations(range(len(shape))))
+    if len(perms) > 24:
+        perms = perms[:: len(perms) // 24]
+    for p in perms:
+        out = tb.tropical_permute(xd, p)
+        torch.cuda.synchronize()
+        assert out.dtype == dt
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), p), f"{dt} permute {shape} {p}")
+    # a strided view of the same tensor
+    v = x[(slice(None, None, 2),) + (slice(None),) * (len(shape) - 1)]
+    vd = device_copy(v)
+    p = tuple(reversed(range(len(shape))))
+    out = tb.tropical_permute(vd, p)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(v.numpy(), p), f"{dt} strided view {shape}")
+
+
+def test_permute_wide_pairs_unaligned_and_rank8(tb, orc):
+    g = torch.Generator().manual_seed(8)
+    # value (float64) and index (int64) moved with one mapping, every path
+    x = wide_tensor((6, 70, 130), torch.float64, g)
+    idx = torch.randint(0, 1 << 40, (6, 70, 130), generator=g, dtype=torch.int64)
+    xd, idd = x.to(DEV), idx.to(DEV)
+    for p in ((0, 1, 2), (1, 0, 2), (0, 2, 1), (2, 1, 0)):
+        out, out2 = tb.tropical_permute(xd, p, x2=idd)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), p), f"f64 pair value {p}")
+        assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), p), f"i64 pair index {p}")
+    # complex64 starting 8 bytes into an allocation (not 16-byte aligned)
+    base = wide_tensor((1 + 40 * 33,), torch.complex64, g).to(DEV)
+    xv = base[1:].view(40, 33)
+    out = tb.tropical_permute(xv, (1, 0))
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(xv.cpu().numpy(), (1, 0)), "c64 unaligned")
+    # rank 8: axes that merge fit the kernels; eight axes that stay apart
+    # (every axis moved, the element words apart from all) do not
+    x8 = wide_tensor((2, 3, 2, 3, 2, 3, 2, 3), torch.float64, g)
+    x8d = x8.to(DEV)
+    p = (1, 2, 3, 4, 5, 6, 7, 0)
+    out = tb.tropical_permute(x8d, p)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x8.numpy(), p), "rank 8 f64")
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_permute(x8d, (7, 6, 5, 4, 3, 2, 1, 0))
+    assert e.value.status == tb.UNSUPPORTED
+    p = (7, 6, 5, 4, 3, 2, 1, 0)
+    out = tb.tropical_permute(x8.to(torch.float32).to(DEV), p)  # 4-byte elements: 8 axes fit
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x8.to(torch.float32).numpy(), p), "rank 8 f32")
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_permute(torch.zeros(4, 4, dtype=torch.float16, device=DEV), (1, 0))
+    assert e.value.status == tb.UNSUPPORTED

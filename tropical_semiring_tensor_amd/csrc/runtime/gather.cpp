@@ -297,18 +297,49 @@ extern "C" trop_status tropical_permute(size_t elem_bytes, int ndim, const int64
         return fail(TROP_ERR_INVALID_ARGUMENT, "NULL shape / stride / perm array");
     if (!in || !out) return fail(TROP_ERR_INVALID_ARGUMENT, "NULL tensor array");
     bool seen[TROP_MAX_DIMS] = {false};
-    int64_t oshape[TROP_MAX_DIMS], ostride[TROP_MAX_DIMS];
+    if (elem_bytes != 4 && elem_bytes != 8 && elem_bytes != 16)
+        return fail(TROP_ERR_UNSUPPORTED, "elements of 4, 8 or 16 bytes only");
+    // An element of W = elem_bytes / 4 words is moved as W words: every
+    // stride is scaled by W and a last axis of W words with unit stride is
+    // appended (omeinsum-rs issue #52, "Resolved design for step 3", kernel
+    // (a) serves f32 / f64 / c32 / c64 tensors and the u32 argmax alike).
+    const int64_t W = (int64_t)(elem_bytes / 4);
+    int64_t oshape[TROP_MAX_DIMS + 1], ostride[TROP_MAX_DIMS + 1];
     for (int d = 0; d < ndim; ++d) {
         const int q = perm[d];
         if (q < 0 || q >= ndim || seen[q]) return fail(TROP_ERR_INVALID_ARGUMENT, "perm is not a permutation");
         seen[q] = true;
         if (shape[q] < 0 || in_strides[q] < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative extent or stride");
+        if (__builtin_mul_overflow(in_strides[q], W, &ostride[d]))
+            return fail(TROP_ERR_INVALID_ARGUMENT, "stride overflows");
         oshape[d] = shape[q];
-        ostride[d] = in_strides[q];
     }
-    if (elem_bytes != 4) return fail(TROP_ERR_UNSUPPORTED, "only 4-byte elements (float32, int32)");
+    int nd = ndim;
+    if (W > 1) {
+        oshape[nd] = W;
+        ostride[nd] = 1;
+        ++nd;
+        // drop extent-1 axes and merge neighbours contiguous in the input
+        // (the word axis merges into a last axis of unit element stride),
+        // so that a rank-8 tensor usually still fits the 8 kernel axes
+        int k = 0;
+        for (int d = 0; d < nd; ++d) {
+            if (oshape[d] == 1) continue;
+            if (k > 0 && ostride[k - 1] == ostride[d] * oshape[d]) {
+                oshape[k - 1] *= oshape[d];
+                ostride[k - 1] = ostride[d];
+            } else {
+                oshape[k] = oshape[d];
+                ostride[k] = ostride[d];
+                ++k;
+            }
+        }
+        nd = k;
+        if (nd > TROP_MAX_DIMS)
+            return fail(TROP_ERR_UNSUPPORTED, "8 output axes that stay apart, with 8- or 16-byte elements");
+    }
     GatherPlan plan;
-    trop_status st = plan_gather(ndim, oshape, ostride, 0, nullptr, nullptr, &plan);
+    trop_status st = plan_gather(nd, oshape, ostride, 0, nullptr, nullptr, &plan);
     if (st != TROP_OK) return st;
     if (plan.path == GP_NONE) return ok();
     int dev = -1;
