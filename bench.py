@@ -268,6 +268,25 @@ def other_workloads(torch, tb, inputs, timer, dev):
         del Ad, Bd, C, I
         torch.cuda.empty_cache()
 
+    # a narrow product with a long K (one 64 x 64 output tile): unsplit, the
+    # whole product is one workgroup's; split along K it spreads over the chip
+    g = torch.Generator(device="cpu").manual_seed(17)
+    As = torch.randn(1, 64, 65536, generator=g).to(dev)
+    Bs = torch.randn(1, 65536, 64, generator=g).to(dev)
+    Cs = torch.empty(1, 64, 64, device=dev)
+    Is = torch.empty(1, 64, 64, dtype=torch.int32, device=dev)
+    ws = torch.empty(tb.tropical_gemm_workspace_size(64, 64, 65536, 1), dtype=torch.uint8, device=dev)
+    ops = 2 * 64 * 64 * 65536
+    t1 = timer.time(lambda: tb.tropical_gemm_strided_batched("max_plus", As, Bs, Cs, Is), reps=5, warmup=1)
+    t2 = timer.time(lambda: tb.tropical_gemm_strided_batched_ws("max_plus", As, Bs, Cs, Is, workspace=ws),
+                    reps=reps, warmup=2)
+    out["maxplus_f32_b1_64x64_k65536"] = {
+        "unsplit_us": round(t1["median_ms"] * 1e3, 1), "split_k_us": round(t2["median_ms"] * 1e3, 1),
+        "unsplit_GOPS": round(ops / (t1["median_ms"] * 1e-3) / 1e9, 1),
+        "split_k_GOPS": round(ops / (t2["median_ms"] * 1e-3) / 1e9, 1), "workspace_bytes": ws.numel()}
+    log(f"[bench] split K 64x64x65536: {out['maxplus_f32_b1_64x64_k65536']}")
+    del As, Bs, Cs, Is, ws
+
     # backward (winner routing) of the headline product: grad_a and grad_b
     # from its argmax and an N(0, 1) upstream gradient
     w = inputs.WORKLOADS[2]

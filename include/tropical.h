@@ -108,7 +108,8 @@ typedef enum {
     TROP_K_GATHER_NAIVE = 5, /* permute/gather, one thread per element   */
     TROP_K_GATHER_REDUCE = 6,/* gather with a (+)-reduction (trace)      */
     TROP_K_GEMM_BACKWARD = 7,/* gradient routed along the argmax         */
-    TROP_K_FAMILIES = 8
+    TROP_K_GEMM_SPLITK_MERGE = 8, /* merge of split-K partials           */
+    TROP_K_FAMILIES = 9
 } trop_kernel_family;
 
 typedef struct {
@@ -155,6 +156,40 @@ TROP_API trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_
                                           void* C, trop_strides sC, int32_t* argmax,
                                           int64_t m, int64_t n, int64_t k, int64_t batch,
                                           void* stream);
+
+/*
+ * Workspace (bytes) with which tropical_gemm_strided_batched_ws splits a
+ * product of this shape along K; 0 when it would not split it.  Host-only.
+ * Errors: TROP_ERR_INVALID_ARGUMENT (negative size, NULL bytes).
+ */
+TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t batch,
+                                         size_t* bytes);
+
+/*
+ * tropical_gemm_strided_batched with a workspace, which lets a product with
+ * few output tiles and a long K run on the whole device: K is cut into
+ * `ksplit` ranges of whole 256-term blocks, each (tile, range) pair is one
+ * unit of the tiled kernel writing a partial value and global argmax into
+ * the workspace, and a merge kernel keeps, per output, the first partial
+ * (in range order) that is strictly better than those before it.  Every
+ * range is scanned with the same strict rule, so the results -- values,
+ * their bits and the smallest winning k -- are those of the unsplit call
+ * (the tie rule of [PR35]'s argmax survives the split).  The split is used
+ * when the product has fewer 64 x 64 output tiles (times batch) than the
+ * device has CUs and K >= 1024; tropical_gemm_workspace_size reports the
+ * bytes (0: no split, and the call equals tropical_gemm_strided_batched).
+ * workspace: NULL with workspace_bytes 0 (never split), or device memory of
+ *   at least that size, used only by work on `stream`.
+ * Errors: as tropical_gemm_strided_batched, plus
+ *   TROP_ERR_WORKSPACE_TOO_SMALL (a non-NULL workspace below the size).
+ */
+TROP_API trop_status tropical_gemm_strided_batched_ws(trop_semiring semiring, trop_dtype dtype,
+                                             const void* A, trop_strides sA,
+                                             const void* B, trop_strides sB,
+                                             void* C, trop_strides sC, int32_t* argmax,
+                                             int64_t m, int64_t n, int64_t k, int64_t batch,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
 
 /*
  * Backward of tropical_gemm_strided_batched: the gradients of

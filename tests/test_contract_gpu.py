@@ -133,3 +133,20 @@ def test_workload5_full(tb, orc):
     Cr, Ir = orc.contract_pair("iijb,kjb->bki", "max_plus", A.numpy(), B.numpy())
     assert_bits_equal(C.cpu().numpy(), Cr, "workload 5")
     assert_equal(I.cpu().numpy(), Ir, "workload 5 argmax")
+
+
+def test_contract_long_contraction_splits_k(tb, orc):
+    """A narrow product with a long contracted extent is split along K
+    inside the pairwise driver (its workspace holds the partials)."""
+    spec = "ikl,klj->ji"
+    g = torch.Generator().manual_seed(31)
+    A = torch.randn(24, 64, 150, generator=g)
+    B = torch.randn(64, 150, 40, generator=g)
+    desc = tb.tropical_contract_pair_describe(spec, A.shape, B.shape)
+    assert "splitK" in desc, desc
+    for sr in ("max_plus", "min_plus"):
+        C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV))
+        torch.cuda.synchronize()
+        Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
+        assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr}")
+        assert_equal(I.cpu().numpy(), Ir, f"{spec} {sr} argmax")

@@ -265,3 +265,43 @@ def test_permute_wide_pairs_unaligned_and_rank8(tb, orc):
     with pytest.raises(tb.TropicalError) as e:
         tb.tropical_permute(torch.zeros(4, 4, dtype=torch.float16, device=DEV), (1, 0))
     assert e.value.status == tb.UNSUPPORTED
+
+
+@pytest.mark.parametrize("R", [2, 4, 8, 16])
+@pytest.mark.parametrize("dims", [(6, 50, 37), (1, 300, 65), (3, 7, 129)], ids=lambda d: "x".join(map(str, d)))
+def test_permute_runs_path(tb, orc, R, dims):
+    """A short contiguous last axis (a run of R words) whose neighbour in the
+    output is not its neighbour in the input: the runs path transposes
+    whole runs through LDS.  Ragged tiles, pairs and unaligned views."""
+    b, p_, q_ = dims
+    g = torch.Generator().manual_seed(R * 1000 + p_)
+    x = torch.randn(b, p_, q_, R, generator=g)
+    idx = torch.randint(-10 ** 6, 10 ** 6, (b, p_, q_, R), generator=g, dtype=torch.int32)
+    xd, idd = x.to(DEV), idx.to(DEV)
+    perm = (0, 2, 1, 3)
+    before = launches(tb)
+    out, out2 = tb.tropical_permute(xd, perm, x2=idd)
+    torch.cuda.synchronize()
+    assert delta(before, launches(tb)) == {"gather_tiled": 1}
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"runs R={R} {dims}")
+    assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), perm), f"runs pair R={R} {dims}")
+    # the run axis moved to the front is not a run any more; the batch
+    # axis last is the other transpose of the runs
+    for perm in ((2, 0, 1, 3), (1, 2, 0, 3)):
+        out = tb.tropical_permute(xd, perm)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"runs R={R} {dims} {perm}")
+    # one word into the allocation: 4-byte aligned only (word accesses)
+    base = torch.randn(1 + x.numel(), generator=g)
+    xv = base[1:].view(x.shape)
+    xvd = base.to(DEV)[1:].view(x.shape)
+    out = tb.tropical_permute(xvd, (0, 2, 1, 3))
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(xv.numpy(), (0, 2, 1, 3)), f"runs unaligned R={R}")
+
+
+def test_runs_path_in_contraction_describe(tb):
+    # the lattice network's boundary gather: a 16-word run (bond 16) whose
+    # neighbour moves from the front to the end
+    desc = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
+    assert "A=gather:runs" in desc, desc

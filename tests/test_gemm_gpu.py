@@ -292,3 +292,100 @@ def test_value_only_special_values_and_signed_zeros(tb, orc):
 def test_value_only_workload2_full(tb, orc):
     A, B = inputs.gemm_operands(2)
     check(tb, orc, "max_plus", A, B, "workload 2 value only", argmax=False)
+
+
+# ---------------------------------------------------------------------------
+# split K (tropical_gemm_strided_batched_ws): few output tiles, long K
+# ---------------------------------------------------------------------------
+
+def gpu_gemm_ws(tb, sr, A, B, argmax=True, workspace=None):
+    from gpu_util import device_copy
+    Ad, Bd = device_copy(A), device_copy(B)
+    b, m, _ = A.shape
+    n = B.shape[2]
+    C = torch.empty(b, m, n, dtype=A.dtype, device=DEV)
+    I = torch.empty(b, m, n, dtype=torch.int32, device=DEV) if argmax else None
+    tb.tropical_gemm_strided_batched_ws(sr, Ad, Bd, C, I, workspace=workspace)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), (I.cpu().numpy() if argmax else None)
+
+
+SPLIT_SHAPES = [(1, 64, 8192, 64), (1, 17, 5000, 33), (3, 70, 3000, 50), (1, 1, 20000, 1),
+                (2, 64, 4096, 130), (1, 5, 1024, 3)]
+
+
+@pytest.mark.parametrize("sr,dt", PAIRS)
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_k_matches_oracle(tb, orc, sr, dt, shape):
+    b, m, k, n = shape
+    assert tb.tropical_gemm_workspace_size(m, n, k, b) > 0, "this shape should split"
+    A, B = make(sr, dt, b, m, k, n, seed=zlib.crc32(repr((sr, dt, shape)).encode()) % 10000,
+                b_col=(shape[0] == 2))
+    Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy())
+    before = dict(tb.tropical_get_stats()["launches"])
+    C, I = gpu_gemm_ws(tb, sr, A, B)
+    after = tb.tropical_get_stats()["launches"]
+    assert after["gemm_splitk_merge"] - before["gemm_splitk_merge"] == 1
+    assert_bits_equal(C, Cr, f"split {sr} {dt} {shape} C")
+    assert_equal(I, Ir, f"split {sr} {dt} {shape} argmax")
+    C, _ = gpu_gemm_ws(tb, sr, A, B, argmax=False)
+    assert_bits_equal(C, Cr, f"split value-only {sr} {dt} {shape} C")
+
+
+def test_split_k_ties_signed_zeros_and_nan_across_ranges(tb, orc):
+    k = 8192
+    # every term equal: the winner is k = 0, in the first range
+    A = torch.zeros(1, 40, k)
+    B = torch.zeros(1, k, 30)
+    C, I = gpu_gemm_ws(tb, "max_plus", A, B)
+    assert (I == 0).all()
+    # the maximum 0 first reached as -0 in the last range and as +0 in an
+    # earlier one, or the other way round: C has the first winner's bits
+    for first, later in ((-0.0, 0.0), (0.0, -0.0)):
+        A = torch.full((1, 8, k), -5.0)
+        B = torch.full((1, k, 8), -0.0)
+        A[0, :, 3000] = first
+        A[0, :, k - 10] = later
+        C, I = gpu_gemm_ws(tb, "max_plus", A, B)
+        Cr, Ir = orc.gemm("max_plus", A.numpy(), B.numpy())
+        assert_bits_equal(C, Cr, f"signed zero {first} then {later}")
+        assert_equal(I, Ir, "signed zero argmax")
+        assert (I == 3000).all()
+    # NaN and +-inf scattered over the ranges
+    g = torch.Generator().manual_seed(12)
+    kinds = ["inf", "-inf", "nan", "-0", "0"]
+    for sr in ("max_plus", "min_plus", "max_mul"):
+        A = special_matrix((1, 30, k), g, kinds)
+        B = special_matrix((1, k, 20), g, kinds)
+        C, I = gpu_gemm_ws(tb, sr, A, B)
+        Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy())
+        assert_bits_equal(C, Cr, f"special split {sr}")
+        assert_equal(I, Ir, f"special split {sr} argmax")
+
+
+def test_split_k_workspace_rules(tb, orc):
+    A, B = make("max_plus", "f32", 1, 64, 8192, 64, seed=3)
+    need = tb.tropical_gemm_workspace_size(64, 64, 8192, 1)
+    assert need > 0
+    # large grids and short K do not split
+    assert tb.tropical_gemm_workspace_size(256, 256, 4096, 64) == 0
+    assert tb.tropical_gemm_workspace_size(64, 64, 1000, 1) == 0
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty(1, 64, 64, device=DEV)
+    with pytest.raises(tb.TropicalError) as e:
+        tb.tropical_gemm_strided_batched_ws("max_plus", Ad, Bd, C,
+                                            workspace=torch.empty(need - 4, dtype=torch.uint8, device=DEV))
+    assert e.value.status == tb.WORKSPACE_TOO_SMALL
+    # a larger workspace is fine; no workspace means no split
+    Cr, Ir = orc.gemm("max_plus", A.numpy(), B.numpy())
+    I = torch.empty(1, 64, 64, dtype=torch.int32, device=DEV)
+    tb.tropical_gemm_strided_batched_ws("max_plus", Ad, Bd, C, I,
+                                        workspace=torch.empty(need + 4096, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert_bits_equal(C.cpu().numpy(), Cr, "larger workspace")
+    before = dict(tb.tropical_get_stats()["launches"])
+    tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, I)
+    torch.cuda.synchronize()
+    assert tb.tropical_get_stats()["launches"]["gemm_splitk_merge"] == before["gemm_splitk_merge"]
+    assert_bits_equal(C.cpu().numpy(), Cr, "no workspace")
+    assert_equal(I.cpu().numpy(), Ir, "no workspace argmax")

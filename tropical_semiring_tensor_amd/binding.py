@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "TROP_OK", 1: "TROP_ERR_INVALID_ARGUMENT", 2: "TROP_ERR_UNSUP
 SEMIRINGS = {"max_plus": 0, "min_plus": 1, "max_mul": 2}
 F32, I32 = 0, 1
 KERNEL_FAMILIES = ["gemm_tiled", "gemm_simple", "fill", "gather_copy", "gather_tiled",
-                   "gather_naive", "gather_reduce", "gemm_backward"]
+                   "gather_naive", "gather_reduce", "gemm_backward", "gemm_splitk_merge"]
 MAX_DIMS = 8
 
 
@@ -48,7 +48,7 @@ class trop_tree_step(ctypes.Structure):
 
 class trop_stats(ctypes.Structure):
     _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
-                ("launches", ctypes.c_uint64 * 8), ("host_syncs", ctypes.c_uint64),
+                ("launches", ctypes.c_uint64 * 9), ("host_syncs", ctypes.c_uint64),
                 ("memcpy_calls", ctypes.c_uint64)]
 
 
@@ -71,6 +71,9 @@ def lib():
     L.tropical_init.argtypes = [i32]
     L.tropical_gemm_strided_batched.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp,
                                                 trop_strides, vp, i64, i64, i64, i64, vp]
+    L.tropical_gemm_strided_batched_ws.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp,
+                                                   trop_strides, vp, i64, i64, i64, i64, vp, sz, vp]
+    L.tropical_gemm_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.tropical_gemm_backward.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp, vp,
                                          trop_strides, vp, trop_strides, vp, trop_strides,
                                          i64, i64, i64, i64, vp]
@@ -96,6 +99,7 @@ def lib():
     L.tropical_get_stats.argtypes = [ctypes.POINTER(trop_stats)]
     L.tropical_reset_stats.restype = None
     for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_gemm_backward", "tropical_permute",
+               "tropical_gemm_strided_batched_ws", "tropical_gemm_workspace_size",
                "tropical_diag_gather", "tropical_contract_pair_workspace_size",
                "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats",
                "tropical_tree_plan_create", "tropical_tree_workspace_size", "tropical_tree_step_info",
@@ -172,6 +176,37 @@ def tropical_gemm_strided_batched(semiring, A, B, C, argmax=None, stream=None):
                                              _ptr(C3), sC, _ptr(argmax), m, n, k, batch,
                                              _stream(stream))
     _check(st, "tropical_gemm_strided_batched")
+    return C, argmax
+
+
+def tropical_gemm_workspace_size(m, n, k, batch=1):
+    nb = ctypes.c_size_t(0)
+    _check(lib().tropical_gemm_workspace_size(int(m), int(n), int(k), int(batch), ctypes.byref(nb)),
+           "tropical_gemm_workspace_size")
+    return nb.value
+
+
+def tropical_gemm_strided_batched_ws(semiring, A, B, C, argmax=None, workspace=None, stream=None):
+    """tropical_gemm_strided_batched with a workspace (split along K when
+    the product has few output tiles and a long K).  workspace: None to
+    allocate tropical_gemm_workspace_size bytes with torch, or a uint8
+    device tensor."""
+    A3, B3, C3 = _as3(A), _as3(B), _as3(C)
+    batch, m, k = A3.shape
+    n = B3.shape[2]
+    if argmax is not None and _as3(argmax).stride() != C3.stride():
+        raise ValueError("argmax must have the strides of C")
+    if workspace is None:
+        nb = tropical_gemm_workspace_size(m, n, k, batch)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=A3.device) if nb else None
+    sA = trop_strides(A3.stride(1), A3.stride(2), A3.stride(0))
+    sB = trop_strides(B3.stride(1), B3.stride(2), B3.stride(0))
+    sC = trop_strides(C3.stride(1), C3.stride(2), C3.stride(0))
+    st = lib().tropical_gemm_strided_batched_ws(_sr(semiring), _dt(A3), _ptr(A3), sA, _ptr(B3), sB,
+                                                _ptr(C3), sC, _ptr(argmax), m, n, k, batch, _ptr(workspace),
+                                                workspace.numel() if workspace is not None else 0,
+                                                _stream(stream))
+    _check(st, "tropical_gemm_strided_batched_ws")
     return C, argmax
 
 

@@ -29,6 +29,22 @@ struct TropGemmParams {
     int32_t a_vec, b_vec;      // 16-byte vector loads are aligned and legal
     int32_t swizzle;           // remap workgroups so each XCD owns a tile range
     int32_t pad_;
+    // split K: the tile stream covers (batch entry, split, tile); split s
+    // takes k in [s kchunk, min((s + 1) kchunk, k)) and writes its partial
+    // value and (global) argmax at C / argmax + s c_split.  ksplit = 1: no
+    // split (kchunk = k, c_split = 0).
+    int64_t ksplit, kchunk, c_split;
+};
+
+// Merge of split-K partials: out = the first strictly better of the
+// ksplit partials (split 0 first), stored [split][batch][m][n] contiguous.
+struct TropSplitMergeParams {
+    const void* pval;
+    const int32_t* pidx;  // may be null (value only)
+    void* C;
+    int32_t* argmax;      // may be null
+    int64_t sc_row, sc_col, sc_batch;
+    int64_t m, n, batch, ksplit;
 };
 
 struct TropFillParams {
@@ -63,6 +79,7 @@ struct TropGatherParams {
     uint32_t mag_s[TROP_MAX_DIMS];
     uint32_t vpr, vpr_m, vpr_s;  // copy path: 16-byte vectors per output row
     int32_t tile_p;              // vectorised tiled path: tile extent along ax_in
+    int32_t run_shift;           // runs path: log2 of the run length R (words)
     // reduction (trace)
     int32_t nred;
     int64_t rshape[TROP_MAX_DIMS];

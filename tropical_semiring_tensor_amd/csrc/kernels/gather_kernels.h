@@ -17,6 +17,10 @@
 //           of the (ax_in, last) plane goes through LDS with one word of
 //           padding per row, so reads are coalesced along ax_in and writes
 //           along the last axis, without LDS bank conflicts;
+//  * runs:  the last output axis is a short run (2 to 16 words) with input
+//           stride 1 and another output axis steps from run to run in the
+//           input; tiles of runs go through LDS so that reads and writes
+//           are long contiguous segments (a transpose of wide elements);
 //  * naive: one thread per output element, digits decoded from the
 //           linear index (the fallback).
 //
@@ -226,6 +230,99 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p)
                 for (int t = 0; t < NT; ++t) {
                     const uint32_t* col = &tile[t][wq * LDT + pl];
                     st16(static_cast<uint32_t*>(p.out[t]) + dst, u32x4{col[0], col[LDT], col[2 * LDT], col[3 * LDT]});
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Runs path.  Axes: Z = the last output axis (extent R = 2^run_shift words,
+// input stride 1), Q = the one before it, P = ax_in with input stride R, so
+// for fixed q the runs p, p + 1, ... are adjacent in the input, and for
+// fixed p the runs q, q + 1, ... are adjacent in the output.  A tile holds
+// RUN_TQ q-rows of RUN_TPR words (RUN_TPR / R runs along P):
+//   read:  each q-row is one contiguous input segment of RUN_TPR words;
+//   write: each p-row is one contiguous output segment of RUN_TQ R words.
+// VEC: 16-byte accesses (every segment start is a multiple of 4 words and
+// both pointers are 16-byte aligned; checked on the host); otherwise words.
+constexpr int RUN_TPR = 128;
+constexpr int RUN_TQ = 32;
+
+template <bool VEC, int NT>
+__device__ __forceinline__ void gather_runs_body(const TropGatherParams& p) {
+    constexpr int LDT = RUN_TPR + 4;  // LDS q-row (keeps 16-byte alignment)
+    __shared__ __attribute__((aligned(16))) uint32_t tile[NT][RUN_TQ * LDT];
+    const int nd = p.ndim;
+    const int P = p.ax_in, Q = nd - 2, Z = nd - 1;
+    const int lr = p.run_shift;
+    const int R = 1 << lr;
+    const int TP = RUN_TPR >> lr;  // runs per tile along P
+    const int64_t EP = p.shape[P], EQ = p.shape[Q];
+    const int64_t sQ = p.istride[Q];
+    int64_t oP = 1;  // output stride of P
+    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    const int tid = threadIdx.x;
+    const int64_t per_batch = p.tiles_p * p.tiles_q;
+    const int64_t nblk = per_batch * p.nbatch;
+    constexpr int RVEC = RUN_TQ * RUN_TPR / 4;  // 16-byte slots of a tile
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t tq = blk % p.tiles_q;
+        const int64_t tp = (blk / p.tiles_q) % p.tiles_p;
+        int64_t bi = blk / per_batch;
+        int64_t ibase = 0, obase = 0, ostride = 1;
+        for (int d = nd - 1; d >= 0; --d) {
+            const int64_t e = p.shape[d];
+            if (d != P && d != Q && d != Z) {
+                const int64_t digit = bi % e;
+                bi /= e;
+                ibase += digit * p.istride[d];
+                obase += digit * ostride;
+            }
+            ostride *= e;
+        }
+        const int64_t p0 = tp * TP, q0 = tq * RUN_TQ;
+        const int np = (int)(EP - p0 < TP ? EP - p0 : TP);
+        const int nq = (int)(EQ - q0 < RUN_TQ ? EQ - q0 : RUN_TQ);
+        const int rw = np << lr;  // words per q-row
+        // read phase: q-row ql, words w .. w + 3
+        for (int v = tid; v < RVEC; v += GATHER_THREADS) {
+            const int ql = v / (RUN_TPR / 4), w = (v % (RUN_TPR / 4)) * 4;
+            if (ql >= nq || w >= rw) continue;
+            const int64_t src = ibase + (p0 << lr) + (q0 + ql) * sQ + w;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t* in = static_cast<const uint32_t*>(p.in[t]);
+                uint32_t* row = &tile[t][ql * LDT + w];
+                if (VEC && w + 4 <= rw) {
+                    const u32x4 x = ld16(in + src);
+                    *reinterpret_cast<u32x4*>(row) = x;
+                } else {
+                    for (int e = 0; e < 4 && w + e < rw; ++e) row[e] = ld4(in + src + e);
+                }
+            }
+        }
+        __syncthreads();
+        // write phase: p-row pl, words w .. w + 3 of its nq R words
+        const int vpr = (RUN_TQ * R) / 4;  // 16-byte slots per p-row
+        const int ow = nq << lr;           // words per p-row
+        for (int v = tid; v < TP * vpr; v += GATHER_THREADS) {
+            const int pl = v / vpr, w = (v % vpr) * 4;
+            if (pl >= np || w >= ow) continue;
+            const int64_t dst = obase + (p0 + pl) * oP + (q0 << lr) + w;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int wi = w + e;
+                    x[e] = tile[t][(wi >> lr) * LDT + (pl << lr) + (wi & (R - 1))];
+                }
+                uint32_t* out = static_cast<uint32_t*>(p.out[t]);
+                if (VEC && w + 4 <= ow) {
+                    st16(out + dst, u32x4{x[0], x[1], x[2], x[3]});
+                } else {
+                    for (int e = 0; e < 4 && w + e < ow; ++e) st4(out + dst + e, x[e]);
                 }
             }
         }

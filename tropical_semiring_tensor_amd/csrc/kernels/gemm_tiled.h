@@ -104,16 +104,25 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t L, int64_t total) {
     return tall * per + (x - tall) * (per - 1) + local;
 }
 
-// Batch entry and output-tile origin of logical tile L.
+// Batch entry, K split, output-tile origin and K extent of logical tile L.
 struct TileCoord {
-    int64_t b, row0, col0;
+    int64_t b, s, row0, col0, kt;
 };
 
+template <bool SPLIT>
 __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
                                                 int64_t total) {
     const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
     const int64_t t = lg % tiles;
-    return {lg / tiles, (t / p.tiles_n) * GEMM_BM, (t % p.tiles_n) * GEMM_BN};
+    const int64_t bs = lg / tiles;
+    TileCoord c{bs, 0, (t / p.tiles_n) * GEMM_BM, (t % p.tiles_n) * GEMM_BN, p.k};
+    if constexpr (SPLIT) {
+        c.b = bs / p.ksplit;
+        c.s = bs % p.ksplit;
+        const int64_t rest = p.k - c.s * p.kchunk;
+        c.kt = rest < p.kchunk ? rest : p.kchunk;
+    }
+    return c;
 }
 
 // One thread's share of one operand tile per slice: NV vectors of 4
@@ -238,13 +247,13 @@ struct OpLoad {
 // the bits of the first winning term, recomputed from global memory at the
 // resolved index (with argmax) or found by a scan along k (value only).
 // Rare and only taken by a wave that holds such an output.
-template <int SR, typename T, bool ARG>
+template <int SR, typename T, bool ARG, bool SPLIT>
 __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoord ct, int tx,
                                                           int ty, T (&best)[GEMM_TR][4],
                                                           const int (&idx)[GEMM_TR][4]) {
     using R = Ring<SR, T>;
-    const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch;
-    const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch;
+    const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
+    const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
     for (int r = 0; r < GEMM_TR; ++r)
         for (int c = 0; c < 4; ++c) {
             const int64_t i = ct.row0 + ty + GEMM_RS * r, j = ct.col0 + tx + 16 * c;
@@ -255,7 +264,7 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
                 const int64_t k = idx[r][c];
                 best[r][c] = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
             } else {
-                for (int64_t k = 0; k < p.k; ++k) {
+                for (int64_t k = 0; k < (SPLIT ? ct.kt : p.k); ++k) {
                     const T t = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
                     if (t == best[r][c]) {
                         best[r][c] = t;
@@ -269,8 +278,10 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
 // The tiled kernel.  A workgroup walks the tiles L = blockIdx.x,
 // blockIdx.x + gridDim.x, ... as one stream of (tile, slice) steps, so the
 // fetch of a tile's first slice overlaps the previous tile's last slice,
-// re-scan and stores.
-template <int SR, typename T, bool ARG>
+// re-scan and stores.  SPLIT: the stream also covers the K ranges of a
+// split-K product (a separate instantiation, so that the unsplit kernel
+// keeps one slice count and one K for every tile).
+template <int SR, typename T, bool ARG, bool SPLIT>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
@@ -290,12 +301,16 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-    const int64_t total = tiles * p.batch;
-    const int nslices = (int)((p.k + GEMM_SL - 1) / GEMM_SL);
+    const int64_t total = tiles * p.batch * (SPLIT ? p.ksplit : 1);
     const int64_t gstride = gridDim.x;
+    // slices of a tile (its K extent: the split's, or the whole K)
+    const int nslices_k = (int)((p.k + GEMM_SL - 1) / GEMM_SL);
+    auto slices_of = [&](const TileCoord& tc) {
+        return SPLIT ? (int)((tc.kt + GEMM_SL - 1) / GEMM_SL) : nslices_k;
+    };
 
     int64_t cL = blockIdx.x;  // tile being computed
-    if (cL >= total || nslices == 0) return;  // K = 0 is handled by the fill kernel
+    if (cL >= total || p.k == 0) return;  // K = 0 is handled by the fill kernel
     if (blockDim.x != GEMM_THREADS) return;   // launched with a block it was not built for
 
     LA la;
@@ -304,24 +319,30 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid);
     const T* const Ag = static_cast<const T*>(p.A);
     const T* const Bg = static_cast<const T*>(p.B);
+    int f_nsl = 0;  // slices of the tile being fetched
     auto point = [&](const TileCoord& tc) {
-        la.at(Ag + tc.b * p.sa_batch, tc.row0, p.sa_row, p.sa_col, tid);
-        lb.at(Bg + tc.b * p.sb_batch, tc.col0, p.sb_col, p.sb_row, tid);
+        la.at(Ag + tc.b * p.sa_batch + (SPLIT ? tc.s * p.kchunk * p.sa_col : 0), tc.row0, p.sa_row, p.sa_col, tid);
+        lb.at(Bg + tc.b * p.sb_batch + (SPLIT ? tc.s * p.kchunk * p.sb_row : 0), tc.col0, p.sb_col, p.sb_row, tid);
+        if constexpr (SPLIT) {
+            la.k_lim = tc.kt;
+            lb.k_lim = tc.kt;
+        }
+        f_nsl = slices_of(tc);
     };
 
     // Fetch cursor: the (tile, slice) whose data was last requested.
     int64_t fL = cL;
     int fg = 0;
-    point(tile_coord(p, fL, tiles, total));
+    point(tile_coord<SPLIT>(p, fL, tiles, total));
     bool fetch_valid = true;
     T ra[NV][4], rb[NV][4];
     auto fetch_next = [&]() {
         ++fg;
-        if (fg == nslices) {
+        if (fg == (SPLIT ? f_nsl : nslices_k)) {
             fg = 0;
             fL += gstride;
             fetch_valid = fL < total;
-            if (fetch_valid) point(tile_coord(p, fL, tiles, total));
+            if (fetch_valid) point(tile_coord<SPLIT>(p, fL, tiles, total));
         }
         if (fetch_valid) {
             la.load(fg, R::zero(), ra);
@@ -340,7 +361,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     }
     __syncthreads();
 
-    TileCoord ct = tile_coord(p, cL, tiles, total);
+    TileCoord ct = tile_coord<SPLIT>(p, cL, tiles, total);
+    int c_nsl = slices_of(ct);  // slices of the tile being computed
     T best[GEMM_TR][4];
     int win[GEMM_TR][4];
     int idx[GEMM_TR][4];
@@ -364,7 +386,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     int ring = 0;        // value only: ring slot of the current slice
     for (;;) {
         const int s = ARG ? g % NSL : ring;
-        const bool last = (g + 1 == nslices);
+        const bool last = (g + 1 == (SPLIT ? c_nsl : nslices_k));
         const bool bend = ARG ? (last || s == NSL - 1) : last;
         // The registers hold slice g + 1 of this tile: its LDS slot is free
         // (argmax: inside the block; value only: the ring slot read two
@@ -382,7 +404,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             // Chunks of the last slice that lie wholly past K hold only
             // padding (terms that cannot win): they are skipped, which makes
             // a small K cost its own chunks and not a whole slice.
-            const int64_t k_left = p.k - (int64_t)g * GEMM_SL;
+            const int64_t k_left = (SPLIT ? ct.kt : p.k) - (int64_t)g * GEMM_SL;
             const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + GEMM_CH - 1) / GEMM_CH) * QPC;
             V fa[2][GEMM_TR], fb[2][4];
 #pragma unroll
@@ -503,11 +525,13 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                             for (int c = 0; c < 4; ++c) any0 |= best[r][c] == (T)0;
                         if (__any(any0))
-                            zero_bits_fixup<SR, T, ARG>(p, ct, tx, ty, best, idx);
+                            zero_bits_fixup<SR, T, ARG, SPLIT>(p, ct, tx, ty, best, idx);
                     }
                 }
-                T* __restrict__ C = static_cast<T*>(p.C) + ct.b * p.sc_batch;
-                int32_t* __restrict__ I = ARG ? p.argmax + ct.b * p.sc_batch : nullptr;
+                const int64_t c_off = ct.b * p.sc_batch + (SPLIT ? ct.s * p.c_split : 0);
+                T* __restrict__ C = static_cast<T*>(p.C) + c_off;
+                int32_t* __restrict__ I = ARG ? p.argmax + c_off : nullptr;
+                const int k_off = SPLIT ? (int)(ct.s * p.kchunk) : 0;  // a split's argmax is global
 #pragma unroll
                 for (int r = 0; r < GEMM_TR; ++r) {
                     const int64_t i = ct.row0 + ty + GEMM_RS * r;
@@ -518,7 +542,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         if (j >= p.n) continue;
                         const int64_t o = i * p.sc_row + j * p.sc_col;
                         C[o] = best[r][c];
-                        if constexpr (ARG) I[o] = idx[r][c];
+                        if constexpr (ARG) I[o] = idx[r][c] + k_off;
                     }
                 }
             }
@@ -530,7 +554,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             fetch_next();
             if (last) {
                 cL += gstride;
-                ct = tile_coord(p, cL, tiles, total);
+                ct = tile_coord<SPLIT>(p, cL, tiles, total);
+                c_nsl = slices_of(ct);
                 reset_outputs();
                 g = -1;
                 blk_k0 = 0;

@@ -10,11 +10,19 @@ using namespace trop;
 #define TROP_GEMM_ENTRIES(NAME, SR, T)                                                        \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_##NAME(         \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, T, true>(p);                                                        \
+        gemm_tiled_body<SR, T, true, false>(p);                                                 \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo_##NAME(      \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, T, false>(p);                                                       \
+        gemm_tiled_body<SR, T, false, false>(p);                                                \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, true>(p);                                                  \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo_split_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, false, true>(p);                                                 \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_simple_##NAME(TropGemmParams p) { \
         gemm_simple_body<SR, T>(p);                                                             \
@@ -22,6 +30,10 @@ using namespace trop;
     extern "C" __global__ __launch_bounds__(256) void trop_gather_reduce_##NAME(                \
         TropGatherParams p) {                                                                   \
         gather_reduce_body<SR, T>(p);                                                           \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gemm_splitk_merge_##NAME(            \
+        TropSplitMergeParams p) {                                                               \
+        splitk_merge_body<SR, T>(p);                                                            \
     }
 
 TROP_GEMM_ENTRIES(maxplus_f32, TROP_SR_MAX_PLUS, float)
@@ -51,6 +63,15 @@ TROP_TILED_VEC(64, 1)
 TROP_TILED_VEC(16, 2)
 TROP_TILED_VEC(32, 2)
 TROP_TILED_VEC(64, 2)
+
+#define TROP_RUNS(NAME, VEC, NT)                                                                  \
+    extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_runs_##NAME(TropGatherParams p) { \
+        gather_runs_body<VEC, NT>(p);                                                                \
+    }
+TROP_RUNS(v_n1, true, 1)
+TROP_RUNS(v_n2, true, 2)
+TROP_RUNS(s_n1, false, 1)
+TROP_RUNS(s_n2, false, 2)
 
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
     gather_naive_body(p);

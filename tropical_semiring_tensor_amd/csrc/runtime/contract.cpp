@@ -302,6 +302,12 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
         P.off_i = off;
         off += align_up((size_t)(P.nb * P.M * P.N) * 4);
     }
+    const SplitK sk = plan_splitk(P.gm, P.gn, P.K, P.nb);
+    if (sk.bytes > 0) {
+        P.off_split = off;
+        P.split_bytes = sk.bytes;
+        off += sk.bytes;
+    }
     P.ws = off;
     return TROP_OK;
 }
@@ -310,10 +316,10 @@ std::string pair_describe(const Plan& P) {
     char buf[512];
     std::snprintf(buf, sizeof(buf),
                   "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm %s batch=%lld m=%lld "
-                  "n=%lld k=%lld; A=%s%s B=%s%s out=%s%s; workspace=%zu",
+                  "n=%lld k=%lld%s; A=%s%s B=%s%s out=%s%s; workspace=%zu",
                   P.batch.c_str(), P.left.c_str(), P.right.c_str(), P.contracted.c_str(), P.a_red.c_str(),
                   P.b_red.c_str(), P.swap ? "B(x)A" : "A(x)B", (long long)P.nb, (long long)P.gm,
-                  (long long)P.gn, (long long)P.K,
+                  (long long)P.gn, (long long)P.K, P.split_bytes ? " splitK" : "",
                   (P.swap ? P.b_fold : P.a_fold) ? "fold" : "gather:",
                   (P.swap ? P.b_fold : P.a_fold) ? "" : gather_path_name((P.swap ? P.gb : P.ga).path),
                   (P.swap ? P.a_fold : P.b_fold) ? "fold" : "gather:",
@@ -357,7 +363,8 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
     void* c_gemm = P.c_direct ? C : static_cast<void*>(ws + P.off_c);
     int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
     const trop_strides sC = {P.gn, 1, P.gm * P.gn};
-    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s);
+    st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s,
+                  P.split_bytes ? ws + P.off_split : nullptr, P.split_bytes);
     if (st != TROP_OK) return st;
     // 3. one paired permute of value and argmax into the output order
     if (!P.c_direct) {
@@ -396,6 +403,7 @@ extern "C" trop_status tropical_contract_pair_workspace_size(const char* spec, c
     // upper bound: room for both operand pre-passes and the output permute
     size_t ws = align_up((size_t)(P.nb * P.M * P.K) * 4) + align_up((size_t)(P.nb * P.K * P.N) * 4);
     if (!P.c_direct) ws += 2 * align_up((size_t)(P.nb * P.M * P.N) * 4);
+    ws += plan_splitk(P.M, P.N, P.K, P.nb).bytes;  // K split of a long, narrow product
     *bytes = ws;
     return ok();
 }

@@ -34,8 +34,9 @@ struct PairPlan {
     int64_t gm = 1, gn = 1;  // GEMM rows and columns
     trop_strides sA{}, sB{};
     GatherPlan ga{}, gb{}, gc{};
-    // workspace layout of the step (bytes, relative to its scratch base)
-    size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, ws = 0;
+    // workspace layout of the step (bytes, relative to its scratch base);
+    // split_bytes > 0: the GEMM is split along K, partials at off_split
+    size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, off_split = 0, split_bytes = 0, ws = 0;
 };
 
 // "lhs,rhs->out" into its three subscripts (spaces ignored).

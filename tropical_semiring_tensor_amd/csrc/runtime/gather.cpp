@@ -77,6 +77,7 @@ const char* gather_path_name(GatherPath p) {
         case GP_TILED: return "tiled";
         case GP_NAIVE: return "naive";
         case GP_REDUCE: return "reduce";
+        case GP_RUNS: return "runs";
     }
     return "?";
 }
@@ -160,6 +161,23 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
         return TROP_OK;
     }
     if (p.istride[nd - 1] == 1) {
+        // A short last axis (a run of 2 to 16 words, e.g. the words of an
+        // 8- or 16-byte element) that another axis steps over in the input:
+        // transpose whole runs through LDS instead of copying short rows.
+        const int64_t R = p.shape[nd - 1];
+        if (nd >= 3 && (R == 2 || R == 4 || R == 8 || R == 16) && !env_flag("TROPICAL_NO_RUNS_PATH")) {
+            for (int d = nd - 3; d >= 0; --d) {
+                if (p.istride[d] != R) continue;
+                plan->path = GP_RUNS;
+                p.ax_in = d;
+                p.run_shift = R == 2 ? 1 : (R == 4 ? 2 : (R == 8 ? 3 : 4));
+                const int64_t tp = 128 / R;
+                p.tiles_p = (p.shape[d] + tp - 1) / tp;
+                p.tiles_q = (p.shape[nd - 2] + 31) / 32;
+                p.nbatch = total / (p.shape[d] * p.shape[nd - 2] * R);
+                return TROP_OK;
+            }
+        }
         plan->path = GP_COPY;
         return TROP_OK;
     }
@@ -269,6 +287,22 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
                 const int base = ntensors == 2 ? K_GATHER_TILED_V16_N2 : K_GATHER_TILED_V16_N1;
                 kid = (KernelId)(base + (tp == 64 ? 2 : (tp == 32 ? 1 : 0)));
             }
+            const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
+            return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
+        }
+        case GP_RUNS: {
+            const int nd = p.ndim, P = p.ax_in, Q = nd - 2;
+            // 16-byte accesses when every segment starts on a 4-word boundary
+            bool vec = p.istride[Q] % 4 == 0;
+            int64_t ostr = 1;
+            for (int d = nd - 1; d >= 0 && vec; --d) {
+                if (d < Q && d != P) vec = p.istride[d] % 4 == 0 && ostr % 4 == 0;
+                if (d == P) vec = ostr % 4 == 0;
+                ostr *= p.shape[d];
+            }
+            for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
+            const KernelId kid = vec ? (ntensors == 2 ? K_GATHER_RUNS_V_N2 : K_GATHER_RUNS_V_N1)
+                                     : (ntensors == 2 ? K_GATHER_RUNS_S_N2 : K_GATHER_RUNS_S_N1);
             const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
             return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
         }

@@ -63,9 +63,36 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
     return TROP_OK;
 }
 
+// Split-K policy: split only a product with fewer output tiles (times
+// batch) than a 256-CU device has CUs, and only when every range keeps at
+// least kSplitMinK terms; aim at about kSplitTarget (tile, range) units.
+constexpr int64_t kSplitTarget = 512;
+constexpr int64_t kSplitMinK = 512;
+constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
+
+SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
+    SplitK s;
+    if (m <= 0 || n <= 0 || batch <= 0 || k < 2 * kSplitMinK) return s;
+    const int64_t units = ((m + 63) / 64) * ((n + 63) / 64) * batch;
+    if (units * 2 > kSplitTarget) return s;
+    int64_t want = (kSplitTarget + units - 1) / units;
+    if (want > k / kSplitMinK) want = k / kSplitMinK;
+    if (want < 2) return s;
+    int64_t chunk = (k + want - 1) / want;
+    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    const int64_t ks = (k + chunk - 1) / chunk;
+    if (ks < 2) return s;
+    s.ksplit = ks;
+    s.kchunk = chunk;
+    const size_t part = (size_t)(ks * batch * m * n) * 4;
+    s.bytes = 2 * ((part + 255) / 256 * 256);
+    return s;
+}
+
 trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
                      const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
-                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream) {
+                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream, void* workspace,
+                     size_t workspace_bytes) {
     if (m == 0 || n == 0 || batch == 0) return TROP_OK;
     const int ri = ring_index(sr, dt);
     if (k == 0) {
@@ -100,6 +127,9 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.n = n;
     p.k = k;
     p.batch = batch;
+    p.ksplit = 1;
+    p.kchunk = k;
+    p.c_split = 0;
 
     if (env_flag("TROPICAL_FORCE_SIMPLE_GEMM")) {
         return launch(dev, (KernelId)(K_GEMM_SIMPLE_MAXPLUS_F32 + ri), TROP_K_GEMM_SIMPLE,
@@ -134,10 +164,28 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.tiles_m = (int32_t)tm;
     p.tiles_n = (int32_t)tn;
     p.swizzle = env_flag("TROPICAL_NO_XCD_SWIZZLE") ? 0 : 1;
-    int64_t total = tm * tn * batch;
+    // split K into ranges when the workspace allows and the shape asks for it:
+    // partials go to [split][batch][m][n] in the workspace
+    const SplitK sk = workspace ? plan_splitk(m, n, k, batch) : SplitK();
+    const bool split = sk.ksplit > 1 && workspace_bytes >= sk.bytes && !env_flag("TROPICAL_NO_SPLIT_K");
+    const int64_t part_elems = split ? sk.ksplit * batch * m * n : 0;
+    if (split) {
+        p.ksplit = sk.ksplit;
+        p.kchunk = sk.kchunk;
+        p.c_split = batch * m * n;
+        p.C = workspace;
+        p.argmax = argmax ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + sk.bytes / 2) : nullptr;
+        p.sc_row = n;
+        p.sc_col = 1;
+        p.sc_batch = m * n;
+        (void)part_elems;
+    }
+    int64_t total = tm * tn * batch * p.ksplit;
     // without an argmax output the value-only kernel skips the chunk record
     // and the re-scan
-    const KernelId kid = (KernelId)((argmax ? K_GEMM_TILED_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
+    const KernelId kid =
+        split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
+              : (KernelId)((argmax ? K_GEMM_TILED_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
     // keeps every workgroup's tiles on one XCD.
@@ -154,20 +202,39 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     if (block != 256 && block != 512)
         return fail(TROP_ERR_HIP, std::string(kernel_name(kid)) + ": unexpected launch bound " +
                                       std::to_string(block));
-    return launch(dev, kid, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
+    trop_status st = launch(dev, kid, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
+    if (st != TROP_OK || !split) return st;
+    TropSplitMergeParams mp{};
+    mp.pval = p.C;
+    mp.pidx = p.argmax;
+    mp.C = C;
+    mp.argmax = argmax;
+    mp.sc_row = sC.row;
+    mp.sc_col = sC.col;
+    mp.sc_batch = sC.batch;
+    mp.m = m;
+    mp.n = n;
+    mp.batch = batch;
+    mp.ksplit = sk.ksplit;
+    return launch(dev, (KernelId)(K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + ri), TROP_K_GEMM_SPLITK_MERGE,
+                  grid_for(m * n * batch, 256), 256, &mp, stream);
 }
 
 }  // namespace trop
 
-extern "C" trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_dtype dtype,
-                                                     const void* A, trop_strides sA, const void* B,
-                                                     trop_strides sB, void* C, trop_strides sC,
-                                                     int32_t* argmax, int64_t m, int64_t n, int64_t k,
-                                                     int64_t batch, void* stream) {
+namespace {
+
+trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, trop_strides sA, const void* B,
+                       trop_strides sB, void* C, trop_strides sC, int32_t* argmax, int64_t m, int64_t n,
+                       int64_t k, int64_t batch, void* workspace, size_t workspace_bytes, void* stream) {
     using namespace trop;
     trop_status st = check_gemm_args(semiring, dtype, sA, sB, sC, m, n, k, batch);
     if (st != TROP_OK) return st;
     if (m == 0 || n == 0 || batch == 0) return ok();
+    const SplitK sk = plan_splitk(m, n, k, batch);
+    if (workspace && sk.bytes > 0 && workspace_bytes < sk.bytes)
+        return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs " + std::to_string(sk.bytes) + " bytes, got " + std::to_string(workspace_bytes));
     int dev = -1;
     st = current_device(&dev);
     if (st != TROP_OK) return st;
@@ -194,7 +261,41 @@ extern "C" trop_status tropical_gemm_strided_batched(trop_semiring semiring, tro
         st = check_device_span(argmax, dev, spanC, 4, "argmax");
         if (st != TROP_OK) return st;
     }
+    const bool use_ws = workspace && sk.bytes > 0;
+    if (use_ws) {
+        st = check_device_span(workspace, dev, (int64_t)(sk.bytes / 4), 4, "workspace");
+        if (st != TROP_OK) return st;
+    }
     st = run_gemm(dev, semiring, dtype, A, sA, B, sB, C, sC, argmax, m, n, k, batch,
-                  static_cast<hipStream_t>(stream));
+                  static_cast<hipStream_t>(stream), use_ws ? workspace : nullptr, use_ws ? sk.bytes : 0);
     return st == TROP_OK ? ok() : st;
+}
+
+}  // namespace
+
+extern "C" trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_dtype dtype,
+                                                     const void* A, trop_strides sA, const void* B,
+                                                     trop_strides sB, void* C, trop_strides sC,
+                                                     int32_t* argmax, int64_t m, int64_t n, int64_t k,
+                                                     int64_t batch, void* stream) {
+    return gemm_entry(semiring, dtype, A, sA, B, sB, C, sC, argmax, m, n, k, batch, nullptr, 0, stream);
+}
+
+extern "C" trop_status tropical_gemm_strided_batched_ws(trop_semiring semiring, trop_dtype dtype,
+                                                        const void* A, trop_strides sA, const void* B,
+                                                        trop_strides sB, void* C, trop_strides sC,
+                                                        int32_t* argmax, int64_t m, int64_t n, int64_t k,
+                                                        int64_t batch, void* workspace, size_t workspace_bytes,
+                                                        void* stream) {
+    return gemm_entry(semiring, dtype, A, sA, B, sB, C, sC, argmax, m, n, k, batch, workspace, workspace_bytes,
+                      stream);
+}
+
+extern "C" trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t batch,
+                                                    size_t* bytes) {
+    using namespace trop;
+    if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
+    *bytes = plan_splitk(m, n, k, batch).bytes;
+    return ok();
 }

@@ -56,6 +56,25 @@ enum KernelId : int {
     K_GEMM_BACKWARD_LANE_PLUS_VEC,
     K_GEMM_BACKWARD_LANE_MUL,
     K_GEMM_BACKWARD_LANE_MUL_VEC,
+    K_GEMM_SPLITK_MERGE_MAXPLUS_F32,  // merge of split-K partials
+    K_GEMM_SPLITK_MERGE_MINPLUS_F32,
+    K_GEMM_SPLITK_MERGE_MAXMUL_F32,
+    K_GEMM_SPLITK_MERGE_MAXPLUS_I32,
+    K_GEMM_SPLITK_MERGE_MINPLUS_I32,
+    K_GEMM_TILED_SPLIT_MAXPLUS_F32,  // tiled GEMM over (tile, K range) units
+    K_GEMM_TILED_SPLIT_MINPLUS_F32,
+    K_GEMM_TILED_SPLIT_MAXMUL_F32,
+    K_GEMM_TILED_SPLIT_MAXPLUS_I32,
+    K_GEMM_TILED_SPLIT_MINPLUS_I32,
+    K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32,
+    K_GEMM_TILED_VO_SPLIT_MINPLUS_F32,
+    K_GEMM_TILED_VO_SPLIT_MAXMUL_F32,
+    K_GEMM_TILED_VO_SPLIT_MAXPLUS_I32,
+    K_GEMM_TILED_VO_SPLIT_MINPLUS_I32,
+    K_GATHER_RUNS_V_N1,  // runs path: 16-byte / word accesses, 1 or 2 tensors
+    K_GATHER_RUNS_V_N2,
+    K_GATHER_RUNS_S_N1,
+    K_GATHER_RUNS_S_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
@@ -88,7 +107,7 @@ trop_status check_device_span(const void* p, int dev, int64_t span_elems, size_t
 bool max_offset(int n, const int64_t* extent, const int64_t* stride, int64_t* out);
 
 // ---- gather planning (gather.cpp) ----------------------------------------
-enum GatherPath { GP_NONE = 0, GP_COPY, GP_TILED, GP_NAIVE, GP_REDUCE };
+enum GatherPath { GP_NONE = 0, GP_COPY, GP_TILED, GP_NAIVE, GP_REDUCE, GP_RUNS };
 struct GatherPlan {
     TropGatherParams params;
     GatherPath path;
@@ -111,10 +130,20 @@ trop_status plan_diag(int in_ndim, const int64_t* in_shape, const int64_t* in_st
                       GatherPlan* plan);
 
 // ---- GEMM (gemm.cpp) -------------------------------------------------------
+// Number of K splits for a product of this shape (1: no split) and the
+// workspace the split partials need (0 when not split).  Host-only.
+struct SplitK {
+    int64_t ksplit = 1, kchunk = 0;
+    size_t bytes = 0;
+};
+SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch);
 // Enqueue without re-validating pointers (used by the contraction driver).
+// `workspace` (may be NULL) holds plan_splitk(...).bytes when a split is
+// wanted; without it the product is not split.
 trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
                      const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
-                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream);
+                     int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream,
+                     void* workspace = nullptr, size_t workspace_bytes = 0);
 trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, trop_strides sB,
                             trop_strides sC, int64_t m, int64_t n, int64_t k, int64_t batch);
 

@@ -47,6 +47,25 @@ static const char* const kNames[K_COUNT] = {
     "trop_gemm_backward_b4096",      "trop_gemm_backward_lane_plus",
     "trop_gemm_backward_lane_plus_vec", "trop_gemm_backward_lane_mul",
     "trop_gemm_backward_lane_mul_vec",
+    "trop_gemm_splitk_merge_maxplus_f32",
+    "trop_gemm_splitk_merge_minplus_f32",
+    "trop_gemm_splitk_merge_maxmul_f32",
+    "trop_gemm_splitk_merge_maxplus_i32",
+    "trop_gemm_splitk_merge_minplus_i32",
+    "trop_gemm_tiled_split_maxplus_f32",
+    "trop_gemm_tiled_split_minplus_f32",
+    "trop_gemm_tiled_split_maxmul_f32",
+    "trop_gemm_tiled_split_maxplus_i32",
+    "trop_gemm_tiled_split_minplus_i32",
+    "trop_gemm_tiled_vo_split_maxplus_f32",
+    "trop_gemm_tiled_vo_split_minplus_f32",
+    "trop_gemm_tiled_vo_split_maxmul_f32",
+    "trop_gemm_tiled_vo_split_maxplus_i32",
+    "trop_gemm_tiled_vo_split_minplus_i32",
+    "trop_gather_runs_v_n1",
+    "trop_gather_runs_v_n2",
+    "trop_gather_runs_s_n1",
+    "trop_gather_runs_s_n2",
 };
 
 const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
