@@ -20,7 +20,9 @@
  *        min-plus:  a (+) b = min(a, b),  a (x) b = a + b,  zero = +inf
  *        max-mul :  a (+) b = max(a, b),  a (x) b = a * b,  zero = +0
  *    For int32 the zero elements are -2^30 / +2^30 and (x) is a saturating
- *    32-bit add; int32 max-mul is not defined (error ORC_UNSUPPORTED).
+ *    32-bit add.  int32 max-mul, which the pages do not cover, takes the
+ *    same rule for its product: the exact product clamped to the int32
+ *    range; its zero is 0 (a term must exceed 0 to win, as for float32).
  *    The argmax is the index k of the first term that achieves the result:
  *    the scan starts from the zero element, goes over k in ascending order
  *    and replaces the running best only on a strictly better term.  A term
@@ -79,6 +81,7 @@ static float zero_f32(int sr)
 
 static int32_t zero_i32(int sr)
 {
+    if (sr == ORC_MAX_MUL) return 0;
     return sr == ORC_MIN_PLUS ? ORC_I32_INF : -ORC_I32_INF;
 }
 
@@ -88,9 +91,9 @@ static float otimes_f32(int sr, float a, float b)
     return a + b;
 }
 
-static int32_t otimes_i32(int32_t a, int32_t b)
+static int32_t otimes_i32(int sr, int32_t a, int32_t b)
 {
-    int64_t s = (int64_t)a + (int64_t)b;
+    int64_t s = (sr == ORC_MAX_MUL) ? (int64_t)a * (int64_t)b : (int64_t)a + (int64_t)b;
     if (s > INT32_MAX) return INT32_MAX;
     if (s < INT32_MIN) return INT32_MIN;
     return (int32_t)s;
@@ -113,7 +116,6 @@ static int valid_pair(int sr, int dt)
 {
     if (sr < ORC_MAX_PLUS || sr > ORC_MAX_MUL) return ORC_BAD_ARG;
     if (dt != ORC_F32 && dt != ORC_I32) return ORC_BAD_ARG;
-    if (dt == ORC_I32 && sr == ORC_MAX_MUL) return ORC_UNSUPPORTED;
     return ORC_OK;
 }
 
@@ -153,7 +155,7 @@ static void gemm_one(int sr, int dt,
         for (int64_t kk = 0; kk < k; ++kk) {
             int32_t x = a[b * sA[2] + i * sA[0] + kk * sA[1]];
             int32_t y = bm[b * sB[2] + kk * sB[0] + j * sB[1]];
-            int32_t t = otimes_i32(x, y);
+            int32_t t = otimes_i32(sr, x, y);
             if (better_i32(sr, t, best)) {
                 best = t;
                 arg = (int32_t)kk;
@@ -517,7 +519,7 @@ int orc_einsum_brute(int sr, int dt, int nlab, const int64_t* extent,
                     arg = (int32_t)p;
                 }
             } else {
-                int32_t t = otimes_i32(((const int32_t*)A)[ao], ((const int32_t*)B)[bo]);
+                int32_t t = otimes_i32(sr, ((const int32_t*)A)[ao], ((const int32_t*)B)[bo]);
                 if (better_i32(sr, t, besti)) {
                     besti = t;
                     arg = (int32_t)p;

@@ -101,9 +101,13 @@ def torch_tropical(sr, A, B):
     At = torch.from_numpy(np.ascontiguousarray(A))
     Bt = torch.from_numpy(np.ascontiguousarray(B))
     if At.dtype == torch.int32:
-        T = At.to(torch.int64)[:, :, :, None] + Bt.to(torch.int64)[:, None, :, :]
+        if sr == "max_mul":
+            T = At.to(torch.int64)[:, :, :, None] * Bt.to(torch.int64)[:, None, :, :]
+            zero = 0
+        else:
+            T = At.to(torch.int64)[:, :, :, None] + Bt.to(torch.int64)[:, None, :, :]
+            zero = I32_INF if sr == "min_plus" else -I32_INF
         T = T.clamp(-(2 ** 31), 2 ** 31 - 1)
-        zero = I32_INF if sr == "min_plus" else -I32_INF
     else:
         if sr == "max_mul":
             T = At[:, :, :, None] * Bt[:, None, :, :]
@@ -125,7 +129,16 @@ def torch_tropical(sr, A, B):
 def _rand_case(sr, dtype, shape_b_m_k_n, seed):
     b, m, k, n = shape_b_m_k_n
     g = torch.Generator().manual_seed(seed)
-    if dtype == "i32":
+    if dtype == "i32" and sr == "max_mul":
+        # small values, zeros, negatives, and +-50000 so that products of
+        # two large entries leave the int32 range on both sides
+        A = torch.randint(-6, 7, (b, m, k), generator=g, dtype=torch.int32)
+        B = torch.randint(-6, 7, (b, k, n), generator=g, dtype=torch.int32)
+        for X in (A, B):
+            big = torch.rand(X.shape, generator=g) < 0.25
+            sign = torch.where(torch.rand(X.shape, generator=g) < 0.7, 1, -1).to(torch.int32)
+            X[big] = (50000 * sign)[big]
+    elif dtype == "i32":
         A = torch.randint(-6, 7, (b, m, k), generator=g, dtype=torch.int32)
         B = torch.randint(-6, 7, (b, k, n), generator=g, dtype=torch.int32)
         A[torch.rand((b, m, k), generator=g) < 0.2] = I32_INF if sr == "min_plus" else -I32_INF
@@ -145,8 +158,6 @@ def pin_torch_crosscheck(orc):
     shapes = [(2, 5, 7, 3), (1, 1, 1, 1), (3, 4, 9, 6)]
     for sr in SR:
         for dtype in ("f32", "i32"):
-            if sr == "max_mul" and dtype == "i32":
-                continue
             for s, shp in enumerate(shapes):
                 A, B = _rand_case(sr, dtype, shp, 100 + s)
                 C, I = orc.gemm(sr, A, B)
@@ -177,7 +188,10 @@ def pin_torch_random_normal(orc):
 # ----------------------------------------------------------------------
 
 def _unit(sr, n, dtype):
-    if dtype == "i32":
+    if dtype == "i32" and sr == "max_mul":
+        M = np.zeros((n, n), dtype=np.int32)
+        np.fill_diagonal(M, 1)
+    elif dtype == "i32":
         z = I32_INF if sr == "min_plus" else -I32_INF
         M = np.full((n, n), z, dtype=np.int32)
         np.fill_diagonal(M, 0)
@@ -192,9 +206,9 @@ def pin_unit_and_zero(orc):
     rng = np.random.default_rng(3)
     for sr in SR:
         for dtype in ("f32", "i32"):
-            if sr == "max_mul" and dtype == "i32":
-                continue
-            if dtype == "i32":
+            if dtype == "i32" and sr == "max_mul":
+                A = rng.integers(1, 10 ** 6, size=(5, 7)).astype(np.int32)
+            elif dtype == "i32":
                 # the int32 sentinel is absorbing only on its own side of 0:
                 # entries <= 0 for max-plus, >= 0 for min-plus
                 A = rng.integers(1, 51, size=(5, 7)).astype(np.int32)
@@ -215,6 +229,29 @@ def pin_unit_and_zero(orc):
             C, I = orc.gemm(sr, A, Z)
             _bits_equal(C[0], np.full((5, 7), Z[0, 1], dtype=Z.dtype), f"A (x) 0 {sr} {dtype}")
             _eq(I[0], np.zeros((5, 7), dtype=np.int32), f"A (x) 0 argmax {sr} {dtype}")
+
+
+def pin_i32_max_mul_hand_worked(orc):
+    """int32 max-mul: the exact product clamped to the int32 range, zero 0
+    (a term must exceed 0 to win).  Each case worked by hand:
+      terms 50000*50000 = 2.5e9 -> 2147483647, 2*7 = 14, -3*100 = -300:
+          C = 2147483647 at k = 0;
+      terms -50000*50000 -> -2147483648, 3*(-2) = -6, 0*5 = 0: nothing
+          exceeds 0, so C = 0 with argmax 0;
+      terms 65536*32768 = 2^31 -> 2147483647, 65536*32767 = 2147418112:
+          C = 2147483647 at k = 0;
+      terms 3*2 = 2*3 = 6*1 = 6: a tie, the first k wins (k = 0);
+      terms 1*(-5) = -5, 7*3 = 21, (-4)*(-6) = 24: C = 24 at k = 2."""
+    cases = [([50000, 2, -3], [50000, 7, 100], 2147483647, 0),
+             ([-50000, 3, 0], [50000, -2, 5], 0, 0),
+             ([65536, 65536], [32768, 32767], 2147483647, 0),
+             ([3, 2, 6], [2, 3, 1], 6, 0),
+             ([1, 7, -4], [-5, 3, -6], 24, 2)]
+    for a, b, c, k in cases:
+        A = np.array([[a]], dtype=np.int32)
+        B = np.array([b], dtype=np.int32).reshape(1, len(b), 1)
+        C, I = orc.gemm("max_mul", A, B)
+        assert int(C[0, 0, 0]) == c and int(I[0, 0, 0]) == k, f"{a} x {b}: {C.ravel()} {I.ravel()}"
 
 
 def pin_empty_and_k0(orc):
@@ -709,7 +746,7 @@ def pin_tree_winner_backtrack(orc):
 
 
 ALL_PINS = [
-    pin_golden_gemm, pin_golden_special_values, pin_golden_einsum,
+    pin_golden_gemm, pin_golden_special_values, pin_golden_einsum, pin_i32_max_mul_hand_worked,
     pin_torch_crosscheck, pin_torch_random_normal, pin_unit_and_zero,
     pin_empty_and_k0, pin_associativity, pin_transpose_symmetry,
     pin_floyd_warshall, pin_semirings_distinct, pin_points, pin_permute,

@@ -48,6 +48,9 @@ MUTANTS = [
     ("plus_is_minus", "    return a + b;\n}", "    return a - b;\n}"),
     ("max_mul_adds", "if (sr == ORC_MAX_MUL) return a * b;", "if (sr == ORC_MAX_MUL) return a + b;"),
     ("wrapping_i32", "    if (s > INT32_MAX) return INT32_MAX;\n", ""),
+    ("maxmul_i32_adds", "(sr == ORC_MAX_MUL) ? (int64_t)a * (int64_t)b", "(sr == ORC_MAX_MUL) ? (int64_t)a + (int64_t)b"),
+    ("maxmul_i32_zero_negative", "    if (sr == ORC_MAX_MUL) return 0;\n", ""),
+    ("maxmul_i32_wraps_low", "    if (s < INT32_MIN) return INT32_MIN;\n", ""),
     ("max_plus_zero_finite", "if (sr == ORC_MAX_PLUS) return -INFINITY;",
      "if (sr == ORC_MAX_PLUS) return -1e30f;"),
     ("min_plus_zero_i32_off", "return sr == ORC_MIN_PLUS ? ORC_I32_INF : -ORC_I32_INF;",

@@ -12,8 +12,8 @@ def test_pin(orc, pin):
 def test_bad_arguments(orc):
     import numpy as np
     import oracle
-    with pytest.raises(oracle.OracleError):
-        orc.gemm("max_mul", np.zeros((2, 2), np.int32), np.zeros((2, 2), np.int32))
+    with pytest.raises(TypeError):
+        orc.gemm("max_plus", np.zeros((2, 2), np.float64), np.zeros((2, 2), np.float64))
     with pytest.raises(oracle.OracleError):
         orc.permute(np.zeros((2, 3), np.float32), (0, 0))
     with pytest.raises(oracle.OracleError):
