@@ -86,9 +86,12 @@ typedef enum {
  * operations out; the standard tropical algebra is used:
  *   TROP_MAX_PLUS  (+) = max, (x) = +, zero = -inf (int32: -2^30)
  *   TROP_MIN_PLUS  (+) = min, (x) = +, zero = +inf (int32: +2^30)
- *   TROP_MAX_MUL   (+) = max, (x) = *, zero = +0   (float32 only)
+ *   TROP_MAX_MUL   (+) = max, (x) = *, zero = +0   (int32: 0)
  * float32 (x) is one IEEE-754 add / multiply, round to nearest even,
- * denormals kept.  int32 (x) is a saturating 32-bit add.
+ * denormals kept.  int32 (x) is a saturating 32-bit add; for int32 max-mul
+ * it is the exact product clamped to [INT32_MIN, INT32_MAX] (the pages
+ * define no int32 max-mul; this extends the saturating rule).  As for
+ * float32, a max-mul term must exceed the zero element 0 to win.
  */
 typedef enum { TROP_MAX_PLUS = 0, TROP_MIN_PLUS = 1, TROP_MAX_MUL = 2 } trop_semiring;
 typedef enum { TROP_F32 = 0, TROP_I32 = 1 } trop_dtype;
@@ -147,8 +150,7 @@ TROP_API trop_status tropical_init(int device);
  * argmax: device int32 pointer with the strides sC, or NULL (not written).
  * m, n, k, batch >= 0; k < 2^31.  k == 0 writes C = zero, argmax = 0.
  * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, negative size or stride),
- *   TROP_ERR_UNSUPPORTED (int32 max-mul), TROP_ERR_NOT_DEVICE_MEMORY,
- *   TROP_ERR_HIP (launch failure).
+ *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP (launch failure).
  */
 TROP_API trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_dtype dtype,
                                           const void* A, trop_strides sA,
@@ -217,8 +219,9 @@ TROP_API trop_status tropical_gemm_strided_batched_ws(trop_semiring semiring, tr
  *   must not overlap each other or the inputs.
  * m, n, k, batch >= 0.
  * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, negative size or stride,
- *   max-mul without A / B), TROP_ERR_UNSUPPORTED (int32 max-mul),
- *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ *   max-mul without A / B), TROP_ERR_UNSUPPORTED (int32 max-mul: its
+ *   clamped product has no gradient defined here), TROP_ERR_NOT_DEVICE_MEMORY,
+ *   TROP_ERR_HIP.
  */
 TROP_API trop_status tropical_gemm_backward(trop_semiring semiring, trop_dtype dtype,
                                    const void* A, trop_strides sA,
@@ -264,8 +267,7 @@ TROP_API trop_status tropical_permute(size_t elem_bytes, int ndim, const int64_t
  * ignored and the call is a pure 4-byte gather.
  * in_ndim, out_ndim <= 8.
  * Errors: TROP_ERR_INVALID_ARGUMENT (extent mismatch, unknown or repeated
- *   output label), TROP_ERR_UNSUPPORTED (int32 max-mul with a reduction),
- *   TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
+ *   output label), TROP_ERR_NOT_DEVICE_MEMORY, TROP_ERR_HIP.
  */
 TROP_API trop_status tropical_diag_gather(trop_semiring semiring, trop_dtype dtype,
                                  int in_ndim, const int64_t* in_shape,
@@ -365,8 +367,8 @@ typedef struct {
  * tropical_tree_plan_destroy.  A plan is immutable: several threads may run
  * it at once, each with its own workspace.
  * Errors: TROP_ERR_INVALID_ARGUMENT (bad enum, slot, subscript or extent;
- *   a step result that no later step reads), TROP_ERR_UNSUPPORTED (int32
- *   max-mul).  The message names the failing step.
+ *   a step result that no later step reads).  The message names the
+ *   failing step.
  */
 TROP_API trop_status tropical_tree_plan_create(trop_semiring semiring, trop_dtype dtype, int n_inputs,
                                       const char* const* input_subs,

@@ -74,11 +74,10 @@ def test_gemm_argument_errors_before_any_device_call(tb):
     L = tb.lib()
     s = tb.trop_strides(1, 1, 1)
     nul = ctypes.c_void_p(0)
-    # unknown semiring / dtype, int32 max-mul, negative sizes and strides
+    # unknown semiring / dtype, negative sizes and strides
     assert L.tropical_gemm_strided_batched(7, 0, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
     assert "semiring" in tb.tropical_last_error()
     assert L.tropical_gemm_strided_batched(0, 9, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
-    assert L.tropical_gemm_strided_batched(2, 1, nul, s, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.UNSUPPORTED
     assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, -1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
     neg = tb.trop_strides(-1, 1, 1)
     assert L.tropical_gemm_strided_batched(0, 0, nul, neg, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
@@ -124,9 +123,10 @@ def test_diag_argument_errors(tb):
                                   tb._i32([2]), nul, nul, None) == tb.INVALID_ARGUMENT
     assert L.tropical_diag_gather(0, 0, 2, tb._i64([3, 4]), tb._i64([4, 1]), tb._i32([1, 2]), 2,
                                   tb._i32([1, 1]), nul, nul, None) == tb.INVALID_ARGUMENT
-    # int32 max-mul with a reduction
-    assert L.tropical_diag_gather(2, 1, 2, tb._i64([3, 3]), tb._i64([3, 1]), tb._i32([1, 1]), 0,
-                                  tb._i32([]), nul, nul, None) == tb.UNSUPPORTED
+    # the int32 max-mul backward is not defined (checked before any device call)
+    z = tb.trop_strides(0, 0, 0)
+    assert L.tropical_gemm_backward(2, 1, nul, z, nul, z, nul, nul, z, nul, z, nul, z, 1, 1, 1, 1,
+                                    nul) == tb.UNSUPPORTED
 
 
 def test_contract_plan_config5(tb):
@@ -240,7 +240,7 @@ def test_tree_step_info_and_plan_reuse(tb):
 
 
 @pytest.mark.parametrize("case", [
-    "bad_slot", "future_slot", "unused_result", "extent_mismatch", "bad_label", "maxmul_i32", "long_sub",
+    "bad_slot", "future_slot", "unused_result", "extent_mismatch", "bad_label", "bad_semiring", "long_sub",
     "no_steps"])
 def test_tree_plan_errors(tb, case):
     import torch
@@ -257,13 +257,13 @@ def test_tree_plan_errors(tb, case):
         shapes = [(2, 3), (3, 4), (5, 5)]
     elif case == "bad_label":
         steps = [(0, 1, "a1"), (3, 2, "ad")]
-    elif case == "maxmul_i32":
-        sr, dt = "max_mul", torch.int32
+    elif case == "bad_semiring":
+        sr = 7
     elif case == "long_sub":
         subs, shapes = ["abcdefghi", "bc", "cd"], [(1,) * 9, (1, 4), (4, 5)]
     elif case == "no_steps":
         steps = []
-    want = tb.UNSUPPORTED if case == "maxmul_i32" else tb.INVALID_ARGUMENT
+    want = tb.INVALID_ARGUMENT
     with pytest.raises(tb.TropicalError) as e:
         tb.tropical_tree_plan_create(sr, dt, subs, shapes, steps)
     assert e.value.status == want

@@ -61,7 +61,7 @@ def test_int32_and_strided_operands(tb, orc):
     A = torch.randint(0, 100, (9, 9, 40, 3), generator=g, dtype=torch.int32)
     Bbig = torch.randint(0, 100, (70, 50, 3), generator=g, dtype=torch.int32)
     B = Bbig[:, 5:45, :]  # non-contiguous operand
-    for sr in ("min_plus", "max_plus"):
+    for sr in ("min_plus", "max_plus", "max_mul"):
         C, I = tb.tropical_contract_pair("iijb,kjb->bki", sr, A.to(DEV), device_copy(B))
         torch.cuda.synchronize()
         Cr, Ir = orc.contract_pair("iijb,kjb->bki", sr, A.numpy(), B.numpy())

@@ -121,7 +121,7 @@ TRACE_CASES = [("iij", "j", (7, 7, 70)), ("iij", "ji", (7, 7, 9)), ("abj", "ja",
 
 
 @pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
-                                   ("max_plus", "i32"), ("min_plus", "i32")])
+                                   ("max_plus", "i32"), ("min_plus", "i32"), ("max_mul", "i32")])
 @pytest.mark.parametrize("inl,outl,shape", TRACE_CASES)
 def test_trace_reduce(tb, orc, sr, dt, inl, outl, shape):
     g = torch.Generator().manual_seed(len(inl) * 7 + shape[0])

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 I32_INF = 1 << 30
 PAIRS = [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
-         ("max_plus", "i32"), ("min_plus", "i32")]
+         ("max_plus", "i32"), ("min_plus", "i32"), ("max_mul", "i32")]
 
 
 @pytest.fixture(scope="module")
@@ -389,3 +389,19 @@ def test_split_k_workspace_rules(tb, orc):
     assert tb.tropical_get_stats()["launches"]["gemm_splitk_merge"] == before["gemm_splitk_merge"]
     assert_bits_equal(C.cpu().numpy(), Cr, "no workspace")
     assert_equal(I.cpu().numpy(), Ir, "no workspace argmax")
+
+
+def test_int32_max_mul_saturation_and_ties(tb, orc):
+    """int32 max-mul: products beyond the int32 range clamp (many terms
+    then tie at INT32_MAX and the first one wins); negative and zero
+    products never beat the zero element 0."""
+    g = torch.Generator().manual_seed(77)
+    b, m, k, n = 2, 70, 600, 66
+    A = torch.randint(-3, 4, (b, m, k), generator=g, dtype=torch.int32)
+    B = torch.randint(-3, 4, (b, k, n), generator=g, dtype=torch.int32)
+    big = torch.tensor([46341, -46341, 65536, 1 << 30, -(1 << 30)], dtype=torch.int32)
+    for X in (A, B):
+        sel = torch.rand(X.shape, generator=g) < 0.1
+        X[sel] = big[torch.randint(0, 5, (int(sel.sum()),), generator=g)]
+    check(tb, orc, "max_mul", A, B, "int32 max-mul saturation")
+    check(tb, orc, "max_mul", -A.abs(), B.abs(), "int32 max-mul all non-positive")

@@ -17,7 +17,7 @@ from tropical_semiring_tensor_amd import inputs
 pytestmark = pytest.mark.gpu
 
 PAIRS = [("max_plus", torch.float32), ("min_plus", torch.float32), ("max_mul", torch.float32),
-         ("max_plus", torch.int32), ("min_plus", torch.int32)]
+         ("max_plus", torch.int32), ("min_plus", torch.int32), ("max_mul", torch.int32)]
 
 
 @pytest.fixture(scope="module")

@@ -41,6 +41,7 @@ TROP_GEMM_ENTRIES(minplus_f32, TROP_SR_MIN_PLUS, float)
 TROP_GEMM_ENTRIES(maxmul_f32, TROP_SR_MAX_MUL, float)
 TROP_GEMM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS, int32_t)
 TROP_GEMM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS, int32_t)
+TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t)
 
 extern "C" __global__ __launch_bounds__(256) void trop_fill(TropFillParams p) { fill_body(p); }
 

@@ -6,10 +6,12 @@
 // not spell the operations out; the standard tropical algebra is used:
 //   max-plus  (+) max  (x) +   zero -inf (int32 -2^30)
 //   min-plus  (+) min  (x) +   zero +inf (int32 +2^30)
-//   max-mul   (+) max  (x) *   zero +0   (float32 only)
+//   max-mul   (+) max  (x) *   zero +0   (int32: 0)
 // float32 (x) is one IEEE add / multiply (the code is built without fast
 // math, FTZ or FMA contraction); int32 (x) is a saturating add, which gfx950
-// does in one instruction (v_add_i32 with the clamp bit).
+// does in one instruction (v_add_i32 with the clamp bit), or for max-mul the
+// exact product clamped to the int32 range (the pages define no int32
+// max-mul; this extends the saturating rule to the product).
 //
 // add2() is the two-input (+).  add3() folds two terms into a running value
 // with one v_max3 / v_min3; it
@@ -89,6 +91,21 @@ struct Ring<TROP_SR_MIN_PLUS, int32_t> {
     static __device__ __forceinline__ int32_t add2(int32_t x, int32_t y) { return min(x, y); }
     static __device__ __forceinline__ int32_t add3(int32_t r, int32_t x, int32_t y) {
         return min(min(r, x), y);
+    }
+};
+
+template <>
+struct Ring<TROP_SR_MAX_MUL, int32_t> {
+    static __device__ __forceinline__ int32_t zero() { return 0; }
+    static __device__ __forceinline__ int32_t one() { return 1; }
+    static __device__ __forceinline__ int32_t mul(int32_t a, int32_t b) {
+        const int64_t t = (int64_t)a * (int64_t)b;
+        return t > INT32_MAX ? INT32_MAX : (t < INT32_MIN ? INT32_MIN : (int32_t)t);
+    }
+    static __device__ __forceinline__ bool better(int32_t t, int32_t b) { return t > b; }
+    static __device__ __forceinline__ int32_t add2(int32_t x, int32_t y) { return max(x, y); }
+    static __device__ __forceinline__ int32_t add3(int32_t r, int32_t x, int32_t y) {
+        return max(max(r, x), y);
     }
 };
 

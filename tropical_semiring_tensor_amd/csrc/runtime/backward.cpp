@@ -106,7 +106,10 @@ extern "C" trop_status tropical_gemm_backward(trop_semiring semiring, trop_dtype
         return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring " + std::to_string((int)semiring));
     if (dtype != TROP_F32 && dtype != TROP_I32)
         return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype " + std::to_string((int)dtype));
-    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    // the max-mul weight is the other operand as float32; an int32 max-mul
+    // product (saturating) has no gradient defined here
+    if (semiring == TROP_MAX_MUL && dtype == TROP_I32)
+        return fail(TROP_ERR_UNSUPPORTED, "the backward of int32 max-mul is not defined");
     if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
     const bool mul = semiring == TROP_MAX_MUL;
     const bool want_a = grad_a && batch > 0 && m > 0 && k > 0;

@@ -429,7 +429,7 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
                                               size_t workspace_bytes, void* stream) {
     if (semiring < TROP_MAX_PLUS || semiring > TROP_MAX_MUL) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring");
     if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
-    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
     Plan P;
     trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P);
     if (st != TROP_OK) return st;

@@ -310,7 +310,7 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);
         case GP_REDUCE: {
             const int ri = ring_index(sr, dt);
-            if (ri < 0) return fail(TROP_ERR_UNSUPPORTED, "reduction needs a float32 semiring or int32 max/min-plus");
+            if (ri < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
             return launch(dev, (KernelId)(K_GATHER_REDUCE_MAXPLUS_F32 + ri), TROP_K_GATHER_REDUCE,
                           grid_for(p.total, 256), 256, &p, stream);
         }
@@ -401,7 +401,7 @@ extern "C" trop_status tropical_diag_gather(trop_semiring semiring, trop_dtype d
     trop_status st = plan_diag(in_ndim, in_shape, in_strides, in_labels, out_ndim, out_labels, &plan);
     if (st != TROP_OK) return st;
     if (plan.path == GP_REDUCE && ring_index(semiring, dtype) < 0)
-        return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+        return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
     if (plan.path == GP_NONE) return ok();
     int dev = -1;
     st = current_device(&dev);

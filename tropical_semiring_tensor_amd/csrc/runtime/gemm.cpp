@@ -32,7 +32,7 @@ uint32_t grid_for(int64_t work, int64_t per_block) {
 
 uint32_t zero_bits(trop_semiring sr, trop_dtype dt) {
     if (dt == TROP_I32) {
-        const int32_t z = (sr == TROP_MIN_PLUS) ? (1 << 30) : -(1 << 30);
+        const int32_t z = (sr == TROP_MAX_MUL) ? 0 : (sr == TROP_MIN_PLUS) ? (1 << 30) : -(1 << 30);
         uint32_t b;
         std::memcpy(&b, &z, 4);
         return b;
@@ -52,7 +52,7 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
         return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring " + std::to_string((int)sr));
     if (dt != TROP_F32 && dt != TROP_I32)
         return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype " + std::to_string((int)dt));
-    if (ring_index(sr, dt) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    if (ring_index(sr, dt) < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
     if (m < 0 || n < 0 || k < 0 || batch < 0)
         return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
     if (k > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "k must be < 2^31 (int32 argmax)");

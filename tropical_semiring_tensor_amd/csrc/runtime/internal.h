@@ -18,23 +18,19 @@ trop_status hip_fail(hipError_t e, const char* what);
 void count_launch(trop_kernel_family fam);
 
 // ---- kernels and the per-device module cache (module.cpp) ----------------
+// Kernels.  A per-semiring family has one entry point per (semiring, dtype)
+// pair, NRING of them in ring_index order, so that its first id plus
+// ring_index(sr, dt) selects the instance.
+constexpr int NRING = 6;
 enum KernelId : int {
-    K_GEMM_TILED_MAXPLUS_F32 = 0,
-    K_GEMM_TILED_MINPLUS_F32,
-    K_GEMM_TILED_MAXMUL_F32,
-    K_GEMM_TILED_MAXPLUS_I32,
-    K_GEMM_TILED_MINPLUS_I32,
-    K_GEMM_SIMPLE_MAXPLUS_F32,
-    K_GEMM_SIMPLE_MINPLUS_F32,
-    K_GEMM_SIMPLE_MAXMUL_F32,
-    K_GEMM_SIMPLE_MAXPLUS_I32,
-    K_GEMM_SIMPLE_MINPLUS_I32,
-    K_GATHER_REDUCE_MAXPLUS_F32,
-    K_GATHER_REDUCE_MINPLUS_F32,
-    K_GATHER_REDUCE_MAXMUL_F32,
-    K_GATHER_REDUCE_MAXPLUS_I32,
-    K_GATHER_REDUCE_MINPLUS_I32,
-    K_FILL,
+    K_GEMM_TILED_MAXPLUS_F32 = 0,                                          // with argmax
+    K_GEMM_TILED_VO_MAXPLUS_F32 = K_GEMM_TILED_MAXPLUS_F32 + NRING,        // value only
+    K_GEMM_TILED_SPLIT_MAXPLUS_F32 = K_GEMM_TILED_VO_MAXPLUS_F32 + NRING,  // over (tile, K range)
+    K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32 = K_GEMM_TILED_SPLIT_MAXPLUS_F32 + NRING,
+    K_GEMM_SIMPLE_MAXPLUS_F32 = K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32 + NRING,
+    K_GATHER_REDUCE_MAXPLUS_F32 = K_GEMM_SIMPLE_MAXPLUS_F32 + NRING,
+    K_GEMM_SPLITK_MERGE_MAXPLUS_F32 = K_GATHER_REDUCE_MAXPLUS_F32 + NRING,  // merge of split-K partials
+    K_FILL = K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,
@@ -44,11 +40,6 @@ enum KernelId : int {
     K_GATHER_TILED_V16_N2,
     K_GATHER_TILED_V32_N2,
     K_GATHER_TILED_V64_N2,
-    K_GEMM_TILED_VO_MAXPLUS_F32,  // value only (no argmax output)
-    K_GEMM_TILED_VO_MINPLUS_F32,
-    K_GEMM_TILED_VO_MAXMUL_F32,
-    K_GEMM_TILED_VO_MAXPLUS_I32,
-    K_GEMM_TILED_VO_MINPLUS_I32,
     K_GEMM_BACKWARD_B256,  // backward, 256 / 1024 / 4096 bins per LDS chunk
     K_GEMM_BACKWARD_B1024,
     K_GEMM_BACKWARD_B4096,
@@ -56,21 +47,6 @@ enum KernelId : int {
     K_GEMM_BACKWARD_LANE_PLUS_VEC,
     K_GEMM_BACKWARD_LANE_MUL,
     K_GEMM_BACKWARD_LANE_MUL_VEC,
-    K_GEMM_SPLITK_MERGE_MAXPLUS_F32,  // merge of split-K partials
-    K_GEMM_SPLITK_MERGE_MINPLUS_F32,
-    K_GEMM_SPLITK_MERGE_MAXMUL_F32,
-    K_GEMM_SPLITK_MERGE_MAXPLUS_I32,
-    K_GEMM_SPLITK_MERGE_MINPLUS_I32,
-    K_GEMM_TILED_SPLIT_MAXPLUS_F32,  // tiled GEMM over (tile, K range) units
-    K_GEMM_TILED_SPLIT_MINPLUS_F32,
-    K_GEMM_TILED_SPLIT_MAXMUL_F32,
-    K_GEMM_TILED_SPLIT_MAXPLUS_I32,
-    K_GEMM_TILED_SPLIT_MINPLUS_I32,
-    K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32,
-    K_GEMM_TILED_VO_SPLIT_MINPLUS_F32,
-    K_GEMM_TILED_VO_SPLIT_MAXMUL_F32,
-    K_GEMM_TILED_VO_SPLIT_MAXPLUS_I32,
-    K_GEMM_TILED_VO_SPLIT_MINPLUS_I32,
     K_GATHER_RUNS_V_N1,  // runs path: 16-byte / word accesses, 1 or 2 tensors
     K_GATHER_RUNS_V_N2,
     K_GATHER_RUNS_S_N1,
@@ -79,7 +55,7 @@ enum KernelId : int {
 };
 const char* kernel_name(KernelId id);
 
-// Index of (semiring, dtype) among the five supported pairs, or -1.
+// Index of (semiring, dtype) among the NRING supported pairs, or -1.
 int ring_index(trop_semiring sr, trop_dtype dt);
 
 // Current device, with the module loaded on it.  On failure returns an

@@ -27,48 +27,44 @@ namespace trop {
 
 extern std::atomic<uint64_t> g_module_loads;
 
-static const char* const kNames[K_COUNT] = {
-    "trop_gemm_tiled_maxplus_f32",   "trop_gemm_tiled_minplus_f32",
-    "trop_gemm_tiled_maxmul_f32",    "trop_gemm_tiled_maxplus_i32",
-    "trop_gemm_tiled_minplus_i32",   "trop_gemm_simple_maxplus_f32",
-    "trop_gemm_simple_minplus_f32",  "trop_gemm_simple_maxmul_f32",
-    "trop_gemm_simple_maxplus_i32",  "trop_gemm_simple_minplus_i32",
-    "trop_gather_reduce_maxplus_f32", "trop_gather_reduce_minplus_f32",
-    "trop_gather_reduce_maxmul_f32", "trop_gather_reduce_maxplus_i32",
-    "trop_gather_reduce_minplus_i32", "trop_fill",
-    "trop_gather_copy",              "trop_gather_tiled",
-    "trop_gather_naive",             "trop_gather_tiled_v16_n1",
-    "trop_gather_tiled_v32_n1",      "trop_gather_tiled_v64_n1",
-    "trop_gather_tiled_v16_n2",      "trop_gather_tiled_v32_n2",
-    "trop_gather_tiled_v64_n2",      "trop_gemm_tiled_vo_maxplus_f32",
-    "trop_gemm_tiled_vo_minplus_f32", "trop_gemm_tiled_vo_maxmul_f32",
-    "trop_gemm_tiled_vo_maxplus_i32", "trop_gemm_tiled_vo_minplus_i32",
-    "trop_gemm_backward_b256",       "trop_gemm_backward_b1024",
-    "trop_gemm_backward_b4096",      "trop_gemm_backward_lane_plus",
-    "trop_gemm_backward_lane_plus_vec", "trop_gemm_backward_lane_mul",
-    "trop_gemm_backward_lane_mul_vec",
-    "trop_gemm_splitk_merge_maxplus_f32",
-    "trop_gemm_splitk_merge_minplus_f32",
-    "trop_gemm_splitk_merge_maxmul_f32",
-    "trop_gemm_splitk_merge_maxplus_i32",
-    "trop_gemm_splitk_merge_minplus_i32",
-    "trop_gemm_tiled_split_maxplus_f32",
-    "trop_gemm_tiled_split_minplus_f32",
-    "trop_gemm_tiled_split_maxmul_f32",
-    "trop_gemm_tiled_split_maxplus_i32",
-    "trop_gemm_tiled_split_minplus_i32",
-    "trop_gemm_tiled_vo_split_maxplus_f32",
-    "trop_gemm_tiled_vo_split_minplus_f32",
-    "trop_gemm_tiled_vo_split_maxmul_f32",
-    "trop_gemm_tiled_vo_split_maxplus_i32",
-    "trop_gemm_tiled_vo_split_minplus_i32",
-    "trop_gather_runs_v_n1",
-    "trop_gather_runs_v_n2",
-    "trop_gather_runs_s_n1",
-    "trop_gather_runs_s_n2",
-};
+namespace {
 
-const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : "?"; }
+// Entry-point names, built once: per-semiring families are prefix + ring
+// suffix (ring_index order), the rest are listed in KernelId order.
+const std::vector<std::string>& kernel_names() {
+    static const std::vector<std::string> names = [] {
+        static const char* const rings[NRING] = {"maxplus_f32", "minplus_f32", "maxmul_f32",
+                                                 "maxplus_i32", "minplus_i32", "maxmul_i32"};
+        static const char* const families[] = {"trop_gemm_tiled_",       "trop_gemm_tiled_vo_",
+                                               "trop_gemm_tiled_split_", "trop_gemm_tiled_vo_split_",
+                                               "trop_gemm_simple_",      "trop_gather_reduce_",
+                                               "trop_gemm_splitk_merge_"};
+        static const char* const singles[] = {
+            "trop_fill",                     "trop_gather_copy",
+            "trop_gather_tiled",             "trop_gather_naive",
+            "trop_gather_tiled_v16_n1",      "trop_gather_tiled_v32_n1",
+            "trop_gather_tiled_v64_n1",      "trop_gather_tiled_v16_n2",
+            "trop_gather_tiled_v32_n2",      "trop_gather_tiled_v64_n2",
+            "trop_gemm_backward_b256",       "trop_gemm_backward_b1024",
+            "trop_gemm_backward_b4096",      "trop_gemm_backward_lane_plus",
+            "trop_gemm_backward_lane_plus_vec", "trop_gemm_backward_lane_mul",
+            "trop_gemm_backward_lane_mul_vec", "trop_gather_runs_v_n1",
+            "trop_gather_runs_v_n2",         "trop_gather_runs_s_n1",
+            "trop_gather_runs_s_n2"};
+        static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
+        static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
+        std::vector<std::string> v;
+        for (const char* f : families)
+            for (const char* r : rings) v.push_back(std::string(f) + r);
+        for (const char* k : singles) v.push_back(k);
+        return v;
+    }();
+    return names;
+}
+
+}  // namespace
+
+const char* kernel_name(KernelId id) { return (id >= 0 && id < K_COUNT) ? kernel_names()[id].c_str() : "?"; }
 
 int ring_index(trop_semiring sr, trop_dtype dt) {
     if (dt == TROP_F32) {
@@ -78,6 +74,7 @@ int ring_index(trop_semiring sr, trop_dtype dt) {
     } else if (dt == TROP_I32) {
         if (sr == TROP_MAX_PLUS) return 3;
         if (sr == TROP_MIN_PLUS) return 4;
+        if (sr == TROP_MAX_MUL) return 5;
     }
     return -1;
 }
@@ -156,9 +153,9 @@ trop_status ensure_module(int dev) {
         } else {
             g_module_loads.fetch_add(1);
             for (int i = 0; i < K_COUNT && st == TROP_OK; ++i) {
-                e = hipModuleGetFunction(&dm->fn[i], dm->module, kNames[i]);
+                e = hipModuleGetFunction(&dm->fn[i], dm->module, kernel_name((KernelId)i));
                 if (e != hipSuccess) {
-                    st = hip_fail(e, kNames[i]);
+                    st = hip_fail(e, kernel_name((KernelId)i));
                     break;
                 }
                 e = hipFuncGetAttribute(&dm->block[i], HIP_FUNC_ATTRIBUTE_MAX_THREADS_PER_BLOCK, dm->fn[i]);
@@ -208,7 +205,7 @@ trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, 
     if (grid == 0) return TROP_OK;
     void* args[] = {params};
     hipError_t e = hipModuleLaunchKernel(dm->fn[id], grid, 1, 1, block, 1, 1, 0, stream, args, nullptr);
-    if (e != hipSuccess) return hip_fail(e, kNames[id]);
+    if (e != hipSuccess) return hip_fail(e, kernel_name(id));
     count_launch(fam);
     return TROP_OK;
 }

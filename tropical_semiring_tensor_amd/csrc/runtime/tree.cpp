@@ -91,7 +91,7 @@ extern "C" trop_status tropical_tree_plan_create(trop_semiring semiring, trop_dt
     *plan = nullptr;
     if (semiring < TROP_MAX_PLUS || semiring > TROP_MAX_MUL) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring");
     if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
-    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "max-mul is defined for float32 only");
+    if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
     if (n_inputs < 1 || n_steps < 1) return fail(TROP_ERR_INVALID_ARGUMENT, "a tree needs inputs and at least one step");
     if (!input_subs || !input_shapes || !steps) return fail(TROP_ERR_INVALID_ARGUMENT, "NULL input or step array");
 
