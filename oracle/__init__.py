@@ -94,7 +94,7 @@ class Oracle:
                                       vp, _I32P]
         L.orc_permute.argtypes = [i32, i32, _I64P, _I64P, _I32P, vp, vp]
         L.orc_diag_gather.argtypes = [i32, i32, i32, _I64P, _I64P, _I32P, i32, _I32P,
-                                      vp, vp]
+                                      vp, vp, _I32P]
         L.orc_einsum_brute.argtypes = [i32, i32, i32, _I64P,
                                        i32, _I32P, _I64P, vp,
                                        i32, _I32P, _I64P, vp,
@@ -230,10 +230,13 @@ class Oracle:
         return out
 
     # -- diagonal / trace ----------------------------------------------------
-    def diag_gather(self, sr, x, in_labels, out_labels):
+    def diag_gather(self, sr, x, in_labels, out_labels, argmax=False):
         """Repeated-label diagonal with (+)-reduction of labels absent from out.
 
-        Labels are strings of single characters (or int sequences).
+        Labels are strings of single characters (or int sequences).  With
+        argmax, also returns the reduction's winner per output: the
+        row-major position over the reduced labels (in order of first
+        appearance) of the first strictly better value, 0 if none.
         """
         x = np.asarray(x)
         ids = {}
@@ -251,11 +254,13 @@ class Oracle:
                 raise OracleError("orc_diag_gather: invalid argument")
             ol.append(ids[c])
         out = np.empty([ext[c] for c in out_labels], dtype=x.dtype)
+        arg = np.empty(out.shape, dtype=np.int32) if argmax else None
         st = self.lib.orc_diag_gather(_sr_code(sr), _dt_code(x), x.ndim, _i64(list(x.shape)),
                                       _i64(_elem_strides(x)), _i32(il), len(ol), _i32(ol),
-                                      _ptr(x), _ptr(out))
+                                      _ptr(x), _ptr(out),
+                                      arg.ctypes.data_as(_I32P) if argmax else None)
         self._check(st, "orc_diag_gather")
-        return out
+        return (out, arg) if argmax else out
 
     # -- brute-force einsum -------------------------------------------------
     def einsum_brute(self, sr, spec, A, B, sum_order=None, argmax=True):

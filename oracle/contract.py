@@ -17,6 +17,14 @@ Canonical orders (row-major):
 batch / left / right labels are taken in output order, contracted labels in
 the order they first appear in A's subscript.  The argmax is therefore the
 row-major linear index over the contracted labels in A-subscript order.
+
+When a pre-pass reduces labels found in one operand only, its winners are
+kept and the argmax covers them too: the row-major linear index over the
+contracted labels (A order), then A's reduced labels (A order), then B's
+(B order) -- the product's winning k, then the pre-pass winner of A at
+that k, then B's.  The contracted labels lead because the product's k is
+chosen first; the pre-pass winners are the ones that produced the values
+the product compared.
 """
 import numpy as np
 
@@ -60,11 +68,15 @@ def roles(la, lb, out):
     return batch, left, right, contracted, a_reduce, b_reduce
 
 
-def _prepare(orc, sr, x, sub, reduce_labels, canonical):
-    """Unary pre-pass (diagonal / trace), then permute to `canonical`."""
+def _prepare(orc, sr, x, sub, reduce_labels, canonical, winners=False):
+    """Unary pre-pass (diagonal / trace), then permute to `canonical`; with
+    `winners`, also the pre-pass reduction's winner index, permuted alike."""
     kept = [c for c in _unique(sub) if c not in reduce_labels]
-    y = orc.diag_gather(sr, x, sub, "".join(kept))
     perm = [kept.index(c) for c in canonical]
+    if winners:
+        y, w = orc.diag_gather(sr, x, sub, "".join(kept), argmax=True)
+        return orc.permute(y, perm), orc.permute(w, perm)
+    y = orc.diag_gather(sr, x, sub, "".join(kept))
     return orc.permute(y, perm)
 
 
@@ -81,11 +93,7 @@ def contract_pair(orc, spec, sr, A, B, argmax=True):
                 raise OracleError(f"extent mismatch for label {c!r}")
             ext[c] = e
     batch, left, right, contracted, a_red, b_red = roles(la, lb, out)
-    if argmax and (a_red or b_red):
-        raise OracleError("argmax through a pre-pass reduction is unsupported")
-
-    A2 = _prepare(orc, sr, A, la, a_red, batch + left + contracted)
-    B2 = _prepare(orc, sr, B, lb, b_red, batch + contracted + right)
+    route = argmax and bool(a_red or b_red)
 
     def prod(labels):
         p = 1
@@ -94,7 +102,23 @@ def contract_pair(orc, spec, sr, A, B, argmax=True):
         return p
 
     nb, m, n, k = prod(batch), prod(left), prod(right), prod(contracted)
+    if route:
+        A2, WA = _prepare(orc, sr, A, la, a_red, batch + left + contracted, winners=True)
+        B2, WB = _prepare(orc, sr, B, lb, b_red, batch + contracted + right, winners=True)
+    else:
+        A2 = _prepare(orc, sr, A, la, a_red, batch + left + contracted)
+        B2 = _prepare(orc, sr, B, lb, b_red, batch + contracted + right)
     C2, I2 = orc.gemm(sr, A2.reshape(nb, m, k), B2.reshape(nb, k, n), argmax=argmax)
+    if route:
+        # the product's k, then the pre-pass winners at that k
+        ra, rb = prod(a_red), prod(b_red)
+        bi, ii, jj = np.meshgrid(np.arange(nb), np.arange(m), np.arange(n), indexing="ij")
+        wa = WA.reshape(nb, m, k)[bi, ii, I2].astype(np.int64)
+        wb = WB.reshape(nb, k, n)[bi, I2, jj].astype(np.int64)
+        full = I2.astype(np.int64) * (ra * rb) + wa * rb + wb
+        if full.size and full.max() >= 2 ** 31:
+            raise OracleError("argmax index does not fit int32")
+        I2 = full.astype(np.int32)
 
     canon = batch + left + right
     shape = [ext[c] for c in canon]

@@ -353,7 +353,7 @@ int orc_permute(int elem_bytes, int ndim, const int64_t* shape,
 int orc_diag_gather(int sr, int dt, int in_ndim, const int64_t* in_shape,
                     const int64_t* in_strides, const int32_t* in_labels,
                     int out_ndim, const int32_t* out_labels,
-                    const void* in, void* out)
+                    const void* in, void* out, int32_t* arg_out)
 {
     if (in_ndim < 0 || in_ndim > ORC_MAX_RANK) return ORC_BAD_ARG;
     if (out_ndim < 0 || out_ndim > ORC_MAX_RANK) return ORC_BAD_ARG;
@@ -417,8 +417,13 @@ int orc_diag_gather(int sr, int dt, int in_ndim, const int64_t* in_shape,
         }
         if (nred == 0) {
             memcpy((char*)out + 4 * o, (const char*)in + 4 * base, 4);
+            if (arg_out) arg_out[o] = 0;
             continue;
         }
+        /* the winner: the position q (row-major over the reduced labels in
+           order of first appearance) of the first strictly better value;
+           0 when nothing beats the zero element */
+        int32_t win = 0;
         if (dt == ORC_F32) {
             float best = zero_f32(sr);
             for (int64_t q = 0; q < rtotal; ++q) {
@@ -429,7 +434,10 @@ int orc_diag_gather(int sr, int dt, int in_ndim, const int64_t* in_shape,
                     rr /= e;
                 }
                 float t = ((const float*)in)[off];
-                if (better_f32(sr, t, best)) best = t;
+                if (better_f32(sr, t, best)) {
+                    best = t;
+                    win = (int32_t)q;
+                }
             }
             ((float*)out)[o] = best;
         } else {
@@ -442,10 +450,14 @@ int orc_diag_gather(int sr, int dt, int in_ndim, const int64_t* in_shape,
                     rr /= e;
                 }
                 int32_t t = ((const int32_t*)in)[off];
-                if (better_i32(sr, t, best)) best = t;
+                if (better_i32(sr, t, best)) {
+                    best = t;
+                    win = (int32_t)q;
+                }
             }
             ((int32_t*)out)[o] = best;
         }
+        if (arg_out) arg_out[o] = win;
     }
     return ORC_OK;
 }

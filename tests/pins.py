@@ -406,6 +406,31 @@ def pin_permute(orc):
                     f"strided permute {dt}")
 
 
+def pin_reduce_winner_vs_torch(orc):
+    """The winner of a (+)-reduction against torch's max / min with
+    indices, which return the first extreme position (torch documents the
+    first index on ties); a value not strictly better than the zero element
+    gives the zero element and index 0."""
+    g = torch.Generator().manual_seed(29)
+    x = torch.randint(-3, 4, (4, 5, 6), generator=g).float()
+    for sr in ("max_plus", "min_plus", "max_mul"):
+        xs = x.abs() * 0.5 if sr == "max_mul" else x
+        out, arg = orc.diag_gather(sr, xs.numpy(), "abc", "b", argmax=True)
+        flat = xs.permute(1, 0, 2).reshape(5, 24)
+        v, i = flat.min(dim=1) if sr == "min_plus" else flat.max(dim=1)
+        if sr == "max_mul":
+            i = torch.where(v > 0, i, torch.zeros_like(i))
+        _bits_equal(out, v.numpy(), f"reduce value {sr}")
+        _eq(arg, i.to(torch.int32).numpy(), f"reduce winner {sr}")
+    # a repeated label (diagonal) and a reduced one together
+    y = torch.randint(-9, 10, (5, 5, 7), generator=g, dtype=torch.int32)
+    out, arg = orc.diag_gather("max_plus", y.numpy(), "iij", "i", argmax=True)
+    d = torch.diagonal(y, dim1=0, dim2=1).T  # (i, j)
+    v, i = d.max(dim=1)
+    _eq(out, v.numpy(), "diag + reduce value")
+    _eq(arg, i.to(torch.int32).numpy(), "diag + reduce winner")
+
+
 def pin_diag(orc):
     g = torch.Generator().manual_seed(37)
     A = torch.randn(4, 4, 3, 2, generator=g)
@@ -480,14 +505,23 @@ def pin_contract_vs_brute(orc):
             Cb, Ib = orc.einsum_brute(sr, spec, A2, B2, sum_order=contracted)
             _bits_equal(C, Cb, f"contract {spec} {sr}")
             _eq(I, Ib, f"contract {spec} {sr} argmax")
-    # a label in one operand only is reduced in the pre-pass (values only)
+    # a label in one operand only is reduced in the pre-pass; its winner is
+    # routed too: the argmax enumerates the contracted labels (A order),
+    # then A's reduced labels, then B's -- on exact data the first
+    # maximiser of that enumeration
     A = rng.integers(-3, 4, size=(3, 3, 4)).astype(np.float32)
     B = rng.integers(-3, 4, size=(4, 2, 5)).astype(np.float32)
-    for spec in ("iij,jkl->k", "aij,jkl->ik"):
+    for spec, order in (("iij,jkl->k", "jil"), ("aij,jkl->ik", "jal"), ("abj,jcd->bc", "jadz")):
         for sr in ("max_plus", "min_plus"):
-            C, _ = orc.contract_pair(spec, sr, A, B, argmax=False)
-            Cb, _ = orc.einsum_brute(sr, spec, A, B, argmax=False)
+            A2 = A if spec != "abj,jcd->bc" else rng.integers(-3, 4, size=(2, 3, 4)).astype(np.float32)
+            B2 = B if spec != "abj,jcd->bc" else rng.integers(-3, 4, size=(4, 2, 3)).astype(np.float32)
+            order2 = [c for c in order if c in spec]
+            C, I = orc.contract_pair(spec, sr, A2, B2)
+            Cb, Ib = orc.einsum_brute(sr, spec, A2, B2, sum_order=order2)
             _bits_equal(C, Cb, f"contract-with-reduce {spec} {sr}")
+            _eq(I, Ib, f"contract-with-reduce {spec} {sr} argmax")
+            C0, _ = orc.contract_pair(spec, sr, A2, B2, argmax=False)
+            _bits_equal(C0, Cb, f"contract-with-reduce {spec} {sr} values only")
 
 
 # ----------------------------------------------------------------------
@@ -750,7 +784,7 @@ ALL_PINS = [
     pin_torch_crosscheck, pin_torch_random_normal, pin_unit_and_zero,
     pin_empty_and_k0, pin_associativity, pin_transpose_symmetry,
     pin_floyd_warshall, pin_semirings_distinct, pin_points, pin_permute,
-    pin_diag, pin_brute_vs_torch, pin_contract_vs_brute,
+    pin_diag, pin_reduce_winner_vs_torch, pin_brute_vs_torch, pin_contract_vs_brute,
     pin_golden_backward, pin_backward_torch_autograd, pin_backward_adjoint_identity,
     pin_backward_finite_difference, pin_tree_vs_brute, pin_tree_winner_backtrack,
 ]

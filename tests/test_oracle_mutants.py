@@ -63,9 +63,12 @@ MUTANTS = [
      "        for (int d = ndim - 1; d >= 0; --d) {\n            int64_t digit = rem % out_shape[d];",
      "        for (int d = 0; d < ndim; ++d) {\n            int64_t digit = rem % out_shape[d];"),
     ("diag_stride_not_summed", "str[found] += in_strides[a];", "str[found] = in_strides[a];"),
-    ("trace_last_wins", "if (better_f32(sr, t, best)) best = t;", "best = t;"),
+    ("trace_last_wins", "                if (better_f32(sr, t, best)) {\n                    best = t;\n                    win",
+     "                if (1) {\n                    best = t;\n                    win"),
     ("brute_argmax_shifted", "bestf = t;\n                    arg = (int32_t)p;",
      "bestf = t;\n                    arg = (int32_t)(p > 0 ? p - 1 : 0);"),
+    ("reduce_winner_not_kept_f32", "best = t;\n                    win = (int32_t)q;", "best = t;"),
+    ("reduce_winner_off_by_one", "win = (int32_t)q;", "win = (int32_t)q + 1;"),
     ("points_swap_ij",
      "pts[3 * p], pts[3 * p + 1], pts[3 * p + 2]", "pts[3 * p], pts[3 * p + 2], pts[3 * p + 1]"),
     # backward (winner routing)
@@ -114,6 +117,11 @@ PY_MUTANTS = [
     ("pair_output_not_permuted", "C = orc.permute(C2.reshape(shape), perm)", "C = C2.reshape(shape)"),
     ("pair_argmax_permuted_differently", "I = orc.permute(I2.reshape(shape), perm) if argmax else None",
      "I = orc.permute(I2.reshape(shape), perm[::-1]) if argmax else None"),
+    ("route_drops_b_winner", "full = I2.astype(np.int64) * (ra * rb) + wa * rb + wb",
+     "full = I2.astype(np.int64) * (ra * rb) + wa * rb"),
+    ("route_b_before_a", "full = I2.astype(np.int64) * (ra * rb) + wa * rb + wb",
+     "full = I2.astype(np.int64) * (ra * rb) + wb * ra + wa"),
+    ("route_winners_at_k0", "wa = WA.reshape(nb, m, k)[bi, ii, I2]", "wa = WA.reshape(nb, m, k)[bi, ii, 0 * I2]"),
     ("tree_rhs_is_lhs", "lb, B = slots[rhs]", "lb, B = slots[lhs]"),
     ("tree_returns_first_step", "return slots[-1][1], winners", "return slots[len(subs)][1], winners"),
     ("tree_result_keeps_lhs_subscript", "slots.append((out, C))", "slots.append((la, C))"),

@@ -19,5 +19,5 @@ def test_bad_arguments(orc):
     with pytest.raises(oracle.OracleError):
         orc.diag_gather("max_plus", np.zeros((2, 3), np.float32), "ii", "i")
     with pytest.raises(oracle.OracleError):
-        orc.contract_pair("iij,jk->k", "max_plus", np.zeros((2, 2, 3), np.float32),
-                          np.zeros((3, 4), np.float32), argmax=True)
+        orc.contract_pair("ij,jk,kl->il", "max_plus", np.zeros((2, 3), np.float32),
+                          np.zeros((3, 4), np.float32))
