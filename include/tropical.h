@@ -112,7 +112,8 @@ typedef enum {
     TROP_K_GATHER_REDUCE = 6,/* gather with a (+)-reduction (trace)      */
     TROP_K_GEMM_BACKWARD = 7,/* gradient routed along the argmax         */
     TROP_K_GEMM_SPLITK_MERGE = 8, /* merge of split-K partials           */
-    TROP_K_FAMILIES = 9
+    TROP_K_ARGMAX_COMPOSE = 9,    /* argmax through pre-pass reductions  */
+    TROP_K_FAMILIES = 10
 } trop_kernel_family;
 
 typedef struct {
@@ -305,8 +306,11 @@ TROP_API trop_status tropical_contract_pair_workspace_size(const char* spec, con
  *   length, <= 8).  C: contiguous row-major over the output labels.
  * argmax: NULL or a contiguous int32 tensor shaped like C; it holds the
  *   row-major linear index over the contracted labels taken in A-subscript
- *   order.  Requesting it when a pre-pass reduction exists is
- *   TROP_ERR_UNSUPPORTED.
+ *   order.  When a pre-pass reduces labels of A or B, the index continues
+ *   over A's reduced labels (A order), then B's (B order): the product's
+ *   winning k, then the winners (first strictly better position) of the
+ *   reductions that produced the two values it compared.  The whole index
+ *   must fit int32 (else TROP_ERR_INVALID_ARGUMENT when requested).
  * workspace: device memory of at least tropical_contract_pair_workspace_size
  *   bytes (may be NULL when that size is 0), used only by work on `stream`.
  * Errors: TROP_ERR_INVALID_ARGUMENT, TROP_ERR_UNSUPPORTED,
@@ -405,8 +409,7 @@ TROP_API trop_status tropical_tree_step_info(trop_tree_plan plan, int step, char
  *     memory, not touched by other work until this run has finished on
  *     `stream` (a later run of any plan on the same stream may reuse it).
  * All argument checks precede the first launch; on error nothing is
- * enqueued.  Errors: as tropical_contract_pair (UNSUPPORTED for an argmax
- *   requested on a step with a pre-pass reduction).
+ * enqueued.  Errors: as tropical_contract_pair.
  */
 TROP_API trop_status tropical_tree_run(trop_tree_plan plan, const void* const* inputs, void* out,
                               int32_t* const* step_argmax, void* workspace, size_t workspace_bytes,

@@ -80,6 +80,13 @@ def _prepare(orc, sr, x, sub, reduce_labels, canonical, winners=False):
     return orc.permute(y, perm)
 
 
+def prod_of(labels, ext):
+    p = 1
+    for c in labels:
+        p *= ext[c]
+    return p
+
+
 def contract_pair(orc, spec, sr, A, B, argmax=True):
     A = np.asarray(A)
     B = np.asarray(B)
@@ -93,7 +100,8 @@ def contract_pair(orc, spec, sr, A, B, argmax=True):
                 raise OracleError(f"extent mismatch for label {c!r}")
             ext[c] = e
     batch, left, right, contracted, a_red, b_red = roles(la, lb, out)
-    route = argmax and bool(a_red or b_red)
+    # (with K = 0 nothing wins anywhere: every index, routed or not, is 0)
+    route = argmax and bool(a_red or b_red) and prod_of(contracted, ext) > 0
 
     def prod(labels):
         p = 1

@@ -91,9 +91,59 @@ def test_pre_pass_reduction_values(tb, orc):
             assert I is None
             Cr, _ = orc.contract_pair(spec, sr, A.numpy(), B.numpy(), argmax=False)
             assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr}")
-    with pytest.raises(tb.TropicalError) as e:
-        tb.tropical_contract_pair("iij,jkl->k", "max_plus", A.to(DEV), B.to(DEV), argmax=True)
-    assert e.value.status == tb.UNSUPPORTED
+
+
+# specs with labels reduced in the pre-pass: on A, on B, on both, with a
+# batch label, a repeated label, and in the B (x) A orientation
+ROUTE_SPECS = [
+    ("iij,jkl->k", (6, 6, 40), (40, 7, 9)),
+    ("aij,jkl->ik", (5, 6, 40), (40, 7, 9)),
+    ("abj,jcd->bc", (4, 30, 50), (50, 20, 3)),
+    ("zaij,zjk->zki", (3, 4, 20, 33), (3, 33, 25)),
+    ("ij,jkl->ki", (70, 65), (65, 3, 66)),
+    ("xabj,jbcy->bca", (2, 5, 17, 40), (40, 17, 6, 3)),
+]
+
+
+@pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
+                                   ("max_plus", "i32"), ("min_plus", "i32"), ("max_mul", "i32")])
+@pytest.mark.parametrize("spec,sa,sb", ROUTE_SPECS, ids=[r[0] for r in ROUTE_SPECS])
+def test_argmax_routed_through_pre_pass_reductions(tb, orc, sr, dt, spec, sa, sb):
+    """The argmax continues over the reduced labels: the product's k, then
+    the reductions' winners at that k.  Small integers make ties common."""
+    g = torch.Generator().manual_seed(len(spec) * 13 + sa[0])
+    if dt == "i32":
+        A = torch.randint(-9, 10, sa, generator=g, dtype=torch.int32)
+        B = torch.randint(-9, 10, sb, generator=g, dtype=torch.int32)
+    elif sr == "max_mul":
+        A = torch.randint(0, 5, sa, generator=g).float() * 0.5
+        B = torch.randint(0, 5, sb, generator=g).float() * 0.25
+    else:
+        A = torch.randint(-4, 5, sa, generator=g).float()
+        B = torch.randint(-4, 5, sb, generator=g).float()
+    C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr} {dt}")
+    assert_equal(I.cpu().numpy(), Ir, f"{spec} {sr} {dt} argmax")
+
+
+def test_routed_argmax_index_range_and_k0(tb, orc):
+    # a zero-extent contracted label: nothing wins, every index is 0
+    A = torch.zeros(5, 0, 3)
+    B = torch.zeros(0, 4)
+    C, I = tb.tropical_contract_pair("ijr,jk->ik", "max_plus", A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair("ijr,jk->ik", "max_plus", A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, "K = 0 with a reduction")
+    assert (I == 0).all()
+    # contracted x reduced extents beyond int32: only values can be asked
+    # for (the check is on sizes, before any pointer is looked at)
+    import ctypes
+    z = ctypes.c_void_p(0)
+    st = tb.lib().tropical_contract_pair(b"ijr,jk->ik", 0, 0, z, tb._i64([1, 1 << 16, 1 << 16]), None, z,
+                                         tb._i64([1 << 16, 1]), None, z, ctypes.c_void_p(16), z, 0, None)
+    assert st == tb.INVALID_ARGUMENT and "int32" in tb.tropical_last_error()
 
 
 def test_golden_einsum(tb):

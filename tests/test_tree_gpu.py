@@ -96,15 +96,13 @@ def test_tree_strided_inputs_and_partial_argmax(tb, orc):
 
 def test_tree_reduction_label(tb, orc):
     # f is in one tensor only and not in the result: reduced in its step's
-    # pre-pass, where no argmax is defined
+    # pre-pass
     subs, steps = ["ab", "bcf", "cd"], [(0, 1, "ac"), (3, 2, "ad")]
     g = torch.Generator().manual_seed(14)
     xs = [torch.randn(s, generator=g) for s in ((30, 40), (40, 50, 6), (50, 20))]
     run_both(tb, orc, "min_plus", torch.float32, subs, xs, steps, argmax=[False, True], what="reduced label")
-    plan = tb.tropical_tree_plan_create("min_plus", torch.float32, subs, [x.shape for x in xs], steps)
-    with pytest.raises(tb.TropicalError) as e:
-        tb.tropical_tree_run(plan, [x.to(DEV) for x in xs], argmax=True)
-    assert e.value.status == tb.UNSUPPORTED
+    # its argmax continues over the reduced label (routed through the pre-pass)
+    run_both(tb, orc, "min_plus", torch.float32, subs, xs, steps, argmax=True, what="routed reduced label")
 
 
 def test_tree_workspace_reuse_across_runs_and_streams(tb, orc):

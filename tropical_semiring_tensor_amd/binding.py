@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "TROP_OK", 1: "TROP_ERR_INVALID_ARGUMENT", 2: "TROP_ERR_UNSUP
 SEMIRINGS = {"max_plus": 0, "min_plus": 1, "max_mul": 2}
 F32, I32 = 0, 1
 KERNEL_FAMILIES = ["gemm_tiled", "gemm_simple", "fill", "gather_copy", "gather_tiled",
-                   "gather_naive", "gather_reduce", "gemm_backward", "gemm_splitk_merge"]
+                   "gather_naive", "gather_reduce", "gemm_backward", "gemm_splitk_merge",
+                   "argmax_compose"]
 MAX_DIMS = 8
 
 
@@ -48,7 +49,7 @@ class trop_tree_step(ctypes.Structure):
 
 class trop_stats(ctypes.Structure):
     _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
-                ("launches", ctypes.c_uint64 * 9), ("host_syncs", ctypes.c_uint64),
+                ("launches", ctypes.c_uint64 * 10), ("host_syncs", ctypes.c_uint64),
                 ("memcpy_calls", ctypes.c_uint64)]
 
 

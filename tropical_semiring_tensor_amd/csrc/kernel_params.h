@@ -87,6 +87,22 @@ struct TropGatherParams {
     int64_t rtotal;
 };
 
+// Argmax through pre-pass reductions: I[o] (the product's k, in the GEMM's
+// canonical (batch, row, col) layout) becomes
+//     k * ra_n * rb_n + wa[k] * rb_n + wb[k]
+// where wa / wb are the pre-pass winners of A and B (null: no reduction on
+// that side), addressed at (batch, row, col, k) through the strides below
+// (a stride of 0 for the GEMM axis the operand does not carry).
+struct TropComposeParams {
+    int32_t* idx;
+    const int32_t* wa;
+    const int32_t* wb;
+    int64_t wa_b, wa_r, wa_c, wa_k;
+    int64_t wb_b, wb_r, wb_c, wb_k;
+    int64_t ra_n, rb_n;
+    int64_t rows, cols, batch;
+};
+
 // Backward (winner routing): one segmented histogram, either the rows of
 // grad_a (segments i, items j, bins k) or the columns of grad_b (segments
 // j, items i, bins k).  The max-mul weight of item t with key k sits at

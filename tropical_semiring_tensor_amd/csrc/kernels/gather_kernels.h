@@ -406,6 +406,10 @@ __device__ __forceinline__ void gather_reduce_body(const TropGatherParams& p) {
     using R = Ring<SR, T>;
     const T* in = static_cast<const T*>(p.in[0]);
     T* out = static_cast<T*>(p.out[0]);
+    // with ntensors = 2, out[1] receives each output's winner: the position
+    // (row-major over the reduced axes) of the first strictly better value,
+    // 0 when nothing beats the zero element
+    int32_t* win_out = p.ntensors == 2 ? static_cast<int32_t*>(p.out[1]) : nullptr;
     for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < p.total;
          o += (int64_t)gridDim.x * blockDim.x) {
         int64_t rem = o, base = 0;
@@ -415,6 +419,7 @@ __device__ __forceinline__ void gather_reduce_body(const TropGatherParams& p) {
             rem /= e;
         }
         T best = R::zero();
+        int64_t win = 0;
         for (int64_t r = 0; r < p.rtotal; ++r) {
             int64_t rr = r, off = base;
             for (int d = p.nred - 1; d >= 0; --d) {
@@ -423,9 +428,29 @@ __device__ __forceinline__ void gather_reduce_body(const TropGatherParams& p) {
                 rr /= e;
             }
             const T v = in[off];
-            if (R::better(v, best)) best = v;
+            if (R::better(v, best)) {
+                best = v;
+                win = r;
+            }
         }
         out[o] = best;
+        if (win_out) win_out[o] = (int32_t)win;
+    }
+}
+
+// Argmax through pre-pass reductions: one thread per output of the GEMM's
+// canonical result, in place (TropComposeParams).
+__device__ __forceinline__ void argmax_compose_body(const TropComposeParams& p) {
+    const int64_t rc = p.rows * p.cols;
+    const int64_t total = rc * p.batch;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = o / rc, t = o % rc, r = t / p.cols, c = t % p.cols;
+        const int64_t k = p.idx[o];
+        int64_t v = k * p.ra_n * p.rb_n;
+        if (p.wa) v += (int64_t)p.wa[b * p.wa_b + r * p.wa_r + c * p.wa_c + k * p.wa_k] * p.rb_n;
+        if (p.wb) v += p.wb[b * p.wb_b + r * p.wb_r + c * p.wb_c + k * p.wb_k];
+        p.idx[o] = (int32_t)v;
     }
 }
 

@@ -45,6 +45,10 @@ TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t)
 
 extern "C" __global__ __launch_bounds__(256) void trop_fill(TropFillParams p) { fill_body(p); }
 
+extern "C" __global__ __launch_bounds__(256) void trop_argmax_compose(TropComposeParams p) {
+    argmax_compose_body(p);
+}
+
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_copy(TropGatherParams p) {
     gather_copy_body(p);
 }

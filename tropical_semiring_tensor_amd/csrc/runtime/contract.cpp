@@ -15,6 +15,7 @@
 // allows" is followed for operands: an operand whose batch, row and column
 // label groups each collapse to one stride, with a unit row or column
 // stride, is read in place instead of being gathered.
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -302,6 +303,24 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
         P.off_i = off;
         off += align_up((size_t)(P.nb * P.M * P.N) * 4);
     }
+    // winners of the pre-pass reductions (for an argmax routed through them)
+    P.red_l = !l_red.empty();
+    P.red_r = !r_red.empty();
+    for (char c : P.a_red) P.ra_n *= P.ext[(int)c];
+    for (char c : P.b_red) P.rb_n *= P.ext[(int)c];
+    {
+        int64_t t = 0;
+        P.route_fits = !__builtin_mul_overflow(P.K, P.ra_n, &t) && !__builtin_mul_overflow(t, P.rb_n, &t) &&
+                       t <= (int64_t)INT32_MAX + 1;
+    }
+    if (P.red_l) {
+        P.off_wl = off;
+        off += align_up((size_t)(P.nb * P.gm * P.K) * 4);
+    }
+    if (P.red_r) {
+        P.off_wr = off;
+        off += align_up((size_t)(P.nb * P.K * P.gn) * 4);
+    }
     const SplitK sk = plan_splitk(P.gm, P.gn, P.K, P.nb);
     if (sk.bytes > 0) {
         P.off_split = off;
@@ -341,21 +360,23 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
     const void* r_ptr = P.swap ? Aptr : Bptr;
     const void* a_use = l_ptr;
     const void* b_use = r_ptr;
+    // an argmax routed through a pre-pass reduction keeps its winners
+    const bool route = argmax && (P.red_l || P.red_r) && P.K > 0;
     if (!P.a_fold) {
         GatherPlan g = P.ga;
         void* dst = ws + P.off_a;
-        const void* in[1] = {l_ptr};
-        void* out[1] = {dst};
-        st = run_gather(dev, g, 1, in, out, semiring, dtype, s);
+        const void* in[2] = {l_ptr, nullptr};
+        void* out[2] = {dst, ws + P.off_wl};
+        st = run_gather(dev, g, route && P.red_l ? 2 : 1, in, out, semiring, dtype, s);
         if (st != TROP_OK) return st;
         a_use = dst;
     }
     if (!P.b_fold) {
         GatherPlan g = P.gb;
         void* dst = ws + P.off_b;
-        const void* in[1] = {r_ptr};
-        void* out[1] = {dst};
-        st = run_gather(dev, g, 1, in, out, semiring, dtype, s);
+        const void* in[2] = {r_ptr, nullptr};
+        void* out[2] = {dst, ws + P.off_wr};
+        st = run_gather(dev, g, route && P.red_r ? 2 : 1, in, out, semiring, dtype, s);
         if (st != TROP_OK) return st;
         b_use = dst;
     }
@@ -366,6 +387,34 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
     st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s,
                   P.split_bytes ? ws + P.off_split : nullptr, P.split_bytes);
     if (st != TROP_OK) return st;
+    if (route) {
+        // the product's k, then the reduction winners at that k, as one
+        // row-major index over (contracted, A's reduced, B's reduced)
+        TropComposeParams cp{};
+        cp.idx = i_gemm;
+        const int32_t* wl = P.red_l ? reinterpret_cast<const int32_t*>(ws + P.off_wl) : nullptr;
+        const int32_t* wr = P.red_r ? reinterpret_cast<const int32_t*>(ws + P.off_wr) : nullptr;
+        // left operand [nb][gm][K], right operand [nb][K][gn]
+        const int64_t l_str[4] = {P.gm * P.K, P.K, 0, 1};
+        const int64_t r_str[4] = {P.K * P.gn, 0, 1, P.gn};
+        const int32_t* wa = P.swap ? wr : wl;
+        const int32_t* wb = P.swap ? wl : wr;
+        const int64_t* sa = P.swap ? r_str : l_str;
+        const int64_t* sb = P.swap ? l_str : r_str;
+        cp.wa = wa;
+        cp.wb = wb;
+        cp.wa_b = sa[0], cp.wa_r = sa[1], cp.wa_c = sa[2], cp.wa_k = sa[3];
+        cp.wb_b = sb[0], cp.wb_r = sb[1], cp.wb_c = sb[2], cp.wb_k = sb[3];
+        cp.ra_n = P.ra_n;
+        cp.rb_n = P.rb_n;
+        cp.rows = P.gm;
+        cp.cols = P.gn;
+        cp.batch = P.nb;
+        const int64_t tot = P.nb * P.gm * P.gn;
+        const uint32_t grid = (uint32_t)std::min<int64_t>((tot + 255) / 256, int64_t(1) << 30);
+        st = launch(dev, K_ARGMAX_COMPOSE, TROP_K_ARGMAX_COMPOSE, grid, 256, &cp, s);
+        if (st != TROP_OK) return st;
+    }
     // 3. one paired permute of value and argmax into the output order
     if (!P.c_direct) {
         GatherPlan g = P.gc;
@@ -404,6 +453,9 @@ extern "C" trop_status tropical_contract_pair_workspace_size(const char* spec, c
     size_t ws = align_up((size_t)(P.nb * P.M * P.K) * 4) + align_up((size_t)(P.nb * P.K * P.N) * 4);
     if (!P.c_direct) ws += 2 * align_up((size_t)(P.nb * P.M * P.N) * 4);
     ws += plan_splitk(P.M, P.N, P.K, P.nb).bytes;  // K split of a long, narrow product
+    // winners of the pre-pass reductions, for an argmax routed through them
+    if (!P.a_red.empty()) ws += align_up((size_t)(P.nb * P.M * P.K) * 4);
+    if (!P.b_red.empty()) ws += align_up((size_t)(P.nb * P.K * P.N) * 4);
     *bytes = ws;
     return ok();
 }
@@ -433,8 +485,8 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     Plan P;
     trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P);
     if (st != TROP_OK) return st;
-    if (argmax && (!P.a_red.empty() || !P.b_red.empty()))
-        return fail(TROP_ERR_UNSUPPORTED, "argmax through a pre-pass reduction is not defined");
+    if (argmax && !P.route_fits)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "the argmax index over the contracted and reduced labels exceeds int32");
     if (P.out_total == 0) return ok();
     if (P.ws > 0 && workspace_bytes < P.ws)
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,

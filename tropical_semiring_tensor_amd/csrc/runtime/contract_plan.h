@@ -37,6 +37,13 @@ struct PairPlan {
     // workspace layout of the step (bytes, relative to its scratch base);
     // split_bytes > 0: the GEMM is split along K, partials at off_split
     size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, off_split = 0, split_bytes = 0, ws = 0;
+    // argmax through pre-pass reductions: the winners of the GEMM's left /
+    // right operand's reduction (when it has one), in its canonical layout,
+    // and the extents of A's and B's reduced labels
+    size_t off_wl = 0, off_wr = 0;
+    bool red_l = false, red_r = false;
+    int64_t ra_n = 1, rb_n = 1;
+    bool route_fits = true;  // K * ra_n * rb_n < 2^31
 };
 
 // "lhs,rhs->out" into its three subscripts (spaces ignored).

@@ -51,6 +51,7 @@ enum KernelId : int {
     K_GATHER_RUNS_V_N2,
     K_GATHER_RUNS_S_N1,
     K_GATHER_RUNS_S_N2,
+    K_ARGMAX_COMPOSE,  // argmax through pre-pass reductions
     K_COUNT
 };
 const char* kernel_name(KernelId id);

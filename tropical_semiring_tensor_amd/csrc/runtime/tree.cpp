@@ -245,9 +245,10 @@ extern "C" trop_status tropical_tree_run(trop_tree_plan plan, const void* const*
     // every check before anything is enqueued
     for (int s = 0; s < n_steps; ++s) {
         const PairPlan& P = T.steps[s].P;
-        if (step_argmax && step_argmax[s] && (!P.a_red.empty() || !P.b_red.empty()))
-            return fail(TROP_ERR_UNSUPPORTED,
-                        "step " + std::to_string(s) + ": argmax through a pre-pass reduction is not defined");
+        if (step_argmax && step_argmax[s] && !P.route_fits)
+            return fail(TROP_ERR_INVALID_ARGUMENT,
+                        "step " + std::to_string(s) + ": the argmax index over the contracted and reduced labels "
+                        "exceeds int32");
     }
     if (T.ws > 0 && workspace_bytes < T.ws)
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
