@@ -179,7 +179,7 @@ TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t 
  * their bits and the smallest winning k -- are those of the unsplit call
  * (the tie rule of [PR35]'s argmax survives the split).  The split is used
  * when the product has fewer 64 x 64 output tiles (times batch) than the
- * device has CUs and K >= 1024; tropical_gemm_workspace_size reports the
+ * device has CUs and K >= 512; tropical_gemm_workspace_size reports the
  * bytes (0: no split, and the call equals tropical_gemm_strided_batched).
  * workspace: NULL with workspace_bytes 0 (never split), or device memory of
  *   at least that size, used only by work on `stream`.

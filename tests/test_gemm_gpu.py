@@ -311,7 +311,7 @@ def gpu_gemm_ws(tb, sr, A, B, argmax=True, workspace=None):
 
 
 SPLIT_SHAPES = [(1, 64, 8192, 64), (1, 17, 5000, 33), (3, 70, 3000, 50), (1, 1, 20000, 1),
-                (2, 64, 4096, 130), (1, 5, 1024, 3)]
+                (2, 64, 4096, 130), (1, 5, 1024, 3), (1, 3, 700, 2), (1, 64, 65536, 64)]
 
 
 @pytest.mark.parametrize("sr,dt", PAIRS)
@@ -369,7 +369,7 @@ def test_split_k_workspace_rules(tb, orc):
     assert need > 0
     # large grids and short K do not split
     assert tb.tropical_gemm_workspace_size(256, 256, 4096, 64) == 0
-    assert tb.tropical_gemm_workspace_size(64, 64, 1000, 1) == 0
+    assert tb.tropical_gemm_workspace_size(64, 64, 500, 1) == 0
     Ad, Bd = A.to(DEV), B.to(DEV)
     C = torch.empty(1, 64, 64, device=DEV)
     with pytest.raises(tb.TropicalError) as e:

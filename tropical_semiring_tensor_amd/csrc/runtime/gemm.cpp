@@ -65,9 +65,10 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
 
 // Split-K policy: split only a product with fewer output tiles (times
 // batch) than a 256-CU device has CUs, and only when every range keeps at
-// least kSplitMinK terms; aim at about kSplitTarget (tile, range) units.
+// least kSplitMinK terms (one resident K-block); aim at about kSplitTarget
+// (tile, range) units.
 constexpr int64_t kSplitTarget = 512;
-constexpr int64_t kSplitMinK = 512;
+constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
 
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
@@ -217,7 +218,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     mp.batch = batch;
     mp.ksplit = sk.ksplit;
     return launch(dev, (KernelId)(K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + ri), TROP_K_GEMM_SPLITK_MERGE,
-                  grid_for(m * n * batch, 256), 256, &mp, stream);
+                  grid_for(m * n * batch * 8, 256), 256, &mp, stream);  // 8 lanes per output
 }
 
 }  // namespace trop
