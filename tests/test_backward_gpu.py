@@ -158,3 +158,26 @@ def test_backward_maxmul_workload4_recipe(tb, orc):
     _, I = orc.gemm("max_mul", A.numpy(), B.numpy())
     G = torch.randn(2, 300, 260, generator=torch.Generator().manual_seed(23))
     run_both(tb, orc, "max_mul", A, B, torch.from_numpy(I), G, 700, "workload 4 recipe backward")
+
+
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE"])
+def test_backward_every_kernel_form(tb, orc, monkeypatch, knob):
+    """The same gradients from the 16-lanes-per-segment form (the default
+    for few segments), the lane-per-segment form and the wave-per-segment
+    form, over hub-heavy and uniform argmaxes, both weights."""
+    if knob:
+        monkeypatch.setenv(knob, "1")
+    b, m, k, n = 3, 70, 200, 130
+    g = torch.Generator().manual_seed(61)
+    G = torch.randn(b, m, n, generator=g)
+    A = torch.rand(b, m, k, generator=g) + 0.5
+    B = torch.rand(b, k, n, generator=g) + 0.5
+    hub = torch.where(torch.rand(b, m, n, generator=g) < 0.8, 3, torch.randint(0, k, (b, m, n), generator=g))
+    for name, I in (("uniform", torch.randint(0, k, (b, m, n), generator=g, dtype=torch.int32)),
+                    ("hub", hub.to(torch.int32))):
+        for sr in ("max_plus", "max_mul"):
+            run_both(tb, orc, sr, A, B, I, G, k, f"{knob} {name} {sr}")
+    # bins not a multiple of the 16 lanes, and fewer bins than lanes
+    for kk in (37, 5):
+        I = torch.randint(0, kk, (b, m, n), generator=g, dtype=torch.int32)
+        run_both(tb, orc, "min_plus", None, None, I, G, kk, f"{knob} k={kk}")

@@ -228,4 +228,116 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
     }
 }
 
+// Split form for up to GBS_LPS * GBS_BPL = 256 bins when the segments alone
+// are too few to fill the device: GBS_LPS neighbouring lanes share one
+// segment, each owning a contiguous range of at most GBS_BPL bins.  Every
+// lane walks all of its segment's items in order (the lanes of a segment
+// load the same addresses at the same time, so the loads are shared) and
+// adds only the items whose key falls in its range, with the running sum of
+// its current bin in a register as in the lane-per-segment form.  Each bin
+// is still one lane's sequential sum in ascending item order.  The bins are
+// then written with the lanes of a segment side by side along the bins.
+constexpr int GBS_LPS = 16;
+constexpr int GBS_BPL = 16;
+constexpr int GBS_LDR = GBS_BPL + 1;
+constexpr int GBS_THREADS = 256;
+
+template <bool MUL, bool VEC>
+__device__ __forceinline__ void gemm_backward_split_body(const TropBackwardParams& p) {
+    __shared__ float bins_all[GBS_THREADS * GBS_LDR];
+    const int tid = threadIdx.x;
+    const int sub = tid % GBS_LPS;
+    const int64_t nseg = p.segs * p.batch;
+    const int32_t K = (int32_t)p.bins;  // <= GBS_LPS * GBS_BPL (checked on the host)
+    const int32_t bpl = (K + GBS_LPS - 1) / GBS_LPS;
+    const int32_t lo = sub * bpl;
+    const int32_t hi = lo + bpl < K ? lo + bpl : K;
+    const int64_t items = p.items;
+    float* row = bins_all + tid * GBS_LDR;
+    constexpr int SPB = GBS_THREADS / GBS_LPS;  // segments per workgroup
+    for (int64_t seg0 = (int64_t)blockIdx.x * SPB; seg0 < nseg; seg0 += (int64_t)gridDim.x * SPB) {
+        const int64_t seg = seg0 + tid / GBS_LPS;
+        const bool live = seg < nseg;
+        const int64_t b = live ? seg / p.segs : 0, s = live ? seg % p.segs : 0;
+        const int32_t* ip = p.idx + b * p.c_batch + s * p.c_seg;
+        const float* gp = p.grad + b * p.c_batch + s * p.c_seg;
+        const float* wp = MUL ? p.w + b * p.w_batch : nullptr;
+        for (int32_t q = 0; q < bpl; ++q) row[q] = 0.0f;
+        lds_order();
+
+        int32_t cur = -1;  // bin whose running sum is in `acc`
+        float acc = 0.0f;
+        int32_t kb[2][GBL_PF];
+        float vb[2][GBL_PF];
+        auto fetch = [&](int64_t t0, int buf) {
+#pragma unroll
+            for (int q = 0; q < GBL_PF / 4; ++q) {
+                const int64_t t = t0 + 4 * q;
+                if (VEC) {
+                    const bool ok = live && t < items;
+                    const int64_t tc = ok ? t : 0;
+                    const int4 k4 = *reinterpret_cast<const int4*>(ip + tc);
+                    const float4 v4 = *reinterpret_cast<const float4*>(gp + tc);
+                    kb[buf][4 * q + 0] = ok ? k4.x : -1;
+                    kb[buf][4 * q + 1] = ok ? k4.y : -1;
+                    kb[buf][4 * q + 2] = ok ? k4.z : -1;
+                    kb[buf][4 * q + 3] = ok ? k4.w : -1;
+                    vb[buf][4 * q + 0] = v4.x;
+                    vb[buf][4 * q + 1] = v4.y;
+                    vb[buf][4 * q + 2] = v4.z;
+                    vb[buf][4 * q + 3] = v4.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = live && t + e < items;
+                        const int64_t off = (ok ? t + e : 0) * p.c_item;
+                        kb[buf][4 * q + e] = ok ? ip[off] : -1;
+                        vb[buf][4 * q + e] = gp[off];
+                    }
+                }
+            }
+        };
+        // (no load at all when a segment has no items: the host does not
+        // validate the argmax / gradient pointers then)
+        if (items > 0) fetch(0, 0);
+        for (int64_t t0 = 0; t0 < items; t0 += 2 * GBL_PF) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t tb = t0 + h * GBL_PF;
+                if (tb >= items) break;
+                if (tb + GBL_PF < items) fetch(tb + GBL_PF, h ^ 1);
+#pragma unroll
+                for (int u = 0; u < GBL_PF; ++u) {
+                    const int32_t key = kb[h][u];
+                    const bool valid = key >= lo && key < hi;  // an item with a key in this lane's range
+                    float v = vb[h][u];
+                    if (MUL && valid) v = v * wp[(int64_t)key * p.w_key + (tb + u) * p.w_item];
+                    const bool sw = valid && key != cur;
+                    if (__any(sw)) {
+                        if (sw && cur >= 0) row[cur - lo] = acc;
+                        lds_order();
+                        if (sw) {
+                            acc = row[key - lo];
+                            cur = key;
+                        }
+                        lds_order();
+                    }
+                    acc = valid ? acc + v : acc;
+                }
+            }
+        }
+        if (cur >= 0) row[cur - lo] = acc;
+        lds_order();
+        // write: lane `sub` of a segment takes bins sub, sub + 16, ... (the
+        // bin's owner lane is bin / bpl, its slot bin % bpl; all in one wave)
+        if (live) {
+            float* out = p.out + b * p.o_batch + s * p.o_seg;
+            const float* seg_rows = bins_all + (tid - sub) * GBS_LDR;
+            for (int32_t k = sub; k < K; k += GBS_LPS)
+                out[(int64_t)k * p.o_bin] = seg_rows[(k / bpl) * GBS_LDR + k % bpl];
+        }
+        lds_order();
+    }
+}
+
 }  // namespace trop

@@ -100,3 +100,13 @@ TROP_BACKWARD_LANE(plus, false, false)
 TROP_BACKWARD_LANE(plus_vec, false, true)
 TROP_BACKWARD_LANE(mul, true, false)
 TROP_BACKWARD_LANE(mul_vec, true, true)
+
+#define TROP_BACKWARD_SPLIT(NAME, MUL, VEC)                                                      \
+    extern "C" __global__ __launch_bounds__(GBS_THREADS) void trop_gemm_backward_split_##NAME(    \
+        TropBackwardParams p) {                                                                  \
+        gemm_backward_split_body<MUL, VEC>(p);                                                   \
+    }
+TROP_BACKWARD_SPLIT(plus, false, false)
+TROP_BACKWARD_SPLIT(plus_vec, false, true)
+TROP_BACKWARD_SPLIT(mul, true, false)
+TROP_BACKWARD_SPLIT(mul_vec, true, true)

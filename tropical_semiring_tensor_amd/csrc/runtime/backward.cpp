@@ -70,6 +70,22 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
         const bool vec = c_item == 1 && items % 4 == 0 && sC.batch % 4 == 0 && c_seg % 4 == 0 &&
                          (reinterpret_cast<uintptr_t>(argmax) & 15u) == 0 &&
                          (reinterpret_cast<uintptr_t>(grad_c) & 15u) == 0;
+        // Items contiguous in a segment (rows of grad_a) but too few
+        // segments for one lane each to fill the device (fewer than 4 waves
+        // per CU): 16 lanes per segment, each owning a range of bins.  (With
+        // strided items -- columns of grad_b -- the 16 lanes of a segment
+        // load 16 bytes per item and wave, and the lane form measures faster.)
+        const int64_t lane_waves = (segs * batch + 63) / 64;
+        if (c_item == 1 && lane_waves < 4 * (int64_t)device_cu_count(dev) && !env_flag_set("TROPICAL_BACKWARD_LANE")) {
+            const KernelId sk =
+                (KernelId)((mul ? K_GEMM_BACKWARD_SPLIT_MUL : K_GEMM_BACKWARD_SPLIT_PLUS) + (vec ? 1 : 0));
+            const int64_t groups = (segs * batch + 15) / 16;  // 16 segments per workgroup
+            int occ = kernel_occupancy(dev, sk);
+            if (occ < 1) occ = 1;
+            const int64_t cap = (int64_t)device_cu_count(dev) * occ;
+            const int64_t grid = groups < cap ? groups : cap;
+            return launch(dev, sk, TROP_K_GEMM_BACKWARD, (uint32_t)(grid < 1 ? 1 : grid), 256, &p, stream);
+        }
         const KernelId lk = (KernelId)((mul ? K_GEMM_BACKWARD_LANE_MUL : K_GEMM_BACKWARD_LANE_PLUS) + (vec ? 1 : 0));
         const int64_t groups = (segs * batch + 63) / 64;
         int occ = kernel_occupancy(dev, lk);

@@ -52,6 +52,10 @@ enum KernelId : int {
     K_GATHER_RUNS_S_N1,
     K_GATHER_RUNS_S_N2,
     K_ARGMAX_COMPOSE,  // argmax through pre-pass reductions
+    K_GEMM_BACKWARD_SPLIT_PLUS,  // backward, 16 lanes per segment (bins <= 256)
+    K_GEMM_BACKWARD_SPLIT_PLUS_VEC,
+    K_GEMM_BACKWARD_SPLIT_MUL,
+    K_GEMM_BACKWARD_SPLIT_MUL_VEC,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
