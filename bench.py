@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="run a 256 MiB copy and 3 headline GEMMs, print nothing else")
+    ap.add_argument("--profile-valu", action="store_true",
+                    help="3 launches each of the headline GEMM (argmax, value only) and of a 4096^3 "
+                         "min-plus f32 GEMM on integer data, for VALU issue counters; prints nothing else")
     ap.add_argument("--network-only", action="store_true",
                     help="run only the lattice-network (contraction tree) legs and print their JSON")
     args = ap.parse_args()
@@ -127,6 +130,24 @@ def main():
 
     def step():
         tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, I)
+
+    if args.profile_valu:
+        g = torch.Generator(device="cpu").manual_seed(5)
+        A4 = torch.randint(1, 1001, (1, 4096, 4096), generator=g, dtype=torch.int32).float().to(dev)
+        B4 = torch.randint(1, 1001, (1, 4096, 4096), generator=g, dtype=torch.int32).float().to(dev)
+        C4 = torch.empty(1, 4096, 4096, device=dev)
+        I4 = torch.empty(1, 4096, 4096, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            step()
+        for _ in range(3):
+            tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, None)
+        for _ in range(3):
+            tb.tropical_gemm_strided_batched("min_plus", A4, B4, C4, I4)
+        for _ in range(3):
+            tb.tropical_gemm_strided_batched("min_plus", A4, B4, C4, None)
+        torch.cuda.synchronize()
+        log("[bench] valu probe done")
+        return
 
     if args.profile_traffic:
         # calibration: a plain device copy of exactly 256 MiB read + 256 MiB written

@@ -200,7 +200,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     }
     uint32_t grid = (uint32_t)(total < slots ? total : slots);
     const int block = kernel_block(dev, kid);  // the launch bound the kernel was built with
-    if (block != 256 && block != 512)
+    if (block != 256 && block != 512 && block != 1024)
         return fail(TROP_ERR_HIP, std::string(kernel_name(kid)) + ": unexpected launch bound " +
                                       std::to_string(block));
     trop_status st = launch(dev, kid, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
