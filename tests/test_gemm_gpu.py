@@ -203,6 +203,16 @@ def test_simple_kernel_and_no_swizzle(tb, orc, monkeypatch):
     monkeypatch.delenv("TROPICAL_FORCE_SIMPLE_GEMM")
     monkeypatch.setenv("TROPICAL_NO_XCD_SWIZZLE", "1")
     check(tb, orc, "max_plus", A, B, "no swizzle")
+    monkeypatch.delenv("TROPICAL_NO_XCD_SWIZZLE")
+    # the 64-bit tile decode (taken when a grid has 2^31 tiles or more),
+    # with and without split K
+    monkeypatch.setenv("TROPICAL_GEMM_COORD64", "1")
+    check(tb, orc, "max_plus", A, B, "64-bit tile decode")
+    A2, B2 = make("min_plus", "f32", 2, 40, 3000, 50, seed=33)
+    C, I = gpu_gemm_ws(tb, "min_plus", A2, B2)
+    Cr, Ir = orc.gemm("min_plus", A2.numpy(), B2.numpy())
+    assert_bits_equal(C, Cr, "64-bit tile decode, split K")
+    assert_equal(I, Ir, "64-bit tile decode, split K argmax")
 
 
 # ---------------------------------------------------------------------------

@@ -34,6 +34,12 @@ struct TropGemmParams {
     // value and (global) argmax at C / argmax + s c_split.  ksplit = 1: no
     // split (kchunk = k, c_split = 0).
     int64_t ksplit, kchunk, c_split;
+    // coord32 = 1: every logical tile index is below 2^31, and the tile
+    // decode divides with 32-bit magic numbers: floor(n / d) =
+    // umulhi(n, *_m) >> *_s for d = tiles_m * tiles_n (tl_*), tiles_n (tn_*)
+    // and ksplit (ks_*); a divisor of 1 is not divided by
+    int32_t coord32;
+    uint32_t tl_m, tl_s, tn_m, tn_s, ks_m, ks_s;
 };
 
 // Merge of split-K partials: out = the first strictly better of the

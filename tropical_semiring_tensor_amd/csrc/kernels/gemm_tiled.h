@@ -109,9 +109,40 @@ struct TileCoord {
     int64_t b, s, row0, col0, kt;
 };
 
+// floor(n / d) with the host's magic pair (d = 1: n itself)
+__device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t d, uint32_t m, uint32_t sh) {
+    return d == 1 ? n : (__umulhi(n, m) >> sh);
+}
+
 template <bool SPLIT>
 __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
                                                 int64_t total) {
+    if (p.coord32) {
+        // the same decode in 32 bits (every index < 2^31)
+        const uint32_t nx = 8, tot = (uint32_t)total;
+        uint32_t lg = (uint32_t)L;
+        if (p.swizzle) {
+            const uint32_t per = (tot + nx - 1) / nx;
+            uint32_t tall = tot % nx;
+            if (tall == 0) tall = nx;
+            const uint32_t x = lg % nx, local = lg / nx;
+            lg = x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
+        }
+        const uint32_t tl = (uint32_t)tiles, tn = (uint32_t)p.tiles_n;
+        const uint32_t bs = mdiv(lg, tl, p.tl_m, p.tl_s);
+        const uint32_t t = lg - bs * tl;
+        const uint32_t tr = mdiv(t, tn, p.tn_m, p.tn_s);
+        TileCoord c{bs, 0, (int64_t)tr * GEMM_BM, (int64_t)(t - tr * tn) * GEMM_BN, p.k};
+        if constexpr (SPLIT) {
+            const uint32_t ks = (uint32_t)p.ksplit;
+            const uint32_t b = mdiv(bs, ks, p.ks_m, p.ks_s);
+            c.b = b;
+            c.s = bs - b * ks;
+            const int64_t rest = p.k - c.s * p.kchunk;
+            c.kt = rest < p.kchunk ? rest : p.kchunk;
+        }
+        return c;
+    }
     const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
     const int64_t t = lg % tiles;
     const int64_t bs = lg / tiles;

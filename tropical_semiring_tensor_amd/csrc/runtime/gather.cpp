@@ -57,16 +57,7 @@ uint32_t tile_grid(int dev, int64_t tiles) {
     return (uint32_t)(tiles < cap ? tiles : cap);
 }
 
-// Magic pair for floor(n / d), n < 2^31, d >= 2: m = floor(2^(31+s) / d) + 1
-// with s = ceil(log2 d); then floor(n / d) = umulhi(n, m) >> (s - 1).  The
-// error term n * (m * d - 2^(31+s)) / (d * 2^(31+s)) stays below 1/d, so
-// the floor is exact.
-void magic(uint64_t d, uint32_t* m, uint32_t* sh) {
-    uint32_t s = 0;
-    while ((uint64_t(1) << s) < d) ++s;
-    *m = (uint32_t)(((uint64_t(1) << (31 + s)) / d) + 1);
-    *sh = s - 1;
-}
+void magic(uint64_t d, uint32_t* m, uint32_t* sh) { magic_u31(d, m, sh); }
 
 }  // namespace
 

@@ -182,6 +182,13 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         (void)part_elems;
     }
     int64_t total = tm * tn * batch * p.ksplit;
+    // 32-bit tile decode with magic-number division (no 64-bit divides per tile)
+    if (total < (int64_t(1) << 31) && !env_flag("TROPICAL_GEMM_COORD64")) {
+        p.coord32 = 1;
+        if (tm * tn >= 2) magic_u31((uint64_t)(tm * tn), &p.tl_m, &p.tl_s);
+        if (tn >= 2) magic_u31((uint64_t)tn, &p.tn_m, &p.tn_s);
+        if (p.ksplit >= 2) magic_u31((uint64_t)p.ksplit, &p.ks_m, &p.ks_s);
+    }
     // without an argmax output the value-only kernel skips the chunk record
     // and the re-scan
     const KernelId kid =

@@ -78,6 +78,17 @@ int kernel_block(int dev, KernelId id);
 trop_status launch(int dev, KernelId id, trop_kernel_family fam, uint32_t grid, uint32_t block,
                    void* params, hipStream_t stream);
 
+// Magic pair for floor(n / d), n < 2^31, d >= 2: m = floor(2^(31+s) / d) + 1
+// with s = ceil(log2 d); then floor(n / d) = umulhi(n, m) >> (s - 1).  The
+// error term n * (m * d - 2^(31+s)) / (d * 2^(31+s)) stays below 1/d, so
+// the floor is exact.
+inline void magic_u31(uint64_t d, uint32_t* m, uint32_t* sh) {
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    *m = (uint32_t)(((uint64_t(1) << (31 + s)) / d) + 1);
+    *sh = s - 1;
+}
+
 // ---- argument checks (validate.cpp) --------------------------------------
 // `p` must be device memory of `dev` holding at least `span_elems` elements
 // of `elem_bytes` from p on (span_elems == 0: only the pointer is checked).
