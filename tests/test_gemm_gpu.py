@@ -415,3 +415,83 @@ def test_int32_max_mul_saturation_and_ties(tb, orc):
         X[sel] = big[torch.randint(0, 5, (int(sel.sum()),), generator=g)]
     check(tb, orc, "max_mul", A, B, "int32 max-mul saturation")
     check(tb, orc, "max_mul", -A.abs(), B.abs(), "int32 max-mul all non-positive")
+
+
+# ---------------------------------------------------------------------------
+# int32 operands near the limits of the saturating ring: non-negative
+# min-plus data with the 2^30 sentinel and values up to INT32_MAX (sums past
+# 2^31 that saturate and must not win), max-plus data in [-2^30, 2^30), and
+# values that break either pattern placed at 16-term chunk, 32- and 64-term
+# slice and 256-term block boundaries, in some tiles and rows only.
+# ---------------------------------------------------------------------------
+
+LIMIT_POOL = {
+    # non-negative pool for min-plus: sums reach 2^32 - 2, past INT32_MAX
+    "min_plus": [0, 1, 2, 3, 5, 1000, I32_INF, I32_INF + 7, 2 ** 31 - 1, 2 ** 31 - 2, I32_INF - 1],
+    # in-range pool for max-plus: [-2^30, 2^30 - 1]
+    "max_plus": [-I32_INF, -(I32_INF - 1), -5, -1, 0, 1, 3, I32_INF - 1, I32_INF - 2],
+}
+LIMIT_BREAKERS = {
+    "min_plus": [-1, -I32_INF, -(2 ** 31)],
+    "max_plus": [I32_INF, -I32_INF - 1, 2 ** 31 - 1, -(2 ** 31)],
+}
+
+
+def limit_case(sr, b, m, k, n, seed, bad_k=(), bad_rows=None, in_b=False):
+    g = torch.Generator().manual_seed(seed)
+    pool = torch.tensor(LIMIT_POOL[sr], dtype=torch.int64)
+    # mostly small values (ties), some from the whole pool
+    lo = -2 if sr == "max_plus" else 0
+    A = torch.randint(lo, lo + 4, (b, m, k), generator=g)
+    B = torch.randint(lo, lo + 4, (b, k, n), generator=g)
+    A = torch.where(torch.rand(b, m, k, generator=g) < 0.3, pool[torch.randint(0, len(pool), (b, m, k), generator=g)], A)
+    B = torch.where(torch.rand(b, k, n, generator=g) < 0.3, pool[torch.randint(0, len(pool), (b, k, n), generator=g)], B)
+    A, B = A.to(torch.int32), B.to(torch.int32)
+    brk = LIMIT_BREAKERS[sr]
+    for t, kk in enumerate(bad_k):
+        v = brk[t % len(brk)]
+        if in_b:
+            cols = bad_rows if bad_rows is not None else range(n)
+            for j in cols:
+                B[:, kk, j] = v
+        else:
+            rows = bad_rows if bad_rows is not None else range(m)
+            for i in rows:
+                A[:, i, kk] = v
+    return A, B
+
+
+LIMIT_CASES = [
+    # (name, (b, m, k, n), bad k positions, rows / columns that get them, in B)
+    ("clean", (2, 70, 300, 90), (), None, False),
+    ("first_term", (1, 70, 300, 90), (0,), [5], False),
+    ("slice3_some_rows", (1, 130, 300, 70), (200,), [3, 100], False),
+    ("vo_slice_edges", (1, 64, 260, 64), (31, 32, 63, 64), [0], True),
+    ("last_term", (2, 65, 257, 66), (256,), [64], True),
+    ("every_block", (1, 40, 700, 40), (255, 256, 511), None, False),
+]
+
+
+@pytest.mark.parametrize("sr", ["min_plus", "max_plus"])
+@pytest.mark.parametrize("case", LIMIT_CASES, ids=lambda c: c[0])
+def test_int32_limit_patterns(tb, orc, sr, case):
+    name, (b, m, k, n), bad_k, rows, in_b = case
+    A, B = limit_case(sr, b, m, k, n, seed=zlib.crc32(repr((sr, name)).encode()) % 10000,
+                     bad_k=bad_k, bad_rows=rows, in_b=in_b)
+    check(tb, orc, sr, A, B, f"int32 limits {sr} {name}")
+    check(tb, orc, sr, A, B, f"int32 limits {sr} {name} value only", argmax=False)
+
+
+@pytest.mark.parametrize("sr", ["min_plus", "max_plus"])
+def test_int32_limit_patterns_split_k(tb, orc, sr):
+    # long K over few tiles: split-K ranges, with a pattern-breaking value inside one range
+    for bad_k in ((), (1500,), (0, 3999)):
+        A, B = limit_case(sr, 1, 17, 4000, 33, seed=71 + len(bad_k), bad_k=bad_k, bad_rows=[0, 16])
+        assert tb.tropical_gemm_workspace_size(17, 33, 4000, 1) > 0
+        Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy())
+        C, I = gpu_gemm_ws(tb, sr, A, B)
+        assert_bits_equal(C, Cr, f"split int32 limits {sr} {bad_k} C")
+        assert_equal(I, Ir, f"split int32 limits {sr} {bad_k} argmax")
+        C, _ = gpu_gemm_ws(tb, sr, A, B, argmax=False)
+        assert_bits_equal(C, Cr, f"split int32 limits {sr} {bad_k} value-only C")
+
