@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="run a 256 MiB copy and 3 headline GEMMs, print nothing else")
+    ap.add_argument("--profile-configs", action="store_true",
+                    help="the program profiled for per-workload counters: a 256 MiB device copy "
+                         "(counter calibration), then three launches of each workload's kernels")
     ap.add_argument("--profile-valu", action="store_true",
                     help="3 launches each of the headline GEMM (argmax, value only) and of a 4096^3 "
                          "min-plus f32 GEMM on integer data, for VALU issue counters; prints nothing else")
@@ -152,6 +155,11 @@ def main():
             tb.tropical_gemm_strided_batched("min_plus", A4, B4, C4, None)
         torch.cuda.synchronize()
         log("[bench] valu probe done")
+        return
+
+    if args.profile_configs:
+        profile_configs(torch, tb, inputs, dev)
+        log("[bench] config probe done")
         return
 
     if args.profile_traffic:
@@ -248,11 +256,85 @@ def main():
                                   "sample": f"{reps} full passes of {w['name']} (64 x 256^3, "
                                             f"{dt:.1f} s; naive b-i-j-k loops, OpenMP over rows)"}
         log(f"[bench] cpu oracle: {cpu_gops:.2f} GOPS on {orc.max_threads()} threads")
+        result["cpu_baseline"].update(cpu_single_thread(orc, inputs, A, B, ops))
+        log(f"[bench] cpu oracle, one thread: {result['cpu_baseline']['single_thread']}")
 
     if not args.quick:
         result["workloads"] = other_workloads(torch, tb, inputs, timer, dev)
 
     print(json.dumps(result), flush=True)
+
+
+def profile_configs(torch, tb, inputs, dev):
+    """One 256 MiB device copy (calibrates the traffic counters), then three
+    launches of each workload's kernels in workload order: GEMMs 1-4 with
+    argmax, and workload 5's einsum (diagonal gather, B permute, GEMM) plus
+    its paired output permute run on its own."""
+    src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for wi in (1, 2, 3, 4):
+        w = inputs.WORKLOADS[wi]
+        A, B = inputs.gemm_operands(wi)
+        Ad, Bd = A.to(dev), B.to(dev)
+        C = torch.empty(w["batch"], w["m"], w["n"], dtype=Ad.dtype, device=dev)
+        I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
+        for _ in range(3):
+            tb.tropical_gemm_strided_batched(w["semiring"], Ad, Bd, C, I)
+        torch.cuda.synchronize()
+        del A, B, Ad, Bd, C, I
+        torch.cuda.empty_cache()
+    A, B = inputs.einsum_operands()
+    Ad, Bd = A.to(dev), B.to(dev)
+    spec = inputs.WORKLOADS[5]["spec"]
+    C = torch.empty(32, 256, 128, device=dev)
+    I = torch.empty(32, 256, 128, dtype=torch.int32, device=dev)
+    ws = torch.empty(tb.tropical_contract_pair_workspace_size(spec, Ad.shape, Bd.shape), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(3):
+        tb.tropical_contract_pair(spec, "max_plus", Ad, Bd, C, I, ws)
+    C2 = torch.empty(32, 128, 256, device=dev)
+    I2 = torch.empty(32, 128, 256, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        tb.tropical_permute(C2, (0, 2, 1), out=C, x2=I2, out2=I)
+    torch.cuda.synchronize()
+
+
+def cpu_single_thread(orc, inputs, A, B, ops):
+    """The oracle on one host thread: workload 1 whole, one batch entry of
+    workload 2 (scaled to the whole), and workload 5's contraction whole;
+    plus the host's CPU model and logical core count."""
+    cores = orc.max_threads()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    orc.set_threads(1)
+    try:
+        A1, B1 = inputs.gemm_operands(1)
+        t0 = time.perf_counter()
+        orc.gemm("max_plus", A1.numpy(), B1.numpy())
+        t1 = time.perf_counter() - t0
+        An, Bn = A.numpy()[:1], B.numpy()[:1]
+        t0 = time.perf_counter()
+        orc.gemm("max_plus", An, Bn)
+        t2 = (time.perf_counter() - t0) * A.shape[0]
+        A5, B5 = inputs.einsum_operands()
+        t0 = time.perf_counter()
+        orc.contract_pair("iijb,kjb->bki", "max_plus", A5.numpy(), B5.numpy())
+        t5 = time.perf_counter() - t0
+    finally:
+        orc.set_threads(cores)
+    return {"single_thread": {"workload1_us": round(t1 * 1e6, 1),
+                              "workload2_GOPS": round(ops / t2 / 1e9, 3),
+                              "workload2_sample": "1 of 64 batch entries, time scaled by 64",
+                              "workload5_ms": round(t5 * 1e3, 1)},
+            "cpu_model": model, "logical_cores": os.cpu_count()}
 
 
 def other_workloads(torch, tb, inputs, timer, dev):

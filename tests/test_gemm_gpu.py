@@ -213,6 +213,27 @@ def test_simple_kernel_and_no_swizzle(tb, orc, monkeypatch):
     Cr, Ir = orc.gemm("min_plus", A2.numpy(), B2.numpy())
     assert_bits_equal(C, Cr, "64-bit tile decode, split K")
     assert_equal(I, Ir, "64-bit tile decode, split K argmax")
+    monkeypatch.delenv("TROPICAL_GEMM_COORD64")
+
+
+@pytest.mark.parametrize("coord64", [False, True])
+@pytest.mark.parametrize("row_raster", [False, True])
+def test_tile_orders(tb, orc, monkeypatch, coord64, row_raster):
+    # grouped raster (groups of 4 tile-rows, the last one shorter) and plain
+    # row-by-row order, with the 32- and 64-bit tile decodes: tile-row counts
+    # 1, 3, 5, 7, 9 and several batch entries, every output written once
+    if coord64:
+        monkeypatch.setenv("TROPICAL_GEMM_COORD64", "1")
+    if row_raster:
+        monkeypatch.setenv("TROPICAL_GEMM_ROW_RASTER", "1")
+    for shape in ((3, 40, 70, 500), (2, 130, 90, 200), (1, 300, 40, 190), (2, 450, 33, 70), (1, 520, 20, 600)):
+        A, B = make("max_plus", "f32", *shape, seed=sum(shape))
+        check(tb, orc, "max_plus", A, B, f"tile order {shape} coord64={coord64} rows={row_raster}")
+    A, B = make("min_plus", "i32", 1, 300, 2000, 100, seed=9)
+    C, I = gpu_gemm_ws(tb, "min_plus", A, B)
+    Cr, Ir = orc.gemm("min_plus", A.numpy(), B.numpy())
+    assert_bits_equal(C, Cr, "tile order split K")
+    assert_equal(I, Ir, "tile order split K argmax")
 
 
 # ---------------------------------------------------------------------------

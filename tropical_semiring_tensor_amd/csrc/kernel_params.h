@@ -15,6 +15,9 @@
 #define TROP_LOAD_K_CONTIG 0   // k is the unit-stride axis (or neither is)
 #define TROP_LOAD_MN_CONTIG 1  // the row (A) / column (B) axis is unit-stride
 
+// tile-rows per group of the GEMM's grouped raster (see group_rows)
+#define TROP_GEMM_GROUP_ROWS 4
+
 struct TropGemmParams {
     const void* A;
     const void* B;
@@ -40,6 +43,14 @@ struct TropGemmParams {
     // and ksplit (ks_*); a divisor of 1 is not divided by
     int32_t coord32;
     uint32_t tl_m, tl_s, tn_m, tn_s, ks_m, ks_s;
+    // grouped raster: inside a batch entry the tiles run in groups of
+    // TROP_GEMM_GROUP_ROWS tile-rows (the last group may be shorter), column
+    // by column and down the rows inside a group, so the workgroups that
+    // run at the same time share a few operand panels.  group_rows = 1:
+    // row by row.  gr_m / gr_s: magic pair of TROP_GEMM_GROUP_ROWS * tiles_n
+    // (coord32).
+    int32_t group_rows;
+    uint32_t gr_m, gr_s;
 };
 
 // Merge of split-K partials: out = the first strictly better of the

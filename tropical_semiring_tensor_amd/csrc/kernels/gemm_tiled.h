@@ -131,8 +131,21 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
         const uint32_t tl = (uint32_t)tiles, tn = (uint32_t)p.tiles_n;
         const uint32_t bs = mdiv(lg, tl, p.tl_m, p.tl_s);
         const uint32_t t = lg - bs * tl;
-        const uint32_t tr = mdiv(t, tn, p.tn_m, p.tn_s);
-        TileCoord c{bs, 0, (int64_t)tr * GEMM_BM, (int64_t)(t - tr * tn) * GEMM_BN, p.k};
+        uint32_t tr, tc;
+        if (p.group_rows > 1) {
+            constexpr uint32_t G = TROP_GEMM_GROUP_ROWS;
+            const uint32_t gsz = G * tn;
+            const uint32_t gi = mdiv(t, gsz, p.gr_m, p.gr_s);
+            const uint32_t r0 = gi * G;
+            const uint32_t rows = min(G, (uint32_t)p.tiles_m - r0);
+            const uint32_t w = t - gi * gsz;
+            tc = rows == G ? w / G : w / rows;
+            tr = r0 + (w - tc * rows);
+        } else {
+            tr = mdiv(t, tn, p.tn_m, p.tn_s);
+            tc = t - tr * tn;
+        }
+        TileCoord c{bs, 0, (int64_t)tr * GEMM_BM, (int64_t)tc * GEMM_BN, p.k};
         if constexpr (SPLIT) {
             const uint32_t ks = (uint32_t)p.ksplit;
             const uint32_t b = mdiv(bs, ks, p.ks_m, p.ks_s);
@@ -146,7 +159,20 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
     const int64_t lg = p.swizzle ? xcd_remap(L, total) : L;
     const int64_t t = lg % tiles;
     const int64_t bs = lg / tiles;
-    TileCoord c{bs, 0, (t / p.tiles_n) * GEMM_BM, (t % p.tiles_n) * GEMM_BN, p.k};
+    int64_t tr, tc;
+    if (p.group_rows > 1) {
+        constexpr int64_t G = TROP_GEMM_GROUP_ROWS;
+        const int64_t gsz = G * p.tiles_n;
+        const int64_t r0 = t / gsz * G;
+        const int64_t rows = p.tiles_m - r0 < G ? p.tiles_m - r0 : G;
+        const int64_t w = t - r0 * p.tiles_n;
+        tc = w / rows;
+        tr = r0 + (w - tc * rows);
+    } else {
+        tr = t / p.tiles_n;
+        tc = t % p.tiles_n;
+    }
+    TileCoord c{bs, 0, tr * GEMM_BM, tc * GEMM_BN, p.k};
     if constexpr (SPLIT) {
         c.b = bs / p.ksplit;
         c.s = bs % p.ksplit;
