@@ -296,7 +296,8 @@ TROP_API trop_status tropical_contract_pair_workspace_size(const char* spec, con
  * contracted, left) -- and lands in the output order with no step 3 (every
  * (x) here is commutative bit for bit, so values and argmax are the same).
  * An operand already collapsible to a batched matrix with a unit row or
- * column stride is used in place.
+ * column stride is used in place.  When both operands need the tiled
+ * transpose kernel in step 1, the two run as one launch.
  * spec: "lhs,rhs->out" with single-letter labels a-z A-Z, explicit output,
  *   no ellipsis; every output label appears in an operand, output labels
  *   are distinct.  batch labels are in A, B and out; left in A and out;

@@ -175,10 +175,11 @@ def test_workload5_full(tb, orc):
     C, I = tb.tropical_contract_pair("iijb,kjb->bki", "max_plus", Ad, Bd)
     torch.cuda.synchronize()
     st = tb.tropical_get_stats()
-    # diag gather, B permute, GEMM taken as B (x) A straight into (b, k, i):
-    # three launches, no output permute
-    assert st["launches_total"] == 3, st
-    assert st["launches"]["gather_tiled"] == 2 and st["launches"]["gemm_tiled"] == 1, st
+    # diag gather and B permute in one paired launch of the tiled gather,
+    # then the GEMM taken as B (x) A straight into (b, k, i): two launches,
+    # no output permute
+    assert st["launches_total"] == 2, st
+    assert st["launches"]["gather_tiled"] == 1 and st["launches"]["gemm_tiled"] == 1, st
     assert st["host_syncs"] == 0 and st["memcpy_calls"] == 0
     Cr, Ir = orc.contract_pair("iijb,kjb->bki", "max_plus", A.numpy(), B.numpy())
     assert_bits_equal(C.cpu().numpy(), Cr, "workload 5")
@@ -200,3 +201,32 @@ def test_contract_long_contraction_splits_k(tb, orc):
         Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
         assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} {sr}")
         assert_equal(I.cpu().numpy(), Ir, f"{spec} {sr} argmax")
+
+
+@pytest.mark.parametrize("paired", [True, False])
+def test_paired_pre_pass_gathers(tb, orc, monkeypatch, paired):
+    """Both operands permuted or diagonal-gathered by the tiled kernel: one
+    paired launch (workgroups split between the two jobs in proportion to
+    their tiles) or two launches, with the same results.  Shapes give the
+    two jobs very different tile counts, the same and different tile widths
+    (which falls back to two launches), a routed argmax through reductions
+    (two tensors per job), and grids past the resident cap."""
+    if not paired:
+        monkeypatch.setenv("TROPICAL_NO_PAIRED_GATHER", "1")
+    g = torch.Generator().manual_seed(41)
+    cases = [
+        ("iijb,kjb->bki", (40, 40, 64, 8), (96, 64, 8)),
+        ("abc,cbd->adb", (64, 48, 32), (32, 48, 128)),
+        ("jib,kjb->bik", (256, 64, 12), (8, 256, 12)),
+        ("ijb,jkb->bik", (512, 512, 4), (512, 256, 4)),
+        ("iirb,kjrb->bki", (20, 20, 3, 8), (48, 36, 3, 8)),
+    ]
+    for spec, sa, sb in cases:
+        A = torch.randint(-9, 10, sa, generator=g).float()
+        B = torch.randint(-9, 10, sb, generator=g).float()
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        C, I = tb.tropical_contract_pair(spec, "max_plus", Ad, Bd)
+        torch.cuda.synchronize()
+        Cr, Ir = orc.contract_pair(spec, "max_plus", A.numpy(), B.numpy())
+        assert_bits_equal(C.cpu().numpy(), Cr, f"{spec} paired={paired}")
+        assert_equal(I.cpu().numpy(), Ir, f"{spec} paired={paired} argmax")

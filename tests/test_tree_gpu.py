@@ -129,7 +129,7 @@ def test_tree_workspace_reuse_across_runs_and_streams(tb, orc):
     assert e.value.status == tb.WORKSPACE_TOO_SMALL
 
 
-def test_tree_stays_on_device(tb):
+def test_tree_stays_on_device(tb, monkeypatch):
     """Counters of one run: kernels only -- no host synchronisation, no copy."""
     net = inputs.grid_network(4, 4, 4, salt=6)
     plan = tb.tropical_tree_plan_create("max_plus", torch.float32, net["subs"], net["shapes"], net["steps"])
@@ -146,7 +146,18 @@ def test_tree_stays_on_device(tb):
     st = tb.tropical_get_stats()
     torch.cuda.synchronize()
     assert st["host_syncs"] == 0 and st["memcpy_calls"] == 0
+    # a step whose two operands both take the tiled gather runs them in one
+    # launch; with pairing off every gather is its own launch
+    assert st["launches_total"] <= len(net["steps"]) + gathers
+    paired = [a.clone() for a in ams]
+    monkeypatch.setenv("TROPICAL_NO_PAIRED_GATHER", "1")
+    tb.tropical_reset_stats()
+    tb.tropical_tree_run(plan, xs, out=out, argmax=ams, workspace=ws)
+    st = tb.tropical_get_stats()
+    torch.cuda.synchronize()
     assert st["launches_total"] == len(net["steps"]) + gathers
+    for a, b in zip(paired, ams):
+        assert torch.equal(a, b)
 
 
 def test_tree_zero_extent_bond(tb, orc):

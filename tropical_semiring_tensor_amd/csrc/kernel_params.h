@@ -104,6 +104,13 @@ struct TropGatherParams {
     int64_t rtotal;
 };
 
+// Two gathers of the vectorised tiled path in one launch: workgroups
+// [0, split) run p[0] and the rest run p[1], each over its own tiles.
+struct TropGatherPairParams {
+    TropGatherParams p[2];
+    int32_t split;
+};
+
 // Argmax through pre-pass reductions: I[o] (the product's k, in the GEMM's
 // canonical (batch, row, col) layout) becomes
 //     k * ra_n * rb_n + wa[k] * rb_n + wb[k]

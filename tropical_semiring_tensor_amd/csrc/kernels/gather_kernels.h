@@ -165,8 +165,9 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
 // 16-byte vectors along P and stores four along Q.  Needs EP, EQ, the input
 // stride of Q and of every other axis to be multiples of 4 and both pointers
 // 16-byte aligned (checked on the host).
+// Workgroup b0 of a set of bstep workgroups walks tiles b0, b0 + bstep, ...
 template <int TP, int NT>
-__device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p) {
+__device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p, int64_t b0, int64_t bstep) {
     constexpr int TQ = 4096 / TP;
     constexpr int LDT = TP + 1;          // LDS row (fixed q) length in words
     constexpr int LPR = TP / 4;          // read phase: lanes per q-row
@@ -187,7 +188,7 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p)
     const int rp = (tid % LPR) * 4, rq = tid / LPR;   // read-phase lane position
     const int wq = (tid % LPQ) * 4, wp = tid / LPQ;   // write-phase lane position
 
-    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    for (int64_t blk = b0; blk < nblk; blk += bstep) {
         const int64_t tq = blk % p.tiles_q;
         const int64_t tp = (blk / p.tiles_q) % p.tiles_p;
         int64_t bi = blk / per_batch;

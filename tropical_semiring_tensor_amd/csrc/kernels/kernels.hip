@@ -60,7 +60,14 @@ extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled(T
 #define TROP_TILED_VEC(TPV, NTV)                                                                \
     extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled_v##TPV##_n##NTV( \
         TropGatherParams p) {                                                                   \
-        gather_tiled_vec_body<TPV, NTV>(p);                                                     \
+        gather_tiled_vec_body<TPV, NTV>(p, blockIdx.x, gridDim.x);                              \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_tiled2_v##TPV##_n##NTV( \
+        TropGatherPairParams q) {                                                               \
+        if ((int)blockIdx.x < q.split)                                                          \
+            gather_tiled_vec_body<TPV, NTV>(q.p[0], blockIdx.x, q.split);                       \
+        else                                                                                    \
+            gather_tiled_vec_body<TPV, NTV>(q.p[1], blockIdx.x - q.split, gridDim.x - q.split); \
     }
 TROP_TILED_VEC(16, 1)
 TROP_TILED_VEC(32, 1)

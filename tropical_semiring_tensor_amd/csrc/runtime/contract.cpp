@@ -362,7 +362,19 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
     const void* b_use = r_ptr;
     // an argmax routed through a pre-pass reduction keeps its winners
     const bool route = argmax && (P.red_l || P.red_r) && P.K > 0;
-    if (!P.a_fold) {
+    if (!P.a_fold && !P.b_fold) {
+        // both operands: one launch when both take the same tiled kernel
+        GatherPlan g0 = P.ga, g1 = P.gb;
+        const void* in0[2] = {l_ptr, nullptr};
+        void* out0[2] = {ws + P.off_a, ws + P.off_wl};
+        const void* in1[2] = {r_ptr, nullptr};
+        void* out1[2] = {ws + P.off_b, ws + P.off_wr};
+        st = run_gather_pair(dev, g0, route && P.red_l ? 2 : 1, in0, out0, g1, route && P.red_r ? 2 : 1, in1,
+                             out1, semiring, dtype, s);
+        if (st != TROP_OK) return st;
+        a_use = ws + P.off_a;
+        b_use = ws + P.off_b;
+    } else if (!P.a_fold) {
         GatherPlan g = P.ga;
         void* dst = ws + P.off_a;
         const void* in[2] = {l_ptr, nullptr};
@@ -370,8 +382,7 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
         st = run_gather(dev, g, route && P.red_l ? 2 : 1, in, out, semiring, dtype, s);
         if (st != TROP_OK) return st;
         a_use = dst;
-    }
-    if (!P.b_fold) {
+    } else if (!P.b_fold) {
         GatherPlan g = P.gb;
         void* dst = ws + P.off_b;
         const void* in[2] = {r_ptr, nullptr};

@@ -236,14 +236,73 @@ trop_status plan_diag(int in_ndim, const int64_t* in_shape, const int64_t* in_st
     return plan_gather(out_ndim, oshape, ostride, nred, rshape, rstride, plan);
 }
 
-trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* const* in, void* const* out,
-                       trop_semiring sr, trop_dtype dt, hipStream_t stream) {
-    TropGatherParams& p = plan.params;
+namespace {
+
+void set_pointers(TropGatherParams& p, int ntensors, const void* const* in, void* const* out) {
     p.ntensors = ntensors;
     for (int t = 0; t < 2; ++t) {
         p.in[t] = t < ntensors ? in[t] : nullptr;
         p.out[t] = t < ntensors ? out[t] : nullptr;
     }
+}
+
+// Tiled path: the kernel for these pointers (16-byte accesses on both sides
+// when every stride, extent and pointer allows) and its number of tiles.
+KernelId prepare_tiled(TropGatherParams& p, int ntensors, int64_t* nblk) {
+    const int nd = p.ndim, P = p.ax_in, Q = nd - 1;
+    const int64_t EP = p.shape[P], EQ = p.shape[Q];
+    bool vec = EP % 4 == 0 && EQ % 4 == 0 && EP >= 4;
+    for (int d = 0; d < nd && vec; ++d)
+        if (d != P) vec = p.istride[d] % 4 == 0;
+    for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
+    KernelId kid = K_GATHER_TILED;
+    if (vec) {
+        const int tp = EP >= 64 ? 64 : (EP >= 32 ? 32 : 16);
+        p.tile_p = tp;
+        p.tiles_p = (EP + tp - 1) / tp;
+        p.tiles_q = (EQ + 4096 / tp - 1) / (4096 / tp);
+        const int base = ntensors == 2 ? K_GATHER_TILED_V16_N2 : K_GATHER_TILED_V16_N1;
+        kid = (KernelId)(base + (tp == 64 ? 2 : (tp == 32 ? 1 : 0)));
+    }
+    *nblk = p.tiles_p * p.tiles_q * p.nbatch;
+    return kid;
+}
+
+}  // namespace
+
+trop_status run_gather_pair(int dev, GatherPlan& g0, int nt0, const void* const* in0, void* const* out0,
+                            GatherPlan& g1, int nt1, const void* const* in1, void* const* out1,
+                            trop_semiring sr, trop_dtype dt, hipStream_t stream) {
+    if (g0.path == GP_TILED && g1.path == GP_TILED && !env_long("TROPICAL_NO_PAIRED_GATHER", 0)) {
+        TropGatherPairParams q{};
+        q.p[0] = g0.params;
+        q.p[1] = g1.params;
+        set_pointers(q.p[0], nt0, in0, out0);
+        set_pointers(q.p[1], nt1, in1, out1);
+        int64_t n0 = 0, n1 = 0;
+        const KernelId k0 = prepare_tiled(q.p[0], nt0, &n0);
+        const KernelId k1 = prepare_tiled(q.p[1], nt1, &n1);
+        if (k0 == k1 && k0 != K_GATHER_TILED && n0 > 0 && n1 > 0) {
+            // workgroups in proportion to the two gathers' tiles (all of them
+            // when both fit under the resident cap), at least one each
+            const int64_t grid = tile_grid(dev, n0 + n1);
+            int64_t s0 = grid == n0 + n1 ? n0 : (grid * n0 + (n0 + n1) / 2) / (n0 + n1);
+            if (s0 < 1) s0 = 1;
+            if (s0 > grid - 1) s0 = grid - 1;
+            q.split = (int32_t)s0;
+            const KernelId kp = (KernelId)(K_GATHER_TILED2_V16_N1 + (k0 - K_GATHER_TILED_V16_N1));
+            return launch(dev, kp, TROP_K_GATHER_TILED, (uint32_t)grid, 256, &q, stream);
+        }
+    }
+    trop_status st = run_gather(dev, g0, nt0, in0, out0, sr, dt, stream);
+    if (st != TROP_OK) return st;
+    return run_gather(dev, g1, nt1, in1, out1, sr, dt, stream);
+}
+
+trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* const* in, void* const* out,
+                       trop_semiring sr, trop_dtype dt, hipStream_t stream) {
+    TropGatherParams& p = plan.params;
+    set_pointers(p, ntensors, in, out);
     switch (plan.path) {
         case GP_NONE:
             return TROP_OK;
@@ -262,23 +321,8 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             return launch(dev, K_GATHER_COPY, TROP_K_GATHER_COPY, stream_grid(dev, work), 256, &p, stream);
         }
         case GP_TILED: {
-            const int nd = p.ndim, P = p.ax_in, Q = nd - 1;
-            const int64_t EP = p.shape[P], EQ = p.shape[Q];
-            // 16-byte accesses on both sides when every stride and extent allows
-            bool vec = EP % 4 == 0 && EQ % 4 == 0 && EP >= 4;
-            for (int d = 0; d < nd && vec; ++d)
-                if (d != P) vec = p.istride[d] % 4 == 0;
-            for (int t = 0; t < ntensors && vec; ++t) vec = aligned16(p.in[t]) && aligned16(p.out[t]);
-            KernelId kid = K_GATHER_TILED;
-            if (vec) {
-                const int tp = EP >= 64 ? 64 : (EP >= 32 ? 32 : 16);
-                p.tile_p = tp;
-                p.tiles_p = (EP + tp - 1) / tp;
-                p.tiles_q = (EQ + 4096 / tp - 1) / (4096 / tp);
-                const int base = ntensors == 2 ? K_GATHER_TILED_V16_N2 : K_GATHER_TILED_V16_N1;
-                kid = (KernelId)(base + (tp == 64 ? 2 : (tp == 32 ? 1 : 0)));
-            }
-            const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
+            int64_t nblk = 0;
+            const KernelId kid = prepare_tiled(p, ntensors, &nblk);
             return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
         }
         case GP_RUNS: {

@@ -56,6 +56,12 @@ enum KernelId : int {
     K_GEMM_BACKWARD_SPLIT_PLUS_VEC,
     K_GEMM_BACKWARD_SPLIT_MUL,
     K_GEMM_BACKWARD_SPLIT_MUL_VEC,
+    K_GATHER_TILED2_V16_N1,  // two tiled gathers in one launch
+    K_GATHER_TILED2_V32_N1,
+    K_GATHER_TILED2_V64_N1,
+    K_GATHER_TILED2_V16_N2,
+    K_GATHER_TILED2_V32_N2,
+    K_GATHER_TILED2_V64_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
@@ -114,6 +120,11 @@ const char* gather_path_name(GatherPath p);
 // Enqueue a planned gather (pointers are set here; checks done by caller).
 trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* const* in,
                        void* const* out, trop_semiring sr, trop_dtype dt, hipStream_t stream);
+// Two independent gathers: one launch when both take the same vectorised
+// tiled kernel, else run_gather twice.
+trop_status run_gather_pair(int dev, GatherPlan& g0, int nt0, const void* const* in0, void* const* out0,
+                            GatherPlan& g1, int nt1, const void* const* in1, void* const* out1,
+                            trop_semiring sr, trop_dtype dt, hipStream_t stream);
 
 // Label-based diagonal / trace gather into a plan (used by the public call
 // and by the contraction driver).
