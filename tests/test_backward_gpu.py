@@ -129,6 +129,35 @@ def test_backward_strided_views_and_one_sided(tb, orc):
     assert_bits_equal(gb.cpu().numpy(), rb, "column-major grad_b")
 
 
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE"])
+def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
+    """Bins summed from denormal gradients, +0 / -0 mixes (a bin of only
+    -0.0 items is +0.0, since sums start at +0.0), exact cancellations to
+    zero and infinities: each kernel form's adds must round and keep
+    denormals exactly as the oracle's sequential float32 loop does."""
+    if knob:
+        monkeypatch.setenv(knob, "1")
+    b, m, k, n = 2, 64, 40, 200
+    g = torch.Generator().manual_seed(81)
+    I = torch.randint(0, k, (b, m, n), generator=g, dtype=torch.int32)
+    I[:, :, ::3] = 5   # one hub bin per row
+    coin = torch.rand(b, m, n, generator=g) < 0.5
+    cases = {
+        "denormal": (torch.rand(b, m, n, generator=g) - 0.5) * 2e-38,
+        "smallest denormals": torch.where(coin, 1e-45, -1.4e-45),
+        "signed zeros": torch.where(coin, 0.0, -0.0),
+        "cancelling": torch.where(coin, 1.5e-38, -1.5e-38),
+        "infinities": torch.where(torch.rand(b, m, n, generator=g) < 0.02, float("inf"),
+                                  torch.randn(b, m, n, generator=g)),
+    }
+    A = torch.rand(b, m, k, generator=g) * 1e-20
+    B = torch.rand(b, k, n, generator=g) * 1e-20
+    for name, G in cases.items():
+        run_both(tb, orc, "max_plus", None, None, I, G, k, f"{knob} {name}")
+    # max-mul: the weight products themselves underflow into denormals
+    run_both(tb, orc, "max_mul", A, B, I, cases["denormal"] * 1e18, k, f"{knob} max_mul denormal")
+
+
 def test_backward_errors(tb):
     I = torch.zeros(1, 4, 5, dtype=torch.int32, device=DEV)
     G = torch.zeros(1, 4, 5, device=DEV)

@@ -9,8 +9,9 @@
 // ("Acceptance criteria": backward consistent with the CPU path through the
 // argmax buffer) and the scatter-add of tropical-gemm PR #35's autograd
 // functions, done the way the rustytorch commit "rtx-backend-cuda: native
-// index_select / index_add" does scatter-add: deterministically, with no
-// float atomics, by walking the adjoint of the selection.
+// index_select / index_add" does scatter-add: deterministically, by walking
+// the adjoint of the selection in a fixed order (the LDS adds below never
+// let two lanes race on one bin).
 //
 // Both gradients are one pattern, a segmented histogram: a segment (a row
 // of dA, or a column of dB) has `items` entries, each with a key (its k*)
@@ -40,6 +41,16 @@ constexpr int GBW_UNROLL = 4;   // 64-item chunks whose loads are issued togethe
 // operations staying in program order; the hardware keeps a wave's LDS
 // operations in order, this keeps the compiler from moving or caching them.
 __device__ __forceinline__ void lds_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// Adds v into an LDS float with the LDS unit's own add (ds_add_f32, no value
+// returned): an IEEE single-precision add rounded to nearest even, with
+// denormals kept.  Where a bin is only ever added to by one lane, the wave's
+// in-order LDS pipeline applies its adds in program order, so the bin is
+// the same sequential sum a plain load-add-store loop gives, without the
+// wave waiting on the load.
+__device__ __forceinline__ void lds_add(float* a, float v) {
+    __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
 
 // NB: bins per LDS chunk and wave (the host picks the smallest of 256, 1024,
 // 4096 that holds all bins, or 4096 and several passes).
@@ -112,12 +123,10 @@ __device__ __forceinline__ void gemm_backward_body(const TropBackwardParams& p) 
 }
 
 // Lane-per-segment form for up to GBL_BINS bins: each of the 64 lanes of a
-// one-wave workgroup walks its own segment item by item, in order.  The
-// running sum of the bin it is adding to stays in a register and goes
-// through LDS only when the key changes, so a segment whose items pile onto
-// a few keys (the usual shape of an argmax: a row's largest entries win for
-// most columns) costs one add per item.  Keys and values are fetched
-// GBL_PF items ahead.  After the walk the wave's bins are written out with
+// one-wave workgroup walks its own segment item by item, in order, adding
+// each item into its own LDS row of bins with lds_add (no lane touches
+// another's row until the walk is over, so every bin is summed in item
+// order).  Keys and values are fetched GBL_PF items ahead.  After the walk the wave's bins are written out with
 // unit-stride accesses, along bins or along segments, whichever the output
 // allows.
 constexpr int GBL_BINS = 256;
@@ -145,8 +154,6 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
         for (int32_t k = 0; k < K; ++k) row[k] = 0.0f;
         lds_order();
 
-        int32_t cur = -1;  // bin whose running sum is in `acc`
-        float acc = 0.0f;
         // items GBL_PF at a time, the next group fetched while this one adds
         int32_t kb[2][GBL_PF];
         float vb[2][GBL_PF];
@@ -196,21 +203,10 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
                     float v = vb[h][u];
                     // (an invalid item reads the weight at (0, 0), which is in range)
                     if (MUL) v = v * wp[(int64_t)(valid ? key : 0) * p.w_key + (valid ? tb + u : 0) * p.w_item];
-                    const bool sw = valid && key != cur;
-                    if (__any(sw)) {
-                        if (sw && cur >= 0) row[cur] = acc;
-                        lds_order();
-                        if (sw) {
-                            acc = row[key];
-                            cur = key;
-                        }
-                        lds_order();
-                    }
-                    acc = valid ? acc + v : acc;
+                    if (valid) lds_add(&row[key], v);
                 }
             }
         }
-        if (cur >= 0) row[cur] = acc;
         lds_order();
         // write the 64 segments' bins
         if (p.o_bin == 1) {
@@ -233,9 +229,9 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
 // segment, each owning a contiguous range of at most GBS_BPL bins.  Every
 // lane walks all of its segment's items in order (the lanes of a segment
 // load the same addresses at the same time, so the loads are shared) and
-// adds only the items whose key falls in its range, with the running sum of
-// its current bin in a register as in the lane-per-segment form.  Each bin
-// is still one lane's sequential sum in ascending item order.  The bins are
+// adds only the items whose key falls in its range, with lds_add as in the
+// lane-per-segment form.  Each bin is still one lane's sequential sum in
+// ascending item order.  The bins are
 // then written with the lanes of a segment side by side along the bins.
 constexpr int GBS_LPS = 16;
 constexpr int GBS_BPL = 16;
@@ -265,8 +261,6 @@ __device__ __forceinline__ void gemm_backward_split_body(const TropBackwardParam
         for (int32_t q = 0; q < bpl; ++q) row[q] = 0.0f;
         lds_order();
 
-        int32_t cur = -1;  // bin whose running sum is in `acc`
-        float acc = 0.0f;
         int32_t kb[2][GBL_PF];
         float vb[2][GBL_PF];
         auto fetch = [&](int64_t t0, int buf) {
@@ -312,21 +306,10 @@ __device__ __forceinline__ void gemm_backward_split_body(const TropBackwardParam
                     const bool valid = key >= lo && key < hi;  // an item with a key in this lane's range
                     float v = vb[h][u];
                     if (MUL && valid) v = v * wp[(int64_t)key * p.w_key + (tb + u) * p.w_item];
-                    const bool sw = valid && key != cur;
-                    if (__any(sw)) {
-                        if (sw && cur >= 0) row[cur - lo] = acc;
-                        lds_order();
-                        if (sw) {
-                            acc = row[key - lo];
-                            cur = key;
-                        }
-                        lds_order();
-                    }
-                    acc = valid ? acc + v : acc;
+                    if (valid) lds_add(&row[key - lo], v);
                 }
             }
         }
-        if (cur >= 0) row[cur - lo] = acc;
         lds_order();
         // write: lane `sub` of a segment takes bins sub, sub + 16, ... (the
         // bin's owner lane is bin / bpl, its slot bin % bpl; all in one wave)
