@@ -91,11 +91,15 @@ __device__ __forceinline__ int64_t gather_row_offset(const TropGatherParams& p, 
     return off;
 }
 
+#ifndef GC_UNROLL
+#define GC_UNROLL 4  // independent 16-byte vectors per thread and iteration
+#endif
+
 __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
     const int64_t inner = p.shape[p.ndim - 1];
     if (p.vec && p.idx32) {
         // 16-byte vectors, 32-bit indices, magic-number division; each thread
-        // keeps four independent vectors in flight per iteration
+        // keeps GC_UNROLL independent vectors in flight per iteration
         const uint32_t nv = (uint32_t)(p.total / 4);
         const uint32_t vpr = p.vpr;
         const uint32_t step = gridDim.x * blockDim.x;
@@ -111,11 +115,11 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
             }
             dst = (int64_t)row * inner + col;
         };
-        for (uint32_t v0 = blockIdx.x * blockDim.x + threadIdx.x; v0 < nv; v0 += 4 * step) {
-            int64_t src[4], dst[4];
-            bool ok[4];
+        for (uint32_t v0 = blockIdx.x * blockDim.x + threadIdx.x; v0 < nv; v0 += GC_UNROLL * step) {
+            int64_t src[GC_UNROLL], dst[GC_UNROLL];
+            bool ok[GC_UNROLL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < GC_UNROLL; ++u) {
                 const uint32_t v = v0 + u * step;
                 ok[u] = v < nv && v >= v0;  // (v >= v0 guards wrap-around)
                 if (ok[u]) offsets(v, src[u], dst[u]);
@@ -123,12 +127,12 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
             for (int t = 0; t < p.ntensors; ++t) {
                 const uint32_t* in = static_cast<const uint32_t*>(p.in[t]);
                 uint32_t* out = static_cast<uint32_t*>(p.out[t]);
-                u32x4 x[4];
+                u32x4 x[GC_UNROLL];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < GC_UNROLL; ++u)
                     if (ok[u]) x[u] = ld16(in + src[u]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < GC_UNROLL; ++u)
                     if (ok[u]) st16(out + dst[u], x[u]);
             }
         }

@@ -50,9 +50,12 @@ uint32_t stream_grid(int dev, int64_t work) {
 }
 
 // Grid of the tiled transpose: one workgroup per tile up to a cap of
-// resident workgroups, each looping over tiles.
-uint32_t tile_grid(int dev, int64_t tiles) {
-    const int64_t per_cu = env_long("TROPICAL_TILED_BLOCKS_PER_CU", 4);  // tuning knob
+// resident workgroups, each looping over tiles.  Measured on 256 MiB
+// transposes (cold cache): 4 per CU is best for the 4-byte tiled kernel;
+// the runs kernel (wide elements, short runs) gains 1-16% at 5.
+uint32_t tile_grid(int dev, int64_t tiles, const char* knob = "TROPICAL_TILED_BLOCKS_PER_CU",
+                   long per_cu_default = 4) {
+    const int64_t per_cu = env_long(knob, per_cu_default);  // tuning knob
     const int64_t cap = (int64_t)device_cu_count(dev) * per_cu;
     return (uint32_t)(tiles < cap ? tiles : cap);
 }
@@ -339,7 +342,8 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             const KernelId kid = vec ? (ntensors == 2 ? K_GATHER_RUNS_V_N2 : K_GATHER_RUNS_V_N1)
                                      : (ntensors == 2 ? K_GATHER_RUNS_S_N2 : K_GATHER_RUNS_S_N1);
             const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
-            return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
+            return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk, "TROPICAL_RUNS_BLOCKS_PER_CU", 5),
+                          256, &p, stream);
         }
         case GP_NAIVE:
             return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);
