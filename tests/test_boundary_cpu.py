@@ -154,6 +154,14 @@ def test_contract_plan_folds_canonical_operands(tb):
     assert "reduceA=a" in d and "A=gather:reduce" in d
 
 
+def test_contract_plan_flat_gather_for_a_small_bond(tb):
+    # A (a=2, i=64, b=512): its canonical (b, i, a) order is a transpose of a
+    # 512 x 2 plane, where a fixed 64-wide tile would be 2/64 in range; B's
+    # (b, a*j) plane is 512 x 128 and keeps the 64 x 64 tiles
+    d = tb.tropical_contract_pair_describe("aib,ajb->bij", (2, 64, 512), (2, 64, 512))
+    assert "A=gather:flat" in d and "B=gather:tiled" in d, d
+
+
 @pytest.mark.parametrize("spec,err", [
     ("ij,jk", tb_err := "INVALID"), ("ij->i", "INVALID"), ("ij,jk->iq", "INVALID"),
     ("i1,jk->ik", "INVALID"), ("ij,jk->ii", "INVALID"), ("ij,j,k->ik", "INVALID"),

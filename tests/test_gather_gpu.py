@@ -1,5 +1,6 @@
 """Parity of the HIP permute and diagonal / trace gather with the CPU oracle
-(bit-exact), through every kernel path (copy, tiled, naive, reduce)."""
+(bit-exact), through every kernel path (copy, tiled, runs, flat, naive,
+reduce)."""
 import itertools
 
 import numpy as np
@@ -300,8 +301,87 @@ def test_permute_runs_path(tb, orc, R, dims):
     assert_bits_equal(out.cpu().numpy(), orc.permute(xv.numpy(), (0, 2, 1, 3)), f"runs unaligned R={R}")
 
 
-def test_runs_path_in_contraction_describe(tb):
+def test_runs_path_in_contraction_describe(tb, monkeypatch):
     # the lattice network's boundary gather: a 16-word run (bond 16) whose
-    # neighbour moves from the front to the end
+    # neighbour moves from the front to the end.  The runs tile (32 runs
+    # along the moved axis) is half in range for its 16, so the flat tile
+    # takes it; with the flat path off it is the runs path.
+    desc = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
+    assert "A=gather:flat" in desc, desc
+    monkeypatch.setenv("TROPICAL_FLAT_PATH", "0")
     desc = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
     assert "A=gather:runs" in desc, desc
+
+
+# (shape, perm) whose transpose plane has a small extent on one side
+FLAT = [
+    ((3001, 2), (1, 0)),          # small P (the read-contiguous axis), ragged Q
+    ((2, 3001), (1, 0)),          # small Q (the write-contiguous axis)
+    ((5, 999, 3), (0, 2, 1)),     # odd small extent: odd LDS rows
+    ((5, 3, 999), (0, 2, 1)),
+    ((700, 6, 7), (2, 1, 0)),     # P = 7 with a batch axis between P and Q
+    ((16, 2, 2050), (0, 2, 1)),
+    ((9, 4, 1500), (2, 0, 1)),    # Q = 4 whose rows are apart in the output
+    ((3, 5, 11, 300), (0, 3, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("mode", ["auto", "force", "0"])
+@pytest.mark.parametrize("shape,perm", FLAT, ids=[f"{s}{p}" for s, p in FLAT])
+def test_permute_flat_path(tb, orc, monkeypatch, mode, shape, perm):
+    """The flat-tile transpose (the small extent whole in each tile) against
+    the oracle, with a paired int32 tensor and an unaligned view; the same
+    shapes with the path forced on for any valid tile, and switched off."""
+    if mode != "auto":
+        monkeypatch.setenv("TROPICAL_FLAT_PATH", mode)
+    g = torch.Generator().manual_seed(sum(shape) + len(perm))
+    x = torch.randn(shape, generator=g)
+    idx = torch.randint(-10 ** 6, 10 ** 6, shape, generator=g, dtype=torch.int32)
+    out, out2 = tb.tropical_permute(x.to(DEV), perm, x2=idx.to(DEV))
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"flat {shape} {perm}")
+    assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), perm), f"flat pair {shape} {perm}")
+    base = torch.randn(1 + x.numel(), generator=g)
+    xv = base[1:].view(shape)
+    out = tb.tropical_permute(base.to(DEV)[1:].view(shape), perm)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(xv.numpy(), perm), f"flat unaligned {shape} {perm}")
+
+
+@pytest.mark.parametrize("dt", [torch.float64, torch.complex64, torch.complex128],
+                         ids=lambda d: str(d).replace("torch.", ""))
+@pytest.mark.parametrize("shape,perm", [((3001, 2), (1, 0)), ((2, 3001), (1, 0)), ((7, 3, 501), (2, 1, 0)),
+                                        ((4, 640, 5), (0, 2, 1))], ids=lambda v: str(v))
+def test_permute_flat_path_wide_elements(tb, orc, dt, shape, perm):
+    """Wide elements on the flat path: each element's words stay together
+    (2 or 4 words per element), pairs with an int64 index."""
+    g = torch.Generator().manual_seed(sum(shape))
+    x = wide_tensor(shape, dt, g)
+    idx = torch.randint(0, 1 << 40, shape, generator=g, dtype=torch.int64)
+    if dt.itemsize == 8:
+        out, out2 = tb.tropical_permute(x.to(DEV), perm, x2=idx.to(DEV))
+        torch.cuda.synchronize()
+        assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), perm), f"{dt} flat pair {shape}")
+    else:
+        out = tb.tropical_permute(x.to(DEV), perm)
+        torch.cuda.synchronize()
+    assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"{dt} flat {shape} {perm}")
+
+
+def test_flat_path_is_taken(tb, orc, monkeypatch):
+    """The planner's choice shows in the contraction description, and the
+    small-bond gather moves the same bits with the path on or off."""
+    d = tb.tropical_contract_pair_describe("aib,ajb->bij", (2, 64, 512), (2, 64, 512))
+    assert "A=gather:flat" in d, d
+    g = torch.Generator().manual_seed(5)
+    A = torch.randn(2, 64, 512, generator=g)
+    B = torch.randn(2, 64, 512, generator=g)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C1, I1 = tb.tropical_contract_pair("aib,ajb->bij", "max_plus", Ad, Bd, argmax=True)
+    monkeypatch.setenv("TROPICAL_FLAT_PATH", "0")
+    C0, I0 = tb.tropical_contract_pair("aib,ajb->bij", "max_plus", Ad, Bd, argmax=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C0.view(torch.int32)) and torch.equal(I1, I0)
+    Co, Io = orc.contract_pair("aib,ajb->bij", "max_plus", A.numpy(), B.numpy())
+    assert_bits_equal(C1.cpu().numpy(), Co, "flat contraction value")
+    assert_equal(I1.cpu().numpy(), Io, "flat contraction argmax")

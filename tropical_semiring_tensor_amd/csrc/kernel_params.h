@@ -96,7 +96,13 @@ struct TropGatherParams {
     uint32_t mag_s[TROP_MAX_DIMS];
     uint32_t vpr, vpr_m, vpr_s;  // copy path: 16-byte vectors per output row
     int32_t tile_p;              // vectorised tiled path: tile extent along ax_in
-    int32_t run_shift;           // runs path: log2 of the run length R (words)
+    int32_t run_shift;           // runs / flat path: log2 of the run length R (words)
+    // flat path: tile of flat_tp elements along ax_in by flat_tq along Q,
+    // LDS row of flat_ld words; flat_z = 1 when the last axis is the
+    // element's words; floor(f / (flat_tp R)) and floor(f / (flat_tq R))
+    // by the magic pairs (fl_m1, fl_s1) and (fl_m2, fl_s2)
+    int32_t flat_tp, flat_tq, flat_ld, flat_z;
+    uint32_t fl_m1, fl_s1, fl_m2, fl_s2;
     // reduction (trace)
     int32_t nred;
     int64_t rshape[TROP_MAX_DIMS];

@@ -9,7 +9,7 @@
 // repeated label that stride is the sum of the repeated axes' strides).
 // The page names the naive one-thread-per-element version as a first cut
 // and a tiled, padded shared-memory transpose as the faster form; here the
-// host picks one of three copy paths per call:
+// host picks one of these paths per call:
 //
 //  * copy:  the last output axis has input stride 1, so rows are copied
 //           with 16-byte vectors (both sides coalesced);
@@ -21,6 +21,9 @@
 //           stride 1 and another output axis steps from run to run in the
 //           input; tiles of runs go through LDS so that reads and writes
 //           are long contiguous segments (a transpose of wide elements);
+//  * flat:  the tiled or runs plane with a small extent on one side; the
+//           tile takes that whole extent and is walked in input order to
+//           read and in output order to write;
 //  * naive: one thread per output element, digits decoded from the
 //           linear index (the fallback).
 //
@@ -386,6 +389,114 @@ __device__ __forceinline__ void gather_tiled_body(const TropGatherParams& p) {
                 const int64_t dst = obase + pv * oP + q;
                 for (int t = 0; t < p.ntensors; ++t)
                     st4(static_cast<uint32_t*>(p.out[t]) + dst, tile[t][lane][pl]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Flat-tile path for a transpose plane with a small extent on one side (a
+// bond of 2..15, the words of a wide element against a short axis).  The
+// fixed-shape tiles above waste most of each tile there: a 64-wide tile of a
+// 2-wide axis moves 2 useful columns.  Here the tile takes the whole small
+// extent and as much of the other axis as fits in FLAT_WORDS words:
+//   P = ax_in, Q = the last output axis before the element's words (Z, if
+//   any: R = 2^run_shift words, contiguous on both sides; R = 1 for 4-byte
+//   elements, where Q is the last axis and P has input stride 1);
+//   a tile is flat_tp elements along P by flat_tq along Q.
+// The read phase walks the tile in input order (q, then p, then the word),
+// so when the tile's P range and the Q step are adjacent in the input the
+// whole tile is one contiguous segment; the write phase walks it in output
+// order (p, then q, then the word), one contiguous segment when the Q range
+// and the P step are adjacent in the output.  The LDS row of a fixed q is
+// flat_ld words (odd: the write phase's column walk is conflict-free).
+// 4-byte accesses, up to FLAT_WORDS / GATHER_THREADS = 16 loads in flight
+// per thread.
+constexpr int FLAT_WORDS = 4096;
+constexpr int FLAT_LDS = 6144;  // >= flat_tq * flat_ld (checked on the host)
+constexpr int FLAT_PER_THREAD = FLAT_WORDS / GATHER_THREADS;
+
+template <int NT>
+__device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
+    __shared__ uint32_t tile[NT][FLAT_LDS];
+    const int nd = p.ndim;
+    const int Z = p.flat_z ? nd - 1 : -1;
+    const int P = p.ax_in, Q = nd - 1 - p.flat_z;
+    const int lr = p.run_shift;  // 0 when there is no word axis
+    const int64_t EP = p.shape[P], EQ = p.shape[Q];
+    const int64_t sP = p.istride[P], sQ = p.istride[Q];
+    int64_t oP = 1;  // output stride of P, in words
+    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    // offsets inside a tile fit in 31 bits (checked on the host)
+    const uint32_t sP32 = (uint32_t)sP, sQ32 = (uint32_t)sQ, oP32 = (uint32_t)oP;
+    const uint32_t rw = (uint32_t)p.flat_tp << lr;  // words of a tile row (fixed q)
+    const uint32_t cw = (uint32_t)p.flat_tq << lr;  // words of a tile column (fixed p)
+    const uint32_t nw = rw * (uint32_t)p.flat_tq;   // words of a full tile, <= FLAT_WORDS
+    const uint32_t ld = (uint32_t)p.flat_ld;
+    const uint32_t wmask = (1u << lr) - 1;
+    const int tid = threadIdx.x;
+    const int64_t per_batch = p.tiles_p * p.tiles_q;
+    const int64_t nblk = per_batch * p.nbatch;
+
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t tq = blk % p.tiles_q;
+        const int64_t tp = (blk / p.tiles_q) % p.tiles_p;
+        int64_t bi = blk / per_batch;
+        int64_t ibase = 0, obase = 0, ostride = 1;
+        for (int d = nd - 1; d >= 0; --d) {
+            const int64_t e = p.shape[d];
+            if (d != P && d != Q && d != Z) {
+                const int64_t digit = bi % e;
+                bi /= e;
+                ibase += digit * p.istride[d];
+                obase += digit * ostride;
+            }
+            ostride *= e;
+        }
+        const int64_t p0 = tp * p.flat_tp, q0 = tq * p.flat_tq;
+        const uint32_t np = (uint32_t)(EP - p0 < p.flat_tp ? EP - p0 : p.flat_tp);
+        const uint32_t nq = (uint32_t)(EQ - q0 < p.flat_tq ? EQ - q0 : p.flat_tq);
+        ibase += p0 * sP + q0 * sQ;         // the tile's first word in the input
+        obase += p0 * oP + (q0 << lr);      // and in the output
+        // The per-element index math below is the same for every tile; an
+        // opaque copy of the thread id keeps the compiler from hoisting all
+        // 16 elements' worth of it out of the loop (150+ live registers).
+        uint32_t tid_t = (uint32_t)tid;
+        asm volatile("" : "+v"(tid_t));
+        // read, in input order; all loads issued before the LDS stores
+        uint32_t v[NT][FLAT_PER_THREAD];
+        uint32_t slot[FLAT_PER_THREAD];
+#pragma unroll
+        for (int i = 0; i < FLAT_PER_THREAD; ++i) {
+            const uint32_t f = tid_t + (uint32_t)i * GATHER_THREADS;
+            const uint32_t ql = fdiv(f, p.fl_m1, p.fl_s1);  // f / rw
+            const uint32_t rem = f - ql * rw;                // pl * R + w
+            const uint32_t pl = rem >> lr;
+            const bool ok = f < nw && pl < np && ql < nq;
+            slot[i] = ok ? ql * ld + rem : 0xffffffffu;
+            // (an element outside the tile loads the tile's first word, which exists)
+            const uint32_t off = ok ? pl * sP32 + ql * sQ32 + (rem & wmask) : 0u;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) v[t][i] = ld4(static_cast<const uint32_t*>(p.in[t]) + ibase + off);
+        }
+#pragma unroll
+        for (int i = 0; i < FLAT_PER_THREAD; ++i)
+            if (slot[i] != 0xffffffffu)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) tile[t][slot[i]] = v[t][i];
+        __syncthreads();
+        // write, in output order
+#pragma unroll
+        for (int i = 0; i < FLAT_PER_THREAD; ++i) {
+            const uint32_t f = tid_t + (uint32_t)i * GATHER_THREADS;
+            const uint32_t pl = fdiv(f, p.fl_m2, p.fl_s2);  // f / cw
+            const uint32_t rem = f - pl * cw;                // ql * R + w
+            const uint32_t ql = rem >> lr;
+            if (f < nw && pl < np && ql < nq) {
+                const uint32_t a = ql * ld + (pl << lr) + (rem & wmask);
+                const uint32_t off = pl * oP32 + rem;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) st4(static_cast<uint32_t*>(p.out[t]) + obase + off, tile[t][a]);
             }
         }
         __syncthreads();

@@ -85,6 +85,13 @@ TROP_RUNS(v_n2, true, 2)
 TROP_RUNS(s_n1, false, 1)
 TROP_RUNS(s_n2, false, 2)
 
+extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_flat_n1(TropGatherParams p) {
+    gather_flat_body<1>(p);
+}
+extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_flat_n2(TropGatherParams p) {
+    gather_flat_body<2>(p);
+}
+
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
     gather_naive_body(p);
 }

@@ -72,9 +72,97 @@ const char* gather_path_name(GatherPath p) {
         case GP_NAIVE: return "naive";
         case GP_REDUCE: return "reduce";
         case GP_RUNS: return "runs";
+        case GP_FLAT: return "flat";
     }
     return "?";
 }
+
+namespace {
+
+// Fraction of a tile sweep along an axis of extent e that is in range.
+double tile_use(int64_t e, int64_t t) { return (double)e / (double)(((e + t - 1) / t) * t); }
+
+// The tiled or runs plan `p` (ax_in set; lr = log2 words per element, z =
+// whether the last axis is the element's words) switches to the flat path
+// where that measured faster (256 MiB transposes, cold cache):
+//  - always in place of the scalar 64 x 64 tile (shapes or pointers that
+//    rule out 16-byte accesses): 0.3-1.9 TB/s there against 2.7-5.2 flat;
+//  - in place of the 16-byte tiled or the runs kernel when at most half of
+//    its fixed tile is in range (a 2-wide axis fills 2/64 of a tile):
+//    e.g. a 4096 x 8 x 2048 transpose 4.05 -> 4.7 TB/s, a 2-wide one
+//    0.13 -> 4.6.
+// `fixed_vec`: whether the tiled kernel would use 16-byte accesses (at
+// planning time, as far as shapes and strides tell).  TROPICAL_FLAT_PATH=0
+// keeps the fixed tiles; =force takes the flat path whenever its tile is
+// valid (tests).
+bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
+    const char* mode = std::getenv("TROPICAL_FLAT_PATH");
+    if (mode && std::strcmp(mode, "0") == 0) return false;
+    const bool force = mode && std::strcmp(mode, "force") == 0;
+    const int nd = p.ndim, P = p.ax_in, Q = nd - 1 - z;
+    const int64_t EP = p.shape[P], EQ = p.shape[Q], R = int64_t(1) << lr;
+    // share of the fixed tile in range
+    double fixed;
+    if (z) {
+        fixed = tile_use(EP, 128 / R) * tile_use(EQ, 32);
+    } else {
+        const int64_t tp = fixed_vec ? (EP >= 64 ? 64 : (EP >= 32 ? 32 : 16)) : 64;
+        fixed = tile_use(EP, tp) * tile_use(EQ, fixed_vec ? 4096 / tp : 64);
+    }
+    // the flat tile: the smaller side whole (or 64 x 64 when both sides are
+    // that long), the other side filled up to 4096 words, rounded down to a
+    // multiple of 32 elements (128-byte segments) where it is that long
+    const int64_t half = (4096 / 2) / R;  // leaves at least 2 along the other side
+    int64_t tp, tq;
+    if (R == 1 && EP >= 64 && EQ >= 64) {
+        tp = tq = 64;
+    } else if (EP <= EQ) {
+        tp = EP < half ? EP : half;
+        tq = 4096 / (tp * R);
+        if (tq >= 64) tq -= tq % 32;
+        if (tq > EQ) tq = EQ;
+    } else {
+        tq = EQ < half ? EQ : half;
+        tp = 4096 / (tq * R);
+        if (tp >= 64) tp -= tp % 32;
+        if (tp > EP) tp = EP;
+    }
+    const int64_t rw = tp * R, cw = tq * R;
+    const int64_t ld = rw % 2 == 0 ? rw + 1 : rw;
+    if (tp < 1 || tq < 2 || rw < 2 || cw < 2 || rw * tq > 4096 || tq * ld > 6144) return false;
+    if (rw * tq < 512) return false;  // too little per tile: per-tile costs dominate
+    // the kernel keeps offsets inside a tile in 31 bits
+    int64_t oP = 1;
+    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    const int64_t lim = int64_t(1) << 31;
+    if ((tp - 1) * p.istride[P] + (tq - 1) * p.istride[Q] + R >= lim || (tp - 1) * oP + cw >= lim) return false;
+    const int64_t pct = env_long("TROPICAL_FLAT_MAX_FIXED_USE_PCT", 50);  // tuning knob
+    const bool scalar_fixed = !z && !fixed_vec;
+    if (!force && !scalar_fixed && !(fixed * 100.0 <= (double)pct)) return false;
+    p.run_shift = lr;
+    p.flat_z = z;
+    p.flat_tp = (int32_t)tp;
+    p.flat_tq = (int32_t)tq;
+    p.flat_ld = (int32_t)ld;
+    magic((uint64_t)rw, &p.fl_m1, &p.fl_s1);
+    magic((uint64_t)cw, &p.fl_m2, &p.fl_s2);
+    p.tiles_p = (EP + tp - 1) / tp;
+    p.tiles_q = (EQ + tq - 1) / tq;
+    p.nbatch = p.total / (EP * EQ * R);
+    return true;
+}
+
+// Whether the tiled kernel can use 16-byte accesses on these shapes and
+// strides (pointers aside).
+bool tiled_vec_shape(const TropGatherParams& p) {
+    const int nd = p.ndim, P = p.ax_in, Q = nd - 1;
+    bool vec = p.shape[P] % 4 == 0 && p.shape[Q] % 4 == 0 && p.shape[P] >= 4;
+    for (int d = 0; d < nd && vec; ++d)
+        if (d != P) vec = p.istride[d] % 4 == 0;
+    return vec;
+}
+
+}  // namespace
 
 trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride, int nred,
                         const int64_t* rshape, const int64_t* rstride, GatherPlan* plan) {
@@ -169,6 +257,7 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
                 p.tiles_p = (p.shape[d] + tp - 1) / tp;
                 p.tiles_q = (p.shape[nd - 2] + 31) / 32;
                 p.nbatch = total / (p.shape[d] * p.shape[nd - 2] * R);
+                if (consider_flat(p, p.run_shift, 1, false)) plan->path = GP_FLAT;
                 return TROP_OK;
             }
         }
@@ -182,6 +271,7 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
             p.tiles_p = (p.shape[d] + 63) / 64;
             p.tiles_q = (p.shape[nd - 1] + 63) / 64;
             p.nbatch = total / (p.shape[d] * p.shape[nd - 1]);
+            if (consider_flat(p, 0, 0, tiled_vec_shape(p))) plan->path = GP_FLAT;
             return TROP_OK;
         }
     }
@@ -273,6 +363,19 @@ KernelId prepare_tiled(TropGatherParams& p, int ntensors, int64_t* nblk) {
 
 }  // namespace
 
+namespace {
+
+// Flat path launch: more workgroups than fit at once (6 per CU by LDS and
+// registers) balanced the tiles best: 8 per CU measured 5.2 TB/s on 2-wide
+// transposes against 4.4-4.9 at 4.
+trop_status launch_flat(int dev, TropGatherParams& p, int ntensors, hipStream_t stream) {
+    const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
+    return launch(dev, ntensors == 2 ? K_GATHER_FLAT_N2 : K_GATHER_FLAT_N1, TROP_K_GATHER_TILED,
+                  tile_grid(dev, nblk, "TROPICAL_FLAT_BLOCKS_PER_CU", 8), 256, &p, stream);
+}
+
+}  // namespace
+
 trop_status run_gather_pair(int dev, GatherPlan& g0, int nt0, const void* const* in0, void* const* out0,
                             GatherPlan& g1, int nt1, const void* const* in1, void* const* out1,
                             trop_semiring sr, trop_dtype dt, hipStream_t stream) {
@@ -285,7 +388,7 @@ trop_status run_gather_pair(int dev, GatherPlan& g0, int nt0, const void* const*
         int64_t n0 = 0, n1 = 0;
         const KernelId k0 = prepare_tiled(q.p[0], nt0, &n0);
         const KernelId k1 = prepare_tiled(q.p[1], nt1, &n1);
-        if (k0 == k1 && k0 != K_GATHER_TILED && n0 > 0 && n1 > 0) {
+        if (k0 == k1 && k0 >= K_GATHER_TILED_V16_N1 && k0 <= K_GATHER_TILED_V64_N2 && n0 > 0 && n1 > 0) {
             // workgroups in proportion to the two gathers' tiles (all of them
             // when both fit under the resident cap), at least one each
             const int64_t grid = tile_grid(dev, n0 + n1);
@@ -326,6 +429,12 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
         case GP_TILED: {
             int64_t nblk = 0;
             const KernelId kid = prepare_tiled(p, ntensors, &nblk);
+            if (kid == K_GATHER_TILED) {
+                // pointers that rule out 16-byte accesses: the flat tile
+                // beats the scalar 64 x 64 one
+                TropGatherParams f = p;
+                if (consider_flat(f, 0, 0, false)) return launch_flat(dev, f, ntensors, stream);
+            }
             return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk), 256, &p, stream);
         }
         case GP_RUNS: {
@@ -345,6 +454,8 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk, "TROPICAL_RUNS_BLOCKS_PER_CU", 5),
                           256, &p, stream);
         }
+        case GP_FLAT:
+            return launch_flat(dev, p, ntensors, stream);
         case GP_NAIVE:
             return launch(dev, K_GATHER_NAIVE, TROP_K_GATHER_NAIVE, grid_for(p.total, 256), 256, &p, stream);
         case GP_REDUCE: {

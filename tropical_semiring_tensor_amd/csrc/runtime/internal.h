@@ -62,6 +62,8 @@ enum KernelId : int {
     K_GATHER_TILED2_V16_N2,
     K_GATHER_TILED2_V32_N2,
     K_GATHER_TILED2_V64_N2,
+    K_GATHER_FLAT_N1,  // flat-tile transpose (a small extent on one side)
+    K_GATHER_FLAT_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
@@ -105,7 +107,7 @@ trop_status check_device_span(const void* p, int dev, int64_t span_elems, size_t
 bool max_offset(int n, const int64_t* extent, const int64_t* stride, int64_t* out);
 
 // ---- gather planning (gather.cpp) ----------------------------------------
-enum GatherPath { GP_NONE = 0, GP_COPY, GP_TILED, GP_NAIVE, GP_REDUCE, GP_RUNS };
+enum GatherPath { GP_NONE = 0, GP_COPY, GP_TILED, GP_NAIVE, GP_REDUCE, GP_RUNS, GP_FLAT };
 struct GatherPlan {
     TropGatherParams params;
     GatherPath path;
