@@ -385,3 +385,32 @@ def test_flat_path_is_taken(tb, orc, monkeypatch):
     Co, Io = orc.contract_pair("aib,ajb->bij", "max_plus", A.numpy(), B.numpy())
     assert_bits_equal(C1.cpu().numpy(), Co, "flat contraction value")
     assert_equal(I1.cpu().numpy(), Io, "flat contraction argmax")
+
+
+MANY_AXES = [(4,) * 7, (8,) * 5, (2, 4, 8, 16, 8, 2), (3, 5, 2, 7, 4, 6), (2,) * 8]
+
+
+@pytest.mark.parametrize("mode", ["auto", "force", "0"])
+@pytest.mark.parametrize("shape", MANY_AXES, ids=lambda s: "x".join(map(str, s)))
+def test_permute_many_small_axes(tb, orc, monkeypatch, mode, shape):
+    """Tensor-network shapes (many axes of small bond): the flat tile's
+    sides are groups of axes (contiguous in the input on one side, in the
+    output on the other); random permutations, a paired int32 tensor, f64."""
+    if mode != "auto":
+        monkeypatch.setenv("TROPICAL_FLAT_PATH", mode)
+    g = torch.Generator().manual_seed(len(shape) * 31 + shape[0])
+    x = torch.randn(shape, generator=g)
+    idx = torch.randint(-10 ** 6, 10 ** 6, shape, generator=g, dtype=torch.int32)
+    x64 = wide_tensor(shape, torch.float64, g)
+    xd, idd, x64d = x.to(DEV), idx.to(DEV), x64.to(DEV)
+    rng = np.random.default_rng(len(shape))
+    for _ in range(10):
+        perm = tuple(int(v) for v in rng.permutation(len(shape)))
+        out, out2 = tb.tropical_permute(xd, perm, x2=idd)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.permute(x.numpy(), perm), f"{shape} {perm}")
+        assert_equal(out2.cpu().numpy(), orc.permute(idx.numpy(), perm), f"pair {shape} {perm}")
+        if len(shape) < 8:  # (8 axes apart plus the element's words exceed the 8 kernel axes)
+            o64 = tb.tropical_permute(x64d, perm)
+            torch.cuda.synchronize()
+            assert_bits_equal(o64.cpu().numpy(), orc.permute(x64.numpy(), perm), f"f64 {shape} {perm}")

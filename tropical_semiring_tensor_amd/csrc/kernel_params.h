@@ -97,12 +97,23 @@ struct TropGatherParams {
     uint32_t vpr, vpr_m, vpr_s;  // copy path: 16-byte vectors per output row
     int32_t tile_p;              // vectorised tiled path: tile extent along ax_in
     int32_t run_shift;           // runs / flat path: log2 of the run length R (words)
-    // flat path: tile of flat_tp elements along ax_in by flat_tq along Q,
+    // flat path.  The P group: output axes fc_pax[0..fc_np) that are one
+    // contiguous block of the input (fc_pax[0] innermost); the Q group:
+    // the last output axes fc_qax[0..fc_nq) (fc_qax[0] = the last one
+    // before the element's words), one contiguous block of the output.  A
+    // tile is flat_tp elements of the P group by flat_tq of the Q group,
+    // whole inner axes (products fc_pin, fc_qin) and a chunk of the
+    // outermost one; group totals fc_ptot, fc_qtot.  fc_postr: output
+    // stride of each P axis, fc_qistr: input stride of each Q axis (words).
     // LDS row of flat_ld words; flat_z = 1 when the last axis is the
     // element's words; floor(f / (flat_tp R)) and floor(f / (flat_tq R))
     // by the magic pairs (fl_m1, fl_s1) and (fl_m2, fl_s2)
     int32_t flat_tp, flat_tq, flat_ld, flat_z;
     uint32_t fl_m1, fl_s1, fl_m2, fl_s2;
+    int32_t fc_np, fc_nq;
+    int32_t fc_pax[4], fc_qax[4];
+    int64_t fc_postr[4], fc_qistr[4];
+    int64_t fc_ptot, fc_qtot, fc_pin, fc_qin;
     // reduction (trace)
     int32_t nred;
     int64_t rshape[TROP_MAX_DIMS];

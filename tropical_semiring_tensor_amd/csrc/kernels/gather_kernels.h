@@ -21,9 +21,9 @@
 //           stride 1 and another output axis steps from run to run in the
 //           input; tiles of runs go through LDS so that reads and writes
 //           are long contiguous segments (a transpose of wide elements);
-//  * flat:  the tiled or runs plane with a small extent on one side; the
-//           tile takes that whole extent and is walked in input order to
-//           read and in output order to write;
+//  * flat:  short read- or write-contiguous axes (small bonds, many small
+//           axes): each side of the tile is a group of axes, walked in
+//           input order to read and in output order to write;
 //  * naive: one thread per output element, digits decoded from the
 //           linear index (the fallback).
 //
@@ -395,48 +395,73 @@ __device__ __forceinline__ void gather_tiled_body(const TropGatherParams& p) {
     }
 }
 
-// Flat-tile path for a transpose plane with a small extent on one side (a
-// bond of 2..15, the words of a wide element against a short axis).  The
-// fixed-shape tiles above waste most of each tile there: a 64-wide tile of a
-// 2-wide axis moves 2 useful columns.  Here the tile takes the whole small
-// extent and as much of the other axis as fits in FLAT_WORDS words:
-//   P = ax_in, Q = the last output axis before the element's words (Z, if
-//   any: R = 2^run_shift words, contiguous on both sides; R = 1 for 4-byte
-//   elements, where Q is the last axis and P has input stride 1);
-//   a tile is flat_tp elements along P by flat_tq along Q.
-// The read phase walks the tile in input order (q, then p, then the word),
-// so when the tile's P range and the Q step are adjacent in the input the
-// whole tile is one contiguous segment; the write phase walks it in output
-// order (p, then q, then the word), one contiguous segment when the Q range
-// and the P step are adjacent in the output.  The LDS row of a fixed q is
-// flat_ld words (odd: the write phase's column walk is conflict-free).
-// 4-byte accesses, up to FLAT_WORDS / GATHER_THREADS = 16 loads in flight
-// per thread.
+// Flat-tile path for transposes whose read- and write-contiguous axes are
+// short (a bond of 2..32, the words of a wide element against a short
+// axis, many small axes).  The fixed tiles above span one axis each way and
+// waste most of the tile there: a 64-wide tile of a 2-wide axis moves 2
+// useful columns, and an 8^8 tensor's 8 x 8 planes fill 1/64 of a tile.
+// Here each side of the tile is a group of axes:
+//   P group: output axes that form one contiguous block of the input
+//            (input strides R, R e0, R e0 e1, ...);
+//   Q group: the last output axes (before the element's words, if any),
+//            one contiguous block of the output;
+// each with its inner axes whole and a chunk of its outermost axis, so a
+// P position p is input word p R and a Q position q output word q R.  The
+// other side's offsets (output offsets of the P positions, input offsets
+// of the Q positions) are the same for every tile and sit in an LDS table
+// built once per workgroup.  The read phase walks the tile in input order
+// (q, then p, then the word) and the write phase in output order (p, then
+// q, then the word), so each side moves in contiguous segments.  The LDS
+// row of a fixed q is flat_ld words (odd: the write phase's column walk is
+// conflict-free).  4-byte accesses, up to 16 loads in flight per thread.
+// GROUPS = false: both groups are single axes, whose offsets are a
+// multiply (no table; the larger LDS tile keeps one more workgroup per CU).
 constexpr int FLAT_WORDS = 4096;
-constexpr int FLAT_LDS = 6144;  // >= flat_tq * flat_ld (checked on the host)
+constexpr int FLAT_LDS_AXES = 6144;    // >= flat_tq * flat_ld (checked on the host)
+constexpr int FLAT_LDS_GROUPS = 5120;  // the same with the table beside it
+constexpr int FLAT_TAB = 2050;         // >= flat_tp + flat_tq (checked on the host)
 constexpr int FLAT_PER_THREAD = FLAT_WORDS / GATHER_THREADS;
 
-template <int NT>
+template <int NT, bool GROUPS>
 __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
-    __shared__ uint32_t tile[NT][FLAT_LDS];
+    __shared__ uint32_t tile[NT][GROUPS ? FLAT_LDS_GROUPS : FLAT_LDS_AXES];
+    __shared__ uint32_t tab[GROUPS ? FLAT_TAB : 1];  // [0, tp): output offsets of P positions; then input offsets of Q positions
     const int nd = p.ndim;
-    const int Z = p.flat_z ? nd - 1 : -1;
-    const int P = p.ax_in, Q = nd - 1 - p.flat_z;
-    const int lr = p.run_shift;  // 0 when there is no word axis
-    const int64_t EP = p.shape[P], EQ = p.shape[Q];
-    const int64_t sP = p.istride[P], sQ = p.istride[Q];
-    int64_t oP = 1;  // output stride of P, in words
-    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    const int lr = p.run_shift;  // log2 words per element
+    const uint32_t tpn = (uint32_t)p.flat_tp, tqn = (uint32_t)p.flat_tq;
+    const int tid = threadIdx.x;
     // offsets inside a tile fit in 31 bits (checked on the host)
-    const uint32_t sP32 = (uint32_t)sP, sQ32 = (uint32_t)sQ, oP32 = (uint32_t)oP;
-    const uint32_t rw = (uint32_t)p.flat_tp << lr;  // words of a tile row (fixed q)
-    const uint32_t cw = (uint32_t)p.flat_tq << lr;  // words of a tile column (fixed p)
-    const uint32_t nw = rw * (uint32_t)p.flat_tq;   // words of a full tile, <= FLAT_WORDS
+    const uint32_t pstr32 = (uint32_t)p.fc_postr[0], qstr32 = (uint32_t)p.fc_qistr[0];
+    for (uint32_t i = tid; GROUPS && i < tpn + tqn; i += GATHER_THREADS) {
+        const bool isp = i < tpn;
+        const int n = isp ? p.fc_np : p.fc_nq;
+        uint32_t r = isp ? i : i - tpn;
+        int64_t off = 0;
+        for (int a = 0; a < n; ++a) {
+            const int ax = isp ? p.fc_pax[a] : p.fc_qax[a];
+            const int64_t st = isp ? p.fc_postr[a] : p.fc_qistr[a];
+            const uint32_t e = (uint32_t)p.shape[ax];
+            const uint32_t digit = a + 1 < n ? r % e : r;  // the outermost axis: the rest of the index
+            off += (int64_t)digit * st;
+            r = a + 1 < n ? r / e : 0;
+        }
+        tab[i] = (uint32_t)off;
+    }
+    uint32_t grp = p.flat_z ? 1u << (nd - 1) : 0u;  // axes outside the batch
+    for (int a = 0; a < p.fc_np; ++a) grp |= 1u << p.fc_pax[a];
+    for (int a = 0; a < p.fc_nq; ++a) grp |= 1u << p.fc_qax[a];
+    const int64_t pstep = p.fc_postr[p.fc_np - 1], qstep = p.fc_qistr[p.fc_nq - 1];
+    // a tile's chunk of the outermost axis of each group (tile sides are
+    // multiples of the inner axes' products)
+    const int64_t pchunk = (uint32_t)tpn / (uint32_t)p.fc_pin, qchunk = (uint32_t)tqn / (uint32_t)p.fc_qin;
+    const uint32_t rw = tpn << lr;  // words of a tile row (fixed q)
+    const uint32_t cw = tqn << lr;  // words of a tile column (fixed p)
+    const uint32_t nw = rw * tqn;   // words of a full tile, <= FLAT_WORDS
     const uint32_t ld = (uint32_t)p.flat_ld;
     const uint32_t wmask = (1u << lr) - 1;
-    const int tid = threadIdx.x;
     const int64_t per_batch = p.tiles_p * p.tiles_q;
     const int64_t nblk = per_batch * p.nbatch;
+    __syncthreads();
 
     for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
         const int64_t tq = blk % p.tiles_q;
@@ -445,7 +470,7 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
         int64_t ibase = 0, obase = 0, ostride = 1;
         for (int d = nd - 1; d >= 0; --d) {
             const int64_t e = p.shape[d];
-            if (d != P && d != Q && d != Z) {
+            if (!((grp >> d) & 1u)) {
                 const int64_t digit = bi % e;
                 bi /= e;
                 ibase += digit * p.istride[d];
@@ -453,11 +478,11 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
             }
             ostride *= e;
         }
-        const int64_t p0 = tp * p.flat_tp, q0 = tq * p.flat_tq;
-        const uint32_t np = (uint32_t)(EP - p0 < p.flat_tp ? EP - p0 : p.flat_tp);
-        const uint32_t nq = (uint32_t)(EQ - q0 < p.flat_tq ? EQ - q0 : p.flat_tq);
-        ibase += p0 * sP + q0 * sQ;         // the tile's first word in the input
-        obase += p0 * oP + (q0 << lr);      // and in the output
+        const int64_t p0 = tp * tpn, q0 = tq * tqn;
+        const uint32_t np = (uint32_t)(p.fc_ptot - p0 < tpn ? p.fc_ptot - p0 : tpn);
+        const uint32_t nq = (uint32_t)(p.fc_qtot - q0 < tqn ? p.fc_qtot - q0 : tqn);
+        ibase += (p0 << lr) + tq * qchunk * qstep;  // the tile's first word in the input
+        obase += tp * pchunk * pstep + (q0 << lr);  // and in the output
         // The per-element index math below is the same for every tile; an
         // opaque copy of the thread id keeps the compiler from hoisting all
         // 16 elements' worth of it out of the loop (150+ live registers).
@@ -471,11 +496,11 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
             const uint32_t f = tid_t + (uint32_t)i * GATHER_THREADS;
             const uint32_t ql = fdiv(f, p.fl_m1, p.fl_s1);  // f / rw
             const uint32_t rem = f - ql * rw;                // pl * R + w
-            const uint32_t pl = rem >> lr;
-            const bool ok = f < nw && pl < np && ql < nq;
+            const bool ok = f < nw && (rem >> lr) < np && ql < nq;
             slot[i] = ok ? ql * ld + rem : 0xffffffffu;
             // (an element outside the tile loads the tile's first word, which exists)
-            const uint32_t off = ok ? pl * sP32 + ql * sQ32 + (rem & wmask) : 0u;
+            const uint32_t qo = GROUPS ? tab[tpn + (ok ? ql : 0u)] : ql * qstr32;
+            const uint32_t off = ok ? rem + qo : 0u;
 #pragma unroll
             for (int t = 0; t < NT; ++t) v[t][i] = ld4(static_cast<const uint32_t*>(p.in[t]) + ibase + off);
         }
@@ -494,7 +519,7 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
             const uint32_t ql = rem >> lr;
             if (f < nw && pl < np && ql < nq) {
                 const uint32_t a = ql * ld + (pl << lr) + (rem & wmask);
-                const uint32_t off = pl * oP32 + rem;
+                const uint32_t off = rem + (GROUPS ? tab[pl] : pl * pstr32);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) st4(static_cast<uint32_t*>(p.out[t]) + obase + off, tile[t][a]);
             }

@@ -85,12 +85,18 @@ TROP_RUNS(v_n2, true, 2)
 TROP_RUNS(s_n1, false, 1)
 TROP_RUNS(s_n2, false, 2)
 
-extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_flat_n1(TropGatherParams p) {
-    gather_flat_body<1>(p);
-}
-extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_flat_n2(TropGatherParams p) {
-    gather_flat_body<2>(p);
-}
+#ifndef TROP_FLAT_WAVES
+#define TROP_FLAT_WAVES 5  // 85-87 VGPRs (5 waves per SIMD); unconstrained it took 105+
+#endif
+#define TROP_FLAT(NAME, NT, GROUPS)                                                                \
+    extern "C" __global__ __launch_bounds__(GATHER_THREADS) __attribute__((amdgpu_waves_per_eu(TROP_FLAT_WAVES))) \
+    void trop_gather_##NAME(TropGatherParams p) {                                                   \
+        gather_flat_body<NT, GROUPS>(p);                                                              \
+    }
+TROP_FLAT(flat_n1, 1, false)
+TROP_FLAT(flat_n2, 2, false)
+TROP_FLAT(flatg_n1, 1, true)
+TROP_FLAT(flatg_n2, 2, true)
 
 extern "C" __global__ __launch_bounds__(GATHER_THREADS) void trop_gather_naive(TropGatherParams p) {
     gather_naive_body(p);

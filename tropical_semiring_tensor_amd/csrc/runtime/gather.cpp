@@ -86,11 +86,15 @@ double tile_use(int64_t e, int64_t t) { return (double)e / (double)(((e + t - 1)
 // whether the last axis is the element's words) switches to the flat path
 // where that measured faster (256 MiB transposes, cold cache):
 //  - always in place of the scalar 64 x 64 tile (shapes or pointers that
-//    rule out 16-byte accesses): 0.3-1.9 TB/s there against 2.7-5.2 flat;
+//    rule out 16-byte accesses): 0.3-1.9 TB/s there against 2.6-5.2 flat;
 //  - in place of the 16-byte tiled or the runs kernel when at most half of
-//    its fixed tile is in range (a 2-wide axis fills 2/64 of a tile):
-//    e.g. a 4096 x 8 x 2048 transpose 4.05 -> 4.7 TB/s, a 2-wide one
-//    0.13 -> 4.6.
+//    its fixed tile is in range (a 2-wide axis fills 2/64 of a tile, the
+//    8 x 8 planes of an 8^8 tensor 1/64).
+// The flat tile's sides are groups of axes: the P group grows from ax_in
+// through the axes that continue it in the input, the Q group from the
+// last axis (before the element's words) towards the front of the output,
+// each until it holds 64 elements, then either while the tile is short of
+// 4096 words (at most 4 axes each).
 // `fixed_vec`: whether the tiled kernel would use 16-byte accesses (at
 // planning time, as far as shapes and strides tell).  TROPICAL_FLAT_PATH=0
 // keeps the fixed tiles; =force takes the flat path whenever its tile is
@@ -100,7 +104,9 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     if (mode && std::strcmp(mode, "0") == 0) return false;
     const bool force = mode && std::strcmp(mode, "force") == 0;
     const int nd = p.ndim, P = p.ax_in, Q = nd - 1 - z;
-    const int64_t EP = p.shape[P], EQ = p.shape[Q], R = int64_t(1) << lr;
+    const int64_t R = int64_t(1) << lr;
+    if (P == Q || P < 0 || Q < 0) return false;
+    const int64_t EP = p.shape[P], EQ = p.shape[Q];
     // share of the fixed tile in range
     double fixed;
     if (z) {
@@ -109,33 +115,84 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
         const int64_t tp = fixed_vec ? (EP >= 64 ? 64 : (EP >= 32 ? 32 : 16)) : 64;
         fixed = tile_use(EP, tp) * tile_use(EQ, fixed_vec ? 4096 / tp : 64);
     }
-    // the flat tile: the smaller side whole (or 64 x 64 when both sides are
-    // that long), the other side filled up to 4096 words, rounded down to a
-    // multiple of 32 elements (128-byte segments) where it is that long
-    const int64_t half = (4096 / 2) / R;  // leaves at least 2 along the other side
-    int64_t tp, tq;
-    if (R == 1 && EP >= 64 && EQ >= 64) {
-        tp = tq = 64;
-    } else if (EP <= EQ) {
-        tp = EP < half ? EP : half;
-        tq = 4096 / (tp * R);
-        if (tq >= 64) tq -= tq % 32;
-        if (tq > EQ) tq = EQ;
-    } else {
-        tq = EQ < half ? EQ : half;
-        tp = 4096 / (tq * R);
-        if (tp >= 64) tp -= tp % 32;
-        if (tp > EP) tp = EP;
+    // the groups
+    int pax[4] = {P, 0, 0, 0}, qax[4] = {Q, 0, 0, 0};
+    int np = 1, nq = 1;
+    int64_t pprod = EP, qprod = EQ;
+    auto taken = [&](int d) {
+        for (int a = 0; a < np; ++a)
+            if (pax[a] == d) return true;
+        for (int a = 0; a < nq; ++a)
+            if (qax[a] == d) return true;
+        return d == nd - 1 && z;
+    };
+    // both groups to 64 elements first; then, while the tile is short of
+    // 4096 words, whichever can still grow (one group may be blocked by
+    // the other: its next axis is already the other's)
+    for (int phase = 0; phase < 2; ++phase)
+    for (bool grew = true; grew;) {
+        grew = false;
+        if (phase == 1 && pprod * qprod * R >= 4096) break;
+        if ((phase == 1 || pprod < 64) && np < 4) {
+            for (int d = 0; d < nd; ++d) {
+                if (!taken(d) && p.istride[d] == pprod * R) {
+                    pax[np++] = d;
+                    pprod *= p.shape[d];
+                    grew = true;
+                    break;
+                }
+            }
+        }
+        if (phase == 1 && grew) continue;  // one axis at a time, P first
+        if ((phase == 1 || qprod < 64) && nq < 4) {
+            const int d = qax[nq - 1] - 1;
+            if (d >= 0 && !taken(d)) {
+                qax[nq++] = d;
+                qprod *= p.shape[d];
+                grew = true;
+            }
+        }
     }
-    const int64_t rw = tp * R, cw = tq * R;
+    const int64_t pin = pprod / p.shape[pax[np - 1]], qin = qprod / p.shape[qax[nq - 1]];
+    // tile: the side with fewer elements whole up to 64 (or 64 when both
+    // are longer), the other side filled up to 4096 words; each side a
+    // multiple of its inner axes' product, a multiple of 32 elements where
+    // it has no inner axes and is that long (128-byte segments)
+    auto fit = [](int64_t total, int64_t inner, int64_t cap) {
+        int64_t t = total < cap ? total : cap;
+        if (inner == 1 && t >= 64) t -= t % 32;
+        return t - t % inner;
+    };
+    const int64_t budget = 4096 / R;
+    int64_t tp, tq;
+    if (pprod <= qprod) {
+        tp = fit(pprod, pin, pprod <= 64 ? pprod : 64);
+        tq = tp > 0 ? fit(qprod, qin, budget / tp) : 0;
+    } else {
+        tq = fit(qprod, qin, qprod <= 64 ? qprod : 64);
+        tp = tq > 0 ? fit(pprod, pin, budget / tq) : 0;
+    }
+    if (tp < pin || tq < qin || tp < 1 || tq < 1) return false;
+    const int64_t rw = tp * R;
     const int64_t ld = rw % 2 == 0 ? rw + 1 : rw;
-    if (tp < 1 || tq < 2 || rw < 2 || cw < 2 || rw * tq > 4096 || tq * ld > 6144) return false;
+    const bool groups = np > 1 || nq > 1;
+    const int64_t lds = groups ? 5120 : 6144;  // the kernel's LDS tile (words)
+    if (tq * ld > lds) tq = fit(qprod, qin, lds / ld);
+    const int64_t cw = tq * R;
+    if (tq < qin || rw < 2 || cw < 2 || rw * tq > 4096 || tq * ld > lds || (groups && tp + tq > 2050)) return false;
     if (rw * tq < 512) return false;  // too little per tile: per-tile costs dominate
-    // the kernel keeps offsets inside a tile in 31 bits
-    int64_t oP = 1;
-    for (int d = P + 1; d < nd; ++d) oP *= p.shape[d];
+    // output strides (words) of the P axes; offsets inside a tile in 31 bits
+    int64_t ostr[TROP_MAX_DIMS];
+    int64_t acc = 1;
+    for (int d = nd - 1; d >= 0; --d) {
+        ostr[d] = acc;
+        acc *= p.shape[d];
+    }
     const int64_t lim = int64_t(1) << 31;
-    if ((tp - 1) * p.istride[P] + (tq - 1) * p.istride[Q] + R >= lim || (tp - 1) * oP + cw >= lim) return false;
+    int64_t pmax = (tp / pin - 1) * ostr[pax[np - 1]], qmax = (tq / qin - 1) * p.istride[qax[nq - 1]];
+    for (int a = 0; a + 1 < np; ++a) pmax += (p.shape[pax[a]] - 1) * ostr[pax[a]];
+    for (int a = 0; a + 1 < nq; ++a) qmax += (p.shape[qax[a]] - 1) * p.istride[qax[a]];
+    if (pmax + cw >= lim || qmax + rw >= lim) return false;
     const int64_t pct = env_long("TROPICAL_FLAT_MAX_FIXED_USE_PCT", 50);  // tuning knob
     const bool scalar_fixed = !z && !fixed_vec;
     if (!force && !scalar_fixed && !(fixed * 100.0 <= (double)pct)) return false;
@@ -146,9 +203,21 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     p.flat_ld = (int32_t)ld;
     magic((uint64_t)rw, &p.fl_m1, &p.fl_s1);
     magic((uint64_t)cw, &p.fl_m2, &p.fl_s2);
-    p.tiles_p = (EP + tp - 1) / tp;
-    p.tiles_q = (EQ + tq - 1) / tq;
-    p.nbatch = p.total / (EP * EQ * R);
+    p.fc_np = np;
+    p.fc_nq = nq;
+    for (int a = 0; a < 4; ++a) {
+        p.fc_pax[a] = a < np ? pax[a] : 0;
+        p.fc_qax[a] = a < nq ? qax[a] : 0;
+        p.fc_postr[a] = a < np ? ostr[pax[a]] : 0;
+        p.fc_qistr[a] = a < nq ? p.istride[qax[a]] : 0;
+    }
+    p.fc_ptot = pprod;
+    p.fc_qtot = qprod;
+    p.fc_pin = pin;
+    p.fc_qin = qin;
+    p.tiles_p = (pprod + tp - 1) / tp;
+    p.tiles_q = (qprod + tq - 1) / tq;
+    p.nbatch = p.total / (pprod * qprod * R);
     return true;
 }
 
@@ -370,8 +439,11 @@ namespace {
 // transposes against 4.4-4.9 at 4.
 trop_status launch_flat(int dev, TropGatherParams& p, int ntensors, hipStream_t stream) {
     const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
-    return launch(dev, ntensors == 2 ? K_GATHER_FLAT_N2 : K_GATHER_FLAT_N1, TROP_K_GATHER_TILED,
-                  tile_grid(dev, nblk, "TROPICAL_FLAT_BLOCKS_PER_CU", 8), 256, &p, stream);
+    const bool groups = p.fc_np > 1 || p.fc_nq > 1;
+    const KernelId kid = groups ? (ntensors == 2 ? K_GATHER_FLATG_N2 : K_GATHER_FLATG_N1)
+                                : (ntensors == 2 ? K_GATHER_FLAT_N2 : K_GATHER_FLAT_N1);
+    return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk, "TROPICAL_FLAT_BLOCKS_PER_CU", 8), 256, &p,
+                  stream);
 }
 
 }  // namespace

@@ -62,8 +62,10 @@ enum KernelId : int {
     K_GATHER_TILED2_V16_N2,
     K_GATHER_TILED2_V32_N2,
     K_GATHER_TILED2_V64_N2,
-    K_GATHER_FLAT_N1,  // flat-tile transpose (a small extent on one side)
+    K_GATHER_FLAT_N1,  // flat-tile transpose (short contiguous axes), single-axis sides
     K_GATHER_FLAT_N2,
+    K_GATHER_FLATG_N1,  // the same with groups of axes (offset tables)
+    K_GATHER_FLATG_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
