@@ -138,6 +138,52 @@ def test_trace_reduce(tb, orc, sr, dt, inl, outl, shape):
                       f"{sr} {dt} {inl}->{outl}")
 
 
+SLICE_CASES = [
+    ("ijk", "ij", (33, 20, 70)),     # reduced axis contiguous: a slice's lanes are neighbours
+    ("ijk", "jk", (300, 7, 9)),      # reduced axis outermost: lanes along the outputs
+    ("ijk", "ik", (5, 300, 9)),
+    ("ii", "", (700, 700)),          # one output, a long diagonal
+    ("iaib", "ab", (40, 3, 40, 5)),  # a diagonal reduced
+    ("abcd", "d", (6, 7, 8, 9)),     # three reduced axes
+]
+
+
+@pytest.mark.parametrize("slices", [None, 1, 2, 4, 8, 16, 64, 256])
+@pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "f32"), ("min_plus", "i32")])
+def test_reduce_slices(tb, orc, monkeypatch, slices, sr, dt):
+    """A reduction split into slices merged by (strictly better, or equal
+    with an earlier position): the same bits as the sequential scan for
+    every slice count and both lane layouts -- ties of +0 / -0 and of equal
+    values, NaN, and values equal to the zero element (which never win)."""
+    if slices:
+        monkeypatch.setenv("TROPICAL_REDUCE_SLICES", str(slices))
+    for inl, outl, shape in SLICE_CASES:
+        g = torch.Generator().manual_seed(sum(shape) + len(inl))
+        if dt == "i32":
+            x = torch.randint(-3, 4, shape, generator=g, dtype=torch.int32)
+        else:
+            x = torch.randint(-3, 4, shape, generator=g).float()
+            u = torch.rand(shape, generator=g)
+            x[u < 0.1] = -0.0
+            x[(u >= 0.1) & (u < 0.15)] = float("nan")
+            x[(u >= 0.15) & (u < 0.2)] = float("-inf") if sr == "max_plus" else float("inf")
+        out = tb.tropical_diag_gather(sr, x.to(DEV), inl, outl)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.diag_gather(sr, x.numpy(), inl, outl),
+                          f"{sr} {dt} {inl}->{outl} slices={slices}")
+    # the reductions' winners feed the routed argmax of a contraction
+    g = torch.Generator().manual_seed(17)
+    A = torch.randint(-2, 3, (4, 300, 50), generator=g).float()
+    B = torch.randint(-2, 3, (50, 20, 3), generator=g).float()
+    if dt == "i32":
+        A, B = A.to(torch.int32), B.to(torch.int32)
+    C, I = tb.tropical_contract_pair("abj,jcd->bc", sr, A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair("abj,jcd->bc", sr, A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, f"routed {sr} {dt} slices={slices}")
+    assert_equal(I.cpu().numpy(), Ir, f"routed argmax {sr} {dt} slices={slices}")
+
+
 def test_workload5_diag_full(tb, orc):
     A, _ = inputs.einsum_operands()
     out = tb.tropical_diag_gather("max_plus", A.to(DEV), "iijb", "bij")

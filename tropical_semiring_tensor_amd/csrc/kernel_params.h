@@ -119,6 +119,14 @@ struct TropGatherParams {
     int64_t rshape[TROP_MAX_DIMS];
     int64_t rstride[TROP_MAX_DIMS];
     int64_t rtotal;
+    // reduce path: red_o outputs per 256-thread workgroup, 256 / red_o
+    // slices of the reduction each; red_sfast: a slice's lanes are
+    // neighbours (the reduction's last axis has input stride 1), else the
+    // outputs' lanes are; floor(r / rshape[d]) by (rmag_m, rmag_s) when
+    // red_idx32 (every reduction index below 2^31)
+    int32_t red_o, red_sfast, red_idx32;
+    uint32_t rmag_m[TROP_MAX_DIMS];
+    uint32_t rmag_s[TROP_MAX_DIMS];
 };
 
 // Two gathers of the vectorised tiled path in one launch: workgroups

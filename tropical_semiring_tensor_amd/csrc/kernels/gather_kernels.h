@@ -542,40 +542,134 @@ __device__ __forceinline__ void gather_naive_body(const TropGatherParams& p) {
     }
 }
 
+// Reduction over labels absent from the output (trace, pre-pass (+)).
+// The semiring's (+) is a max or a min: a selection, exact in any grouping.
+// The sequential definition -- start from the zero element, take a value
+// only when strictly better -- yields the first position (row-major over
+// the reduced axes) whose value equals the extreme, or the zero element
+// with position 0 when nothing beats it (NaN never does).  Here each output
+// is reduced by 256 / red_o threads, each over an interleaved slice of the
+// positions in ascending order, and the slices' (value, position) pairs
+// are merged with "strictly better, or equal with an earlier position":
+// the same first position, the same bits (+0 against -0 included), in any
+// grouping.  Slices merge by wave shuffles, then (across waves) in LDS.
+template <int SR, typename T>
+__device__ __forceinline__ void reduce_merge(T& b, int64_t& w, T v, int64_t r) {
+    using R = Ring<SR, T>;
+    // w < 0: nothing beat the zero element yet; a real partial (r >= 0) is
+    // strictly better than the zero element, and never NaN
+    if (r < 0) return;
+    if (w < 0 || R::better(v, b) || (!R::better(b, v) && r < w)) {
+        b = v;
+        w = r;
+    }
+}
+
+template <int SR, typename T>
+__device__ __forceinline__ T shfl_xor_t(T v, int m) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __shfl_xor(__builtin_bit_cast(int, v), m));
+    }
+}
+
 template <int SR, typename T>
 __device__ __forceinline__ void gather_reduce_body(const TropGatherParams& p) {
     using R = Ring<SR, T>;
+    __shared__ T part_v[GATHER_THREADS];
+    __shared__ int64_t part_r[GATHER_THREADS];
     const T* in = static_cast<const T*>(p.in[0]);
     T* out = static_cast<T*>(p.out[0]);
-    // with ntensors = 2, out[1] receives each output's winner: the position
-    // (row-major over the reduced axes) of the first strictly better value,
-    // 0 when nothing beats the zero element
+    // with ntensors = 2, out[1] receives each output's winner position
     int32_t* win_out = p.ntensors == 2 ? static_cast<int32_t*>(p.out[1]) : nullptr;
-    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < p.total;
-         o += (int64_t)gridDim.x * blockDim.x) {
-        int64_t rem = o, base = 0;
-        for (int d = p.ndim - 1; d >= 0; --d) {
-            const int64_t e = p.shape[d];
-            base += (rem % e) * p.istride[d];
-            rem /= e;
-        }
+    const int O = p.red_o, S = GATHER_THREADS / O;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool sfast = p.red_sfast != 0;
+    const int ol = sfast ? tid / S : tid % O;  // output of this thread within the block
+    const int s = sfast ? tid % S : tid / O;   // its slice
+    for (int64_t ob = (int64_t)blockIdx.x * O; ob < p.total; ob += (int64_t)gridDim.x * O) {
+        const int64_t o = ob + ol;
         T best = R::zero();
-        int64_t win = 0;
-        for (int64_t r = 0; r < p.rtotal; ++r) {
-            int64_t rr = r, off = base;
-            for (int d = p.nred - 1; d >= 0; --d) {
-                const int64_t e = p.rshape[d];
-                off += (rr % e) * p.rstride[d];
-                rr /= e;
+        int64_t win = -1;
+        if (o < p.total) {
+            int64_t rem = o, base = 0;
+            for (int d = p.ndim - 1; d >= 0; --d) {
+                const int64_t e = p.shape[d];
+                base += (rem % e) * p.istride[d];
+                rem /= e;
             }
-            const T v = in[off];
-            if (R::better(v, best)) {
-                best = v;
-                win = r;
+            auto offset = [&](int64_t r) -> int64_t {
+                if (p.nred == 1) return r * p.rstride[0];
+                int64_t off = 0;
+                if (p.red_idx32) {
+                    uint32_t rr = (uint32_t)r;
+                    for (int d = p.nred - 1; d >= 0; --d) {
+                        const uint32_t q = fdiv(rr, p.rmag_m[d], p.rmag_s[d]);
+                        off += (int64_t)(rr - q * (uint32_t)p.rshape[d]) * p.rstride[d];
+                        rr = q;
+                    }
+                } else {
+                    int64_t rr = r;
+                    for (int d = p.nred - 1; d >= 0; --d) {
+                        off += (rr % p.rshape[d]) * p.rstride[d];
+                        rr /= p.rshape[d];
+                    }
+                }
+                return off;
+            };
+            // four positions' loads in flight, then taken in ascending order
+            int64_t r = s;
+            for (; r + 3 * (int64_t)S < p.rtotal; r += 4 * (int64_t)S) {
+                T v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = in[base + offset(r + u * (int64_t)S)];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (R::better(v[u], best)) {
+                        best = v[u];
+                        win = r + u * (int64_t)S;
+                    }
+            }
+            for (; r < p.rtotal; r += S) {
+                const T v = in[base + offset(r)];
+                if (R::better(v, best)) {
+                    best = v;
+                    win = r;
+                }
             }
         }
-        out[o] = best;
-        if (win_out) win_out[o] = (int32_t)win;
+        // merge the slices of each output: inside the wave by shuffles
+        // (sfast: the S lanes of an output are neighbours; else, with
+        // O < 64, lanes O apart share an output), then across the waves in
+        // LDS (the butterfly leaves every lane with its wave's merge)
+        const int lo = sfast ? 1 : O, hi = sfast ? S : 64;
+        for (int m = lo; m < hi; m <<= 1) {
+            const T v = shfl_xor_t<SR, T>(best, m);
+            const int64_t rr = __shfl_xor(win, m);
+            reduce_merge<SR, T>(best, win, v, rr);
+        }
+        if (sfast || S == 1) {
+            // the output's slices were all in this wave (sfast: S <= 64)
+            if (o < p.total && s == 0) {
+                out[o] = best;
+                if (win_out) win_out[o] = (int32_t)(win < 0 ? 0 : win);
+            }
+        } else {
+            part_v[tid] = best;
+            part_r[tid] = win;
+            __syncthreads();
+            if (tid < O && ob + tid < p.total) {
+                // O < 64: lane tid of each wave holds that wave's merge;
+                // else the S slices sit O threads apart
+                const int n = O < 64 ? GATHER_THREADS / 64 : S;
+                const int step = O < 64 ? 64 : O;
+                T b = part_v[tid];
+                int64_t w = part_r[tid];
+                for (int q = 1; q < n; ++q) reduce_merge<SR, T>(b, w, part_v[tid + q * step], part_r[tid + q * step]);
+                out[ob + tid] = b;
+                if (win_out) win_out[ob + tid] = (int32_t)(w < 0 ? 0 : w);
+            }
+            __syncthreads();
+        }
     }
 }
 

@@ -305,6 +305,24 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
     p.rtotal = rtotal;
     if (nr > 0 || rtotal == 0) {
         plan->path = GP_REDUCE;
+        // Slices per output: doubled while the grid is short of 256k threads
+        // and the reduction has two positions per slice, at most 64 when a
+        // slice's lanes are neighbours (the reduction's last axis has input
+        // stride 1: coalesced along it), else 256.  One thread per output
+        // reading a long reduction alone ran at 0.2 TB/s (a 2048-long max
+        // over an outer axis) and took 4.6 ms for the trace of an 8192^2
+        // matrix.
+        const bool sfast = nr > 0 && p.rstride[nr - 1] == 1 && rtotal >= 8;
+        const int64_t smax = sfast ? 64 : 256;
+        int64_t S = 1;
+        while (S < smax && total * S < 256 * 1024 && 2 * S <= rtotal) S *= 2;
+        const long forced = env_long("TROPICAL_REDUCE_SLICES", 0);  // tests: 1 .. smax, a power of two
+        if (forced > 0 && forced <= smax && (forced & (forced - 1)) == 0) S = forced;
+        p.red_o = (int32_t)(256 / S);
+        p.red_sfast = sfast && S > 1 ? 1 : 0;
+        p.red_idx32 = rtotal < (int64_t(1) << 31) ? 1 : 0;
+        for (int d = 0; d < nr && p.red_idx32; ++d)
+            if (p.rshape[d] >= 2) magic((uint64_t)p.rshape[d], &p.rmag_m[d], &p.rmag_s[d]);
         return TROP_OK;
     }
     if (env_flag("TROPICAL_FORCE_NAIVE_PERMUTE")) {
@@ -534,7 +552,7 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
             const int ri = ring_index(sr, dt);
             if (ri < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
             return launch(dev, (KernelId)(K_GATHER_REDUCE_MAXPLUS_F32 + ri), TROP_K_GATHER_REDUCE,
-                          grid_for(p.total, 256), 256, &p, stream);
+                          grid_for(p.total, p.red_o), 256, &p, stream);
         }
     }
     return fail(TROP_ERR_INVALID_ARGUMENT, "bad gather plan");
