@@ -369,6 +369,13 @@ FLAT = [
     ((16, 2, 2050), (0, 2, 1)),
     ((9, 4, 1500), (2, 0, 1)),    # Q = 4 whose rows are apart in the output
     ((3, 5, 11, 300), (0, 3, 2, 1)),
+    # batched transposes of small matrices: tiles of several whole blocks
+    ((999, 8, 8), (0, 2, 1)),
+    ((4097, 2, 2), (0, 2, 1)),
+    ((777, 2, 3), (0, 2, 1)),
+    ((333, 5, 6, 7), (0, 3, 1, 2)),
+    ((16, 16, 16, 16, 16), (0, 1, 2, 4, 3)),
+    ((3, 1500, 4, 4), (0, 1, 3, 2)),
 ]
 
 
@@ -397,7 +404,8 @@ def test_permute_flat_path(tb, orc, monkeypatch, mode, shape, perm):
 @pytest.mark.parametrize("dt", [torch.float64, torch.complex64, torch.complex128],
                          ids=lambda d: str(d).replace("torch.", ""))
 @pytest.mark.parametrize("shape,perm", [((3001, 2), (1, 0)), ((2, 3001), (1, 0)), ((7, 3, 501), (2, 1, 0)),
-                                        ((4, 640, 5), (0, 2, 1))], ids=lambda v: str(v))
+                                        ((4, 640, 5), (0, 2, 1)), ((1001, 4, 4), (0, 2, 1)),
+                                        ((555, 3, 2), (0, 2, 1))], ids=lambda v: str(v))
 def test_permute_flat_path_wide_elements(tb, orc, dt, shape, perm):
     """Wide elements on the flat path: each element's words stay together
     (2 or 4 words per element), pairs with an int64 index."""

@@ -114,6 +114,17 @@ struct TropGatherParams {
     int32_t fc_pax[4], fc_qax[4];
     int64_t fc_postr[4], fc_qistr[4];
     int64_t fc_ptot, fc_qtot, fc_pin, fc_qin;
+    // blocks: when the whole P x Q block is small and the output axis
+    // fc_xax just outside it steps by the block (fc_xstr words) in the
+    // input and in the output, a tile holds flat_nx consecutive blocks
+    // (fc_xax = -1, flat_nx = 1: none); floor(f / block words) by
+    // (fl_m3, fl_s3)
+    int32_t fc_xax, flat_nx;
+    int64_t fc_xstr, tiles_x;
+    uint32_t fl_m3, fl_s3;
+    // floor(n / tiles_q), floor(n / tiles_p), floor(n / tiles_x) by magic
+    // pairs (for idx32 plans; a divisor of 1 is taken as is)
+    uint32_t tl_m[3], tl_s[3];
     // reduction (trace)
     int32_t nred;
     int64_t rshape[TROP_MAX_DIMS];

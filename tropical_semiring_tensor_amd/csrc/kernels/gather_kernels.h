@@ -409,7 +409,10 @@ __device__ __forceinline__ void gather_tiled_body(const TropGatherParams& p) {
 // P position p is input word p R and a Q position q output word q R.  The
 // other side's offsets (output offsets of the P positions, input offsets
 // of the Q positions) are the same for every tile and sit in an LDS table
-// built once per workgroup.  The read phase walks the tile in input order
+// built once per workgroup.  When the whole P x Q block is small (a batched
+// transpose of 16 x 16 matrices) and the axis just outside it steps by the
+// block in the input and in the output, a tile holds several consecutive
+// blocks.  The read phase walks the tile in input order
 // (q, then p, then the word) and the write phase in output order (p, then
 // q, then the word), so each side moves in contiguous segments.  The LDS
 // row of a fixed q is flat_ld words (odd: the write phase's column walk is
@@ -422,7 +425,10 @@ constexpr int FLAT_LDS_GROUPS = 5120;  // the same with the table beside it
 constexpr int FLAT_TAB = 2050;         // >= flat_tp + flat_tq (checked on the host)
 constexpr int FLAT_PER_THREAD = FLAT_WORDS / GATHER_THREADS;
 
-template <int NT, bool GROUPS>
+// BLOCKS = false: one P x Q block per tile (flat_nx = 1); the block index
+// math is compiled out (the kernel is close to VALU-bound: ~20 VALU per
+// word moved at ~2 words per clock per CU each way).
+template <int NT, bool GROUPS, bool BLOCKS>
 __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
     __shared__ uint32_t tile[NT][GROUPS ? FLAT_LDS_GROUPS : FLAT_LDS_AXES];
     __shared__ uint32_t tab[GROUPS ? FLAT_TAB : 1];  // [0, tp): output offsets of P positions; then input offsets of Q positions
@@ -450,39 +456,73 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
     uint32_t grp = p.flat_z ? 1u << (nd - 1) : 0u;  // axes outside the batch
     for (int a = 0; a < p.fc_np; ++a) grp |= 1u << p.fc_pax[a];
     for (int a = 0; a < p.fc_nq; ++a) grp |= 1u << p.fc_qax[a];
+    if (p.fc_xax >= 0) grp |= 1u << p.fc_xax;
     const int64_t pstep = p.fc_postr[p.fc_np - 1], qstep = p.fc_qistr[p.fc_nq - 1];
     // a tile's chunk of the outermost axis of each group (tile sides are
     // multiples of the inner axes' products)
     const int64_t pchunk = (uint32_t)tpn / (uint32_t)p.fc_pin, qchunk = (uint32_t)tqn / (uint32_t)p.fc_qin;
     const uint32_t rw = tpn << lr;  // words of a tile row (fixed q)
     const uint32_t cw = tqn << lr;  // words of a tile column (fixed p)
-    const uint32_t nw = rw * tqn;   // words of a full tile, <= FLAT_WORDS
+    const uint32_t nwb = rw * tqn;  // words of one P x Q block
+    const uint32_t nx = BLOCKS ? (uint32_t)p.flat_nx : 1u;
+    const uint32_t nw = nwb * nx;   // words of a full tile, <= FLAT_WORDS
     const uint32_t ld = (uint32_t)p.flat_ld;
+    const uint32_t lb = tqn * ld;   // LDS words of one block
     const uint32_t wmask = (1u << lr) - 1;
-    const int64_t per_batch = p.tiles_p * p.tiles_q;
+    const int64_t bstr = p.fc_xstr;
+    const int64_t EX = p.fc_xax >= 0 ? p.shape[p.fc_xax] : 1;
+    const int64_t per_batch = p.tiles_p * p.tiles_q * p.tiles_x;
     const int64_t nblk = per_batch * p.nbatch;
     __syncthreads();
 
     for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t tq = blk % p.tiles_q;
-        const int64_t tp = (blk / p.tiles_q) % p.tiles_p;
-        int64_t bi = blk / per_batch;
+        int64_t tq, tp, tx;
         int64_t ibase = 0, obase = 0, ostride = 1;
-        for (int d = nd - 1; d >= 0; --d) {
-            const int64_t e = p.shape[d];
-            if (!((grp >> d) & 1u)) {
-                const int64_t digit = bi % e;
-                bi /= e;
-                ibase += digit * p.istride[d];
-                obase += digit * ostride;
+        if (p.idx32) {
+            // every tile index is below 2^31: 32-bit magic divisions (the
+            // 64-bit ones are long software sequences, per tile)
+            auto div = [](uint32_t n, int64_t d, uint32_t m, uint32_t sh) { return d == 1 ? n : fdiv(n, m, sh); };
+            const uint32_t b = (uint32_t)blk;
+            const uint32_t b1 = div(b, p.tiles_q, p.tl_m[0], p.tl_s[0]);
+            const uint32_t b2 = div(b1, p.tiles_p, p.tl_m[1], p.tl_s[1]);
+            uint32_t bi = div(b2, p.tiles_x, p.tl_m[2], p.tl_s[2]);
+            tq = b - b1 * (uint32_t)p.tiles_q;
+            tp = b1 - b2 * (uint32_t)p.tiles_p;
+            tx = b2 - bi * (uint32_t)p.tiles_x;
+            for (int d = nd - 1; d >= 0; --d) {
+                const int64_t e = p.shape[d];
+                if (!((grp >> d) & 1u)) {
+                    const uint32_t q = fdiv(bi, p.mag_m[d], p.mag_s[d]);  // batch axes have extents >= 2
+                    const uint32_t digit = bi - q * (uint32_t)e;
+                    bi = q;
+                    ibase += (int64_t)digit * p.istride[d];
+                    obase += (int64_t)digit * ostride;
+                }
+                ostride *= e;
             }
-            ostride *= e;
+        } else {
+            tq = blk % p.tiles_q;
+            tp = (blk / p.tiles_q) % p.tiles_p;
+            tx = (blk / (p.tiles_q * p.tiles_p)) % p.tiles_x;
+            int64_t bi = blk / per_batch;
+            for (int d = nd - 1; d >= 0; --d) {
+                const int64_t e = p.shape[d];
+                if (!((grp >> d) & 1u)) {
+                    const int64_t digit = bi % e;
+                    bi /= e;
+                    ibase += digit * p.istride[d];
+                    obase += digit * ostride;
+                }
+                ostride *= e;
+            }
         }
         const int64_t p0 = tp * tpn, q0 = tq * tqn;
         const uint32_t np = (uint32_t)(p.fc_ptot - p0 < tpn ? p.fc_ptot - p0 : tpn);
         const uint32_t nq = (uint32_t)(p.fc_qtot - q0 < tqn ? p.fc_qtot - q0 : tqn);
-        ibase += (p0 << lr) + tq * qchunk * qstep;  // the tile's first word in the input
-        obase += tp * pchunk * pstep + (q0 << lr);  // and in the output
+        const int64_t x0 = tx * nx;
+        const uint32_t nxv = (uint32_t)(EX - x0 < nx ? EX - x0 : nx);  // blocks in range
+        ibase += (p0 << lr) + tq * qchunk * qstep + x0 * bstr;  // the tile's first word in the input
+        obase += tp * pchunk * pstep + (q0 << lr) + x0 * bstr;  // and in the output
         // The per-element index math below is the same for every tile; an
         // opaque copy of the thread id keeps the compiler from hoisting all
         // 16 elements' worth of it out of the loop (150+ live registers).
@@ -494,13 +534,15 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
 #pragma unroll
         for (int i = 0; i < FLAT_PER_THREAD; ++i) {
             const uint32_t f = tid_t + (uint32_t)i * GATHER_THREADS;
-            const uint32_t ql = fdiv(f, p.fl_m1, p.fl_s1);  // f / rw
-            const uint32_t rem = f - ql * rw;                // pl * R + w
-            const bool ok = f < nw && (rem >> lr) < np && ql < nq;
-            slot[i] = ok ? ql * ld + rem : 0xffffffffu;
+            const uint32_t xb = BLOCKS ? fdiv(f, p.fl_m3, p.fl_s3) : 0u;  // block: f / nwb
+            const uint32_t fb = f - xb * nwb;
+            const uint32_t ql = fdiv(fb, p.fl_m1, p.fl_s1);  // fb / rw
+            const uint32_t rem = fb - ql * rw;                // pl * R + w
+            const bool ok = f < nw && (!BLOCKS || xb < nxv) && (rem >> lr) < np && ql < nq;
+            slot[i] = ok ? xb * lb + ql * ld + rem : 0xffffffffu;
             // (an element outside the tile loads the tile's first word, which exists)
             const uint32_t qo = GROUPS ? tab[tpn + (ok ? ql : 0u)] : ql * qstr32;
-            const uint32_t off = ok ? rem + qo : 0u;
+            const uint32_t off = ok ? (uint32_t)(xb * bstr) + rem + qo : 0u;
 #pragma unroll
             for (int t = 0; t < NT; ++t) v[t][i] = ld4(static_cast<const uint32_t*>(p.in[t]) + ibase + off);
         }
@@ -514,12 +556,14 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
 #pragma unroll
         for (int i = 0; i < FLAT_PER_THREAD; ++i) {
             const uint32_t f = tid_t + (uint32_t)i * GATHER_THREADS;
-            const uint32_t pl = fdiv(f, p.fl_m2, p.fl_s2);  // f / cw
-            const uint32_t rem = f - pl * cw;                // ql * R + w
+            const uint32_t xb = BLOCKS ? fdiv(f, p.fl_m3, p.fl_s3) : 0u;  // block: f / nwb
+            const uint32_t fb = f - xb * nwb;
+            const uint32_t pl = fdiv(fb, p.fl_m2, p.fl_s2);  // fb / cw
+            const uint32_t rem = fb - pl * cw;                // ql * R + w
             const uint32_t ql = rem >> lr;
-            if (f < nw && pl < np && ql < nq) {
-                const uint32_t a = ql * ld + (pl << lr) + (rem & wmask);
-                const uint32_t off = rem + (GROUPS ? tab[pl] : pl * pstr32);
+            if (f < nw && (!BLOCKS || xb < nxv) && pl < np && ql < nq) {
+                const uint32_t a = xb * lb + ql * ld + (pl << lr) + (rem & wmask);
+                const uint32_t off = (uint32_t)(xb * bstr) + rem + (GROUPS ? tab[pl] : pl * pstr32);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) st4(static_cast<uint32_t*>(p.out[t]) + obase + off, tile[t][a]);
             }

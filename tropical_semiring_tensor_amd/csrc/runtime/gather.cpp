@@ -94,7 +94,8 @@ double tile_use(int64_t e, int64_t t) { return (double)e / (double)(((e + t - 1)
 // through the axes that continue it in the input, the Q group from the
 // last axis (before the element's words) towards the front of the output,
 // each until it holds 64 elements, then either while the tile is short of
-// 4096 words (at most 4 axes each).
+// 4096 words (at most 4 axes each); a small whole block is repeated along
+// the axis just outside it where that axis is contiguous on both sides.
 // `fixed_vec`: whether the tiled kernel would use 16-byte accesses (at
 // planning time, as far as shapes and strides tell).  TROPICAL_FLAT_PATH=0
 // keeps the fixed tiles; =force takes the flat path whenever its tile is
@@ -180,7 +181,34 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     if (tq * ld > lds) tq = fit(qprod, qin, lds / ld);
     const int64_t cw = tq * R;
     if (tq < qin || rw < 2 || cw < 2 || rw * tq > 4096 || tq * ld > lds || (groups && tp + tq > 2050)) return false;
-    if (rw * tq < 512) return false;  // too little per tile: per-tile costs dominate
+    // blocks: with the whole P x Q block in a tile and short of 4096 words,
+    // the output axis just outside it (every later output axis is in a
+    // group) can hold several blocks when it steps by one dense block in
+    // the input too (its output stride is the block by construction)
+    int xax = -1;
+    int64_t nx = 1, bsz = 0;
+    const int last = nd - 1 - z;
+    if (tp == pprod && tq == qprod && 2 * rw * tq <= 4096) {
+        int m = nd;
+        int64_t mx = R - 1;  // the block's last word, relative to its first
+        for (int a = 0; a < np; ++a) {
+            m = pax[a] < m ? pax[a] : m;
+            mx += (p.shape[pax[a]] - 1) * p.istride[pax[a]];
+        }
+        for (int a = 0; a < nq; ++a) {
+            m = qax[a] < m ? qax[a] : m;
+            mx += (p.shape[qax[a]] - 1) * p.istride[qax[a]];
+        }
+        const int64_t blk = rw * tq;
+        if (m >= 1 && np + nq == last - m + 1 && mx + 1 == blk && p.istride[m - 1] == blk) {
+            xax = m - 1;
+            bsz = blk;
+            nx = 4096 / blk;
+            if (nx * tq * ld > lds) nx = lds / (tq * ld);
+            if (nx > p.shape[xax]) nx = p.shape[xax];
+        }
+    }
+    if (rw * tq * nx < 512) return false;  // too little per tile: per-tile costs dominate
     // output strides (words) of the P axes; offsets inside a tile in 31 bits
     int64_t ostr[TROP_MAX_DIMS];
     int64_t acc = 1;
@@ -192,7 +220,7 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     int64_t pmax = (tp / pin - 1) * ostr[pax[np - 1]], qmax = (tq / qin - 1) * p.istride[qax[nq - 1]];
     for (int a = 0; a + 1 < np; ++a) pmax += (p.shape[pax[a]] - 1) * ostr[pax[a]];
     for (int a = 0; a + 1 < nq; ++a) qmax += (p.shape[qax[a]] - 1) * p.istride[qax[a]];
-    if (pmax + cw >= lim || qmax + rw >= lim) return false;
+    if (pmax + cw >= lim || qmax + rw >= lim || nx * bsz >= lim) return false;
     const int64_t pct = env_long("TROPICAL_FLAT_MAX_FIXED_USE_PCT", 50);  // tuning knob
     const bool scalar_fixed = !z && !fixed_vec;
     if (!force && !scalar_fixed && !(fixed * 100.0 <= (double)pct)) return false;
@@ -217,7 +245,16 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     p.fc_qin = qin;
     p.tiles_p = (pprod + tp - 1) / tp;
     p.tiles_q = (qprod + tq - 1) / tq;
-    p.nbatch = p.total / (pprod * qprod * R);
+    p.fc_xax = xax;
+    p.flat_nx = (int32_t)nx;
+    p.fc_xstr = bsz;
+    magic((uint64_t)(rw * tq), &p.fl_m3, &p.fl_s3);
+    const int64_t ex = xax >= 0 ? p.shape[xax] : 1;
+    p.tiles_x = (ex + nx - 1) / nx;
+    p.nbatch = p.total / (pprod * qprod * R * ex);
+    const int64_t tl[3] = {p.tiles_q, p.tiles_p, p.tiles_x};
+    for (int i = 0; i < 3; ++i)
+        if (tl[i] >= 2 && p.idx32) magic((uint64_t)tl[i], &p.tl_m[i], &p.tl_s[i]);
     return true;
 }
 
@@ -456,10 +493,11 @@ namespace {
 // registers) balanced the tiles best: 8 per CU measured 5.2 TB/s on 2-wide
 // transposes against 4.4-4.9 at 4.
 trop_status launch_flat(int dev, TropGatherParams& p, int ntensors, hipStream_t stream) {
-    const int64_t nblk = p.tiles_p * p.tiles_q * p.nbatch;
-    const bool groups = p.fc_np > 1 || p.fc_nq > 1;
-    const KernelId kid = groups ? (ntensors == 2 ? K_GATHER_FLATG_N2 : K_GATHER_FLATG_N1)
-                                : (ntensors == 2 ? K_GATHER_FLAT_N2 : K_GATHER_FLAT_N1);
+    const int64_t nblk = p.tiles_p * p.tiles_q * p.tiles_x * p.nbatch;
+    const bool groups = p.fc_np > 1 || p.fc_nq > 1, blocks = p.flat_nx > 1;
+    const int n2 = ntensors == 2 ? 1 : 0;
+    const KernelId kid = (KernelId)((blocks ? (groups ? K_GATHER_FLATGB_N1 : K_GATHER_FLATB_N1)
+                                            : (groups ? K_GATHER_FLATG_N1 : K_GATHER_FLAT_N1)) + n2);
     return launch(dev, kid, TROP_K_GATHER_TILED, tile_grid(dev, nblk, "TROPICAL_FLAT_BLOCKS_PER_CU", 8), 256, &p,
                   stream);
 }

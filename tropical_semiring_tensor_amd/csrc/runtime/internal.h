@@ -66,6 +66,10 @@ enum KernelId : int {
     K_GATHER_FLAT_N2,
     K_GATHER_FLATG_N1,  // the same with groups of axes (offset tables)
     K_GATHER_FLATG_N2,
+    K_GATHER_FLATB_N1,  // several P x Q blocks per tile, single-axis sides
+    K_GATHER_FLATB_N2,
+    K_GATHER_FLATGB_N1,  // several blocks per tile, groups of axes
+    K_GATHER_FLATGB_N2,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
