@@ -376,6 +376,11 @@ FLAT = [
     ((333, 5, 6, 7), (0, 3, 1, 2)),
     ((16, 16, 16, 16, 16), (0, 1, 2, 4, 3)),
     ((3, 1500, 4, 4), (0, 1, 3, 2)),
+    # the block transposed in place with the axis outside it moved: blocks
+    # contiguous in the input only / in the output only
+    ((16, 16, 16, 16, 16), (2, 0, 1, 4, 3)),
+    ((8, 8, 60, 3, 4), (2, 0, 1, 4, 3)),
+    ((40, 6, 5), (1, 2, 0)),
 ]
 
 

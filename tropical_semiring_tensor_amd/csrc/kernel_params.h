@@ -114,13 +114,13 @@ struct TropGatherParams {
     int32_t fc_pax[4], fc_qax[4];
     int64_t fc_postr[4], fc_qistr[4];
     int64_t fc_ptot, fc_qtot, fc_pin, fc_qin;
-    // blocks: when the whole P x Q block is small and the output axis
-    // fc_xax just outside it steps by the block (fc_xstr words) in the
-    // input and in the output, a tile holds flat_nx consecutive blocks
-    // (fc_xax = -1, flat_nx = 1: none); floor(f / block words) by
-    // (fl_m3, fl_s3)
+    // blocks: when the whole P x Q block is small, a tile holds flat_nx
+    // consecutive blocks along the axis fc_xax, which steps by fc_xstr
+    // words in the input and fc_xostr in the output (one of them the
+    // block itself: blocks adjacent on that side); fc_xax = -1,
+    // flat_nx = 1: none; floor(f / block words) by (fl_m3, fl_s3)
     int32_t fc_xax, flat_nx;
-    int64_t fc_xstr, tiles_x;
+    int64_t fc_xstr, fc_xostr, tiles_x;
     uint32_t fl_m3, fl_s3;
     // floor(n / tiles_q), floor(n / tiles_p), floor(n / tiles_x) by magic
     // pairs (for idx32 plans; a divisor of 1 is taken as is)

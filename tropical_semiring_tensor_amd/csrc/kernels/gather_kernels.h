@@ -410,9 +410,9 @@ __device__ __forceinline__ void gather_tiled_body(const TropGatherParams& p) {
 // other side's offsets (output offsets of the P positions, input offsets
 // of the Q positions) are the same for every tile and sit in an LDS table
 // built once per workgroup.  When the whole P x Q block is small (a batched
-// transpose of 16 x 16 matrices) and the axis just outside it steps by the
-// block in the input and in the output, a tile holds several consecutive
-// blocks.  The read phase walks the tile in input order
+// transpose of 16 x 16 matrices) and another axis steps from block to
+// block in the input or in the output, a tile holds several consecutive
+// blocks along it.  The read phase walks the tile in input order
 // (q, then p, then the word) and the write phase in output order (p, then
 // q, then the word), so each side moves in contiguous segments.  The LDS
 // row of a fixed q is flat_ld words (odd: the write phase's column walk is
@@ -469,7 +469,7 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
     const uint32_t ld = (uint32_t)p.flat_ld;
     const uint32_t lb = tqn * ld;   // LDS words of one block
     const uint32_t wmask = (1u << lr) - 1;
-    const int64_t bstr = p.fc_xstr;
+    const int64_t bstr = p.fc_xstr, bostr = p.fc_xostr;
     const int64_t EX = p.fc_xax >= 0 ? p.shape[p.fc_xax] : 1;
     const int64_t per_batch = p.tiles_p * p.tiles_q * p.tiles_x;
     const int64_t nblk = per_batch * p.nbatch;
@@ -521,8 +521,8 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
         const uint32_t nq = (uint32_t)(p.fc_qtot - q0 < tqn ? p.fc_qtot - q0 : tqn);
         const int64_t x0 = tx * nx;
         const uint32_t nxv = (uint32_t)(EX - x0 < nx ? EX - x0 : nx);  // blocks in range
-        ibase += (p0 << lr) + tq * qchunk * qstep + x0 * bstr;  // the tile's first word in the input
-        obase += tp * pchunk * pstep + (q0 << lr) + x0 * bstr;  // and in the output
+        ibase += (p0 << lr) + tq * qchunk * qstep + x0 * bstr;   // the tile's first word in the input
+        obase += tp * pchunk * pstep + (q0 << lr) + x0 * bostr;  // and in the output
         // The per-element index math below is the same for every tile; an
         // opaque copy of the thread id keeps the compiler from hoisting all
         // 16 elements' worth of it out of the loop (150+ live registers).
@@ -563,7 +563,7 @@ __device__ __forceinline__ void gather_flat_body(const TropGatherParams& p) {
             const uint32_t ql = rem >> lr;
             if (f < nw && (!BLOCKS || xb < nxv) && pl < np && ql < nq) {
                 const uint32_t a = xb * lb + ql * ld + (pl << lr) + (rem & wmask);
-                const uint32_t off = (uint32_t)(xb * bstr) + rem + (GROUPS ? tab[pl] : pl * pstr32);
+                const uint32_t off = (uint32_t)(xb * bostr) + rem + (GROUPS ? tab[pl] : pl * pstr32);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) st4(static_cast<uint32_t*>(p.out[t]) + obase + off, tile[t][a]);
             }

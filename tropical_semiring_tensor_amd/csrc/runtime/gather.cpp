@@ -95,7 +95,7 @@ double tile_use(int64_t e, int64_t t) { return (double)e / (double)(((e + t - 1)
 // last axis (before the element's words) towards the front of the output,
 // each until it holds 64 elements, then either while the tile is short of
 // 4096 words (at most 4 axes each); a small whole block is repeated along
-// the axis just outside it where that axis is contiguous on both sides.
+// an axis that steps from block to block on at least one side.
 // `fixed_vec`: whether the tiled kernel would use 16-byte accesses (at
 // planning time, as far as shapes and strides tell).  TROPICAL_FLAT_PATH=0
 // keeps the fixed tiles; =force takes the flat path whenever its tile is
@@ -181,16 +181,25 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     if (tq * ld > lds) tq = fit(qprod, qin, lds / ld);
     const int64_t cw = tq * R;
     if (tq < qin || rw < 2 || cw < 2 || rw * tq > 4096 || tq * ld > lds || (groups && tp + tq > 2050)) return false;
+    // output strides (words)
+    int64_t ostr[TROP_MAX_DIMS];
+    int64_t acc = 1;
+    for (int d = nd - 1; d >= 0; --d) {
+        ostr[d] = acc;
+        acc *= p.shape[d];
+    }
     // blocks: with the whole P x Q block in a tile and short of 4096 words,
-    // the output axis just outside it (every later output axis is in a
-    // group) can hold several blocks when it steps by one dense block in
-    // the input too (its output stride is the block by construction)
+    // a tile holds several blocks along an axis that steps by one block on
+    // at least one side: first one contiguous on both sides (the output
+    // axis just outside the block, every later output axis in a group,
+    // stepping by the dense block in the input too), then one contiguous
+    // in the input, then the output axis just outside the block
     int xax = -1;
-    int64_t nx = 1, bsz = 0;
+    int64_t nx = 1, bsz = 0, bosz = 0;
     const int last = nd - 1 - z;
     if (tp == pprod && tq == qprod && 2 * rw * tq <= 4096) {
         int m = nd;
-        int64_t mx = R - 1;  // the block's last word, relative to its first
+        int64_t mx = R - 1;  // the block's last word in the input, relative to its first
         for (int a = 0; a < np; ++a) {
             m = pax[a] < m ? pax[a] : m;
             mx += (p.shape[pax[a]] - 1) * p.istride[pax[a]];
@@ -200,27 +209,31 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
             mx += (p.shape[qax[a]] - 1) * p.istride[qax[a]];
         }
         const int64_t blk = rw * tq;
-        if (m >= 1 && np + nq == last - m + 1 && mx + 1 == blk && p.istride[m - 1] == blk) {
+        const bool in_dense = mx + 1 == blk;
+        const bool out_adj = m >= 1 && np + nq == last - m + 1;  // axis m - 1 steps by the block in the output
+        if (out_adj && in_dense && p.istride[m - 1] == blk) {
             xax = m - 1;
-            bsz = blk;
+        } else {
+            for (int d = 0; d < nd && in_dense && xax < 0; ++d)
+                if (!taken(d) && p.istride[d] == blk) xax = d;
+            if (xax < 0 && out_adj) xax = m - 1;
+        }
+        if (xax >= 0) {
+            bsz = p.istride[xax];
+            bosz = ostr[xax];
             nx = 4096 / blk;
             if (nx * tq * ld > lds) nx = lds / (tq * ld);
             if (nx > p.shape[xax]) nx = p.shape[xax];
+            if (nx < 2) xax = -1, nx = 1, bsz = bosz = 0;
         }
     }
     if (rw * tq * nx < 512) return false;  // too little per tile: per-tile costs dominate
-    // output strides (words) of the P axes; offsets inside a tile in 31 bits
-    int64_t ostr[TROP_MAX_DIMS];
-    int64_t acc = 1;
-    for (int d = nd - 1; d >= 0; --d) {
-        ostr[d] = acc;
-        acc *= p.shape[d];
-    }
+    // offsets inside a tile in 31 bits
     const int64_t lim = int64_t(1) << 31;
     int64_t pmax = (tp / pin - 1) * ostr[pax[np - 1]], qmax = (tq / qin - 1) * p.istride[qax[nq - 1]];
     for (int a = 0; a + 1 < np; ++a) pmax += (p.shape[pax[a]] - 1) * ostr[pax[a]];
     for (int a = 0; a + 1 < nq; ++a) qmax += (p.shape[qax[a]] - 1) * p.istride[qax[a]];
-    if (pmax + cw >= lim || qmax + rw >= lim || nx * bsz >= lim) return false;
+    if (pmax + cw >= lim || qmax + rw >= lim || nx * bsz >= lim || nx * bosz >= lim) return false;
     const int64_t pct = env_long("TROPICAL_FLAT_MAX_FIXED_USE_PCT", 50);  // tuning knob
     const bool scalar_fixed = !z && !fixed_vec;
     if (!force && !scalar_fixed && !(fixed * 100.0 <= (double)pct)) return false;
@@ -248,6 +261,7 @@ bool consider_flat(TropGatherParams& p, int lr, int z, bool fixed_vec) {
     p.fc_xax = xax;
     p.flat_nx = (int32_t)nx;
     p.fc_xstr = bsz;
+    p.fc_xostr = bosz;
     magic((uint64_t)(rw * tq), &p.fl_m3, &p.fl_s3);
     const int64_t ex = xax >= 0 ? p.shape[xax] : 1;
     p.tiles_x = (ex + nx - 1) / nx;
