@@ -26,6 +26,17 @@ def tb():
     return binding
 
 
+@pytest.fixture(autouse=True, params=["auto", "wide", "narrow"])
+def gemm_setting(request, monkeypatch):
+    """Every test under both argmax kernel settings: the host picks the
+    narrow one (K-block 256, loads ahead, one workgroup per CU) for fewer
+    than two tiles per CU and the wide one (float: K-block 128, 4 waves per
+    SIMD) otherwise; "wide" and "narrow" force one for any shape."""
+    if request.param != "auto":
+        monkeypatch.setenv("TROPICAL_GEMM_SETTING", request.param)
+    return request.param
+
+
 def make(sr, dt, b, m, k, n, seed, ties=True, a_col=False, b_col=False):
     g = torch.Generator().manual_seed(seed)
     if dt == "i32":

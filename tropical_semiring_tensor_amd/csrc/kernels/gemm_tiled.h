@@ -76,12 +76,32 @@ constexpr bool GEMM_CHAIN_RECORD = TROP_GEMM_CHAIN_RECORD != 0;
 #ifndef TROP_GEMM_KBLK
 #define TROP_GEMM_KBLK 256
 #endif
+// The wide float argmax kernels (many tiles): K-block 128, slices of 32
+// terms, and no second LDS fragment or re-scan buffer in flight.  That fits
+// them in 128 VGPRs (from 170), so two 512-thread workgroups share a CU (4
+// waves per SIMD instead of 2) and the adds of one wave pair with the max3s
+// of another: against the setting below, +6% on 64 x 256^3, +9% at
+// K = 1024, +5% on max-mul.  With one tile per CU or less the second
+// workgroup has nothing to do, the loads are no longer hidden and the
+// K = 256 products re-scan twice: there (NARROW) and in the split-K
+// kernels, and in the int32 kernels (their adds do not pair; the extra
+// waves cost them 12%), the K-block is 256, slices 64, both buffers kept.
+#ifndef TROP_GEMM_F32_KBLK
+#define TROP_GEMM_F32_KBLK 128
+#endif
+#ifndef TROP_GEMM_F32_SLICE_ARG
+#define TROP_GEMM_F32_SLICE_ARG 32
+#endif
 
-template <bool ARG>
+template <bool ARG, typename T, bool NARROW>
 struct GemmCfg {
+    static constexpr bool F32A = ARG && std::is_same<T, float>::value && !NARROW;
     // K terms resident in LDS: a block (argmax) or a ring of two slices
-    static constexpr int SL = ARG ? TROP_GEMM_SLICE_ARG : TROP_GEMM_SLICE_VO;  // slice (terms)
-    static constexpr int KB = ARG ? TROP_GEMM_KBLK : 2 * SL;
+    static constexpr int SL = ARG ? (F32A ? TROP_GEMM_F32_SLICE_ARG : TROP_GEMM_SLICE_ARG)
+                                  : TROP_GEMM_SLICE_VO;  // slice (terms)
+    static constexpr int KB = ARG ? (F32A ? TROP_GEMM_F32_KBLK : TROP_GEMM_KBLK) : 2 * SL;
+    // next LDS fragment (main loop) and next chunk (re-scan) loaded ahead
+    static constexpr bool PF = !F32A;
     static constexpr int NSL = KB / SL;  // slices per block
     static_assert(SL % GEMM_CH == 0 && KB % SL == 0, "whole chunks per slice, whole slices per block");
     // LDS row length in words: 4 words of padding put rows r and r + 1 in
@@ -338,11 +358,11 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
 // re-scan and stores.  SPLIT: the stream also covers the K ranges of a
 // split-K product (a separate instantiation, so that the unsplit kernel
 // keeps one slice count and one K for every tile).
-template <int SR, typename T, bool ARG, bool SPLIT>
+template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
-    using Cfg = GemmCfg<ARG>;
+    using Cfg = GemmCfg<ARG, T, NARROW>;
     constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR, GEMM_SL = Cfg::SL;
     constexpr int NV = 16 * GEMM_SL / GEMM_THREADS;  // vectors per thread, operand and slice
     static_assert(NV >= 1 && NV * GEMM_THREADS == 16 * GEMM_SL, "whole vectors per thread");
@@ -473,15 +493,24 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 if (q % QPC == 0 && q > 0 && q >= q_end) break;  // uniform over the workgroup
-                const int cur = q & 1, nxt = cur ^ 1;
-                if (q + 1 < NQ) {
+                const int cur = Cfg::PF ? q & 1 : 0, nxt = cur ^ 1;
+                if constexpr (Cfg::PF) {
+                    if (q + 1 < NQ) {
+#pragma unroll
+                        for (int r = 0; r < GEMM_TR; ++r)
+                            fa[nxt][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * (q + 1));
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk +
+                                                                     4 * (((q + 1) & ~3) | (((q + 1) & 3) ^ c)));
+                    }
+                } else if (q > 0) {
 #pragma unroll
                     for (int r = 0; r < GEMM_TR; ++r)
-                        fa[nxt][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * (q + 1));
+                        fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * q);
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk +
-                                                                 4 * (((q + 1) & ~3) | (((q + 1) & 3) ^ c)));
+                        fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * ((q & ~3) | ((q & 3) ^ c)));
                 }
 #pragma unroll
                 for (int r = 0; r < GEMM_TR; ++r)
@@ -541,11 +570,15 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         bv[buf][u] = *reinterpret_cast<const V*>(bp + 4 * (u ^ c));
                     }
                 };
-                rs_load(0, 0);
+                if constexpr (Cfg::PF) rs_load(0, 0);
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
-                    const int r = n / 4, c = n % 4, cur = n & 1;
-                    if (n + 1 < NS) rs_load(n + 1, cur ^ 1);
+                    const int r = n / 4, c = n % 4, cur = Cfg::PF ? n & 1 : 0;
+                    if constexpr (Cfg::PF) {
+                        if (n + 1 < NS) rs_load(n + 1, cur ^ 1);
+                    } else {
+                        rs_load(n, 0);
+                    }
                     const T bst = best[r][c];
                     int f = GEMM_CH - 1;
 #pragma unroll

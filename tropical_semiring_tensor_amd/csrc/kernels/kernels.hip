@@ -7,14 +7,24 @@
 
 using namespace trop;
 
-#define TROP_GEMM_ENTRIES(NAME, SR, T)                                                        \
-    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_##NAME(         \
+// ARGW: the wide argmax kernels' register target (the float ones are held
+// to 4 waves per SIMD, i.e. 128 VGPRs; see the float argmax setting in
+// gemm_tiled.h).  trop_gemm_tiled_n_*: the narrow setting, for products
+// with at most two tiles per CU.
+#define TROP_ARGW_F32 __attribute__((amdgpu_waves_per_eu(4)))
+#define TROP_ARGW_I32
+#define TROP_GEMM_ENTRIES(NAME, SR, T, ARGW)                                                  \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_##NAME(    \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, false>(p);                                                 \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo_##NAME(      \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, false, false>(p);                                                \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_n_##NAME(       \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, true>(p);                                           \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
         TropGemmParams p) {                                                                     \
@@ -36,12 +46,12 @@ using namespace trop;
         splitk_merge_body<SR, T>(p);                                                            \
     }
 
-TROP_GEMM_ENTRIES(maxplus_f32, TROP_SR_MAX_PLUS, float)
-TROP_GEMM_ENTRIES(minplus_f32, TROP_SR_MIN_PLUS, float)
-TROP_GEMM_ENTRIES(maxmul_f32, TROP_SR_MAX_MUL, float)
-TROP_GEMM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS, int32_t)
-TROP_GEMM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS, int32_t)
-TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t)
+TROP_GEMM_ENTRIES(maxplus_f32, TROP_SR_MAX_PLUS, float, TROP_ARGW_F32)
+TROP_GEMM_ENTRIES(minplus_f32, TROP_SR_MIN_PLUS, float, TROP_ARGW_F32)
+TROP_GEMM_ENTRIES(maxmul_f32, TROP_SR_MAX_MUL, float, TROP_ARGW_F32)
+TROP_GEMM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS, int32_t, TROP_ARGW_I32)
+TROP_GEMM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS, int32_t, TROP_ARGW_I32)
+TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t, TROP_ARGW_I32)
 
 extern "C" __global__ __launch_bounds__(256) void trop_fill(TropFillParams p) { fill_body(p); }
 

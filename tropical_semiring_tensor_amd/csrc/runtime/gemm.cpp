@@ -193,9 +193,18 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     }
     // without an argmax output the value-only kernel skips the chunk record
     // and the re-scan
+    // With an argmax, products of fewer than two tiles per CU take the
+    // narrow setting (one workgroup per CU, loads ahead, K-block 256): the
+    // wide one's second workgroup would have no tile.
+    bool narrow = argmax && total < 2 * (int64_t)device_cu_count(dev);
+    if (const char* f = std::getenv("TROPICAL_GEMM_SETTING")) {  // tests: "wide" or "narrow"
+        if (std::strcmp(f, "wide") == 0) narrow = false;
+        if (std::strcmp(f, "narrow") == 0) narrow = argmax;
+    }
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
-              : (KernelId)((argmax ? K_GEMM_TILED_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
+              : (KernelId)((argmax ? (narrow ? K_GEMM_TILED_N_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32)
+                                   : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
     // keeps every workgroup's tiles on one XCD.
