@@ -106,6 +106,11 @@ def lib():
                "tropical_tree_plan_create", "tropical_tree_workspace_size", "tropical_tree_step_info",
                "tropical_tree_run", "tropical_tree_describe"):
         getattr(L, fn).restype = ctypes.c_int
+    # declared argument types: ctypes then converts plain ints (data
+    # pointers, sizes) without inspecting each argument's type per call
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.tropical_gemm_strided_batched.argtypes = [ctypes.c_int, ctypes.c_int, vp, trop_strides, vp, trop_strides,
+                                                vp, trop_strides, vp, i64, i64, i64, i64, vp]
     _lib = L
     return L
 
@@ -126,6 +131,22 @@ def _dt(t):
     if t.dtype == torch.int32:
         return I32
     raise TypeError(f"float32 or int32 tensors only, got {t.dtype}")
+
+
+# torch's current stream as a raw pointer, without building a Stream object
+# per call (the public call below is the fallback)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_ptr(stream, t):
+    """Raw stream pointer (int) for a call on tensor t's device."""
+    if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.device.index if t.device.index is not None else torch.cuda.current_device())
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _stream(stream):
@@ -168,14 +189,14 @@ def tropical_gemm_strided_batched(semiring, A, B, C, argmax=None, stream=None):
     A3, B3, C3 = _as3(A), _as3(B), _as3(C)
     batch, m, k = A3.shape
     n = B3.shape[2]
-    if argmax is not None and _as3(argmax).stride() != C3.stride():
+    a, b, c = A3.stride(), B3.stride(), C3.stride()
+    if argmax is not None and _as3(argmax).stride() != c:
         raise ValueError("argmax must have the strides of C")
-    sA = trop_strides(A3.stride(1), A3.stride(2), A3.stride(0))
-    sB = trop_strides(B3.stride(1), B3.stride(2), B3.stride(0))
-    sC = trop_strides(C3.stride(1), C3.stride(2), C3.stride(0))
-    st = lib().tropical_gemm_strided_batched(_sr(semiring), _dt(A3), _ptr(A3), sA, _ptr(B3), sB,
-                                             _ptr(C3), sC, _ptr(argmax), m, n, k, batch,
-                                             _stream(stream))
+    st = lib().tropical_gemm_strided_batched(_sr(semiring), _dt(A3), A3.data_ptr(), trop_strides(a[1], a[2], a[0]),
+                                             B3.data_ptr(), trop_strides(b[1], b[2], b[0]), C3.data_ptr(),
+                                             trop_strides(c[1], c[2], c[0]),
+                                             argmax.data_ptr() if argmax is not None else None,
+                                             m, n, k, batch, _stream_ptr(stream, A3))
     _check(st, "tropical_gemm_strided_batched")
     return C, argmax
 
