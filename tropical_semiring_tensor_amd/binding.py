@@ -151,6 +151,8 @@ def _stream_ptr(stream, t):
 
 def _stream(stream):
     if stream is None:
+        if _raw_stream is not None:
+            return ctypes.c_void_p(_raw_stream(torch.cuda.current_device()))
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
