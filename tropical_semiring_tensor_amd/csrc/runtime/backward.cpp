@@ -76,7 +76,9 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
         // strided items -- columns of grad_b -- the 16 lanes of a segment
         // load 16 bytes per item and wave, and the lane form measures faster.)
         const int64_t lane_waves = (segs * batch + 63) / 64;
-        if (c_item == 1 && lane_waves < 4 * (int64_t)device_cu_count(dev) && !env_flag_set("TROPICAL_BACKWARD_LANE")) {
+        const bool split_any = env_flag_set("TROPICAL_BACKWARD_SPLIT");  // tests: the split form for strided items too
+        if ((c_item == 1 || split_any) && lane_waves < 4 * (int64_t)device_cu_count(dev) &&
+            !env_flag_set("TROPICAL_BACKWARD_LANE")) {
             const KernelId sk =
                 (KernelId)((mul ? K_GEMM_BACKWARD_SPLIT_MUL : K_GEMM_BACKWARD_SPLIT_PLUS) + (vec ? 1 : 0));
             const int64_t groups = (segs * batch + 15) / 16;  // 16 segments per workgroup
