@@ -112,7 +112,7 @@ def main():
                     help="run only the lattice-network (contraction tree) legs and print their JSON")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
