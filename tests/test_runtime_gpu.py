@@ -116,3 +116,33 @@ def test_module_load_failure_is_not_cached():
     assert out.returncode == 0, out.stderr
     assert "FAILED_AS_EXPECTED 0" in out.stdout, out.stdout
     assert "RECOVERED 1" in out.stdout, out.stdout
+
+
+@pytest.mark.parametrize("setting", ["wide", "narrow"])
+def test_gemm_graph_capture_replays_both_settings(tb, monkeypatch, setting):
+    """The argmax GEMM captured in a HIP graph, in both kernel settings (the
+    wide one spills a few registers to scratch): every replay, with eager
+    work and synchronisations between them, gives the eager result."""
+    monkeypatch.setenv("TROPICAL_GEMM_SETTING", setting)
+    g = torch.Generator().manual_seed(41)
+    A = torch.randn(8, 256, 300, generator=g).to(DEV)
+    B = torch.randn(8, 300, 256, generator=g).to(DEV)
+    C0 = torch.empty(8, 256, 256, device=DEV)
+    I0 = torch.empty(8, 256, 256, dtype=torch.int32, device=DEV)
+    tb.tropical_gemm_strided_batched("max_plus", A, B, C0, I0)
+    torch.cuda.synchronize()
+    C = torch.empty_like(C0)
+    I = torch.empty_like(I0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        tb.tropical_gemm_strided_batched("max_plus", A, B, C, I, stream=s)
+    for rep in range(3):
+        C.fill_(0.0)
+        I.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int32), C0.view(torch.int32)), f"replay {rep}"
+        assert torch.equal(I, I0), f"replay {rep} argmax"
