@@ -129,7 +129,8 @@ def test_backward_strided_views_and_one_sided(tb, orc):
     assert_bits_equal(gb.cpu().numpy(), rb, "column-major grad_b")
 
 
-@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT"])
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
+                                  "TROPICAL_BACKWARD_RANGE"])
 def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
     """Bins summed from denormal gradients, +0 / -0 mixes (a bin of only
     -0.0 items is +0.0, since sums start at +0.0), exact cancellations to
@@ -189,11 +190,13 @@ def test_backward_maxmul_workload4_recipe(tb, orc):
     run_both(tb, orc, "max_mul", A, B, torch.from_numpy(I), G, 700, "workload 4 recipe backward")
 
 
-@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT"])
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
+                                  "TROPICAL_BACKWARD_RANGE"])
 def test_backward_every_kernel_form(tb, orc, monkeypatch, knob):
     """The same gradients from the 16-lanes-per-segment form (the default
-    for few segments), the lane-per-segment form and the wave-per-segment
-    form, over hub-heavy and uniform argmaxes, both weights."""
+    for few segments), the lane-per-segment form, the wave-per-segment
+    form and the 64-bin range form, over hub-heavy and uniform argmaxes,
+    both weights."""
     if knob:
         monkeypatch.setenv(knob, "1")
     b, m, k, n = 3, 70, 200, 130

@@ -131,27 +131,50 @@ __device__ __forceinline__ void gemm_backward_body(const TropBackwardParams& p) 
 // allows.
 constexpr int GBL_BINS = 256;
 constexpr int GBL_LDR = GBL_BINS + 1;  // padded row: lane l, bin k at bank (l + k) mod 64
+constexpr int GBR_BINS = 64;           // bins per workgroup in the range form
 constexpr int GBL_PF = 16;             // items fetched per step (4 groups of 4)
 
 // MUL: multiply by the weight operand.  VEC: items are contiguous
 // (c_item == 1), their count is a multiple of 4 and every segment start is
 // 16-byte aligned, so each lane reads four items with one 16-byte load.
-template <bool MUL, bool VEC>
+//
+// NB < GBL_BINS (range form): a workgroup holds the bins [lo, lo + NB) of its
+// 64 segments, so a group of segments is ceil(bins / NB) units of work, each
+// walking all items and adding those whose key is in its range.  The units
+// of one group go to workgroups b, b + 8, b + 16, ... (one XCD under the
+// round-robin dispatch), whose repeated item reads then hit the same L2.
+template <bool MUL, bool VEC, int NB = GBL_BINS>
 __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams& p) {
-    __shared__ float bins[64 * GBL_LDR];
+    constexpr int LDR = NB + 1;  // padded row: lane l, bin k at bank (l + k) mod 64
+    constexpr bool RANGE = NB < GBL_BINS;
+    __shared__ float bins[64 * LDR];
     const int lane = threadIdx.x & 63;
     const int64_t nseg = p.segs * p.batch;
     const int32_t K = (int32_t)p.bins;  // <= GBL_BINS (checked on the host)
     const int64_t items = p.items;
-    float* row = bins + lane * GBL_LDR;
-    for (int64_t seg0 = (int64_t)blockIdx.x * 64; seg0 < nseg; seg0 += (int64_t)gridDim.x * 64) {
+    float* row = bins + lane * LDR;
+    const int64_t ngroups = (nseg + 63) / 64;
+    const int32_t nr = RANGE ? (K + NB - 1) / NB : 1;  // bin ranges per group
+    const int64_t units = RANGE ? (ngroups + 7) / 8 * 8 * nr : ngroups;
+    for (int64_t w = blockIdx.x; w < units; w += gridDim.x) {
+        int64_t g = w;
+        int32_t lo = 0;
+        if (RANGE) {
+            const int64_t per = 8 * (int64_t)nr, blk = w / per;
+            const int32_t r = (int32_t)(w - blk * per);
+            g = blk * 8 + (r & 7);
+            lo = (r >> 3) * NB;
+            if (g >= ngroups) continue;  // (uniform over the workgroup)
+        }
+        const int32_t kn = RANGE ? min(NB, K - lo) : K;  // bins of this unit
+        const int64_t seg0 = g * 64;
         const int64_t seg = seg0 + lane;
         const bool live = seg < nseg;
         const int64_t b = live ? seg / p.segs : 0, s = live ? seg % p.segs : 0;
         const int32_t* ip = p.idx + b * p.c_batch + s * p.c_seg;
         const float* gp = p.grad + b * p.c_batch + s * p.c_seg;
         const float* wp = MUL ? p.w + b * p.w_batch : nullptr;
-        for (int32_t k = 0; k < K; ++k) row[k] = 0.0f;
+        for (int32_t k = 0; k < kn; ++k) row[k] = 0.0f;
         lds_order();
 
         // items GBL_PF at a time, the next group fetched while this one adds
@@ -199,11 +222,12 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
 #pragma unroll
                 for (int u = 0; u < GBL_PF; ++u) {
                     const int32_t key = kb[h][u];
-                    const bool valid = (uint32_t)key < (uint32_t)K;  // an item, with a key in [0, bins)
+                    // an item, with a key in [lo, lo + kn) (a subset of [0, bins))
+                    const bool valid = (uint32_t)(key - lo) < (uint32_t)kn;
                     float v = vb[h][u];
                     // (an invalid item reads the weight at (0, 0), which is in range)
                     if (MUL) v = v * wp[(int64_t)(valid ? key : 0) * p.w_key + (valid ? tb + u : 0) * p.w_item];
-                    if (valid) lds_add(&row[key], v);
+                    if (valid) lds_add(&row[key - lo], v);
                 }
             }
         }
@@ -213,12 +237,12 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
             for (int r = 0; r < 64; ++r) {
                 const int64_t sg = seg0 + r;
                 if (sg >= nseg) break;
-                float* out = p.out + (sg / p.segs) * p.o_batch + (sg % p.segs) * p.o_seg;
-                for (int32_t k = lane; k < K; k += 64) out[k] = bins[r * GBL_LDR + k];
+                float* out = p.out + (sg / p.segs) * p.o_batch + (sg % p.segs) * p.o_seg + lo;
+                for (int32_t k = lane; k < kn; k += 64) out[k] = bins[r * LDR + k];
             }
         } else if (live) {
-            float* out = p.out + b * p.o_batch + s * p.o_seg;
-            for (int32_t k = 0; k < K; ++k) out[k * p.o_bin] = row[k];
+            float* out = p.out + b * p.o_batch + s * p.o_seg + (int64_t)lo * p.o_bin;
+            for (int32_t k = 0; k < kn; ++k) out[k * p.o_bin] = row[k];
         }
         lds_order();
     }

@@ -135,6 +135,14 @@ TROP_BACKWARD_LANE(plus_vec, false, true)
 TROP_BACKWARD_LANE(mul, true, false)
 TROP_BACKWARD_LANE(mul_vec, true, true)
 
+#define TROP_BACKWARD_RANGE(NAME, MUL)                                                           \
+    extern "C" __global__ __launch_bounds__(64) void trop_gemm_backward_range_##NAME(            \
+        TropBackwardParams p) {                                                                  \
+        gemm_backward_lane_body<MUL, false, GBR_BINS>(p);                                        \
+    }
+TROP_BACKWARD_RANGE(plus, false)
+TROP_BACKWARD_RANGE(mul, true)
+
 #define TROP_BACKWARD_SPLIT(NAME, MUL, VEC)                                                      \
     extern "C" __global__ __launch_bounds__(GBS_THREADS) void trop_gemm_backward_split_##NAME(    \
         TropBackwardParams p) {                                                                  \

@@ -88,8 +88,26 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
             const int64_t grid = groups < cap ? groups : cap;
             return launch(dev, sk, TROP_K_GEMM_BACKWARD, (uint32_t)(grid < 1 ? 1 : grid), 256, &p, stream);
         }
-        const KernelId lk = (KernelId)((mul ? K_GEMM_BACKWARD_LANE_MUL : K_GEMM_BACKWARD_LANE_PLUS) + (vec ? 1 : 0));
         const int64_t groups = (segs * batch + 63) / 64;
+        // Strided items (columns of grad_b) with too few segments for one
+        // lane each to fill the device: the range form, 64 bins per
+        // workgroup, ceil(bins / 64) workgroups per 64 segments.
+        // TROPICAL_BACKWARD_RANGE=1 forces it (tests); =0 or
+        // TROPICAL_BACKWARD_LANE keeps the lane form.
+        const char* rv = std::getenv("TROPICAL_BACKWARD_RANGE");
+        const bool range = rv && *rv ? rv[0] != '0'
+                                     : c_item != 1 && bins > 64 && lane_waves < 4 * (int64_t)device_cu_count(dev) &&
+                                           !env_flag_set("TROPICAL_BACKWARD_LANE");
+        if (range) {
+            const KernelId rk = mul ? K_GEMM_BACKWARD_RANGE_MUL : K_GEMM_BACKWARD_RANGE_PLUS;
+            const int64_t units = (groups + 7) / 8 * 8 * ((bins + 63) / 64);
+            int occ = kernel_occupancy(dev, rk);
+            if (occ < 1) occ = 1;
+            const int64_t cap = (int64_t)device_cu_count(dev) * occ;
+            const int64_t grid = units < cap ? units : cap;
+            return launch(dev, rk, TROP_K_GEMM_BACKWARD, (uint32_t)(grid < 1 ? 1 : grid), 64, &p, stream);
+        }
+        const KernelId lk = (KernelId)((mul ? K_GEMM_BACKWARD_LANE_MUL : K_GEMM_BACKWARD_LANE_PLUS) + (vec ? 1 : 0));
         int occ = kernel_occupancy(dev, lk);
         if (occ < 1) occ = 1;
         const int64_t cap = (int64_t)device_cu_count(dev) * occ;

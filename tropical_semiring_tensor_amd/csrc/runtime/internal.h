@@ -71,6 +71,8 @@ enum KernelId : int {
     K_GATHER_FLATB_N2,
     K_GATHER_FLATGB_N1,  // several blocks per tile, groups of axes
     K_GATHER_FLATGB_N2,
+    K_GEMM_BACKWARD_RANGE_PLUS,  // backward, lane form over 64-bin ranges
+    K_GEMM_BACKWARD_RANGE_MUL,
     K_COUNT
 };
 const char* kernel_name(KernelId id);

@@ -59,7 +59,8 @@ const std::vector<std::string>& kernel_names() {
             "trop_gather_flat_n1",           "trop_gather_flat_n2",
             "trop_gather_flatg_n1",          "trop_gather_flatg_n2",
             "trop_gather_flatb_n1",          "trop_gather_flatb_n2",
-            "trop_gather_flatgb_n1",         "trop_gather_flatgb_n2"};
+            "trop_gather_flatgb_n1",         "trop_gather_flatgb_n2",
+            "trop_gemm_backward_range_plus", "trop_gemm_backward_range_mul"};
         static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
         static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
         std::vector<std::string> v;
