@@ -1,20 +1,23 @@
 """Benchmark of the tropical hot path on one MI355X.
 
-A step is one tropical_gemm_strided_batched call on the headline workload:
-max-plus f32 with argmax, batch 64, M = N = K = 256 (inputs seeded,
-synthetic, resident in HBM before timing starts).  It prints ONE JSON line
-with the tropical GOPS (2 ops per (output, k) term) plus:
-  roofline      the GEMM kernel against the VALU peak for tropical terms:
-                a term needs one add and half a max3 / min3; gfx950 issues
-                adds on all 128 FP32 lanes per CU per clock (the lanes behind
-                the 157.3 TFLOP/s FP32 figure) and max / min on 64 of them,
-                so at best 128 / 1.5 = 85.3 terms per CU per clock:
-                256 CU x 85.3 x 2.4 GHz x 2 ops = 104.9 T tropical ops/s
+A step is one tropical_gemm_strided_batched call on the headline workload,
+the largest GEMM workload that fits one GPU: max-mul f32 with argmax,
+batch 16, M = N = K = 2048, B column-major (inputs seeded, synthetic,
+resident in HBM before timing starts).  It prints ONE JSON line with the
+tropical GOPS (2 ops per (output, k) term) plus:
+  roofline      the GEMM kernel against MI355X's published FP32 vector peak,
+                157.3 TFLOP/s (256 CUs x 128 lanes x 2 x 2.4 GHz).  A max-mul
+                term is one multiply and half a v_max3; gfx950 has no packed
+                max, so an f32 tropical kernel tops out below this figure.
+                Alongside: the fraction of one 64-lane pipe per SIMD
+                (78.6 T) and of the builder's own issue-rate derivation
+                (104.9 T, not a published peak)
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
-  workloads     the other four workloads: workload 1 latency, 3 and 4 GOPS,
+  workloads     the other workloads: workload 2 (64 x 256^3 max-plus) with
+                its own roofline keys, workload 1 latency, workload 3 GOPS,
                 the einsum path of workload 5 per kernel (GB/s vs 8 TB/s HBM
-                for the gathers, GOPS for its GEMM), and a >= 256 MiB permute
-                sweep
+                for the gathers, GOPS for its GEMM), the backward, the lattice
+                networks, and a >= 256 MiB permute / diagonal / trace sweep
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
        python bench.py --profile-traffic   (the program profiled for HBM
            counters: one 256 MiB device copy of known size, then three
@@ -30,13 +33,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-FP32_DATASHEET_T = 157.3                     # FP32 vector peak: 128 FMA lanes / CU / clock
-# tropical terms: 1 add (any of the 128 lanes) + 1/2 max3 (64 lanes) each
-VALU_PEAK_T = 256 * (128 / 1.5) * 2.4e9 * 2 / 1e12   # 104.9 T tropical ops/s
-SINGLE_ISSUE_T = 256 * 64 * 2.4e9 * 2 / 1e12         # 78.6: one term per lane of a 64-lane SIMD set
+FP32_PEAK_T = 157.3                          # MI355X FP32 vector peak (published)
+SINGLE_PIPE_T = 256 * 64 * 2.4e9 * 2 / 1e12  # 78.6: one term per lane of a 64-lane SIMD set per clock
+# the builder's own derivation from measured issue rates (adds on 128 lanes,
+# max3 on 64, perfectly overlapped): not a published figure
+DERIVED_ISSUE_T = 256 * (128 / 1.5) * 2.4e9 * 2 / 1e12   # 104.9
 HBM_PEAK_GBS = 8000.0
-# the sources of the headline kernel (trop_gemm_tiled_maxplus_f32): its
-# body, its semiring operations and its argument block
+HEADLINE = 4
+# the sources of the GEMM kernels: body, semiring operations, argument block
 KERNEL_SOURCES = ["tropical_semiring_tensor_amd/csrc/kernels/gemm_tiled.h",
                   "tropical_semiring_tensor_amd/csrc/kernels/ring.h",
                   "tropical_semiring_tensor_amd/csrc/kernel_params.h"]
@@ -93,6 +97,55 @@ class Timer:
         return {"median_ms": times[len(times) // 2], "min_ms": times[0], "max_ms": times[-1]}
 
 
+def gemm_case(torch, tb, inputs, wid, dev):
+    """Device operands, outputs and one step of GEMM workload `wid`."""
+    w = inputs.WORKLOADS[wid]
+    A, B = inputs.gemm_operands(wid)
+    Ad = A.to(dev)
+    # a column-major B keeps its layout on the device
+    Bd = B.to(dev) if B.is_contiguous() else B.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    dt = torch.int32 if w["dtype"] == "i32" else torch.float32
+    C = torch.empty(w["batch"], w["m"], w["n"], dtype=dt, device=dev)
+    I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
+    ops = 2 * w["batch"] * w["m"] * w["n"] * w["k"]
+
+    def step():
+        tb.tropical_gemm_strided_batched(w["semiring"], Ad, Bd, C, I)
+
+    return {"w": w, "A": A, "B": B, "Ad": Ad, "Bd": Bd, "C": C, "I": I, "ops": ops, "step": step}
+
+
+def timed_steps(torch, step, steps, warmup, settle_s):
+    """ms per step of `steps` launches back to back between HIP events on
+    the launch stream, after `settle_s` seconds of untimed launches (the
+    clocks the GPU holds under this load, not its idle ramp) and `warmup`
+    more."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def roofline_keys(ops, kern_ms, kernel):
+    achieved_t = ops / (kern_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(achieved_t, 3), "peak": FP32_PEAK_T, "unit": "TFLOP/s",
+            "frac": round(achieved_t / FP32_PEAK_T, 4), "kernel": kernel, "kernel_us": round(kern_ms * 1e3, 2),
+            "frac_of_one_64_lane_pipe_78.6T": round(achieved_t / SINGLE_PIPE_T, 4),
+            "frac_of_derived_issue_bound_104.9T": round(achieved_t / DERIVED_ISSUE_T, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,8 +159,8 @@ def main():
                     help="the program profiled for per-workload counters: a 256 MiB device copy "
                          "(counter calibration), then three launches of each workload's kernels")
     ap.add_argument("--profile-valu", action="store_true",
-                    help="3 launches each of the headline GEMM (argmax, value only) and of a 4096^3 "
-                         "min-plus f32 GEMM on integer data, for VALU issue counters; prints nothing else")
+                    help="3 launches each of the headline GEMM, of workload 2 (argmax, value only) and of "
+                         "a 4096^3 min-plus f32 GEMM on integer data, for VALU issue counters")
     ap.add_argument("--network-only", action="store_true",
                     help="run only the lattice-network (contraction tree) legs and print their JSON")
     args = ap.parse_args()
@@ -128,18 +181,17 @@ def main():
         print(json.dumps(tree_workloads(torch, tb, inputs, timer, dev)), flush=True)
         return
 
-    # ---------------- headline: workload 2 ----------------
-    w = inputs.WORKLOADS[2]
-    A, B = inputs.gemm_operands(2)
-    Ad, Bd = A.to(dev), B.to(dev)
-    C = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.float32, device=dev)
-    I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
-    ops = 2 * w["batch"] * w["m"] * w["n"] * w["k"]
+    if args.profile_configs:
+        profile_configs(torch, tb, inputs, dev)
+        log("[bench] config probe done")
+        return
 
-    def step():
-        tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, I)
+    # ---------------- headline: workload 4 ----------------
+    hc = gemm_case(torch, tb, inputs, HEADLINE, dev)
+    w, ops, step = hc["w"], hc["ops"], hc["step"]
 
     if args.profile_valu:
+        c2 = gemm_case(torch, tb, inputs, 2, dev)
         g = torch.Generator(device="cpu").manual_seed(5)
         A4 = torch.randint(1, 1001, (1, 4096, 4096), generator=g, dtype=torch.int32).float().to(dev)
         B4 = torch.randint(1, 1001, (1, 4096, 4096), generator=g, dtype=torch.int32).float().to(dev)
@@ -148,18 +200,15 @@ def main():
         for _ in range(3):
             step()
         for _ in range(3):
-            tb.tropical_gemm_strided_batched("max_plus", Ad, Bd, C, None)
+            c2["step"]()
+        for _ in range(3):
+            tb.tropical_gemm_strided_batched("max_plus", c2["Ad"], c2["Bd"], c2["C"], None)
         for _ in range(3):
             tb.tropical_gemm_strided_batched("min_plus", A4, B4, C4, I4)
         for _ in range(3):
             tb.tropical_gemm_strided_batched("min_plus", A4, B4, C4, None)
         torch.cuda.synchronize()
         log("[bench] valu probe done")
-        return
-
-    if args.profile_configs:
-        profile_configs(torch, tb, inputs, dev)
-        log("[bench] config probe done")
         return
 
     if args.profile_traffic:
@@ -177,36 +226,18 @@ def main():
         log("[bench] traffic probe done")
         return
 
-    # Settle: about 0.3 s of untimed launches first, so the timed steps see
-    # the clocks the GPU holds under this load rather than its idle ramp.
-    settle_t0 = time.perf_counter()
-    while time.perf_counter() - settle_t0 < 0.3:
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize()
-    log(f"[bench] workload 2 headline: warmup {args.warmup}, steps {args.steps}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] workload {HEADLINE} headline: warmup {args.warmup}, steps {args.steps}")
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
+    ms_per_step = timed_steps(torch, step, args.steps, args.warmup, settle_s=0.3)
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
     value_gops = ops / (ms_per_step * 1e-3) / 1e9
     # One step is one launch of the GEMM kernel, back to back on one stream:
     # the timed region's per-step time is the kernel's average duration.
-    kern_ms = ms_per_step
-    achieved_t = ops / (kern_ms * 1e-3) / 1e12
-    # for reference, events bracketing single launches (adds launch overhead)
-    per = timer.time(step, reps=max(10, args.steps), warmup=0)
-    log(f"[bench] workload 2: {ms_per_step * 1e3:.1f} us/step, {value_gops:.0f} GOPS, "
-        f"single-launch events {per['median_ms'] * 1e3:.1f} us, wall {wall:.3f} s")
+    kernel = "trop_gemm_tiled_maxmul_f32"
+    roof = roofline_keys(ops, ms_per_step, kernel)
+    roof["traffic"] = traffic_from_profile(w["name"])
+    log(f"[bench] workload {HEADLINE}: {ms_per_step * 1e3:.1f} us/step, {value_gops:.0f} GOPS, "
+        f"frac {roof['frac']}, wall {wall:.3f} s")
 
     result = {
         "metric": "tropical GOPS (batched GEMM+argmax) % VALU peak; permute/gather GB/s % HBM",
@@ -220,47 +251,37 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,1), resident in HBM)",
-        "config": {"workload": w["name"], "semiring": "max_plus", "batch": w["batch"], "m": w["m"],
-                   "n": w["n"], "k": w["k"], "argmax": True, "layout": "row-major A and B"},
-        "roofline": {
-            "bound": "alu",
-            "achieved": round(achieved_t, 3),
-            "peak": round(VALU_PEAK_T, 2),
-            "unit": "TFLOP/s",
-            "frac": round(achieved_t / VALU_PEAK_T, 4),
-            "traffic": traffic_from_profile(w["name"]),
-            "kernel": "trop_gemm_tiled_maxplus_f32",
-            "kernel_us": round(kern_ms * 1e3, 2),
-            "single_launch_event_us": round(per["median_ms"] * 1e3, 2),
-            "frac_of_fp32_datasheet": round(achieved_t / FP32_DATASHEET_T, 4),
-            "frac_of_single_issue": round(achieved_t / SINGLE_ISSUE_T, 4),
-        },
+        "data": "synthetic (seeded U(0,1], resident in HBM)",
+        "config": {"workload": w["name"], "semiring": "max_mul", "batch": w["batch"], "m": w["m"],
+                   "n": w["n"], "k": w["k"], "argmax": True, "layout": "row-major A, column-major B"},
+        "roofline": roof,
     }
 
     # ---------------- CPU oracle baseline ----------------
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.default()
-        An, Bn = A.numpy(), B.numpy()
-        orc.gemm("max_plus", An[:1], Bn[:1])  # warm
-        reps, dt = 0, 0.0
+        An, Bn = hc["A"].numpy(), hc["B"].numpy()
+        orc.gemm("max_mul", An[:1, :64], Bn[:1])  # warm
+        done, dt = 0, 0.0
         t0 = time.perf_counter()
-        while dt < 8.0 and reps < 200:       # bounded: about 8 s of CPU work
-            orc.gemm("max_plus", An, Bn)
-            reps += 1
+        while dt < 10.0 and done < w["batch"]:   # bounded: about 10 s of CPU work
+            orc.gemm("max_mul", An[done:done + 1], Bn[done:done + 1])
+            done += 1
             dt = time.perf_counter() - t0
-        cpu_gops = reps * ops / dt / 1e9
+        cpu_gops = done * (ops // w["batch"]) / dt / 1e9
         result["cpu_baseline"] = {"value": round(cpu_gops, 3), "unit": "GOPS",
                                   "cores": orc.max_threads(), "kind": "oracle",
-                                  "sample": f"{reps} full passes of {w['name']} (64 x 256^3, "
-                                            f"{dt:.1f} s; naive b-i-j-k loops, OpenMP over rows)"}
+                                  "sample": f"{done} of the {w['batch']} batch entries of {w['name']} "
+                                            f"(2048^3 each, {dt:.1f} s; naive b-i-j-k loops, OpenMP over rows)"}
         log(f"[bench] cpu oracle: {cpu_gops:.2f} GOPS on {orc.max_threads()} threads")
-        result["cpu_baseline"].update(cpu_single_thread(orc, inputs, A, B, ops))
+        result["cpu_baseline"].update(cpu_single_thread(orc, inputs))
         log(f"[bench] cpu oracle, one thread: {result['cpu_baseline']['single_thread']}")
 
     if not args.quick:
-        result["workloads"] = other_workloads(torch, tb, inputs, timer, dev)
+        del hc
+        torch.cuda.empty_cache()
+        result["workloads"] = other_workloads(torch, tb, inputs, timer, dev, args)
 
     print(json.dumps(result), flush=True)
 
@@ -303,7 +324,7 @@ def profile_configs(torch, tb, inputs, dev):
     torch.cuda.synchronize()
 
 
-def cpu_single_thread(orc, inputs, A, B, ops):
+def cpu_single_thread(orc, inputs):
     """The oracle on one host thread: workload 1 whole, one batch entry of
     workload 2 (scaled to the whole), and workload 5's contraction whole;
     plus the host's CPU model and logical core count."""
@@ -320,6 +341,9 @@ def cpu_single_thread(orc, inputs, A, B, ops):
         t0 = time.perf_counter()
         orc.gemm("max_plus", A1.numpy(), B1.numpy())
         t1 = time.perf_counter() - t0
+        A, B = inputs.gemm_operands(2)
+        w = inputs.WORKLOADS[2]
+        ops = 2 * w["batch"] * w["m"] * w["n"] * w["k"]
         An, Bn = A.numpy()[:1], B.numpy()[:1]
         t0 = time.perf_counter()
         orc.gemm("max_plus", An, Bn)
@@ -337,7 +361,7 @@ def cpu_single_thread(orc, inputs, A, B, ops):
             "cpu_model": model, "logical_cores": os.cpu_count()}
 
 
-def other_workloads(torch, tb, inputs, timer, dev):
+def other_workloads(torch, tb, inputs, timer, dev, args):
     out = {}
     reps = 10
     # flush buffer for cold-cache runs: 1 GiB write evicts the 256 MB MALL
@@ -345,6 +369,16 @@ def other_workloads(torch, tb, inputs, timer, dev):
 
     def flush():
         flush_buf.fill_(1.0)
+
+    # workload 2 (64 x 256^3 max-plus), timed like the headline
+    c2 = gemm_case(torch, tb, inputs, 2, dev)
+    ms = timed_steps(torch, c2["step"], 200, 5, settle_s=0.3)
+    rec = roofline_keys(c2["ops"], ms, "trop_gemm_tiled_maxplus_f32")
+    rec.update({"GOPS": round(c2["ops"] / (ms * 1e-3) / 1e9, 1),
+                "traffic": traffic_from_profile(c2["w"]["name"])})
+    out[c2["w"]["name"]] = rec
+    log(f"[bench] workload 2: {ms * 1e3:.1f} us/step, frac {rec['frac']}")
+    del c2
 
     # workload 1: latency of one small call
     A, B = inputs.gemm_operands(1)
@@ -356,24 +390,15 @@ def other_workloads(torch, tb, inputs, timer, dev):
     log(f"[bench] workload 1: {t['median_ms'] * 1e3:.1f} us")
     del Ad, Bd, C, I
 
-    # workloads 3 and 4
-    for wid, sr in ((3, "min_plus"), (4, "max_mul")):
-        w = inputs.WORKLOADS[wid]
-        A, B = inputs.gemm_operands(wid)
-        Ad = A.to(dev)
-        Bd = B.to(dev) if B.is_contiguous() else B.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
-        del A, B
-        dt = torch.int32 if w["dtype"] == "i32" else torch.float32
-        C = torch.empty(w["batch"], w["m"], w["n"], dtype=dt, device=dev)
-        I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
-        t = timer.time(lambda: tb.tropical_gemm_strided_batched(sr, Ad, Bd, C, I), reps=5, warmup=1)
-        ops = 2 * w["batch"] * w["m"] * w["n"] * w["k"]
-        tops = ops / (t["median_ms"] * 1e-3) / 1e12
-        out[w["name"]] = {"ms": round(t["median_ms"], 3), "GOPS": round(tops * 1e3, 1),
-                          "frac_valu_peak": round(tops / VALU_PEAK_T, 4)}
-        log(f"[bench] workload {wid}: {t['median_ms']:.3f} ms, {tops * 1e3:.0f} GOPS")
-        del Ad, Bd, C, I
-        torch.cuda.empty_cache()
+    # workload 3 (int32 min-plus 4096^3)
+    c3 = gemm_case(torch, tb, inputs, 3, dev)
+    ms = timed_steps(torch, c3["step"], 10, 1, settle_s=0.1)
+    rec = roofline_keys(c3["ops"], ms, "trop_gemm_tiled_minplus_i32")
+    rec["GOPS"] = round(c3["ops"] / (ms * 1e-3) / 1e9, 1)
+    out[c3["w"]["name"]] = rec
+    log(f"[bench] workload 3: {ms:.3f} ms, frac {rec['frac']}")
+    del c3
+    torch.cuda.empty_cache()
 
     # a narrow product with a long K (one 64 x 64 output tile): unsplit, the
     # whole product is one workgroup's; split along K it spreads over the chip
@@ -471,7 +496,7 @@ def other_workloads(torch, tb, inputs, timer, dev):
         else:
             ops = 2 * 32 * 256 * 128 * 256
             rec["GOPS"] = round(ops / (b2b * 1e-3) / 1e9, 1)
-            rec["frac_valu_peak"] = round(ops / (b2b * 1e-3) / 1e12 / VALU_PEAK_T, 4)
+            rec["frac_fp32_peak"] = round(ops / (b2b * 1e-3) / 1e12 / FP32_PEAK_T, 4)
         w5[name] = rec
         log(f"[bench] workload 5 {name}: {rec}")
     out["einsum_iijb_kjb_bki_f32"] = w5
@@ -503,7 +528,39 @@ def other_workloads(torch, tb, inputs, timer, dev):
     sweep["batched_transpose_f64_(b,i,k)->(b,k,i)"] = {"MiB_moved": 2 * 8 * X64.numel() // 2 ** 20,
                                                         "cold_GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     log(f"[bench] sweep f64 batched transpose: {gbs:.0f} GB/s")
-    del Y, X64
+    del Y, X64, X
+    torch.cuda.empty_cache()
+    # repeated-label gathers at the same scale: the tensor is allocated whole
+    # (8 GiB) but only its diagonal is read.  Algorithmic bytes are the
+    # diagonal elements read plus the elements written.
+    D = torch.empty(64, 64, 2048, 256, device=dev)      # workload 5's iijb, scaled
+    Y = torch.empty(256, 64, 2048, device=dev)
+    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iijb", "bij", out=Y), reps=reps, warmup=2,
+                   flush=flush)
+    gbs = 2 * 4 * Y.numel() / (t["median_ms"] * 1e-3) / 1e9
+    sweep["diagonal_(i,i,j,b)->(b,i,j)"] = {"MiB_moved": 2 * 4 * Y.numel() // 2 ** 20, "cold_GBs": round(gbs, 1),
+                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] sweep diagonal iijb->bij: {gbs:.0f} GB/s")
+    del D, Y
+    torch.cuda.empty_cache()
+    D = torch.empty(64, 64, 524288, device=dev)
+    Y = torch.empty(64, 524288, device=dev)
+    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "ij", out=Y), reps=reps, warmup=2,
+                   flush=flush)
+    gbs = 2 * 4 * Y.numel() / (t["median_ms"] * 1e-3) / 1e9
+    sweep["diagonal_(i,i,j)->(i,j)"] = {"MiB_moved": 2 * 4 * Y.numel() // 2 ** 20, "cold_GBs": round(gbs, 1),
+                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] sweep diagonal iij->ij: {gbs:.0f} GB/s")
+    Yr = torch.empty(524288, device=dev)
+    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "j", out=Yr), reps=reps, warmup=2,
+                   flush=flush)
+    nbytes = 4 * (Y.numel() + Yr.numel())
+    gbs = nbytes / (t["median_ms"] * 1e-3) / 1e9
+    sweep["trace_max_(i,i,j)->(j)"] = {"MiB_moved": nbytes // 2 ** 20, "cold_GBs": round(gbs, 1),
+                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] sweep trace iij->j: {gbs:.0f} GB/s")
+    del D, Y, Yr
+    torch.cuda.empty_cache()
     out["permute_sweep_256MiB"] = sweep
     clk = clock_mhz()
     if clk:

@@ -120,8 +120,6 @@ typedef struct {
     uint64_t module_loads;             /* hipModuleLoadData calls, all devices  */
     uint64_t launches_total;           /* kernels enqueued                      */
     uint64_t launches[TROP_K_FAMILIES];/* per trop_kernel_family                */
-    uint64_t host_syncs;               /* host-blocking syncs issued: always 0  */
-    uint64_t memcpy_calls;             /* host<->device copies issued: always 0 */
 } trop_stats;
 
 /*

@@ -177,10 +177,14 @@ def test_contract_extent_mismatch(tb):
         tb.tropical_contract_pair_describe("ij,jk->ik", (2, 3), (4, 5))
 
 
-def test_stats_start_clean(tb):
+def test_stats_counters_are_consistent(tb):
     s = tb.tropical_get_stats()
-    assert s["host_syncs"] == 0 and s["memcpy_calls"] == 0
     assert set(s["launches"]) == set(tb.KERNEL_FAMILIES)
+    # every launch is counted once overall and once in its family
+    assert s["launches_total"] == sum(s["launches"].values())
+    tb.tropical_reset_stats()
+    s = tb.tropical_get_stats()
+    assert s["launches_total"] == 0 and not any(s["launches"].values())
 
 
 # ---------------------------------------------------------------------------

@@ -35,7 +35,6 @@ def test_module_loaded_once(tb):
     torch.cuda.synchronize()
     st = tb.tropical_get_stats()
     assert st["module_loads"] == before == 1
-    assert st["host_syncs"] == 0 and st["memcpy_calls"] == 0
 
 
 def test_host_and_pinned_pointers_rejected(tb):

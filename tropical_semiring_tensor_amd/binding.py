@@ -49,8 +49,7 @@ class trop_tree_step(ctypes.Structure):
 
 class trop_stats(ctypes.Structure):
     _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
-                ("launches", ctypes.c_uint64 * 10), ("host_syncs", ctypes.c_uint64),
-                ("memcpy_calls", ctypes.c_uint64)]
+                ("launches", ctypes.c_uint64 * 10)]
 
 
 _lib = None
@@ -475,8 +474,7 @@ def tropical_get_stats():
     s = trop_stats()
     _check(lib().tropical_get_stats(ctypes.byref(s)), "tropical_get_stats")
     return {"module_loads": s.module_loads, "launches_total": s.launches_total,
-            "launches": {name: s.launches[i] for i, name in enumerate(KERNEL_FAMILIES)},
-            "host_syncs": s.host_syncs, "memcpy_calls": s.memcpy_calls}
+            "launches": {name: s.launches[i] for i, name in enumerate(KERNEL_FAMILIES)}}
 
 
 def tropical_reset_stats():

@@ -223,7 +223,7 @@ __device__ __forceinline__ void gemm_backward_lane_body(const TropBackwardParams
                 for (int u = 0; u < GBL_PF; ++u) {
                     const int32_t key = kb[h][u];
                     // an item, with a key in [lo, lo + kn) (a subset of [0, bins))
-                    const bool valid = (uint32_t)(key - lo) < (uint32_t)kn;
+                    const bool valid = (uint32_t)key - (uint32_t)lo < (uint32_t)kn;  // unsigned: no overflow for any key
                     float v = vb[h][u];
                     // (an invalid item reads the weight at (0, 0), which is in range)
                     if (MUL) v = v * wp[(int64_t)(valid ? key : 0) * p.w_key + (valid ? tb + u : 0) * p.w_item];

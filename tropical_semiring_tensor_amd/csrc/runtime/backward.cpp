@@ -92,12 +92,13 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
         // Strided items (columns of grad_b) with too few segments for one
         // lane each to fill the device: the range form, 64 bins per
         // workgroup, ceil(bins / 64) workgroups per 64 segments.
-        // TROPICAL_BACKWARD_RANGE=1 forces it (tests); =0 or
-        // TROPICAL_BACKWARD_LANE keeps the lane form.
+        // TROPICAL_BACKWARD_LANE (the plain lane form) wins over everything;
+        // otherwise TROPICAL_BACKWARD_RANGE=1 forces the range form for any
+        // segments (tests) and =0 keeps the lane form.
         const char* rv = std::getenv("TROPICAL_BACKWARD_RANGE");
-        const bool range = rv && *rv ? rv[0] != '0'
-                                     : c_item != 1 && bins > 64 && lane_waves < 4 * (int64_t)device_cu_count(dev) &&
-                                           !env_flag_set("TROPICAL_BACKWARD_LANE");
+        const bool range = !env_flag_set("TROPICAL_BACKWARD_LANE") &&
+                           (rv && *rv ? rv[0] != '0'
+                                      : c_item != 1 && bins > 64 && lane_waves < 4 * (int64_t)device_cu_count(dev));
         if (range) {
             const KernelId rk = mul ? K_GEMM_BACKWARD_RANGE_MUL : K_GEMM_BACKWARD_RANGE_PLUS;
             const int64_t units = (groups + 7) / 8 * 8 * ((bins + 63) / 64);

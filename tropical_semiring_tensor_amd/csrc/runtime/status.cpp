@@ -43,10 +43,6 @@ extern "C" trop_status tropical_get_stats(trop_stats* out) {
     out->module_loads = trop::g_module_loads.load();
     out->launches_total = trop::g_launches_total.load();
     for (int i = 0; i < TROP_K_FAMILIES; ++i) out->launches[i] = trop::g_launches[i].load();
-    // The library never blocks the host on the device and never copies
-    // between host and device: there is no call site that could count.
-    out->host_syncs = 0;
-    out->memcpy_calls = 0;
     return trop::ok();
 }
 
