@@ -233,7 +233,7 @@ def main():
     value_gops = ops / (ms_per_step * 1e-3) / 1e9
     # One step is one launch of the GEMM kernel, back to back on one stream:
     # the timed region's per-step time is the kernel's average duration.
-    kernel = "trop_gemm_tiled_maxmul_f32"
+    kernel = "trop_gemm_tiled_g_maxmul_f32"
     roof = roofline_keys(ops, ms_per_step, kernel)
     roof["traffic"] = traffic_from_profile(w["name"])
     log(f"[bench] workload {HEADLINE}: {ms_per_step * 1e3:.1f} us/step, {value_gops:.0f} GOPS, "

@@ -26,12 +26,14 @@ def tb():
     return binding
 
 
-@pytest.fixture(autouse=True, params=["auto", "wide", "narrow"])
+@pytest.fixture(autouse=True, params=["auto", "wide", "narrow", "global"])
 def gemm_setting(request, monkeypatch):
-    """Every test under both argmax kernel settings: the host picks the
-    narrow one (K-block 256, loads ahead, one workgroup per CU) for fewer
-    than two tiles per CU and the wide one (float: K-block 128, 4 waves per
-    SIMD) otherwise; "wide" and "narrow" force one for any shape."""
+    """Every test under every argmax kernel setting: the host picks the
+    global-resolve kernel (two-slice ring, argmax resolved once per tile
+    from global memory) for K > 256, else the narrow one (K-block 256,
+    loads ahead, one workgroup per CU) for fewer than two tiles per CU and
+    the wide one (float: K-block 128, 4 waves per SIMD) otherwise; "wide",
+    "narrow" and "global" force one for any shape."""
     if request.param != "auto":
         monkeypatch.setenv("TROPICAL_GEMM_SETTING", request.param)
     return request.param

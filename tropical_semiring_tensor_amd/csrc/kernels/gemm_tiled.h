@@ -38,6 +38,16 @@
 //
 // Without an argmax output the same loop runs with no record and no
 // re-scan, and LDS holds a ring of two slices instead of a block.
+//
+// Global resolve (GRES, products with a long K): LDS holds the same ring of
+// two slices as the value-only kernel, the record keeps the index of the
+// last strictly improving chunk over the tile's whole K, and the first
+// winner is found once per output and tile, after the last slice, by
+// re-reading that one chunk of both operands from global memory (it was
+// streamed through the tile moments before, so it comes from L2 or the
+// memory-side cache).  That replaces one LDS re-scan per resident block
+// (16 of them at K = 2048) with one 128-byte re-read per output; for short
+// K the re-read outweighs the re-scans and the resident-block forms stay.
 #pragma once
 #include <type_traits>
 
@@ -93,17 +103,34 @@ constexpr bool GEMM_CHAIN_RECORD = TROP_GEMM_CHAIN_RECORD != 0;
 #define TROP_GEMM_F32_SLICE_ARG 32
 #endif
 
-template <bool ARG, typename T, bool NARROW>
+// Global-resolve kernels: slice (terms) and whether the next LDS fragment
+// is loaded ahead in the main loop.
+#ifndef TROP_GEMM_SLICE_GR
+#define TROP_GEMM_SLICE_GR 32
+#endif
+#ifndef TROP_GEMM_GR_PF
+#define TROP_GEMM_GR_PF 0
+#endif
+#ifndef TROP_GEMM_CH_GR
+#define TROP_GEMM_CH_GR 16  // argmax chunk of the global-resolve kernels (terms)
+#endif
+
+template <bool ARG, typename T, bool NARROW, bool GRES = false>
 struct GemmCfg {
-    static constexpr bool F32A = ARG && std::is_same<T, float>::value && !NARROW;
+    static constexpr bool F32A = ARG && std::is_same<T, float>::value && !NARROW && !GRES;
+    // an LDS block resident for the argmax re-scan (else a ring of two slices)
+    static constexpr bool BLOCK = ARG && !GRES;
     // K terms resident in LDS: a block (argmax) or a ring of two slices
-    static constexpr int SL = ARG ? (F32A ? TROP_GEMM_F32_SLICE_ARG : TROP_GEMM_SLICE_ARG)
-                                  : TROP_GEMM_SLICE_VO;  // slice (terms)
-    static constexpr int KB = ARG ? (F32A ? TROP_GEMM_F32_KBLK : TROP_GEMM_KBLK) : 2 * SL;
+    static constexpr int SL = GRES ? TROP_GEMM_SLICE_GR
+                                   : ARG ? (F32A ? TROP_GEMM_F32_SLICE_ARG : TROP_GEMM_SLICE_ARG)
+                                         : TROP_GEMM_SLICE_VO;  // slice (terms)
+    static constexpr int KB = BLOCK ? (F32A ? TROP_GEMM_F32_KBLK : TROP_GEMM_KBLK) : 2 * SL;
     // next LDS fragment (main loop) and next chunk (re-scan) loaded ahead
-    static constexpr bool PF = !F32A;
+    static constexpr bool PF = GRES ? TROP_GEMM_GR_PF != 0 : !F32A;
+    // argmax chunk (terms): one record per chunk and output
+    static constexpr int CH = GRES ? TROP_GEMM_CH_GR : GEMM_CH;
     static constexpr int NSL = KB / SL;  // slices per block
-    static_assert(SL % GEMM_CH == 0 && KB % SL == 0, "whole chunks per slice, whole slices per block");
+    static_assert(SL % CH == 0 && KB % SL == 0, "whole chunks per slice, whole slices per block");
     // LDS row length in words: 4 words of padding put rows r and r + 1 in
     // different 16-byte bank groups, so 16 lanes reading 16 consecutive rows
     // at one k take distinct banks
@@ -352,28 +379,185 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
         }
 }
 
+// Global resolve of a finished tile, with the whole workgroup.  Each thread
+// has parked its outputs' values and chunk records in LDS (`rv`, `rw`: the
+// 64 x 64 tile row by row, rows GEMM_RLD words apart).  A wave then takes
+// 512 of the outputs, four lanes to an output: lane q of the four re-reads
+// terms 4q .. 4q + 3 of the output's last improving chunk from global
+// memory (one 16-byte load per operand when k is the unit-stride axis, so
+// a load instruction touches 16 cache lines, not 64) and finds the first
+// of them equal to the final value; the four answers combine by shuffles
+// into the first in the chunk, written back to `rw` as the relative k (0 for
+// an output that nothing beat).  Terms past the tile's K extent are not
+// read: they are padding in the main loop and cannot win.  Loads are
+// issued for every lane (an output with nothing to resolve reads the tile's
+// first element), so the compiler can keep several steps in flight.
+constexpr int GEMM_RLD = 65;  // row length of the parked tile (words; odd: rows in different banks)
+#ifndef TROP_GEMM_RESOLVE_UNROLL
+#define TROP_GEMM_RESOLVE_UNROLL 4  // resolve steps (16 outputs each) per group of loads
+#endif
+#define TROP_PRAGMA_(x) _Pragma(#x)
+#define TROP_PRAGMA(x) TROP_PRAGMA_(x)
+
+#ifndef TROP_GEMM_RESOLVE_CALL
+#define TROP_GEMM_RESOLVE_CALL 0
+#endif
+#if TROP_GEMM_RESOLVE_CALL
+// a call, not inlined: its registers are saved once per tile at the call
+// instead of constraining the allocation of the main loop
+#define TROP_RESOLVE_ATTR __attribute__((noinline))
+#else
+#define TROP_RESOLVE_ATTR __forceinline__
+#endif
+template <int SR, typename T, bool SPLIT, int CH>
+__device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoord ct, int tid, const T* rv,
+                                             int* rw) {
+    using R = Ring<SR, T>;
+    using V = vec4<T>;
+    constexpr int QL = CH / 16;  // quads per lane: lane q reads quads q, q + 4, ...
+    static_assert(CH % 16 == 0, "four lanes share a chunk of whole quads");
+    const int64_t kt = SPLIT ? ct.kt : p.k;
+    const T* const A = static_cast<const T*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
+    const T* const B = static_cast<const T*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
+    // 16-byte loads along k: k is the unit-stride axis with aligned rows
+    // (A) / columns (B); a quad starts at a multiple of 4 terms
+    const bool a_kv = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec;
+    const bool b_kv = p.b_mode == TROP_LOAD_K_CONTIG && p.b_vec;
+    const int lane = tid & 63, wave = tid >> 6, q = lane & 3;
+    constexpr int WAVES = GEMM_THREADS / 64;
+    constexpr int PER_WAVE = GEMM_BM * GEMM_BN / WAVES;  // outputs per wave
+    const int rlim = (int)(p.m - ct.row0 < GEMM_BM ? p.m - ct.row0 : GEMM_BM);
+    const int clim = (int)(p.n - ct.col0 < GEMM_BN ? p.n - ct.col0 : GEMM_BN);
+    const int kt32 = (int)kt;  // K < 2^31
+    if (a_kv && b_kv && (kt32 & 3) == 0) {
+        // both operands k-contiguous and K a multiple of 4: every quad is
+        // wholly inside or wholly past K, and each lane makes one 16-byte
+        // load per operand and quad (a lane with nothing to read loads the
+        // tile's first quad and ignores it).  Steps go in groups of G: all
+        // of a group's LDS reads, then its loads, its compares and its LDS
+        // writes, so the writes of one step cannot hold back the loads of
+        // the next.
+        constexpr int G = TROP_GEMM_RESOLVE_UNROLL;
+        static_assert((PER_WAVE / 16) % G == 0, "whole groups of steps");
+        const T* const Ar = A + ct.row0 * p.sa_row;
+        const T* const Bc = B + ct.col0 * p.sb_col;
+#pragma unroll 1
+        for (int st0 = 0; st0 < PER_WAVE / 16; st0 += G) {
+            T bst[G];
+            int w[G], off[G];
+            bool live[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int o = wave * PER_WAVE + 16 * (st0 + g) + (lane >> 2);
+                const int row = o >> 6, col = o & 63;
+                off[g] = row * GEMM_RLD + col;
+                bst[g] = rv[off[g]];
+                w[g] = rw[off[g]];
+                live[g] = row < rlim && col < clim;
+            }
+            V x[G][QL], y[G][QL];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int row = off[g] / GEMM_RLD, col = off[g] - row * GEMM_RLD;
+                live[g] = live[g] && w[g] >= 0;
+#pragma unroll
+                for (int h = 0; h < QL; ++h) {
+                    const int k0 = w[g] * CH + 4 * (q + 4 * h);
+                    const bool in = live[g] && k0 < kt32;
+                    x[g][h] = *reinterpret_cast<const V*>(Ar + (in ? row : 0) * p.sa_row + (in ? k0 : 0));
+                    y[g][h] = *reinterpret_cast<const V*>(Bc + (in ? col : 0) * p.sb_col + (in ? k0 : 0));
+                }
+            }
+            int f[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                f[g] = CH;  // first matching term of this lane's quads, as its place in the chunk
+#pragma unroll
+                for (int h = QL - 1; h >= 0; --h) {
+                    const int kq = 4 * (q + 4 * h);
+                    const bool in = live[g] && w[g] * CH + kq < kt32;
+                    f[g] = in && R::mul(x[g][h].w, y[g][h].w) == bst[g] ? kq + 3 : f[g];
+                    f[g] = in && R::mul(x[g][h].z, y[g][h].z) == bst[g] ? kq + 2 : f[g];
+                    f[g] = in && R::mul(x[g][h].y, y[g][h].y) == bst[g] ? kq + 1 : f[g];
+                    f[g] = in && R::mul(x[g][h].x, y[g][h].x) == bst[g] ? kq : f[g];
+                }
+                // the first match among the output's four lanes (quad permutes)
+                f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0xB1, 0xF, 0xF, true));  // lane ^ 1
+                f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0x4E, 0xF, 0xF, true));  // lane ^ 2
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (q == 0) rw[off[g]] = live[g] ? w[g] * CH + f[g] : 0;
+        }
+        return;
+    }
+    for (int st = 0; st < PER_WAVE / 16; ++st) {
+        const int o = wave * PER_WAVE + 16 * st + (lane >> 2);
+        const int row = o >> 6, col = o & 63;
+        const T bst = rv[row * GEMM_RLD + col];
+        const int w = rw[row * GEMM_RLD + col];
+        const bool live = w >= 0 && row < rlim && col < clim;
+        int f = CH;
+#pragma unroll
+        for (int h = QL - 1; h >= 0; --h) {
+            const int kq = 4 * (q + 4 * h);  // the quad's first term within the chunk
+            const int64_t k0 = live ? (int64_t)w * CH + kq : 0;
+            const T* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k0 * p.sa_col;
+            const T* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k0 * p.sb_row;
+            T ta[4], tb[4];
+            if (a_kv && k0 + 4 <= kt) {
+                const V x = *reinterpret_cast<const V*>(a);
+                ta[0] = x.x, ta[1] = x.y, ta[2] = x.z, ta[3] = x.w;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ta[u] = k0 + u < kt ? a[u * p.sa_col] : R::zero();
+            }
+            if (b_kv && k0 + 4 <= kt) {
+                const V x = *reinterpret_cast<const V*>(b);
+                tb[0] = x.x, tb[1] = x.y, tb[2] = x.z, tb[3] = x.w;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) tb[u] = k0 + u < kt ? b[u * p.sb_row] : R::one();
+            }
+#pragma unroll
+            for (int u = 3; u >= 0; --u) f = (R::mul(ta[u], tb[u]) == bst) ? kq + u : f;
+        }
+        f = min(f, __shfl_xor(f, 1));
+        f = min(f, __shfl_xor(f, 2));
+        if (q == 0) rw[row * GEMM_RLD + col] = live ? w * CH + f : 0;
+    }
+}
+
 // The tiled kernel.  A workgroup walks the tiles L = blockIdx.x,
 // blockIdx.x + gridDim.x, ... as one stream of (tile, slice) steps, so the
 // fetch of a tile's first slice overlaps the previous tile's last slice,
 // re-scan and stores.  SPLIT: the stream also covers the K ranges of a
 // split-K product (a separate instantiation, so that the unsplit kernel
 // keeps one slice count and one K for every tile).
-template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT>
+template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
-    using Cfg = GemmCfg<ARG, T, NARROW>;
+    using Cfg = GemmCfg<ARG, T, NARROW, GRES>;
+    static_assert(!GRES || ARG, "the global resolve is an argmax form");
+    constexpr bool BLK = Cfg::BLOCK;  // resident block + LDS re-scan
     constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR, GEMM_SL = Cfg::SL;
     constexpr int NV = 16 * GEMM_SL / GEMM_THREADS;  // vectors per thread, operand and slice
     static_assert(NV >= 1 && NV * GEMM_THREADS == 16 * GEMM_SL, "whole vectors per thread");
     constexpr int NQ = GEMM_SL / 4;         // k-quads per slice
-    constexpr int QPC = GEMM_CH / 4;        // k-quads per chunk
-    constexpr int CPS = GEMM_SL / GEMM_CH;  // chunks per slice
+    constexpr int CH = Cfg::CH;              // argmax chunk (terms)
+    constexpr int QPC = CH / 4;              // k-quads per chunk
+    constexpr int CPS = GEMM_SL / CH;        // chunks per slice
     using LA = OpLoad<T, NV, LDR, false, GEMM_SL>;
     using LB = OpLoad<T, NV, LDR, true, GEMM_SL>;
     static_assert(GEMM_SL % 16 == 0 && LDR % 4 == 0, "slots and rows keep the swizzle inside 16-word groups");
-    __shared__ __attribute__((aligned(16))) T As[GEMM_BM * LDR];
-    __shared__ __attribute__((aligned(16))) T Bs[GEMM_BN * LDR];
+    // A's rows, then B's columns (one array: the global resolve parks a
+    // finished tile over both)
+    __shared__ __attribute__((aligned(16))) T Ss[(GEMM_BM + GEMM_BN) * LDR];
+    T* const As = Ss;
+    T* const Bs = Ss + GEMM_BM * LDR;
+    static_assert(!GRES || (GEMM_BM + GEMM_BN) * LDR >= 2 * GEMM_BM * GEMM_RLD,
+                  "the parked tile fits in the operand rings");
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
@@ -462,14 +646,14 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     int64_t blk_k0 = 0;  // first k of the resident block
     int ring = 0;        // value only: ring slot of the current slice
     for (;;) {
-        const int s = ARG ? g % NSL : ring;
+        const int s = BLK ? g % NSL : ring;
         const bool last = (g + 1 == (SPLIT ? c_nsl : nslices_k));
-        const bool bend = ARG ? (last || s == NSL - 1) : last;
+        const bool bend = BLK ? (last || s == NSL - 1) : last;
         // The registers hold slice g + 1 of this tile: its LDS slot is free
         // (argmax: inside the block; value only: the ring slot read two
         // slices ago), so park it now and fetch the step after it.
         if (!bend) {
-            const int sn = (ARG ? s + 1 : s ^ 1) * GEMM_SL;
+            const int sn = (BLK ? s + 1 : s ^ 1) * GEMM_SL;
             la.store(As, sn, ra);
             lb.store(Bs, sn, rb);
             fetch_next();
@@ -482,7 +666,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             // padding (terms that cannot win): they are skipped, which makes
             // a small K cost its own chunks and not a whole slice.
             const int64_t k_left = (SPLIT ? ct.kt : p.k) - (int64_t)g * GEMM_SL;
-            const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + GEMM_CH - 1) / GEMM_CH) * QPC;
+            const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + CH - 1) / CH) * QPC;
             V fa[2][GEMM_TR], fb[2][4];
 #pragma unroll
             for (int r = 0; r < GEMM_TR; ++r) fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk);
@@ -530,7 +714,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 if constexpr (ARG) {
                     if (q % QPC == QPC - 1) {
                         // record the chunk if it beats everything before it
-                        const int cid = s * CPS + q / QPC;  // chunk within the block
+                        // chunk within the block, or (GRES) within the tile's K
+                        const int cid = (GRES ? g : s) * CPS + q / QPC;
 #pragma unroll
                         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
@@ -551,7 +736,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
         }
 
         if (bend) {
-            if constexpr (ARG) {
+            if constexpr (BLK) {
                 // Re-scan the winning chunk of every output that improved in
                 // this block: the first term equal to the best.  Slots run in
                 // sequence with the 16-byte reads of the next slot issued
@@ -596,6 +781,32 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             }
 
             if (last) {
+                if constexpr (GRES) {
+                    // park values and chunk records, resolve, read back
+                    T* const rv = Ss;
+                    int* const rw = reinterpret_cast<int*>(Ss + GEMM_BM * GEMM_RLD);
+                    __syncthreads();  // every wave is done with the operand rings
+#pragma unroll
+                    for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int o = (ty + GEMM_RS * r) * GEMM_RLD + tx + 16 * c;
+                            rv[o] = best[r][c];
+                            rw[o] = win[r][c];
+                        }
+                    __syncthreads();
+                    resolve_tile<SR, T, SPLIT, CH>(p, ct, tid, rv, rw);
+                    __syncthreads();
+#pragma unroll
+                    for (int r = 0; r < GEMM_TR; ++r)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int o = (ty + GEMM_RS * r) * GEMM_RLD + tx + 16 * c;
+                            idx[r][c] = rw[o];
+                            best[r][c] = rv[o];  // (reloaded: nothing stays live across the resolve)
+                        }
+                    __syncthreads();  // the rings are refilled below
+                }
                 // The tile is complete.  C takes the bits of the first
                 // winning term; they can differ from the running maximum's
                 // only for a zero value (+0 against -0).
@@ -637,8 +848,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 }
             }
             if (!fetch_valid) break;  // no further step for this workgroup
-            if constexpr (ARG) __syncthreads();  // every wave is done with this block
-            const int sn = ARG ? 0 : (s ^ 1) * GEMM_SL;
+            if constexpr (BLK) __syncthreads();  // every wave is done with this block
+            const int sn = BLK ? 0 : (s ^ 1) * GEMM_SL;
             la.store(As, sn, ra);
             lb.store(Bs, sn, rb);
             fetch_next();

@@ -13,6 +13,11 @@ using namespace trop;
 // with at most two tiles per CU.
 #define TROP_ARGW_F32 __attribute__((amdgpu_waves_per_eu(4)))
 #define TROP_ARGW_I32
+// the global-resolve argmax kernels (long K): 4 waves per SIMD
+#ifndef TROP_GR_WAVES
+#define TROP_GR_WAVES 4
+#endif
+#define TROP_ARGW_GR __attribute__((amdgpu_waves_per_eu(TROP_GR_WAVES)))
 #define TROP_GEMM_ENTRIES(NAME, SR, T, ARGW)                                                  \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_##NAME(    \
         TropGemmParams p) {                                                                     \
@@ -25,6 +30,10 @@ using namespace trop;
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_n_##NAME(       \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, false, true>(p);                                           \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_GR void trop_gemm_tiled_g_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, true>(p);                                    \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
         TropGemmParams p) {                                                                     \

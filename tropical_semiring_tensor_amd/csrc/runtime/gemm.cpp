@@ -70,6 +70,12 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
+// Products with a longer K take the global-resolve argmax kernel
+// (TROPICAL_GEMM_GRES_MIN_K overrides, for measurements).
+const int64_t kGresMinK = [] {
+    const char* v = std::getenv("TROPICAL_GEMM_GRES_MIN_K");
+    return v && *v ? (int64_t)std::strtoll(v, nullptr, 10) : (int64_t)256;
+}();
 
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     SplitK s;
@@ -197,13 +203,26 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // narrow setting (one workgroup per CU, loads ahead, K-block 256): the
     // wide one's second workgroup would have no tile.
     bool narrow = argmax && total < 2 * (int64_t)device_cu_count(dev);
-    if (const char* f = std::getenv("TROPICAL_GEMM_SETTING")) {  // tests: "wide" or "narrow"
-        if (std::strcmp(f, "wide") == 0) narrow = false;
-        if (std::strcmp(f, "narrow") == 0) narrow = argmax;
+    // A long K resolves each output's argmax once per tile from global
+    // memory instead of once per resident K-block from LDS, where both
+    // operands are read along k in 16-byte quads (K a multiple of 4); the
+    // other layouts would re-read a strided operand element by element.
+    const bool kvec = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec && p.b_mode == TROP_LOAD_K_CONTIG && p.b_vec &&
+                      k % 4 == 0;
+    bool gres = argmax && k > kGresMinK && kvec;
+    if (const char* f = std::getenv("TROPICAL_GEMM_SETTING")) {  // tests: "wide", "narrow" or "global"
+        if (std::strcmp(f, "wide") == 0) narrow = gres = false;
+        if (std::strcmp(f, "narrow") == 0) {
+            narrow = argmax;
+            gres = false;
+        }
+        if (std::strcmp(f, "global") == 0) gres = argmax;
     }
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
-              : (KernelId)((argmax ? (narrow ? K_GEMM_TILED_N_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32)
+              : (KernelId)((argmax ? (gres     ? K_GEMM_TILED_G_MAXPLUS_F32
+                                      : narrow ? K_GEMM_TILED_N_MAXPLUS_F32
+                                               : K_GEMM_TILED_MAXPLUS_F32)
                                    : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
