@@ -274,6 +274,10 @@ TROP_API trop_status tropical_diag_gather(trop_semiring semiring, trop_dtype dty
                                  int out_ndim, const int32_t* out_labels,
                                  const void* in, void* out, void* stream);
 
+/* Scratch held by tropical_contract_pair_noalloc on every device it runs
+ * on (a file-scope device array, until the process ends). */
+#define TROP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
 /*
  * Workspace (bytes) that tropical_contract_pair needs for `spec` with these
  * operand shapes.  Host-only, touches no device.  Errors as for
@@ -320,6 +324,26 @@ TROP_API trop_status tropical_contract_pair(const char* spec, trop_semiring semi
                                    const void* B, const int64_t* shapeB, const int64_t* stridesB,
                                    void* C, int32_t* argmax,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tropical_contract_pair for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors,
+ * minus the workspace: the intermediates live in the library's own
+ * TROP_NOALLOC_SCRATCH_BYTES of device memory per device (a file-scope
+ * array whose address is looked up once per device, at tropical_init or on
+ * the first call there).  A contraction whose
+ * tropical_contract_pair_workspace_size exceeds that limit is rejected with
+ * TROP_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  This call
+ * allocates nothing and calls no allocating routine.  Every call on one
+ * device shares that device's scratch: calls that overlap on one device
+ * (other streams, other host threads) race and must be ordered by the
+ * caller; calls on one stream are ordered by it.
+ */
+TROP_API trop_status tropical_contract_pair_noalloc(const char* spec, trop_semiring semiring, trop_dtype dtype,
+                                                    const void* A, const int64_t* shapeA, const int64_t* stridesA,
+                                                    const void* B, const int64_t* shapeB, const int64_t* stridesB,
+                                                    void* C, int32_t* argmax, void* stream);
 
 /*
  * Host-only: write a one-line text description of the plan that

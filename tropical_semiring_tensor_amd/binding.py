@@ -86,6 +86,8 @@ def lib():
                                          vp, vp, vp, sz, vp]
     L.tropical_contract_pair_describe.argtypes = [ctypes.c_char_p, I64P, I64P, I64P, I64P,
                                                   ctypes.c_char_p, sz]
+    L.tropical_contract_pair_noalloc.argtypes = [ctypes.c_char_p, i32, i32, vp, I64P, I64P, vp, I64P, I64P,
+                                                 vp, vp, vp]
     PP = ctypes.POINTER
     L.tropical_tree_plan_create.argtypes = [i32, i32, i32, PP(ctypes.c_char_p), PP(I64P), PP(I64P), i32,
                                             PP(trop_tree_step), PP(vp)]
@@ -102,6 +104,7 @@ def lib():
                "tropical_gemm_strided_batched_ws", "tropical_gemm_workspace_size",
                "tropical_diag_gather", "tropical_contract_pair_workspace_size",
                "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats",
+               "tropical_contract_pair_noalloc",
                "tropical_tree_plan_create", "tropical_tree_workspace_size", "tropical_tree_step_info",
                "tropical_tree_run", "tropical_tree_describe"):
         getattr(L, fn).restype = ctypes.c_int
@@ -365,6 +368,20 @@ def tropical_contract_pair(spec, semiring, A, B, C=None, argmax=True, workspace=
                                       _ptr(C), _ptr(argmax), _ptr(workspace), workspace.numel(),
                                       _stream(stream))
     _check(st, "tropical_contract_pair")
+    return C, argmax
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TROP_NOALLOC_SCRATCH_BYTES in include/tropical.h
+
+
+def tropical_contract_pair_noalloc(spec, semiring, A, B, C, argmax=None, stream=None):
+    """Pairwise tropical einsum into the caller's C (and argmax, or None)
+    with the library's own scratch: the call allocates nothing, so C (and
+    argmax) must be given."""
+    st = lib().tropical_contract_pair_noalloc(spec.encode(), _sr(semiring), _dt(A), _ptr(A), _i64(A.shape),
+                                              _i64(A.stride()), _ptr(B), _i64(B.shape), _i64(B.stride()),
+                                              _ptr(C), _ptr(argmax), _stream(stream))
+    _check(st, "tropical_contract_pair_noalloc")
     return C, argmax
 
 

@@ -5,7 +5,8 @@
    fast math, FTZ or FMA contraction: every tropical term is one IEEE op.
 2. The code object is embedded into the library with an assembler .incbin.
 3. The host runtime (C++17, HIP runtime API only, no kernels) is compiled
-   with g++ and linked against libamdhip64.
+   with g++ and linked against libamdhip64; its one source with device data
+   (the allocation-free call's scratch array) is compiled by hipcc.
 
 Output: tropical_semiring_tensor_amd/lib/libtropical.so (in-tree).
 """
@@ -31,6 +32,8 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-We
               "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
 RUNTIME_SRCS = ["status.cpp", "module.cpp", "validate.cpp", "gemm.cpp", "gather.cpp", "contract.cpp",
                 "backward.cpp", "tree.cpp"]
+# host runtime sources with device data (compiled by hipcc, gfx950 only)
+RUNTIME_HIP_SRCS = ["noalloc.hip"]
 
 
 def _run(cmd):
@@ -58,9 +61,18 @@ def build(verbose=False):
         _run(["g++", *HOST_FLAGS, "-c", os.path.join(HERE, "runtime", name), "-o", obj])
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(RUNTIME_SRCS) + 1)) as ex:
+    def compile_hip_host(name):
+        obj = os.path.join(BUILD, name.replace(".hip", ".o"))
+        _run([HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", os.path.join(HERE, "runtime", name), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(RUNTIME_SRCS) + 2)) as ex:
         fut_co = ex.submit(build_code_object, co)
+        fut_hip = [ex.submit(compile_hip_host, n) for n in RUNTIME_HIP_SRCS]
         objs = list(ex.map(compile_host, RUNTIME_SRCS))
+        objs += [f.result() for f in fut_hip]
         fut_co.result()
 
     with open(blob, "w") as f:

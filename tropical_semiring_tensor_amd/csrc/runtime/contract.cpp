@@ -485,11 +485,12 @@ extern "C" trop_status tropical_contract_pair_describe(const char* spec, const i
     return ok();
 }
 
-extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring semiring, trop_dtype dtype,
-                                              const void* Aptr, const int64_t* shapeA, const int64_t* stridesA,
-                                              const void* Bptr, const int64_t* shapeB, const int64_t* stridesB,
-                                              void* C, int32_t* argmax, void* workspace,
-                                              size_t workspace_bytes, void* stream) {
+namespace trop {
+
+trop_status contract_pair_call(const char* spec, trop_semiring semiring, trop_dtype dtype, const void* Aptr,
+                               const int64_t* shapeA, const int64_t* stridesA, const void* Bptr,
+                               const int64_t* shapeB, const int64_t* stridesB, void* C, int32_t* argmax,
+                               void* workspace, size_t workspace_bytes, bool fixed_scratch, void* stream) {
     if (semiring < TROP_MAX_PLUS || semiring > TROP_MAX_MUL) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown semiring");
     if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
@@ -499,9 +500,15 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
     if (argmax && !P.route_fits)
         return fail(TROP_ERR_INVALID_ARGUMENT, "the argmax index over the contracted and reduced labels exceeds int32");
     if (P.out_total == 0) return ok();
-    if (P.ws > 0 && workspace_bytes < P.ws)
+    if (P.ws > 0 && workspace_bytes < P.ws) {
+        if (fixed_scratch)
+            return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
+                        "this contraction needs " + std::to_string(P.ws) +
+                            " bytes of scratch; the allocation-free call holds at most " +
+                            std::to_string(workspace_bytes) + " (use tropical_contract_pair with a workspace)");
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(P.ws) + " bytes, got " + std::to_string(workspace_bytes));
+    }
 
     int dev = -1;
     st = current_device(&dev);
@@ -520,11 +527,22 @@ extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring se
         st = check_device_span(argmax, dev, P.out_total, 4, "argmax");
         if (st != TROP_OK) return st;
     }
-    if (P.ws > 0) {
+    if (P.ws > 0 && !fixed_scratch) {
         st = check_device_span(workspace, dev, (int64_t)(P.ws / 4), 4, "workspace");
         if (st != TROP_OK) return st;
     }
     st = pair_run(dev, P, semiring, dtype, Aptr, Bptr, C, argmax, workspace, static_cast<hipStream_t>(stream));
     if (st != TROP_OK) return st;
     return ok();
+}
+
+}  // namespace trop
+
+extern "C" trop_status tropical_contract_pair(const char* spec, trop_semiring semiring, trop_dtype dtype,
+                                              const void* Aptr, const int64_t* shapeA, const int64_t* stridesA,
+                                              const void* Bptr, const int64_t* shapeB, const int64_t* stridesB,
+                                              void* C, int32_t* argmax, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    return contract_pair_call(spec, semiring, dtype, Aptr, shapeA, stridesA, Bptr, shapeB, stridesB, C, argmax,
+                              workspace, workspace_bytes, false, stream);
 }

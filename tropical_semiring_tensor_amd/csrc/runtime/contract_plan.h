@@ -57,6 +57,15 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
 
 std::string pair_describe(const PairPlan& P);
 
+// tropical_contract_pair with its argument and pointer checks: `workspace`
+// holds `workspace_bytes`; fixed_scratch: it is the library's own
+// allocation-free scratch (not checked as a caller pointer, and a plan that
+// needs more is rejected with that limit in the message).
+trop_status contract_pair_call(const char* spec, trop_semiring semiring, trop_dtype dtype, const void* A,
+                               const int64_t* shapeA, const int64_t* stridesA, const void* B,
+                               const int64_t* shapeB, const int64_t* stridesB, void* C, int32_t* argmax,
+                               void* workspace, size_t workspace_bytes, bool fixed_scratch, void* stream);
+
 // Enqueue a planned contraction on `stream`: no pointer checks here (the
 // callers check spans).  `scratch` holds P.ws bytes.  Requesting `argmax`
 // with a pre-pass reduction is the caller's error to reject.

@@ -107,6 +107,11 @@ inline void magic_u31(uint64_t d, uint32_t* m, uint32_t* sh) {
     *sh = s - 1;
 }
 
+// ---- the allocation-free call's scratch (noalloc.hip) ---------------------
+// Device address of the library's own scratch array on device `dev`, which
+// must be current (looked up once per device).
+trop_status noalloc_scratch(int dev, void** out);
+
 // ---- argument checks (validate.cpp) --------------------------------------
 // `p` must be device memory of `dev` holding at least `span_elems` elements
 // of `elem_bytes` from p on (span_elems == 0: only the pointer is checked).

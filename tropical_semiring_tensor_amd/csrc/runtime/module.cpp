@@ -230,5 +230,18 @@ extern "C" trop_status tropical_init(int device) {
     if (device < 0 || device >= n)
         return trop::fail(TROP_ERR_INVALID_ARGUMENT, "tropical_init: no device " + std::to_string(device));
     trop_status st = trop::ensure_module(device);
+    if (st != TROP_OK) return st;
+    // the allocation-free call's scratch: its address on this device, looked
+    // up with the device current
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return trop::hip_fail(e, "hipGetDevice");
+    if (cur != device) {
+        e = hipSetDevice(device);
+        if (e != hipSuccess) return trop::hip_fail(e, "hipSetDevice");
+    }
+    void* scratch = nullptr;
+    st = trop::noalloc_scratch(device, &scratch);
+    if (cur != device) (void)hipSetDevice(cur);
     return st == TROP_OK ? trop::ok() : st;
 }
