@@ -97,8 +97,10 @@ class Timer:
         return {"median_ms": times[len(times) // 2], "min_ms": times[0], "max_ms": times[-1]}
 
 
-def gemm_case(torch, tb, inputs, wid, dev):
-    """Device operands, outputs and one step of GEMM workload `wid`."""
+def gemm_case(torch, tb, inputs, wid, dev, workspace=False):
+    """Device operands, outputs and one step of GEMM workload `wid`
+    (workspace: through tropical_gemm_strided_batched_ws with the workspace
+    tropical_gemm_workspace_size asks for)."""
     w = inputs.WORKLOADS[wid]
     A, B = inputs.gemm_operands(wid)
     Ad = A.to(dev)
@@ -109,10 +111,18 @@ def gemm_case(torch, tb, inputs, wid, dev):
     I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
     ops = 2 * w["batch"] * w["m"] * w["n"] * w["k"]
 
-    def step():
-        tb.tropical_gemm_strided_batched(w["semiring"], Ad, Bd, C, I)
+    ws = None
+    if workspace:
+        nbytes = tb.tropical_gemm_workspace_size(w["m"], w["n"], w["k"], w["batch"])
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
-    return {"w": w, "A": A, "B": B, "Ad": Ad, "Bd": Bd, "C": C, "I": I, "ops": ops, "step": step}
+    def step():
+        if ws is None:
+            tb.tropical_gemm_strided_batched(w["semiring"], Ad, Bd, C, I)
+        else:
+            tb.tropical_gemm_strided_batched_ws(w["semiring"], Ad, Bd, C, I, workspace=ws)
+
+    return {"w": w, "A": A, "B": B, "Ad": Ad, "Bd": Bd, "C": C, "I": I, "ops": ops, "step": step, "ws": ws}
 
 
 def timed_steps(torch, step, steps, warmup, settle_s):
@@ -289,7 +299,8 @@ def main():
 def profile_configs(torch, tb, inputs, dev):
     """One 256 MiB device copy (calibrates the traffic counters), then three
     launches of each workload's kernels in workload order: GEMMs 1-4 with
-    argmax, and workload 5's einsum (diagonal gather, B permute, GEMM) plus
+    argmax (workload 3 through the workspace call: domain pre-pass and float
+    mode), and workload 5's einsum (diagonal gather, B permute, GEMM) plus
     its paired output permute run on its own."""
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -298,15 +309,11 @@ def profile_configs(torch, tb, inputs, dev):
     torch.cuda.synchronize()
     del src, dst
     for wi in (1, 2, 3, 4):
-        w = inputs.WORKLOADS[wi]
-        A, B = inputs.gemm_operands(wi)
-        Ad, Bd = A.to(dev), B.to(dev)
-        C = torch.empty(w["batch"], w["m"], w["n"], dtype=Ad.dtype, device=dev)
-        I = torch.empty(w["batch"], w["m"], w["n"], dtype=torch.int32, device=dev)
+        c = gemm_case(torch, tb, inputs, wi, dev, workspace=(wi == 3))
         for _ in range(3):
-            tb.tropical_gemm_strided_batched(w["semiring"], Ad, Bd, C, I)
+            c["step"]()
         torch.cuda.synchronize()
-        del A, B, Ad, Bd, C, I
+        del c
         torch.cuda.empty_cache()
     A, B = inputs.einsum_operands()
     Ad, Bd = A.to(dev), B.to(dev)
@@ -390,13 +397,20 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     log(f"[bench] workload 1: {t['median_ms'] * 1e3:.1f} us")
     del Ad, Bd, C, I
 
-    # workload 3 (int32 min-plus 4096^3)
-    c3 = gemm_case(torch, tb, inputs, 3, dev)
+    # workload 3 (int32 min-plus 4096^3) through the workspace call: its
+    # data lie in the float-exact domain, so a pre-pass flags that and the
+    # float-mode kernel computes; the plain call (no workspace) alongside
+    c3 = gemm_case(torch, tb, inputs, 3, dev, workspace=True)
     ms = timed_steps(torch, c3["step"], 10, 1, settle_s=0.1)
-    rec = roofline_keys(c3["ops"], ms, "trop_gemm_tiled_minplus_i32")
+    rec = roofline_keys(c3["ops"], ms, "trop_gemm_fm_minplus_i32 (after trop_gemm_domain_minplus_i32)")
     rec["GOPS"] = round(c3["ops"] / (ms * 1e-3) / 1e9, 1)
+    rec["call"] = "tropical_gemm_strided_batched_ws (float mode)"
+    plain = lambda: tb.tropical_gemm_strided_batched("min_plus", c3["Ad"], c3["Bd"], c3["C"], c3["I"])
+    ms_plain = timed_steps(torch, plain, 10, 1, settle_s=0.1)
+    rec["plain_call_int32_kernel_ms"] = round(ms_plain, 3)
+    rec["plain_call_GOPS"] = round(c3["ops"] / (ms_plain * 1e-3) / 1e9, 1)
     out[c3["w"]["name"]] = rec
-    log(f"[bench] workload 3: {ms:.3f} ms, frac {rec['frac']}")
+    log(f"[bench] workload 3: {ms:.3f} ms (float mode), {ms_plain:.3f} ms (int32 kernel), frac {rec['frac']}")
     del c3
     torch.cuda.empty_cache()
 

@@ -113,7 +113,8 @@ typedef enum {
     TROP_K_GEMM_BACKWARD = 7,/* gradient routed along the argmax         */
     TROP_K_GEMM_SPLITK_MERGE = 8, /* merge of split-K partials           */
     TROP_K_ARGMAX_COMPOSE = 9,    /* argmax through pre-pass reductions  */
-    TROP_K_FAMILIES = 10
+    TROP_K_GEMM_DOMAIN = 10,      /* int32 float-mode domain pre-pass    */
+    TROP_K_FAMILIES = 11
 } trop_kernel_family;
 
 typedef struct {

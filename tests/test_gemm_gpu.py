@@ -440,8 +440,9 @@ def test_split_k_workspace_rules(tb, orc):
     A, B = make("max_plus", "f32", 1, 64, 8192, 64, seed=3)
     need = tb.tropical_gemm_workspace_size(64, 64, 8192, 1)
     assert need > 0
-    # large grids and short K do not split
-    assert tb.tropical_gemm_workspace_size(256, 256, 4096, 64) == 0
+    # large grids and short K do not split (a large grid gets room for the
+    # domain flags of the int32 float mode instead)
+    assert tb.tropical_gemm_workspace_size(256, 256, 4096, 64) == 4 * 256
     assert tb.tropical_gemm_workspace_size(64, 64, 500, 1) == 0
     Ad, Bd = A.to(DEV), B.to(DEV)
     C = torch.empty(1, 64, 64, device=DEV)
@@ -558,3 +559,113 @@ def test_int32_limit_patterns_split_k(tb, orc, sr):
         C, _ = gpu_gemm_ws(tb, sr, A, B, argmax=False)
         assert_bits_equal(C, Cr, f"split int32 limits {sr} {bad_k} value-only C")
 
+
+
+# ---------------------------------------------------------------------------
+# float mode of int32 max-plus / min-plus (tropical_gemm_strided_batched_ws
+# and the contraction paths, whose workspace holds the domain pre-pass's
+# flags): min-plus data in [0, 2^23) or [2^30, 2^31), max-plus data in
+# (-2^23, 2^23) are computed in float; one value outside sends the product to
+# the int32 kernel.  Either way every output and argmax matches the oracle.
+# ---------------------------------------------------------------------------
+
+FM_POOL = {
+    "min_plus": [0, 1, 2, 3, 999, 2 ** 23 - 2, 2 ** 23 - 1, I32_INF, I32_INF + 5, 2 ** 31 - 1],
+    "max_plus": [-(2 ** 23) + 1, -(2 ** 23) + 2, -5, -1, 0, 1, 3, 2 ** 23 - 2, 2 ** 23 - 1],
+}
+FM_OUTSIDE = {
+    "min_plus": [-1, 2 ** 23, I32_INF - 1, -(2 ** 31)],
+    "max_plus": [2 ** 23, -(2 ** 23), I32_INF, -I32_INF, 2 ** 31 - 1],
+}
+FM_SLOTS = 256  # domain flags at the start of the workspace
+
+
+def fm_case(sr, b, m, k, n, seed, outside=None, in_b=False, b_col=False):
+    g = torch.Generator().manual_seed(seed)
+    pool = torch.tensor(FM_POOL[sr], dtype=torch.int64)
+    lo = -2 if sr == "max_plus" else 0
+    A = torch.randint(lo, lo + 5, (b, m, k), generator=g)
+    B = torch.randint(lo, lo + 5, (b, k, n), generator=g)
+    A = torch.where(torch.rand(b, m, k, generator=g) < 0.2, pool[torch.randint(0, len(pool), (b, m, k), generator=g)], A)
+    B = torch.where(torch.rand(b, k, n, generator=g) < 0.2, pool[torch.randint(0, len(pool), (b, k, n), generator=g)], B)
+    A, B = A.to(torch.int32), B.to(torch.int32)
+    if outside is not None:
+        X = B if in_b else A
+        pos = tuple(int(torch.randint(0, d, (1,), generator=g)) for d in X.shape)
+        X[pos] = outside
+    if b_col:
+        B = B.transpose(1, 2).contiguous().transpose(1, 2)
+    return A, B
+
+
+def gpu_gemm_fm(tb, sr, A, B, argmax=True):
+    """The product through the workspace call; returns (C, I, flags)."""
+    from gpu_util import device_copy
+    Ad, Bd = device_copy(A), device_copy(B)
+    b, m, k = A.shape
+    n = B.shape[2]
+    ws = torch.zeros(max(4, tb.tropical_gemm_workspace_size(m, n, k, b)), dtype=torch.uint8, device=DEV)
+    C = torch.empty(b, m, n, dtype=torch.int32, device=DEV)
+    I = torch.empty(b, m, n, dtype=torch.int32, device=DEV) if argmax else None
+    tb.tropical_gemm_strided_batched_ws(sr, Ad, Bd, C, I, workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws[:4 * FM_SLOTS].view(torch.int32).cpu().numpy() if ws.numel() >= 4 * FM_SLOTS else None
+    return C.cpu().numpy(), (I.cpu().numpy() if argmax else None), flags
+
+
+@pytest.mark.parametrize("sr", ["min_plus", "max_plus"])
+@pytest.mark.parametrize("outside", [None, 0, 1, 2, 3], ids=lambda o: "inside" if o is None else f"outside{o}")
+@pytest.mark.parametrize("argmax", [True, False])
+def test_int32_float_mode(tb, orc, monkeypatch, sr, outside, argmax):
+    monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "1")  # at any size
+    # (K below 512: no split-K, whose partials would take the workspace)
+    for shape, in_b, b_col in (((2, 130, 480, 90), False, False), ((1, 70, 500, 130), True, True),
+                               ((3, 65, 17, 63), False, True)):
+        v = None if outside is None else FM_OUTSIDE[sr][outside % len(FM_OUTSIDE[sr])]
+        A, B = fm_case(sr, *shape, seed=sum(shape) + (outside or 0), outside=v, in_b=in_b, b_col=b_col)
+        C, I, flags = gpu_gemm_fm(tb, sr, A, B, argmax)
+        assert flags is not None
+        # the pre-pass saw what the data holds
+        assert (flags == 0).all() if v is None else (flags != 0).any(), (shape, v)
+        Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy(), argmax=argmax)
+        assert_equal(C, Cr, f"float mode {sr} {shape} outside={v} C")
+        if argmax:
+            assert_equal(I, Ir, f"float mode {sr} {shape} outside={v} argmax")
+
+
+def test_int32_float_mode_off_and_sizes(tb, orc, monkeypatch):
+    # never taken with the knob at 0 (no workspace asked for small products
+    # either); taken for large ones without the knob
+    monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "0")
+    assert tb.tropical_gemm_workspace_size(130, 90, 480, 2) == 0
+    A, B = fm_case("min_plus", 2, 130, 480, 90, seed=5)
+    C, I, flags = gpu_gemm_fm(tb, "min_plus", A, B)
+    assert flags is None
+    Cr, Ir = orc.gemm("min_plus", A.numpy(), B.numpy())
+    assert_equal(C, Cr, "knob 0 C")
+    assert_equal(I, Ir, "knob 0 argmax")
+    monkeypatch.delenv("TROPICAL_GEMM_INT_FLOAT")
+    assert tb.tropical_gemm_workspace_size(130, 90, 480, 2) == 0
+    assert tb.tropical_gemm_workspace_size(4096, 4096, 4096, 1) == 4 * FM_SLOTS
+
+
+def test_workload3_full_float_mode(tb, orc):
+    # workload 3 (min-plus int32 4096^3, U{1..1000} with 20% 2^30) is in the
+    # float domain: through the workspace call, every output against the oracle
+    A, B, Cr, Ir = _full_reference(orc, 3)
+    C, I, flags = gpu_gemm_fm(tb, "min_plus", A, B)
+    assert flags is not None and (flags == 0).all()
+    assert_equal(C, Cr, "workload 3 float mode C")
+    assert_equal(I, Ir, "workload 3 float mode argmin")
+
+
+def test_int32_float_mode_in_contractions(tb, orc, monkeypatch):
+    monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "1")
+    for sr, outside in (("min_plus", None), ("max_plus", None), ("min_plus", -1), ("max_plus", 2 ** 23)):
+        A, B = fm_case(sr, 3, 70, 300, 50, seed=61, outside=outside)
+        for spec in ("bij,bjk->bik", "bij,bjk->kbi"):
+            C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV))
+            torch.cuda.synchronize()
+            Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
+            assert_equal(C.cpu().numpy(), Cr, f"contraction {spec} {sr} outside={outside} C")
+            assert_equal(I.cpu().numpy(), Ir, f"contraction {spec} {sr} outside={outside} argmax")

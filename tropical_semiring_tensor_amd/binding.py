@@ -25,7 +25,7 @@ SEMIRINGS = {"max_plus": 0, "min_plus": 1, "max_mul": 2}
 F32, I32 = 0, 1
 KERNEL_FAMILIES = ["gemm_tiled", "gemm_simple", "fill", "gather_copy", "gather_tiled",
                    "gather_naive", "gather_reduce", "gemm_backward", "gemm_splitk_merge",
-                   "argmax_compose"]
+                   "argmax_compose", "gemm_domain"]
 MAX_DIMS = 8
 
 
@@ -49,7 +49,7 @@ class trop_tree_step(ctypes.Structure):
 
 class trop_stats(ctypes.Structure):
     _fields_ = [("module_loads", ctypes.c_uint64), ("launches_total", ctypes.c_uint64),
-                ("launches", ctypes.c_uint64 * 10)]
+                ("launches", ctypes.c_uint64 * 11)]
 
 
 _lib = None

@@ -51,6 +51,24 @@ struct TropGemmParams {
     // (coord32).
     int32_t group_rows;
     uint32_t gr_m, gr_s;
+    // launch gate of a checked int32 product (float mode): mode_slots flags
+    // from the domain pre-pass, nonzero = some value outside the domain; the
+    // launch proceeds only if (all flags zero) == mode_run.  NULL: no gate.
+    const int32_t* mode_flags;
+    int32_t mode_slots, mode_run;
+};
+
+// Domain pre-pass of an int32 max-plus / min-plus product (float mode):
+// workgroup w writes flags[w] = 1 if some element of A (batch, m, k) or B
+// (batch, k, n) that it scanned lies outside the semiring's float-exact
+// domain, else 0.  Every flag is written.
+struct TropDomainParams {
+    const int32_t* A;
+    const int32_t* B;
+    int32_t* flags;
+    int64_t sa_row, sa_col, sa_batch;
+    int64_t sb_row, sb_col, sb_batch;
+    int64_t m, n, k, batch;
 };
 
 // Merge of split-K partials: out = the first strictly better of the

@@ -107,4 +107,61 @@ __device__ __forceinline__ void fill_body(const TropFillParams& p) {
     }
 }
 
+// Domain pre-pass of the float mode of int32 max-plus / min-plus products
+// (see zero_of in gemm_tiled.h): is every element of A and B inside the
+// semiring's float-exact domain?  min-plus: [0, 2^23) or [2^30, 2^31)
+// -- with the top bit of the 31 flipped that is one interval below
+// 2^30 + 2^23; max-plus: (-2^23, 2^23), shifted by 2^23 - 1 onto one
+// unsigned interval below 2^24 - 1.
+template <int SR>
+__device__ __forceinline__ uint32_t outside_domain(int32_t x) {
+    if constexpr (SR == TROP_SR_MIN_PLUS) {
+        return ((uint32_t)x ^ 0x40000000u) >= 0x40800000u;
+    } else {
+        return (uint32_t)x + 0x7FFFFFu >= 0xFFFFFFu;
+    }
+}
+
+// Scan one operand: batch entries of r x c elements with strides (sb, sr,
+// sc); each workgroup takes rows blockIdx.x, blockIdx.x + gridDim.x, ...,
+// its threads run along the unit-stride axis when there is one (16-byte
+// loads when aligned).
+template <int SR>
+__device__ __forceinline__ uint32_t domain_scan(const int32_t* X, int64_t nb, int64_t r, int64_t c, int64_t sb,
+                                                int64_t sr, int64_t sc) {
+    if (sr == 1 && sc != 1) {
+        const int64_t t = r;
+        r = c;
+        c = t;
+        sr = sc;
+        sc = 1;
+    }
+    uint32_t bad = 0;
+    const int64_t rows = nb * r;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const int64_t b = row / r, i = row - b * r;
+        const int32_t* base = X + b * sb + i * sr;
+        if (sc == 1 && (reinterpret_cast<uintptr_t>(base) & 15u) == 0) {
+            const int64_t nv = c / 4;
+            for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+                const vec4<int32_t> x = reinterpret_cast<const vec4<int32_t>*>(base)[v];
+                bad |= outside_domain<SR>(x.x) | outside_domain<SR>(x.y) | outside_domain<SR>(x.z) |
+                       outside_domain<SR>(x.w);
+            }
+            for (int64_t e = nv * 4 + threadIdx.x; e < c; e += blockDim.x) bad |= outside_domain<SR>(base[e]);
+        } else {
+            for (int64_t e = threadIdx.x; e < c; e += blockDim.x) bad |= outside_domain<SR>(base[e * sc]);
+        }
+    }
+    return bad;
+}
+
+template <int SR>
+__device__ __forceinline__ void gemm_domain_body(const TropDomainParams& p) {
+    uint32_t bad = domain_scan<SR>(p.A, p.batch, p.m, p.k, p.sa_batch, p.sa_row, p.sa_col);
+    bad |= domain_scan<SR>(p.B, p.batch, p.k, p.n, p.sb_batch, p.sb_row, p.sb_col);
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) p.flags[blockIdx.x] = bad ? 1 : 0;
+}
+
 }  // namespace trop

@@ -249,10 +249,17 @@ __device__ __forceinline__ int mc_k(int vi) { return vi >> 4; }
 // bsw = 4 c, a compile-time constant in the compute loop.
 __device__ __forceinline__ int bsw(int row) { return ((row >> 4) & 3) << 2; }
 
-template <typename T, int NV, int LDR, bool SWZ, int SL>
+// Exact conversion of a staged element to the compute type (int32 data
+// computed in float: see the float mode of the int32 products below).
+template <typename T, typename TG>
+__device__ __forceinline__ T to_compute(TG x) {
+    return static_cast<T>(x);
+}
+
+template <typename T, int NV, int LDR, bool SWZ, int SL, typename TG = T>
 struct OpLoad {
-    using V = vec4<T>;
-    const T* q0;       // element 0 of vector 0 of slice 0
+    using V = vec4<TG>;
+    const TG* q0;      // element 0 of vector 0 of slice 0
     int64_t k_step;    // elements per slice along k
     int64_t v_step;    // elements between vectors v and v + 1
     int64_t e_str;     // elements between the 4 elements of a vector
@@ -295,7 +302,7 @@ struct OpLoad {
 
     // Point at a tile: X is the operand of the batch entry, mn_start the
     // tile's first row / column, str_mn the stride along it.
-    __device__ __forceinline__ void at(const T* X, int64_t mn_start, int64_t str_mn, int64_t str_k,
+    __device__ __forceinline__ void at(const TG* X, int64_t mn_start, int64_t str_mn, int64_t str_k,
                                        int tid) {
         const int64_t m_rel = mn_c ? mc_row(tid) : kc_row(tid);
         mn = mn_start + m_rel;
@@ -304,29 +311,29 @@ struct OpLoad {
     }
 
     __device__ __forceinline__ void load(int g, T pad, T (&r)[NV][4]) const {
-        const T* q = q0 + (int64_t)g * k_step;
+        const TG* q = q0 + (int64_t)g * k_step;
         const int64_t kb = k0 + (int64_t)g * SL;
         const bool full = mn_full && (int64_t)(g + 1) * SL <= k_lim;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const T* qv = q + v * v_step;
+            const TG* qv = q + v * v_step;
             if (full) {
                 if (vec) {
                     const V x = *reinterpret_cast<const V*>(qv);
-                    r[v][0] = x.x;
-                    r[v][1] = x.y;
-                    r[v][2] = x.z;
-                    r[v][3] = x.w;
+                    r[v][0] = to_compute<T>(x.x);
+                    r[v][1] = to_compute<T>(x.y);
+                    r[v][2] = to_compute<T>(x.z);
+                    r[v][3] = to_compute<T>(x.w);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r[v][e] = qv[e * e_str];
+                    for (int e = 0; e < 4; ++e) r[v][e] = to_compute<T>(qv[e * e_str]);
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t kk = kb + kv * v + (mn_c ? 0 : e);
                     const int64_t mm = mn + (mn_c ? e : 0);
-                    r[v][e] = (kk < k_lim && mm < mn_lim) ? qv[e * e_str] : pad;
+                    r[v][e] = (kk < k_lim && mm < mn_lim) ? to_compute<T>(qv[e * e_str]) : pad;
                 }
             }
         }
@@ -341,7 +348,7 @@ struct OpLoad {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) d[e * LDR] = r[v][e];
             } else {
-                *reinterpret_cast<V*>(d) = V{r[v][0], r[v][1], r[v][2], r[v][3]};
+                *reinterpret_cast<vec4<T>*>(d) = vec4<T>{r[v][0], r[v][1], r[v][2], r[v][3]};
             }
         }
     }
@@ -409,16 +416,16 @@ constexpr int GEMM_RLD = 65;  // row length of the parked tile (words; odd: rows
 #else
 #define TROP_RESOLVE_ATTR __forceinline__
 #endif
-template <int SR, typename T, bool SPLIT, int CH>
+template <int SR, typename T, bool SPLIT, int CH, typename TG = T>
 __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoord ct, int tid, const T* rv,
                                              int* rw) {
     using R = Ring<SR, T>;
-    using V = vec4<T>;
+    using V = vec4<TG>;
     constexpr int QL = CH / 16;  // quads per lane: lane q reads quads q, q + 4, ...
     static_assert(CH % 16 == 0, "four lanes share a chunk of whole quads");
     const int64_t kt = SPLIT ? ct.kt : p.k;
-    const T* const A = static_cast<const T*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
-    const T* const B = static_cast<const T*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
+    const TG* const A = static_cast<const TG*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
+    const TG* const B = static_cast<const TG*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
     // 16-byte loads along k: k is the unit-stride axis with aligned rows
     // (A) / columns (B); a quad starts at a multiple of 4 terms
     const bool a_kv = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec;
@@ -439,8 +446,8 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         // the next.
         constexpr int G = TROP_GEMM_RESOLVE_UNROLL;
         static_assert((PER_WAVE / 16) % G == 0, "whole groups of steps");
-        const T* const Ar = A + ct.row0 * p.sa_row;
-        const T* const Bc = B + ct.col0 * p.sb_col;
+        const TG* const Ar = A + ct.row0 * p.sa_row;
+        const TG* const Bc = B + ct.col0 * p.sb_col;
 #pragma unroll 1
         for (int st0 = 0; st0 < PER_WAVE / 16; st0 += G) {
             T bst[G];
@@ -476,10 +483,12 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
                 for (int h = QL - 1; h >= 0; --h) {
                     const int kq = 4 * (q + 4 * h);
                     const bool in = live[g] && w[g] * CH + kq < kt32;
-                    f[g] = in && R::mul(x[g][h].w, y[g][h].w) == bst[g] ? kq + 3 : f[g];
-                    f[g] = in && R::mul(x[g][h].z, y[g][h].z) == bst[g] ? kq + 2 : f[g];
-                    f[g] = in && R::mul(x[g][h].y, y[g][h].y) == bst[g] ? kq + 1 : f[g];
-                    f[g] = in && R::mul(x[g][h].x, y[g][h].x) == bst[g] ? kq : f[g];
+                    const V& xa = x[g][h];
+                    const V& yb = y[g][h];
+                    f[g] = in && R::mul(to_compute<T>(xa.w), to_compute<T>(yb.w)) == bst[g] ? kq + 3 : f[g];
+                    f[g] = in && R::mul(to_compute<T>(xa.z), to_compute<T>(yb.z)) == bst[g] ? kq + 2 : f[g];
+                    f[g] = in && R::mul(to_compute<T>(xa.y), to_compute<T>(yb.y)) == bst[g] ? kq + 1 : f[g];
+                    f[g] = in && R::mul(to_compute<T>(xa.x), to_compute<T>(yb.x)) == bst[g] ? kq : f[g];
                 }
                 // the first match among the output's four lanes (quad permutes)
                 f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0xB1, 0xF, 0xF, true));  // lane ^ 1
@@ -502,22 +511,24 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         for (int h = QL - 1; h >= 0; --h) {
             const int kq = 4 * (q + 4 * h);  // the quad's first term within the chunk
             const int64_t k0 = live ? (int64_t)w * CH + kq : 0;
-            const T* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k0 * p.sa_col;
-            const T* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k0 * p.sb_row;
+            const TG* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k0 * p.sa_col;
+            const TG* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k0 * p.sb_row;
             T ta[4], tb[4];
             if (a_kv && k0 + 4 <= kt) {
                 const V x = *reinterpret_cast<const V*>(a);
-                ta[0] = x.x, ta[1] = x.y, ta[2] = x.z, ta[3] = x.w;
+                ta[0] = to_compute<T>(x.x), ta[1] = to_compute<T>(x.y), ta[2] = to_compute<T>(x.z),
+                ta[3] = to_compute<T>(x.w);
             } else {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) ta[u] = k0 + u < kt ? a[u * p.sa_col] : R::zero();
+                for (int u = 0; u < 4; ++u) ta[u] = k0 + u < kt ? to_compute<T>(a[u * p.sa_col]) : R::zero();
             }
             if (b_kv && k0 + 4 <= kt) {
                 const V x = *reinterpret_cast<const V*>(b);
-                tb[0] = x.x, tb[1] = x.y, tb[2] = x.z, tb[3] = x.w;
+                tb[0] = to_compute<T>(x.x), tb[1] = to_compute<T>(x.y), tb[2] = to_compute<T>(x.z),
+                tb[3] = to_compute<T>(x.w);
             } else {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) tb[u] = k0 + u < kt ? b[u * p.sb_row] : R::one();
+                for (int u = 0; u < 4; ++u) tb[u] = k0 + u < kt ? to_compute<T>(b[u * p.sb_row]) : R::one();
             }
 #pragma unroll
             for (int u = 3; u >= 0; --u) f = (R::mul(ta[u], tb[u]) == bst) ? kq + u : f;
@@ -534,12 +545,45 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
 // re-scan and stores.  SPLIT: the stream also covers the K ranges of a
 // split-K product (a separate instantiation, so that the unsplit kernel
 // keeps one slice count and one K for every tile).
-template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false>
+// Float mode of int32 max-plus / min-plus products (TG = int32_t, T =
+// float): the operands are converted on staging and every term is one f32
+// add.  A separate pre-pass has checked that all of A and B lie in a domain
+// where that is exact for every term that can win -- min-plus: [0, 2^23) or
+// [2^30, 2^31) (a sum of two values below 2^23 is an integer below 2^24; a
+// sum with a value of 2^30 or more is at least 2^30 in both rings and never
+// beats the zero element 2^30); max-plus: (-2^23, 2^23) (every sum exact).
+// The running value starts at the int32 zero element, +-2^30, exact in
+// float, so the same terms win, and C is that exact integer.
+template <int SR, typename T, typename TG>
+__device__ __forceinline__ T zero_of() {
+    if constexpr (std::is_same<T, TG>::value) {
+        return Ring<SR, T>::zero();
+    } else {
+        static_assert(SR != TROP_SR_MAX_MUL, "no float mode for max-mul");
+        return SR == TROP_SR_MIN_PLUS ? (T)(1 << 30) : -(T)(1 << 30);
+    }
+}
+
+// Launch gate: a product whose int32 data was checked by the domain
+// pre-pass is launched twice, once in float mode (mode_run = 1) and once
+// with int32 arithmetic (mode_run = 0); each launch reads the pre-pass
+// flags (one per pre-pass workgroup, nonzero = a value outside the domain)
+// and only the one that matches proceeds.  Uniform over the workgroup.
+__device__ __forceinline__ bool mode_gate_open(const TropGemmParams& p) {
+    if (!p.mode_flags) return true;
+    int bad = 0;
+    for (int i = threadIdx.x; i < p.mode_slots; i += blockDim.x) bad |= p.mode_flags[i];
+    const bool in_domain = __syncthreads_or(bad) == 0;
+    return in_domain == (p.mode_run != 0);
+}
+
+template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false, typename TG = T>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
     using Cfg = GemmCfg<ARG, T, NARROW, GRES>;
     static_assert(!GRES || ARG, "the global resolve is an argmax form");
+    constexpr bool FM = !std::is_same<T, TG>::value;  // int32 data computed in float
     constexpr bool BLK = Cfg::BLOCK;  // resident block + LDS re-scan
     constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR, GEMM_SL = Cfg::SL;
     constexpr int NV = 16 * GEMM_SL / GEMM_THREADS;  // vectors per thread, operand and slice
@@ -548,8 +592,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     constexpr int CH = Cfg::CH;              // argmax chunk (terms)
     constexpr int QPC = CH / 4;              // k-quads per chunk
     constexpr int CPS = GEMM_SL / CH;        // chunks per slice
-    using LA = OpLoad<T, NV, LDR, false, GEMM_SL>;
-    using LB = OpLoad<T, NV, LDR, true, GEMM_SL>;
+    using LA = OpLoad<T, NV, LDR, false, GEMM_SL, TG>;
+    using LB = OpLoad<T, NV, LDR, true, GEMM_SL, TG>;
     static_assert(GEMM_SL % 16 == 0 && LDR % 4 == 0, "slots and rows keep the swizzle inside 16-word groups");
     // A's rows, then B's columns (one array: the global resolve parks a
     // finished tile over both)
@@ -573,13 +617,14 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     int64_t cL = blockIdx.x;  // tile being computed
     if (cL >= total || p.k == 0) return;  // K = 0 is handled by the fill kernel
     if (blockDim.x != GEMM_THREADS) return;   // launched with a block it was not built for
+    if (!mode_gate_open(p)) return;          // the other launch of a checked int32 product runs
 
     LA la;
     LB lb;
     la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid);
     lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid);
-    const T* const Ag = static_cast<const T*>(p.A);
-    const T* const Bg = static_cast<const T*>(p.B);
+    const TG* const Ag = static_cast<const TG*>(p.A);
+    const TG* const Bg = static_cast<const TG*>(p.B);
     int f_nsl = 0;  // slices of the tile being fetched
     auto point = [&](const TileCoord& tc) {
         la.at(Ag + tc.b * p.sa_batch + (SPLIT ? tc.s * p.kchunk * p.sa_col : 0), tc.row0, p.sa_row, p.sa_col, tid);
@@ -632,7 +677,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                best[r][c] = R::zero();
+                best[r][c] = zero_of<SR, T, TG>();
                 win[r][c] = -1;
                 idx[r][c] = 0;
             }
@@ -795,7 +840,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                             rw[o] = win[r][c];
                         }
                     __syncthreads();
-                    resolve_tile<SR, T, SPLIT, CH>(p, ct, tid, rv, rw);
+                    resolve_tile<SR, T, SPLIT, CH, TG>(p, ct, tid, rv, rw);
                     __syncthreads();
 #pragma unroll
                     for (int r = 0; r < GEMM_TR; ++r)
@@ -810,7 +855,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 // The tile is complete.  C takes the bits of the first
                 // winning term; they can differ from the running maximum's
                 // only for a zero value (+0 against -0).
-                if constexpr (std::is_same<T, float>::value) {
+                if constexpr (std::is_same<TG, float>::value) {
                     if constexpr (SR == TROP_SR_MAX_MUL) {
                         // the zero element is +0 and a term must exceed it to
                         // win: a zero value means nothing won
@@ -830,7 +875,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                     }
                 }
                 const int64_t c_off = ct.b * p.sc_batch + (SPLIT ? ct.s * p.c_split : 0);
-                T* __restrict__ C = static_cast<T*>(p.C) + c_off;
+                TG* __restrict__ C = static_cast<TG*>(p.C) + c_off;
                 int32_t* __restrict__ I = ARG ? p.argmax + c_off : nullptr;
                 const int k_off = SPLIT ? (int)(ct.s * p.kchunk) : 0;  // a split's argmax is global
 #pragma unroll
@@ -842,7 +887,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         const int64_t j = ct.col0 + tx + 16 * c;
                         if (j >= p.n) continue;
                         const int64_t o = i * p.sc_row + j * p.sc_col;
-                        C[o] = best[r][c];
+                        C[o] = static_cast<TG>(best[r][c]);  // (float mode: an exact integer)
                         if constexpr (ARG) I[o] = idx[r][c] + k_off;
                     }
                 }

@@ -62,6 +62,32 @@ TROP_GEMM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS, int32_t, TROP_ARGW_I32)
 TROP_GEMM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS, int32_t, TROP_ARGW_I32)
 TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t, TROP_ARGW_I32)
 
+// Float mode of int32 max-plus / min-plus products (the domain pre-pass,
+// then the float-mode kernel and the int32 kernel, each gated on its
+// flags): wide, narrow, global-resolve and value-only forms.
+#define TROP_GEMM_FM_ENTRIES(NAME, SR)                                                          \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_F32 void trop_gemm_fm_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, float, true, false, false, false, int32_t>(p);                      \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_fmn_##NAME(            \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, float, true, false, true, false, int32_t>(p);                       \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_GR void trop_gemm_fmg_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, float, true, false, false, true, int32_t>(p);                       \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_fmvo_##NAME(           \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, float, false, false, false, false, int32_t>(p);                     \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gemm_domain_##NAME(TropDomainParams p) { \
+        gemm_domain_body<SR>(p);                                                                \
+    }
+TROP_GEMM_FM_ENTRIES(maxplus_i32, TROP_SR_MAX_PLUS)
+TROP_GEMM_FM_ENTRIES(minplus_i32, TROP_SR_MIN_PLUS)
+
 extern "C" __global__ __launch_bounds__(256) void trop_fill(TropFillParams p) { fill_body(p); }
 
 extern "C" __global__ __launch_bounds__(256) void trop_argmax_compose(TropComposeParams p) {

@@ -321,11 +321,14 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
         P.off_wr = off;
         off += align_up((size_t)(P.nb * P.K * P.gn) * 4);
     }
-    const SplitK sk = plan_splitk(P.gm, P.gn, P.K, P.nb);
-    if (sk.bytes > 0) {
+    // the GEMM's own workspace: split-K partials, or the domain flags of
+    // the float mode of int32 products
+    P.gemm_split = plan_splitk(P.gm, P.gn, P.K, P.nb).ksplit > 1;
+    const size_t gws = gemm_workspace_bytes(P.gm, P.gn, P.K, P.nb);
+    if (gws > 0) {
         P.off_split = off;
-        P.split_bytes = sk.bytes;
-        off += sk.bytes;
+        P.split_bytes = gws;
+        off += ws_align(gws);
     }
     P.ws = off;
     return TROP_OK;
@@ -338,7 +341,7 @@ std::string pair_describe(const Plan& P) {
                   "n=%lld k=%lld%s; A=%s%s B=%s%s out=%s%s; workspace=%zu",
                   P.batch.c_str(), P.left.c_str(), P.right.c_str(), P.contracted.c_str(), P.a_red.c_str(),
                   P.b_red.c_str(), P.swap ? "B(x)A" : "A(x)B", (long long)P.nb, (long long)P.gm,
-                  (long long)P.gn, (long long)P.K, P.split_bytes ? " splitK" : "",
+                  (long long)P.gn, (long long)P.K, P.gemm_split ? " splitK" : "",
                   (P.swap ? P.b_fold : P.a_fold) ? "fold" : "gather:",
                   (P.swap ? P.b_fold : P.a_fold) ? "" : gather_path_name((P.swap ? P.gb : P.ga).path),
                   (P.swap ? P.a_fold : P.b_fold) ? "fold" : "gather:",
@@ -463,7 +466,7 @@ extern "C" trop_status tropical_contract_pair_workspace_size(const char* spec, c
     // upper bound: room for both operand pre-passes and the output permute
     size_t ws = align_up((size_t)(P.nb * P.M * P.K) * 4) + align_up((size_t)(P.nb * P.K * P.N) * 4);
     if (!P.c_direct) ws += 2 * align_up((size_t)(P.nb * P.M * P.N) * 4);
-    ws += plan_splitk(P.M, P.N, P.K, P.nb).bytes;  // K split of a long, narrow product
+    ws += ws_align(gemm_workspace_bytes(P.M, P.N, P.K, P.nb));  // split K, or int32 float-mode flags
     // winners of the pre-pass reductions, for an argmax routed through them
     if (!P.a_red.empty()) ws += align_up((size_t)(P.nb * P.M * P.K) * 4);
     if (!P.b_red.empty()) ws += align_up((size_t)(P.nb * P.K * P.N) * 4);

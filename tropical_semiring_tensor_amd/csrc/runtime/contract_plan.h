@@ -35,8 +35,10 @@ struct PairPlan {
     trop_strides sA{}, sB{};
     GatherPlan ga{}, gb{}, gc{};
     // workspace layout of the step (bytes, relative to its scratch base);
-    // split_bytes > 0: the GEMM is split along K, partials at off_split
+    // split_bytes > 0: the GEMM's own workspace at off_split (split-K
+    // partials when gemm_split, else the float-mode domain flags)
     size_t off_a = 0, off_b = 0, off_c = 0, off_i = 0, off_split = 0, split_bytes = 0, ws = 0;
+    bool gemm_split = false;
     // argmax through pre-pass reductions: the winners of the GEMM's left /
     // right operand's reduction (when it has one), in its canonical layout,
     // and the extents of A's and B's reduced labels

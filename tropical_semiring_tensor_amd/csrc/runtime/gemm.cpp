@@ -77,6 +77,30 @@ const int64_t kGresMinK = [] {
     return v && *v ? (int64_t)std::strtoll(v, nullptr, 10) : (int64_t)256;
 }();
 
+// Float mode of int32 max-plus / min-plus products: the domain pre-pass
+// runs kFmSlots workgroups, one flag each, in the workspace; it is taken
+// for products of at least kFmMinTerms terms (below that the pre-pass and
+// the second, gated launch cost more than the float arithmetic saves).
+// TROPICAL_GEMM_INT_FLOAT=0 never takes it, =1 takes it at any size.
+constexpr int kFmSlots = 256;
+constexpr size_t kFmBytes = kFmSlots * sizeof(int32_t);
+constexpr int64_t kFmMinTerms = int64_t(1) << 32;
+
+int fm_knob() {
+    const char* v = std::getenv("TROPICAL_GEMM_INT_FLOAT");
+    if (!v || !*v) return -1;
+    return v[0] == '0' ? 0 : 1;
+}
+
+bool fm_size_ok(int64_t m, int64_t n, int64_t k, int64_t batch) {
+    const int knob = fm_knob();
+    if (knob >= 0) return knob == 1;
+    int64_t t = 0;
+    if (__builtin_mul_overflow(m, n, &t) || __builtin_mul_overflow(t, k, &t) || __builtin_mul_overflow(t, batch, &t))
+        return true;
+    return t >= kFmMinTerms;
+}
+
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     SplitK s;
     if (m <= 0 || n <= 0 || batch <= 0 || k < 2 * kSplitMinK) return s;
@@ -94,6 +118,13 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     const size_t part = (size_t)(ks * batch * m * n) * 4;
     s.bytes = 2 * ((part + 255) / 256 * 256);
     return s;
+}
+
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch) {
+    if (m <= 0 || n <= 0 || k <= 0 || batch <= 0) return 0;
+    const SplitK sk = plan_splitk(m, n, k, batch);
+    if (sk.bytes > 0) return sk.bytes;
+    return fm_size_ok(m, n, k, batch) ? kFmBytes : 0;
 }
 
 trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
@@ -227,20 +258,60 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
     // keeps every workgroup's tiles on one XCD.
-    int per_cu = kernel_occupancy(dev, kid);
-    if (per_cu < 1) per_cu = 1;
-    int64_t slots = (int64_t)device_cu_count(dev) * per_cu / 8 * 8;
-    if (slots < 8) slots = 8;
-    if (const char* cap = std::getenv("TROPICAL_GEMM_MAX_WORKGROUPS")) {  // tuning knob
-        long v = std::strtol(cap, nullptr, 10);
-        if (v >= 8) slots = v / 8 * 8;
+    auto launch_tiled = [&](KernelId id) -> trop_status {
+        int per_cu = kernel_occupancy(dev, id);
+        if (per_cu < 1) per_cu = 1;
+        int64_t slots = (int64_t)device_cu_count(dev) * per_cu / 8 * 8;
+        if (slots < 8) slots = 8;
+        if (const char* cap = std::getenv("TROPICAL_GEMM_MAX_WORKGROUPS")) {  // tuning knob
+            long v = std::strtol(cap, nullptr, 10);
+            if (v >= 8) slots = v / 8 * 8;
+        }
+        const uint32_t grid = (uint32_t)(total < slots ? total : slots);
+        const int block = kernel_block(dev, id);  // the launch bound the kernel was built with
+        if (block != 256 && block != 512 && block != 1024)
+            return fail(TROP_ERR_HIP, std::string(kernel_name(id)) + ": unexpected launch bound " +
+                                          std::to_string(block));
+        return launch(dev, id, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
+    };
+    // Float mode of an int32 max-plus / min-plus product: the domain
+    // pre-pass writes its flags into the workspace, then the float-mode
+    // kernel and the int32 kernel are both enqueued, each gated on the flags
+    // so that exactly one of them computes.  No host round trip.
+    const bool fm = dt == TROP_I32 && sr != TROP_MAX_MUL && !split && workspace && workspace_bytes >= kFmBytes &&
+                    fm_size_ok(m, n, k, batch);
+    if (fm) {
+        TropDomainParams d{};
+        d.A = static_cast<const int32_t*>(A);
+        d.B = static_cast<const int32_t*>(B);
+        d.flags = static_cast<int32_t*>(workspace);
+        d.sa_row = sA.row;
+        d.sa_col = sA.col;
+        d.sa_batch = sA.batch;
+        d.sb_row = sB.row;
+        d.sb_col = sB.col;
+        d.sb_batch = sB.batch;
+        d.m = m;
+        d.n = n;
+        d.k = k;
+        d.batch = batch;
+        const int mp = sr == TROP_MIN_PLUS ? 1 : 0;
+        trop_status st = launch(dev, (KernelId)(K_GEMM_DOMAIN_MAXPLUS + mp), TROP_K_GEMM_DOMAIN, kFmSlots, 256, &d,
+                                stream);
+        if (st != TROP_OK) return st;
+        p.mode_flags = d.flags;
+        p.mode_slots = kFmSlots;
+        p.mode_run = 1;
+        const KernelId fid = (KernelId)((argmax ? (gres     ? K_GEMM_FMG_MAXPLUS
+                                                   : narrow ? K_GEMM_FMN_MAXPLUS
+                                                            : K_GEMM_FM_MAXPLUS)
+                                                : K_GEMM_FMVO_MAXPLUS) + mp);
+        st = launch_tiled(fid);
+        if (st != TROP_OK) return st;
+        p.mode_run = 0;
+        return launch_tiled(kid);
     }
-    uint32_t grid = (uint32_t)(total < slots ? total : slots);
-    const int block = kernel_block(dev, kid);  // the launch bound the kernel was built with
-    if (block != 256 && block != 512 && block != 1024)
-        return fail(TROP_ERR_HIP, std::string(kernel_name(kid)) + ": unexpected launch bound " +
-                                      std::to_string(block));
-    trop_status st = launch(dev, kid, TROP_K_GEMM_TILED, grid, (uint32_t)block, &p, stream);
+    trop_status st = launch_tiled(kid);
     if (st != TROP_OK || !split) return st;
     TropSplitMergeParams mp{};
     mp.pval = p.C;
@@ -273,6 +344,9 @@ trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, 
     if (workspace && sk.bytes > 0 && workspace_bytes < sk.bytes)
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(sk.bytes) + " bytes, got " + std::to_string(workspace_bytes));
+    // (the float mode of int32 products uses a workspace when one of its
+    // size is given, and is skipped otherwise)
+    const size_t ws_need = gemm_workspace_bytes(m, n, k, batch);
     int dev = -1;
     st = current_device(&dev);
     if (st != TROP_OK) return st;
@@ -299,13 +373,13 @@ trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, 
         st = check_device_span(argmax, dev, spanC, 4, "argmax");
         if (st != TROP_OK) return st;
     }
-    const bool use_ws = workspace && sk.bytes > 0;
+    const bool use_ws = workspace && ws_need > 0 && workspace_bytes >= ws_need;
     if (use_ws) {
-        st = check_device_span(workspace, dev, (int64_t)(sk.bytes / 4), 4, "workspace");
+        st = check_device_span(workspace, dev, (int64_t)(ws_need / 4), 4, "workspace");
         if (st != TROP_OK) return st;
     }
     st = run_gemm(dev, semiring, dtype, A, sA, B, sB, C, sC, argmax, m, n, k, batch,
-                  static_cast<hipStream_t>(stream), use_ws ? workspace : nullptr, use_ws ? sk.bytes : 0);
+                  static_cast<hipStream_t>(stream), use_ws ? workspace : nullptr, use_ws ? ws_need : 0);
     return st == TROP_OK ? ok() : st;
 }
 
@@ -334,6 +408,6 @@ extern "C" trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_
     using namespace trop;
     if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
-    *bytes = plan_splitk(m, n, k, batch).bytes;
+    *bytes = gemm_workspace_bytes(m, n, k, batch);
     return ok();
 }

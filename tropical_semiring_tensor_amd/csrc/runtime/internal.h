@@ -74,6 +74,19 @@ enum KernelId : int {
     K_GATHER_FLATGB_N2,
     K_GEMM_BACKWARD_RANGE_PLUS,  // backward, lane form over 64-bin ranges
     K_GEMM_BACKWARD_RANGE_MUL,
+    // float mode of int32 max-plus / min-plus: per form, max-plus then
+    // min-plus (wide, narrow, global resolve, value only), and the domain
+    // pre-pass
+    K_GEMM_FM_MAXPLUS,
+    K_GEMM_FM_MINPLUS,
+    K_GEMM_FMN_MAXPLUS,
+    K_GEMM_FMN_MINPLUS,
+    K_GEMM_FMG_MAXPLUS,
+    K_GEMM_FMG_MINPLUS,
+    K_GEMM_FMVO_MAXPLUS,
+    K_GEMM_FMVO_MINPLUS,
+    K_GEMM_DOMAIN_MAXPLUS,
+    K_GEMM_DOMAIN_MINPLUS,
     K_COUNT
 };
 const char* kernel_name(KernelId id);
@@ -157,6 +170,11 @@ struct SplitK {
     size_t bytes = 0;
 };
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch);
+// Workspace a product of this shape can use: the split-K partials when it
+// is split, else room for the domain flags of the float mode of int32
+// max-plus / min-plus when it is large enough to take it (any dtype: the
+// sizing calls know no dtype), else 0.  Host-only.
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
 // Enqueue without re-validating pointers (used by the contraction driver).
 // `workspace` (may be NULL) holds plan_splitk(...).bytes when a split is
 // wanted; without it the product is not split.

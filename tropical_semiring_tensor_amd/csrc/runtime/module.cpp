@@ -61,7 +61,12 @@ const std::vector<std::string>& kernel_names() {
             "trop_gather_flatg_n1",          "trop_gather_flatg_n2",
             "trop_gather_flatb_n1",          "trop_gather_flatb_n2",
             "trop_gather_flatgb_n1",         "trop_gather_flatgb_n2",
-            "trop_gemm_backward_range_plus", "trop_gemm_backward_range_mul"};
+            "trop_gemm_backward_range_plus", "trop_gemm_backward_range_mul",
+            "trop_gemm_fm_maxplus_i32",      "trop_gemm_fm_minplus_i32",
+            "trop_gemm_fmn_maxplus_i32",     "trop_gemm_fmn_minplus_i32",
+            "trop_gemm_fmg_maxplus_i32",     "trop_gemm_fmg_minplus_i32",
+            "trop_gemm_fmvo_maxplus_i32",    "trop_gemm_fmvo_minplus_i32",
+            "trop_gemm_domain_maxplus_i32",  "trop_gemm_domain_minplus_i32"};
         static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
         static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
         std::vector<std::string> v;
