@@ -473,3 +473,44 @@ def test_permute_many_small_axes(tb, orc, monkeypatch, mode, shape):
             o64 = tb.tropical_permute(x64d, perm)
             torch.cuda.synchronize()
             assert_bits_equal(o64.cpu().numpy(), orc.permute(x64.numpy(), perm), f"f64 {shape} {perm}")
+
+
+# reductions with many outputs along an input-contiguous last axis: four
+# adjacent outputs per thread with 16-byte loads (TROPICAL_REDUCE_VEC=0
+# keeps one output per thread); both against the oracle
+VEC_TRACE_CASES = [("iij", "j", (7, 7, 72)), ("ijk", "jk", (300, 8, 16)), ("ijk", "ik", (5, 300, 12)),
+                   ("iaib", "ab", (40, 3, 40, 8)), ("abcd", "cd", (6, 7, 8, 12)), ("iij", "j", (64, 64, 8192))]
+
+
+@pytest.mark.parametrize("vec", [True, False])
+@pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "f32"), ("max_mul", "f32"),
+                                   ("max_plus", "i32"), ("min_plus", "i32"), ("max_mul", "i32")])
+def test_trace_reduce_vec(tb, orc, monkeypatch, vec, sr, dt):
+    if not vec:
+        monkeypatch.setenv("TROPICAL_REDUCE_VEC", "0")
+    for inl, outl, shape in VEC_TRACE_CASES:
+        g = torch.Generator().manual_seed(sum(shape) + len(inl))
+        if dt == "i32":
+            x = torch.randint(-3, 4, shape, generator=g, dtype=torch.int32)
+        else:
+            x = torch.randint(-3, 4, shape, generator=g).float()
+            u = torch.rand(shape, generator=g)
+            x[u < 0.1] = -0.0
+            x[(u >= 0.1) & (u < 0.15)] = float("nan")
+            x[(u >= 0.15) & (u < 0.2)] = float("-inf") if sr != "min_plus" else float("inf")
+        out = tb.tropical_diag_gather(sr, x.to(DEV), inl, outl)
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), orc.diag_gather(sr, x.numpy(), inl, outl),
+                          f"{sr} {dt} {inl}->{outl} {shape} vec={vec}")
+    # winners of a vectorised pre-pass reduction route a contraction's argmax
+    A = torch.randint(-2, 3, (5, 40, 52), generator=g).float()
+    B = torch.randint(-2, 3, (52, 24), generator=g).float()
+    if dt == "i32":
+        A, B = A.to(torch.int32), B.to(torch.int32)
+    if sr == "max_mul":
+        A, B = A.abs(), B.abs()
+    C, I = tb.tropical_contract_pair("abj,jk->bk", sr, A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair("abj,jk->bk", sr, A.numpy(), B.numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, f"routed {sr} {dt} vec={vec}")
+    assert_equal(I.cpu().numpy(), Ir, f"routed argmax {sr} {dt} vec={vec}")

@@ -154,6 +154,9 @@ struct TropGatherParams {
     // outputs' lanes are; floor(r / rshape[d]) by (rmag_m, rmag_s) when
     // red_idx32 (every reduction index below 2^31)
     int32_t red_o, red_sfast, red_idx32;
+    // red_vec: the four-outputs-per-thread form applies (strides and
+    // extents allow it; the pointers' alignment is checked at launch)
+    int32_t red_vec;
     uint32_t rmag_m[TROP_MAX_DIMS];
     uint32_t rmag_s[TROP_MAX_DIMS];
 };

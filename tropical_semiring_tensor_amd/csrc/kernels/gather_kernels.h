@@ -616,6 +616,69 @@ __device__ __forceinline__ T shfl_xor_t(T v, int m) {
     }
 }
 
+// Reduction with many outputs whose last axis is contiguous in the input
+// (one thread per output would read 4 bytes at a time, a long-strided walk
+// per thread): each thread takes four adjacent outputs and reads the four
+// values at each reduction position with one 16-byte load, eight positions
+// in flight, then scans them in ascending position with the strict test --
+// the same first winner and bits as the sequential definition, per output.
+// The host checks: the last output axis has input stride 1 and extent a
+// multiple of 4, every other output and reduction stride is a multiple of
+// 4, the reduction has fewer than 2^31 positions, and the input and outputs
+// are 16-byte aligned.
+template <int SR, typename T>
+__device__ __forceinline__ void gather_reduce_vec_body(const TropGatherParams& p) {
+    using R = Ring<SR, T>;
+    using V = vec4<T>;
+    constexpr int U = 8;  // reduction positions in flight
+    const T* in = static_cast<const T*>(p.in[0]);
+    T* out = static_cast<T*>(p.out[0]);
+    int32_t* win_out = p.ntensors == 2 ? static_cast<int32_t*>(p.out[1]) : nullptr;
+    const int64_t inner = p.shape[p.ndim - 1];
+    const int64_t nvec = p.total / 4;
+    const int rt = (int)p.rtotal;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = 4 * v;
+        const int64_t base = gather_row_offset(p, o / inner) + o % inner;
+        T best[4] = {R::zero(), R::zero(), R::zero(), R::zero()};
+        int win[4] = {0, 0, 0, 0};
+        auto offset = [&](int r) -> int64_t {
+            if (p.nred == 1) return (int64_t)r * p.rstride[0];
+            int64_t off = 0;
+            uint32_t rr = (uint32_t)r;
+            for (int d = p.nred - 1; d >= 0; --d) {
+                const uint32_t q = fdiv(rr, p.rmag_m[d], p.rmag_s[d]);
+                off += (int64_t)(rr - q * (uint32_t)p.rshape[d]) * p.rstride[d];
+                rr = q;
+            }
+            return off;
+        };
+        auto take = [&](const V& x, int r) {
+            const T e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool up = R::better(e[c], best[c]);
+                best[c] = up ? e[c] : best[c];
+                win[c] = up ? r : win[c];
+            }
+        };
+        int r = 0;
+        for (; r + U <= rt; r += U) {
+            V x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(in + base + offset(r + u)));
+#pragma unroll
+            for (int u = 0; u < U; ++u) take(x[u], r + u);
+        }
+        for (; r < rt; ++r) take(__builtin_nontemporal_load(reinterpret_cast<const V*>(in + base + offset(r))), r);
+        __builtin_nontemporal_store(V{best[0], best[1], best[2], best[3]}, reinterpret_cast<V*>(out + o));
+        if (win_out)
+            __builtin_nontemporal_store(vec4<int32_t>{win[0], win[1], win[2], win[3]},
+                                        reinterpret_cast<vec4<int32_t>*>(win_out + o));
+    }
+}
+
 template <int SR, typename T>
 __device__ __forceinline__ void gather_reduce_body(const TropGatherParams& p) {
     using R = Ring<SR, T>;

@@ -50,6 +50,10 @@ using namespace trop;
         TropGatherParams p) {                                                                   \
         gather_reduce_body<SR, T>(p);                                                           \
     }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gather_reduce_vec_##NAME(            \
+        TropGatherParams p) {                                                                   \
+        gather_reduce_vec_body<SR, T>(p);                                                       \
+    }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_splitk_merge_##NAME(            \
         TropSplitMergeParams p) {                                                               \
         splitk_merge_body<SR, T>(p);                                                            \

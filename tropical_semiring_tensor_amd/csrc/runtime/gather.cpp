@@ -374,6 +374,14 @@ trop_status plan_gather(int ndim, const int64_t* oshape, const int64_t* ostride,
         p.red_idx32 = rtotal < (int64_t(1) << 31) ? 1 : 0;
         for (int d = 0; d < nr && p.red_idx32; ++d)
             if (p.rshape[d] >= 2) magic((uint64_t)p.rshape[d], &p.rmag_m[d], &p.rmag_s[d]);
+        // One slice per output and the last output axis contiguous in the
+        // input with every stride a multiple of 4 elements: four adjacent
+        // outputs per thread with 16-byte loads (TROPICAL_REDUCE_VEC=0: never)
+        bool vec = S == 1 && p.red_idx32 && p.istride[nd - 1] == 1 && p.shape[nd - 1] % 4 == 0 &&
+                   !(env_long("TROPICAL_REDUCE_VEC", 1) == 0);
+        for (int d = 0; d < nd - 1 && vec; ++d) vec = p.istride[d] % 4 == 0;
+        for (int d = 0; d < nr && vec; ++d) vec = p.rstride[d] % 4 == 0;
+        p.red_vec = vec ? 1 : 0;
         return TROP_OK;
     }
     if (env_flag("TROPICAL_FORCE_NAIVE_PERMUTE")) {
@@ -603,6 +611,11 @@ trop_status run_gather(int dev, GatherPlan& plan, int ntensors, const void* cons
         case GP_REDUCE: {
             const int ri = ring_index(sr, dt);
             if (ri < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
+            const bool vec = p.red_vec && aligned16(p.in[0]) && aligned16(p.out[0]) &&
+                             (ntensors < 2 || aligned16(p.out[1])) && p.rtotal > 0;
+            if (vec)
+                return launch(dev, (KernelId)(K_GATHER_REDUCE_VEC_MAXPLUS_F32 + ri), TROP_K_GATHER_REDUCE,
+                              grid_for(p.total / 4, 256), 256, &p, stream);
             return launch(dev, (KernelId)(K_GATHER_REDUCE_MAXPLUS_F32 + ri), TROP_K_GATHER_REDUCE,
                           grid_for(p.total, p.red_o), 256, &p, stream);
         }

@@ -32,7 +32,8 @@ enum KernelId : int {
     K_GEMM_SPLITK_MERGE_MAXPLUS_F32 = K_GATHER_REDUCE_MAXPLUS_F32 + NRING,  // merge of split-K partials
     K_GEMM_TILED_N_MAXPLUS_F32 = K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + NRING,  // with argmax, few tiles
     K_GEMM_TILED_G_MAXPLUS_F32 = K_GEMM_TILED_N_MAXPLUS_F32 + NRING,  // with argmax, global resolve (long K)
-    K_FILL = K_GEMM_TILED_G_MAXPLUS_F32 + NRING,
+    K_GATHER_REDUCE_VEC_MAXPLUS_F32 = K_GEMM_TILED_G_MAXPLUS_F32 + NRING,  // reduce, 4 outputs per thread
+    K_FILL = K_GATHER_REDUCE_VEC_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,

@@ -39,7 +39,7 @@ const std::vector<std::string>& kernel_names() {
                                                "trop_gemm_tiled_split_", "trop_gemm_tiled_vo_split_",
                                                "trop_gemm_simple_",      "trop_gather_reduce_",
                                                "trop_gemm_splitk_merge_", "trop_gemm_tiled_n_",
-                                               "trop_gemm_tiled_g_"};
+                                               "trop_gemm_tiled_g_",     "trop_gather_reduce_vec_"};
         static const char* const singles[] = {
             "trop_fill",                     "trop_gather_copy",
             "trop_gather_tiled",             "trop_gather_naive",
