@@ -26,15 +26,20 @@ def tb():
     return binding
 
 
-@pytest.fixture(autouse=True, params=["auto", "wide", "narrow", "global"])
+@pytest.fixture(autouse=True, params=["auto", "wide", "narrow", "global", "general"])
 def gemm_setting(request, monkeypatch):
     """Every test under every argmax kernel setting: the host picks the
     global-resolve kernel (two-slice ring, argmax resolved once per tile
     from global memory) for K > 256, else the narrow one (K-block 256,
     loads ahead, one workgroup per CU) for fewer than two tiles per CU and
     the wide one (float: K-block 128, 4 waves per SIMD) otherwise; "wide",
-    "narrow" and "global" force one for any shape."""
-    if request.param != "auto":
+    "narrow" and "global" force one for any shape.  "general": the automatic
+    choice with the instances whose operand layouts are fixed at compile
+    time switched off (their general counterparts then run the same
+    shapes)."""
+    if request.param == "general":
+        monkeypatch.setenv("TROPICAL_GEMM_FIXED_LAYOUT", "0")
+    elif request.param != "auto":
         monkeypatch.setenv("TROPICAL_GEMM_SETTING", request.param)
     return request.param
 

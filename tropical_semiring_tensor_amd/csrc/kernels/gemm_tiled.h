@@ -256,7 +256,13 @@ __device__ __forceinline__ T to_compute(TG x) {
     return static_cast<T>(x);
 }
 
-template <typename T, int NV, int LDR, bool SWZ, int SL, typename TG = T>
+// Operand layout of a kernel instance: read from the launch's arguments
+// (LAYOUT_ANY), or fixed at compile time to 16-byte vectors along k
+// (LAYOUT_KV) or along the rows / columns (LAYOUT_MV), which removes the
+// other paths and their registers.
+constexpr int LAYOUT_ANY = 0, LAYOUT_KV = 1, LAYOUT_MV = 2;
+
+template <typename T, int NV, int LDR, bool SWZ, int SL, typename TG = T, int LAYOUT = LAYOUT_ANY>
 struct OpLoad {
     using V = vec4<TG>;
     const TG* q0;      // element 0 of vector 0 of slice 0
@@ -269,25 +275,27 @@ struct OpLoad {
     int lds0;          // LDS word offset of element 0 (slot 0)
     int lds_v;         // LDS words between vectors v and v + 1
     int kv;            // k between vectors v and v + 1
-    bool mn_c, vec, mn_full;
+    bool mn_c_, vec_, mn_full;
+    __device__ __forceinline__ bool mn_c() const { return LAYOUT == LAYOUT_ANY ? mn_c_ : LAYOUT == LAYOUT_MV; }
+    __device__ __forceinline__ bool vec() const { return LAYOUT == LAYOUT_ANY ? vec_ : true; }
 
     // Position of this thread's elements (independent of the tile).
     __device__ __forceinline__ void init(int mode, int v16, int64_t str_mn, int64_t str_k,
                                          int64_t mnl, int64_t kl, int tid) {
-        mn_c = (mode == TROP_LOAD_MN_CONTIG);
-        vec = v16 != 0;
+        mn_c_ = (mode == TROP_LOAD_MN_CONTIG);
+        vec_ = v16 != 0;
         mn_lim = mnl;
         k_lim = kl;
         k_step = (int64_t)SL * str_k;
         // vector v + 1 = vector index + GEMM_THREADS: the same row, k further
         // on by GEMM_THREADS / 16 (MN_CONTIG) or 16 GEMM_THREADS / 256
         // (K_CONTIG)
-        kv = mn_c ? mc_k(GEMM_THREADS) : kc_k(GEMM_THREADS);
+        kv = mn_c() ? mc_k(GEMM_THREADS) : kc_k(GEMM_THREADS);
         v_step = kv * str_k;
         lds_v = kv;
         // (the swizzle only touches bits 2-3 of k, and the slot offset and
         // vector steps added later are multiples of 16)
-        if (mn_c) {
+        if (mn_c()) {
             e_str = str_mn;
             k0 = mc_k(tid);
             mn = mc_row(tid);
@@ -304,7 +312,7 @@ struct OpLoad {
     // tile's first row / column, str_mn the stride along it.
     __device__ __forceinline__ void at(const TG* X, int64_t mn_start, int64_t str_mn, int64_t str_k,
                                        int tid) {
-        const int64_t m_rel = mn_c ? mc_row(tid) : kc_row(tid);
+        const int64_t m_rel = mn_c() ? mc_row(tid) : kc_row(tid);
         mn = mn_start + m_rel;
         q0 = X + mn * str_mn + k0 * str_k;
         mn_full = mn_start + 64 <= mn_lim;
@@ -318,7 +326,7 @@ struct OpLoad {
         for (int v = 0; v < NV; ++v) {
             const TG* qv = q + v * v_step;
             if (full) {
-                if (vec) {
+                if (vec()) {
                     const V x = *reinterpret_cast<const V*>(qv);
                     r[v][0] = to_compute<T>(x.x);
                     r[v][1] = to_compute<T>(x.y);
@@ -331,8 +339,8 @@ struct OpLoad {
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int64_t kk = kb + kv * v + (mn_c ? 0 : e);
-                    const int64_t mm = mn + (mn_c ? e : 0);
+                    const int64_t kk = kb + kv * v + (mn_c() ? 0 : e);
+                    const int64_t mm = mn + (mn_c() ? e : 0);
                     r[v][e] = (kk < k_lim && mm < mn_lim) ? to_compute<T>(qv[e * e_str]) : pad;
                 }
             }
@@ -344,7 +352,7 @@ struct OpLoad {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             T* d = S + lds0 + sk + lds_v * v;
-            if (mn_c) {
+            if (mn_c()) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) d[e * LDR] = r[v][e];
             } else {
@@ -416,7 +424,7 @@ constexpr int GEMM_RLD = 65;  // row length of the parked tile (words; odd: rows
 #else
 #define TROP_RESOLVE_ATTR __forceinline__
 #endif
-template <int SR, typename T, bool SPLIT, int CH, typename TG = T>
+template <int SR, typename T, bool SPLIT, int CH, typename TG = T, bool FIXED_KV = false>
 __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoord ct, int tid, const T* rv,
                                              int* rw) {
     using R = Ring<SR, T>;
@@ -436,7 +444,9 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
     const int rlim = (int)(p.m - ct.row0 < GEMM_BM ? p.m - ct.row0 : GEMM_BM);
     const int clim = (int)(p.n - ct.col0 < GEMM_BN ? p.n - ct.col0 : GEMM_BN);
     const int kt32 = (int)kt;  // K < 2^31
-    if (a_kv && b_kv && (kt32 & 3) == 0) {
+    // (FIXED_KV: an instance for operands read along k in 16-byte vectors,
+    // launched only when K is a multiple of 4)
+    if (FIXED_KV || (a_kv && b_kv && (kt32 & 3) == 0)) {
         // both operands k-contiguous and K a multiple of 4: every quad is
         // wholly inside or wholly past K, and each lane makes one 16-byte
         // load per operand and quad (a lane with nothing to read loads the
@@ -500,6 +510,7 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         }
         return;
     }
+    if constexpr (FIXED_KV) return;
     for (int st = 0; st < PER_WAVE / 16; ++st) {
         const int o = wave * PER_WAVE + 16 * st + (lane >> 2);
         const int row = o >> 6, col = o & 63;
@@ -577,7 +588,8 @@ __device__ __forceinline__ bool mode_gate_open(const TropGemmParams& p) {
     return in_domain == (p.mode_run != 0);
 }
 
-template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false, typename TG = T>
+template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false, typename TG = T,
+          int LAYOUT_A = LAYOUT_ANY, int LAYOUT_B = LAYOUT_ANY>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
@@ -592,8 +604,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     constexpr int CH = Cfg::CH;              // argmax chunk (terms)
     constexpr int QPC = CH / 4;              // k-quads per chunk
     constexpr int CPS = GEMM_SL / CH;        // chunks per slice
-    using LA = OpLoad<T, NV, LDR, false, GEMM_SL, TG>;
-    using LB = OpLoad<T, NV, LDR, true, GEMM_SL, TG>;
+    using LA = OpLoad<T, NV, LDR, false, GEMM_SL, TG, LAYOUT_A>;
+    using LB = OpLoad<T, NV, LDR, true, GEMM_SL, TG, LAYOUT_B>;
     static_assert(GEMM_SL % 16 == 0 && LDR % 4 == 0, "slots and rows keep the swizzle inside 16-word groups");
     // A's rows, then B's columns (one array: the global resolve parks a
     // finished tile over both)
@@ -840,7 +852,8 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                             rw[o] = win[r][c];
                         }
                     __syncthreads();
-                    resolve_tile<SR, T, SPLIT, CH, TG>(p, ct, tid, rv, rw);
+                    resolve_tile<SR, T, SPLIT, CH, TG, LAYOUT_A == LAYOUT_KV && LAYOUT_B == LAYOUT_KV>(p, ct, tid, rv,
+                                                                                            rw);
                     __syncthreads();
 #pragma unroll
                     for (int r = 0; r < GEMM_TR; ++r)

@@ -35,6 +35,14 @@ using namespace trop;
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, false, false, true>(p);                                    \
     }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_GR void trop_gemm_tiled_gkk_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, true, T, LAYOUT_KV, LAYOUT_KV>(p);           \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_km_##NAME(     \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV>(p);          \
+    }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, true>(p);                                                  \
@@ -85,6 +93,10 @@ TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t, TROP_ARGW_I32)
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_fmvo_##NAME(           \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, float, false, false, false, false, int32_t>(p);                     \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_F32 void trop_gemm_fmkm_##NAME( \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, float, true, false, false, false, int32_t, LAYOUT_KV, LAYOUT_MV>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_domain_##NAME(TropDomainParams p) { \
         gemm_domain_body<SR>(p);                                                                \

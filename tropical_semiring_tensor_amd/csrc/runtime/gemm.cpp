@@ -22,6 +22,11 @@ bool env_flag(const char* name) {
     return v && *v && std::strcmp(v, "0") != 0;
 }
 
+bool env_flag_off(const char* name) {
+    const char* v = std::getenv(name);
+    return v && std::strcmp(v, "0") == 0;
+}
+
 constexpr uint32_t kMaxGrid = 1u << 30;
 
 uint32_t grid_for(int64_t work, int64_t per_block) {
@@ -249,11 +254,23 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         }
         if (std::strcmp(f, "global") == 0) gres = argmax;
     }
+    // the global-resolve instance with both operands' loads fixed at
+    // compile time (16-byte vectors along k) where the layout is that one
+    // (TROPICAL_GEMM_FIXED_LAYOUT=0: always the general instance)
+    // Instances with both operands' loads fixed at compile time (16-byte
+    // vectors; fewer registers) where the layout is theirs: the global
+    // resolve with A and B read along k, the wide form with A along k and B
+    // along its rows (row-major A and B).  TROPICAL_GEMM_FIXED_LAYOUT=0:
+    // always the general instances.
+    const bool fixed_ok = !env_flag_off("TROPICAL_GEMM_FIXED_LAYOUT");
+    const bool kmvec = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec && p.b_mode == TROP_LOAD_MN_CONTIG && p.b_vec;
+    const bool fixed = gres && kvec && fixed_ok;
+    const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
-              : (KernelId)((argmax ? (gres     ? K_GEMM_TILED_G_MAXPLUS_F32
+              : (KernelId)((argmax ? (gres     ? (fixed ? K_GEMM_TILED_GKK_MAXPLUS_F32 : K_GEMM_TILED_G_MAXPLUS_F32)
                                       : narrow ? K_GEMM_TILED_N_MAXPLUS_F32
-                                               : K_GEMM_TILED_MAXPLUS_F32)
+                                               : (fixed_km ? K_GEMM_TILED_KM_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32))
                                    : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
@@ -304,7 +321,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         p.mode_run = 1;
         const KernelId fid = (KernelId)((argmax ? (gres     ? K_GEMM_FMG_MAXPLUS
                                                    : narrow ? K_GEMM_FMN_MAXPLUS
-                                                            : K_GEMM_FM_MAXPLUS)
+                                                            : (fixed_km ? K_GEMM_FMKM_MAXPLUS : K_GEMM_FM_MAXPLUS))
                                                 : K_GEMM_FMVO_MAXPLUS) + mp);
         st = launch_tiled(fid);
         if (st != TROP_OK) return st;

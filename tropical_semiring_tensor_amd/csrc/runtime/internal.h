@@ -33,7 +33,9 @@ enum KernelId : int {
     K_GEMM_TILED_N_MAXPLUS_F32 = K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + NRING,  // with argmax, few tiles
     K_GEMM_TILED_G_MAXPLUS_F32 = K_GEMM_TILED_N_MAXPLUS_F32 + NRING,  // with argmax, global resolve (long K)
     K_GATHER_REDUCE_VEC_MAXPLUS_F32 = K_GEMM_TILED_G_MAXPLUS_F32 + NRING,  // reduce, 4 outputs per thread
-    K_FILL = K_GATHER_REDUCE_VEC_MAXPLUS_F32 + NRING,
+    K_GEMM_TILED_GKK_MAXPLUS_F32 = K_GATHER_REDUCE_VEC_MAXPLUS_F32 + NRING,  // global resolve, both operands k-vector
+    K_GEMM_TILED_KM_MAXPLUS_F32 = K_GEMM_TILED_GKK_MAXPLUS_F32 + NRING,  // wide, A k-vector, B column-vector
+    K_FILL = K_GEMM_TILED_KM_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,
@@ -88,6 +90,8 @@ enum KernelId : int {
     K_GEMM_FMVO_MINPLUS,
     K_GEMM_DOMAIN_MAXPLUS,
     K_GEMM_DOMAIN_MINPLUS,
+    K_GEMM_FMKM_MAXPLUS,  // float mode, wide, A k-vector, B column-vector
+    K_GEMM_FMKM_MINPLUS,
     K_COUNT
 };
 const char* kernel_name(KernelId id);

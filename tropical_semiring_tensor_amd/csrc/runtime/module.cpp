@@ -39,7 +39,8 @@ const std::vector<std::string>& kernel_names() {
                                                "trop_gemm_tiled_split_", "trop_gemm_tiled_vo_split_",
                                                "trop_gemm_simple_",      "trop_gather_reduce_",
                                                "trop_gemm_splitk_merge_", "trop_gemm_tiled_n_",
-                                               "trop_gemm_tiled_g_",     "trop_gather_reduce_vec_"};
+                                               "trop_gemm_tiled_g_",     "trop_gather_reduce_vec_",
+                                               "trop_gemm_tiled_gkk_",   "trop_gemm_tiled_km_"};
         static const char* const singles[] = {
             "trop_fill",                     "trop_gather_copy",
             "trop_gather_tiled",             "trop_gather_naive",
@@ -66,7 +67,8 @@ const std::vector<std::string>& kernel_names() {
             "trop_gemm_fmn_maxplus_i32",     "trop_gemm_fmn_minplus_i32",
             "trop_gemm_fmg_maxplus_i32",     "trop_gemm_fmg_minplus_i32",
             "trop_gemm_fmvo_maxplus_i32",    "trop_gemm_fmvo_minplus_i32",
-            "trop_gemm_domain_maxplus_i32",  "trop_gemm_domain_minplus_i32"};
+            "trop_gemm_domain_maxplus_i32",  "trop_gemm_domain_minplus_i32",
+            "trop_gemm_fmkm_maxplus_i32",    "trop_gemm_fmkm_minplus_i32"};
         static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
         static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
         std::vector<std::string> v;
