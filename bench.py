@@ -243,7 +243,7 @@ def main():
     value_gops = ops / (ms_per_step * 1e-3) / 1e9
     # One step is one launch of the GEMM kernel, back to back on one stream:
     # the timed region's per-step time is the kernel's average duration.
-    kernel = "trop_gemm_tiled_g_maxmul_f32"
+    kernel = "trop_gemm_tiled_gkk_maxmul_f32"
     roof = roofline_keys(ops, ms_per_step, kernel)
     roof["traffic"] = traffic_from_profile(w["name"])
     log(f"[bench] workload {HEADLINE}: {ms_per_step * 1e3:.1f} us/step, {value_gops:.0f} GOPS, "
@@ -380,7 +380,7 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     # workload 2 (64 x 256^3 max-plus), timed like the headline
     c2 = gemm_case(torch, tb, inputs, 2, dev)
     ms = timed_steps(torch, c2["step"], 200, 5, settle_s=0.3)
-    rec = roofline_keys(c2["ops"], ms, "trop_gemm_tiled_maxplus_f32")
+    rec = roofline_keys(c2["ops"], ms, "trop_gemm_tiled_km_maxplus_f32")
     rec.update({"GOPS": round(c2["ops"] / (ms * 1e-3) / 1e9, 1),
                 "traffic": traffic_from_profile(c2["w"]["name"])})
     out[c2["w"]["name"]] = rec
@@ -402,7 +402,7 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     # float-mode kernel computes; the plain call (no workspace) alongside
     c3 = gemm_case(torch, tb, inputs, 3, dev, workspace=True)
     ms = timed_steps(torch, c3["step"], 10, 1, settle_s=0.1)
-    rec = roofline_keys(c3["ops"], ms, "trop_gemm_fm_minplus_i32 (after trop_gemm_domain_minplus_i32)")
+    rec = roofline_keys(c3["ops"], ms, "trop_gemm_fmkm_minplus_i32 (after trop_gemm_domain_minplus_i32)")
     rec["GOPS"] = round(c3["ops"] / (ms * 1e-3) / 1e9, 1)
     rec["call"] = "tropical_gemm_strided_batched_ws (float mode)"
     plain = lambda: tb.tropical_gemm_strided_batched("min_plus", c3["Ad"], c3["Bd"], c3["C"], c3["I"])
