@@ -130,14 +130,15 @@ def test_backward_strided_views_and_one_sided(tb, orc):
 
 
 @pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
-                                  "TROPICAL_BACKWARD_RANGE"])
+                                  "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
 def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
     """Bins summed from denormal gradients, +0 / -0 mixes (a bin of only
     -0.0 items is +0.0, since sums start at +0.0), exact cancellations to
     zero and infinities: each kernel form's adds must round and keep
     denormals exactly as the oracle's sequential float32 loop does."""
     if knob:
-        monkeypatch.setenv(knob, "1")
+        # (the staged form is the default; its knob set to 0 turns it off)
+        monkeypatch.setenv(knob, "0" if knob == "TROPICAL_BACKWARD_STAGED" else "1")
     b, m, k, n = 2, 64, 40, 200
     g = torch.Generator().manual_seed(81)
     I = torch.randint(0, k, (b, m, n), generator=g, dtype=torch.int32)
@@ -157,6 +158,25 @@ def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
         run_both(tb, orc, "max_plus", None, None, I, G, k, f"{knob} {name}")
     # max-mul: the weight products themselves underflow into denormals
     run_both(tb, orc, "max_mul", A, B, I, cases["denormal"] * 1e18, k, f"{knob} max_mul denormal")
+
+
+@pytest.mark.parametrize("items", [3, 31, 32, 33, 64, 96, 100])
+def test_backward_staged_pieces(tb, orc, items):
+    """The staged form's pieces of 32 items: fewer than one piece, exactly
+    one, two and three, and a ragged last piece; bin counts that leave
+    waves with no range (k = 2), ranges of one bin (k = 4), a ragged last
+    range (k = 129) and full ranges (k = 256); segments across batch
+    entries and not a multiple of 64; contiguous (grad_a) and strided
+    (grad_b) items, both weights."""
+    g = torch.Generator().manual_seed(items)
+    b, m, n = 3, items, items   # grad_a walks n items per row, grad_b m per column
+    for k in (2, 4, 129, 256):
+        I = torch.randint(0, k, (b, m, n), generator=g, dtype=torch.int32)
+        G = torch.randn(b, m, n, generator=g)
+        A = torch.rand(b, m, k, generator=g) + 0.5
+        B = torch.rand(b, k, n, generator=g) + 0.5
+        for sr in ("max_plus", "max_mul"):
+            run_both(tb, orc, sr, A, B, I, G, k, f"staged items={items} k={k} {sr}")
 
 
 def test_backward_errors(tb):
@@ -191,14 +211,16 @@ def test_backward_maxmul_workload4_recipe(tb, orc):
 
 
 @pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
-                                  "TROPICAL_BACKWARD_RANGE"])
+                                  "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
 def test_backward_every_kernel_form(tb, orc, monkeypatch, knob):
-    """The same gradients from the 16-lanes-per-segment form (the default
-    for few segments), the lane-per-segment form, the wave-per-segment
-    form and the 64-bin range form, over hub-heavy and uniform argmaxes,
-    both weights."""
+    """The same gradients from the staged form (the default), the
+    16-lanes-per-segment form, the lane-per-segment form, the
+    wave-per-segment form, the 64-bin range form and the choice among them
+    without the staged form, over hub-heavy and uniform argmaxes, both
+    weights."""
     if knob:
-        monkeypatch.setenv(knob, "1")
+        # (the staged form is the default; its knob set to 0 turns it off)
+        monkeypatch.setenv(knob, "0" if knob == "TROPICAL_BACKWARD_STAGED" else "1")
     b, m, k, n = 3, 70, 200, 130
     g = torch.Generator().manual_seed(61)
     G = torch.randn(b, m, n, generator=g)

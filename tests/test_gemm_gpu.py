@@ -235,18 +235,21 @@ def test_simple_kernel_and_no_swizzle(tb, orc, monkeypatch):
 
 
 @pytest.mark.parametrize("coord64", [False, True])
-@pytest.mark.parametrize("row_raster", [False, True])
-def test_tile_orders(tb, orc, monkeypatch, coord64, row_raster):
-    # grouped raster (groups of 4 tile-rows, the last one shorter) and plain
-    # row-by-row order, with the 32- and 64-bit tile decodes: tile-row counts
-    # 1, 3, 5, 7, 9 and several batch entries, every output written once
+@pytest.mark.parametrize("rows", ["default", "1", "3", "8"])
+def test_tile_orders(tb, orc, monkeypatch, coord64, rows):
+    # grouped raster (groups of 3, 4 or 8 tile-rows, the last one shorter)
+    # and plain row-by-row order, with the 32- and 64-bit tile decodes:
+    # tile-row counts 1, 3, 5, 7, 9 and several batch entries, every output
+    # written once
     if coord64:
         monkeypatch.setenv("TROPICAL_GEMM_COORD64", "1")
-    if row_raster:
+    if rows == "1":
         monkeypatch.setenv("TROPICAL_GEMM_ROW_RASTER", "1")
+    elif rows != "default":
+        monkeypatch.setenv("TROPICAL_GEMM_GROUP_ROWS", rows)
     for shape in ((3, 40, 70, 500), (2, 130, 90, 200), (1, 300, 40, 190), (2, 450, 33, 70), (1, 520, 20, 600)):
         A, B = make("max_plus", "f32", *shape, seed=sum(shape))
-        check(tb, orc, "max_plus", A, B, f"tile order {shape} coord64={coord64} rows={row_raster}")
+        check(tb, orc, "max_plus", A, B, f"tile order {shape} coord64={coord64} rows={rows}")
     A, B = make("min_plus", "i32", 1, 300, 2000, 100, seed=9)
     C, I = gpu_gemm_ws(tb, "min_plus", A, B)
     Cr, Ir = orc.gemm("min_plus", A.numpy(), B.numpy())

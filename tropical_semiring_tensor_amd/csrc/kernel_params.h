@@ -44,11 +44,10 @@ struct TropGemmParams {
     int32_t coord32;
     uint32_t tl_m, tl_s, tn_m, tn_s, ks_m, ks_s;
     // grouped raster: inside a batch entry the tiles run in groups of
-    // TROP_GEMM_GROUP_ROWS tile-rows (the last group may be shorter), column
-    // by column and down the rows inside a group, so the workgroups that
-    // run at the same time share a few operand panels.  group_rows = 1:
-    // row by row.  gr_m / gr_s: magic pair of TROP_GEMM_GROUP_ROWS * tiles_n
-    // (coord32).
+    // group_rows tile-rows (the last group may be shorter), column by column
+    // and down the rows inside a group, so the workgroups that run at the
+    // same time share a few operand panels.  group_rows = 1: row by row.
+    // gr_m / gr_s: magic pair of group_rows * tiles_n (coord32).
     int32_t group_rows;
     uint32_t gr_m, gr_s;
     // launch gate of a checked int32 product (float mode): mode_slots flags

@@ -347,4 +347,222 @@ __device__ __forceinline__ void gemm_backward_split_body(const TropBackwardParam
     }
 }
 
+// Staged form for up to GBT_WAVES * GBT_RW = 256 bins: a workgroup owns 64
+// segments at a time and GBT_WAVES waves, wave w holding bins
+// [w W, w W + W) (W = ceil(bins / GBT_WAVES)) of all 64 segments, lane l
+// those of segment l, in LDS.  The segments' items come in pieces of GBT_T:
+// the whole workgroup loads a piece into registers (each thread a few items
+// of one segment, all loads issued at once, the next piece but one already
+// in flight while a piece is walked), multiplies in the max-mul weights and
+// writes keys and values to an LDS stage laid out [item][segment].  Then
+// every wave walks the piece in item order, lane l reading item t of its
+// own segment (64 consecutive words: no bank conflicts) and adding it to
+// its bin with a plain LDS read, add and write, a few items per round trip
+// (see the walk).  A bin is one lane's sum in ascending item order, so the
+// result is the sequential one.  The walk reads LDS only: the memory
+// latency of the items is paid once per piece for the whole workgroup
+// instead of once per few items per lane, and no LDS atomic is used (the
+// LDS float add costs about four cycles per active lane).
+constexpr int GBT_WAVES = 4;
+constexpr int GBT_THREADS = 64 * GBT_WAVES;
+constexpr int GBT_RW = 64;              // most bins per wave
+constexpr int GBT_LDR = GBT_RW + 1;     // padded row: lane l, bin k at bank (l + k) mod 64
+constexpr int GBT_T = 32;               // items per staged piece
+constexpr int GBT_G = 4;                // items per group of the walk (bins read together)
+constexpr int GBT_IPT = GBT_T * 64 / GBT_THREADS;  // items loaded per thread and piece
+static_assert(GBT_IPT % 4 == 0 && GBT_T % (4 * GBT_WAVES) == 0, "whole quads per thread");
+
+// VEC: items contiguous (c_item == 1), their count a multiple of 4 and every
+// segment start 16-byte aligned: a thread loads quads of items with one
+// 16-byte load per tensor; otherwise item t of the 64 segments is loaded
+// with one element load per lane (coalesced when segments are contiguous).
+template <bool MUL, bool VEC>
+__device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardParams& p) {
+    __shared__ float bins[GBT_WAVES * 64 * GBT_LDR];
+    __shared__ int32_t stage_k[2][GBT_T][64];
+    __shared__ float stage_v[2][GBT_T][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int32_t K = (int32_t)p.bins;  // <= GBT_WAVES * GBT_RW (checked on the host)
+    const int32_t W = (K + GBT_WAVES - 1) / GBT_WAVES;
+    const int32_t lo = wave * W;
+    const int32_t kn = K - lo < W ? (K - lo > 0 ? K - lo : 0) : W;  // bins of this wave (uniform)
+    float* const row = bins + (wave * 64 + lane) * GBT_LDR;
+    const int64_t nseg = p.segs * p.batch;
+    const int64_t items = p.items;
+    const int64_t ngroups = (nseg + 63) / 64;
+    const int64_t npieces = (items + GBT_T - 1) / GBT_T;
+    // item (within a piece) of this thread's j-th load: VEC, quads
+    // wave + GBT_WAVES h; else items wave + GBT_WAVES j
+    auto item_of = [&](int j) -> int {
+        return VEC ? 4 * (wave + GBT_WAVES * (j / 4)) + (j & 3) : wave + GBT_WAVES * j;
+    };
+
+    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+        const int64_t seg0 = g * 64;
+        const int64_t seg = seg0 + lane;  // this thread's segment, for loads and the walk
+        const bool live = seg < nseg;
+        const int64_t b = live ? seg / p.segs : 0, s = live ? seg % p.segs : 0;
+        const int32_t* ip = p.idx + b * p.c_batch + s * p.c_seg;
+        const float* gp = p.grad + b * p.c_batch + s * p.c_seg;
+        const float* wp = MUL ? p.w + b * p.w_batch : nullptr;
+        for (int32_t k = 0; k < kn; ++k) row[k] = 0.0f;
+        lds_order();
+
+        int32_t ka[GBT_IPT], kb[GBT_IPT];
+        float va[GBT_IPT], vb[GBT_IPT], wa[GBT_IPT];
+        // Piece pc's loads keep the raw values: whether an item exists (its
+        // segment is live and it lies before `items`) is applied when it is
+        // staged, so that no instruction right after a load waits on it, and
+        // every step issues the same loads (past the last piece they re-read
+        // the segment's last items, which is harmless), so the waits before
+        // staging count only the loads issued since.  A lane past the last
+        // segment reads the first segment's items.
+        // (a missing item's load is clamped to the segment's last item, an
+        // arithmetic clamp rather than a select, so that the compiler keeps
+        // the loads free of branches)
+        auto exists = [&](int64_t pc, int j) { return live && pc * GBT_T + item_of(j) < items; };
+        auto load = [&](int64_t pc, int32_t(&kr)[GBT_IPT], float(&vr)[GBT_IPT]) {
+            if (VEC) {
+#pragma unroll
+                for (int h = 0; h < GBT_IPT / 4; ++h) {
+                    const int64_t tc = min(pc * GBT_T + item_of(4 * h), items - 4);  // whole quads
+                    const int4 k4 = *reinterpret_cast<const int4*>(ip + tc);
+                    const float4 v4 = *reinterpret_cast<const float4*>(gp + tc);
+                    kr[4 * h + 0] = k4.x;
+                    kr[4 * h + 1] = k4.y;
+                    kr[4 * h + 2] = k4.z;
+                    kr[4 * h + 3] = k4.w;
+                    vr[4 * h + 0] = v4.x;
+                    vr[4 * h + 1] = v4.y;
+                    vr[4 * h + 2] = v4.z;
+                    vr[4 * h + 3] = v4.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < GBT_IPT; ++j) {
+                    const int64_t off = min(pc * GBT_T + item_of(j), items - 1) * p.c_item;
+                    kr[j] = ip[off];
+                    vr[j] = gp[off];
+                }
+            }
+        };
+        // max-mul: the weight of each item with a key in [0, bins) (others
+        // read the weight at (0, 0), which is in range, and are not added;
+        // the address is masked, not selected, for the same reason)
+        auto weights = [&](int64_t pc, const int32_t(&kr)[GBT_IPT]) {
+#pragma unroll
+            for (int j = 0; j < GBT_IPT; ++j) {
+                const bool valid = exists(pc, j) && (uint32_t)kr[j] < (uint32_t)K;
+                const int64_t t = pc * GBT_T + item_of(j);
+                wa[j] = wp[((int64_t)kr[j] * p.w_key + t * p.w_item) & -(int64_t)valid];
+            }
+        };
+        auto stage = [&](int buf, int64_t pc, const int32_t(&kr)[GBT_IPT], const float(&vr)[GBT_IPT]) {
+#pragma unroll
+            for (int j = 0; j < GBT_IPT; ++j) {
+                stage_k[buf][item_of(j)][lane] = exists(pc, j) ? kr[j] : -1;
+                stage_v[buf][item_of(j)][lane] = MUL ? vr[j] * wa[j] : vr[j];
+            }
+        };
+
+        // (no load at all when a segment has no items: the host does not
+        // validate the argmax / gradient pointers then)
+        if (npieces > 0) {
+            load(0, ka, va);
+            if (MUL) weights(0, ka);
+            stage(0, 0, ka, va);
+            load(1, ka, va);
+        }
+        __syncthreads();
+        // Piece pc: its keys and values are in stage buffer pc % 2, piece
+        // pc + 1 in registers `cur` (loaded one step ago), and piece pc + 2
+        // is loaded into `nxt` before the walk.  Two steps per iteration
+        // with the register sets swapped, so that no copy waits on a load.
+        auto step = [&](int64_t pc, int32_t(&ck)[GBT_IPT], float(&cv)[GBT_IPT], int32_t(&nk)[GBT_IPT],
+                        float(&nv)[GBT_IPT]) {
+            const int buf = (int)(pc & 1);
+            if (MUL) weights(pc + 1, ck);
+            load(pc + 2, nk, nv);
+            if (kn > 0) {
+                // the piece's keys and values first (the reads in flight
+                // together), then the adds in item order
+                int32_t kk[GBT_T];
+                float vv[GBT_T];
+#pragma unroll
+                for (int t = 0; t < GBT_T; ++t) {
+                    kk[t] = stage_k[buf][t][lane];
+                    vv[t] = stage_v[buf][t][lane];
+                }
+                // Groups of GBT_G items: the group's bins are read together,
+                // each new sum starts from the latest earlier item of the
+                // group with the same bin (else from the read), and the sums
+                // are written in item order, so a bin sees its items in
+                // order with one LDS round trip per group.  Keys outside
+                // [lo, lo + kn) (-1 included) use bins kn .. GBT_RW of the
+                // row, which are never read out.
+#pragma unroll
+                for (int t0 = 0; t0 < GBT_T; t0 += GBT_G) {
+                    uint32_t ix[GBT_G];
+                    float rd[GBT_G], nw[GBT_G];
+#pragma unroll
+                    for (int u = 0; u < GBT_G; ++u) {
+                        ix[u] = min((uint32_t)kk[t0 + u] - (uint32_t)lo, (uint32_t)GBT_RW);  // unsigned: no overflow
+                        rd[u] = row[ix[u]];
+                    }
+#pragma unroll
+                    for (int u = 0; u < GBT_G; ++u) {
+                        float a = rd[u];
+#pragma unroll
+                        for (int e = 0; e < u; ++e) a = ix[u] == ix[e] ? nw[e] : a;  // later e wins
+                        nw[u] = a + vv[t0 + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < GBT_G; ++u) row[ix[u]] = nw[u];
+                }
+            }
+            if (pc + 1 < npieces) stage(buf ^ 1, pc + 1, ck, cv);
+            __syncthreads();  // piece pc + 1 staged; piece pc's buffer is free
+        };
+        for (int64_t pc = 0; pc < npieces; pc += 2) {
+            step(pc, ka, va, kb, vb);
+            if (pc + 1 < npieces) step(pc + 1, kb, vb, ka, va);
+        }
+        lds_order();
+        // write the 64 segments' bins of this wave's range
+        if (kn > 0) {
+            constexpr int WB = 8;  // LDS reads in flight per batch of stores
+            if (p.o_bin == 1) {
+                // lane = bin: each segment's bins are one contiguous store
+                int64_t ob = seg0 / p.segs, os = seg0 - ob * p.segs;  // segment seg0 + r, stepped
+                for (int r0 = 0; r0 < 64; r0 += WB) {
+                    float v[WB];
+#pragma unroll
+                    for (int u = 0; u < WB; ++u) v[u] = bins[(wave * 64 + r0 + u) * GBT_LDR + lane];
+#pragma unroll
+                    for (int u = 0; u < WB; ++u) {
+                        if (seg0 + r0 + u < nseg && lane < kn) p.out[ob * p.o_batch + os * p.o_seg + lo + lane] = v[u];
+                        if (++os == p.segs) {
+                            os = 0;
+                            ++ob;
+                        }
+                    }
+                }
+            } else if (live) {
+                // lane = segment: bin k of the 64 segments side by side
+                float* out = p.out + b * p.o_batch + s * p.o_seg + (int64_t)lo * p.o_bin;
+                for (int32_t k0 = 0; k0 < kn; k0 += WB) {
+                    float v[WB];
+#pragma unroll
+                    for (int u = 0; u < WB; ++u) v[u] = row[k0 + u < GBT_RW ? k0 + u : GBT_RW];
+#pragma unroll
+                    for (int u = 0; u < WB; ++u)
+                        if (k0 + u < kn) out[(int64_t)(k0 + u) * p.o_bin] = v[u];
+                }
+            }
+        }
+        lds_order();
+    }
+}
+
 }  // namespace trop

@@ -180,13 +180,13 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
         const uint32_t t = lg - bs * tl;
         uint32_t tr, tc;
         if (p.group_rows > 1) {
-            constexpr uint32_t G = TROP_GEMM_GROUP_ROWS;
+            const uint32_t G = (uint32_t)p.group_rows;
             const uint32_t gsz = G * tn;
             const uint32_t gi = mdiv(t, gsz, p.gr_m, p.gr_s);
             const uint32_t r0 = gi * G;
             const uint32_t rows = min(G, (uint32_t)p.tiles_m - r0);
             const uint32_t w = t - gi * gsz;
-            tc = rows == G ? w / G : w / rows;
+            tc = w / rows;
             tr = r0 + (w - tc * rows);
         } else {
             tr = mdiv(t, tn, p.tn_m, p.tn_s);
@@ -208,7 +208,7 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
     const int64_t bs = lg / tiles;
     int64_t tr, tc;
     if (p.group_rows > 1) {
-        constexpr int64_t G = TROP_GEMM_GROUP_ROWS;
+        const int64_t G = p.group_rows;
         const int64_t gsz = G * p.tiles_n;
         const int64_t r0 = t / gsz * G;
         const int64_t rows = p.tiles_m - r0 < G ? p.tiles_m - r0 : G;

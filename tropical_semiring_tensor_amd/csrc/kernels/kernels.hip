@@ -203,3 +203,13 @@ TROP_BACKWARD_SPLIT(plus, false, false)
 TROP_BACKWARD_SPLIT(plus_vec, false, true)
 TROP_BACKWARD_SPLIT(mul, true, false)
 TROP_BACKWARD_SPLIT(mul_vec, true, true)
+
+#define TROP_BACKWARD_STAGED(NAME, MUL, VEC)                                                     \
+    extern "C" __global__ __launch_bounds__(GBT_THREADS) void trop_gemm_backward_staged_##NAME(   \
+        TropBackwardParams p) {                                                                  \
+        gemm_backward_staged_body<MUL, VEC>(p);                                                  \
+    }
+TROP_BACKWARD_STAGED(plus, false, false)
+TROP_BACKWARD_STAGED(plus_vec, false, true)
+TROP_BACKWARD_STAGED(mul, true, false)
+TROP_BACKWARD_STAGED(mul_vec, true, true)

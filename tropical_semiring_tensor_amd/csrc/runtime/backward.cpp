@@ -60,16 +60,34 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
     p.items = items;
     p.bins = bins;
     p.mul = mul ? 1 : 0;
-    // Up to 256 bins: one lane per segment, each walking its items in order
-    // (cheap whatever the key distribution).  More bins: one wave per
-    // segment with the bins in LDS, the smallest chunk that holds them all
-    // (else 4096 and several passes).
+    // Up to 256 bins: one lane per segment and bin range, each walking its
+    // items in order (cheap whatever the key distribution).  More bins: one
+    // wave per segment with the bins in LDS, the smallest chunk that holds
+    // them all (else 4096 and several passes).
     if (bins <= 256 && !env_flag_set("TROPICAL_BACKWARD_WAVE")) {
         // 16-byte item loads when items are contiguous, a multiple of 4, and
         // every segment start is 16-byte aligned
         const bool vec = c_item == 1 && items % 4 == 0 && sC.batch % 4 == 0 && c_seg % 4 == 0 &&
                          (reinterpret_cast<uintptr_t>(argmax) & 15u) == 0 &&
                          (reinterpret_cast<uintptr_t>(grad_c) & 15u) == 0;
+        // The staged form: 64 segments and four bin ranges per workgroup,
+        // items loaded a piece at a time by the whole workgroup and walked
+        // from LDS.  The forms below stay for the knobs that force them
+        // (TROPICAL_BACKWARD_LANE / _SPLIT / _RANGE; TROPICAL_BACKWARD_STAGED=0
+        // keeps the choice among them).
+        const char* sv = std::getenv("TROPICAL_BACKWARD_STAGED");
+        const bool staged = !env_flag_set("TROPICAL_BACKWARD_LANE") && !env_flag_set("TROPICAL_BACKWARD_SPLIT") &&
+                            !std::getenv("TROPICAL_BACKWARD_RANGE") && !(sv && *sv && sv[0] == '0');
+        if (staged) {
+            const KernelId tk =
+                (KernelId)((mul ? K_GEMM_BACKWARD_STAGED_MUL : K_GEMM_BACKWARD_STAGED_PLUS) + (vec ? 1 : 0));
+            const int64_t groups = (segs * batch + 63) / 64;  // 64 segments per workgroup
+            int occ = kernel_occupancy(dev, tk);
+            if (occ < 1) occ = 1;
+            const int64_t cap = (int64_t)device_cu_count(dev) * occ;
+            const int64_t grid = groups < cap ? groups : cap;
+            return launch(dev, tk, TROP_K_GEMM_BACKWARD, (uint32_t)(grid < 1 ? 1 : grid), 256, &p, stream);
+        }
         // Items contiguous in a segment (rows of grad_a) but too few
         // segments for one lane each to fill the device (fewer than 4 waves
         // per CU): 16 lanes per segment, each owning a range of bins.  (With

@@ -207,7 +207,12 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.tiles_m = (int32_t)tm;
     p.tiles_n = (int32_t)tn;
     p.swizzle = env_flag("TROPICAL_NO_XCD_SWIZZLE") ? 0 : 1;
-    p.group_rows = env_flag("TROPICAL_GEMM_ROW_RASTER") ? 1 : TROP_GEMM_GROUP_ROWS;
+    p.group_rows = TROP_GEMM_GROUP_ROWS;
+    if (const char* g = std::getenv("TROPICAL_GEMM_GROUP_ROWS")) {  // tuning knob: tile-rows per group
+        const long v = std::strtol(g, nullptr, 10);
+        if (v >= 1 && v <= 64) p.group_rows = (int32_t)v;
+    }
+    if (env_flag("TROPICAL_GEMM_ROW_RASTER")) p.group_rows = 1;
     // split K into ranges when the workspace allows and the shape asks for it:
     // partials go to [split][batch][m][n] in the workspace
     const SplitK sk = workspace ? plan_splitk(m, n, k, batch) : SplitK();
@@ -231,7 +236,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         if (tm * tn >= 2) magic_u31((uint64_t)(tm * tn), &p.tl_m, &p.tl_s);
         if (tn >= 2) magic_u31((uint64_t)tn, &p.tn_m, &p.tn_s);
         if (p.ksplit >= 2) magic_u31((uint64_t)p.ksplit, &p.ks_m, &p.ks_s);
-        magic_u31((uint64_t)(TROP_GEMM_GROUP_ROWS * tn), &p.gr_m, &p.gr_s);
+        magic_u31((uint64_t)(p.group_rows * tn), &p.gr_m, &p.gr_s);
     }
     // without an argmax output the value-only kernel skips the chunk record
     // and the re-scan

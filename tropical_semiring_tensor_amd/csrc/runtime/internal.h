@@ -92,6 +92,10 @@ enum KernelId : int {
     K_GEMM_DOMAIN_MINPLUS,
     K_GEMM_FMKM_MAXPLUS,  // float mode, wide, A k-vector, B column-vector
     K_GEMM_FMKM_MINPLUS,
+    K_GEMM_BACKWARD_STAGED_PLUS,  // backward, items staged through LDS per 64 segments (bins <= 256)
+    K_GEMM_BACKWARD_STAGED_PLUS_VEC,
+    K_GEMM_BACKWARD_STAGED_MUL,
+    K_GEMM_BACKWARD_STAGED_MUL_VEC,
     K_COUNT
 };
 const char* kernel_name(KernelId id);

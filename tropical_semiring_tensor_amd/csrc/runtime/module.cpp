@@ -68,7 +68,9 @@ const std::vector<std::string>& kernel_names() {
             "trop_gemm_fmg_maxplus_i32",     "trop_gemm_fmg_minplus_i32",
             "trop_gemm_fmvo_maxplus_i32",    "trop_gemm_fmvo_minplus_i32",
             "trop_gemm_domain_maxplus_i32",  "trop_gemm_domain_minplus_i32",
-            "trop_gemm_fmkm_maxplus_i32",    "trop_gemm_fmkm_minplus_i32"};
+            "trop_gemm_fmkm_maxplus_i32",    "trop_gemm_fmkm_minplus_i32",
+            "trop_gemm_backward_staged_plus", "trop_gemm_backward_staged_plus_vec",
+            "trop_gemm_backward_staged_mul",  "trop_gemm_backward_staged_mul_vec"};
         static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
         static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
         std::vector<std::string> v;
