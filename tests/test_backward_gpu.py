@@ -164,13 +164,14 @@ def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
 def test_backward_staged_pieces(tb, orc, items):
     """The staged form's pieces of 32 items: fewer than one piece, exactly
     one, two and three, and a ragged last piece; bin counts that leave
-    waves with no range (k = 2), ranges of one bin (k = 4), a ragged last
-    range (k = 129) and full ranges (k = 256); segments across batch
-    entries and not a multiple of 64; contiguous (grad_a) and strided
-    (grad_b) items, both weights."""
+    waves with no range (k = 2), ranges of one bin (k = 4), ranges of four
+    (k = 16: the 16-byte output stores), a ragged last range (k = 129) and
+    full ranges (k = 256); segments across batch entries and not a
+    multiple of 64 or of 4; contiguous (grad_a) and strided (grad_b)
+    items, both weights."""
     g = torch.Generator().manual_seed(items)
     b, m, n = 3, items, items   # grad_a walks n items per row, grad_b m per column
-    for k in (2, 4, 129, 256):
+    for k in (2, 4, 16, 129, 256):
         I = torch.randint(0, k, (b, m, n), generator=g, dtype=torch.int32)
         G = torch.randn(b, m, n, generator=g)
         A = torch.rand(b, m, k, generator=g) + 0.5

@@ -532,7 +532,34 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
         // write the 64 segments' bins of this wave's range
         if (kn > 0) {
             constexpr int WB = 8;  // LDS reads in flight per batch of stores
-            if (p.o_bin == 1) {
+            const bool vec_out = p.o_bin == 1 && kn % 4 == 0 && lo % 4 == 0 && p.o_seg % 4 == 0 &&
+                                 p.o_batch % 4 == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
+            if (vec_out) {
+                // 16 lanes per segment, four bins each: one 16-byte store per
+                // lane, four segments per instruction
+                const int rr = lane >> 4, q = lane & 15;
+                int64_t sg = seg0 + rr;
+                int64_t ob = sg / p.segs, os = sg - ob * p.segs;  // segment seg0 + r0 + rr, stepped by 4
+                for (int r0 = 0; r0 < 64; r0 += 16) {
+                    float4 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float* src = bins + (wave * 64 + r0 + 4 * u + rr) * GBT_LDR + 4 * q;
+                        v[u] = make_float4(src[0], src[1], src[2], src[3]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (sg < nseg && 4 * q < kn)
+                            *reinterpret_cast<float4*>(p.out + ob * p.o_batch + os * p.o_seg + lo + 4 * q) = v[u];
+                        sg += 4;
+                        os += 4;
+                        while (os >= p.segs) {
+                            os -= p.segs;
+                            ++ob;
+                        }
+                    }
+                }
+            } else if (p.o_bin == 1) {
                 // lane = bin: each segment's bins are one contiguous store
                 int64_t ob = seg0 / p.segs, os = seg0 - ob * p.segs;  // segment seg0 + r, stepped
                 for (int r0 = 0; r0 < 64; r0 += WB) {
@@ -546,6 +573,29 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
                             os = 0;
                             ++ob;
                         }
+                    }
+                }
+            } else if (p.o_seg == 1 && kn % 4 == 0 && p.segs % 4 == 0 && p.o_bin % 4 == 0 && p.o_batch % 4 == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0) {
+                // segments side by side in the output: lane (sq, kb) writes
+                // bin k0 + kb of segments 4 sq .. 4 sq + 3 (one batch entry,
+                // since segs % 4 == 0) with one 16-byte store
+                const int sq = lane & 15, kb = lane >> 4;
+                const int64_t sg = seg0 + 4 * sq;
+                const int64_t qb = sg / p.segs, qs = sg - qb * p.segs;
+                float* out = p.out + qb * p.o_batch + qs + (int64_t)lo * p.o_bin;
+                const float* src = bins + (wave * 64 + 4 * sq) * GBT_LDR;
+                for (int32_t k0 = 0; k0 < kn; k0 += 16) {
+                    float4 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int k = min(k0 + 4 * u + kb, GBT_RW);
+                        v[u] = make_float4(src[k], src[GBT_LDR + k], src[2 * GBT_LDR + k], src[3 * GBT_LDR + k]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int k = k0 + 4 * u + kb;
+                        if (sg < nseg && k < kn) *reinterpret_cast<float4*>(out + (int64_t)k * p.o_bin) = v[u];
                     }
                 }
             } else if (live) {
