@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-traffic", action="store_true",
-                    help="run a 256 MiB copy and 3 headline GEMMs, print nothing else")
+                    help="run a 256 MiB copy, 3 headline GEMMs and 3 workload-2 GEMMs, print nothing else")
     ap.add_argument("--profile-configs", action="store_true",
                     help="the program profiled for per-workload counters: a 256 MiB device copy "
                          "(counter calibration), then three launches of each workload's kernels")
@@ -233,6 +233,12 @@ def main():
         for _ in range(3):
             step()
         torch.cuda.synchronize()
+        # then workload 2's kernel (another entry point, so its dispatches
+        # are told apart by name)
+        c2 = gemm_case(torch, tb, inputs, 2, dev)
+        for _ in range(3):
+            c2["step"]()
+        torch.cuda.synchronize()
         log("[bench] traffic probe done")
         return
 
@@ -300,8 +306,9 @@ def profile_configs(torch, tb, inputs, dev):
     """One 256 MiB device copy (calibrates the traffic counters), then three
     launches of each workload's kernels in workload order: GEMMs 1-4 with
     argmax (workload 3 through the workspace call: domain pre-pass and float
-    mode), and workload 5's einsum (diagonal gather, B permute, GEMM) plus
-    its paired output permute run on its own."""
+    mode), workload 5's einsum (diagonal gather, B permute, GEMM) plus its
+    paired output permute run on its own, and workload 2's backward (both
+    gradients)."""
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -328,6 +335,17 @@ def profile_configs(torch, tb, inputs, dev):
     I2 = torch.empty(32, 128, 256, dtype=torch.int32, device=dev)
     for _ in range(3):
         tb.tropical_permute(C2, (0, 2, 1), out=C, x2=I2, out2=I)
+    torch.cuda.synchronize()
+    del Ad, Bd, C, I, C2, I2, ws
+    # workload 2's backward: grad_a and grad_b from the forward's argmax
+    c = gemm_case(torch, tb, inputs, 2, dev)
+    c["step"]()
+    w2 = c["w"]
+    G = torch.randn(w2["batch"], w2["m"], w2["n"], generator=torch.Generator().manual_seed(22)).to(dev)
+    gA = torch.empty(w2["batch"], w2["m"], w2["k"], device=dev)
+    gB = torch.empty(w2["batch"], w2["k"], w2["n"], device=dev)
+    for _ in range(3):
+        tb.tropical_gemm_backward("max_plus", c["I"], G, k=w2["k"], grad_a=gA, grad_b=gB)
     torch.cuda.synchronize()
 
 
