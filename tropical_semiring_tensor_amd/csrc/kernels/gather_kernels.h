@@ -166,23 +166,34 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
     }
 }
 
-// Transpose through LDS with 16-byte global accesses on both sides.  A tile
-// covers TP elements along ax_in (P, input stride 1) and TQ = 4096 / TP
-// along the last output axis (Q, output stride 1).  Each thread loads four
-// 16-byte vectors along P and stores four along Q.  Needs EP, EQ, the input
-// stride of Q and of every other axis to be multiples of 4 and both pointers
-// 16-byte aligned (checked on the host).
-// Workgroup b0 of a set of bstep workgroups walks tiles b0, b0 + bstep, ...
+// Transpose through LDS with 16-byte accesses everywhere.  A tile covers TP
+// elements along ax_in (P, input stride 1) and TQ = 4096 / TP along the last
+// output axis (Q, output stride 1).  LDS holds the tile row by row along P
+// (row q: TP words), and quad c of row q sits at quad c ^ s(q),
+// s(q) = (q / 4) mod (TP / 4).
+//   read:  each thread loads four 16-byte vectors along P (four q, RPP
+//          apart) and writes each as one 16-byte LDS store: the lanes of a
+//          row fill it (a permutation of its quads), so no two lanes of a
+//          16-lane group share a bank;
+//   write: each thread takes one 4 x 4 block (q-quad bq, p-quad bp): four
+//          16-byte LDS reads of rows 4 bq .. 4 bq + 3, a transpose in
+//          registers, and four 16-byte stores along Q, one per p.  Lanes run
+//          along bq, so their reads fall on the quads bp ^ bq of rows TP words
+//          apart: distinct quads for up to TP / 4 neighbouring lanes.
+// Every LDS access is 16 bytes wide (four times fewer LDS instructions than
+// word accesses).  Needs EP, EQ, the input stride of Q and of every other
+// axis to be multiples of 4 and both pointers 16-byte aligned (checked on the
+// host).  Workgroup b0 of a set of bstep workgroups walks tiles b0,
+// b0 + bstep, ...
 template <int TP, int NT>
 __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p, int64_t b0, int64_t bstep) {
     constexpr int TQ = 4096 / TP;
-    constexpr int LDT = TP + 1;          // LDS row (fixed q) length in words
-    constexpr int LPR = TP / 4;          // read phase: lanes per q-row
+    constexpr int NQP = TP / 4;                 // quads per LDS row
+    constexpr int LPR = TP / 4;                 // read phase: lanes per q-row
     constexpr int RPP = GATHER_THREADS / LPR;   // q-rows per pass
-    constexpr int LPQ = TQ / 4;          // write phase: lanes per p-row
-    constexpr int PPP = GATHER_THREADS / LPQ;   // p-rows per pass
-    static_assert(RPP * 4 == TQ && PPP * 4 == TP, "four passes per phase");
-    __shared__ uint32_t tile[NT][TQ * LDT];
+    constexpr int BQ = TQ / 4;                  // write phase: q-quads per tile
+    static_assert(RPP * 4 == TQ && BQ * NQP == GATHER_THREADS, "four read passes, one block per thread");
+    __shared__ __attribute__((aligned(16))) uint32_t tile[NT][TQ * TP];
     const int nd = p.ndim;
     const int P = p.ax_in, Q = nd - 1;
     const int64_t EP = p.shape[P], EQ = p.shape[Q];
@@ -192,8 +203,9 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p,
     const int tid = threadIdx.x;
     const int64_t per_batch = p.tiles_p * p.tiles_q;
     const int64_t nblk = per_batch * p.nbatch;
-    const int rp = (tid % LPR) * 4, rq = tid / LPR;   // read-phase lane position
-    const int wq = (tid % LPQ) * 4, wp = tid / LPQ;   // write-phase lane position
+    const int rc = tid % LPR, rq = tid / LPR;   // read phase: p-quad, q-row within a pass
+    const int bq = tid % BQ, bp = tid / BQ;     // write phase: the thread's 4 x 4 block
+    auto swz = [](int q) { return (q >> 2) & (NQP - 1); };
 
     for (int64_t blk = b0; blk < nblk; blk += bstep) {
         const int64_t tq = blk % p.tiles_q;
@@ -211,34 +223,35 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p,
             ostride *= e;
         }
         const int64_t p0 = tp * TP, q0 = tq * TQ;
-        const int64_t pp = p0 + rp;
+        const int64_t pp = p0 + 4 * rc;
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
             const int ql = pass * RPP + rq;
             const int64_t q = q0 + ql;
             if (pp < EP && q < EQ) {
                 const int64_t src = ibase + pp + q * sQ;
-                #pragma unroll
+#pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const u32x4 x = ld16(static_cast<const uint32_t*>(p.in[t]) + src);
-                    uint32_t* row = &tile[t][ql * LDT + rp];
-                    row[0] = x.x; row[1] = x.y; row[2] = x.z; row[3] = x.w;
+                    *reinterpret_cast<u32x4*>(&tile[t][ql * TP + 4 * (rc ^ swz(ql))]) = x;
                 }
             }
         }
         __syncthreads();
-        const int64_t q = q0 + wq;
+        const int64_t qv = q0 + 4 * bq;
+        const int64_t pv0 = p0 + 4 * bp;
+        if (qv < EQ && pv0 < EP) {
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int pl = pass * PPP + wp;
-            const int64_t pv = p0 + pl;
-            if (pv < EP && q < EQ) {
-                const int64_t dst = obase + pv * oP + q;
-                #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const uint32_t* col = &tile[t][wq * LDT + pl];
-                    st16(static_cast<uint32_t*>(p.out[t]) + dst, u32x4{col[0], col[LDT], col[2 * LDT], col[3 * LDT]});
-                }
+            for (int t = 0; t < NT; ++t) {
+                u32x4 r[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    r[j] = *reinterpret_cast<const u32x4*>(&tile[t][(4 * bq + j) * TP + 4 * (bp ^ swz(4 * bq))]);
+                uint32_t* out = static_cast<uint32_t*>(p.out[t]) + obase + pv0 * oP + qv;
+                st16(out, u32x4{r[0].x, r[1].x, r[2].x, r[3].x});
+                st16(out + oP, u32x4{r[0].y, r[1].y, r[2].y, r[3].y});
+                st16(out + 2 * oP, u32x4{r[0].z, r[1].z, r[2].z, r[3].z});
+                st16(out + 3 * oP, u32x4{r[0].w, r[1].w, r[2].w, r[3].w});
             }
         }
         __syncthreads();
