@@ -72,6 +72,10 @@ struct TropDomainParams {
 
 // Merge of split-K partials: out = the first strictly better of the
 // ksplit partials (split 0 first), stored [split][batch][m][n] contiguous.
+// Lanes of the split-K merge per output (a power of two up to 64; the grid
+// has one thread per lane).
+#define TROP_MERGE_LANES 16
+
 struct TropSplitMergeParams {
     const void* pval;
     const int32_t* pidx;  // may be null (value only)

@@ -46,8 +46,10 @@ __device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
 // consecutive ranges in order (the first taken as is, then only strictly
 // better ones), and the lanes then combine pairwise, the better value
 // winning and, on equal values, the earlier range.  That is the same first
-// strict winner over all ranges, found with MERGE_G loads in flight.
-constexpr int MERGE_G = 8;
+// strict winner over all ranges, found with MERGE_G x MERGE_U loads in flight
+// per output.
+constexpr int MERGE_G = TROP_MERGE_LANES;
+constexpr int MERGE_U = 8;  // ranges per lane whose loads are in flight together
 
 template <int SR, typename T>
 __device__ __forceinline__ void splitk_merge_body(const TropSplitMergeParams& p) {
@@ -67,12 +69,25 @@ __device__ __forceinline__ void splitk_merge_body(const TropSplitMergeParams& p)
         T best = R::zero();
         int32_t arg = 0;
         int32_t rb = nr;  // range of `best`; nr = none (an empty run)
-        for (int32_t r = r0; r < r1; ++r) {
-            const T v = pv[(int64_t)r * total + o];
-            if (r == r0 || R::better(v, best)) {
-                best = v;
-                arg = p.pidx ? p.pidx[(int64_t)r * total + o] : 0;
-                rb = r;
+        // MERGE_U ranges at a time: their loads issued together (a range past
+        // r1 re-reads range r0, in bounds, and is not considered), then
+        // scanned in order
+        for (int32_t ra = r0; ra < r1; ra += MERGE_U) {
+            T v[MERGE_U];
+            int32_t a[MERGE_U];
+#pragma unroll
+            for (int u = 0; u < MERGE_U; ++u) {
+                const int64_t off = (int64_t)(ra + u < r1 ? ra + u : r0) * total + o;
+                v[u] = pv[off];
+                a[u] = p.pidx ? p.pidx[off] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < MERGE_U; ++u) {
+                const int32_t r = ra + u;
+                const bool take = r < r1 && (r == r0 || R::better(v[u], best));
+                best = take ? v[u] : best;
+                arg = take ? a[u] : arg;
+                rb = take ? r : rb;
             }
         }
 #pragma unroll

@@ -348,7 +348,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     mp.batch = batch;
     mp.ksplit = sk.ksplit;
     return launch(dev, (KernelId)(K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + ri), TROP_K_GEMM_SPLITK_MERGE,
-                  grid_for(m * n * batch * 8, 256), 256, &mp, stream);  // 8 lanes per output
+                  grid_for(m * n * batch * TROP_MERGE_LANES, 256), 256, &mp, stream);
 }
 
 }  // namespace trop
