@@ -179,7 +179,9 @@ __device__ __forceinline__ void gather_copy_body(const TropGatherParams& p) {
 //          16-byte LDS reads of rows 4 bq .. 4 bq + 3, a transpose in
 //          registers, and four 16-byte stores along Q, one per p.  Lanes run
 //          along bq, so their reads fall on the quads bp ^ bq of rows TP words
-//          apart: distinct quads for up to TP / 4 neighbouring lanes.
+//          apart: distinct quads for up to TP / 4 neighbouring lanes (and,
+//          with the row exchange below for narrow tiles, distinct banks for
+//          16).
 // Every LDS access is 16 bytes wide (four times fewer LDS instructions than
 // word accesses).  Needs EP, EQ, the input stride of Q and of every other
 // axis to be multiples of 4 and both pointers 16-byte aligned (checked on the
@@ -206,6 +208,12 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p,
     const int rc = tid % LPR, rq = tid / LPR;   // read phase: p-quad, q-row within a pass
     const int bq = tid % BQ, bp = tid / BQ;     // write phase: the thread's 4 x 4 block
     auto swz = [](int q) { return (q >> 2) & (NQP - 1); };
+    // Rows narrower than the 64 banks (TP = 16, 32) also trade places inside
+    // groups of RG = 64 / TP rows, so that the lanes of a 16-lane group whose
+    // quads coincide read rows in different bank ranges.
+    constexpr int RG = TP >= 64 ? 1 : 64 / TP;
+    constexpr int RSH = TP == 16 ? 4 : 5;  // log2(TP / 4) + 2
+    auto prow = [](int q) { return RG == 1 ? q : q ^ ((q >> RSH) & (RG - 1)); };
 
     for (int64_t blk = b0; blk < nblk; blk += bstep) {
         const int64_t tq = blk % p.tiles_q;
@@ -233,7 +241,7 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p,
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const u32x4 x = ld16(static_cast<const uint32_t*>(p.in[t]) + src);
-                    *reinterpret_cast<u32x4*>(&tile[t][ql * TP + 4 * (rc ^ swz(ql))]) = x;
+                    *reinterpret_cast<u32x4*>(&tile[t][prow(ql) * TP + 4 * (rc ^ swz(ql))]) = x;
                 }
             }
         }
@@ -246,7 +254,7 @@ __device__ __forceinline__ void gather_tiled_vec_body(const TropGatherParams& p,
                 u32x4 r[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    r[j] = *reinterpret_cast<const u32x4*>(&tile[t][(4 * bq + j) * TP + 4 * (bp ^ swz(4 * bq))]);
+                    r[j] = *reinterpret_cast<const u32x4*>(&tile[t][prow(4 * bq + j) * TP + 4 * (bp ^ swz(4 * bq))]);
                 uint32_t* out = static_cast<uint32_t*>(p.out[t]) + obase + pv0 * oP + qv;
                 st16(out, u32x4{r[0].x, r[1].x, r[2].x, r[3].x});
                 st16(out + oP, u32x4{r[0].y, r[1].y, r[2].y, r[3].y});
