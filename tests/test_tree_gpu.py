@@ -2,10 +2,11 @@
 
 Every step of a tree is a pairwise contraction, so the oracle's tree (its
 pairwise steps in the same order) and the device tree must agree bit for bit
-in the result and in every step's argmax.  At the benchmark's network size
-the oracle cannot run the whole tree in seconds; there the tree is checked
-against the device's own pairwise calls, each step's sampled outputs against
-the oracle's brute-force einsum, and the winner routing against the result.
+in the result and in every step's argmax, at the benchmark's network size
+too (the oracle's tree takes ~15-30 s there).  That network is further
+checked against the device's own pairwise calls, each step's sampled outputs
+against the oracle's brute-force einsum, and the winner routing against the
+result.
 """
 import numpy as np
 import pytest
@@ -227,7 +228,8 @@ def _brute_points(orc, sr, la, lb, out, A, B, points, argmax):
 
 def test_tree_benchmark_network_full_size(tb, orc):
     """The 5 x 5 lattice with bond 16 (64 MiB intermediates) as the benchmark
-    runs it: the tree equals the device's own pairwise calls bit for bit,
+    runs it: the result and every step's argmax equal the oracle's tree bit
+    for bit; the tree equals the device's own pairwise calls bit for bit,
     sampled outputs of every step equal the oracle's brute force, and
     following the argmax from the result down to the inputs recomputes the
     result exactly (the same additions in the same order)."""
@@ -236,6 +238,12 @@ def test_tree_benchmark_network_full_size(tb, orc):
     xs = [x.to(DEV) for x in net["tensors"]]
     plan = tb.tropical_tree_plan_create("max_plus", torch.float32, subs, net["shapes"], steps)
     out, ams = tb.tropical_tree_run(plan, xs, argmax=True)
+    torch.cuda.synchronize()
+    ref, rams = orc.contract_tree("max_plus", [x.numpy() for x in net["tensors"]], list(net["subs"]), steps,
+                                  argmax=True)
+    assert_bits_equal(out.cpu().numpy(), ref, "5x5 bond-16 network result")
+    for s, r in enumerate(rams):
+        assert_equal(ams[s].cpu().numpy(), r, f"5x5 bond-16 network argmax of step {s}")
     # the same steps through tropical_contract_pair, keeping intermediates
     slots = list(xs)
     for s, (l, r, o) in enumerate(steps):
