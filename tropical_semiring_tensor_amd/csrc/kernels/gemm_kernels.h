@@ -151,21 +151,29 @@ __device__ __forceinline__ uint32_t domain_scan(const int32_t* X, int64_t nb, in
         sr = sc;
         sc = 1;
     }
+    // one wave per row at a time (rows of different waves in flight
+    // together), the row's 16-byte vectors unrolled so that a lane's loads
+    // are issued together
     uint32_t bad = 0;
     const int64_t rows = nb * r;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / 64);
+    for (int64_t row = wid; row < rows; row += nw) {
         const int64_t b = row / r, i = row - b * r;
         const int32_t* base = X + b * sb + i * sr;
         if (sc == 1 && (reinterpret_cast<uintptr_t>(base) & 15u) == 0) {
             const int64_t nv = c / 4;
-            for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+#pragma unroll 16
+            for (int64_t v = lane; v < nv; v += 64) {
                 const vec4<int32_t> x = reinterpret_cast<const vec4<int32_t>*>(base)[v];
                 bad |= outside_domain<SR>(x.x) | outside_domain<SR>(x.y) | outside_domain<SR>(x.z) |
                        outside_domain<SR>(x.w);
             }
-            for (int64_t e = nv * 4 + threadIdx.x; e < c; e += blockDim.x) bad |= outside_domain<SR>(base[e]);
+            for (int64_t e = nv * 4 + lane; e < c; e += 64) bad |= outside_domain<SR>(base[e]);
         } else {
-            for (int64_t e = threadIdx.x; e < c; e += blockDim.x) bad |= outside_domain<SR>(base[e * sc]);
+#pragma unroll 8
+            for (int64_t e = lane; e < c; e += 64) bad |= outside_domain<SR>(base[e * sc]);
         }
     }
     return bad;
