@@ -470,7 +470,7 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     out["backward_maxplus_f32_b64_256"] = {
         "back_to_back_us": round(b2b * 1e3, 2), "cold_us": round(cold["median_ms"] * 1e3, 2),
         "bytes": nbytes, "back_to_back_GBs": round(nbytes / (b2b * 1e-3) / 1e9, 1),
-        "frac_hbm": round(nbytes / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "launches": 2}
+        "frac_hbm": round(nbytes / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "launches": 1}
     log(f"[bench] backward (workload 2): {out['backward_maxplus_f32_b64_256']}")
     del Ad, Bd, C, I, G, gA, gB
     torch.cuda.empty_cache()

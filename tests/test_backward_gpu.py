@@ -129,8 +129,8 @@ def test_backward_strided_views_and_one_sided(tb, orc):
     assert_bits_equal(gb.cpu().numpy(), rb, "column-major grad_b")
 
 
-@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
-                                  "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_NO_PAIR", "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE",
+                                  "TROPICAL_BACKWARD_SPLIT", "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
 def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
     """Bins summed from denormal gradients, +0 / -0 mixes (a bin of only
     -0.0 items is +0.0, since sums start at +0.0), exact cancellations to
@@ -160,15 +160,19 @@ def test_backward_denormal_zero_and_inf_gradients(tb, orc, monkeypatch, knob):
     run_both(tb, orc, "max_mul", A, B, I, cases["denormal"] * 1e18, k, f"{knob} max_mul denormal")
 
 
-@pytest.mark.parametrize("items", [3, 31, 32, 33, 64, 96, 100])
-def test_backward_staged_pieces(tb, orc, items):
-    """The staged form's pieces of 32 items: fewer than one piece, exactly
-    one, two and three, and a ragged last piece; bin counts that leave
+@pytest.mark.parametrize("pair", [True, False])
+@pytest.mark.parametrize("items", [3, 15, 16, 17, 32, 33, 64, 100])
+def test_backward_staged_pieces(tb, orc, monkeypatch, items, pair):
+    """The staged form's pieces of 16 items: fewer than one piece, exactly
+    one, two and four, and a ragged last piece; both gradients in one
+    launch and one launch each; bin counts that leave
     waves with no range (k = 2), ranges of one bin (k = 4), ranges of four
     (k = 16: the 16-byte output stores), a ragged last range (k = 129) and
     full ranges (k = 256); segments across batch entries and not a
     multiple of 64 or of 4; contiguous (grad_a) and strided (grad_b)
     items, both weights."""
+    if not pair:
+        monkeypatch.setenv("TROPICAL_BACKWARD_NO_PAIR", "1")
     g = torch.Generator().manual_seed(items)
     b, m, n = 3, items, items   # grad_a walks n items per row, grad_b m per column
     for k in (2, 4, 16, 129, 256):
@@ -211,11 +215,12 @@ def test_backward_maxmul_workload4_recipe(tb, orc):
     run_both(tb, orc, "max_mul", A, B, torch.from_numpy(I), G, 700, "workload 4 recipe backward")
 
 
-@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE", "TROPICAL_BACKWARD_SPLIT",
-                                  "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
+@pytest.mark.parametrize("knob", [None, "TROPICAL_BACKWARD_NO_PAIR", "TROPICAL_BACKWARD_LANE", "TROPICAL_BACKWARD_WAVE",
+                                  "TROPICAL_BACKWARD_SPLIT", "TROPICAL_BACKWARD_RANGE", "TROPICAL_BACKWARD_STAGED"])
 def test_backward_every_kernel_form(tb, orc, monkeypatch, knob):
-    """The same gradients from the staged form (the default), the
-    16-lanes-per-segment form, the lane-per-segment form, the
+    """The same gradients from the staged form (the default: both
+    gradients in one launch; with TROPICAL_BACKWARD_NO_PAIR one launch
+    each), the 16-lanes-per-segment form, the lane-per-segment form, the
     wave-per-segment form, the 64-bin range form and the choice among them
     without the staged form, over hub-heavy and uniform argmaxes, both
     weights."""

@@ -203,3 +203,10 @@ struct TropBackwardParams {
     int32_t mul;  // max-mul: multiply by the weight
     int32_t pad_;
 };
+
+// Two gradients in one launch (the staged backward): workgroups below
+// `split` take p[0], the rest p[1].
+struct TropBackwardPairParams {
+    TropBackwardParams p[2];
+    int64_t split;
+};

@@ -351,24 +351,26 @@ __device__ __forceinline__ void gemm_backward_split_body(const TropBackwardParam
 // segments at a time and GBT_WAVES waves, wave w holding bins
 // [w W, w W + W) (W = ceil(bins / GBT_WAVES)) of all 64 segments, lane l
 // those of segment l, in LDS.  The segments' items come in pieces of GBT_T:
-// the whole workgroup loads a piece into registers (each thread a few items
-// of one segment, all loads issued at once, the next piece but one already
-// in flight while a piece is walked), multiplies in the max-mul weights and
-// writes keys and values to an LDS stage laid out [item][segment].  Then
-// every wave walks the piece in item order, lane l reading item t of its
-// own segment (64 consecutive words: no bank conflicts) and adding it to
-// its bin with a plain LDS read, add and write, a few items per round trip
-// (see the walk).  A bin is one lane's sum in ascending item order, so the
-// result is the sequential one.  The walk reads LDS only: the memory
-// latency of the items is paid once per piece for the whole workgroup
-// instead of once per few items per lane, and no LDS atomic is used (the
-// LDS float add costs about four cycles per active lane).
+// the whole workgroup loads a piece into registers (each thread a few items;
+// 16-byte loads along the items or across four segments where the layout
+// allows; the piece after next already in flight while a piece is walked),
+// multiplies in the max-mul weights and writes keys (16-bit) and values to
+// an LDS stage laid out [item][segment].  Then every wave walks the piece in
+// item order, lane l reading item t of its own segment and adding it to its
+// bin with a plain LDS read, add and write, two items per round trip (see
+// the walk).  A bin is one lane's sum in ascending item order, so the result
+// is the sequential one.  The walk reads LDS only: the memory latency of the
+// items is paid once per piece for the whole workgroup instead of once per
+// few items per lane, and no LDS atomic is used (the LDS float add costs
+// about four cycles per active lane).  A workgroup takes 77 KB of LDS, so
+// two share a CU; the paired entry runs both gradients in one launch, one
+// workgroup of each per CU, and their phases overlap.
 constexpr int GBT_WAVES = 4;
 constexpr int GBT_THREADS = 64 * GBT_WAVES;
 constexpr int GBT_RW = 64;              // most bins per wave
 constexpr int GBT_LDR = GBT_RW + 1;     // padded row: lane l, bin k at bank (l + k) mod 64
-constexpr int GBT_T = 32;               // items per staged piece
-constexpr int GBT_G = 4;                // items per group of the walk (bins read together)
+constexpr int GBT_T = 16;               // items per staged piece
+constexpr int GBT_G = 2;                // items per group of the walk (bins read together)
 constexpr int GBT_IPT = GBT_T * 64 / GBT_THREADS;  // items loaded per thread and piece
 static_assert(GBT_IPT % 4 == 0 && GBT_T % (4 * GBT_WAVES) == 0, "whole quads per thread");
 
@@ -376,11 +378,28 @@ static_assert(GBT_IPT % 4 == 0 && GBT_T % (4 * GBT_WAVES) == 0, "whole quads per
 // segment start 16-byte aligned: a thread loads quads of items with one
 // 16-byte load per tensor; otherwise item t of the 64 segments is loaded
 // with one element load per lane (coalesced when segments are contiguous).
-template <bool MUL, bool VEC>
-__device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardParams& p) {
-    __shared__ float bins[GBT_WAVES * 64 * GBT_LDR];
-    __shared__ int32_t stage_k[2][GBT_T][64];
-    __shared__ float stage_v[2][GBT_T][64];
+// The workgroup's LDS: the bins of its four ranges and the two stage
+// buffers (keys as 16-bit words: bins <= 256, GBT_NOKEY for no item or a key
+// outside [0, bins)).  77 KB, so that two workgroups share a CU.
+constexpr uint16_t GBT_NOKEY = 0xFFFF;
+struct GbtLds {
+    alignas(16) float bins[GBT_WAVES * 64 * GBT_LDR];
+    uint16_t stage_k[2][GBT_T][64];
+    float stage_v[2][GBT_T][64];
+};
+
+// Item loads of the staged form: elements (one per lane and item), 16-byte
+// vectors along the items (items contiguous), or 16-byte vectors across four
+// neighbouring segments (segments contiguous, their count a multiple of 4).
+constexpr int GBT_LOAD_ELEM = 0, GBT_LOAD_ITEMS = 1, GBT_LOAD_SEGS = 2;
+
+// Walks groups g0, g0 + gstep, ... of 64 segments.
+template <bool MUL, int LM>
+__device__ __forceinline__ void gemm_backward_staged_run(const TropBackwardParams& p, int64_t g0, int64_t gstep,
+                                                         GbtLds& L) {
+    float* const bins = L.bins;
+    uint16_t(&stage_k)[2][GBT_T][64] = L.stage_k;
+    float(&stage_v)[2][GBT_T][64] = L.stage_v;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int32_t K = (int32_t)p.bins;  // <= GBT_WAVES * GBT_RW (checked on the host)
@@ -392,13 +411,21 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
     const int64_t items = p.items;
     const int64_t ngroups = (nseg + 63) / 64;
     const int64_t npieces = (items + GBT_T - 1) / GBT_T;
-    // item (within a piece) of this thread's j-th load: VEC, quads
-    // wave + GBT_WAVES h; else items wave + GBT_WAVES j
+    constexpr bool VEC = LM == GBT_LOAD_ITEMS, SVEC = LM == GBT_LOAD_SEGS;
+    // The j-th value this thread loads: its item within the piece and its
+    // segment within the group (the stage column).  Items along: quads
+    // wave + GBT_WAVES h of segment `lane`; elements: items wave + GBT_WAVES j
+    // of segment `lane`; across segments: item (tid / 16) + 16 (j / 4) of
+    // segments 4 (tid % 16) .. 4 (tid % 16) + 3.
+    constexpr int SQ = GBT_THREADS / 16;  // across segments: items per pass
     auto item_of = [&](int j) -> int {
-        return VEC ? 4 * (wave + GBT_WAVES * (j / 4)) + (j & 3) : wave + GBT_WAVES * j;
+        return VEC ? 4 * (wave + GBT_WAVES * (j / 4)) + (j & 3)
+                   : (SVEC ? tid / 16 + SQ * (j / 4) : wave + GBT_WAVES * j);
     };
+    auto col_of = [&](int j) -> int { return SVEC ? 4 * (tid & 15) + (j & 3) : lane; };
+    static_assert(!SVEC || (GBT_IPT / 4) * SQ == GBT_T, "across segments: whole passes per piece");
 
-    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    for (int64_t g = g0; g < ngroups; g += gstep) {
         const int64_t seg0 = g * 64;
         const int64_t seg = seg0 + lane;  // this thread's segment, for loads and the walk
         const bool live = seg < nseg;
@@ -406,7 +433,20 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
         const int32_t* ip = p.idx + b * p.c_batch + s * p.c_seg;
         const float* gp = p.grad + b * p.c_batch + s * p.c_seg;
         const float* wp = MUL ? p.w + b * p.w_batch : nullptr;
-        for (int32_t k = 0; k < kn; ++k) row[k] = 0.0f;
+        // across segments: this thread loads segments seg0 + 4 (tid % 16) ..
+        // + 3, which share a batch entry (segs % 4 == 0)
+        const int64_t lseg = SVEC ? seg0 + 4 * (tid & 15) : seg;
+        const bool llive = lseg < nseg;
+        const int64_t lb = SVEC ? (llive ? lseg / p.segs : 0) : b, ls = SVEC ? (llive ? lseg % p.segs : 0) : s;
+        const int32_t* lip = SVEC ? p.idx + lb * p.c_batch + ls : ip;
+        const float* lgp = SVEC ? p.grad + lb * p.c_batch + ls : gp;
+        const float* lwp = MUL ? p.w + lb * p.w_batch : nullptr;
+        {
+            // the wave's 64 rows are one contiguous block: cleared with
+            // 16-byte stores (padding and unread words included)
+            float4* const wrows = reinterpret_cast<float4*>(bins + wave * 64 * GBT_LDR);
+            for (int v = lane; v < 64 * GBT_LDR / 4; v += 64) wrows[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         lds_order();
 
         int32_t ka[GBT_IPT], kb[GBT_IPT];
@@ -421,9 +461,24 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
         // (a missing item's load is clamped to the segment's last item, an
         // arithmetic clamp rather than a select, so that the compiler keeps
         // the loads free of branches)
-        auto exists = [&](int64_t pc, int j) { return live && pc * GBT_T + item_of(j) < items; };
+        auto exists = [&](int64_t pc, int j) { return llive && pc * GBT_T + item_of(j) < items; };
         auto load = [&](int64_t pc, int32_t(&kr)[GBT_IPT], float(&vr)[GBT_IPT]) {
-            if (VEC) {
+            if (SVEC) {
+#pragma unroll
+                for (int h = 0; h < GBT_IPT / 4; ++h) {
+                    const int64_t off = min(pc * GBT_T + item_of(4 * h), items - 1) * p.c_item;
+                    const int4 k4 = *reinterpret_cast<const int4*>(lip + off);
+                    const float4 v4 = *reinterpret_cast<const float4*>(lgp + off);
+                    kr[4 * h + 0] = k4.x;
+                    kr[4 * h + 1] = k4.y;
+                    kr[4 * h + 2] = k4.z;
+                    kr[4 * h + 3] = k4.w;
+                    vr[4 * h + 0] = v4.x;
+                    vr[4 * h + 1] = v4.y;
+                    vr[4 * h + 2] = v4.z;
+                    vr[4 * h + 3] = v4.w;
+                }
+            } else if (VEC) {
 #pragma unroll
                 for (int h = 0; h < GBT_IPT / 4; ++h) {
                     const int64_t tc = min(pc * GBT_T + item_of(4 * h), items - 4);  // whole quads
@@ -455,14 +510,15 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
             for (int j = 0; j < GBT_IPT; ++j) {
                 const bool valid = exists(pc, j) && (uint32_t)kr[j] < (uint32_t)K;
                 const int64_t t = pc * GBT_T + item_of(j);
-                wa[j] = wp[((int64_t)kr[j] * p.w_key + t * p.w_item) & -(int64_t)valid];
+                wa[j] = lwp[((int64_t)kr[j] * p.w_key + t * p.w_item) & -(int64_t)valid];
             }
         };
         auto stage = [&](int buf, int64_t pc, const int32_t(&kr)[GBT_IPT], const float(&vr)[GBT_IPT]) {
 #pragma unroll
             for (int j = 0; j < GBT_IPT; ++j) {
-                stage_k[buf][item_of(j)][lane] = exists(pc, j) ? kr[j] : -1;
-                stage_v[buf][item_of(j)][lane] = MUL ? vr[j] * wa[j] : vr[j];
+                stage_k[buf][item_of(j)][col_of(j)] =
+                    exists(pc, j) && (uint32_t)kr[j] < (uint32_t)K ? (uint16_t)kr[j] : GBT_NOKEY;
+                stage_v[buf][item_of(j)][col_of(j)] = MUL ? vr[j] * wa[j] : vr[j];
             }
         };
 
@@ -487,7 +543,7 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
             if (kn > 0) {
                 // the piece's keys and values first (the reads in flight
                 // together), then the adds in item order
-                int32_t kk[GBT_T];
+                uint32_t kk[GBT_T];
                 float vv[GBT_T];
 #pragma unroll
                 for (int t = 0; t < GBT_T; ++t) {
@@ -507,7 +563,7 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
                     float rd[GBT_G], nw[GBT_G];
 #pragma unroll
                     for (int u = 0; u < GBT_G; ++u) {
-                        ix[u] = min((uint32_t)kk[t0 + u] - (uint32_t)lo, (uint32_t)GBT_RW);  // unsigned: no overflow
+                        ix[u] = min(kk[t0 + u] - (uint32_t)lo, (uint32_t)GBT_RW);  // unsigned: GBT_NOKEY and keys below lo land past GBT_RW
                         rd[u] = row[ix[u]];
                     }
 #pragma unroll
@@ -613,6 +669,25 @@ __device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardPara
         }
         lds_order();
     }
+}
+
+template <bool MUL, int LM>
+__device__ __forceinline__ void gemm_backward_staged_body(const TropBackwardParams& p) {
+    __shared__ GbtLds L;
+    gemm_backward_staged_run<MUL, LM>(p, blockIdx.x, gridDim.x, L);
+}
+
+// Both gradients in one launch: workgroups [0, split) take the first job's
+// groups, the rest the second's.  With two workgroups per CU, a CU then holds
+// one of each, and the phases of one (item loads, staging, the output
+// write) overlap the other's walk.
+template <bool MUL, int LA, int LB>
+__device__ __forceinline__ void gemm_backward_staged_pair_body(const TropBackwardPairParams& q) {
+    __shared__ GbtLds L;
+    if ((int64_t)blockIdx.x < q.split)
+        gemm_backward_staged_run<MUL, LA>(q.p[0], blockIdx.x, q.split, L);
+    else
+        gemm_backward_staged_run<MUL, LB>(q.p[1], blockIdx.x - q.split, gridDim.x - q.split, L);
 }
 
 }  // namespace trop

@@ -204,12 +204,34 @@ TROP_BACKWARD_SPLIT(plus_vec, false, true)
 TROP_BACKWARD_SPLIT(mul, true, false)
 TROP_BACKWARD_SPLIT(mul_vec, true, true)
 
-#define TROP_BACKWARD_STAGED(NAME, MUL, VEC)                                                     \
+#define TROP_BACKWARD_STAGED(NAME, MUL, LM)                                                      \
     extern "C" __global__ __launch_bounds__(GBT_THREADS) void trop_gemm_backward_staged_##NAME(   \
         TropBackwardParams p) {                                                                  \
-        gemm_backward_staged_body<MUL, VEC>(p);                                                  \
+        gemm_backward_staged_body<MUL, LM>(p);                                                   \
     }
-TROP_BACKWARD_STAGED(plus, false, false)
-TROP_BACKWARD_STAGED(plus_vec, false, true)
-TROP_BACKWARD_STAGED(mul, true, false)
-TROP_BACKWARD_STAGED(mul_vec, true, true)
+// item loads: e = elements, i = 16-byte along items, s = 16-byte across segments
+TROP_BACKWARD_STAGED(plus_e, false, GBT_LOAD_ELEM)
+TROP_BACKWARD_STAGED(plus_i, false, GBT_LOAD_ITEMS)
+TROP_BACKWARD_STAGED(plus_s, false, GBT_LOAD_SEGS)
+TROP_BACKWARD_STAGED(mul_e, true, GBT_LOAD_ELEM)
+TROP_BACKWARD_STAGED(mul_i, true, GBT_LOAD_ITEMS)
+TROP_BACKWARD_STAGED(mul_s, true, GBT_LOAD_SEGS)
+
+// both gradients in one launch; suffix: each job's item loads
+#define TROP_BACKWARD_STAGED2(NAME, MUL, LA, LB)                                                 \
+    extern "C" __global__ __launch_bounds__(GBT_THREADS) void trop_gemm_backward_staged2_##NAME(  \
+        TropBackwardPairParams q) {                                                              \
+        gemm_backward_staged_pair_body<MUL, LA, LB>(q);                                          \
+    }
+#define TROP_BACKWARD_STAGED2_ALL(NAME, MUL)                                           \
+    TROP_BACKWARD_STAGED2(NAME##_ee, MUL, GBT_LOAD_ELEM, GBT_LOAD_ELEM)                \
+    TROP_BACKWARD_STAGED2(NAME##_ei, MUL, GBT_LOAD_ELEM, GBT_LOAD_ITEMS)               \
+    TROP_BACKWARD_STAGED2(NAME##_es, MUL, GBT_LOAD_ELEM, GBT_LOAD_SEGS)                \
+    TROP_BACKWARD_STAGED2(NAME##_ie, MUL, GBT_LOAD_ITEMS, GBT_LOAD_ELEM)               \
+    TROP_BACKWARD_STAGED2(NAME##_ii, MUL, GBT_LOAD_ITEMS, GBT_LOAD_ITEMS)              \
+    TROP_BACKWARD_STAGED2(NAME##_is, MUL, GBT_LOAD_ITEMS, GBT_LOAD_SEGS)               \
+    TROP_BACKWARD_STAGED2(NAME##_se, MUL, GBT_LOAD_SEGS, GBT_LOAD_ELEM)                \
+    TROP_BACKWARD_STAGED2(NAME##_si, MUL, GBT_LOAD_SEGS, GBT_LOAD_ITEMS)               \
+    TROP_BACKWARD_STAGED2(NAME##_ss, MUL, GBT_LOAD_SEGS, GBT_LOAD_SEGS)
+TROP_BACKWARD_STAGED2_ALL(plus, false)
+TROP_BACKWARD_STAGED2_ALL(mul, true)

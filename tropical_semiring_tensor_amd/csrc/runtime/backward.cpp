@@ -33,15 +33,22 @@ trop_status check_span3(const void* p, int dev, int64_t batch, int64_t rows, int
     return check_device_span(p, dev, span + 1, 4, what);
 }
 
-// Enqueue one gradient.  seg_*: strides that step between segments, item_*
-// within a segment; the weight of item t with key k is at
+// One gradient's launch parameters.  seg_*: strides that step between
+// segments, item_* within a segment; the weight of item t with key k is at
 // w + b * w.batch + k * w_key + t * w_item.
-trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, trop_strides sC,
-                        int64_t c_seg, int64_t c_item, const float* w, int64_t w_batch,
-                        int64_t w_key, int64_t w_item, bool mul, float* out, int64_t o_batch,
-                        int64_t o_seg, int64_t o_bin, int64_t segs, int64_t items, int64_t bins,
-                        int64_t batch, hipStream_t stream) {
-    TropBackwardParams p{};
+struct GradJob {
+    TropBackwardParams p;
+    bool vec;     // 16-byte loads along the items
+    int mode;     // the staged form's item loads: 0 elements, 1 along items, 2 across segments
+    bool staged;  // the staged form (up to 256 bins, no knob forcing another form)
+};
+
+GradJob make_job(const int32_t* argmax, const float* grad_c, trop_strides sC, int64_t c_seg, int64_t c_item,
+                 const float* w, int64_t w_batch, int64_t w_key, int64_t w_item, bool mul, float* out,
+                 int64_t o_batch, int64_t o_seg, int64_t o_bin, int64_t segs, int64_t items, int64_t bins,
+                 int64_t batch) {
+    GradJob j{};
+    TropBackwardParams& p = j.p;
     p.idx = argmax;
     p.grad = grad_c;
     p.w = mul ? w : nullptr;
@@ -60,27 +67,61 @@ trop_status launch_grad(int dev, const int32_t* argmax, const float* grad_c, tro
     p.items = items;
     p.bins = bins;
     p.mul = mul ? 1 : 0;
+    // 16-byte item loads when items are contiguous, a multiple of 4, and
+    // every segment start is 16-byte aligned
+    const bool aligned =
+        (reinterpret_cast<uintptr_t>(argmax) & 15u) == 0 && (reinterpret_cast<uintptr_t>(grad_c) & 15u) == 0;
+    j.vec = c_item == 1 && items % 4 == 0 && sC.batch % 4 == 0 && c_seg % 4 == 0 && aligned;
+    // 16-byte loads across four segments when the segments are contiguous,
+    // their count a multiple of 4 and every item row 16-byte aligned
+    const bool svec = c_seg == 1 && segs % 4 == 0 && sC.batch % 4 == 0 && c_item % 4 == 0 && aligned;
+    j.mode = j.vec ? 1 : (svec ? 2 : 0);
+    // The staged form: 64 segments and four bin ranges per workgroup, items
+    // loaded a piece at a time by the whole workgroup and walked from LDS.
+    // The other forms stay for the knobs that force them
+    // (TROPICAL_BACKWARD_LANE / _SPLIT / _RANGE / _WAVE;
+    // TROPICAL_BACKWARD_STAGED=0 keeps the choice among them).
+    const char* sv = std::getenv("TROPICAL_BACKWARD_STAGED");
+    j.staged = bins <= 256 && !env_flag_set("TROPICAL_BACKWARD_WAVE") && !env_flag_set("TROPICAL_BACKWARD_LANE") &&
+               !env_flag_set("TROPICAL_BACKWARD_SPLIT") && !std::getenv("TROPICAL_BACKWARD_RANGE") &&
+               !(sv && *sv && sv[0] == '0');
+    return j;
+}
+
+// Both gradients in one launch of the staged form: two workgroups per CU,
+// one of each gradient, whose phases overlap.  Each gradient gets at most
+// half of the resident workgroups.
+trop_status launch_staged_pair(int dev, const GradJob& a, const GradJob& b, hipStream_t stream) {
+    const bool mul = a.p.mul != 0;
+    const KernelId kid =
+        (KernelId)((mul ? K_GEMM_BACKWARD_STAGED2_MUL : K_GEMM_BACKWARD_STAGED2_PLUS) + 3 * a.mode + b.mode);
+    int occ = kernel_occupancy(dev, kid);
+    if (occ < 1) occ = 1;
+    const int64_t cap = (int64_t)device_cu_count(dev) * occ;
+    const int64_t half = cap / 2 > 0 ? cap / 2 : 1;
+    const int64_t ga = (a.p.segs * a.p.batch + 63) / 64, gb = (b.p.segs * b.p.batch + 63) / 64;
+    const int64_t na = ga < half ? ga : half;
+    const int64_t nb = gb < cap - na ? gb : cap - na;
+    TropBackwardPairParams q{};
+    q.p[0] = a.p;
+    q.p[1] = b.p;
+    q.split = na < 1 ? 1 : na;
+    const int64_t grid = q.split + (nb < 1 ? 1 : nb);
+    return launch(dev, kid, TROP_K_GEMM_BACKWARD, (uint32_t)grid, 256, &q, stream);
+}
+
+// Enqueue one gradient.
+trop_status launch_grad(int dev, const GradJob& job, hipStream_t stream) {
+    TropBackwardParams p = job.p;
+    const bool mul = p.mul != 0, vec = job.vec;
+    const int64_t c_item = p.c_item, segs = p.segs, batch = p.batch, bins = p.bins;
     // Up to 256 bins: one lane per segment and bin range, each walking its
     // items in order (cheap whatever the key distribution).  More bins: one
     // wave per segment with the bins in LDS, the smallest chunk that holds
     // them all (else 4096 and several passes).
     if (bins <= 256 && !env_flag_set("TROPICAL_BACKWARD_WAVE")) {
-        // 16-byte item loads when items are contiguous, a multiple of 4, and
-        // every segment start is 16-byte aligned
-        const bool vec = c_item == 1 && items % 4 == 0 && sC.batch % 4 == 0 && c_seg % 4 == 0 &&
-                         (reinterpret_cast<uintptr_t>(argmax) & 15u) == 0 &&
-                         (reinterpret_cast<uintptr_t>(grad_c) & 15u) == 0;
-        // The staged form: 64 segments and four bin ranges per workgroup,
-        // items loaded a piece at a time by the whole workgroup and walked
-        // from LDS.  The forms below stay for the knobs that force them
-        // (TROPICAL_BACKWARD_LANE / _SPLIT / _RANGE; TROPICAL_BACKWARD_STAGED=0
-        // keeps the choice among them).
-        const char* sv = std::getenv("TROPICAL_BACKWARD_STAGED");
-        const bool staged = !env_flag_set("TROPICAL_BACKWARD_LANE") && !env_flag_set("TROPICAL_BACKWARD_SPLIT") &&
-                            !std::getenv("TROPICAL_BACKWARD_RANGE") && !(sv && *sv && sv[0] == '0');
-        if (staged) {
-            const KernelId tk =
-                (KernelId)((mul ? K_GEMM_BACKWARD_STAGED_MUL : K_GEMM_BACKWARD_STAGED_PLUS) + (vec ? 1 : 0));
+        if (job.staged) {
+            const KernelId tk = (KernelId)((mul ? K_GEMM_BACKWARD_STAGED_MUL : K_GEMM_BACKWARD_STAGED_PLUS) + job.mode);
             const int64_t groups = (segs * batch + 63) / 64;  // 64 segments per workgroup
             int occ = kernel_occupancy(dev, tk);
             if (occ < 1) occ = 1;
@@ -186,18 +227,26 @@ extern "C" trop_status tropical_gemm_backward(trop_semiring semiring, trop_dtype
         st = check_span3(grad_a, dev, batch, m, k, sGA, "grad_a");
         if (st == TROP_OK && mul && n > 0) st = check_span3(B, dev, batch, k, n, sB, "B");
         if (st != TROP_OK) return st;
-        // rows of grad_a: segments i, items j, bins k; weight B[b][k][j]
-        st = launch_grad(dev, argmax, grad_c, sC, sC.row, sC.col, static_cast<const float*>(B), sB.batch,
-                         sB.row, sB.col, mul, grad_a, sGA.batch, sGA.row, sGA.col, m, n, k, batch, s);
-        if (st != TROP_OK) return st;
     }
     if (want_b) {
         st = check_span3(grad_b, dev, batch, k, n, sGB, "grad_b");
         if (st == TROP_OK && mul && m > 0) st = check_span3(A, dev, batch, m, k, sA, "A");
         if (st != TROP_OK) return st;
-        // columns of grad_b: segments j, items i, bins k; weight A[b][i][k]
-        st = launch_grad(dev, argmax, grad_c, sC, sC.col, sC.row, static_cast<const float*>(A), sA.batch,
-                         sA.col, sA.row, mul, grad_b, sGB.batch, sGB.col, sGB.row, n, m, k, batch, s);
+    }
+    // rows of grad_a: segments i, items j, bins k; weight B[b][k][j]
+    const GradJob ja = make_job(argmax, grad_c, sC, sC.row, sC.col, static_cast<const float*>(B), sB.batch, sB.row,
+                                sB.col, mul, grad_a, sGA.batch, sGA.row, sGA.col, m, n, k, batch);
+    // columns of grad_b: segments j, items i, bins k; weight A[b][i][k]
+    const GradJob jb = make_job(argmax, grad_c, sC, sC.col, sC.row, static_cast<const float*>(A), sA.batch, sA.col,
+                                sA.row, mul, grad_b, sGB.batch, sGB.col, sGB.row, n, m, k, batch);
+    if (want_a && want_b && ja.staged && jb.staged && !env_flag_set("TROPICAL_BACKWARD_NO_PAIR"))
+        return launch_staged_pair(dev, ja, jb, s);
+    if (want_a) {
+        st = launch_grad(dev, ja, s);
+        if (st != TROP_OK) return st;
+    }
+    if (want_b) {
+        st = launch_grad(dev, jb, s);
         if (st != TROP_OK) return st;
     }
     return ok();

@@ -92,11 +92,12 @@ enum KernelId : int {
     K_GEMM_DOMAIN_MINPLUS,
     K_GEMM_FMKM_MAXPLUS,  // float mode, wide, A k-vector, B column-vector
     K_GEMM_FMKM_MINPLUS,
-    K_GEMM_BACKWARD_STAGED_PLUS,  // backward, items staged through LDS per 64 segments (bins <= 256)
-    K_GEMM_BACKWARD_STAGED_PLUS_VEC,
-    K_GEMM_BACKWARD_STAGED_MUL,
-    K_GEMM_BACKWARD_STAGED_MUL_VEC,
-    K_COUNT
+    K_GEMM_BACKWARD_STAGED_PLUS,  // backward, items staged through LDS per 64 segments (bins <= 256);
+                                  // + load mode (elements, along items, across segments)
+    K_GEMM_BACKWARD_STAGED_MUL = K_GEMM_BACKWARD_STAGED_PLUS + 3,
+    K_GEMM_BACKWARD_STAGED2_PLUS = K_GEMM_BACKWARD_STAGED_MUL + 3,  // both gradients: + 3 mode(a) + mode(b)
+    K_GEMM_BACKWARD_STAGED2_MUL = K_GEMM_BACKWARD_STAGED2_PLUS + 9,
+    K_COUNT = K_GEMM_BACKWARD_STAGED2_MUL + 9
 };
 const char* kernel_name(KernelId id);
 

@@ -69,8 +69,18 @@ const std::vector<std::string>& kernel_names() {
             "trop_gemm_fmvo_maxplus_i32",    "trop_gemm_fmvo_minplus_i32",
             "trop_gemm_domain_maxplus_i32",  "trop_gemm_domain_minplus_i32",
             "trop_gemm_fmkm_maxplus_i32",    "trop_gemm_fmkm_minplus_i32",
-            "trop_gemm_backward_staged_plus", "trop_gemm_backward_staged_plus_vec",
-            "trop_gemm_backward_staged_mul",  "trop_gemm_backward_staged_mul_vec"};
+            "trop_gemm_backward_staged_plus_e", "trop_gemm_backward_staged_plus_i",
+            "trop_gemm_backward_staged_plus_s", "trop_gemm_backward_staged_mul_e",
+            "trop_gemm_backward_staged_mul_i", "trop_gemm_backward_staged_mul_s",
+            "trop_gemm_backward_staged2_plus_ee", "trop_gemm_backward_staged2_plus_ei",
+            "trop_gemm_backward_staged2_plus_es", "trop_gemm_backward_staged2_plus_ie",
+            "trop_gemm_backward_staged2_plus_ii", "trop_gemm_backward_staged2_plus_is",
+            "trop_gemm_backward_staged2_plus_se", "trop_gemm_backward_staged2_plus_si",
+            "trop_gemm_backward_staged2_plus_ss", "trop_gemm_backward_staged2_mul_ee",
+            "trop_gemm_backward_staged2_mul_ei", "trop_gemm_backward_staged2_mul_es",
+            "trop_gemm_backward_staged2_mul_ie", "trop_gemm_backward_staged2_mul_ii",
+            "trop_gemm_backward_staged2_mul_is", "trop_gemm_backward_staged2_mul_se",
+            "trop_gemm_backward_staged2_mul_si", "trop_gemm_backward_staged2_mul_ss"};
         static_assert(sizeof(families) / sizeof(families[0]) * NRING == K_FILL, "families");
         static_assert(K_FILL + sizeof(singles) / sizeof(singles[0]) == K_COUNT, "single kernels");
         std::vector<std::string> v;
