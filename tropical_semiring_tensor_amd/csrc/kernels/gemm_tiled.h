@@ -458,31 +458,45 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         static_assert((PER_WAVE / 16) % G == 0, "whole groups of steps");
         const TG* const Ar = A + ct.row0 * p.sa_row;
         const TG* const Bc = B + ct.col0 * p.sb_col;
+        // FIXED_KV: the host launches this instance only when every element
+        // of the tile's row and column panels lies below 2^29 elements from
+        // the panel's start, so a quad's place is a 32-bit byte offset from a
+        // wave-uniform base (no 64-bit address arithmetic per step)
+        const uint32_t sa_b = (uint32_t)p.sa_row * (uint32_t)sizeof(TG);
+        const uint32_t sb_b = (uint32_t)p.sb_col * (uint32_t)sizeof(TG);
 #pragma unroll 1
         for (int st0 = 0; st0 < PER_WAVE / 16; st0 += G) {
             T bst[G];
-            int w[G], off[G];
+            int w[G], off[G], row[G], col[G];
             bool live[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int o = wave * PER_WAVE + 16 * (st0 + g) + (lane >> 2);
-                const int row = o >> 6, col = o & 63;
-                off[g] = row * GEMM_RLD + col;
+                row[g] = o >> 6;
+                col[g] = o & 63;
+                off[g] = row[g] * GEMM_RLD + col[g];
                 bst[g] = rv[off[g]];
                 w[g] = rw[off[g]];
-                live[g] = row < rlim && col < clim;
+                live[g] = row[g] < rlim && col[g] < clim;
             }
             V x[G][QL], y[G][QL];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int row = off[g] / GEMM_RLD, col = off[g] - row * GEMM_RLD;
                 live[g] = live[g] && w[g] >= 0;
 #pragma unroll
                 for (int h = 0; h < QL; ++h) {
                     const int k0 = w[g] * CH + 4 * (q + 4 * h);
                     const bool in = live[g] && k0 < kt32;
-                    x[g][h] = *reinterpret_cast<const V*>(Ar + (in ? row : 0) * p.sa_row + (in ? k0 : 0));
-                    y[g][h] = *reinterpret_cast<const V*>(Bc + (in ? col : 0) * p.sb_col + (in ? k0 : 0));
+                    if constexpr (FIXED_KV) {
+                        const uint32_t kb = (uint32_t)k0 * (uint32_t)sizeof(TG);
+                        const uint32_t oa = in ? (uint32_t)row[g] * sa_b + kb : 0u;
+                        const uint32_t ob = in ? (uint32_t)col[g] * sb_b + kb : 0u;
+                        x[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Ar) + oa);
+                        y[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Bc) + ob);
+                    } else {
+                        x[g][h] = *reinterpret_cast<const V*>(Ar + (in ? row[g] : 0) * p.sa_row + (in ? k0 : 0));
+                        y[g][h] = *reinterpret_cast<const V*>(Bc + (in ? col[g] : 0) * p.sb_col + (in ? k0 : 0));
+                    }
                 }
             }
             int f[G];

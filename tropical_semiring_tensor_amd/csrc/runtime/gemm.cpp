@@ -269,7 +269,11 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // always the general instances.
     const bool fixed_ok = !env_flag_off("TROPICAL_GEMM_FIXED_LAYOUT");
     const bool kmvec = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec && p.b_mode == TROP_LOAD_MN_CONTIG && p.b_vec;
-    const bool fixed = gres && kvec && fixed_ok;
+    // (the fixed global-resolve instance addresses a tile's panels with
+    // 32-bit byte offsets: every element within 2^29 of the panel's start)
+    const int64_t pan_lim = int64_t(1) << 29;
+    const bool pan32 = 63 * p.sa_row + k < pan_lim && 63 * p.sb_col + k < pan_lim;
+    const bool fixed = gres && kvec && fixed_ok && pan32;
     const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
