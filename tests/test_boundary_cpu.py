@@ -154,6 +154,29 @@ def test_contract_plan_folds_canonical_operands(tb):
     assert "reduceA=a" in d and "A=gather:reduce" in d
 
 
+def test_contract_plan_two_level_k(tb, monkeypatch):
+    # the lattice-network step: the running result's first and last axes
+    # are contracted, the GEMM reads it in place with runs of 16 along k
+    d = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
+    assert "gemm A(x)B batch=1 m=65536 n=256 k=256" in d and "A=fold:krun16 B=fold" in d, d
+    # runs of two inner labels; the right operand; both, swapped
+    assert "A=fold:krun16" in tb.tropical_contract_pair_describe("vwef,vefA->wA", (3, 5, 2, 8), (3, 2, 8, 4))
+    assert "B=fold:krun8" in tb.tropical_contract_pair_describe("wke,kAe->wA", (7, 6, 8), (6, 5, 8))
+    d = tb.tropical_contract_pair_describe("vwe,vAe->Aw", (5, 7, 4), (5, 6, 4))
+    assert "B(x)A" in d and "A=fold:krun4 B=fold:krun4" in d, d
+    # runs of 2 or 32 elements, or an inner label off the unit stride, are gathered
+    assert "A=gather" in tb.tropical_contract_pair_describe("vwe,veA->wA", (5, 7, 2), (5, 2, 6))
+    assert "A=gather" in tb.tropical_contract_pair_describe("vwe,veA->wA", (5, 7, 32), (5, 32, 6))
+    assert "A=gather" in tb.tropical_contract_pair_describe("vwe,veA->wA", (5, 7, 16), (5, 16, 6),
+                                                            (1, 5, 35), None)
+    # (with the inner label at unit stride the axis order does not matter)
+    assert "A=fold:krun16" in tb.tropical_contract_pair_describe("vew,veA->wA", (5, 16, 7), (5, 16, 6),
+                                                                 (16 * 7, 1, 16), None)
+    monkeypatch.setenv("TROPICAL_NO_KRUN_FOLD", "1")
+    d = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
+    assert "A=gather" in d, d
+
+
 def test_contract_plan_flat_gather_for_a_small_bond(tb):
     # A (a=2, i=64, b=512): its canonical (b, i, a) order is a transpose of a
     # 512 x 2 plane, where a fixed 64-wide tile would be 2/64 in range; B's

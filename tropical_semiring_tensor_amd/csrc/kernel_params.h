@@ -55,6 +55,14 @@ struct TropGemmParams {
     // launch proceeds only if (all flags zero) == mode_run.  NULL: no gate.
     const int32_t* mode_flags;
     int32_t mode_slots, mode_run;
+    // two-level k of an operand read along k: a_krun > 0 splits A's k as
+    // k = hi a_krun + lo, lo on the unit-stride axis (sa_col = 1, a_krun a
+    // power of two from 4 to 16) and hi at stride sa_khi, so element (i, k)
+    // sits at i sa_row + (k / a_krun) sa_khi + k % a_krun -- an operand whose
+    // contracted axes lie on both sides of its free axes, read in place.
+    // 0: k at stride sa_col.  b_krun / sb_khi: the same for B (sb_row = 1).
+    int32_t a_krun, b_krun;
+    int64_t sa_khi, sb_khi;
 };
 
 // Domain pre-pass of an int32 max-plus / min-plus product (float mode):

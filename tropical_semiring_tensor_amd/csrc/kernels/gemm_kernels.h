@@ -24,7 +24,8 @@ __device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
         T best = R::zero();
         int arg = 0;
         for (int64_t k = 0; k < p.k; ++k) {
-            const T term = R::mul(A[k * p.sa_col], B[k * p.sb_row]);
+            const T term = R::mul(A[k_offset(k, p.a_krun, p.sa_khi, p.sa_col)],
+                                  B[k_offset(k, p.b_krun, p.sb_khi, p.sb_row)]);
             if (R::better(term, best)) {
                 best = term;
                 arg = (int)k;

@@ -161,6 +161,17 @@ __device__ __forceinline__ uint32_t mdiv(uint32_t n, uint32_t d, uint32_t m, uin
     return d == 1 ? n : (__umulhi(n, m) >> sh);
 }
 
+// Element offset of k along an operand's k axis: k stride sk, or (krun > 0)
+// the two-level k of TropGemmParams (k / krun at stride khi, k % krun on the
+// unit-stride axis).
+__device__ __forceinline__ int64_t k_offset(int64_t k, int32_t krun, int64_t khi, int64_t sk) {
+    if (krun > 0) {
+        const int sh = __builtin_ctz((uint32_t)krun);
+        return (k >> sh) * khi + (k & (krun - 1));
+    }
+    return k * sk;
+}
+
 template <bool SPLIT>
 __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
                                                 int64_t total) {
@@ -271,6 +282,7 @@ struct OpLoad {
     int64_t e_str;     // elements between the 4 elements of a vector
     int64_t mn;        // row / column of element 0
     int64_t k0;        // k of element 0 in slice 0
+    int64_t koff0;     // element offset of k0 along the k axis
     int64_t mn_lim, k_lim;
     int lds0;          // LDS word offset of element 0 (slot 0)
     int lds_v;         // LDS words between vectors v and v + 1
@@ -281,7 +293,7 @@ struct OpLoad {
 
     // Position of this thread's elements (independent of the tile).
     __device__ __forceinline__ void init(int mode, int v16, int64_t str_mn, int64_t str_k,
-                                         int64_t mnl, int64_t kl, int tid) {
+                                         int64_t mnl, int64_t kl, int tid, int32_t krun, int64_t khi) {
         mn_c_ = (mode == TROP_LOAD_MN_CONTIG);
         vec_ = v16 != 0;
         mn_lim = mnl;
@@ -306,6 +318,16 @@ struct OpLoad {
             mn = kc_row(tid);
             lds0 = kc_row(tid) * LDR + (kc_k(tid) ^ (SWZ ? bsw(kc_row(tid)) : 0));
         }
+        koff0 = k0 * str_k;
+        if (!mn_c() && krun > 0) {
+            // two-level k: a slice, the vector step and a thread's first k
+            // are whole runs of krun apart plus a place inside a run (SL and
+            // kv are multiples of 16, k0 of 4, krun divides 16)
+            const int sh = __builtin_ctz((uint32_t)krun);
+            k_step = (int64_t)(SL >> sh) * khi;
+            v_step = (int64_t)(kv >> sh) * khi;
+            koff0 = (int64_t)(k0 >> sh) * khi + (k0 & (krun - 1));
+        }
     }
 
     // Point at a tile: X is the operand of the batch entry, mn_start the
@@ -314,14 +336,16 @@ struct OpLoad {
                                        int tid) {
         const int64_t m_rel = mn_c() ? mc_row(tid) : kc_row(tid);
         mn = mn_start + m_rel;
-        q0 = X + mn * str_mn + k0 * str_k;
+        q0 = X + mn * str_mn + koff0;
         mn_full = mn_start + 64 <= mn_lim;
     }
 
     __device__ __forceinline__ void load(int g, T pad, T (&r)[NV][4]) const {
         const TG* q = q0 + (int64_t)g * k_step;
-        const int64_t kb = k0 + (int64_t)g * SL;
-        const bool full = mn_full && (int64_t)(g + 1) * SL <= k_lim;
+        // K < 2^31 (the host's limit: int32 argmax), so the slice bounds
+        // compare in 32 bits (a scalar compare; 64-bit ones go to the VALU)
+        const uint32_t kb = (uint32_t)k0 + (uint32_t)g * SL;
+        const bool full = mn_full && (uint32_t)(g + 1) * (uint32_t)SL <= (uint32_t)k_lim;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const TG* qv = q + v * v_step;
@@ -339,9 +363,9 @@ struct OpLoad {
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int64_t kk = kb + kv * v + (mn_c() ? 0 : e);
+                    const uint32_t kk = kb + (uint32_t)(kv * v + (mn_c() ? 0 : e));
                     const int64_t mm = mn + (mn_c() ? e : 0);
-                    r[v][e] = (kk < k_lim && mm < mn_lim) ? to_compute<T>(qv[e * e_str]) : pad;
+                    r[v][e] = (kk < (uint32_t)k_lim && mm < mn_lim) ? to_compute<T>(qv[e * e_str]) : pad;
                 }
             }
         }
@@ -371,8 +395,10 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
                                                           int ty, T (&best)[GEMM_TR][4],
                                                           const int (&idx)[GEMM_TR][4]) {
     using R = Ring<SR, T>;
-    const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
-    const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
+    const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch +
+                 (SPLIT ? k_offset(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
+    const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch +
+                 (SPLIT ? k_offset(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
     for (int r = 0; r < GEMM_TR; ++r)
         for (int c = 0; c < 4; ++c) {
             const int64_t i = ct.row0 + ty + GEMM_RS * r, j = ct.col0 + tx + 16 * c;
@@ -381,10 +407,12 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
             const T* b = B + j * p.sb_col;
             if constexpr (ARG) {
                 const int64_t k = idx[r][c];
-                best[r][c] = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
+                best[r][c] = R::mul(a[k_offset(k, p.a_krun, p.sa_khi, p.sa_col)],
+                                    b[k_offset(k, p.b_krun, p.sb_khi, p.sb_row)]);
             } else {
                 for (int64_t k = 0; k < (SPLIT ? ct.kt : p.k); ++k) {
-                    const T t = R::mul(a[k * p.sa_col], b[k * p.sb_row]);
+                    const T t = R::mul(a[k_offset(k, p.a_krun, p.sa_khi, p.sa_col)],
+                                       b[k_offset(k, p.b_krun, p.sb_khi, p.sb_row)]);
                     if (t == best[r][c]) {
                         best[r][c] = t;
                         break;
@@ -432,8 +460,10 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
     constexpr int QL = CH / 16;  // quads per lane: lane q reads quads q, q + 4, ...
     static_assert(CH % 16 == 0, "four lanes share a chunk of whole quads");
     const int64_t kt = SPLIT ? ct.kt : p.k;
-    const TG* const A = static_cast<const TG*>(p.A) + ct.b * p.sa_batch + (SPLIT ? ct.s * p.kchunk * p.sa_col : 0);
-    const TG* const B = static_cast<const TG*>(p.B) + ct.b * p.sb_batch + (SPLIT ? ct.s * p.kchunk * p.sb_row : 0);
+    const TG* const A = static_cast<const TG*>(p.A) + ct.b * p.sa_batch +
+                        (SPLIT ? k_offset(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
+    const TG* const B = static_cast<const TG*>(p.B) + ct.b * p.sb_batch +
+                        (SPLIT ? k_offset(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
     // 16-byte loads along k: k is the unit-stride axis with aligned rows
     // (A) / columns (B); a quad starts at a multiple of 4 terms
     const bool a_kv = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec;
@@ -464,64 +494,87 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         // wave-uniform base (no 64-bit address arithmetic per step)
         const uint32_t sa_b = (uint32_t)p.sa_row * (uint32_t)sizeof(TG);
         const uint32_t sb_b = (uint32_t)p.sb_col * (uint32_t)sizeof(TG);
+        // byte offset of a quad's first k (two-level k: whole runs at the
+        // run stride, then the place inside the run)
+        const int a_sh = p.a_krun > 0 ? __builtin_ctz((uint32_t)p.a_krun) : 0;
+        const int b_sh = p.b_krun > 0 ? __builtin_ctz((uint32_t)p.b_krun) : 0;
+        const uint32_t a_hi = p.a_krun > 0 ? (uint32_t)p.sa_khi * (uint32_t)sizeof(TG) : 0u;
+        const uint32_t b_hi = p.b_krun > 0 ? (uint32_t)p.sb_khi * (uint32_t)sizeof(TG) : 0u;
+        const uint32_t a_lo = p.a_krun > 0 ? (uint32_t)p.a_krun - 1 : ~0u;
+        const uint32_t b_lo = p.b_krun > 0 ? (uint32_t)p.b_krun - 1 : ~0u;
+        // one copy of the loop per k layout (a uniform choice, made once)
+        auto steps = [&](auto two_c) {
+            constexpr bool TWO = decltype(two_c)::value;
 #pragma unroll 1
-        for (int st0 = 0; st0 < PER_WAVE / 16; st0 += G) {
-            T bst[G];
-            int w[G], off[G], row[G], col[G];
-            bool live[G];
+            for (int st0 = 0; st0 < PER_WAVE / 16; st0 += G) {
+                T bst[G];
+                int w[G], off[G], row[G], col[G];
+                bool live[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int o = wave * PER_WAVE + 16 * (st0 + g) + (lane >> 2);
-                row[g] = o >> 6;
-                col[g] = o & 63;
-                off[g] = row[g] * GEMM_RLD + col[g];
-                bst[g] = rv[off[g]];
-                w[g] = rw[off[g]];
-                live[g] = row[g] < rlim && col[g] < clim;
-            }
-            V x[G][QL], y[G][QL];
+                for (int g = 0; g < G; ++g) {
+                    const int o = wave * PER_WAVE + 16 * (st0 + g) + (lane >> 2);
+                    row[g] = o >> 6;
+                    col[g] = o & 63;
+                    off[g] = row[g] * GEMM_RLD + col[g];
+                    bst[g] = rv[off[g]];
+                    w[g] = rw[off[g]];
+                    live[g] = row[g] < rlim && col[g] < clim;
+                }
+                V x[G][QL], y[G][QL];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                live[g] = live[g] && w[g] >= 0;
+                for (int g = 0; g < G; ++g) {
+                    live[g] = live[g] && w[g] >= 0;
 #pragma unroll
-                for (int h = 0; h < QL; ++h) {
-                    const int k0 = w[g] * CH + 4 * (q + 4 * h);
-                    const bool in = live[g] && k0 < kt32;
-                    if constexpr (FIXED_KV) {
-                        const uint32_t kb = (uint32_t)k0 * (uint32_t)sizeof(TG);
-                        const uint32_t oa = in ? (uint32_t)row[g] * sa_b + kb : 0u;
-                        const uint32_t ob = in ? (uint32_t)col[g] * sb_b + kb : 0u;
-                        x[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Ar) + oa);
-                        y[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Bc) + ob);
-                    } else {
-                        x[g][h] = *reinterpret_cast<const V*>(Ar + (in ? row[g] : 0) * p.sa_row + (in ? k0 : 0));
-                        y[g][h] = *reinterpret_cast<const V*>(Bc + (in ? col[g] : 0) * p.sb_col + (in ? k0 : 0));
+                    for (int h = 0; h < QL; ++h) {
+                        const int k0 = w[g] * CH + 4 * (q + 4 * h);
+                        const bool in = live[g] && k0 < kt32;
+                        if constexpr (FIXED_KV) {
+                            const uint32_t ku = (uint32_t)k0;
+                            uint32_t ka = ku * (uint32_t)sizeof(TG), kb = ka;
+                            if constexpr (TWO) {
+                                ka = (ku >> a_sh) * a_hi + (ku & a_lo) * (uint32_t)sizeof(TG);
+                                kb = (ku >> b_sh) * b_hi + (ku & b_lo) * (uint32_t)sizeof(TG);
+                            }
+                            const uint32_t oa = in ? (uint32_t)row[g] * sa_b + ka : 0u;
+                            const uint32_t ob = in ? (uint32_t)col[g] * sb_b + kb : 0u;
+                            x[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Ar) + oa);
+                            y[g][h] = *reinterpret_cast<const V*>(reinterpret_cast<const char*>(Bc) + ob);
+                        } else {
+                            const int64_t ka = TWO ? k_offset(k0, p.a_krun, p.sa_khi, 1) : k0;
+                            const int64_t kb = TWO ? k_offset(k0, p.b_krun, p.sb_khi, 1) : k0;
+                            x[g][h] = *reinterpret_cast<const V*>(Ar + (in ? row[g] * p.sa_row + ka : 0));
+                            y[g][h] = *reinterpret_cast<const V*>(Bc + (in ? col[g] * p.sb_col + kb : 0));
+                        }
                     }
                 }
-            }
-            int f[G];
+                int f[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                f[g] = CH;  // first matching term of this lane's quads, as its place in the chunk
+                for (int g = 0; g < G; ++g) {
+                    f[g] = CH;  // first matching term of this lane's quads, as its place in the chunk
 #pragma unroll
-                for (int h = QL - 1; h >= 0; --h) {
-                    const int kq = 4 * (q + 4 * h);
-                    const bool in = live[g] && w[g] * CH + kq < kt32;
-                    const V& xa = x[g][h];
-                    const V& yb = y[g][h];
-                    f[g] = in && R::mul(to_compute<T>(xa.w), to_compute<T>(yb.w)) == bst[g] ? kq + 3 : f[g];
-                    f[g] = in && R::mul(to_compute<T>(xa.z), to_compute<T>(yb.z)) == bst[g] ? kq + 2 : f[g];
-                    f[g] = in && R::mul(to_compute<T>(xa.y), to_compute<T>(yb.y)) == bst[g] ? kq + 1 : f[g];
-                    f[g] = in && R::mul(to_compute<T>(xa.x), to_compute<T>(yb.x)) == bst[g] ? kq : f[g];
+                    for (int h = QL - 1; h >= 0; --h) {
+                        const int kq = 4 * (q + 4 * h);
+                        const bool in = live[g] && w[g] * CH + kq < kt32;
+                        const V& xa = x[g][h];
+                        const V& yb = y[g][h];
+                        f[g] = in && R::mul(to_compute<T>(xa.w), to_compute<T>(yb.w)) == bst[g] ? kq + 3 : f[g];
+                        f[g] = in && R::mul(to_compute<T>(xa.z), to_compute<T>(yb.z)) == bst[g] ? kq + 2 : f[g];
+                        f[g] = in && R::mul(to_compute<T>(xa.y), to_compute<T>(yb.y)) == bst[g] ? kq + 1 : f[g];
+                        f[g] = in && R::mul(to_compute<T>(xa.x), to_compute<T>(yb.x)) == bst[g] ? kq : f[g];
+                    }
+                    // the first match among the output's four lanes (quad permutes)
+                    f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0xB1, 0xF, 0xF, true));  // lane ^ 1
+                    f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0x4E, 0xF, 0xF, true));  // lane ^ 2
                 }
-                // the first match among the output's four lanes (quad permutes)
-                f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0xB1, 0xF, 0xF, true));  // lane ^ 1
-                f[g] = min(f[g], __builtin_amdgcn_mov_dpp(f[g], 0x4E, 0xF, 0xF, true));  // lane ^ 2
-            }
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-                if (q == 0) rw[off[g]] = live[g] ? w[g] * CH + f[g] : 0;
-        }
+                for (int g = 0; g < G; ++g)
+                    if (q == 0) rw[off[g]] = live[g] ? w[g] * CH + f[g] : 0;
+            }
+        };
+        if ((p.a_krun | p.b_krun) != 0)
+            steps(std::true_type{});
+        else
+            steps(std::false_type{});
         return;
     }
     if constexpr (FIXED_KV) return;
@@ -536,8 +589,10 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
         for (int h = QL - 1; h >= 0; --h) {
             const int kq = 4 * (q + 4 * h);  // the quad's first term within the chunk
             const int64_t k0 = live ? (int64_t)w * CH + kq : 0;
-            const TG* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k0 * p.sa_col;
-            const TG* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k0 * p.sb_row;
+            // (a quad lies inside one run of a two-level k: krun is a
+            // multiple of 4, so its 4 terms are at unit stride)
+            const TG* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k_offset(k0, p.a_krun, p.sa_khi, p.sa_col);
+            const TG* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k_offset(k0, p.b_krun, p.sb_khi, p.sb_row);
             T ta[4], tb[4];
             if (a_kv && k0 + 4 <= kt) {
                 const V x = *reinterpret_cast<const V*>(a);
@@ -647,14 +702,16 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 
     LA la;
     LB lb;
-    la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid);
-    lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid);
+    la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid, p.a_krun, p.sa_khi);
+    lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid, p.b_krun, p.sb_khi);
     const TG* const Ag = static_cast<const TG*>(p.A);
     const TG* const Bg = static_cast<const TG*>(p.B);
     int f_nsl = 0;  // slices of the tile being fetched
     auto point = [&](const TileCoord& tc) {
-        la.at(Ag + tc.b * p.sa_batch + (SPLIT ? tc.s * p.kchunk * p.sa_col : 0), tc.row0, p.sa_row, p.sa_col, tid);
-        lb.at(Bg + tc.b * p.sb_batch + (SPLIT ? tc.s * p.kchunk * p.sb_row : 0), tc.col0, p.sb_col, p.sb_row, tid);
+        la.at(Ag + tc.b * p.sa_batch + (SPLIT ? k_offset(tc.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0),
+              tc.row0, p.sa_row, p.sa_col, tid);
+        lb.at(Bg + tc.b * p.sb_batch + (SPLIT ? k_offset(tc.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0),
+              tc.col0, p.sb_col, p.sb_row, tid);
         if constexpr (SPLIT) {
             la.k_lim = tc.kt;
             lb.k_lim = tc.kt;

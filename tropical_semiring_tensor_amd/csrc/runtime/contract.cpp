@@ -17,6 +17,7 @@
 // stride, is read in place instead of being gathered.
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -176,6 +177,41 @@ bool try_fold(const Plan& P, const Operand& op, const std::string& reduce, const
     return true;
 }
 
+// Can `op` be read in place with a two-level k?  The batch group and the
+// free group (rows of the GEMM's left operand, columns of its right one)
+// each collapse to one stride; the contracted group `gk` splits into outer
+// labels that collapse to one stride (hi) and inner labels that collapse to
+// unit stride with 4, 8 or 16 elements in all (the run), so that k =
+// outer index * run + inner index is the row-major index over gk.  The
+// GEMM then reads 16-byte vectors inside the runs instead of a gathered
+// copy.  k_is_col: gk is the operand's column group (the left operand).
+bool try_fold_two(const Plan& P, const Operand& op, const std::string& reduce, const std::string& gb,
+                  const std::string& gfree, const std::string& gk, bool k_is_col, trop_strides* s,
+                  int32_t* run, int64_t* hi) {
+    if (!reduce.empty()) return false;
+    if (const char* v = std::getenv("TROPICAL_NO_KRUN_FOLD"))  // tests: gather instead
+        if (*v && *v != '0') return false;
+    if (unique(op.sub).size() != op.sub.size()) return false;
+    int64_t sb, sf;
+    if (!group_stride(P, op, gb, &sb) || !group_stride(P, op, gfree, &sf)) return false;
+    for (size_t j = 1; j < gk.size(); ++j) {
+        const std::string outer = gk.substr(0, gk.size() - j), inner = gk.substr(gk.size() - j);
+        int64_t r = 1;
+        for (char c : inner) r = r > 16 ? r : r * P.ext[(int)c];
+        if (!krun_ok((int32_t)std::min<int64_t>(r, 17))) continue;
+        int64_t si = 0, so = 0;
+        if (!group_stride(P, op, inner, &si) || si != 1) continue;
+        if (!group_stride(P, op, outer, &so)) continue;
+        *run = (int32_t)r;
+        *hi = so;
+        s->batch = sb;
+        s->row = k_is_col ? sf : 1;
+        s->col = k_is_col ? 1 : sf;
+        return true;
+    }
+    return false;
+}
+
 trop_status plan_operand(const Plan& P, const Operand& op, const std::string& canonical, GatherPlan* g) {
     int32_t in_lab[TROP_MAX_DIMS], out_lab[TROP_MAX_DIMS];
     for (size_t d = 0; d < op.sub.size(); ++d) in_lab[d] = op.sub[d];
@@ -257,13 +293,15 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
     const std::string& l_red = P.swap ? P.b_red : P.a_red;
     const std::string& r_red = P.swap ? P.a_red : P.b_red;
 
-    P.a_fold = try_fold(P, L, l_red, P.batch, rows, P.contracted, &P.sA);
+    P.a_fold = try_fold(P, L, l_red, P.batch, rows, P.contracted, &P.sA) ||
+               try_fold_two(P, L, l_red, P.batch, rows, P.contracted, true, &P.sA, &P.kr.a_run, &P.kr.a_hi);
     if (!P.a_fold) {
         st = plan_operand(P, L, canL, &P.ga);
         if (st != TROP_OK) return st;
         P.sA = {P.K, 1, P.gm * P.K};
     }
-    P.b_fold = try_fold(P, Rt, r_red, P.batch, P.contracted, cols, &P.sB);
+    P.b_fold = try_fold(P, Rt, r_red, P.batch, P.contracted, cols, &P.sB) ||
+               try_fold_two(P, Rt, r_red, P.batch, cols, P.contracted, false, &P.sB, &P.kr.b_run, &P.kr.b_hi);
     if (!P.b_fold) {
         st = plan_operand(P, Rt, canR, &P.gb);
         if (st != TROP_OK) return st;
@@ -335,17 +373,21 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
 }
 
 std::string pair_describe(const Plan& P) {
-    char buf[512];
+    // how the GEMM reads A and B: "fold" (in place), "fold:krunR" (in place
+    // with a two-level k of run R) or "gather:<path>"
+    auto how = [&](bool fold, int32_t run, const GatherPlan& g) {
+        if (!fold) return std::string("gather:") + gather_path_name(g.path);
+        return run > 0 ? "fold:krun" + std::to_string(run) : std::string("fold");
+    };
+    const std::string ha = P.swap ? how(P.b_fold, P.kr.b_run, P.gb) : how(P.a_fold, P.kr.a_run, P.ga);
+    const std::string hb = P.swap ? how(P.a_fold, P.kr.a_run, P.ga) : how(P.b_fold, P.kr.b_run, P.gb);
+    char buf[640];
     std::snprintf(buf, sizeof(buf),
                   "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm %s batch=%lld m=%lld "
-                  "n=%lld k=%lld%s; A=%s%s B=%s%s out=%s%s; workspace=%zu",
+                  "n=%lld k=%lld%s; A=%s B=%s out=%s%s; workspace=%zu",
                   P.batch.c_str(), P.left.c_str(), P.right.c_str(), P.contracted.c_str(), P.a_red.c_str(),
                   P.b_red.c_str(), P.swap ? "B(x)A" : "A(x)B", (long long)P.nb, (long long)P.gm,
-                  (long long)P.gn, (long long)P.K, P.gemm_split ? " splitK" : "",
-                  (P.swap ? P.b_fold : P.a_fold) ? "fold" : "gather:",
-                  (P.swap ? P.b_fold : P.a_fold) ? "" : gather_path_name((P.swap ? P.gb : P.ga).path),
-                  (P.swap ? P.a_fold : P.b_fold) ? "fold" : "gather:",
-                  (P.swap ? P.a_fold : P.b_fold) ? "" : gather_path_name((P.swap ? P.ga : P.gb).path),
+                  (long long)P.gn, (long long)P.K, P.gemm_split ? " splitK" : "", ha.c_str(), hb.c_str(),
                   P.c_direct ? "direct" : "permute:", P.c_direct ? "" : gather_path_name(P.gc.path), P.ws);
     return buf;
 }
@@ -399,7 +441,7 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
     int32_t* i_gemm = P.c_direct ? argmax : (argmax ? reinterpret_cast<int32_t*>(ws + P.off_i) : nullptr);
     const trop_strides sC = {P.gn, 1, P.gm * P.gn};
     st = run_gemm(dev, semiring, dtype, a_use, P.sA, b_use, P.sB, c_gemm, sC, i_gemm, P.gm, P.gn, P.K, P.nb, s,
-                  P.split_bytes ? ws + P.off_split : nullptr, P.split_bytes);
+                  P.split_bytes ? ws + P.off_split : nullptr, P.split_bytes, &P.kr);
     if (st != TROP_OK) return st;
     if (route) {
         // the product's k, then the reduction winners at that k, as one

@@ -46,6 +46,10 @@ struct PairPlan {
     bool red_l = false, red_r = false;
     int64_t ra_n = 1, rb_n = 1;
     bool route_fits = true;  // K * ra_n * rb_n < 2^31
+    // an operand folded with a two-level k (its contracted labels on both
+    // sides of its free ones): a_run / a_hi for the GEMM's left operand,
+    // b_run / b_hi for its right one (0: plain fold or gathered)
+    GemmKRuns kr{};
 };
 
 // "lhs,rhs->out" into its three subscripts (spaces ignored).

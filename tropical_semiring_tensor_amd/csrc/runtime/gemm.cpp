@@ -135,7 +135,7 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch) {
 trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
                      const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
                      int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream, void* workspace,
-                     size_t workspace_bytes) {
+                     size_t workspace_bytes, const GemmKRuns* kr) {
     if (m == 0 || n == 0 || batch == 0) return TROP_OK;
     const int ri = ring_index(sr, dt);
     if (k == 0) {
@@ -174,6 +174,17 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     p.kchunk = k;
     p.c_split = 0;
 
+    // two-level k (contracted axes on both sides of the free ones): read
+    // along k, 16-byte vectors inside the runs
+    const bool a_two = kr && kr->a_run > 0, b_two = kr && kr->b_run > 0;
+    if (a_two) {
+        p.a_krun = kr->a_run;
+        p.sa_khi = kr->a_hi;
+    }
+    if (b_two) {
+        p.b_krun = kr->b_run;
+        p.sb_khi = kr->b_hi;
+    }
     if (env_flag("TROPICAL_FORCE_SIMPLE_GEMM")) {
         return launch(dev, (KernelId)(K_GEMM_SIMPLE_MAXPLUS_F32 + ri), TROP_K_GEMM_SIMPLE,
                       grid_for(m * n * batch, 256), 256, &p, stream);
@@ -181,7 +192,10 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
 
     // A: row-major (k unit-stride), column-major (i unit-stride), or
     // neither (element-wise loads along k).
-    if (sA.col == 1) {
+    if (a_two) {
+        p.a_mode = TROP_LOAD_K_CONTIG;
+        p.a_vec = aligned16(A) && sA.row % 4 == 0 && sA.batch % 4 == 0 && kr->a_hi % 4 == 0;
+    } else if (sA.col == 1) {
         p.a_mode = TROP_LOAD_K_CONTIG;
         p.a_vec = aligned16(A) && sA.row % 4 == 0 && sA.batch % 4 == 0;
     } else if (sA.row == 1) {
@@ -192,7 +206,10 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         p.a_vec = 0;
     }
     // B: row-major (j unit-stride), column-major (k unit-stride), or neither.
-    if (sB.col == 1) {
+    if (b_two) {
+        p.b_mode = TROP_LOAD_K_CONTIG;
+        p.b_vec = aligned16(B) && sB.col % 4 == 0 && sB.batch % 4 == 0 && kr->b_hi % 4 == 0;
+    } else if (sB.col == 1) {
         p.b_mode = TROP_LOAD_MN_CONTIG;
         p.b_vec = aligned16(B) && sB.row % 4 == 0 && sB.batch % 4 == 0;
     } else if (sB.row == 1) {
@@ -272,7 +289,9 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // (the fixed global-resolve instance addresses a tile's panels with
     // 32-bit byte offsets: every element within 2^29 of the panel's start)
     const int64_t pan_lim = int64_t(1) << 29;
-    const bool pan32 = 63 * p.sa_row + k < pan_lim && 63 * p.sb_col + k < pan_lim;
+    const int64_t a_kspan = a_two ? (k - 1) / p.a_krun * p.sa_khi + p.a_krun : k;
+    const int64_t b_kspan = b_two ? (k - 1) / p.b_krun * p.sb_khi + p.b_krun : k;
+    const bool pan32 = 63 * p.sa_row + a_kspan < pan_lim && 63 * p.sb_col + b_kspan < pan_lim;
     const bool fixed = gres && kvec && fixed_ok && pan32;
     const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
     const KernelId kid =
@@ -304,8 +323,9 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // pre-pass writes its flags into the workspace, then the float-mode
     // kernel and the int32 kernel are both enqueued, each gated on the flags
     // so that exactly one of them computes.  No host round trip.
+    // (the domain pre-pass reads plain strides: not with a two-level k)
     const bool fm = dt == TROP_I32 && sr != TROP_MAX_MUL && !split && workspace && workspace_bytes >= kFmBytes &&
-                    fm_size_ok(m, n, k, batch);
+                    !a_two && !b_two && fm_size_ok(m, n, k, batch);
     if (fm) {
         TropDomainParams d{};
         d.A = static_cast<const int32_t*>(A);

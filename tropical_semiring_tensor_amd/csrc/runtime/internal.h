@@ -185,13 +185,24 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch);
 // max-plus / min-plus when it is large enough to take it (any dtype: the
 // sizing calls know no dtype), else 0.  Host-only.
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
+// Two-level k of the GEMM's operands (TropGemmParams a_krun / sa_khi):
+// a_run > 0 reads A's k as k = hi a_run + lo, lo at unit stride (sA.col = 1)
+// and hi at stride a_hi; a_run is 4, 8 or 16.  Likewise b_run / b_hi with
+// sB.row = 1.  0: plain strides.
+struct GemmKRuns {
+    int32_t a_run = 0, b_run = 0;
+    int64_t a_hi = 0, b_hi = 0;
+};
+inline bool krun_ok(int32_t r) { return r == 4 || r == 8 || r == 16; }
+
 // Enqueue without re-validating pointers (used by the contraction driver).
 // `workspace` (may be NULL) holds plan_splitk(...).bytes when a split is
-// wanted; without it the product is not split.
+// wanted; without it the product is not split.  `kr` (may be NULL): a
+// two-level k, checked by the caller (krun_ok, unit inner stride).
 trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, trop_strides sA,
                      const void* B, trop_strides sB, void* C, trop_strides sC, int32_t* argmax,
                      int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t stream,
-                     void* workspace = nullptr, size_t workspace_bytes = 0);
+                     void* workspace = nullptr, size_t workspace_bytes = 0, const GemmKRuns* kr = nullptr);
 trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, trop_strides sB,
                             trop_strides sC, int64_t m, int64_t n, int64_t k, int64_t batch);
 
