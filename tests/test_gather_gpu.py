@@ -351,7 +351,10 @@ def test_runs_path_in_contraction_describe(tb, monkeypatch):
     # the lattice network's boundary gather: a 16-word run (bond 16) whose
     # neighbour moves from the front to the end.  The runs tile (32 runs
     # along the moved axis) is half in range for its 16, so the flat tile
-    # takes it; with the flat path off it is the runs path.
+    # takes it; with the flat path off it is the runs path.  (By default the
+    # GEMM reads this operand in place with a two-level k: the gather is
+    # asked for here.)
+    monkeypatch.setenv("TROPICAL_NO_KRUN_FOLD", "1")
     desc = tb.tropical_contract_pair_describe("vwxyze,veAf->wxyzAf", (16,) * 6, (16,) * 4)
     assert "A=gather:flat" in desc, desc
     monkeypatch.setenv("TROPICAL_FLAT_PATH", "0")

@@ -172,6 +172,14 @@ __device__ __forceinline__ int64_t k_offset(int64_t k, int32_t krun, int64_t khi
     return k * sk;
 }
 
+// k_offset in an instance built with the two-level k (KR), plain strides
+// otherwise (the fixed-layout instances: no registers spent on it).
+template <bool KR>
+__device__ __forceinline__ int64_t k_off(int64_t k, int32_t krun, int64_t khi, int64_t sk) {
+    if constexpr (KR) return k_offset(k, krun, khi, sk);
+    return k * sk;
+}
+
 template <bool SPLIT>
 __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
                                                 int64_t total) {
@@ -390,15 +398,15 @@ struct OpLoad {
 // the bits of the first winning term, recomputed from global memory at the
 // resolved index (with argmax) or found by a scan along k (value only).
 // Rare and only taken by a wave that holds such an output.
-template <int SR, typename T, bool ARG, bool SPLIT>
+template <int SR, typename T, bool ARG, bool SPLIT, bool KR>
 __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoord ct, int tx,
                                                           int ty, T (&best)[GEMM_TR][4],
                                                           const int (&idx)[GEMM_TR][4]) {
     using R = Ring<SR, T>;
     const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch +
-                 (SPLIT ? k_offset(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
+                 (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
     const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch +
-                 (SPLIT ? k_offset(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
+                 (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
     for (int r = 0; r < GEMM_TR; ++r)
         for (int c = 0; c < 4; ++c) {
             const int64_t i = ct.row0 + ty + GEMM_RS * r, j = ct.col0 + tx + 16 * c;
@@ -407,12 +415,12 @@ __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoo
             const T* b = B + j * p.sb_col;
             if constexpr (ARG) {
                 const int64_t k = idx[r][c];
-                best[r][c] = R::mul(a[k_offset(k, p.a_krun, p.sa_khi, p.sa_col)],
-                                    b[k_offset(k, p.b_krun, p.sb_khi, p.sb_row)]);
+                best[r][c] = R::mul(a[k_off<KR>(k, p.a_krun, p.sa_khi, p.sa_col)],
+                                    b[k_off<KR>(k, p.b_krun, p.sb_khi, p.sb_row)]);
             } else {
                 for (int64_t k = 0; k < (SPLIT ? ct.kt : p.k); ++k) {
-                    const T t = R::mul(a[k_offset(k, p.a_krun, p.sa_khi, p.sa_col)],
-                                       b[k_offset(k, p.b_krun, p.sb_khi, p.sb_row)]);
+                    const T t = R::mul(a[k_off<KR>(k, p.a_krun, p.sa_khi, p.sa_col)],
+                                       b[k_off<KR>(k, p.b_krun, p.sb_khi, p.sb_row)]);
                     if (t == best[r][c]) {
                         best[r][c] = t;
                         break;
@@ -452,7 +460,7 @@ constexpr int GEMM_RLD = 65;  // row length of the parked tile (words; odd: rows
 #else
 #define TROP_RESOLVE_ATTR __forceinline__
 #endif
-template <int SR, typename T, bool SPLIT, int CH, typename TG = T, bool FIXED_KV = false>
+template <int SR, typename T, bool SPLIT, int CH, typename TG = T, bool FIXED_KV = false, bool KR = true>
 __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoord ct, int tid, const T* rv,
                                              int* rw) {
     using R = Ring<SR, T>;
@@ -461,9 +469,9 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
     static_assert(CH % 16 == 0, "four lanes share a chunk of whole quads");
     const int64_t kt = SPLIT ? ct.kt : p.k;
     const TG* const A = static_cast<const TG*>(p.A) + ct.b * p.sa_batch +
-                        (SPLIT ? k_offset(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
+                        (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
     const TG* const B = static_cast<const TG*>(p.B) + ct.b * p.sb_batch +
-                        (SPLIT ? k_offset(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
+                        (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
     // 16-byte loads along k: k is the unit-stride axis with aligned rows
     // (A) / columns (B); a quad starts at a multiple of 4 terms
     const bool a_kv = p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec;
@@ -571,8 +579,8 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
                     if (q == 0) rw[off[g]] = live[g] ? w[g] * CH + f[g] : 0;
             }
         };
-        if ((p.a_krun | p.b_krun) != 0)
-            steps(std::true_type{});
+        if (KR && (p.a_krun | p.b_krun) != 0)
+            steps(std::integral_constant<bool, KR>{});
         else
             steps(std::false_type{});
         return;
@@ -591,8 +599,8 @@ __device__ TROP_RESOLVE_ATTR void resolve_tile(const TropGemmParams& p, TileCoor
             const int64_t k0 = live ? (int64_t)w * CH + kq : 0;
             // (a quad lies inside one run of a two-level k: krun is a
             // multiple of 4, so its 4 terms are at unit stride)
-            const TG* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k_offset(k0, p.a_krun, p.sa_khi, p.sa_col);
-            const TG* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k_offset(k0, p.b_krun, p.sb_khi, p.sb_row);
+            const TG* a = A + (ct.row0 + (live ? row : 0)) * p.sa_row + k_off<KR>(k0, p.a_krun, p.sa_khi, p.sa_col);
+            const TG* b = B + (ct.col0 + (live ? col : 0)) * p.sb_col + k_off<KR>(k0, p.b_krun, p.sb_khi, p.sb_row);
             T ta[4], tb[4];
             if (a_kv && k0 + 4 <= kt) {
                 const V x = *reinterpret_cast<const V*>(a);
@@ -658,7 +666,7 @@ __device__ __forceinline__ bool mode_gate_open(const TropGemmParams& p) {
 }
 
 template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false, typename TG = T,
-          int LAYOUT_A = LAYOUT_ANY, int LAYOUT_B = LAYOUT_ANY>
+          int LAYOUT_A = LAYOUT_ANY, int LAYOUT_B = LAYOUT_ANY, bool KR = true>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
@@ -702,15 +710,16 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 
     LA la;
     LB lb;
-    la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid, p.a_krun, p.sa_khi);
-    lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid, p.b_krun, p.sb_khi);
+    // (KR: the instance reads a two-level k when the launch asks for one)
+    la.init(p.a_mode, p.a_vec, p.sa_row, p.sa_col, p.m, p.k, tid, KR ? p.a_krun : 0, KR ? p.sa_khi : 0);
+    lb.init(p.b_mode, p.b_vec, p.sb_col, p.sb_row, p.n, p.k, tid, KR ? p.b_krun : 0, KR ? p.sb_khi : 0);
     const TG* const Ag = static_cast<const TG*>(p.A);
     const TG* const Bg = static_cast<const TG*>(p.B);
     int f_nsl = 0;  // slices of the tile being fetched
     auto point = [&](const TileCoord& tc) {
-        la.at(Ag + tc.b * p.sa_batch + (SPLIT ? k_offset(tc.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0),
+        la.at(Ag + tc.b * p.sa_batch + (SPLIT ? k_off<KR>(tc.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0),
               tc.row0, p.sa_row, p.sa_col, tid);
-        lb.at(Bg + tc.b * p.sb_batch + (SPLIT ? k_offset(tc.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0),
+        lb.at(Bg + tc.b * p.sb_batch + (SPLIT ? k_off<KR>(tc.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0),
               tc.col0, p.sb_col, p.sb_row, tid);
         if constexpr (SPLIT) {
             la.k_lim = tc.kt;
@@ -792,7 +801,11 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             const int sk = s * GEMM_SL;
             // Chunks of the last slice that lie wholly past K hold only
             // padding (terms that cannot win): they are skipped, which makes
-            // a small K cost its own chunks and not a whole slice.
+            // a small K cost its own chunks and not a whole slice.  Not in
+            // the global-resolve kernels (K > 256, at most one partial
+            // slice): there the exit would make the running values' register
+            // depend on where the slice ended, which costs a copy of every
+            // one of them per slice.
             const int64_t k_left = (SPLIT ? ct.kt : p.k) - (int64_t)g * GEMM_SL;
             const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + CH - 1) / CH) * QPC;
             V fa[2][GEMM_TR], fb[2][4];
@@ -804,7 +817,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             T prev[GEMM_TR][4];  // argmax: the best before the current chunk
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                if (q % QPC == 0 && q > 0 && q >= q_end) break;  // uniform over the workgroup
+                if (!GRES && q % QPC == 0 && q > 0 && q >= q_end) break;  // uniform over the workgroup
                 const int cur = Cfg::PF ? q & 1 : 0, nxt = cur ^ 1;
                 if constexpr (Cfg::PF) {
                     if (q + 1 < NQ) {
@@ -923,7 +936,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                             rw[o] = win[r][c];
                         }
                     __syncthreads();
-                    resolve_tile<SR, T, SPLIT, CH, TG, LAYOUT_A == LAYOUT_KV && LAYOUT_B == LAYOUT_KV>(p, ct, tid, rv,
+                    resolve_tile<SR, T, SPLIT, CH, TG, LAYOUT_A == LAYOUT_KV && LAYOUT_B == LAYOUT_KV, KR>(p, ct, tid, rv,
                                                                                             rw);
                     __syncthreads();
 #pragma unroll
@@ -955,7 +968,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                             for (int c = 0; c < 4; ++c) any0 |= best[r][c] == (T)0;
                         if (__any(any0))
-                            zero_bits_fixup<SR, T, ARG, SPLIT>(p, ct, tx, ty, best, idx);
+                            zero_bits_fixup<SR, T, ARG, SPLIT, KR>(p, ct, tx, ty, best, idx);
                     }
                 }
                 const int64_t c_off = ct.b * p.sc_batch + (SPLIT ? ct.s * p.c_split : 0);

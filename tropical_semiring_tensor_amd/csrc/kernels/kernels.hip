@@ -25,6 +25,10 @@ using namespace trop;
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo_##NAME(      \
         TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, false, false, false, false, T, LAYOUT_ANY, LAYOUT_ANY, false>(p); \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vor_##NAME(     \
+        TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, false, false>(p);                                                \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_n_##NAME(       \
@@ -37,11 +41,15 @@ using namespace trop;
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_GR void trop_gemm_tiled_gkk_##NAME( \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, T, true, false, false, true, T, LAYOUT_KV, LAYOUT_KV>(p);           \
+        gemm_tiled_body<SR, T, true, false, false, true, T, LAYOUT_KV, LAYOUT_KV, false>(p);    \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_km_##NAME(     \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV>(p);          \
+        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV, false>(p);   \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_kmr_##NAME(    \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV, true>(p);    \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
         TropGemmParams p) {                                                                     \
@@ -80,23 +88,23 @@ TROP_GEMM_ENTRIES(maxmul_i32, TROP_SR_MAX_MUL, int32_t, TROP_ARGW_I32)
 #define TROP_GEMM_FM_ENTRIES(NAME, SR)                                                          \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_F32 void trop_gemm_fm_##NAME( \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, float, true, false, false, false, int32_t>(p);                      \
+        gemm_tiled_body<SR, float, true, false, false, false, int32_t, LAYOUT_ANY, LAYOUT_ANY, false>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_fmn_##NAME(            \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, float, true, false, true, false, int32_t>(p);                       \
+        gemm_tiled_body<SR, float, true, false, true, false, int32_t, LAYOUT_ANY, LAYOUT_ANY, false>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_GR void trop_gemm_fmg_##NAME( \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, float, true, false, false, true, int32_t>(p);                       \
+        gemm_tiled_body<SR, float, true, false, false, true, int32_t, LAYOUT_ANY, LAYOUT_ANY, false>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_fmvo_##NAME(           \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, float, false, false, false, false, int32_t>(p);                     \
+        gemm_tiled_body<SR, float, false, false, false, false, int32_t, LAYOUT_ANY, LAYOUT_ANY, false>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) TROP_ARGW_F32 void trop_gemm_fmkm_##NAME( \
         TropGemmParams p) {                                                                     \
-        gemm_tiled_body<SR, float, true, false, false, false, int32_t, LAYOUT_KV, LAYOUT_MV>(p); \
+        gemm_tiled_body<SR, float, true, false, false, false, int32_t, LAYOUT_KV, LAYOUT_MV, false>(p); \
     }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_domain_##NAME(TropDomainParams p) { \
         gemm_domain_body<SR>(p);                                                                \

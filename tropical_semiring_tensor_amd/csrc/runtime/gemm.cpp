@@ -292,14 +292,18 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     const int64_t a_kspan = a_two ? (k - 1) / p.a_krun * p.sa_khi + p.a_krun : k;
     const int64_t b_kspan = b_two ? (k - 1) / p.b_krun * p.sb_khi + p.b_krun : k;
     const bool pan32 = 63 * p.sa_row + a_kspan < pan_lim && 63 * p.sb_col + b_kspan < pan_lim;
-    const bool fixed = gres && kvec && fixed_ok && pan32;
+    // (the fixed instances are built without the two-level k; the km form
+    // has a second instance with it)
+    const bool fixed = gres && kvec && fixed_ok && pan32 && !a_two && !b_two;
     const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
+    const KernelId km_id = a_two || b_two ? K_GEMM_TILED_KMR_MAXPLUS_F32 : K_GEMM_TILED_KM_MAXPLUS_F32;
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
               : (KernelId)((argmax ? (gres     ? (fixed ? K_GEMM_TILED_GKK_MAXPLUS_F32 : K_GEMM_TILED_G_MAXPLUS_F32)
                                       : narrow ? K_GEMM_TILED_N_MAXPLUS_F32
-                                               : (fixed_km ? K_GEMM_TILED_KM_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32))
-                                   : K_GEMM_TILED_VO_MAXPLUS_F32) + ri);
+                                               : (fixed_km ? km_id : K_GEMM_TILED_MAXPLUS_F32))
+                                   : (a_two || b_two ? K_GEMM_TILED_VOR_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32)) +
+                         ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8
     // keeps every workgroup's tiles on one XCD.

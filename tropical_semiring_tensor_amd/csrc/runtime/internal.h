@@ -35,7 +35,9 @@ enum KernelId : int {
     K_GATHER_REDUCE_VEC_MAXPLUS_F32 = K_GEMM_TILED_G_MAXPLUS_F32 + NRING,  // reduce, 4 outputs per thread
     K_GEMM_TILED_GKK_MAXPLUS_F32 = K_GATHER_REDUCE_VEC_MAXPLUS_F32 + NRING,  // global resolve, both operands k-vector
     K_GEMM_TILED_KM_MAXPLUS_F32 = K_GEMM_TILED_GKK_MAXPLUS_F32 + NRING,  // wide, A k-vector, B column-vector
-    K_FILL = K_GEMM_TILED_KM_MAXPLUS_F32 + NRING,
+    K_GEMM_TILED_KMR_MAXPLUS_F32 = K_GEMM_TILED_KM_MAXPLUS_F32 + NRING,  // the same, with a two-level k
+    K_GEMM_TILED_VOR_MAXPLUS_F32 = K_GEMM_TILED_KMR_MAXPLUS_F32 + NRING,  // value only, with a two-level k
+    K_FILL = K_GEMM_TILED_VOR_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,

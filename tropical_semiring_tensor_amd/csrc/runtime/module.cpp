@@ -40,7 +40,8 @@ const std::vector<std::string>& kernel_names() {
                                                "trop_gemm_simple_",      "trop_gather_reduce_",
                                                "trop_gemm_splitk_merge_", "trop_gemm_tiled_n_",
                                                "trop_gemm_tiled_g_",     "trop_gather_reduce_vec_",
-                                               "trop_gemm_tiled_gkk_",   "trop_gemm_tiled_km_"};
+                                               "trop_gemm_tiled_gkk_",   "trop_gemm_tiled_km_",
+                                               "trop_gemm_tiled_kmr_",   "trop_gemm_tiled_vor_"};
         static const char* const singles[] = {
             "trop_fill",                     "trop_gather_copy",
             "trop_gather_tiled",             "trop_gather_naive",
