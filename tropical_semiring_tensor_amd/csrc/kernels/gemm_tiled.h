@@ -114,6 +114,12 @@ constexpr bool GEMM_CHAIN_RECORD = TROP_GEMM_CHAIN_RECORD != 0;
 #ifndef TROP_GEMM_CH_GR
 #define TROP_GEMM_CH_GR 16  // argmax chunk of the global-resolve kernels (terms)
 #endif
+// Argmax chunk of the wide float kernels (K-block 128: each output re-scans
+// one chunk per block, so a shorter chunk halves the re-scan for one more
+// record per 8 terms)
+#ifndef TROP_GEMM_CH_WIDE
+#define TROP_GEMM_CH_WIDE 8
+#endif
 
 template <bool ARG, typename T, bool NARROW, bool GRES = false>
 struct GemmCfg {
@@ -128,7 +134,7 @@ struct GemmCfg {
     // next LDS fragment (main loop) and next chunk (re-scan) loaded ahead
     static constexpr bool PF = GRES ? TROP_GEMM_GR_PF != 0 : !F32A;
     // argmax chunk (terms): one record per chunk and output
-    static constexpr int CH = GRES ? TROP_GEMM_CH_GR : GEMM_CH;
+    static constexpr int CH = GRES ? TROP_GEMM_CH_GR : F32A ? TROP_GEMM_CH_WIDE : GEMM_CH;
     static constexpr int NSL = KB / SL;  // slices per block
     static_assert(SL % CH == 0 && KB % SL == 0, "whole chunks per slice, whole slices per block");
     // LDS row length in words: 4 words of padding put rows r and r + 1 in
@@ -884,16 +890,17 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 // before the current slot's scan.  A slot that did not improve
                 // scans chunk 0 and keeps its index.
                 constexpr int NS = GEMM_TR * 4;
-                V av[2][4], bv[2][4];
+                V av[2][QPC], bv[2][QPC];
                 auto rs_load = [&](int n, int buf) {
                     const int r = n / 4, c = n % 4;
                     const int w = win[r][c] < 0 ? 0 : win[r][c];
-                    const T* ap = a_row + r * GEMM_RS * LDR + w * GEMM_CH;
-                    const T* bp = b_col + c * 16 * LDR + w * GEMM_CH;
+                    const T* ap = a_row + r * GEMM_RS * LDR + w * CH;
+                    const T* bp = b_col + c * 16 * LDR;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
+                    for (int u = 0; u < QPC; ++u) {
                         av[buf][u] = *reinterpret_cast<const V*>(ap + 4 * u);
-                        bv[buf][u] = *reinterpret_cast<const V*>(bp + 4 * (u ^ c));
+                        // (B's quads are swizzled: quad q of column c-group at q ^ c)
+                        bv[buf][u] = *reinterpret_cast<const V*>(bp + 4 * ((w * QPC + u) ^ c));
                     }
                 };
                 if constexpr (Cfg::PF) rs_load(0, 0);
@@ -906,16 +913,16 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         rs_load(n, 0);
                     }
                     const T bst = best[r][c];
-                    int f = GEMM_CH - 1;
+                    int f = CH - 1;
 #pragma unroll
-                    for (int u = 3; u >= 0; --u) {
+                    for (int u = QPC - 1; u >= 0; --u) {
                         const V a = av[cur][u], b = bv[cur][u];
                         f = (R::mul(a.w, b.w) == bst) ? 4 * u + 3 : f;
                         f = (R::mul(a.z, b.z) == bst) ? 4 * u + 2 : f;
                         f = (R::mul(a.y, b.y) == bst) ? 4 * u + 1 : f;
                         f = (R::mul(a.x, b.x) == bst) ? 4 * u : f;
                     }
-                    idx[r][c] = win[r][c] >= 0 ? (int)blk_k0 + win[r][c] * GEMM_CH + f : idx[r][c];
+                    idx[r][c] = win[r][c] >= 0 ? (int)blk_k0 + win[r][c] * CH + f : idx[r][c];
                     win[r][c] = -1;
                 }
                 blk_k0 += Cfg::KB;
