@@ -10,8 +10,9 @@
 //    (output, k): one add / multiply per term and one v_max3 / v_min3 per
 //    two terms.
 //  * An exact per-term argmax would add a compare and two selects per term.
-//    Instead the running value is compared once per chunk of CH = 16 terms
-//    (one compare + one select: which chunk last improved strictly).  The
+//    Instead the running value is compared once per chunk of CH terms (16;
+//    8 in the wide float kernels, whose K-block is short) (one compare + one
+//    select: which chunk last improved strictly).  The
 //    kernel keeps a whole K-block of KBLK terms of both operand tiles
 //    resident in LDS; at the end of each block every output whose best
 //    improved inside it re-scans its winning chunk for the first term equal
