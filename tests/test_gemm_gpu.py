@@ -100,6 +100,26 @@ def test_layouts(tb, orc, sr, dt, a_col, b_col):
     check(tb, orc, sr, A, B, f"{sr} {dt} a_col={a_col} b_col={b_col}")
 
 
+@pytest.mark.parametrize("sr,dt", PAIRS)
+@pytest.mark.parametrize("n", [1, 5, 16])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_at_most_16_columns(tb, orc, sr, dt, n, b_col):
+    """Products with at most 16 columns: each thread computes one 16-column
+    group (the 64 x 64 tile's other 48 columns would be padding), with B
+    row-major (the fixed-layout form) or column-major (the general one),
+    over more tiles than two per CU, with and without argmax."""
+    A, B = make(sr, dt, 8, 4100, 200, n, seed=n * 7 + b_col, b_col=b_col)
+    check(tb, orc, sr, A, B, f"{sr} {dt} n={n} b_col={b_col}")
+    check(tb, orc, sr, A, B, f"{sr} {dt} n={n} b_col={b_col} value only", argmax=False)
+
+
+def test_at_most_16_columns_many_tiles_per_workgroup(tb, orc, monkeypatch):
+    monkeypatch.setenv("TROPICAL_GEMM_MAX_WORKGROUPS", "8")
+    for sr in ("max_plus", "max_mul"):
+        A, B = make(sr, "f32", 3, 1000, 140, 16, seed=3)
+        check(tb, orc, sr, A, B, f"{sr} n=16, 8 workgroups")
+
+
 @pytest.mark.parametrize("k", [1, 2, 15, 16, 17, 31, 32, 255, 256, 257, 511, 512, 513, 1000])
 def test_k_around_chunk_and_block(tb, orc, k):
     for sr in ("max_plus", "min_plus"):

@@ -405,17 +405,17 @@ struct OpLoad {
 // the bits of the first winning term, recomputed from global memory at the
 // resolved index (with argmax) or found by a scan along k (value only).
 // Rare and only taken by a wave that holds such an output.
-template <int SR, typename T, bool ARG, bool SPLIT, bool KR>
+template <int SR, typename T, bool ARG, bool SPLIT, bool KR, int NC>
 __device__ __forceinline__ void zero_bits_fixup(const TropGemmParams& p, TileCoord ct, int tx,
-                                                          int ty, T (&best)[GEMM_TR][4],
-                                                          const int (&idx)[GEMM_TR][4]) {
+                                                          int ty, T (&best)[GEMM_TR][NC],
+                                                          const int (&idx)[GEMM_TR][NC]) {
     using R = Ring<SR, T>;
     const T* A = static_cast<const T*>(p.A) + ct.b * p.sa_batch +
                  (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.a_krun, p.sa_khi, p.sa_col) : 0);
     const T* B = static_cast<const T*>(p.B) + ct.b * p.sb_batch +
                  (SPLIT ? k_off<KR>(ct.s * p.kchunk, p.b_krun, p.sb_khi, p.sb_row) : 0);
     for (int r = 0; r < GEMM_TR; ++r)
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int64_t i = ct.row0 + ty + GEMM_RS * r, j = ct.col0 + tx + 16 * c;
             if (i >= p.m || j >= p.n || !(best[r][c] == (T)0)) continue;
             const T* a = A + i * p.sa_row;
@@ -673,12 +673,16 @@ __device__ __forceinline__ bool mode_gate_open(const TropGemmParams& p) {
 }
 
 template <int SR, typename T, bool ARG, bool SPLIT, bool NARROW = SPLIT, bool GRES = false, typename TG = T,
-          int LAYOUT_A = LAYOUT_ANY, int LAYOUT_B = LAYOUT_ANY, bool KR = true>
+          int LAYOUT_A = LAYOUT_ANY, int LAYOUT_B = LAYOUT_ANY, bool KR = true, int NC = 4>
 __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     using R = Ring<SR, T>;
     using V = vec4<T>;
     using Cfg = GemmCfg<ARG, T, NARROW, GRES>;
     static_assert(!GRES || ARG, "the global resolve is an argmax form");
+    // NC: 16-column groups a thread computes (4: the 64 x 64 tile; 1: only
+    // the tile's first 16 columns, for products with at most 16 columns --
+    // the rest of the tile would be padding)
+    static_assert(NC == 4 || (NC == 1 && !GRES), "one column group: resident-block and value-only forms");
     constexpr bool FM = !std::is_same<T, TG>::value;  // int32 data computed in float
     constexpr bool BLK = Cfg::BLOCK;  // resident block + LDS re-scan
     constexpr int NSL = Cfg::NSL, LDR = Cfg::LDR, GEMM_SL = Cfg::SL;
@@ -768,14 +772,14 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 
     TileCoord ct = tile_coord<SPLIT>(p, cL, tiles, total);
     int c_nsl = slices_of(ct);  // slices of the tile being computed
-    T best[GEMM_TR][4];
-    int win[GEMM_TR][4];
-    int idx[GEMM_TR][4];
+    T best[GEMM_TR][NC];
+    int win[GEMM_TR][NC];
+    int idx[GEMM_TR][NC];
     auto reset_outputs = [&]() {
 #pragma unroll
         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 best[r][c] = zero_of<SR, T, TG>();
                 win[r][c] = -1;
                 idx[r][c] = 0;
@@ -815,13 +819,13 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             // one of them per slice.
             const int64_t k_left = (SPLIT ? ct.kt : p.k) - (int64_t)g * GEMM_SL;
             const int q_end = k_left >= GEMM_SL ? NQ : (int)((k_left + CH - 1) / CH) * QPC;
-            V fa[2][GEMM_TR], fb[2][4];
+            V fa[2][GEMM_TR], fb[2][NC];
 #pragma unroll
             for (int r = 0; r < GEMM_TR; ++r) fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * c);
-            T cm[GEMM_TR][4];    // argmax: (+) of the current chunk's terms
-            T prev[GEMM_TR][4];  // argmax: the best before the current chunk
+            for (int c = 0; c < NC; ++c) fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * c);
+            T cm[GEMM_TR][NC];    // argmax: (+) of the current chunk's terms
+            T prev[GEMM_TR][NC];  // argmax: the best before the current chunk
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 if (!GRES && q % QPC == 0 && q > 0 && q >= q_end) break;  // uniform over the workgroup
@@ -832,7 +836,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                         for (int r = 0; r < GEMM_TR; ++r)
                             fa[nxt][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * (q + 1));
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
+                        for (int c = 0; c < NC; ++c)
                             fb[nxt][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk +
                                                                      4 * (((q + 1) & ~3) | (((q + 1) & 3) ^ c)));
                     }
@@ -841,13 +845,13 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                     for (int r = 0; r < GEMM_TR; ++r)
                         fa[0][r] = *reinterpret_cast<const V*>(a_row + r * GEMM_RS * LDR + sk + 4 * q);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < NC; ++c)
                         fb[0][c] = *reinterpret_cast<const V*>(b_col + c * 16 * LDR + sk + 4 * ((q & ~3) | ((q & 3) ^ c)));
                 }
 #pragma unroll
                 for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
+                    for (int c = 0; c < NC; ++c) {
                         const V a = fa[cur][r], b = fb[cur][c];
                         if constexpr (ARG && !GEMM_CHAIN_RECORD) {
                             T v = (q % QPC == 0) ? R::add2(R::mul(a.x, b.x), R::mul(a.y, b.y))
@@ -867,7 +871,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                            for (int c = 0; c < 4; ++c) {
+                            for (int c = 0; c < NC; ++c) {
                                 // one compare feeds both selects (a select,
                                 // unlike max, needs no NaN canonicalisation)
                                 if constexpr (GEMM_CHAIN_RECORD) {
@@ -890,10 +894,10 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 // sequence with the 16-byte reads of the next slot issued
                 // before the current slot's scan.  A slot that did not improve
                 // scans chunk 0 and keeps its index.
-                constexpr int NS = GEMM_TR * 4;
+                constexpr int NS = GEMM_TR * NC;
                 V av[2][QPC], bv[2][QPC];
                 auto rs_load = [&](int n, int buf) {
-                    const int r = n / 4, c = n % 4;
+                    const int r = n / NC, c = n % NC;
                     const int w = win[r][c] < 0 ? 0 : win[r][c];
                     const T* ap = a_row + r * GEMM_RS * LDR + w * CH;
                     const T* bp = b_col + c * 16 * LDR;
@@ -907,7 +911,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                 if constexpr (Cfg::PF) rs_load(0, 0);
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
-                    const int r = n / 4, c = n % 4, cur = Cfg::PF ? n & 1 : 0;
+                    const int r = n / NC, c = n % NC, cur = Cfg::PF ? n & 1 : 0;
                     if constexpr (Cfg::PF) {
                         if (n + 1 < NS) rs_load(n + 1, cur ^ 1);
                     } else {
@@ -938,7 +942,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                     for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
+                        for (int c = 0; c < NC; ++c) {
                             const int o = (ty + GEMM_RS * r) * GEMM_RLD + tx + 16 * c;
                             rv[o] = best[r][c];
                             rw[o] = win[r][c];
@@ -950,7 +954,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                     for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
+                        for (int c = 0; c < NC; ++c) {
                             const int o = (ty + GEMM_RS * r) * GEMM_RLD + tx + 16 * c;
                             idx[r][c] = rw[o];
                             best[r][c] = rv[o];  // (reloaded: nothing stays live across the resolve)
@@ -967,16 +971,16 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
 #pragma unroll
                         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                            for (int c = 0; c < 4; ++c)
+                            for (int c = 0; c < NC; ++c)
                                 best[r][c] = best[r][c] == (T)0 ? R::zero() : best[r][c];
                     } else {
                         bool any0 = false;
 #pragma unroll
                         for (int r = 0; r < GEMM_TR; ++r)
 #pragma unroll
-                            for (int c = 0; c < 4; ++c) any0 |= best[r][c] == (T)0;
+                            for (int c = 0; c < NC; ++c) any0 |= best[r][c] == (T)0;
                         if (__any(any0))
-                            zero_bits_fixup<SR, T, ARG, SPLIT, KR>(p, ct, tx, ty, best, idx);
+                            zero_bits_fixup<SR, T, ARG, SPLIT, KR, NC>(p, ct, tx, ty, best, idx);
                     }
                 }
                 const int64_t c_off = ct.b * p.sc_batch + (SPLIT ? ct.s * p.c_split : 0);
@@ -988,7 +992,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
                     const int64_t i = ct.row0 + ty + GEMM_RS * r;
                     if (i >= p.m) continue;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
+                    for (int c = 0; c < NC; ++c) {
                         const int64_t j = ct.col0 + tx + 16 * c;
                         if (j >= p.n) continue;
                         const int64_t o = i * p.sc_row + j * p.sc_col;

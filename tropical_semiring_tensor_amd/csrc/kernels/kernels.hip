@@ -51,6 +51,18 @@ using namespace trop;
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV, true>(p);    \
     }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_w1_##NAME(     \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_ANY, LAYOUT_ANY, true, 1>(p); \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) ARGW void trop_gemm_tiled_km1_##NAME(    \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, true, false, false, false, T, LAYOUT_KV, LAYOUT_MV, true, 1>(p); \
+    }                                                                                           \
+    extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_vo1_##NAME(     \
+        TropGemmParams p) {                                                                     \
+        gemm_tiled_body<SR, T, false, false, false, false, T, LAYOUT_ANY, LAYOUT_ANY, true, 1>(p); \
+    }                                                                                           \
     extern "C" __global__ __launch_bounds__(GEMM_THREADS) void trop_gemm_tiled_split_##NAME(   \
         TropGemmParams p) {                                                                     \
         gemm_tiled_body<SR, T, true, true>(p);                                                  \

@@ -296,13 +296,21 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // has a second instance with it)
     const bool fixed = gres && kvec && fixed_ok && pan32 && !a_two && !b_two;
     const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
-    const KernelId km_id = a_two || b_two ? K_GEMM_TILED_KMR_MAXPLUS_F32 : K_GEMM_TILED_KM_MAXPLUS_F32;
+    // At most 16 columns: the forms whose threads compute one 16-column
+    // group (the tile's other 48 columns would be padding), both with the
+    // two-level k.  TROPICAL_GEMM_NO_NARROW_N=1: the 64-column forms.
+    const bool n16 = n <= 16 && !env_flag("TROPICAL_GEMM_NO_NARROW_N");
+    const KernelId km_id = n16 ? K_GEMM_TILED_KM1_MAXPLUS_F32
+                               : (a_two || b_two ? K_GEMM_TILED_KMR_MAXPLUS_F32 : K_GEMM_TILED_KM_MAXPLUS_F32);
+    const KernelId wide_id = n16 ? K_GEMM_TILED_W1_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32;
+    const KernelId vo_id = n16 ? K_GEMM_TILED_VO1_MAXPLUS_F32
+                               : (a_two || b_two ? K_GEMM_TILED_VOR_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32);
     const KernelId kid =
         split ? (KernelId)((argmax ? K_GEMM_TILED_SPLIT_MAXPLUS_F32 : K_GEMM_TILED_VO_SPLIT_MAXPLUS_F32) + ri)
               : (KernelId)((argmax ? (gres     ? (fixed ? K_GEMM_TILED_GKK_MAXPLUS_F32 : K_GEMM_TILED_G_MAXPLUS_F32)
                                       : narrow ? K_GEMM_TILED_N_MAXPLUS_F32
-                                               : (fixed_km ? km_id : K_GEMM_TILED_MAXPLUS_F32))
-                                   : (a_two || b_two ? K_GEMM_TILED_VOR_MAXPLUS_F32 : K_GEMM_TILED_VO_MAXPLUS_F32)) +
+                                               : (fixed_km ? km_id : wide_id))
+                                   : vo_id) +
                          ri);
     // Persistent grid: as many workgroups as the CUs hold at once (LDS and
     // registers decide), each walking a stream of tiles.  A multiple of 8

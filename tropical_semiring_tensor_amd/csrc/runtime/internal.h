@@ -37,7 +37,12 @@ enum KernelId : int {
     K_GEMM_TILED_KM_MAXPLUS_F32 = K_GEMM_TILED_GKK_MAXPLUS_F32 + NRING,  // wide, A k-vector, B column-vector
     K_GEMM_TILED_KMR_MAXPLUS_F32 = K_GEMM_TILED_KM_MAXPLUS_F32 + NRING,  // the same, with a two-level k
     K_GEMM_TILED_VOR_MAXPLUS_F32 = K_GEMM_TILED_KMR_MAXPLUS_F32 + NRING,  // value only, with a two-level k
-    K_FILL = K_GEMM_TILED_VOR_MAXPLUS_F32 + NRING,
+    // one 16-column group per thread (products with at most 16 columns):
+    // the wide form, its fixed-layout form, the value-only form
+    K_GEMM_TILED_W1_MAXPLUS_F32 = K_GEMM_TILED_VOR_MAXPLUS_F32 + NRING,
+    K_GEMM_TILED_KM1_MAXPLUS_F32 = K_GEMM_TILED_W1_MAXPLUS_F32 + NRING,
+    K_GEMM_TILED_VO1_MAXPLUS_F32 = K_GEMM_TILED_KM1_MAXPLUS_F32 + NRING,
+    K_FILL = K_GEMM_TILED_VO1_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,

@@ -41,7 +41,9 @@ const std::vector<std::string>& kernel_names() {
                                                "trop_gemm_splitk_merge_", "trop_gemm_tiled_n_",
                                                "trop_gemm_tiled_g_",     "trop_gather_reduce_vec_",
                                                "trop_gemm_tiled_gkk_",   "trop_gemm_tiled_km_",
-                                               "trop_gemm_tiled_kmr_",   "trop_gemm_tiled_vor_"};
+                                               "trop_gemm_tiled_kmr_",   "trop_gemm_tiled_vor_",
+                                               "trop_gemm_tiled_w1_",    "trop_gemm_tiled_km1_",
+                                               "trop_gemm_tiled_vo1_"};
         static const char* const singles[] = {
             "trop_fill",                     "trop_gather_copy",
             "trop_gather_tiled",             "trop_gather_naive",
