@@ -171,6 +171,10 @@ def main():
     ap.add_argument("--profile-valu", action="store_true",
                     help="3 launches each of the headline GEMM, of workload 2 (argmax, value only) and of "
                          "a 4096^3 min-plus f32 GEMM on integer data, for VALU issue counters")
+    ap.add_argument("--profile-sweep", action="store_true",
+                    help="each 256 MiB permute / diagonal-gather sweep pattern twice, each after a 1 GiB "
+                         "fill, in a fixed order, then a 256 MiB device copy twice (for kernel traces and "
+                         "counters of the sweep)")
     ap.add_argument("--network-only", action="store_true",
                     help="run only the lattice-network (contraction tree) legs and print their JSON")
     args = ap.parse_args()
@@ -194,6 +198,10 @@ def main():
     if args.profile_configs:
         profile_configs(torch, tb, inputs, dev)
         log("[bench] config probe done")
+        return
+    if args.profile_sweep:
+        profile_sweep(torch, tb, dev)
+        log("[bench] sweep probe done")
         return
 
     # ---------------- headline: workload 4 ----------------
@@ -300,6 +308,46 @@ def main():
         result["workloads"] = other_workloads(torch, tb, inputs, timer, dev, args)
 
     print(json.dumps(result), flush=True)
+
+
+SWEEP_ORDER = ["inner_to_front", "swap_outer_inner", "batched_transpose", "keep_inner", "diagonal_iijb_bij",
+               "diagonal_iij_ij", "trace_iij_j", "device_copy"]
+
+
+def profile_sweep(torch, tb, dev):
+    """The 256 MiB sweep patterns of the full run, each launched twice after
+    a 1 GiB fill, in SWEEP_ORDER, then torch's 256 MiB device copy twice."""
+    flush_buf = torch.empty(256 * 2 ** 20, dtype=torch.float32, device=dev)
+
+    def twice(fn):
+        for _ in range(2):
+            flush_buf.fill_(1.0)
+            fn()
+            torch.cuda.synchronize()
+
+    g = torch.Generator(device="cpu").manual_seed(7)
+    X = torch.randn(256, 2048, 128, generator=g).to(dev)
+    for perm in ((2, 0, 1), (2, 1, 0), (0, 2, 1), (1, 0, 2)):
+        Y = torch.empty([X.shape[p] for p in perm], device=dev)
+        twice(lambda: tb.tropical_permute(X, perm, out=Y))
+        del Y
+    del X
+    torch.cuda.empty_cache()
+    D = torch.empty(64, 64, 2048, 256, device=dev)
+    Y = torch.empty(256, 64, 2048, device=dev)
+    twice(lambda: tb.tropical_diag_gather("max_plus", D, "iijb", "bij", out=Y))
+    del D, Y
+    torch.cuda.empty_cache()
+    D = torch.empty(64, 64, 524288, device=dev)
+    Y = torch.empty(64, 524288, device=dev)
+    Yr = torch.empty(524288, device=dev)
+    twice(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "ij", out=Y))
+    twice(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "j", out=Yr))
+    del D, Y, Yr
+    torch.cuda.empty_cache()
+    src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    twice(lambda: dst.copy_(src))
 
 
 def profile_configs(torch, tb, inputs, dev):
@@ -537,8 +585,27 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
 
     out["network_tree"] = tree_workloads(torch, tb, inputs, timer, dev)
 
-    # supplementary sweep: the workload-5 permute patterns at >= 256 MiB
+    # supplementary sweep: the workload-5 permute patterns at >= 256 MiB.
+    # Each row: one call after a 1 GiB fill that evicts the memory-side
+    # cache (event-timed, so it includes the launch), and three calls back
+    # to back after the fill (per call; a 512 MiB stream does not fit the
+    # 256 MB cache, so each call still reads from HBM).
     sweep = {}
+
+    def sweep_row(name, fn, nbytes):
+        t1 = timer.time(fn, reps=reps, warmup=2, flush=flush)["median_ms"]
+
+        def three():
+            fn()
+            fn()
+            fn()
+        t3 = timer.time(three, reps=reps, warmup=0, flush=flush)["median_ms"] / 3
+        g1, g3 = nbytes / (t1 * 1e-3) / 1e9, nbytes / (t3 * 1e-3) / 1e9
+        sweep[name] = {"MiB_moved": nbytes // 2 ** 20, "cold_GBs": round(g1, 1),
+                       "frac_hbm": round(g1 / HBM_PEAK_GBS, 4), "stream_GBs": round(g3, 1),
+                       "frac_hbm_stream": round(g3 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] sweep {name}: {g1:.0f} GB/s one call, {g3:.0f} GB/s three in a row")
+
     g = torch.Generator(device="cpu").manual_seed(7)
     X = torch.randn(256, 2048, 128, generator=g).to(dev)  # 256 MiB
     cases = {"inner_to_front_(k,j,b)->(b,k,j)": (2, 0, 1),
@@ -546,20 +613,13 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
              "keep_inner_(a,b,c)->(b,a,c)": (1, 0, 2)}
     for name, perm in cases.items():
         Y = torch.empty([X.shape[p] for p in perm], device=dev)
-        t = timer.time(lambda: tb.tropical_permute(X, perm, out=Y), reps=reps, warmup=2, flush=flush)
-        gbs = 2 * 4 * X.numel() / (t["median_ms"] * 1e-3) / 1e9
-        sweep[name] = {"MiB_moved": 2 * 4 * X.numel() // 2 ** 20, "cold_GBs": round(gbs, 1),
-                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"[bench] sweep {name}: {gbs:.0f} GB/s")
+        sweep_row(name, lambda: tb.tropical_permute(X, perm, out=Y), 2 * 4 * X.numel())
         del Y
     # the same bytes as 8-byte elements (float64): moved as word pairs
     X64 = X.view(torch.float64)
     Y = torch.empty(256, 64, 2048, dtype=torch.float64, device=dev)
-    t = timer.time(lambda: tb.tropical_permute(X64, (0, 2, 1), out=Y), reps=reps, warmup=2, flush=flush)
-    gbs = 2 * 8 * X64.numel() / (t["median_ms"] * 1e-3) / 1e9
-    sweep["batched_transpose_f64_(b,i,k)->(b,k,i)"] = {"MiB_moved": 2 * 8 * X64.numel() // 2 ** 20,
-                                                        "cold_GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    log(f"[bench] sweep f64 batched transpose: {gbs:.0f} GB/s")
+    sweep_row("batched_transpose_f64_(b,i,k)->(b,k,i)", lambda: tb.tropical_permute(X64, (0, 2, 1), out=Y),
+              2 * 8 * X64.numel())
     del Y, X64, X
     torch.cuda.empty_cache()
     # repeated-label gathers at the same scale: the tensor is allocated whole
@@ -567,30 +627,17 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     # diagonal elements read plus the elements written.
     D = torch.empty(64, 64, 2048, 256, device=dev)      # workload 5's iijb, scaled
     Y = torch.empty(256, 64, 2048, device=dev)
-    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iijb", "bij", out=Y), reps=reps, warmup=2,
-                   flush=flush)
-    gbs = 2 * 4 * Y.numel() / (t["median_ms"] * 1e-3) / 1e9
-    sweep["diagonal_(i,i,j,b)->(b,i,j)"] = {"MiB_moved": 2 * 4 * Y.numel() // 2 ** 20, "cold_GBs": round(gbs, 1),
-                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    log(f"[bench] sweep diagonal iijb->bij: {gbs:.0f} GB/s")
+    sweep_row("diagonal_(i,i,j,b)->(b,i,j)", lambda: tb.tropical_diag_gather("max_plus", D, "iijb", "bij", out=Y),
+              2 * 4 * Y.numel())
     del D, Y
     torch.cuda.empty_cache()
     D = torch.empty(64, 64, 524288, device=dev)
     Y = torch.empty(64, 524288, device=dev)
-    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "ij", out=Y), reps=reps, warmup=2,
-                   flush=flush)
-    gbs = 2 * 4 * Y.numel() / (t["median_ms"] * 1e-3) / 1e9
-    sweep["diagonal_(i,i,j)->(i,j)"] = {"MiB_moved": 2 * 4 * Y.numel() // 2 ** 20, "cold_GBs": round(gbs, 1),
-                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    log(f"[bench] sweep diagonal iij->ij: {gbs:.0f} GB/s")
+    sweep_row("diagonal_(i,i,j)->(i,j)", lambda: tb.tropical_diag_gather("max_plus", D, "iij", "ij", out=Y),
+              2 * 4 * Y.numel())
     Yr = torch.empty(524288, device=dev)
-    t = timer.time(lambda: tb.tropical_diag_gather("max_plus", D, "iij", "j", out=Yr), reps=reps, warmup=2,
-                   flush=flush)
-    nbytes = 4 * (Y.numel() + Yr.numel())
-    gbs = nbytes / (t["median_ms"] * 1e-3) / 1e9
-    sweep["trace_max_(i,i,j)->(j)"] = {"MiB_moved": nbytes // 2 ** 20, "cold_GBs": round(gbs, 1),
-                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    log(f"[bench] sweep trace iij->j: {gbs:.0f} GB/s")
+    sweep_row("trace_max_(i,i,j)->(j)", lambda: tb.tropical_diag_gather("max_plus", D, "iij", "j", out=Yr),
+              4 * (Y.numel() + Yr.numel()))
     del D, Y, Yr
     torch.cuda.empty_cache()
     out["permute_sweep_256MiB"] = sweep
