@@ -412,7 +412,9 @@ def gpu_gemm_ws(tb, sr, A, B, argmax=True, workspace=None):
 
 
 SPLIT_SHAPES = [(1, 64, 8192, 64), (1, 17, 5000, 33), (3, 70, 3000, 50), (1, 1, 20000, 1),
-                (2, 64, 4096, 130), (1, 5, 1024, 3), (1, 3, 700, 2), (1, 64, 65536, 64)]
+                (2, 64, 4096, 130), (1, 5, 1024, 3), (1, 3, 700, 2), (1, 64, 65536, 64),
+                # tiny products: ranges of 64 terms (K = 256 on one tile; a ragged last range)
+                (1, 1, 256, 1), (1, 16, 256, 16), (2, 100, 300, 70)]
 
 
 @pytest.mark.parametrize("sr,dt", PAIRS)
@@ -469,9 +471,12 @@ def test_split_k_workspace_rules(tb, orc):
     need = tb.tropical_gemm_workspace_size(64, 64, 8192, 1)
     assert need > 0
     # large grids and short K do not split (a large grid gets room for the
-    # domain flags of the int32 float mode instead)
+    # domain flags of the int32 float mode instead); a tiny product splits
+    # into ranges of 64 terms, the others into whole 256-term blocks
     assert tb.tropical_gemm_workspace_size(256, 256, 4096, 64) == 4 * 256
-    assert tb.tropical_gemm_workspace_size(64, 64, 500, 1) == 0
+    assert tb.tropical_gemm_workspace_size(64, 64, 100, 1) == 0
+    assert tb.tropical_gemm_workspace_size(64, 64, 500, 1) == 2 * 4 * 64 * 64 * 4  # 4 ranges of 128
+    assert tb.tropical_gemm_workspace_size(64, 64, 65536, 1) == 2 * 4 * 64 * 64 * 256  # 256 ranges of 256
     Ad, Bd = A.to(DEV), B.to(DEV)
     C = torch.empty(1, 64, 64, device=DEV)
     with pytest.raises(tb.TropicalError) as e:
@@ -646,7 +651,9 @@ def gpu_gemm_fm(tb, sr, A, B, argmax=True):
 @pytest.mark.parametrize("argmax", [True, False])
 def test_int32_float_mode(tb, orc, monkeypatch, sr, outside, argmax):
     monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "1")  # at any size
-    # (K below 512: no split-K, whose partials would take the workspace)
+    # (no split-K, whose partials would take the workspace: these products
+    # are small enough for ranges of 64 terms otherwise)
+    monkeypatch.setenv("TROPICAL_SPLITK_TINY", "0")
     for shape, in_b, b_col in (((2, 130, 480, 90), False, False), ((1, 70, 500, 130), True, True),
                                ((3, 65, 17, 63), False, True)):
         v = None if outside is None else FM_OUTSIDE[sr][outside % len(FM_OUTSIDE[sr])]
@@ -663,7 +670,9 @@ def test_int32_float_mode(tb, orc, monkeypatch, sr, outside, argmax):
 
 def test_int32_float_mode_off_and_sizes(tb, orc, monkeypatch):
     # never taken with the knob at 0 (no workspace asked for small products
-    # either); taken for large ones without the knob
+    # either, split-K ranges of 64 terms off); taken for large ones without
+    # the knob
+    monkeypatch.setenv("TROPICAL_SPLITK_TINY", "0")
     monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "0")
     assert tb.tropical_gemm_workspace_size(130, 90, 480, 2) == 0
     A, B = fm_case("min_plus", 2, 130, 480, 90, seed=5)
@@ -689,6 +698,7 @@ def test_workload3_full_float_mode(tb, orc):
 
 def test_int32_float_mode_in_contractions(tb, orc, monkeypatch):
     monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", "1")
+    monkeypatch.setenv("TROPICAL_SPLITK_TINY", "0")  # (else these split into 64-term ranges)
     for sr, outside in (("min_plus", None), ("max_plus", None), ("min_plus", -1), ("max_plus", 2 ** 23)):
         A, B = fm_case(sr, 3, 70, 300, 50, seed=61, outside=outside)
         for spec in ("bij,bjk->bik", "bij,bjk->kbi"):

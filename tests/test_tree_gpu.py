@@ -141,7 +141,8 @@ def test_tree_stays_on_device(tb, monkeypatch):
            for s in range(len(net["steps"]))]
     torch.cuda.synchronize()
     desc = tb.tropical_tree_describe(plan)
-    gathers = desc.count("gather:") + desc.count("permute:")
+    # (a step split along K adds its merge launch)
+    gathers = desc.count("gather:") + desc.count("permute:") + desc.count("splitK")
     tb.tropical_reset_stats()
     tb.tropical_tree_run(plan, xs, out=out, argmax=ams, workspace=ws)
     st = tb.tropical_get_stats()

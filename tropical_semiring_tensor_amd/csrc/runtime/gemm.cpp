@@ -71,10 +71,17 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
 // Split-K policy: split only a product with fewer output tiles (times
 // batch) than a 256-CU device has CUs, and only when every range keeps at
 // least kSplitMinK terms (one resident K-block); aim at about kSplitTarget
-// (tile, range) units.
+// (tile, range) units.  A tiny product -- fewer than kSplitTinyUnits
+// (tile, 256-term block) pairs, i.e. busy on a quarter of the CUs at most
+// -- takes ranges of kSplitTinyK terms instead: a single 64 x 64 tile with
+// K = 256 runs its four slices one after another on one CU, and as four
+// ranges on four CUs plus the merge it finished in about two thirds of the
+// time.
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
+constexpr int64_t kSplitTinyUnits = 64;
+constexpr int64_t kSplitTinyK = 64;  // one slice of the split kernels
 // Products with a longer K take the global-resolve argmax kernel
 // (TROPICAL_GEMM_GRES_MIN_K overrides, for measurements).
 const int64_t kGresMinK = [] {
@@ -108,14 +115,22 @@ bool fm_size_ok(int64_t m, int64_t n, int64_t k, int64_t batch) {
 
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     SplitK s;
-    if (m <= 0 || n <= 0 || batch <= 0 || k < 2 * kSplitMinK) return s;
-    const int64_t units = ((m + 63) / 64) * ((n + 63) / 64) * batch;
+    if (m <= 0 || n <= 0 || batch <= 0 || k <= 0) return s;
+    int64_t units = 0;
+    if (__builtin_mul_overflow((m + 63) / 64, (n + 63) / 64, &units) ||
+        __builtin_mul_overflow(units, batch, &units))
+        return s;
     if (units * 2 > kSplitTarget) return s;
+    const int64_t blocks = k / 256 > 1 ? k / 256 : 1;
+    const bool tiny = units * blocks < kSplitTinyUnits && !env_flag_off("TROPICAL_SPLITK_TINY");
+    const int64_t min_k = tiny ? kSplitTinyK : kSplitMinK;
+    const int64_t align = tiny ? kSplitTinyK : kSplitAlign;
+    if (k < 2 * min_k) return s;
     int64_t want = (kSplitTarget + units - 1) / units;
-    if (want > k / kSplitMinK) want = k / kSplitMinK;
+    if (want > k / min_k) want = k / min_k;
     if (want < 2) return s;
     int64_t chunk = (k + want - 1) / want;
-    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    chunk = (chunk + align - 1) / align * align;
     const int64_t ks = (k + chunk - 1) / chunk;
     if (ks < 2) return s;
     s.ksplit = ks;
