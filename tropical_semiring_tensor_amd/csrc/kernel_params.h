@@ -80,8 +80,7 @@ struct TropDomainParams {
 
 // Merge of split-K partials: out = the first strictly better of the
 // ksplit partials (split 0 first), stored [split][batch][m][n] contiguous.
-// Lanes of the split-K merge per output (a power of two up to 64; the grid
-// has one thread per lane).
+// Most lanes of the split-K merge per output (a power of two up to 64).
 #define TROP_MERGE_LANES 16
 
 struct TropSplitMergeParams {
@@ -91,6 +90,9 @@ struct TropSplitMergeParams {
     int32_t* argmax;      // may be null
     int64_t sc_row, sc_col, sc_batch;
     int64_t m, n, batch, ksplit;
+    // lanes per output: a power of two from 1 to TROP_MERGE_LANES (the grid
+    // has one thread per lane and output)
+    int32_t lanes, pad_;
 };
 
 struct TropFillParams {

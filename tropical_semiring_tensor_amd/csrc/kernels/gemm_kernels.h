@@ -43,12 +43,13 @@ __device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
 // bits of its first winning term, and the smallest winning k (a range that
 // only ties an earlier one loses).
 //
-// MERGE_G consecutive lanes share one output: lane c scans its own run of
+// G consecutive lanes share one output (G = p.lanes, a power of two up to
+// MERGE_G, about one lane per MERGE_U ranges): lane c scans its own run of
 // consecutive ranges in order (the first taken as is, then only strictly
 // better ones), and the lanes then combine pairwise, the better value
 // winning and, on equal values, the earlier range.  That is the same first
-// strict winner over all ranges, found with MERGE_G x MERGE_U loads in flight
-// per output.
+// strict winner over all ranges, found with G x MERGE_U loads in flight per
+// output.
 constexpr int MERGE_G = TROP_MERGE_LANES;
 constexpr int MERGE_U = 8;  // ranges per lane whose loads are in flight together
 
@@ -58,14 +59,17 @@ __device__ __forceinline__ void splitk_merge_body(const TropSplitMergeParams& p)
     const int64_t mn = p.m * p.n;
     const int64_t total = mn * p.batch;
     const T* pv = static_cast<const T*>(p.pval);
+    // (value only: the index loads read the values, in bounds, and are not used)
+    const int32_t* pi = p.pidx ? p.pidx : reinterpret_cast<const int32_t*>(pv);
     const int32_t nr = (int32_t)p.ksplit;
-    const int32_t per = (nr + MERGE_G - 1) / MERGE_G;  // ranges per lane
-    // (total * MERGE_G is a multiple of MERGE_G, so the lanes of one output
-    // are active or inactive together)
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total * MERGE_G;
+    const int32_t G = p.lanes, gsh = __builtin_ctz((uint32_t)G);
+    const int32_t per = (nr + G - 1) / G;  // ranges per lane
+    // (total * G is a multiple of G, so the lanes of one output are active
+    // or inactive together)
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total * G;
          t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t o = t / MERGE_G;
-        const int32_t c = (int32_t)(t % MERGE_G);
+        const int64_t o = t >> gsh;
+        const int32_t c = (int32_t)(t & (G - 1));
         const int32_t r0 = c * per, r1 = r0 + per < nr ? r0 + per : nr;
         T best = R::zero();
         int32_t arg = 0;
@@ -80,7 +84,7 @@ __device__ __forceinline__ void splitk_merge_body(const TropSplitMergeParams& p)
             for (int u = 0; u < MERGE_U; ++u) {
                 const int64_t off = (int64_t)(ra + u < r1 ? ra + u : r0) * total + o;
                 v[u] = pv[off];
-                a[u] = p.pidx ? p.pidx[off] : 0;
+                a[u] = pi[off];
             }
 #pragma unroll
             for (int u = 0; u < MERGE_U; ++u) {
@@ -91,8 +95,7 @@ __device__ __forceinline__ void splitk_merge_body(const TropSplitMergeParams& p)
                 rb = take ? r : rb;
             }
         }
-#pragma unroll
-        for (int m = 1; m < MERGE_G; m <<= 1) {
+        for (int m = 1; m < G; m <<= 1) {  // (uniform)
             const T ov = __shfl_xor(best, m);
             const int32_t oa = __shfl_xor(arg, m);
             const int32_t orb = __shfl_xor(rb, m);

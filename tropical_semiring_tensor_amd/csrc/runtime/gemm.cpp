@@ -71,12 +71,12 @@ trop_status check_gemm_args(trop_semiring sr, trop_dtype dt, trop_strides sA, tr
 // Split-K policy: split only a product with fewer output tiles (times
 // batch) than a 256-CU device has CUs, and only when every range keeps at
 // least kSplitMinK terms (one resident K-block); aim at about kSplitTarget
-// (tile, range) units.  A tiny product -- fewer than kSplitTinyUnits
-// (tile, 256-term block) pairs, i.e. busy on a quarter of the CUs at most
-// -- takes ranges of kSplitTinyK terms instead: a single 64 x 64 tile with
-// K = 256 runs its four slices one after another on one CU, and as four
-// ranges on four CUs plus the merge it finished in about two thirds of the
-// time.
+// (tile, range) units.  A tiny product -- at most kSplitTinyUnits (tile,
+// 256-term block) pairs, i.e. busy on a quarter of the CUs at most -- takes
+// ranges of kSplitTinyK terms instead: a single 64 x 64 tile with K = 256
+// runs its four slices one after another on one CU, and as four ranges on
+// four CUs plus the merge it finished in about two thirds of the time.
+// (128 and more pairs measured slower split that way.)
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
@@ -122,7 +122,7 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
         return s;
     if (units * 2 > kSplitTarget) return s;
     const int64_t blocks = k / 256 > 1 ? k / 256 : 1;
-    const bool tiny = units * blocks < kSplitTinyUnits && !env_flag_off("TROPICAL_SPLITK_TINY");
+    const bool tiny = units * blocks <= kSplitTinyUnits && !env_flag_off("TROPICAL_SPLITK_TINY");
     const int64_t min_k = tiny ? kSplitTinyK : kSplitMinK;
     const int64_t align = tiny ? kSplitTinyK : kSplitAlign;
     if (k < 2 * min_k) return s;
@@ -398,8 +398,11 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     mp.n = n;
     mp.batch = batch;
     mp.ksplit = sk.ksplit;
+    // about one lane per 8 ranges (each lane keeps 8 loads in flight)
+    mp.lanes = 1;
+    while (mp.lanes < TROP_MERGE_LANES && mp.lanes * 8 < sk.ksplit) mp.lanes *= 2;
     return launch(dev, (KernelId)(K_GEMM_SPLITK_MERGE_MAXPLUS_F32 + ri), TROP_K_GEMM_SPLITK_MERGE,
-                  grid_for(m * n * batch * TROP_MERGE_LANES, 256), 256, &mp, stream);
+                  grid_for(m * n * batch * mp.lanes, 256), 256, &mp, stream);
 }
 
 }  // namespace trop
