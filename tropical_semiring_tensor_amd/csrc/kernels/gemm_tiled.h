@@ -187,7 +187,9 @@ __device__ __forceinline__ int64_t k_off(int64_t k, int32_t krun, int64_t khi, i
     return k * sk;
 }
 
-template <bool SPLIT>
+// BN: the columns of a tile (64; 16 for the forms whose threads compute one
+// 16-column group)
+template <bool SPLIT, int BN = GEMM_BN>
 __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t L, int64_t tiles,
                                                 int64_t total) {
     if (p.coord32) {
@@ -218,7 +220,7 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
             tr = mdiv(t, tn, p.tn_m, p.tn_s);
             tc = t - tr * tn;
         }
-        TileCoord c{bs, 0, (int64_t)tr * GEMM_BM, (int64_t)tc * GEMM_BN, p.k};
+        TileCoord c{bs, 0, (int64_t)tr * GEMM_BM, (int64_t)tc * BN, p.k};
         if constexpr (SPLIT) {
             const uint32_t ks = (uint32_t)p.ksplit;
             const uint32_t b = mdiv(bs, ks, p.ks_m, p.ks_s);
@@ -245,7 +247,7 @@ __device__ __forceinline__ TileCoord tile_coord(const TropGemmParams& p, int64_t
         tr = t / p.tiles_n;
         tc = t % p.tiles_n;
     }
-    TileCoord c{bs, 0, tr * GEMM_BM, tc * GEMM_BN, p.k};
+    TileCoord c{bs, 0, tr * GEMM_BM, tc * BN, p.k};
     if constexpr (SPLIT) {
         c.b = bs / p.ksplit;
         c.s = bs % p.ksplit;
@@ -742,7 +744,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     // Fetch cursor: the (tile, slice) whose data was last requested.
     int64_t fL = cL;
     int fg = 0;
-    point(tile_coord<SPLIT>(p, fL, tiles, total));
+    point(tile_coord<SPLIT, 16 * NC>(p, fL, tiles, total));
     bool fetch_valid = true;
     T ra[NV][4], rb[NV][4];
     auto fetch_next = [&]() {
@@ -751,7 +753,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             fg = 0;
             fL += gstride;
             fetch_valid = fL < total;
-            if (fetch_valid) point(tile_coord<SPLIT>(p, fL, tiles, total));
+            if (fetch_valid) point(tile_coord<SPLIT, 16 * NC>(p, fL, tiles, total));
         }
         if (fetch_valid) {
             la.load(fg, R::zero(), ra);
@@ -770,7 +772,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
     }
     __syncthreads();
 
-    TileCoord ct = tile_coord<SPLIT>(p, cL, tiles, total);
+    TileCoord ct = tile_coord<SPLIT, 16 * NC>(p, cL, tiles, total);
     int c_nsl = slices_of(ct);  // slices of the tile being computed
     T best[GEMM_TR][NC];
     int win[GEMM_TR][NC];
@@ -1009,7 +1011,7 @@ __device__ __forceinline__ void gemm_tiled_body(const TropGemmParams& p) {
             fetch_next();
             if (last) {
                 cL += gstride;
-                ct = tile_coord<SPLIT>(p, cL, tiles, total);
+                ct = tile_coord<SPLIT, 16 * NC>(p, cL, tiles, total);
                 c_nsl = slices_of(ct);
                 reset_outputs();
                 g = -1;

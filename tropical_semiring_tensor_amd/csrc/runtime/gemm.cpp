@@ -82,6 +82,7 @@ constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
 constexpr int64_t kSplitTinyUnits = 64;
 constexpr int64_t kSplitTinyK = 64;  // one slice of the split kernels
+constexpr int64_t kTiny16Tiles = 64;  // products of at most this many tiles take 16-column tiles
 // Products with a longer K take the global-resolve argmax kernel
 // (TROPICAL_GEMM_GRES_MIN_K overrides, for measurements).
 const int64_t kGresMinK = [] {
@@ -291,6 +292,31 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         }
         if (std::strcmp(f, "global") == 0) gres = argmax;
     }
+    // One 16-column group per thread, in tiles of 64 rows x 16 columns:
+    // products with at most 16 columns (a 64-column tile would be three
+    // quarters padding), and tiny products (at most kTiny16Tiles 64 x 64
+    // tiles), which then spread over four times the workgroups.  The wide
+    // forms only: not with split K, the global resolve or a forced narrow
+    // setting.  TROPICAL_GEMM_NO_NARROW_N=1: the 64-column forms.
+    // Float mode of an int32 product (its kernels have 64-column tiles); the
+    // domain pre-pass reads plain strides: not with a two-level k.
+    const bool fm = dt == TROP_I32 && sr != TROP_MAX_MUL && !split && workspace && workspace_bytes >= kFmBytes &&
+                    !a_two && !b_two && fm_size_ok(m, n, k, batch);
+    const char* setting = std::getenv("TROPICAL_GEMM_SETTING");
+    const bool forced_narrow = setting && std::strcmp(setting, "narrow") == 0;
+    const bool n16 = !split && !gres && !fm && !forced_narrow && !env_flag("TROPICAL_GEMM_NO_NARROW_N") &&
+                     (n <= 16 || (tm * tn * batch <= kTiny16Tiles && !env_flag_off("TROPICAL_GEMM_TINY16")));
+    if (n16) {
+        narrow = false;
+        const int64_t tn16 = (n + 15) / 16;
+        p.tiles_n = (int32_t)tn16;
+        total = tm * tn16 * batch * p.ksplit;
+        if (p.coord32) {
+            if (tm * tn16 >= 2) magic_u31((uint64_t)(tm * tn16), &p.tl_m, &p.tl_s);
+            if (tn16 >= 2) magic_u31((uint64_t)tn16, &p.tn_m, &p.tn_s);
+            magic_u31((uint64_t)(p.group_rows * tn16), &p.gr_m, &p.gr_s);
+        }
+    }
     // the global-resolve instance with both operands' loads fixed at
     // compile time (16-byte vectors along k) where the layout is that one
     // (TROPICAL_GEMM_FIXED_LAYOUT=0: always the general instance)
@@ -311,10 +337,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // has a second instance with it)
     const bool fixed = gres && kvec && fixed_ok && pan32 && !a_two && !b_two;
     const bool fixed_km = !gres && !narrow && kmvec && fixed_ok;
-    // At most 16 columns: the forms whose threads compute one 16-column
-    // group (the tile's other 48 columns would be padding), both with the
-    // two-level k.  TROPICAL_GEMM_NO_NARROW_N=1: the 64-column forms.
-    const bool n16 = n <= 16 && !env_flag("TROPICAL_GEMM_NO_NARROW_N");
+    // (the 16-column forms have the two-level k)
     const KernelId km_id = n16 ? K_GEMM_TILED_KM1_MAXPLUS_F32
                                : (a_two || b_two ? K_GEMM_TILED_KMR_MAXPLUS_F32 : K_GEMM_TILED_KM_MAXPLUS_F32);
     const KernelId wide_id = n16 ? K_GEMM_TILED_W1_MAXPLUS_F32 : K_GEMM_TILED_MAXPLUS_F32;
@@ -350,9 +373,6 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // pre-pass writes its flags into the workspace, then the float-mode
     // kernel and the int32 kernel are both enqueued, each gated on the flags
     // so that exactly one of them computes.  No host round trip.
-    // (the domain pre-pass reads plain strides: not with a two-level k)
-    const bool fm = dt == TROP_I32 && sr != TROP_MAX_MUL && !split && workspace && workspace_bytes >= kFmBytes &&
-                    !a_two && !b_two && fm_size_ok(m, n, k, batch);
     if (fm) {
         TropDomainParams d{};
         d.A = static_cast<const int32_t*>(A);
