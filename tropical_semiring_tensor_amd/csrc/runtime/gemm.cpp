@@ -82,7 +82,10 @@ constexpr int64_t kSplitMinK = 256;
 constexpr int64_t kSplitAlign = 256;  // ranges are whole resident K-blocks
 constexpr int64_t kSplitTinyUnits = 64;
 constexpr int64_t kSplitTinyK = 64;  // one slice of the split kernels
-constexpr int64_t kTiny16Tiles = 64;  // products of at most this many tiles take 16-column tiles
+// Products of at most this many 64 x 64 tiles take 64 x 16 tiles (with 256
+// tiles, a 64 x 16 grid of 1024 measured slower: 23 -> 35 us on 32 x 256 x
+// 128 x 256; with 128, faster: 21.3 -> 18.5 us on 8 x 256^3)
+constexpr int64_t kTiny16Tiles = 128;
 // Products with a longer K take the global-resolve argmax kernel
 // (TROPICAL_GEMM_GRES_MIN_K overrides, for measurements).
 const int64_t kGresMinK = [] {
@@ -294,7 +297,7 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     }
     // One 16-column group per thread, in tiles of 64 rows x 16 columns:
     // products with at most 16 columns (a 64-column tile would be three
-    // quarters padding), and tiny products (at most kTiny16Tiles 64 x 64
+    // quarters padding), and small products (at most kTiny16Tiles 64 x 64
     // tiles), which then spread over four times the workgroups.  The wide
     // forms only: not with split K, the global resolve or a forced narrow
     // setting.  TROPICAL_GEMM_NO_NARROW_N=1: the 64-column forms.
