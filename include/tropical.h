@@ -170,7 +170,8 @@ TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t 
 /*
  * tropical_gemm_strided_batched with a workspace, which lets a product with
  * few output tiles and a long K run on the whole device: K is cut into
- * `ksplit` ranges of whole 256-term blocks, each (tile, range) pair is one
+ * `ksplit` ranges (of whole 256-term blocks; of 64 terms for a product of
+ * at most 64 (tile, 256-term block) pairs), each (tile, range) pair is one
  * unit of the tiled kernel writing a partial value and global argmax into
  * the workspace, and a merge kernel keeps, per output, the first partial
  * (in range order) that is strictly better than those before it.  Every
@@ -178,8 +179,10 @@ TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t 
  * their bits and the smallest winning k -- are those of the unsplit call
  * (the tie rule of [PR35]'s argmax survives the split).  The split is used
  * when the product has fewer 64 x 64 output tiles (times batch) than the
- * device has CUs and K >= 512; tropical_gemm_workspace_size reports the
- * bytes (0: no split, and the call equals tropical_gemm_strided_batched).
+ * device has CUs and K >= 512 (K >= 128 for those small products), and the
+ * int32 float mode takes 1 KiB of it for a large unsplit product;
+ * tropical_gemm_workspace_size reports the bytes (0: neither, and the call
+ * equals tropical_gemm_strided_batched).
  * workspace: NULL with workspace_bytes 0 (never split), or device memory of
  *   at least that size, used only by work on `stream`.
  * Errors: as tropical_gemm_strided_batched, plus
