@@ -161,7 +161,8 @@ TROP_API trop_status tropical_gemm_strided_batched(trop_semiring semiring, trop_
 
 /*
  * Workspace (bytes) with which tropical_gemm_strided_batched_ws splits a
- * product of this shape along K; 0 when it would not split it.  Host-only.
+ * product of this shape along K (or, unsplit and large, gives an int32
+ * max-plus / min-plus product its float mode); 0 when neither.  Host-only.
  * Errors: TROP_ERR_INVALID_ARGUMENT (negative size, NULL bytes).
  */
 TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t batch,
