@@ -129,6 +129,29 @@ def test_diag_argument_errors(tb):
                                     nul) == tb.UNSUPPORTED
 
 
+def test_gemm_workspace_policy(tb, monkeypatch):
+    """Split-K and float-mode workspace sizes (host only).  Partials are two
+    arrays (values, argmax) of ranges x batch x m x n words, each rounded up
+    to 256 bytes."""
+    def parts(ranges, b, m, n):
+        one = -(-(ranges * b * m * n * 4) // 256) * 256
+        return 2 * one
+    ws = tb.tropical_gemm_workspace_size
+    # a large grid: no split, room for the int32 float mode's 256 flags
+    assert ws(256, 256, 4096, 64) == 4 * 256
+    # one tile, K = 65536: 256 ranges of 256 (not tiny: 256 (tile, block) pairs)
+    assert ws(64, 64, 65536, 1) == parts(256, 1, 64, 64)
+    # tiny products (at most 64 (tile, 256-term block) pairs): ranges of 64 terms
+    assert ws(64, 64, 500, 1) == parts(4, 1, 64, 64)  # 4 ranges of 128 (ceil(500/7) -> 128)
+    assert ws(1, 1, 256, 1) == parts(4, 1, 1, 1)
+    assert ws(4096, 16, 256, 1) == parts(4, 1, 4096, 16)  # 64 tiles
+    assert ws(64, 64, 100, 1) == 0  # K < 128
+    assert ws(4096, 64, 256, 2) == 0  # 128 tiles: neither tiny nor few enough to split
+    monkeypatch.setenv("TROPICAL_SPLITK_TINY", "0")
+    assert ws(64, 64, 500, 1) == 0 and ws(1, 1, 256, 1) == 0
+    assert ws(64, 64, 65536, 1) == parts(256, 1, 64, 64)
+
+
 def test_contract_plan_config5(tb):
     d = tb.tropical_contract_pair_describe("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
     assert "batch=b left=i right=k contracted=j" in d
