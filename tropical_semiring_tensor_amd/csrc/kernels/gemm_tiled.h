@@ -32,7 +32,10 @@
 //
 // Tiling: 256 threads (4 waves) or 512 (8 waves), a 64x64 output tile per
 // workgroup, 16 or 8 outputs per thread at rows ty + RS r and columns
-// tx + 16 c (tx = tid % 16, ty = tid / 16, RS = threads / 16).  K is staged through LDS in slices of SL terms;
+// tx + 16 c (tx = tid % 16, ty = tid / 16, RS = threads / 16).  The forms
+// with one 16-column group per thread (NC = 1: products with at most 16
+// columns, small products) take 64 x 16 tiles, c = 0 only.  K is staged
+// through LDS in slices of SL terms;
 // the slice after next is fetched into registers while the current one
 // computes and the next one is written to LDS at its start, so one barrier
 // per slice suffices (one more at the end of each resident block).
