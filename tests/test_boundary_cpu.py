@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tropical.h")
@@ -150,6 +151,40 @@ def test_gemm_workspace_policy(tb, monkeypatch):
     monkeypatch.setenv("TROPICAL_SPLITK_TINY", "0")
     assert ws(64, 64, 500, 1) == 0 and ws(1, 1, 256, 1) == 0
     assert ws(64, 64, 65536, 1) == parts(256, 1, 64, 64)
+
+
+def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
+    """The strided size query (host only): room for a transposed copy of a
+    row-major B (1 KiB in, batch x k x n words rounded up to 256 bytes) for
+    an argmax product with K >= 512 and a multiple of 4, A read along k, at
+    least 256 rows and 2^30 terms, not split; else the plain size (the
+    knob at 1: K > 256 at any size)."""
+    def t(*shape, col=False):
+        x = torch.empty(*shape, device="meta")
+        return x.transpose(1, 2).contiguous().transpose(1, 2) if col else x
+
+    def copy(b, k, n):
+        return 1024 + -(-(b * k * n * 4) // 256) * 256
+    ws = tb.tropical_gemm_workspace_size_strided
+    assert ws(t(1, 4096, 4096), t(1, 4096, 4096)) == copy(1, 4096, 4096)
+    assert ws(t(16, 2048, 2048), t(16, 2048, 2048)) == copy(16, 2048, 2048)
+    # no copy: column-major B, column-major A, no argmax, K <= 256 or not a
+    # multiple of 4, fewer than 256 rows or 2^30 terms, a split product
+    assert ws(t(16, 2048, 2048), t(16, 2048, 2048, col=True)) == tb.tropical_gemm_workspace_size(2048, 2048, 2048, 16)
+    assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096)) == tb.tropical_gemm_workspace_size(4096, 4096, 4096, 1)
+    assert ws(t(1, 4096, 4096), t(1, 4096, 4096), with_argmax=False) == 4 * 256
+    assert ws(t(64, 256, 256), t(64, 256, 256)) == 0
+    assert ws(t(1, 4096, 4094), t(1, 4094, 4096)) == 4 * 256
+    assert ws(t(64, 128, 1024), t(64, 1024, 2048)) == 4 * 256  # 128 rows: the float-mode flags only
+    assert ws(t(1, 256, 512), t(1, 512, 4160)) == 0  # 260 tiles, 2^29 terms
+    assert ws(t(1, 4096, 300), t(1, 300, 4096)) == 4 * 256  # K = 300
+    assert ws(t(1, 64, 65536), t(1, 65536, 64)) == tb.tropical_gemm_workspace_size(64, 64, 65536, 1)
+    # the knob: 1 at any size (not split), 0 never
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    assert ws(t(43, 130, 260), t(43, 260, 90)) == copy(43, 260, 90)
+    assert ws(t(1, 64, 65536), t(1, 65536, 64)) == tb.tropical_gemm_workspace_size(64, 64, 65536, 1)
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "0")
+    assert ws(t(1, 4096, 4096), t(1, 4096, 4096)) == 4 * 256
 
 
 def test_contract_plan_config5(tb):

@@ -637,7 +637,7 @@ def gpu_gemm_fm(tb, sr, A, B, argmax=True):
     Ad, Bd = device_copy(A), device_copy(B)
     b, m, k = A.shape
     n = B.shape[2]
-    ws = torch.zeros(max(4, tb.tropical_gemm_workspace_size(m, n, k, b)), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(4, tb.tropical_gemm_workspace_size_strided(Ad, Bd, argmax)), dtype=torch.uint8, device=DEV)
     C = torch.empty(b, m, n, dtype=torch.int32, device=DEV)
     I = torch.empty(b, m, n, dtype=torch.int32, device=DEV) if argmax else None
     tb.tropical_gemm_strided_batched_ws(sr, Ad, Bd, C, I, workspace=ws)

@@ -74,6 +74,8 @@ def lib():
     L.tropical_gemm_strided_batched_ws.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp,
                                                    trop_strides, vp, i64, i64, i64, i64, vp, sz, vp]
     L.tropical_gemm_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
+    L.tropical_gemm_workspace_size_strided.argtypes = [trop_strides, trop_strides, i32, i64, i64, i64, i64,
+                                                       ctypes.POINTER(sz)]
     L.tropical_gemm_backward.argtypes = [i32, i32, vp, trop_strides, vp, trop_strides, vp, vp,
                                          trop_strides, vp, trop_strides, vp, trop_strides,
                                          i64, i64, i64, i64, vp]
@@ -102,6 +104,7 @@ def lib():
     L.tropical_reset_stats.restype = None
     for fn in ("tropical_init", "tropical_gemm_strided_batched", "tropical_gemm_backward", "tropical_permute",
                "tropical_gemm_strided_batched_ws", "tropical_gemm_workspace_size",
+               "tropical_gemm_workspace_size_strided",
                "tropical_diag_gather", "tropical_contract_pair_workspace_size",
                "tropical_contract_pair", "tropical_contract_pair_describe", "tropical_get_stats",
                "tropical_contract_pair_noalloc",
@@ -212,10 +215,25 @@ def tropical_gemm_workspace_size(m, n, k, batch=1):
     return nb.value
 
 
+def tropical_gemm_workspace_size_strided(A, B, with_argmax=True):
+    """Workspace bytes for tropical_gemm_strided_batched_ws with the shapes
+    and strides of the (batch, m, k) and (batch, k, n) tensors A and B."""
+    A3, B3 = _as3(A), _as3(B)
+    batch, m, k = A3.shape
+    n = B3.shape[2]
+    sA = trop_strides(A3.stride(1), A3.stride(2), A3.stride(0))
+    sB = trop_strides(B3.stride(1), B3.stride(2), B3.stride(0))
+    nb = ctypes.c_size_t(0)
+    _check(lib().tropical_gemm_workspace_size_strided(sA, sB, 1 if with_argmax else 0, m, n, k, batch,
+                                                      ctypes.byref(nb)), "tropical_gemm_workspace_size_strided")
+    return nb.value
+
+
 def tropical_gemm_strided_batched_ws(semiring, A, B, C, argmax=None, workspace=None, stream=None):
     """tropical_gemm_strided_batched with a workspace (split along K when
-    the product has few output tiles and a long K).  workspace: None to
-    allocate tropical_gemm_workspace_size bytes with torch, or a uint8
+    the product has few output tiles and a long K; a transposed copy of a
+    row-major B for a long-K argmax product).  workspace: None to allocate
+    tropical_gemm_workspace_size_strided bytes with torch, or a uint8
     device tensor."""
     A3, B3, C3 = _as3(A), _as3(B), _as3(C)
     batch, m, k = A3.shape
@@ -223,7 +241,7 @@ def tropical_gemm_strided_batched_ws(semiring, A, B, C, argmax=None, workspace=N
     if argmax is not None and _as3(argmax).stride() != C3.stride():
         raise ValueError("argmax must have the strides of C")
     if workspace is None:
-        nb = tropical_gemm_workspace_size(m, n, k, batch)
+        nb = tropical_gemm_workspace_size_strided(A3, B3, argmax is not None)
         workspace = torch.empty(nb, dtype=torch.uint8, device=A3.device) if nb else None
     sA = trop_strides(A3.stride(1), A3.stride(2), A3.stride(0))
     sB = trop_strides(B3.stride(1), B3.stride(2), B3.stride(0))

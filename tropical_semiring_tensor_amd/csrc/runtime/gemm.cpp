@@ -117,6 +117,28 @@ bool fm_size_ok(int64_t m, int64_t n, int64_t k, int64_t batch) {
     return t >= kFmMinTerms;
 }
 
+// Transposed copy of B: an argmax product with a long K whose B is
+// row-major (j unit-stride) and whose A is read along k in 16-byte quads
+// copies B into the workspace as (batch, n, k), k unit-stride, so that the
+// global-resolve kernel reads both operands in quads along k.  The copy
+// moves 8 bytes per element of B, each of which the product then reads
+// m / 64 times: taken for at least kBtMinRows rows, kBtMinTerms terms and
+// K >= kBtMinK (4096^3 min-plus f32: 3.45 -> 2.88 ms; 2048^3 max-plus:
+// 472 -> 388 us; 4096 x 300 x 4096: 306 -> 310 us, not taken).  The copy
+// sits after the float-mode flags.  TROPICAL_GEMM_B_TRANSPOSE=0 never
+// takes it, =1 at any size with K > kGresMinK.
+constexpr size_t kBtOffset = 1024;
+static_assert(kFmBytes <= kBtOffset, "the float-mode flags overlap the copy of B");
+constexpr int64_t kBtMinRows = 256;
+constexpr int64_t kBtMinTerms = int64_t(1) << 30;
+constexpr int64_t kBtMinK = 512;
+
+int bt_knob() {
+    const char* v = std::getenv("TROPICAL_GEMM_B_TRANSPOSE");
+    if (!v || !*v) return -1;
+    return v[0] == '0' ? 0 : 1;
+}
+
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     SplitK s;
     if (m <= 0 || n <= 0 || batch <= 0 || k <= 0) return s;
@@ -142,6 +164,24 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     const size_t part = (size_t)(ks * batch * m * n) * 4;
     s.bytes = 2 * ((part + 255) / 256 * 256);
     return s;
+}
+
+// Workspace bytes with which run_gemm copies B transposed for these
+// operand strides (0: not for this layout or shape).  The pointers' 16-byte
+// alignment is checked at the call.
+size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch) {
+    const int knob = bt_knob();
+    if (knob == 0 || !argmax || m <= 0 || n <= 0 || batch <= 0 || k <= kGresMinK || k % 4 != 0) return 0;
+    if (sA.col != 1 || sA.row % 4 != 0 || sA.batch % 4 != 0 || sB.col != 1) return 0;
+    if (plan_splitk(m, n, k, batch).bytes > 0) return 0;
+    int64_t e = 0;
+    if (__builtin_mul_overflow(batch, k, &e) || __builtin_mul_overflow(e, n, &e) || e > (INT64_MAX >> 3)) return 0;
+    if (knob < 0) {
+        int64_t t = 0;
+        const bool many = __builtin_mul_overflow(e, m, &t) || t >= kBtMinTerms;
+        if (m < kBtMinRows || k < kBtMinK || !many) return 0;
+    }
+    return kBtOffset + (size_t)((e * 4 + 255) / 256 * 256);
 }
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch) {
@@ -238,6 +278,32 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         p.b_mode = TROP_LOAD_K_CONTIG;
         p.b_vec = 0;
     }
+    // transposed copy of B in the workspace (see kBtOffset): B is then
+    // read along k in 16-byte quads, by the global-resolve kernel (not under
+    // a forced wide or narrow setting)
+    const char* setting = std::getenv("TROPICAL_GEMM_SETTING");
+    const bool setting_local = setting && (std::strcmp(setting, "wide") == 0 || std::strcmp(setting, "narrow") == 0);
+    const size_t bt_need = workspace && !a_two && !b_two && !setting_local && p.a_mode == TROP_LOAD_K_CONTIG &&
+                                   p.a_vec && p.b_mode == TROP_LOAD_MN_CONTIG
+                               ? bt_bytes(sA, sB, argmax != nullptr, m, n, k, batch)
+                               : 0;
+    if (bt_need > 0 && workspace_bytes >= bt_need && aligned16(workspace)) {
+        void* Bt = static_cast<char*>(workspace) + kBtOffset;
+        const int64_t oshape[3] = {batch, n, k}, ostride[3] = {sB.batch, sB.col, sB.row};
+        GatherPlan g{};
+        trop_status st = plan_gather(3, oshape, ostride, 0, nullptr, nullptr, &g);
+        if (st != TROP_OK) return st;
+        const void* gin[1] = {B};
+        void* gout[1] = {Bt};
+        st = run_gather(dev, g, 1, gin, gout, sr, dt, stream);
+        if (st != TROP_OK) return st;
+        p.B = Bt;
+        p.sb_row = 1;
+        p.sb_col = k;
+        p.sb_batch = k * n;
+        p.b_mode = TROP_LOAD_K_CONTIG;
+        p.b_vec = 1;  // (k % 4 == 0, the copy 256-byte aligned)
+    }
     const int64_t tm = (m + 63) / 64, tn = (n + 63) / 64;
     if (tm > INT32_MAX || tn > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "matrix too large");
     p.tiles_m = (int32_t)tm;
@@ -305,7 +371,6 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
     // domain pre-pass reads plain strides: not with a two-level k.
     const bool fm = dt == TROP_I32 && sr != TROP_MAX_MUL && !split && workspace && workspace_bytes >= kFmBytes &&
                     !a_two && !b_two && fm_size_ok(m, n, k, batch);
-    const char* setting = std::getenv("TROPICAL_GEMM_SETTING");
     const bool forced_narrow = setting && std::strcmp(setting, "narrow") == 0;
     const bool n16 = !split && !gres && !fm && !forced_narrow && !env_flag("TROPICAL_GEMM_NO_NARROW_N") &&
                      (n <= 16 || (tm * tn * batch <= kTiny16Tiles && !env_flag_off("TROPICAL_GEMM_TINY16")));
@@ -443,9 +508,11 @@ trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, 
     if (workspace && sk.bytes > 0 && workspace_bytes < sk.bytes)
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(sk.bytes) + " bytes, got " + std::to_string(workspace_bytes));
-    // (the float mode of int32 products uses a workspace when one of its
-    // size is given, and is skipped otherwise)
-    const size_t ws_need = gemm_workspace_bytes(m, n, k, batch);
+    // (the float mode of int32 products and the transposed copy of B use a
+    // workspace when one of their size is given, and are skipped otherwise)
+    const size_t ws_base = gemm_workspace_bytes(m, n, k, batch);
+    const size_t ws_bt = workspace ? bt_bytes(sA, sB, argmax != nullptr, m, n, k, batch) : 0;
+    const size_t ws_need = ws_bt > ws_base && workspace_bytes >= ws_bt ? ws_bt : ws_base;
     int dev = -1;
     st = current_device(&dev);
     if (st != TROP_OK) return st;
@@ -508,5 +575,17 @@ extern "C" trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_
     if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
     *bytes = gemm_workspace_bytes(m, n, k, batch);
+    return ok();
+}
+
+extern "C" trop_status tropical_gemm_workspace_size_strided(trop_strides sA, trop_strides sB, int with_argmax,
+                                                            int64_t m, int64_t n, int64_t k, int64_t batch,
+                                                            size_t* bytes) {
+    using namespace trop;
+    if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
+    const size_t base = gemm_workspace_bytes(m, n, k, batch);
+    const size_t bt = bt_bytes(sA, sB, with_argmax != 0, m, n, k, batch);
+    *bytes = bt > base ? bt : base;
     return ok();
 }

@@ -192,6 +192,9 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch);
 // max-plus / min-plus when it is large enough to take it (any dtype: the
 // sizing calls know no dtype), else 0.  Host-only.
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
+// Workspace bytes with which run_gemm copies a row-major B transposed (an
+// argmax product with a long K and A read along k; 0: not taken)
+size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch);
 // Two-level k of the GEMM's operands (TropGemmParams a_krun / sa_khi):
 // a_run > 0 reads A's k as k = hi a_run + lo, lo at unit stride (sA.col = 1)
 // and hi at stride a_hi; a_run is 4, 8 or 16.  Likewise b_run / b_hi with
