@@ -353,8 +353,8 @@ def profile_sweep(torch, tb, dev):
 def profile_configs(torch, tb, inputs, dev):
     """One 256 MiB device copy (calibrates the traffic counters), then three
     launches of each workload's kernels in workload order: GEMMs 1-4 with
-    argmax (workload 3 through the workspace call: domain pre-pass and float
-    mode), workload 5's einsum (diagonal gather, B permute, GEMM) plus its
+    argmax (workload 3 through the workspace call: domain pre-pass,
+    transposed copy of B and float mode), workload 5's einsum (diagonal gather, B permute, GEMM) plus its
     paired output permute run on its own, and workload 2's backward (both
     gradients)."""
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
