@@ -25,6 +25,7 @@ CASES = [
     ("min_plus", "i32", 43, 130, 260, 90),
     ("max_plus", "f32", 11, 260, 1028, 300),
     ("min_plus", "i32", 11, 260, 1028, 300),
+    ("max_mul", "i32", 43, 130, 260, 90),
 ]
 
 
@@ -43,6 +44,8 @@ def operands(sr, dt, b, m, k, n, seed):
         if sr == "min_plus":
             A, B = A.abs(), B.abs()
             B[torch.rand(B.shape, generator=g) < 0.2] = 1 << 30
+        if sr == "max_mul":
+            A, B = A.abs(), B.abs()
         return A, B
     if sr == "max_mul":
         return (torch.randint(1, 9, (b, m, k), generator=g).float() * 0.125,
@@ -128,3 +131,20 @@ def test_no_copy_without_argmax_or_with_the_knob_off(tb, orc, monkeypatch):
     assert not ws.any()
     assert_bits_equal(C.cpu().numpy(), Cr, "knob 0")
 
+
+
+def test_transposed_copy_of_a_broadcast_b(tb, orc, monkeypatch):
+    """B shared by every batch entry (batch stride 0): the copy holds one
+    transposed B per entry, and the results match the oracle."""
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    b, m, k, n = 43, 130, 260, 90
+    A, B = operands("max_plus", "f32", b, m, k, n, seed=5)
+    B1 = B[:1].contiguous()
+    Ad, Bd = A.to(DEV), B1.to(DEV).expand(b, k, n)
+    assert Bd.stride(0) == 0
+    ws = torch.zeros(tb.tropical_gemm_workspace_size_strided(Ad, Bd), dtype=torch.uint8, device=DEV)
+    C, I = run(tb, "max_plus", Ad, Bd, ws)
+    assert torch.equal(copy_of_b(ws, b, k, n), B1.expand(b, k, n).view(torch.int32).transpose(1, 2))
+    Cr, Ir = orc.gemm("max_plus", A.numpy(), B1.expand(b, k, n).contiguous().numpy())
+    assert_bits_equal(C.cpu().numpy(), Cr, "broadcast B C")
+    assert_equal(I.cpu().numpy(), Ir, "broadcast B argmax")
