@@ -187,6 +187,20 @@ def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
     assert ws(t(1, 4096, 4096), t(1, 4096, 4096)) == 4 * 256
 
 
+def test_contract_plan_gathers_b_along_k_for_long_k(tb, monkeypatch):
+    """A long-K contraction whose right operand would be read with its free
+    index at unit stride gathers it with k at unit stride (the workspace
+    holds the copy); one already read along k stays in place."""
+    d = tb.tropical_contract_pair_describe("ij,jk->ik", (2048, 2048), (2048, 2048))
+    assert "A=fold B=gather:tiled:kcol" in d and "workspace=16778240" in d, d
+    assert "B=fold" in tb.tropical_contract_pair_describe("ij,kj->ik", (2048, 2048), (2048, 2048))
+    # split along K (few tiles), K <= 256, or the knob at 0: in place
+    assert "B=fold" in tb.tropical_contract_pair_describe("ij,jk->ik", (1024, 1024), (1024, 1024))
+    assert "B=fold" in tb.tropical_contract_pair_describe("bij,bjk->bik", (64, 256, 256), (64, 256, 256))
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "0")
+    assert "B=fold" in tb.tropical_contract_pair_describe("ij,jk->ik", (2048, 2048), (2048, 2048))
+
+
 def test_contract_plan_config5(tb):
     d = tb.tropical_contract_pair_describe("iijb,kjb->bki", (128, 128, 256, 32), (256, 256, 32))
     assert "batch=b left=i right=k contracted=j" in d

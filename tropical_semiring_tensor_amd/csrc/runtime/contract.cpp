@@ -302,10 +302,17 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
     }
     P.b_fold = try_fold(P, Rt, r_red, P.batch, P.contracted, cols, &P.sB) ||
                try_fold_two(P, Rt, r_red, P.batch, cols, P.contracted, false, &P.sB, &P.kr.b_run, &P.kr.b_hi);
+    // A long K with A read along k: B is read along k too (from a copy in
+    // (batch, cols, contracted) order where it would otherwise be read with
+    // j at unit stride), so that the GEMM takes its global-resolve form
+    const bool a_along_k = !P.a_fold || (P.kr.a_run == 0 && P.sA.col == 1 && P.sA.row % 4 == 0 && P.sA.batch % 4 == 0);
+    const bool b_kcol = a_along_k && kcol_b_pays(P.gm, P.gn, P.K, P.nb);
+    if (P.b_fold && b_kcol && P.kr.b_run == 0 && P.sB.row != 1) P.b_fold = false;
+    P.b_kcol = !P.b_fold && b_kcol;
     if (!P.b_fold) {
-        st = plan_operand(P, Rt, canR, &P.gb);
+        st = plan_operand(P, Rt, b_kcol ? P.batch + cols + P.contracted : canR, &P.gb);
         if (st != TROP_OK) return st;
-        P.sB = {P.gn, 1, P.K * P.gn};
+        P.sB = b_kcol ? trop_strides{1, P.K, P.K * P.gn} : trop_strides{P.gn, 1, P.K * P.gn};
     }
     P.c_direct = (canC == P.lo);
     if (!P.c_direct) {
@@ -379,8 +386,10 @@ std::string pair_describe(const Plan& P) {
         if (!fold) return std::string("gather:") + gather_path_name(g.path);
         return run > 0 ? "fold:krun" + std::to_string(run) : std::string("fold");
     };
-    const std::string ha = P.swap ? how(P.b_fold, P.kr.b_run, P.gb) : how(P.a_fold, P.kr.a_run, P.ga);
-    const std::string hb = P.swap ? how(P.a_fold, P.kr.a_run, P.ga) : how(P.b_fold, P.kr.b_run, P.gb);
+    // (":kcol": the GEMM's right operand gathered with k at unit stride)
+    const std::string hr = how(P.b_fold, P.kr.b_run, P.gb) + (P.b_kcol ? ":kcol" : "");
+    const std::string ha = P.swap ? hr : how(P.a_fold, P.kr.a_run, P.ga);
+    const std::string hb = P.swap ? how(P.a_fold, P.kr.a_run, P.ga) : hr;
     char buf[640];
     std::snprintf(buf, sizeof(buf),
                   "batch=%s left=%s right=%s contracted=%s reduceA=%s reduceB=%s; gemm %s batch=%lld m=%lld "
@@ -450,9 +459,10 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
         cp.idx = i_gemm;
         const int32_t* wl = P.red_l ? reinterpret_cast<const int32_t*>(ws + P.off_wl) : nullptr;
         const int32_t* wr = P.red_r ? reinterpret_cast<const int32_t*>(ws + P.off_wr) : nullptr;
-        // left operand [nb][gm][K], right operand [nb][K][gn]
+        // left operand [nb][gm][K], right operand [nb][K][gn] (or
+        // [nb][gn][K] when gathered along k)
         const int64_t l_str[4] = {P.gm * P.K, P.K, 0, 1};
-        const int64_t r_str[4] = {P.K * P.gn, 0, 1, P.gn};
+        const int64_t r_str[4] = {P.K * P.gn, 0, P.b_kcol ? P.K : 1, P.b_kcol ? 1 : P.gn};
         const int32_t* wa = P.swap ? wr : wl;
         const int32_t* wb = P.swap ? wl : wr;
         const int64_t* sa = P.swap ? r_str : l_str;

@@ -28,6 +28,7 @@ struct PairPlan {
     int64_t out_total = 1;
     int64_t span_a = 0, span_b = 0;  // elements of A / B reached (0: empty operand)
     bool a_fold = false, b_fold = false, c_direct = false;
+    bool b_kcol = false;  // the GEMM's right operand gathered in (batch, cols, contracted) order
     // swap: the GEMM's left operand is B and its right operand is A, so that
     // the product comes out as (batch, right, left), the output order
     bool swap = false;

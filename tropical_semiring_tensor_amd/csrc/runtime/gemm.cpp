@@ -166,21 +166,25 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     return s;
 }
 
+bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch) {
+    const int knob = bt_knob();
+    if (knob == 0 || m <= 0 || n <= 0 || batch <= 0 || k <= kGresMinK || k % 4 != 0) return false;
+    if (plan_splitk(m, n, k, batch).bytes > 0) return false;
+    if (knob > 0) return true;
+    int64_t t = 0;
+    const bool many = __builtin_mul_overflow(m, n, &t) || __builtin_mul_overflow(t, k, &t) ||
+                      __builtin_mul_overflow(t, batch, &t) || t >= kBtMinTerms;
+    return m >= kBtMinRows && k >= kBtMinK && many;
+}
+
 // Workspace bytes with which run_gemm copies B transposed for these
 // operand strides (0: not for this layout or shape).  The pointers' 16-byte
 // alignment is checked at the call.
 size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch) {
-    const int knob = bt_knob();
-    if (knob == 0 || !argmax || m <= 0 || n <= 0 || batch <= 0 || k <= kGresMinK || k % 4 != 0) return 0;
-    if (sA.col != 1 || sA.row % 4 != 0 || sA.batch % 4 != 0 || sB.col != 1) return 0;
-    if (plan_splitk(m, n, k, batch).bytes > 0) return 0;
+    if (!argmax || sA.col != 1 || sA.row % 4 != 0 || sA.batch % 4 != 0 || sB.col != 1) return 0;
+    if (!kcol_b_pays(m, n, k, batch)) return 0;
     int64_t e = 0;
     if (__builtin_mul_overflow(batch, k, &e) || __builtin_mul_overflow(e, n, &e) || e > (INT64_MAX >> 3)) return 0;
-    if (knob < 0) {
-        int64_t t = 0;
-        const bool many = __builtin_mul_overflow(e, m, &t) || t >= kBtMinTerms;
-        if (m < kBtMinRows || k < kBtMinK || !many) return 0;
-    }
     return kBtOffset + (size_t)((e * 4 + 255) / 256 * 256);
 }
 

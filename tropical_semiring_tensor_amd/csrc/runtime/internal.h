@@ -192,6 +192,13 @@ SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch);
 // max-plus / min-plus when it is large enough to take it (any dtype: the
 // sizing calls know no dtype), else 0.  Host-only.
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
+// Does a long-K product of this shape gain from reading B along k (k unit
+// stride) when A is read along k?  The global-resolve argmax kernel then
+// reads both operands in 16-byte quads along k (the value-only kernel is no
+// slower).  At least 256 rows, 2^30 terms and K >= 512, K a multiple of 4,
+// not split along K (TROPICAL_GEMM_B_TRANSPOSE=0: never, =1: any unsplit
+// product with K > 256).
+bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch);
 // Workspace bytes with which run_gemm copies a row-major B transposed (an
 // argmax product with a long K and A read along k; 0: not taken)
 size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch);
