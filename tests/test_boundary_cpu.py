@@ -188,17 +188,22 @@ def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
 
 
 def test_contract_plan_gathers_b_along_k_for_long_k(tb, monkeypatch):
-    """A long-K contraction whose right operand would be read with its free
-    index at unit stride gathers it with k at unit stride (the workspace
-    holds the copy); one already read along k stays in place."""
+    """A long-K contraction whose operands would be read with their free
+    index at unit stride gathers them with k at unit stride (the workspace
+    holds the copies); one already read along k stays in place."""
     d = tb.tropical_contract_pair_describe("ij,jk->ik", (2048, 2048), (2048, 2048))
     assert "A=fold B=gather:tiled:kcol" in d and "workspace=16778240" in d, d
     assert "B=fold" in tb.tropical_contract_pair_describe("ij,kj->ik", (2048, 2048), (2048, 2048))
+    # a left operand read with its free index at unit stride is gathered along k too
+    d = tb.tropical_contract_pair_describe("ji,jk->ik", (2048, 2048), (2048, 2048))
+    assert "A=gather:tiled B=gather:tiled:kcol" in d, d
+    assert "A=gather:tiled B=fold" in tb.tropical_contract_pair_describe("ji,kj->ik", (2048, 2048), (2048, 2048))
     # split along K (few tiles), K <= 256, or the knob at 0: in place
     assert "B=fold" in tb.tropical_contract_pair_describe("ij,jk->ik", (1024, 1024), (1024, 1024))
     assert "B=fold" in tb.tropical_contract_pair_describe("bij,bjk->bik", (64, 256, 256), (64, 256, 256))
     monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "0")
     assert "B=fold" in tb.tropical_contract_pair_describe("ij,jk->ik", (2048, 2048), (2048, 2048))
+    assert "A=fold B=fold" in tb.tropical_contract_pair_describe("ji,jk->ik", (2048, 2048), (2048, 2048))
 
 
 def test_contract_plan_config5(tb):

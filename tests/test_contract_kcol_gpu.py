@@ -1,7 +1,8 @@
-"""Contractions with a long K: the GEMM's right operand is gathered with k
-at unit stride (":kcol" in the plan) where it would otherwise be read with
-its free index at unit stride, so that the product reads both operands
-along k.  Each case is compared bit for bit with the oracle's decomposed
+"""Contractions with a long K: the GEMM reads both operands along k.  An
+operand that would be read with its free index at unit stride is gathered
+with k at unit stride instead (the left one in (batch, rows, contracted)
+order, the right one in (batch, cols, contracted) order, ":kcol" in the
+plan).  Each case is compared bit for bit with the oracle's decomposed
 pipeline, values and argmax, including an argmax routed through a pre-pass
 reduction of the gathered operand (its winners then lie in the gathered
 order) and a product taken as B (x) A.  Small integer entries make ties
@@ -13,14 +14,17 @@ from gpu_util import DEV, assert_bits_equal, assert_equal
 
 pytestmark = pytest.mark.gpu
 
-# (spec, shape A, shape B, operand gathered along k): more than 256 output
-# tiles (never split along K), K = 260 or 264
+# (spec, shape A, shape B, what the plan reads): more than 256 output tiles
+# (never split along K), K = 260 or 264
 CASES = [
-    ("ij,jk->ik", (1100, 260), (260, 1000), "B"),
-    ("bij,bjk->bik", (3, 700, 264), (3, 264, 650), "B"),
-    ("ij,jkl->ik", (1100, 260), (260, 1000, 3), "B"),      # B's l reduced: winners routed
-    ("ji,kj->ki", (260, 1100), (1000, 260), "A"),          # taken as B (x) A
-    ("jil,kj->ki", (260, 1100, 2), (1000, 260), "A"),      # ... with A's l reduced
+    ("ij,jk->ik", (1100, 260), (260, 1000), "A=fold B=gather:tiled:kcol"),
+    ("bij,bjk->bik", (3, 700, 264), (3, 264, 650), "A=fold B=gather:flat:kcol"),
+    ("ij,jkl->ik", (1100, 260), (260, 1000, 3), "A=fold B=gather:reduce:kcol"),  # B's l reduced: winners routed
+    ("ji,kj->ki", (260, 1100), (1000, 260), "A=gather:tiled:kcol B=fold"),  # taken as B (x) A
+    ("jil,kj->ki", (260, 1100, 2), (1000, 260), "A=gather:reduce:kcol B=fold"),  # ... with A's l reduced
+    ("ji,kj->ik", (260, 1100), (1000, 260), "A=gather:tiled B=fold"),  # A gathered along k
+    ("ji,jk->ik", (260, 1100), (260, 1000), "A=gather:tiled B=gather:tiled:kcol"),  # both
+    ("bjil,bjk->bik", (2, 264, 700, 2), (2, 264, 650), "A=gather:reduce B=gather:flat:kcol"),  # A reduced
 ]
 
 
@@ -42,10 +46,10 @@ def operands(sr, sa, sb, seed):
 @pytest.mark.parametrize("sr", ["max_plus", "min_plus", "max_mul"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_right_operand_gathered_along_k(tb, orc, monkeypatch, sr, case):
-    spec, sa, sb, side = case
+    spec, sa, sb, how = case
     monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")  # at any size
     desc = tb.tropical_contract_pair_describe(spec, sa, sb)
-    assert f"{side}=gather:" in desc and ":kcol" in desc, desc
+    assert how in desc, desc
     A, B = operands(sr, sa, sb, seed=sum(sa) + sum(sb))
     for argmax in (True, False):
         C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV), argmax=argmax)
@@ -67,3 +71,17 @@ def test_same_bits_as_the_row_major_read(tb, orc, monkeypatch):
     C2, I2 = tb.tropical_contract_pair(spec, "max_plus", Ad, Bd)
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int32), C2.view(torch.int32)) and torch.equal(I1, I2)
+
+
+def test_allocation_free_call_gathers_along_k_too(tb, monkeypatch):
+    """The allocation-free call runs the same plan from its own scratch."""
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    for spec, sa, sb in (("ji,jk->ik", (260, 1100), (260, 1000)), ("ij,jk->ik", (1100, 264), (264, 1000))):
+        A, B = operands("max_plus", sa, sb, seed=11)
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        Cw, Iw = tb.tropical_contract_pair(spec, "max_plus", Ad, Bd)
+        C = torch.full(Cw.shape, -7.0, device=DEV)
+        I = torch.full(Cw.shape, -7, dtype=torch.int32, device=DEV)
+        tb.tropical_contract_pair_noalloc(spec, "max_plus", Ad, Bd, C, I)
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int32), Cw.view(torch.int32)) and torch.equal(I, Iw), spec

@@ -295,6 +295,13 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
 
     P.a_fold = try_fold(P, L, l_red, P.batch, rows, P.contracted, &P.sA) ||
                try_fold_two(P, L, l_red, P.batch, rows, P.contracted, true, &P.sA, &P.kr.a_run, &P.kr.a_hi);
+    // A long K (the size rule of kcol_b_pays): the GEMM reads both operands
+    // along k in its global-resolve form, so a left operand that would be
+    // read with its free index at unit stride is gathered in (batch, rows,
+    // contracted) order, and the right one likewise below
+    const bool long_k = kcol_b_pays(P.gm, P.gn, P.K, P.nb);
+    if (P.a_fold && long_k && P.kr.a_run == 0 && !(P.sA.col == 1 && P.sA.row % 4 == 0 && P.sA.batch % 4 == 0))
+        P.a_fold = false;
     if (!P.a_fold) {
         st = plan_operand(P, L, canL, &P.ga);
         if (st != TROP_OK) return st;
@@ -302,11 +309,10 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
     }
     P.b_fold = try_fold(P, Rt, r_red, P.batch, P.contracted, cols, &P.sB) ||
                try_fold_two(P, Rt, r_red, P.batch, cols, P.contracted, false, &P.sB, &P.kr.b_run, &P.kr.b_hi);
-    // A long K with A read along k: B is read along k too (from a copy in
-    // (batch, cols, contracted) order where it would otherwise be read with
-    // j at unit stride), so that the GEMM takes its global-resolve form
-    const bool a_along_k = !P.a_fold || (P.kr.a_run == 0 && P.sA.col == 1 && P.sA.row % 4 == 0 && P.sA.batch % 4 == 0);
-    const bool b_kcol = a_along_k && kcol_b_pays(P.gm, P.gn, P.K, P.nb);
+    // the right operand: read along k from a copy in (batch, cols,
+    // contracted) order where it would otherwise be read with its free
+    // index at unit stride (the left one is read along k by now)
+    const bool b_kcol = long_k;
     if (P.b_fold && b_kcol && P.kr.b_run == 0 && P.sB.row != 1) P.b_fold = false;
     P.b_kcol = !P.b_fold && b_kcol;
     if (!P.b_fold) {
