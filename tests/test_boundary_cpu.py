@@ -154,11 +154,12 @@ def test_gemm_workspace_policy(tb, monkeypatch):
 
 
 def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
-    """The strided size query (host only): room for a transposed copy of a
-    row-major B (1 KiB in, batch x k x n words rounded up to 256 bytes) for
-    an argmax product with K >= 512 and a multiple of 4, A read along k, at
-    least 256 rows and 2^30 terms, not split; else the plain size (the
-    knob at 1: K > 256 at any size)."""
+    """The strided size query (host only): room for transposed copies of a
+    row-major B (1 KiB in, batch x k x n words rounded up to 256 bytes) and
+    of a column-major A (after it, batch x m x k words) for an argmax
+    product with K >= 512 and a multiple of 4, at least 256 rows and 2^30
+    terms, not split; else the plain size (the knob at 1: K > 256 at any
+    size)."""
     def t(*shape, col=False):
         x = torch.empty(*shape, device="meta")
         return x.transpose(1, 2).contiguous().transpose(1, 2) if col else x
@@ -171,7 +172,10 @@ def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
     # no copy: column-major B, column-major A, no argmax, K <= 256 or not a
     # multiple of 4, fewer than 256 rows or 2^30 terms, a split product
     assert ws(t(16, 2048, 2048), t(16, 2048, 2048, col=True)) == tb.tropical_gemm_workspace_size(2048, 2048, 2048, 16)
-    assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096)) == tb.tropical_gemm_workspace_size(4096, 4096, 4096, 1)
+    # a column-major A is copied too (after B's copy), also beside a column-major B
+    assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096)) == copy(1, 4096, 4096) + 4096 * 4096 * 4
+    assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096, col=True)) == copy(1, 4096, 4096)
+    assert ws(t(2, 1000, 2048, col=True), t(2, 2048, 600, col=True)) == copy(2, 2048, 1000)
     assert ws(t(1, 4096, 4096), t(1, 4096, 4096), with_argmax=False) == 4 * 256
     assert ws(t(64, 256, 256), t(64, 256, 256)) == 0
     assert ws(t(1, 4096, 4094), t(1, 4094, 4096)) == 4 * 256

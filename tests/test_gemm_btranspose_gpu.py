@@ -1,6 +1,7 @@
-"""A row-major B copied transposed into the workspace: an argmax product
-with K > 256 (a multiple of 4) and A read along k then reads both operands
-along k, as for a column-major B.  Each case is compared bit for bit with
+"""Operands copied transposed into the workspace: an argmax product with
+K > 256 (a multiple of 4) copies a row-major B (when A is read along k) and
+a column-major A, and then reads both operands along k, as for a row-major
+A and a column-major B.  Each case is compared bit for bit with
 the oracle, and the copy is checked to hold B with k as its unit-stride
 axis (so the path under test ran); a workspace of the split / float-mode
 size gets no copy and the same bits.  Small integer entries make ties
@@ -148,3 +149,30 @@ def test_transposed_copy_of_a_broadcast_b(tb, orc, monkeypatch):
     Cr, Ir = orc.gemm("max_plus", A.numpy(), B1.expand(b, k, n).contiguous().numpy())
     assert_bits_equal(C.cpu().numpy(), Cr, "broadcast B C")
     assert_equal(I.cpu().numpy(), Ir, "broadcast B argmax")
+
+
+@pytest.mark.parametrize("b_col", [False, True], ids=["rowB", "colB"])
+@pytest.mark.parametrize("sr,dt", [("max_plus", "f32"), ("min_plus", "i32"), ("max_mul", "f32")])
+def test_transposed_copy_of_a_column_major_a(tb, orc, monkeypatch, sr, dt, b_col):
+    """A column-major A (i unit-stride) is copied as (batch, m, k) after B's
+    copy (when B is row-major, it is copied too): both then read along k."""
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    b, m, k, n = 43, 130, 264, 90
+    A, B = operands(sr, dt, b, m, k, n, seed=21 + b_col)
+    Ad = A.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    Bd = B.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) if b_col else B.to(DEV)
+    a_off = BT_OFF if b_col else copy_bytes(b, k, n)
+    nb = tb.tropical_gemm_workspace_size_strided(Ad, Bd)
+    assert nb == a_off + -(-(b * m * k * 4) // 256) * 256
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    C, I = run(tb, sr, Ad, Bd, ws)
+    a_copy = ws[a_off:a_off + b * m * k * 4].view(torch.int32).view(b, m, k).cpu()
+    assert torch.equal(a_copy, A.view(torch.int32))
+    if not b_col:
+        assert torch.equal(copy_of_b(ws, b, k, n), B.view(torch.int32).transpose(1, 2))
+    Cr, Ir = orc.gemm(sr, A.numpy(), B.numpy())
+    if dt == "i32":
+        assert_equal(C.cpu().numpy(), Cr, f"{sr} column-major A C")
+    else:
+        assert_bits_equal(C.cpu().numpy(), Cr, f"{sr} column-major A C")
+    assert_equal(I.cpu().numpy(), Ir, f"{sr} column-major A argmax")

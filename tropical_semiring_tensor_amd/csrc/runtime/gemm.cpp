@@ -117,18 +117,19 @@ bool fm_size_ok(int64_t m, int64_t n, int64_t k, int64_t batch) {
     return t >= kFmMinTerms;
 }
 
-// Transposed copy of B: an argmax product with a long K whose B is
-// row-major (j unit-stride) and whose A is read along k in 16-byte quads
-// copies B into the workspace as (batch, n, k), k unit-stride, so that the
-// global-resolve kernel reads both operands in quads along k.  The copy
-// moves 8 bytes per element of B, each of which the product then reads
-// m / 64 times: taken for at least kBtMinRows rows, kBtMinTerms terms and
-// K >= kBtMinK (4096^3 min-plus f32: 3.45 -> 2.88 ms; 2048^3 max-plus:
-// 472 -> 388 us; 4096 x 300 x 4096: 306 -> 310 us, not taken).  The copy
-// sits after the float-mode flags.  TROPICAL_GEMM_B_TRANSPOSE=0 never
-// takes it, =1 at any size with K > kGresMinK.
+// Transposed copies of the operands: an argmax product with a long K whose
+// B is row-major (j unit-stride) copies B into the workspace as (batch, n,
+// k), k unit-stride, and one whose A is column-major (i unit-stride) copies
+// A as (batch, m, k), so that the global-resolve kernel reads both
+// operands in 16-byte quads along k.  A copy moves 8 bytes per element,
+// each of which the product then reads m / 64 (B) or n / 64 (A) times:
+// taken for at least kBtMinRows rows, kBtMinTerms terms and K >= kBtMinK
+// (4096^3 min-plus f32: 3.45 -> 2.88 ms; 2048^3 max-plus: 472 -> 388 us;
+// 4096 x 300 x 4096: 306 -> 310 us, not taken).  The copies sit after the
+// float-mode flags, B's first.  TROPICAL_GEMM_B_TRANSPOSE=0 never takes
+// them, =1 at any size with K > kGresMinK.
 constexpr size_t kBtOffset = 1024;
-static_assert(kFmBytes <= kBtOffset, "the float-mode flags overlap the copy of B");
+static_assert(kFmBytes <= kBtOffset, "the float-mode flags overlap the operand copies");
 constexpr int64_t kBtMinRows = 256;
 constexpr int64_t kBtMinTerms = int64_t(1) << 30;
 constexpr int64_t kBtMinK = 512;
@@ -177,15 +178,36 @@ bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch) {
     return m >= kBtMinRows && k >= kBtMinK && many;
 }
 
-// Workspace bytes with which run_gemm copies B transposed for these
-// operand strides (0: not for this layout or shape).  The pointers' 16-byte
-// alignment is checked at the call.
-size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch) {
-    if (!argmax || sA.col != 1 || sA.row % 4 != 0 || sA.batch % 4 != 0 || sB.col != 1) return 0;
-    if (!kcol_b_pays(m, n, k, batch)) return 0;
-    int64_t e = 0;
-    if (__builtin_mul_overflow(batch, k, &e) || __builtin_mul_overflow(e, n, &e) || e > (INT64_MAX >> 3)) return 0;
-    return kBtOffset + (size_t)((e * 4 + 255) / 256 * 256);
+// The operand copies run_gemm makes for these strides (none: not for this
+// layout or shape).  A is copied when column-major, B when row-major and A
+// is then read along k; the pointers' 16-byte alignment is checked at the
+// call.
+OperandCopies plan_copies(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k,
+                          int64_t batch) {
+    OperandCopies c;
+    if (!argmax || !kcol_b_pays(m, n, k, batch)) return c;
+    const bool a_along_k = sA.col == 1 && sA.row % 4 == 0 && sA.batch % 4 == 0;
+    const bool a_copy = sA.col != 1 && sA.row == 1;
+    if (!a_along_k && !a_copy) return c;
+    const bool b_copy = sB.col == 1;
+    if (!a_copy && !b_copy) return c;
+    int64_t ea = 0, eb = 0;
+    if (__builtin_mul_overflow(batch, k, &ea) || __builtin_mul_overflow(ea, m, &ea) || ea > (INT64_MAX >> 4) ||
+        __builtin_mul_overflow(batch, k, &eb) || __builtin_mul_overflow(eb, n, &eb) || eb > (INT64_MAX >> 4))
+        return c;
+    size_t off = kBtOffset;
+    if (b_copy) {
+        c.b = true;
+        c.b_off = off;
+        off += (size_t)((eb * 4 + 255) / 256 * 256);
+    }
+    if (a_copy) {
+        c.a = true;
+        c.a_off = off;
+        off += (size_t)((ea * 4 + 255) / 256 * 256);
+    }
+    c.bytes = off;
+    return c;
 }
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch) {
@@ -282,31 +304,48 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         p.b_mode = TROP_LOAD_K_CONTIG;
         p.b_vec = 0;
     }
-    // transposed copy of B in the workspace (see kBtOffset): B is then
-    // read along k in 16-byte quads, by the global-resolve kernel (not under
-    // a forced wide or narrow setting)
+    // transposed copies of the operands in the workspace (see kBtOffset):
+    // both are then read along k in 16-byte quads, by the global-resolve
+    // kernel (not under a forced wide or narrow setting)
     const char* setting = std::getenv("TROPICAL_GEMM_SETTING");
     const bool setting_local = setting && (std::strcmp(setting, "wide") == 0 || std::strcmp(setting, "narrow") == 0);
-    const size_t bt_need = workspace && !a_two && !b_two && !setting_local && p.a_mode == TROP_LOAD_K_CONTIG &&
-                                   p.a_vec && p.b_mode == TROP_LOAD_MN_CONTIG
-                               ? bt_bytes(sA, sB, argmax != nullptr, m, n, k, batch)
-                               : 0;
-    if (bt_need > 0 && workspace_bytes >= bt_need && aligned16(workspace)) {
-        void* Bt = static_cast<char*>(workspace) + kBtOffset;
-        const int64_t oshape[3] = {batch, n, k}, ostride[3] = {sB.batch, sB.col, sB.row};
-        GatherPlan g{};
-        trop_status st = plan_gather(3, oshape, ostride, 0, nullptr, nullptr, &g);
-        if (st != TROP_OK) return st;
-        const void* gin[1] = {B};
-        void* gout[1] = {Bt};
-        st = run_gather(dev, g, 1, gin, gout, sr, dt, stream);
-        if (st != TROP_OK) return st;
-        p.B = Bt;
-        p.sb_row = 1;
-        p.sb_col = k;
-        p.sb_batch = k * n;
-        p.b_mode = TROP_LOAD_K_CONTIG;
-        p.b_vec = 1;  // (k % 4 == 0, the copy 256-byte aligned)
+    const OperandCopies cp = workspace && !a_two && !b_two && !setting_local
+                                 ? plan_copies(sA, sB, argmax != nullptr, m, n, k, batch)
+                                 : OperandCopies();
+    if (cp.bytes > 0 && workspace_bytes >= cp.bytes && aligned16(workspace)) {
+        // one operand's copy: output (batch, rows, k) contiguous, read
+        // through the operand's strides
+        auto copy = [&](const void* src, int64_t rows, int64_t s_batch, int64_t s_rows, int64_t s_k,
+                        size_t off) -> trop_status {
+            const int64_t oshape[3] = {batch, rows, k}, ostride[3] = {s_batch, s_rows, s_k};
+            GatherPlan g{};
+            trop_status st = plan_gather(3, oshape, ostride, 0, nullptr, nullptr, &g);
+            if (st != TROP_OK) return st;
+            const void* gin[1] = {src};
+            void* gout[1] = {static_cast<char*>(workspace) + off};
+            return run_gather(dev, g, 1, gin, gout, sr, dt, stream);
+        };
+        if (cp.a) {
+            trop_status st = copy(A, m, sA.batch, sA.row, sA.col, cp.a_off);
+            if (st != TROP_OK) return st;
+            p.A = static_cast<char*>(workspace) + cp.a_off;
+            p.sa_row = k;
+            p.sa_col = 1;
+            p.sa_batch = m * k;
+            p.a_mode = TROP_LOAD_K_CONTIG;
+            p.a_vec = 1;  // (k % 4 == 0, the copy 256-byte aligned)
+        }
+        // (B only when A is now read along k: its alignment is known here)
+        if (cp.b && p.a_mode == TROP_LOAD_K_CONTIG && p.a_vec) {
+            trop_status st = copy(B, n, sB.batch, sB.col, sB.row, cp.b_off);
+            if (st != TROP_OK) return st;
+            p.B = static_cast<char*>(workspace) + cp.b_off;
+            p.sb_row = 1;
+            p.sb_col = k;
+            p.sb_batch = k * n;
+            p.b_mode = TROP_LOAD_K_CONTIG;
+            p.b_vec = 1;
+        }
     }
     const int64_t tm = (m + 63) / 64, tn = (n + 63) / 64;
     if (tm > INT32_MAX || tn > INT32_MAX) return fail(TROP_ERR_INVALID_ARGUMENT, "matrix too large");
@@ -515,7 +554,7 @@ trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, 
     // (the float mode of int32 products and the transposed copy of B use a
     // workspace when one of their size is given, and are skipped otherwise)
     const size_t ws_base = gemm_workspace_bytes(m, n, k, batch);
-    const size_t ws_bt = workspace ? bt_bytes(sA, sB, argmax != nullptr, m, n, k, batch) : 0;
+    const size_t ws_bt = workspace ? plan_copies(sA, sB, argmax != nullptr, m, n, k, batch).bytes : 0;
     const size_t ws_need = ws_bt > ws_base && workspace_bytes >= ws_bt ? ws_bt : ws_base;
     int dev = -1;
     st = current_device(&dev);
@@ -589,7 +628,7 @@ extern "C" trop_status tropical_gemm_workspace_size_strided(trop_strides sA, tro
     if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
     const size_t base = gemm_workspace_bytes(m, n, k, batch);
-    const size_t bt = bt_bytes(sA, sB, with_argmax != 0, m, n, k, batch);
+    const size_t bt = plan_copies(sA, sB, with_argmax != 0, m, n, k, batch).bytes;
     *bytes = bt > base ? bt : base;
     return ok();
 }

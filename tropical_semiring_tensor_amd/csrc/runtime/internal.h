@@ -199,9 +199,16 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
 // not split along K (TROPICAL_GEMM_B_TRANSPOSE=0: never, =1: any unsplit
 // product with K > 256).
 bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch);
-// Workspace bytes with which run_gemm copies a row-major B transposed (an
-// argmax product with a long K and A read along k; 0: not taken)
-size_t bt_bytes(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k, int64_t batch);
+// The transposed operand copies run_gemm makes in the workspace for an
+// argmax product with a long K: a column-major A as (batch, m, k), a
+// row-major B as (batch, n, k) when A is read along k; their byte offsets
+// and the workspace bytes they need (0: none).
+struct OperandCopies {
+    bool a = false, b = false;
+    size_t a_off = 0, b_off = 0, bytes = 0;
+};
+OperandCopies plan_copies(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k,
+                          int64_t batch);
 // Two-level k of the GEMM's operands (TropGemmParams a_krun / sa_khi):
 // a_run > 0 reads A's k as k = hi a_run + lo, lo at unit stride (sA.col = 1)
 // and hi at stride a_hi; a_run is 4, 8 or 16.  Likewise b_run / b_hi with
