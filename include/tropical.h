@@ -184,7 +184,7 @@ TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t 
  * the copies hold the same values, so the results are unchanged).  A
  * workspace of tropical_gemm_workspace_size's bytes gets no copy.
  * Host-only.
- * Errors: TROP_ERR_INVALID_ARGUMENT (negative size, NULL bytes).
+ * Errors: TROP_ERR_INVALID_ARGUMENT (negative size or stride, NULL bytes).
  */
 TROP_API trop_status tropical_gemm_workspace_size_strided(trop_strides sA, trop_strides sB, int with_argmax,
                                                  int64_t m, int64_t n, int64_t k, int64_t batch,

@@ -83,6 +83,13 @@ def test_gemm_argument_errors_before_any_device_call(tb):
     neg = tb.trop_strides(-1, 1, 1)
     assert L.tropical_gemm_strided_batched(0, 0, nul, neg, nul, s, nul, s, nul, 1, 1, 1, 1, nul) == tb.INVALID_ARGUMENT
     assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, 1, 1, 2 ** 31, 1, nul) == tb.INVALID_ARGUMENT
+    # the strided workspace query: NULL bytes, negative sizes and strides
+    nb = ctypes.c_size_t(0)
+    assert L.tropical_gemm_workspace_size_strided(s, s, 1, 4, 4, 4, 1, None) == tb.INVALID_ARGUMENT
+    assert L.tropical_gemm_workspace_size_strided(s, s, 1, 4, -4, 4, 1, ctypes.byref(nb)) == tb.INVALID_ARGUMENT
+    assert L.tropical_gemm_workspace_size_strided(s, neg, 1, 4, 4, 4, 1, ctypes.byref(nb)) == tb.INVALID_ARGUMENT
+    assert "stride" in tb.tropical_last_error()
+    assert L.tropical_gemm_workspace_size_strided(s, s, 1, 4, 4, 4, 1, ctypes.byref(nb)) == tb.OK and nb.value == 0
     # an empty output is a no-op before any pointer is looked at
     assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, 0, 5, 5, 3, nul) == tb.OK
     assert L.tropical_gemm_strided_batched(1, 1, nul, s, nul, s, nul, s, nul, 4, 4, 4, 0, nul) == tb.OK

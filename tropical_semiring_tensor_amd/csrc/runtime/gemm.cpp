@@ -627,6 +627,8 @@ extern "C" trop_status tropical_gemm_workspace_size_strided(trop_strides sA, tro
     using namespace trop;
     if (!bytes) return fail(TROP_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (m < 0 || n < 0 || k < 0 || batch < 0) return fail(TROP_ERR_INVALID_ARGUMENT, "negative size");
+    if (sA.row < 0 || sA.col < 0 || sA.batch < 0 || sB.row < 0 || sB.col < 0 || sB.batch < 0)
+        return fail(TROP_ERR_INVALID_ARGUMENT, "negative stride");
     const size_t base = gemm_workspace_bytes(m, n, k, batch);
     const size_t bt = plan_copies(sA, sB, with_argmax != 0, m, n, k, batch).bytes;
     *bytes = bt > base ? bt : base;
