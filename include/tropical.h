@@ -329,9 +329,9 @@ TROP_API trop_status tropical_contract_pair_workspace_size(const char* spec, con
  * 4, at least 256 rows and 2^30 terms, not split) an operand that would be
  * read with its free index at unit stride is gathered with k at unit
  * stride instead ((batch, rows, contracted) for the product's left
- * operand, (batch, cols, contracted) for its right one), so that the
- * product reads both operands along k (TROPICAL_GEMM_B_TRANSPOSE as for
- * tropical_gemm_workspace_size_strided).  When both operands need the
+ * operand, (batch, cols, contracted) for its right one, the latter only
+ * with an argmax output), so that the product reads both operands along k
+ * (TROPICAL_GEMM_B_TRANSPOSE as for tropical_gemm_workspace_size_strided).  When both operands need the
  * tiled transpose kernel in step 1, the two run as one launch.
  * spec: "lhs,rhs->out" with single-letter labels a-z A-Z, explicit output,
  *   no ellipsis; every output label appears in an operand, output labels

@@ -242,7 +242,7 @@ bool operand_span(const Operand& op, int64_t* span) {
 
 trop_status pair_plan(const std::string& la, const std::string& lb, const std::string& lo,
                       const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
-                      const int64_t* stridesB, Plan& P) {
+                      const int64_t* stridesB, Plan& P, bool value_only) {
     P = Plan();
     P.la = la;
     P.lb = lb;
@@ -311,8 +311,10 @@ trop_status pair_plan(const std::string& la, const std::string& lb, const std::s
                try_fold_two(P, Rt, r_red, P.batch, cols, P.contracted, false, &P.sB, &P.kr.b_run, &P.kr.b_hi);
     // the right operand: read along k from a copy in (batch, cols,
     // contracted) order where it would otherwise be read with its free
-    // index at unit stride (the left one is read along k by now)
-    const bool b_kcol = long_k;
+    // index at unit stride (the left one is read along k by now); not
+    // without an argmax output, whose kernel reads either layout as fast
+    // (the copy would only add its traffic)
+    const bool b_kcol = long_k && !value_only;
     if (P.b_fold && b_kcol && P.kr.b_run == 0 && P.sB.row != 1) P.b_fold = false;
     P.b_kcol = !P.b_fold && b_kcol;
     if (!P.b_fold) {
@@ -501,11 +503,11 @@ trop_status pair_run(int dev, const Plan& P, trop_semiring semiring, trop_dtype 
 namespace {
 
 trop_status build_plan(const char* spec, const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
-                       const int64_t* stridesB, Plan& P) {
+                       const int64_t* stridesB, Plan& P, bool value_only = false) {
     std::string la, lb, lo;
     trop_status st = pair_parse(spec, &la, &lb, &lo);
     if (st != TROP_OK) return st;
-    return pair_plan(la, lb, lo, shapeA, stridesA, shapeB, stridesB, P);
+    return pair_plan(la, lb, lo, shapeA, stridesA, shapeB, stridesB, P, value_only);
 }
 
 }  // namespace
@@ -556,7 +558,7 @@ trop_status contract_pair_call(const char* spec, trop_semiring semiring, trop_dt
     if (dtype != TROP_F32 && dtype != TROP_I32) return fail(TROP_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (ring_index(semiring, dtype) < 0) return fail(TROP_ERR_UNSUPPORTED, "no such semiring / dtype pair");
     Plan P;
-    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P);
+    trop_status st = build_plan(spec, shapeA, stridesA, shapeB, stridesB, P, argmax == nullptr);
     if (st != TROP_OK) return st;
     if (argmax && !P.route_fits)
         return fail(TROP_ERR_INVALID_ARGUMENT, "the argmax index over the contracted and reduced labels exceeds int32");

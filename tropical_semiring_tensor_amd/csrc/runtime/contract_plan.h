@@ -57,10 +57,13 @@ struct PairPlan {
 trop_status pair_parse(const char* spec, std::string* la, std::string* lb, std::string* lo);
 
 // Plan `la,lb->lo` for operands of these shapes and element strides
-// (strides NULL: contiguous row-major).
+// (strides NULL: contiguous row-major).  value_only: a call without an
+// argmax output (a long K then keeps a right operand read in place: only
+// the argmax form gains from reading it along k); its workspace is at most
+// that of the argmax plan.
 trop_status pair_plan(const std::string& la, const std::string& lb, const std::string& lo,
                       const int64_t* shapeA, const int64_t* stridesA, const int64_t* shapeB,
-                      const int64_t* stridesB, PairPlan& P);
+                      const int64_t* stridesB, PairPlan& P, bool value_only = false);
 
 std::string pair_describe(const PairPlan& P);
 
