@@ -172,12 +172,12 @@ TROP_API trop_status tropical_gemm_workspace_size(int64_t m, int64_t n, int64_t 
  * Workspace (bytes) for tropical_gemm_strided_batched_ws with these operand
  * strides: tropical_gemm_workspace_size's bytes, or more when the call
  * would copy operands transposed.  The copies are made for a product with
- * an argmax output (with_argmax != 0), K >= 512 and a multiple of 4, at
- * least 256 rows and 2^30 terms, and no split along K: a row-major B
- * (sB.col == 1) is copied as [batch][n][k] when A is read along k
+ * K >= 512 and a multiple of 4, at least 256 rows and 2^30 terms, and no
+ * split along K: a column-major A (sA.row == 1, sA.col != 1) is copied as
+ * [batch][m][k], and, with an argmax output (with_argmax != 0), a
+ * row-major B (sB.col == 1) as [batch][n][k] when A is read along k
  * (sA.col == 1, sA.row and sA.batch multiples of 4, A 16-byte aligned, or
- * A copied), and a column-major A (sA.row == 1, sA.col != 1) as
- * [batch][m][k].  They sit in the workspace 1 KiB in (after the int32
+ * A copied).  They sit in the workspace 1 KiB in (after the int32
  * float-mode flags), B's first, each batch*rows*k*4 bytes rounded up to
  * 256.  The product then reads both operands along k as it does for a
  * row-major A and a column-major B (one argmax resolve per output tile;

@@ -184,6 +184,8 @@ def test_gemm_workspace_with_transposed_b(tb, monkeypatch):
     assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096, col=True)) == copy(1, 4096, 4096)
     assert ws(t(2, 1000, 2048, col=True), t(2, 2048, 600, col=True)) == copy(2, 2048, 1000)
     assert ws(t(1, 4096, 4096), t(1, 4096, 4096), with_argmax=False) == 4 * 256
+    # without an argmax only a column-major A is copied
+    assert ws(t(1, 4096, 4096, col=True), t(1, 4096, 4096), with_argmax=False) == copy(1, 4096, 4096)
     assert ws(t(64, 256, 256), t(64, 256, 256)) == 0
     assert ws(t(1, 4096, 4094), t(1, 4094, 4096)) == 4 * 256
     assert ws(t(64, 128, 1024), t(64, 1024, 2048)) == 4 * 256  # 128 rows: the float-mode flags only

@@ -176,3 +176,20 @@ def test_transposed_copy_of_a_column_major_a(tb, orc, monkeypatch, sr, dt, b_col
     else:
         assert_bits_equal(C.cpu().numpy(), Cr, f"{sr} column-major A C")
     assert_equal(I.cpu().numpy(), Ir, f"{sr} column-major A argmax")
+
+
+def test_value_only_copies_a_column_major_a(tb, orc, monkeypatch):
+    """Without an argmax output only a column-major A is copied (a row-major
+    B is read in place)."""
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    b, m, k, n = 43, 130, 264, 90
+    A, B = operands("min_plus", "f32", b, m, k, n, seed=31)
+    Ad = A.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    Bd = B.to(DEV)
+    nb = tb.tropical_gemm_workspace_size_strided(Ad, Bd, with_argmax=False)
+    assert nb == copy_bytes(b, k, m)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    C, _ = run(tb, "min_plus", Ad, Bd, ws, argmax=False)
+    assert torch.equal(ws[BT_OFF:BT_OFF + b * m * k * 4].view(torch.int32).view(b, m, k).cpu(), A.view(torch.int32))
+    Cr, _ = orc.gemm("min_plus", A.numpy(), B.numpy(), argmax=False)
+    assert_bits_equal(C.cpu().numpy(), Cr, "value only, column-major A")

@@ -179,17 +179,19 @@ bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch) {
 }
 
 // The operand copies run_gemm makes for these strides (none: not for this
-// layout or shape).  A is copied when column-major, B when row-major and A
-// is then read along k; the pointers' 16-byte alignment is checked at the
-// call.
+// layout or shape).  A is copied when column-major, B when row-major, A is
+// then read along k and the product has an argmax output; the pointers'
+// 16-byte alignment is checked at the call.
 OperandCopies plan_copies(trop_strides sA, trop_strides sB, bool argmax, int64_t m, int64_t n, int64_t k,
                           int64_t batch) {
     OperandCopies c;
-    if (!argmax || !kcol_b_pays(m, n, k, batch)) return c;
+    if (!kcol_b_pays(m, n, k, batch)) return c;
     const bool a_along_k = sA.col == 1 && sA.row % 4 == 0 && sA.batch % 4 == 0;
     const bool a_copy = sA.col != 1 && sA.row == 1;
     if (!a_along_k && !a_copy) return c;
-    const bool b_copy = sB.col == 1;
+    // (B only with an argmax output: the value-only kernel reads a
+    // row-major B as fast)
+    const bool b_copy = argmax && sB.col == 1;
     if (!a_copy && !b_copy) return c;
     int64_t ea = 0, eb = 0;
     if (__builtin_mul_overflow(batch, k, &ea) || __builtin_mul_overflow(ea, m, &ea) || ea > (INT64_MAX >> 4) ||

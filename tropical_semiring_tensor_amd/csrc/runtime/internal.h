@@ -199,10 +199,10 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t batch);
 // not split along K (TROPICAL_GEMM_B_TRANSPOSE=0: never, =1: any unsplit
 // product with K > 256).
 bool kcol_b_pays(int64_t m, int64_t n, int64_t k, int64_t batch);
-// The transposed operand copies run_gemm makes in the workspace for an
-// argmax product with a long K: a column-major A as (batch, m, k), a
-// row-major B as (batch, n, k) when A is read along k; their byte offsets
-// and the workspace bytes they need (0: none).
+// The transposed operand copies run_gemm makes in the workspace for a
+// product with a long K: a column-major A as (batch, m, k), and with an
+// argmax output a row-major B as (batch, n, k) when A is read along k;
+// their byte offsets and the workspace bytes they need (0: none).
 struct OperandCopies {
     bool a = false, b = false;
     size_t a_off = 0, b_off = 0, bytes = 0;
