@@ -90,6 +90,10 @@ def test_gemm_argument_errors_before_any_device_call(tb):
     assert L.tropical_gemm_workspace_size_strided(s, neg, 1, 4, 4, 4, 1, ctypes.byref(nb)) == tb.INVALID_ARGUMENT
     assert "stride" in tb.tropical_last_error()
     assert L.tropical_gemm_workspace_size_strided(s, s, 1, 4, 4, 4, 1, ctypes.byref(nb)) == tb.OK and nb.value == 0
+    # sizes near the int64 limit: answered without overflow (no split, K >= 2^31 is no call's)
+    big = 2 ** 62
+    assert L.tropical_gemm_workspace_size(big, 1, 2 ** 62, 1, ctypes.byref(nb)) == tb.OK
+    assert L.tropical_gemm_workspace_size_strided(s, s, 1, big, big, big, big, ctypes.byref(nb)) == tb.OK
     # an empty output is a no-op before any pointer is looked at
     assert L.tropical_gemm_strided_batched(0, 0, nul, s, nul, s, nul, s, nul, 0, 5, 5, 3, nul) == tb.OK
     assert L.tropical_gemm_strided_batched(1, 1, nul, s, nul, s, nul, s, nul, 4, 4, 4, 0, nul) == tb.OK

@@ -142,12 +142,14 @@ int bt_knob() {
 
 SplitK plan_splitk(int64_t m, int64_t n, int64_t k, int64_t batch) {
     SplitK s;
-    if (m <= 0 || n <= 0 || batch <= 0 || k <= 0) return s;
+    // (K < 2^31, as the calls require: the sizes below then stay far from
+    // overflow, units being at most kSplitTarget / 2)
+    if (m <= 0 || n <= 0 || batch <= 0 || k <= 0 || k >= (int64_t(1) << 31)) return s;
     int64_t units = 0;
     if (__builtin_mul_overflow((m + 63) / 64, (n + 63) / 64, &units) ||
         __builtin_mul_overflow(units, batch, &units))
         return s;
-    if (units * 2 > kSplitTarget) return s;
+    if (units > kSplitTarget / 2) return s;
     const int64_t blocks = k / 256 > 1 ? k / 256 : 1;
     const bool tiny = units * blocks <= kSplitTinyUnits && !env_flag_off("TROPICAL_SPLITK_TINY");
     const int64_t min_k = tiny ? kSplitTinyK : kSplitMinK;
