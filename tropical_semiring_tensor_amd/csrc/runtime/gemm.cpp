@@ -555,7 +555,7 @@ trop_status gemm_entry(trop_semiring semiring, trop_dtype dtype, const void* A, 
     if (workspace && sk.bytes > 0 && workspace_bytes < sk.bytes)
         return fail(TROP_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs " + std::to_string(sk.bytes) + " bytes, got " + std::to_string(workspace_bytes));
-    // (the float mode of int32 products and the transposed copy of B use a
+    // (the float mode of int32 products and the transposed operand copies use a
     // workspace when one of their size is given, and are skipped otherwise)
     const size_t ws_base = gemm_workspace_bytes(m, n, k, batch);
     const size_t ws_bt = workspace ? plan_copies(sA, sB, argmax != nullptr, m, n, k, batch).bytes : 0;
