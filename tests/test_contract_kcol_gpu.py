@@ -85,3 +85,23 @@ def test_allocation_free_call_gathers_along_k_too(tb, monkeypatch):
         tb.tropical_contract_pair_noalloc(spec, "max_plus", Ad, Bd, C, I)
         torch.cuda.synchronize()
         assert torch.equal(C.view(torch.int32), Cw.view(torch.int32)) and torch.equal(I, Iw), spec
+
+
+@pytest.mark.parametrize("float_mode", ["0", "1"])
+@pytest.mark.parametrize("sr", ["max_plus", "min_plus", "max_mul"])
+def test_int32_operands_gathered_along_k(tb, orc, monkeypatch, sr, float_mode):
+    """int32 operands gathered along k, with the int32 kernel or (max-plus,
+    min-plus) the float mode, whose flags share the GEMM's workspace."""
+    monkeypatch.setenv("TROPICAL_GEMM_B_TRANSPOSE", "1")
+    monkeypatch.setenv("TROPICAL_GEMM_INT_FLOAT", float_mode)
+    spec, sa, sb = "ji,jk->ik", (260, 1100), (260, 1000)
+    assert "A=gather:tiled B=gather:tiled:kcol" in tb.tropical_contract_pair_describe(spec, sa, sb)
+    g = torch.Generator().manual_seed(41)
+    lo = 0 if sr != "max_plus" else -9
+    A = torch.randint(lo, 10, sa, generator=g, dtype=torch.int32)
+    B = torch.randint(lo, 10, sb, generator=g, dtype=torch.int32)
+    C, I = tb.tropical_contract_pair(spec, sr, A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    Cr, Ir = orc.contract_pair(spec, sr, A.numpy(), B.numpy())
+    assert_equal(C.cpu().numpy(), Cr, f"{sr} int32 C")
+    assert_equal(I.cpu().numpy(), Ir, f"{sr} int32 argmax")
