@@ -37,6 +37,125 @@ __device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
     }
 }
 
+// Products with a short K (1..SK_MAXK) and up to 256 columns, a multiple
+// of 4 (the host takes it for 192..256 columns and many rows): each lane holds four columns of B (all K rows) in registers, the
+// workgroup stages blocks of SK_ROWS rows of A in LDS, and each wave walks
+// rows SK_RPW at a time, computing the lane's outputs as the sequential scan does (k
+// ascending, the zero element to start, strict compare: the same values,
+// bits and smallest winning k as the simple kernel) and writing them as one
+// 16-byte store each for C and the argmax.  A tiled kernel at this K runs
+// one slice per tile, its loads, compute and stores one after another;
+// here B is loaded once per batch entry and the output writes stream.
+// Needs C (and the argmax) with unit column stride, rows and batch strides
+// multiples of 4 and 16-byte aligned (checked on the host).
+constexpr int SK_MAXK = 16;
+constexpr int SK_ROWS = 32;  // rows per unit of work
+constexpr int SK_RPW = 2;    // rows a wave computes together (independent chains)
+
+template <int SR, typename T, bool ARG>
+__device__ __forceinline__ void gemm_smallk_run(const TropGemmParams& p, T (&As)[SK_ROWS][SK_MAXK]) {
+    using R = Ring<SR, T>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = (int)(blockDim.x >> 6);
+    const int K = (int)p.k;
+    const int64_t m = p.m;
+    const int64_t j0 = 4 * (int64_t)lane;
+    const bool jl = j0 < p.n;  // (n % 4 == 0)
+    const int64_t rblocks = (m + SK_ROWS - 1) / SK_ROWS;
+    const int64_t units = rblocks * p.batch;
+    const T* A = static_cast<const T*>(p.A);
+    const T* B = static_cast<const T*>(p.B);
+    T bv[SK_MAXK][4];
+    int64_t cur_b = -1;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int64_t b = u / rblocks, r0 = (u - b * rblocks) * SK_ROWS;
+        __syncthreads();  // the previous unit's rows are read
+        // A's rows: element e of the SK_ROWS x K block is row e % SK_ROWS,
+        // term e / SK_ROWS (consecutive threads take consecutive rows)
+        for (int e = tid; e < SK_ROWS * SK_MAXK; e += blockDim.x) {
+            const int r = e % SK_ROWS, kk = e / SK_ROWS;
+            const int64_t i = r0 + r;
+            if (i < m && kk < K)
+                As[r][kk] = A[b * p.sa_batch + i * p.sa_row + k_offset(kk, p.a_krun, p.sa_khi, p.sa_col)];
+        }
+        if (b != cur_b) {
+            cur_b = b;
+            // a row-major B with 16-byte aligned rows: one 16-byte load per k
+            const bool bvec = p.sb_col == 1 && p.b_krun == 0 && (p.sb_row & 3) == 0 && (p.sb_batch & 3) == 0 &&
+                              (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
+#pragma unroll
+            for (int kk = 0; kk < SK_MAXK; ++kk) {
+                if (jl && kk < K && bvec) {
+                    const vec4<T> v = *reinterpret_cast<const vec4<T>*>(B + b * p.sb_batch + kk * p.sb_row + j0);
+                    bv[kk][0] = v.x;
+                    bv[kk][1] = v.y;
+                    bv[kk][2] = v.z;
+                    bv[kk][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        bv[kk][c] = (jl && kk < K) ? B[b * p.sb_batch + k_offset(kk, p.b_krun, p.sb_khi, p.sb_row) +
+                                                       (j0 + c) * p.sb_col]
+                                                   : R::zero();
+                }
+            }
+        }
+        __syncthreads();
+        // SK_RPW rows at a time per wave: 4 * SK_RPW independent chains
+        for (int rr = wave * SK_RPW; rr < SK_ROWS; rr += nwaves * SK_RPW) {
+            if (r0 + rr >= m) break;  // (uniform over the wave)
+            T best[SK_RPW][4];
+            int32_t arg[SK_RPW][4];
+#pragma unroll
+            for (int h = 0; h < SK_RPW; ++h)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    best[h][c] = R::zero();
+                    arg[h][c] = 0;
+                }
+#pragma unroll
+            for (int kk = 0; kk < SK_MAXK; ++kk) {
+                if (kk < K) {
+#pragma unroll
+                    for (int h = 0; h < SK_RPW; ++h) {
+                        const T a = As[rr + h][kk];  // (rows past m: staged garbage, never stored)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const T t = R::mul(a, bv[kk][c]);
+                            const bool up = R::better(t, best[h][c]);
+                            best[h][c] = up ? t : best[h][c];
+                            if (ARG) arg[h][c] = up ? kk : arg[h][c];
+                        }
+                    }
+                }
+            }
+            if (jl) {
+#pragma unroll
+                for (int h = 0; h < SK_RPW; ++h) {
+                    const int64_t i = r0 + rr + h;
+                    if (i < m) {
+                        const int64_t off = b * p.sc_batch + i * p.sc_row + j0;
+                        *reinterpret_cast<vec4<T>*>(static_cast<T*>(p.C) + off) =
+                            vec4<T>{best[h][0], best[h][1], best[h][2], best[h][3]};
+                        if (ARG)
+                            *reinterpret_cast<vec4<int32_t>*>(p.argmax + off) =
+                                vec4<int32_t>{arg[h][0], arg[h][1], arg[h][2], arg[h][3]};
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int SR, typename T>
+__device__ __forceinline__ void gemm_smallk_body(const TropGemmParams& p) {
+    __shared__ T As[SK_ROWS][SK_MAXK];
+    if (p.argmax)
+        gemm_smallk_run<SR, T, true>(p, As);
+    else
+        gemm_smallk_run<SR, T, false>(p, As);
+}
+
 // Split-K merge: the partials of the K ranges, in range order, each the
 // result of the strict scan over its own range of k.  Keeping the first
 // strictly better one reproduces the scan over all of K: its value, the

@@ -74,6 +74,9 @@ using namespace trop;
     extern "C" __global__ __launch_bounds__(256) void trop_gemm_simple_##NAME(TropGemmParams p) { \
         gemm_simple_body<SR, T>(p);                                                             \
     }                                                                                           \
+    extern "C" __global__ __launch_bounds__(256) void trop_gemm_smallk_##NAME(TropGemmParams p) { \
+        gemm_smallk_body<SR, T>(p);                                                             \
+    }                                                                                           \
     extern "C" __global__ __launch_bounds__(256) void trop_gather_reduce_##NAME(                \
         TropGatherParams p) {                                                                   \
         gather_reduce_body<SR, T>(p);                                                           \

@@ -42,7 +42,9 @@ enum KernelId : int {
     K_GEMM_TILED_W1_MAXPLUS_F32 = K_GEMM_TILED_VOR_MAXPLUS_F32 + NRING,
     K_GEMM_TILED_KM1_MAXPLUS_F32 = K_GEMM_TILED_W1_MAXPLUS_F32 + NRING,
     K_GEMM_TILED_VO1_MAXPLUS_F32 = K_GEMM_TILED_KM1_MAXPLUS_F32 + NRING,
-    K_FILL = K_GEMM_TILED_VO1_MAXPLUS_F32 + NRING,
+    // short K (at most 16), B held in registers
+    K_GEMM_SMALLK_MAXPLUS_F32 = K_GEMM_TILED_VO1_MAXPLUS_F32 + NRING,
+    K_FILL = K_GEMM_SMALLK_MAXPLUS_F32 + NRING,
     K_GATHER_COPY,
     K_GATHER_TILED,
     K_GATHER_NAIVE,

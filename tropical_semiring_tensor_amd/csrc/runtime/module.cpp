@@ -43,7 +43,7 @@ const std::vector<std::string>& kernel_names() {
                                                "trop_gemm_tiled_gkk_",   "trop_gemm_tiled_km_",
                                                "trop_gemm_tiled_kmr_",   "trop_gemm_tiled_vor_",
                                                "trop_gemm_tiled_w1_",    "trop_gemm_tiled_km1_",
-                                               "trop_gemm_tiled_vo1_"};
+                                               "trop_gemm_tiled_vo1_",   "trop_gemm_smallk_"};
         static const char* const singles[] = {
             "trop_fill",                     "trop_gather_copy",
             "trop_gather_tiled",             "trop_gather_naive",
