@@ -66,12 +66,13 @@ def check(tb, orc, sr, A, B, what, argmax=True):
 SHAPES = [(1, 32768, 16, 256), (1, 32801, 1, 196), (2, 16411, 15, 252), (3, 11000, 2, 200)]
 
 
+@pytest.mark.parametrize("argmax", [True, False], ids=["argmax", "value_only"])
 @pytest.mark.parametrize("sr,dt", PAIRS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_short_k_matches_oracle(tb, orc, sr, dt, shape):
+def test_short_k_matches_oracle(tb, orc, sr, dt, shape, argmax):
     b, m, k, n = shape
     A, B = make(sr, dt, b, m, k, n, seed=sum(shape) + len(sr))
-    check(tb, orc, sr, A, B, f"{sr} {dt} {shape}")
+    check(tb, orc, sr, A, B, f"{sr} {dt} {shape}", argmax=argmax)
 
 
 @pytest.mark.parametrize("layout", ["colA", "colB", "colA_colB", "strided"])
