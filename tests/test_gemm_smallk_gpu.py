@@ -1,5 +1,5 @@
-"""The short-K GEMM kernel (K <= 16, 192..256 columns, at least 32768 rows
-in all): B held in registers, rows of A streamed.  Every case is compared
+"""The short-K GEMM kernel (K <= 16; 192..256 columns and at least 32768
+rows in all, or 128..191 columns and at least 65536 rows): B held in registers, rows of A streamed.  Every case is compared
 bit for bit with the oracle, values and argmax, over semirings, dtypes,
 operand layouts, ragged rows, K at its ends, special values and int32
 limits; the same products with the kernel switched off give the same
@@ -63,7 +63,9 @@ def check(tb, orc, sr, A, B, what, argmax=True):
         assert_equal(I, Ir, what + " argmax")
 
 
-SHAPES = [(1, 32768, 16, 256), (1, 32801, 1, 196), (2, 16411, 15, 252), (3, 11000, 2, 200)]
+SHAPES = [(1, 32768, 16, 256), (1, 32801, 1, 196), (2, 16411, 15, 252), (3, 11000, 2, 200),
+          # 128..191 columns: two rows per wave's lane groups
+          (1, 65600, 8, 132), (2, 32800, 3, 128)]
 
 
 @pytest.mark.parametrize("argmax", [True, False], ids=["argmax", "value_only"])

@@ -38,16 +38,19 @@ __device__ __forceinline__ void gemm_simple_body(const TropGemmParams& p) {
 }
 
 // Products with a short K (1..SK_MAXK) and up to 256 columns, a multiple
-// of 4 (the host takes it for 192..256 columns and many rows): each lane holds four columns of B (all K rows) in registers, the
-// workgroup stages blocks of SK_ROWS rows of A in LDS, and each wave walks
-// rows SK_RPW at a time, computing the lane's outputs as the sequential scan does (k
-// ascending, the zero element to start, strict compare: the same values,
-// bits and smallest winning k as the simple kernel) and writing them as one
-// 16-byte store each for C and the argmax.  A tiled kernel at this K runs
-// one slice per tile, its loads, compute and stores one after another;
-// here B is loaded once per batch entry and the output writes stream.
-// Needs C (and the argmax) with unit column stride, rows and batch strides
-// multiples of 4 and 16-byte aligned (checked on the host).
+// of 4 (the host takes it for 128..256 columns and many rows).  Each lane
+// holds four columns of B (all K rows) in registers; a row takes the 16,
+// 32 or 64 lanes that cover its columns, so a wave computes 4, 2 or 1 rows
+// per lane group step.  The workgroup stages blocks of SK_ROWS rows of A in
+// LDS, and each lane group walks rows SK_RPW at a time, computing the
+// lane's outputs as the sequential scan does (k ascending, the zero
+// element to start, strict compare: the same values, bits and smallest
+// winning k as the simple kernel) and writing them as one 16-byte store
+// each for C and the argmax.  A tiled kernel at this K runs one slice per
+// tile, its loads, compute and stores one after another; here B is loaded
+// once per batch entry and the output writes stream.  Needs C (and the
+// argmax) with unit column stride, rows and batch strides multiples of 4
+// and 16-byte aligned (checked on the host).
 constexpr int SK_MAXK = 16;
 constexpr int SK_ROWS = 32;  // rows per unit of work
 constexpr int SK_RPW = 2;    // rows a wave computes together (independent chains)
@@ -59,8 +62,13 @@ __device__ __forceinline__ void gemm_smallk_run(const TropGemmParams& p, T (&As)
     const int nwaves = (int)(blockDim.x >> 6);
     const int K = (int)p.k;
     const int64_t m = p.m;
-    const int64_t j0 = 4 * (int64_t)lane;
+    // lanes per row: the power of two of 16, 32 or 64 that covers n / 4
+    // column groups; the wave's 64 / lpr lane groups take different rows
+    const int lsh = p.n > 128 ? 6 : (p.n > 64 ? 5 : 4);
+    const int lpr = 1 << lsh, sub = lane >> lsh;
+    const int64_t j0 = 4 * (int64_t)(lane & (lpr - 1));
     const bool jl = j0 < p.n;  // (n % 4 == 0)
+    const int rstep = SK_RPW << (6 - lsh);  // rows a wave covers per step
     const int64_t rblocks = (m + SK_ROWS - 1) / SK_ROWS;
     const int64_t units = rblocks * p.batch;
     const T* A = static_cast<const T*>(p.A);
@@ -101,9 +109,11 @@ __device__ __forceinline__ void gemm_smallk_run(const TropGemmParams& p, T (&As)
             }
         }
         __syncthreads();
-        // SK_RPW rows at a time per wave: 4 * SK_RPW independent chains
-        for (int rr = wave * SK_RPW; rr < SK_ROWS; rr += nwaves * SK_RPW) {
-            if (r0 + rr >= m) break;  // (uniform over the wave)
+        // rstep rows at a time per wave (SK_RPW per lane group): 4 * SK_RPW
+        // independent chains per lane
+        for (int rw = wave * rstep; rw < SK_ROWS; rw += nwaves * rstep) {
+            if (r0 + rw >= m) break;  // (uniform over the wave)
+            const int rr = rw + sub * SK_RPW;  // this lane group's first row
             T best[SK_RPW][4];
             int32_t arg[SK_RPW][4];
 #pragma unroll

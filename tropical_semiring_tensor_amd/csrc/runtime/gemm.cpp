@@ -86,15 +86,19 @@ constexpr int64_t kSplitTinyK = 64;  // one slice of the split kernels
 // tiles, a 64 x 16 grid of 1024 measured slower: 23 -> 35 us on 32 x 256 x
 // 128 x 256; with 128, faster: 21.3 -> 18.5 us on 8 x 256^3)
 constexpr int64_t kTiny16Tiles = 128;
-// Products with K <= kSmallKMax, kSmallKMinN..256 columns and at least
+// Products with K <= kSmallKMax, 192..256 columns and at least
 // kSmallKMinRows rows (times batch) take the short-K kernel
 // (TROPICAL_GEMM_SMALLK=0: never).  65536 x 256 x 16 with argmax: 49.6 ->
 // 39.5 us (column-major A 54.8 -> 39.5), K = 4: 44 -> 27.5 us; with fewer
 // rows its per-workgroup set-up shows (16384 x 256 x 16: 16.6 -> 19.0 us),
 // with fewer columns its idle lanes (131072 x 128 x 16: 50.6 -> 67.8 us).
+// 128..191 columns (two rows per lane group): from kSmallKMinRows128 rows
+// (131072 x 128 x 16: 49.7 -> 41.5 us; 65536 x 128 x 16: 27.5 -> 26.4 us;
+// fewer than 128 columns measured no faster).
 constexpr int64_t kSmallKMax = 16;
-constexpr int64_t kSmallKMinN = 192;
+constexpr int64_t kSmallKMinN = 128;
 constexpr int64_t kSmallKMinRows = 32768;
+constexpr int64_t kSmallKMinRows128 = 65536;
 // Products with a longer K take the global-resolve argmax kernel
 // (TROPICAL_GEMM_GRES_MIN_K overrides, for measurements).
 const int64_t kGresMinK = [] {
@@ -287,14 +291,15 @@ trop_status run_gemm(int dev, trop_semiring sr, trop_dtype dt, const void* A, tr
         return launch(dev, (KernelId)(K_GEMM_SIMPLE_MAXPLUS_F32 + ri), TROP_K_GEMM_SIMPLE,
                       grid_for(m * n * batch, 256), 256, &p, stream);
     }
-    // A short K with 192..256 columns: B held in registers, rows of A
+    // A short K with 128..256 columns: B held in registers, rows of A
     // streamed (gemm_smallk_body; not under a forced GEMM setting, which
     // the tests use to drive the tiled kernels at these shapes)
     {
         const char* forced = std::getenv("TROPICAL_GEMM_SETTING");
         const bool c_ok = sC.col == 1 && sC.row % 4 == 0 && sC.batch % 4 == 0 && aligned16(C) &&
                           (!argmax || aligned16(argmax));
-        if (k >= 1 && k <= kSmallKMax && n >= kSmallKMinN && n <= 256 && n % 4 == 0 && m * batch >= kSmallKMinRows &&
+        if (k >= 1 && k <= kSmallKMax && n >= kSmallKMinN && n <= 256 && n % 4 == 0 &&
+            m * batch >= (n >= 192 ? kSmallKMinRows : kSmallKMinRows128) &&
             c_ok && !(forced && *forced) && !env_flag_off("TROPICAL_GEMM_SMALLK")) {
             const KernelId id = (KernelId)(K_GEMM_SMALLK_MAXPLUS_F32 + ri);
             int per_cu = kernel_occupancy(dev, id);
