@@ -504,6 +504,28 @@ def other_workloads(torch, tb, inputs, timer, dev, args):
     log(f"[bench] split K 64x64x65536: {out['maxplus_f32_b1_64x64_k65536']}")
     del As, Bs, Cs, Is, ws
 
+    # a short-K product (a lattice network's boundary step, K = 16): the
+    # short-K kernel against the tiled kernels (TROPICAL_GEMM_SMALLK=0)
+    g = torch.Generator(device="cpu").manual_seed(18)
+    As = torch.randn(1, 65536, 16, generator=g).to(dev)
+    Bs = torch.randn(1, 16, 256, generator=g).to(dev)
+    Cs = torch.empty(1, 65536, 256, device=dev)
+    Is = torch.empty(1, 65536, 256, dtype=torch.int32, device=dev)
+    ops = 2 * 65536 * 256 * 16
+    f = lambda: tb.tropical_gemm_strided_batched("max_plus", As, Bs, Cs, Is)
+    t_sk = timed_steps(torch, f, 20, 2, settle_s=0.05)
+    os.environ["TROPICAL_GEMM_SMALLK"] = "0"
+    try:
+        t_tiled = timed_steps(torch, f, 20, 2, settle_s=0.05)
+    finally:
+        del os.environ["TROPICAL_GEMM_SMALLK"]
+    out["maxplus_f32_b1_65536x256_k16"] = {
+        "short_k_us": round(t_sk * 1e3, 1), "tiled_us": round(t_tiled * 1e3, 1),
+        "short_k_GOPS": round(ops / (t_sk * 1e-3) / 1e9, 1),
+        "output_GBs": round(2 * 4 * 65536 * 256 / (t_sk * 1e-3) / 1e9, 1)}
+    log(f"[bench] short K 65536x256x16: {out['maxplus_f32_b1_65536x256_k16']}")
+    del As, Bs, Cs, Is
+
     # backward (winner routing) of the headline product: grad_a and grad_b
     # from its argmax and an N(0, 1) upstream gradient
     w = inputs.WORKLOADS[2]
